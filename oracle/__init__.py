@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for RACE attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or executes anything here, and this
+package never imports the product.
+
+The arithmetic lives in ``race_oracle.c`` (plain C, fp64, OpenMP over
+independent elements only); this module marshals numpy arrays to it.  The
+steps it follows are listed, with their sources, in that file's header:
+normalise, project on W[L][P][d], tanh, corner softmax at temperature tau,
+bucket sums A and B, ratio readout, causal running sums, and the exact
+backward of all of it.
+
+Every function takes float arrays of any precision and computes in fp64 on
+exactly the values given (a bf16 or fp32 input is widened without rounding).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "race_oracle.c")
+_LIB = os.path.join(_HERE, "librace_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile race_oracle.c into librace_oracle.so next to it (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
+             "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64, c_int, c_dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.race_oracle_threads.argtypes = [c_int]
+        lib.race_oracle_threads.restype = c_int
+        lib.race_oracle_hash.argtypes = [dp, i64, c_int, dp, c_int, c_int, c_dbl, c_int, dp, dp]
+        lib.race_oracle_hash.restype = c_int
+        lib.race_oracle_forward.argtypes = [dp, dp, dp, dp, c_int, c_int, c_dbl, c_int, c_int,
+                                            i64, i64, c_int, dp, dp]
+        lib.race_oracle_forward.restype = c_int
+        lib.race_oracle_forward_backward.argtypes = [dp, dp, dp, dp, dp, c_int, c_int, c_dbl,
+                                                     c_int, i64, i64, c_int, dp, dp, dp, dp, dp]
+        lib.race_oracle_forward_backward.restype = c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def threads(n: int = 0) -> int:
+    """Set the OpenMP thread count (n > 0) and return the count in use."""
+    return int(_load().race_oracle_threads(int(n)))
+
+
+def _check(err: int, what: str) -> None:
+    if err == 1:
+        raise ValueError(f"oracle {what}: invalid arguments")
+    if err == 2:
+        raise MemoryError(f"oracle {what}: out of host memory")
+    if err:
+        raise RuntimeError(f"oracle {what}: error {err}")
+
+
+def soft_hash(x, W, tau: float, hard: bool = False):
+    """Soft (or hard) bucket assignment of the rows of x[n, d].
+
+    Returns (phi[n, L, R], z[n, L, P]) with z = tanh(W x_hat) and phi the
+    softmax over the R = 2^P corners of the logits (1/tau) <z_l, c_r>.
+    """
+    x = _f64(x)
+    W = _f64(W)
+    L, P, d = W.shape
+    n = x.shape[0]
+    assert x.shape == (n, d)
+    R = 1 << P
+    phi = np.empty((n, L, R))
+    z = np.empty((n, L, P))
+    _check(_load().race_oracle_hash(_ptr(x), n, d, _ptr(W), L, P, float(tau), int(hard),
+                                    _ptr(phi), _ptr(z)), "hash")
+    return phi, z
+
+
+def forward(q, k, v, W, tau: float, causal: bool, hard: bool = False):
+    """RACE attention forward on [..., N, d] inputs; returns (o, den) in fp64.
+
+    den is the readout denominator sum_l phi_l(q)^T A_l of every row.
+    """
+    q, k, v, W = _f64(q), _f64(k), _f64(v), _f64(W)
+    assert q.shape == k.shape == v.shape and q.ndim >= 2
+    N, d = q.shape[-2:]
+    BH = int(np.prod(q.shape[:-2], dtype=np.int64))
+    L, P, dw = W.shape
+    assert dw == d
+    o = np.empty(q.shape)
+    den = np.empty(q.shape[:-1])
+    _check(_load().race_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), L, P, float(tau),
+                                       int(causal), int(hard), BH, N, d, _ptr(o), _ptr(den)),
+           "forward")
+    return o, den
+
+
+def forward_backward(q, k, v, g, W, tau: float, causal: bool):
+    """Forward plus the exact backward for upstream gradient g = dL/do.
+
+    Returns (o, den, dq, dk, dv), all fp64.  The backward uses this call's own
+    forward results only.
+    """
+    q, k, v, g, W = _f64(q), _f64(k), _f64(v), _f64(g), _f64(W)
+    assert q.shape == k.shape == v.shape == g.shape and q.ndim >= 2
+    N, d = q.shape[-2:]
+    BH = int(np.prod(q.shape[:-2], dtype=np.int64))
+    L, P, dw = W.shape
+    assert dw == d
+    o = np.empty(q.shape)
+    den = np.empty(q.shape[:-1])
+    dq = np.empty(q.shape)
+    dk = np.empty(q.shape)
+    dv = np.empty(q.shape)
+    _check(_load().race_oracle_forward_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(W), L, P, float(tau), int(causal), BH, N, d,
+        _ptr(o), _ptr(den), _ptr(dq), _ptr(dk), _ptr(dv)), "forward_backward")
+    return o, den, dq, dk, dv
