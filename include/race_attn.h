@@ -1,0 +1,107 @@
+/*
+ * race_attn.h -- C ABI of the RACE attention library for AMD Instinct MI355X
+ * (gfx950).  Build: librace_attn.so (hand-written HIP kernels).
+ *
+ * RACE attention replaces softmax attention by a strictly linear sketch
+ * (page "RACE Attention: A Strictly Linear-Time Attention for Long-Sequence
+ * Training", gist.science/zh/paper/2510.04008, technical summary §2.2 and
+ * §2.3; the es/pt/fr/de pages of the same paper, technical summaries §2):
+ *
+ *   1. each row x of Q and K is L2-normalised, projected on Gaussian
+ *      hyperplanes W[L][P][d] and squashed, z = tanh(W x_hat);
+ *   2. per table l, the row is soft-assigned over the R = 2^P hypercube
+ *      corners c_r in {-1,+1}^P: phi_l = softmax_r(<z_l, c_r> / tau), with
+ *      c_rp = +1 when bit p of r is set;
+ *   3. the keys are summed into per-table bucket statistics
+ *      A_l = sum_j phi_l(k_j) and B_l = sum_j phi_l(k_j) v_j^T;
+ *   4. query i reads out o_i = sum_l phi_l(q_i)^T B_l / sum_l phi_l(q_i)^T A_l;
+ *   5. in causal mode the sums run over keys j <= i only (streaming
+ *      cumulative statistics, zh §2.3).
+ *   tau is the soft-hash temperature (tau = 1/beta of zh §3).
+ *
+ * Conventions shared by every entry point
+ *   - Q, K, V, O, dO, dQ, dK, dV: device pointers to contiguous [B][H][N][d]
+ *     tensors of type `dt` (RACE_F32: float, RACE_BF16: bfloat16 bits).
+ *   - W: device pointer, contiguous fp32 [L][P][d], shared by every (b, h).
+ *   - den: device pointer, fp32 [B][H][N]: the readout denominator
+ *     m_i = sum_l phi_l(q_i)^T A_l of every row, written by the forward and
+ *     read by the backward (the analogue of a softmax log-sum-exp).
+ *   - workspace: device pointer of at least race_attn_workspace_bytes() bytes,
+ *     256-byte aligned, owned by the caller; its contents are scratch and
+ *     need not be preserved between calls.
+ *   - stream: a hipStream_t.  Every kernel is enqueued on it; calls return
+ *     after enqueueing, without synchronising.  The library never allocates,
+ *     frees or synchronises, keeps no global mutable state and is safe to
+ *     call from several threads.
+ *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32),
+ *     any B, H, N >= 1 (int64 offsets), tau finite and > 0.
+ *   - chunk: tokens per scan segment, 0 = the library chooses; otherwise a
+ *     multiple of 16.  It changes only the order of the floating-point sums.
+ *
+ * Errors are returned synchronously, before anything is enqueued, and leave
+ * every output untouched:
+ *   RACE_ERR_NULL        a required pointer is NULL
+ *   RACE_ERR_SHAPE       B, H, N, d, L or P not positive, or N too large
+ *   RACE_ERR_UNSUPPORTED valid but not implemented (d, P, L, dtype)
+ *   RACE_ERR_TAU         tau not finite or tau <= 0
+ *   RACE_ERR_CHUNK       chunk not 0 and not a positive multiple of 16
+ *   RACE_ERR_WORKSPACE   ws_bytes smaller than required, or misaligned
+ *   RACE_ERR_HIP         a kernel launch failed (hipGetLastError)
+ * Non-finite input values propagate to the outputs; they are not checked.
+ */
+#ifndef RACE_ATTN_H
+#define RACE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RACE_OK = 0,
+    RACE_ERR_NULL = 1,
+    RACE_ERR_SHAPE = 2,
+    RACE_ERR_UNSUPPORTED = 3,
+    RACE_ERR_TAU = 4,
+    RACE_ERR_CHUNK = 5,
+    RACE_ERR_WORKSPACE = 6,
+    RACE_ERR_HIP = 7
+} race_status_t;
+
+typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
+
+/* Workspace size, in bytes, that race_attn_forward (for_backward = 0) or
+ * race_attn_backward (for_backward = 1) needs for this problem.  Pure host
+ * function; `bytes` (host pointer) receives the size. */
+race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, int P,
+                                        int causal, int chunk, race_dtype_t dt,
+                                        int for_backward, size_t *bytes);
+
+/* Forward pass, steps 1-5 above (zh §2.2 bucket aggregation and output
+ * reconstruction; zh §2.3 causal streaming).  Writes O [B][H][N][d] (type dt)
+ * and den [B][H][N] (fp32). */
+race_status_t race_attn_forward(const void *Q, const void *K, const void *V, const float *W,
+                                int L, int P, float tau, int causal, int B, int H, int64_t N,
+                                int d, race_dtype_t dt, int chunk, void *O, float *den,
+                                void *workspace, size_t ws_bytes, void *stream);
+
+/* Backward pass: the exact gradient of the forward (the pages state the
+ * method is differentiable end to end, es §2 item 3, fr §3 item 3).  Given
+ * Q, K, V, W, the forward's O and den, and dO = dLoss/dO, writes dQ, dK, dV
+ * (type dt, [B][H][N][d]).  W is a fixed random projection: no dW. */
+race_status_t race_attn_backward(const void *Q, const void *K, const void *V, const float *W,
+                                 const void *O, const float *den, const void *dO, int L,
+                                 int P, float tau, int causal, int B, int H, int64_t N, int d,
+                                 race_dtype_t dt, int chunk, void *dQ, void *dK, void *dV,
+                                 void *workspace, size_t ws_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *race_attn_status_string(race_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RACE_ATTN_H */

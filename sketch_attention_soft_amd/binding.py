@@ -1,0 +1,156 @@
+"""Thin ctypes binding of librace_attn.so (declared in include/race_attn.h).
+
+Argument marshalling only: shape/dtype/device checks, workspace allocation
+through torch, and the current HIP stream.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librace_attn.so")
+
+RACE_F32, RACE_BF16 = 0, 1
+STATUS = {
+    0: "RACE_OK", 1: "RACE_ERR_NULL", 2: "RACE_ERR_SHAPE", 3: "RACE_ERR_UNSUPPORTED",
+    4: "RACE_ERR_TAU", 5: "RACE_ERR_CHUNK", 6: "RACE_ERR_WORKSPACE", 7: "RACE_ERR_HIP",
+}
+EXPORTS = ("race_attn_workspace_bytes", "race_attn_forward", "race_attn_backward",
+           "race_attn_status_string")
+
+_lib = None
+
+
+class RaceError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load librace_attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                                 ctypes.c_size_t)
+        L.race_attn_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+                                                ctypes.POINTER(sz)]
+        L.race_attn_workspace_bytes.restype = i32
+        L.race_attn_forward.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i32, i64, i32,
+                                        i32, i32, vp, vp, vp, sz, vp]
+        L.race_attn_forward.restype = i32
+        L.race_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, i32, i32,
+                                         i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.race_attn_backward.restype = i32
+        L.race_attn_status_string.argtypes = [i32]
+        L.race_attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise RaceError(code, lib().race_attn_status_string(code).decode())
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return RACE_F32
+    if dtype == torch.bfloat16:
+        return RACE_BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def workspace_bytes(B, H, N, d, L, P, causal, chunk, dtype, for_backward) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_workspace_bytes(B, H, N, d, L, P, int(causal), chunk,
+                                           dtype_code(dtype), int(for_backward),
+                                           ctypes.byref(out)))
+    return out.value
+
+
+def _shape(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return q.shape
+
+
+def _check_tensors(ref: torch.Tensor, *ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("Q, K, V (and O, dO) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if ref.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None):
+    """RACE attention forward; returns (o, den)."""
+    B, H, N, d = _shape(q)
+    _check_tensors(q, k, v)
+    if W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous() or W.device != q.device:
+        raise ValueError("W must be a contiguous fp32 [L, P, d] tensor on the same device")
+    L, P, _ = W.shape
+    o = torch.empty_like(q)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().race_attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P,
+                                   float(tau), int(causal), B, H, N, d, dtype_code(q.dtype),
+                                   chunk, o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), _stream()))
+    return o, den
+
+
+def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, workspace=None):
+    """RACE attention backward; returns (dq, dk, dv)."""
+    B, H, N, d = _shape(q)
+    _check_tensors(q, k, v, o, do)
+    if den.dtype != torch.float32 or den.shape != (B, H, N) or not den.is_contiguous():
+        raise ValueError("den must be a contiguous fp32 [B, H, N] tensor")
+    L, P, _ = W.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, True)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().race_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
+                                    o.data_ptr(), den.data_ptr(), do.data_ptr(), L, P, float(tau),
+                                    int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
+                                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+class RaceAttention(torch.autograd.Function):
+    """Autograd wrapper: o = race_attention(q, k, v); W is a fixed projection."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, W, tau, causal, chunk=0):
+        o, den = forward(q, k, v, W, tau, causal, chunk)
+        ctx.save_for_backward(q, k, v, W, o, den)
+        ctx.cfg = (tau, causal, chunk)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, W, o, den = ctx.saved_tensors
+        tau, causal, chunk = ctx.cfg
+        dq, dk, dv = backward(q, k, v, W, o, den, do.contiguous(), tau, causal, chunk)
+        return dq, dk, dv, None, None, None, None
+
+
+def race_attention(q, k, v, W, tau: float = 1.0, causal: bool = True, chunk: int = 0):
+    return RaceAttention.apply(q, k, v, W, tau, causal, chunk)
