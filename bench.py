@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark: RACE attention forward + backward on one MI355X.
+
+One step = race_attn_forward + race_attn_backward (the whole hot path) over
+the workload's synthetic, seeded inputs, already resident in HBM.  Prints one
+JSON line with tokens/s, the roofline position of the dominant kernel
+(timed live with HIP events recorded by the library around each kernel) and
+the fp64 oracle timed on the host cores on a bounded prefix of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "RACE attn fwd+bwd tokens/s at N=4M causal d=64; % of MFMA/HBM roofline"
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def algorithmic_per_token(w):
+    """Algorithmic work of the method per token (one (b, h) row).
+
+    flops: projections 2 d L P per hashed row (Q and K in the forward; again
+    for the recomputed hash and the dx_hat = du W product of Q and K in the
+    backward), sketch and readout 2 F (d+1) each, the query-side gradient
+    2 F (d+1), the gradient sketch 2 F (d+1), dV and dphi(k) 2 F d each.
+    bytes: one read of every input and one write of every output per pass.
+    """
+    d, L, P = w.d, w.L, w.P
+    F, d1 = L * (1 << P), d + 1
+    e = 2 if w.dtype == "bf16" else 4
+    proj = 2 * d * L * P
+    per_kernel = {
+        "hash_q": proj, "hash_k": proj,
+        "seg_sum_kv": 2 * F * d1, "readout_o": 2 * F * d1,
+        "hash_q_chain": proj, "hash_k_chain": proj,
+        "seg_sum_qd_t": 2 * F * d1,
+        "dpsi_q": 2 * F * d1 + proj, "dpsi_k": 2 * F * d + proj,
+        "readout_dv": 2 * F * d,
+    }
+    fwd_flops = 4 * d * L * P + 4 * F * d1
+    bwd_flops = 8 * d * L * P + 4 * F * d1 + 4 * F * d
+    if not w.backward:
+        per_kernel = {k: v for k, v in per_kernel.items()
+                      if k in ("hash_q", "hash_k", "seg_sum_kv", "readout_o")}
+        return fwd_flops, 4 * d * e + 4, per_kernel
+    return fwd_flops + bwd_flops, 12 * d * e + 8, per_kernel
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_n4m_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=262144,
+                    help="tokens of the workload's first head timed on the oracle (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "path is a design note, not part of this library", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sketch_attention_soft_amd import binding
+    from sketch_attention_soft_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    x = I.workload_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def put(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = put(x["q"]), put(x["k"]), put(x["v"])
+    do = put(x["do"]) if w.backward else None
+    W = torch.from_numpy(x["W"]).to(dev)
+    del x
+    print(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3)) if w.backward else None
+    wsf = torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, False),
+                      dtype=torch.uint8, device=dev)
+    wsb = (torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, True),
+                       dtype=torch.uint8, device=dev) if w.backward else None)
+
+    def step(trf=None, trb=None):
+        binding.forward(q, k, v, W, w.tau, w.causal, w.chunk, workspace=wsf, out=(o, den),
+                        trace=trf)
+        if w.backward:
+            binding.backward(q, k, v, W, o, den, do, w.tau, w.causal, w.chunk, workspace=wsb,
+                             out=grads, trace=trb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    traces = [(binding.Trace(), binding.Trace() if w.backward else None) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(*traces[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    tokens = w.tokens
+    value = tokens / (ms * 1e-3)
+    print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel averages over the timed steps
+    kern: dict[str, float] = {}
+    for tf, tb in traces:
+        for tr in (tf, tb):
+            if tr is None:
+                continue
+            for name, t in tr.results():
+                kern[name] = kern.get(name, 0.0) + t / args.steps
+    flops_tok, bytes_tok, per_kernel = algorithmic_per_token(w)
+    dom = max(kern, key=kern.get)
+    dom_ms = kern[dom]
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = per_kernel.get(dom, 0) * tokens / (dom_ms * 1e-3) / 1e12
+    t_mfma = flops_tok * tokens / (peak * 1e12) * 1e3
+    t_hbm = bytes_tok * tokens / (PEAK_HBM_GBS * 1e9) * 1e3
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 5), "traffic": None, "kernel": dom,
+                "kernel_ms": round(dom_ms, 4)}
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        n_cpu = min(args.cpu_tokens, w.N)
+        xs = I.workload_inputs(w, n_rows=n_cpu)
+        hq, hk, hv = (I.to_f64(xs[n], w.dtype)[:1, :1] for n in ("q", "k", "v"))
+        cores = oracle.threads()
+        tc = time.time()
+        if w.backward:
+            hg = I.to_f64(xs["do"], w.dtype)[:1, :1]
+            oracle.forward_backward(hq, hk, hv, hg, xs["W"], w.tau, w.causal)
+        else:
+            oracle.forward(hq, hk, hv, xs["W"], w.tau, w.causal)
+        dt = time.time() - tc
+        cpu = {"value": round(n_cpu / dt, 1), "unit": "tokens/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"first {n_cpu} tokens of head 0 of {w.name}, "
+                         f"{'fwd+bwd' if w.backward else 'fwd'} in fp64 ({dt:.1f} s)"}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Philox N(0,1); Q, K rows L2-normalised)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "L": w.L,
+                   "P": w.P, "tau": w.tau, "causal": w.causal,
+                   "passes": "fwd+bwd" if w.backward else "fwd", "chunk": w.chunk},
+        "roofline": roofline,
+        "step_roofline": {"t_mfma_ms": round(t_mfma, 4), "t_hbm_ms": round(t_hbm, 4),
+                          "frac": round(max(t_mfma, t_hbm) / ms, 5)},
+        "kernels_ms": {k2: round(v2, 4) for k2, v2 in kern.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -97,6 +97,35 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
                                  race_dtype_t dt, int chunk, void *dQ, void *dK, void *dV,
                                  void *workspace, size_t ws_bytes, void *stream);
 
+/* Per-kernel timing for the *_ex entry points.  The caller creates the HIP
+ * events (hipEventCreate, timing enabled) and owns them; the library records
+ * start[i] / stop[i] on the call's stream around the i-th kernel it enqueues
+ * (at most `capacity` kernels, capacity <= RACE_TRACE_MAX) and sets count
+ * and name[i] (static strings).  Elapsed times are read by the caller after
+ * the stream has completed. */
+#define RACE_TRACE_MAX 24
+typedef struct {
+    int capacity;
+    int count;
+    void *start[RACE_TRACE_MAX];
+    void *stop[RACE_TRACE_MAX];
+    const char *name[RACE_TRACE_MAX];
+} race_trace_t;
+
+/* race_attn_forward / race_attn_backward with optional tracing (trace may
+ * be NULL, which is exactly the plain entry point). */
+race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, const float *W,
+                                   int L, int P, float tau, int causal, int B, int H, int64_t N,
+                                   int d, race_dtype_t dt, int chunk, void *O, float *den,
+                                   void *workspace, size_t ws_bytes, void *stream,
+                                   race_trace_t *trace);
+race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
+                                    const float *W, const void *O, const float *den,
+                                    const void *dO, int L, int P, float tau, int causal, int B,
+                                    int H, int64_t N, int d, race_dtype_t dt, int chunk, void *dQ,
+                                    void *dK, void *dV, void *workspace, size_t ws_bytes,
+                                    void *stream, race_trace_t *trace);
+
 /* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);
 

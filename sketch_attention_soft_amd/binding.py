@@ -20,7 +20,36 @@ STATUS = {
     4: "RACE_ERR_TAU", 5: "RACE_ERR_CHUNK", 6: "RACE_ERR_WORKSPACE", 7: "RACE_ERR_HIP",
 }
 EXPORTS = ("race_attn_workspace_bytes", "race_attn_forward", "race_attn_backward",
-           "race_attn_status_string")
+           "race_attn_forward_ex", "race_attn_backward_ex", "race_attn_status_string")
+TRACE_MAX = 24
+
+
+class _RaceTrace(ctypes.Structure):
+    _fields_ = [("capacity", ctypes.c_int), ("count", ctypes.c_int),
+                ("start", ctypes.c_void_p * TRACE_MAX), ("stop", ctypes.c_void_p * TRACE_MAX),
+                ("name", ctypes.c_char_p * TRACE_MAX)]
+
+
+class Trace:
+    """Caller-owned HIP events that the *_ex entry points record around
+    every kernel they enqueue (see race_trace_t in include/race_attn.h)."""
+
+    def __init__(self, capacity: int = TRACE_MAX):
+        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(capacity)]
+        for a, b in self.events:  # materialise the underlying hipEvent_t
+            a.record()
+            b.record()
+        self.st = _RaceTrace()
+        self.st.capacity = capacity
+        for i, (a, b) in enumerate(self.events):
+            self.st.start[i] = a.cuda_event
+            self.st.stop[i] = b.cuda_event
+
+    def results(self):
+        """[(kernel name, milliseconds)] of the last traced call (after a sync)."""
+        return [(self.st.name[i].decode(), self.events[i][0].elapsed_time(self.events[i][1]))
+                for i in range(self.st.count)]
 
 _lib = None
 
@@ -49,6 +78,11 @@ def lib():
         L.race_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, i32, i32,
                                          i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_backward.restype = i32
+        tp = ctypes.POINTER(_RaceTrace)
+        L.race_attn_forward_ex.argtypes = L.race_attn_forward.argtypes + [tp]
+        L.race_attn_forward_ex.restype = i32
+        L.race_attn_backward_ex.argtypes = L.race_attn_backward.argtypes + [tp]
+        L.race_attn_backward_ex.restype = i32
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -96,41 +130,55 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None):
-    """RACE attention forward; returns (o, den)."""
+def _tp(trace):
+    return ctypes.byref(trace.st) if trace is not None else None
+
+
+def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None, out=None,
+            trace: Trace | None = None):
+    """RACE attention forward; returns (o, den).  out = (o, den) reuses buffers."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v)
     if W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous() or W.device != q.device:
         raise ValueError("W must be a contiguous fp32 [L, P, d] tensor on the same device")
     L, P, _ = W.shape
-    o = torch.empty_like(q)
-    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, den = out
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().race_attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P,
-                                   float(tau), int(causal), B, H, N, d, dtype_code(q.dtype),
-                                   chunk, o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
-                                   workspace.numel(), _stream()))
+    _check(lib().race_attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L,
+                                      P, float(tau), int(causal), B, H, N, d,
+                                      dtype_code(q.dtype), chunk, o.data_ptr(), den.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream(),
+                                      _tp(trace)))
     return o, den
 
 
-def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, workspace=None):
-    """RACE attention backward; returns (dq, dk, dv)."""
+def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, workspace=None,
+             out=None, trace: Trace | None = None):
+    """RACE attention backward; returns (dq, dk, dv).  out = (dq, dk, dv) reuses buffers."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v, o, do)
     if den.dtype != torch.float32 or den.shape != (B, H, N) or not den.is_contiguous():
         raise ValueError("den must be a contiguous fp32 [B, H, N] tensor")
     L, P, _ = W.shape
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, True)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().race_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
-                                    o.data_ptr(), den.data_ptr(), do.data_ptr(), L, P, float(tau),
-                                    int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
-                                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                    workspace.data_ptr(), workspace.numel(), _stream()))
+    _check(lib().race_attn_backward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
+                                       o.data_ptr(), den.data_ptr(), do.data_ptr(), L, P,
+                                       float(tau), int(causal), B, H, N, d, dtype_code(q.dtype),
+                                       chunk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                       workspace.data_ptr(), workspace.numel(), _stream(),
+                                       _tp(trace)))
     return dq, dk, dv
 
 

@@ -20,6 +20,33 @@ constexpr int64_t kMaxN = (int64_t)1 << 40;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Records caller-owned events around each launch when a trace is given.
+struct Tracer {
+    race_trace_t *t;
+    hipStream_t s;
+    void begin(const char *name) const
+    {
+        if (t && t->count < t->capacity) {
+            t->name[t->count] = name;
+            (void)hipEventRecord(static_cast<hipEvent_t>(t->start[t->count]), s);
+        }
+    }
+    void end() const
+    {
+        if (t && t->count < t->capacity) {
+            (void)hipEventRecord(static_cast<hipEvent_t>(t->stop[t->count]), s);
+            t->count++;
+        }
+    }
+};
+
+#define LAUNCH(tr, name, kern, grid, block, ...)                                   \
+    do {                                                                          \
+        (tr).begin(name);                                                         \
+        hipLaunchKernelGGL(kern, grid, block, 0, (tr).s, __VA_ARGS__);            \
+        (tr).end();                                                               \
+    } while (0)
+
 struct Plan {
     int64_t BH, N, rows;
     int L, nw, F, LP;
@@ -104,102 +131,103 @@ int hash_grid(int64_t rows)
 
 template <typename T, int NW>
 void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const float *W, float tau,
-                    int causal, T *O, float *den, char *ws, hipStream_t s)
+                    int causal, T *O, float *den, char *ws, const Tracer &tr)
 {
     float *tq = reinterpret_cast<float *>(ws + p.f_tq);
     float *tk = reinterpret_cast<float *>(ws + p.f_tk);
     float *st = reinterpret_cast<float *>(ws + p.f_st);
     const float inv_tau = 1.0f / tau;
-    const int hg = hash_grid(p.rows);
-    hipLaunchKernelGGL((race::hash_kernel<T, false>), dim3(hg), dim3(256), 0, s, Q, p.rows, W,
-                       p.L, inv_tau, tq);
-    hipLaunchKernelGGL((race::hash_kernel<T, false>), dim3(hg), dim3(256), 0, s, K, p.rows, W,
-                       p.L, inv_tau, tk);
+    const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
+    LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
+    LAUNCH(tr, "hash_k", (race::hash_kernel<T, false>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
     const race::ValSrc<T> vs{V, nullptr, nullptr};
-    const int nblk = (int)(p.BH * p.nseg);
-    hipLaunchKernelGGL((race::seg_sum_kernel<T, NW, false, false>), dim3(nblk), dim3(NW * 64), 0,
-                       s, tk, race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st);
+    const dim3 nblk((unsigned)(p.BH * p.nseg));
+    LAUNCH(tr, "seg_sum_kv", (race::seg_sum_kernel<T, NW, false, false>), nblk, bw, tk, race::NP,
+           vs, p.N, p.L, (int)p.seg, p.nseg, st);
     const int64_t elems = (int64_t)p.F * race::NCOL;
-    hipLaunchKernelGGL(race::scan_kernel, dim3((unsigned)((elems + 255) / 256), (unsigned)p.BH),
-                       dim3(256), 0, s, st, p.nseg, elems, 0);
+    const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
+    LAUNCH(tr, "scan_kv", race::scan_kernel, sgrid, b256, st, p.nseg, elems, 0);
     if (causal)
-        hipLaunchKernelGGL((race::readout_kernel<T, NW, true, false>), dim3(nblk), dim3(NW * 64),
-                           0, s, tq, tk, race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
+        LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, true, false>), nblk, bw, tq, tk,
+               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
     else
-        hipLaunchKernelGGL((race::readout_kernel<T, NW, false, false>), dim3(nblk), dim3(NW * 64),
-                           0, s, tq, tk, race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
+        LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, false, false>), nblk, bw, tq, tk,
+               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
+}
+
+template <typename T, int NW, int CAUSAL>
+void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
+                          const T *O, const float *den, const T *dO, float tau, T *dQ, T *dK,
+                          T *dV, char *ws, const Tracer &tr)
+{
+    float *tq = reinterpret_cast<float *>(ws + p.b_tq);
+    float *tk = reinterpret_cast<float *>(ws + p.b_tk);
+    float *sS = reinterpret_cast<float *>(ws + p.b_s);    // key state, CxF layout
+    float *sGt = reinterpret_cast<float *>(ws + p.b_gt);  // gradient state, CxF layout
+    float *sG = reinterpret_cast<float *>(ws + p.b_g);    // gradient state, FxC layout
+    char *wt = ws + p.b_wt;
+    const float inv_tau = 1.0f / tau;
+    const int lp32 = (p.LP + 31) / 32 * 32;
+    const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
+    LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,
+           p.LP, lp32, wt);
+    LAUNCH(tr, "hash_q_chain", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L,
+           inv_tau, tq);
+    LAUNCH(tr, "hash_k_chain", (race::hash_kernel<T, true>), hg, b256, K, p.rows, W, p.L,
+           inv_tau, tk);
+    const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
+    const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
+    const dim3 nblk((unsigned)(p.BH * p.nseg));
+    const int64_t elems = (int64_t)p.F * race::NCOL;
+    const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
+    const int ts = 2 * race::NP;
+    // key-side state S (CxF, for dQ): prefix over segments
+    LAUNCH(tr, "seg_sum_kv_t", (race::seg_sum_kernel<T, NW, true, false>), nblk, bw, tk, ts, vv,
+           p.N, p.L, (int)p.seg, p.nseg, sS);
+    LAUNCH(tr, "scan_kv_t", race::scan_kernel, sgrid, b256, sS, p.nseg, elems, 0);
+    // query-side gradient states G (CxF for dK, FxC for dV): suffix over segments
+    LAUNCH(tr, "seg_sum_qd_t", (race::seg_sum_kernel<T, NW, true, true>), nblk, bw, tq, ts, vd,
+           p.N, p.L, (int)p.seg, p.nseg, sGt);
+    LAUNCH(tr, "scan_qd_t", race::scan_kernel, sgrid, b256, sGt, p.nseg, elems, 1);
+    LAUNCH(tr, "seg_sum_qd", (race::seg_sum_kernel<T, NW, false, true>), nblk, bw, tq, ts, vd,
+           p.N, p.L, (int)p.seg, p.nseg, sG);
+    LAUNCH(tr, "scan_qd", race::scan_kernel, sgrid, b256, sG, p.nseg, elems, 1);
+    // dQ: readers Q (values D), writers K (values [v|1]), token order
+    LAUNCH(tr, "dpsi_q", (race::dpsi_kernel<T, NW, CAUSAL, false, true>), nblk, bw, Q, tq, tk, vd,
+           vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ);
+    // dK: readers K (values [v|1]), writers Q (values D), reverse order
+    LAUNCH(tr, "dpsi_k", (race::dpsi_kernel<T, NW, CAUSAL, true, false>), nblk, bw, K, tk, tq, vv,
+           vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK);
+    // dV: keys read the FxC gradient state, reverse order
+    LAUNCH(tr, "readout_dv", (race::readout_kernel<T, NW, CAUSAL != 0, true>), nblk, bw, tk, tq,
+           ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr);
 }
 
 template <typename T, int NW>
 void launch_backward(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                      const T *O, const float *den, const T *dO, float tau, int causal, T *dQ,
-                     T *dK, T *dV, char *ws, hipStream_t s)
+                     T *dK, T *dV, char *ws, const Tracer &tr)
 {
-    float *tq = reinterpret_cast<float *>(ws + p.b_tq);
-    float *tk = reinterpret_cast<float *>(ws + p.b_tk);
-    float *sS = reinterpret_cast<float *>(ws + p.b_s);    // key state, [80 x F] layout
-    float *sGt = reinterpret_cast<float *>(ws + p.b_gt);  // gradient state, [80 x F] layout
-    float *sG = reinterpret_cast<float *>(ws + p.b_g);    // gradient state, [F x 80] layout
-    char *wt = ws + p.b_wt;
-    const float inv_tau = 1.0f / tau;
-    const int hg = hash_grid(p.rows);
-    const int lp32 = (p.LP + 31) / 32 * 32;
-    hipLaunchKernelGGL(race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), dim3(256), 0, s,
-                       W, p.LP, lp32, wt);
-    hipLaunchKernelGGL((race::hash_kernel<T, true>), dim3(hg), dim3(256), 0, s, Q, p.rows, W,
-                       p.L, inv_tau, tq);
-    hipLaunchKernelGGL((race::hash_kernel<T, true>), dim3(hg), dim3(256), 0, s, K, p.rows, W,
-                       p.L, inv_tau, tk);
-    const race::ValSrc<T> vv{V, nullptr, nullptr};     // [v | 1]
-    const race::ValSrc<T> vd{dO, O, den};              // [dO/m | -(dO.o)/m]
-    const int nblk = (int)(p.BH * p.nseg);
-    const int64_t elems = (int64_t)p.F * race::NCOL;
-    const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
-    const int ts = 2 * race::NP;
-    // key-side state S^T (for dQ), prefix over segments
-    hipLaunchKernelGGL((race::seg_sum_kernel<T, NW, true, false>), dim3(nblk), dim3(NW * 64), 0,
-                       s, tk, ts, vv, p.N, p.L, (int)p.seg, p.nseg, sS);
-    hipLaunchKernelGGL(race::scan_kernel, sgrid, dim3(256), 0, s, sS, p.nseg, elems, 0);
-    // query-side gradient states G^T (for dK) and G (for dV), suffix over segments
-    hipLaunchKernelGGL((race::seg_sum_kernel<T, NW, true, true>), dim3(nblk), dim3(NW * 64), 0,
-                       s, tq, ts, vd, p.N, p.L, (int)p.seg, p.nseg, sGt);
-    hipLaunchKernelGGL(race::scan_kernel, sgrid, dim3(256), 0, s, sGt, p.nseg, elems, 1);
-    hipLaunchKernelGGL((race::seg_sum_kernel<T, NW, false, true>), dim3(nblk), dim3(NW * 64), 0,
-                       s, tq, ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG);
-    hipLaunchKernelGGL(race::scan_kernel, sgrid, dim3(256), 0, s, sG, p.nseg, elems, 1);
-    // dQ: readers Q (values D), writers K (values [v|1]), forward order
-    // dK: readers K (values [v|1]), writers Q (values D), reverse order
-    if (causal) {
-        hipLaunchKernelGGL((race::dpsi_kernel<T, NW, 1, false, true>), dim3(nblk), dim3(NW * 64),
-                           0, s, Q, tq, tk, vd, vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ);
-        hipLaunchKernelGGL((race::dpsi_kernel<T, NW, 1, true, false>), dim3(nblk), dim3(NW * 64),
-                           0, s, K, tk, tq, vv, vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK);
-        hipLaunchKernelGGL((race::readout_kernel<T, NW, true, true>), dim3(nblk), dim3(NW * 64), 0,
-                           s, tk, tq, ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr);
-    } else {
-        hipLaunchKernelGGL((race::dpsi_kernel<T, NW, 0, false, true>), dim3(nblk), dim3(NW * 64),
-                           0, s, Q, tq, tk, vd, vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ);
-        hipLaunchKernelGGL((race::dpsi_kernel<T, NW, 0, true, false>), dim3(nblk), dim3(NW * 64),
-                           0, s, K, tk, tq, vv, vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK);
-        hipLaunchKernelGGL((race::readout_kernel<T, NW, false, true>), dim3(nblk), dim3(NW * 64),
-                           0, s, tk, tq, ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr);
-    }
+    if (causal)
+        launch_backward_body<T, NW, 1>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, tr);
+    else
+        launch_backward_body<T, NW, 0>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, tr);
 }
 
 template <typename T>
 void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V, const float *W,
-                      float tau, int causal, void *O, float *den, char *ws, hipStream_t s)
+                      float tau, int causal, void *O, float *den, char *ws, const Tracer &tr)
 {
     auto q = static_cast<const T *>(Q);
     auto k = static_cast<const T *>(K);
     auto v = static_cast<const T *>(V);
     auto o = static_cast<T *>(O);
     switch (p.nw) {
-    case 1: launch_forward<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, s); break;
-    case 2: launch_forward<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, s); break;
-    case 4: launch_forward<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, s); break;
+    case 1: launch_forward<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+    case 2: launch_forward<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+    case 4: launch_forward<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
     default:
-        if constexpr (sizeof(T) == 2) launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, s);
+        if constexpr (sizeof(T) == 2) launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, tr);
         break;
     }
 }
@@ -208,7 +236,7 @@ template <typename T>
 void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *V,
                        const float *W, const void *O, const float *den, const void *dO,
                        float tau, int causal, void *dQ, void *dK, void *dV, char *ws,
-                       hipStream_t s)
+                       const Tracer &tr)
 {
     auto q = static_cast<const T *>(Q);
     auto k = static_cast<const T *>(K);
@@ -219,14 +247,24 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     auto dk = static_cast<T *>(dK);
     auto dv = static_cast<T *>(dV);
     switch (p.nw) {
-    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, s); break;
-    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, s); break;
-    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, s); break;
+    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr); break;
+    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr); break;
+    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr); break;
     default:
         if constexpr (sizeof(T) == 2)
-            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, s);
+            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr);
         break;
     }
+}
+
+race_status_t check_trace(race_trace_t *trace)
+{
+    if (!trace) return RACE_OK;
+    if (trace->capacity < 0 || trace->capacity > RACE_TRACE_MAX) return RACE_ERR_SHAPE;
+    for (int i = 0; i < trace->capacity; ++i)
+        if (!trace->start[i] || !trace->stop[i]) return RACE_ERR_NULL;
+    trace->count = 0;
+    return RACE_OK;
 }
 
 }  // namespace
@@ -246,10 +284,11 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     return RACE_OK;
 }
 
-race_status_t race_attn_forward(const void *Q, const void *K, const void *V, const float *W,
-                                int L, int P, float tau, int causal, int B, int H, int64_t N,
-                                int d, race_dtype_t dt, int chunk, void *O, float *den,
-                                void *workspace, size_t ws_bytes, void *stream)
+race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, const float *W,
+                                   int L, int P, float tau, int causal, int B, int H, int64_t N,
+                                   int d, race_dtype_t dt, int chunk, void *O, float *den,
+                                   void *workspace, size_t ws_bytes, void *stream,
+                                   race_trace_t *trace)
 {
     if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
     Plan p;
@@ -257,13 +296,48 @@ race_status_t race_attn_forward(const void *Q, const void *K, const void *V, con
     if (st != RACE_OK) return st;
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = check_trace(trace)) != RACE_OK) return st;
+    const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
-        dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, s);
+        dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, tr);
     else
-        dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, s);
+        dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, tr);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_forward(const void *Q, const void *K, const void *V, const float *W,
+                                int L, int P, float tau, int causal, int B, int H, int64_t N,
+                                int d, race_dtype_t dt, int chunk, void *O, float *den,
+                                void *workspace, size_t ws_bytes, void *stream)
+{
+    return race_attn_forward_ex(Q, K, V, W, L, P, tau, causal, B, H, N, d, dt, chunk, O, den,
+                                workspace, ws_bytes, stream, nullptr);
+}
+
+race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
+                                    const float *W, const void *O, const float *den,
+                                    const void *dO, int L, int P, float tau, int causal, int B,
+                                    int H, int64_t N, int d, race_dtype_t dt, int chunk, void *dQ,
+                                    void *dK, void *dV, void *workspace, size_t ws_bytes,
+                                    void *stream, race_trace_t *trace)
+{
+    if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !workspace)
+        return RACE_ERR_NULL;
+    Plan p;
+    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    if (st != RACE_OK) return st;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if ((st = check_ws(p, p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
+    if ((st = check_trace(trace)) != RACE_OK) return st;
+    const Tracer tr{trace, static_cast<hipStream_t>(stream)};
+    (void)hipGetLastError();
+    char *ws = static_cast<char *>(workspace);
+    if (dt == RACE_BF16)
+        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, tr);
+    else
+        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 
@@ -273,21 +347,8 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
                                  race_dtype_t dt, int chunk, void *dQ, void *dK, void *dV,
                                  void *workspace, size_t ws_bytes, void *stream)
 {
-    if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !workspace)
-        return RACE_ERR_NULL;
-    Plan p;
-    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
-    if (st != RACE_OK) return st;
-    if ((st = check_tau(tau)) != RACE_OK) return st;
-    if ((st = check_ws(p, p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    char *ws = static_cast<char *>(workspace);
-    if (dt == RACE_BF16)
-        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, s);
-    else
-        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, s);
-    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+    return race_attn_backward_ex(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk,
+                                 dQ, dK, dV, workspace, ws_bytes, stream, nullptr);
 }
 
 const char *race_attn_status_string(race_status_t status)
