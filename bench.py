@@ -38,7 +38,16 @@ def algorithmic_per_token(w):
     F, d1 = L * (1 << P), d + 1
     e = 2 if w.dtype == "bf16" else 4
     proj = 2 * d * L * P
+    # kernels that hash their own rows carry those projections
     per_kernel = {
+        # fused kernels (bf16, L <= 32)
+        "sum_kv": proj + 2 * F * d1,            # hash K, sketch of the keys
+        "fwd_o": proj + 2 * F * d1,             # hash Q, readout
+        "sum_qd": proj + 2 * F * d1,            # recomputed hash Q, gradient sketch
+        "dq": proj + 2 * F * d1 + proj,         # hash Q, query-side gradient, dx_hat = du W
+        "dk": proj + 2 * F * d + proj,          # hash K, dphi(k), dx_hat = du W
+        "dv": 2 * F * d,                        # dV readout
+        # unfused kernels (fp32, L > 32)
         "hash_q": proj, "hash_k": proj,
         "seg_sum_kv": 2 * F * d1, "readout_o": 2 * F * d1,
         "hash_q_chain": proj, "hash_k_chain": proj,
@@ -49,8 +58,6 @@ def algorithmic_per_token(w):
     fwd_flops = 4 * d * L * P + 4 * F * d1
     bwd_flops = 8 * d * L * P + 4 * F * d1 + 4 * F * d
     if not w.backward:
-        per_kernel = {k: v for k, v in per_kernel.items()
-                      if k in ("hash_q", "hash_k", "seg_sum_kv", "readout_o")}
         return fwd_flops, 4 * d * e + 4, per_kernel
     return fwd_flops + bwd_flops, 12 * d * e + 8, per_kernel
 

@@ -126,6 +126,15 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
                                     void *dK, void *dV, void *workspace, size_t ws_bytes,
                                     void *stream, race_trace_t *trace);
 
+/* Diagnostic: the polynomial the kernels use for t = tanh(tanh(v) / tau).
+ * With e = exp(-2|v|) and y = 2e - 1, t = sign(v) * sum_k coef[k] y^k for
+ * k = 0 .. *deg (Chebyshev interpolation of tanh(((1-e)/(1+e))/tau) on
+ * e in [0, 1], fitted in fp64 on the host to the accuracy the dtype needs).
+ * coef receives RACE_SQUASH_MAXDEG + 1 floats; *deg = -1 means the kernels
+ * evaluate the function directly instead. */
+#define RACE_SQUASH_MAXDEG 16
+race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
+
 /* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);
 

@@ -10,6 +10,7 @@
 
 #include "race_bwd.h"
 #include "race_common.h"
+#include "race_fused.h"
 #include "race_fwd.h"
 
 namespace {
@@ -87,6 +88,7 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
         if (seg > 8192) seg = 8192;
     }
     if (seg > n16) seg = n16;
+    seg = (seg + 31) / 32 * 32;  // whole 32-token sub-chunks per segment
     p->seg = seg;
     p->nseg = (N + seg - 1) / seg;
     if (p->BH * p->nseg > 0x7fffffffLL) return RACE_ERR_SHAPE;
@@ -107,6 +109,64 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->b_wt = p->b_g + p->st_bytes;
     p->b_total = p->b_wt + p->wt_bytes;
     return RACE_OK;
+}
+
+// h(e) = tanh(((1 - e)/(1 + e)) / tau) on e in [0, 1], the outer tanh of
+// t = tanh(tanh(v) / tau) written through e = exp(-2|v|).
+double squash_ref(double e, double tau) { return std::tanh(((1.0 - e) / (1.0 + e)) / tau); }
+
+// Chebyshev interpolation of h at the Chebyshev nodes of y = 2e - 1, in fp64,
+// at the kernels' fixed degree for the dtype, converted to monomial
+// coefficients in y.  Kept when its fp32 Horner evaluation stays within the
+// dtype's target on a dense grid; otherwise deg = -1 (direct evaluation).
+race::Squash fit_squash(float tau, race_dtype_t dt)
+{
+    race::Squash sq;
+    std::memset(&sq, 0, sizeof sq);
+    sq.inv_tau = 1.0f / tau;
+    sq.deg = -1;
+    const double target = dt == RACE_BF16 ? 1e-5 : 2.5e-7;
+    const int deg = dt == RACE_BF16 ? race::SqDeg<bf16>::v : race::SqDeg<float>::v;
+    constexpr int NG = 4001;
+    const int n = deg + 1;
+    double fk[race::MAXDEG + 1], a[race::MAXDEG + 1];
+    for (int k = 0; k < n; ++k) {
+        const double y = std::cos(M_PI * (k + 0.5) / n);
+        fk[k] = squash_ref(0.5 * (y + 1.0), tau);
+    }
+    for (int j = 0; j < n; ++j) {
+        double sum = 0.0;
+        for (int k = 0; k < n; ++k) sum += fk[k] * std::cos(M_PI * j * (k + 0.5) / n);
+        a[j] = (j == 0 ? 1.0 : 2.0) * sum / n;
+    }
+    // sum_j a_j T_j(y) in the monomial basis, T_{j+1} = 2y T_j - T_{j-1}
+    double mono[race::MAXDEG + 1] = {0}, tm1[race::MAXDEG + 2] = {0}, t0[race::MAXDEG + 2] = {0},
+           t1[race::MAXDEG + 2] = {0};
+    t0[0] = 1.0;
+    for (int j = 0; j < n; ++j) {
+        for (int i = 0; i <= j; ++i) mono[i] += a[j] * t0[i];
+        for (int i = 0; i <= j + 1; ++i)
+            t1[i] = (i > 0 ? 2.0 * t0[i - 1] : 0.0) - (i <= j - 1 ? tm1[i] : 0.0);
+        for (int i = 0; i <= j + 1; ++i) {
+            tm1[i] = t0[i];
+            t0[i] = t1[i];
+        }
+    }
+    float c[race::MAXDEG + 1];
+    for (int i = 0; i <= deg; ++i) c[i] = (float)mono[i];
+    double err = 0.0;
+    for (int k = 0; k < NG; ++k) {
+        const double e = (double)k / (NG - 1);
+        const float y = 2.0f * (float)e - 1.0f;
+        float h = c[deg];
+        for (int i = deg - 1; i >= 0; --i) h = std::fma(h, y, c[i]);
+        err = std::fmax(err, std::fabs((double)h - squash_ref(e, tau)));
+    }
+    if (err <= target) {
+        for (int i = 0; i <= deg; ++i) sq.c[i] = c[i];
+        sq.deg = deg;
+    }
+    return sq;
 }
 
 race_status_t check_tau(float tau)
@@ -138,6 +198,26 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     float *st = reinterpret_cast<float *>(ws + p.f_st);
     const float inv_tau = 1.0f / tau;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
+    if constexpr (sizeof(T) == 2 && NW <= 4) {
+        // fused path: 4 tables per wave, 2*NW waves
+        constexpr int FW = 2 * NW, HT = 1;
+        const dim3 bf(FW * 64);
+        const race::Squash sq = fit_squash(tau, RACE_BF16);
+        const dim3 nblk((unsigned)(p.BH * p.nseg));
+        const int64_t elems = (int64_t)p.F * race::NCOL;
+        const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
+        const race::ValSrc<T> vv{V, nullptr, nullptr};
+        LAUNCH(tr, "sum_kv", (race::fused_sum_kernel<T, FW, HT, false, 1>), nblk, bf, K, vv, W,
+               p.L, sq, p.N, (int)p.seg, p.nseg, st, nullptr);
+        LAUNCH(tr, "scan_kv", race::scan_kernel, sgrid, b256, st, p.nseg, elems, 0);
+        if (causal)
+            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, FW, HT, true, false>), nblk, bf, Q, K,
+                   vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
+        else
+            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, FW, HT, false, false>), nblk, bf, Q, K,
+                   vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
+        return;
+    }
     LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
     LAUNCH(tr, "hash_k", (race::hash_kernel<T, false>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
     const race::ValSrc<T> vs{V, nullptr, nullptr};
@@ -169,6 +249,33 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     const float inv_tau = 1.0f / tau;
     const int lp32 = (p.LP + 31) / 32 * 32;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
+    if constexpr (sizeof(T) == 2 && NW <= 4) {
+        // fused path: 4 tables per wave, 2*NW waves
+        constexpr int FW = 2 * NW, HT = 1;
+        const dim3 bf(FW * 64);
+        const race::Squash sq = fit_squash(tau, RACE_BF16);
+        const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
+        const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
+        const dim3 nblk((unsigned)(p.BH * p.nseg));
+        const int64_t elems = (int64_t)p.F * race::NCOL;
+        const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
+        // key state S (CxF, for dQ): prefix over segments
+        LAUNCH(tr, "sum_kv_t", (race::fused_sum_kernel<T, FW, HT, false, 2>), nblk, bf, K, vv, W,
+               p.L, sq, p.N, (int)p.seg, p.nseg, nullptr, sS);
+        LAUNCH(tr, "scan_kv_t", race::scan_kernel, sgrid, b256, sS, p.nseg, elems, 0);
+        // gradient state G (FxC for dV and CxF for dK): suffix over segments
+        LAUNCH(tr, "sum_qd", (race::fused_sum_kernel<T, FW, HT, true, 3>), nblk, bf, Q, vd, W,
+               p.L, sq, p.N, (int)p.seg, p.nseg, sG, sGt);
+        LAUNCH(tr, "scan_qd", race::scan_kernel, sgrid, b256, sG, p.nseg, elems, 1);
+        LAUNCH(tr, "scan_qd_t", race::scan_kernel, sgrid, b256, sGt, p.nseg, elems, 1);
+        LAUNCH(tr, "dq", (race::fused_dpsi_kernel<T, FW, HT, CAUSAL != 0, false, true>), nblk, bf,
+               Q, K, vd, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, sS, dQ);
+        LAUNCH(tr, "dk", (race::fused_dpsi_kernel<T, FW, HT, CAUSAL != 0, true, false>), nblk, bf,
+               K, Q, vv, vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sGt, dK);
+        LAUNCH(tr, "dv", (race::fused_walk_kernel<T, FW, HT, CAUSAL != 0, true>), nblk, bf, K, Q,
+               vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sG, dV, nullptr);
+        return;
+    }
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,
            p.LP, lp32, wt);
     LAUNCH(tr, "hash_q_chain", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L,
@@ -349,6 +456,18 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
 {
     return race_attn_backward_ex(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk,
                                  dQ, dK, dV, workspace, ws_bytes, stream, nullptr);
+}
+
+race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg)
+{
+    if (!coef || !deg) return RACE_ERR_NULL;
+    race_status_t st = check_tau(tau);
+    if (st != RACE_OK) return st;
+    if (dt != RACE_F32 && dt != RACE_BF16) return RACE_ERR_UNSUPPORTED;
+    const race::Squash sq = fit_squash(tau, dt);
+    for (int i = 0; i <= race::MAXDEG; ++i) coef[i] = sq.c[i];
+    *deg = sq.deg;
+    return RACE_OK;
 }
 
 const char *race_attn_status_string(race_status_t status)

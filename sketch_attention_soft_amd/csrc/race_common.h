@@ -138,6 +138,15 @@ template <typename T> __device__ __forceinline__ F4<T> acc2frag4(const floatx4 &
     return f;
 }
 
+// Workgroup barrier that orders LDS only: global loads in flight (prefetches
+// of the next chunk) are not waited for, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

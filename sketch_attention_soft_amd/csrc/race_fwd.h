@@ -337,7 +337,23 @@ __global__ __launch_bounds__(256) void scan_kernel(float *__restrict__ st, int64
     if (e >= elems) return;
     float *p = st + (int64_t)blockIdx.y * (nseg + 1) * elems + e;
     float run = 0.f;
-    for (int64_t i = 0; i < nseg; ++i) {
+    constexpr int U = 8;  // loads in flight per thread
+    int64_t i = 0;
+    for (; i + U <= nseg; i += U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = reverse ? nseg - 1 - (i + u) : i + u;
+            v[u] = p[g * elems];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = reverse ? nseg - 1 - (i + u) : i + u;
+            p[g * elems] = run;
+            run += v[u];
+        }
+    }
+    for (; i < nseg; ++i) {
         const int64_t g = reverse ? nseg - 1 - i : i;
         const float v = p[g * elems];
         p[g * elems] = run;
