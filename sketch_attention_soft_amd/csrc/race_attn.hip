@@ -13,6 +13,18 @@
 #include "race_fused.h"
 #include "race_fwd.h"
 
+// Hash tiles (4 tables each) per wave of the fused kernels: 1 gives 2x as
+// many waves with half the registers each.
+#ifndef RACE_HT_SUM
+#define RACE_HT_SUM 1
+#endif
+#ifndef RACE_HT_WALK
+#define RACE_HT_WALK 1
+#endif
+#ifndef RACE_HT_DPSI
+#define RACE_HT_DPSI 1
+#endif
+
 namespace {
 
 using race::bf16;
@@ -51,6 +63,7 @@ struct Tracer {
 struct Plan {
     int64_t BH, N, rows;
     int L, nw, F, LP;
+    bool fused;        // bf16 and L <= 32: kernels hash their own rows
     int64_t seg, nseg;
     size_t st_bytes;   // one set of segment states (nseg + 1 per head)
     size_t t_bytes;    // forward hash features of Q or K
@@ -92,11 +105,13 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->seg = seg;
     p->nseg = (N + seg - 1) / seg;
     if (p->BH * p->nseg > 0x7fffffffLL) return RACE_ERR_SHAPE;
+    p->fused = dt == RACE_BF16 && L <= 32;
     p->st_bytes = align256((size_t)p->BH * (p->nseg + 1) * p->F * race::NCOL * sizeof(float));
-    p->t_bytes = align256((size_t)p->rows * L * race::NP * sizeof(float));
-    p->tb_bytes = align256((size_t)p->rows * L * 2 * race::NP * sizeof(float));
+    // the fused kernels keep hash features on chip: no per-row buffers
+    p->t_bytes = p->fused ? 0 : align256((size_t)p->rows * L * race::NP * sizeof(float));
+    p->tb_bytes = p->fused ? 0 : align256((size_t)p->rows * L * 2 * race::NP * sizeof(float));
     const int lp32 = (p->LP + 31) / 32 * 32;
-    p->wt_bytes = align256((size_t)race::HD * lp32 * (2 * sizeof(bf16) + sizeof(float)));
+    p->wt_bytes = p->fused ? 0 : align256((size_t)race::HD * lp32 * (2 * sizeof(bf16) + sizeof(float)));
     p->f_tq = 0;
     p->f_tk = p->f_tq + p->t_bytes;
     p->f_st = p->f_tk + p->t_bytes;
@@ -139,14 +154,17 @@ race::Squash fit_squash(float tau, race_dtype_t dt)
         for (int k = 0; k < n; ++k) sum += fk[k] * std::cos(M_PI * j * (k + 0.5) / n);
         a[j] = (j == 0 ? 1.0 : 2.0) * sum / n;
     }
-    // sum_j a_j T_j(y) in the monomial basis, T_{j+1} = 2y T_j - T_{j-1}
+    // sum_j a_j T_j(y) in the monomial basis: T_0 = 1, T_1 = y,
+    // T_{j+1} = 2y T_j - T_{j-1}
     double mono[race::MAXDEG + 1] = {0}, tm1[race::MAXDEG + 2] = {0}, t0[race::MAXDEG + 2] = {0},
            t1[race::MAXDEG + 2] = {0};
     t0[0] = 1.0;
     for (int j = 0; j < n; ++j) {
         for (int i = 0; i <= j; ++i) mono[i] += a[j] * t0[i];
-        for (int i = 0; i <= j + 1; ++i)
-            t1[i] = (i > 0 ? 2.0 * t0[i - 1] : 0.0) - (i <= j - 1 ? tm1[i] : 0.0);
+        for (int i = 0; i <= j + 1; ++i) {
+            const double up = i > 0 ? t0[i - 1] : 0.0;
+            t1[i] = j == 0 ? up : 2.0 * up - (i <= j - 1 ? tm1[i] : 0.0);
+        }
         for (int i = 0; i <= j + 1; ++i) {
             tm1[i] = t0[i];
             t0[i] = t1[i];
@@ -199,23 +217,23 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     const float inv_tau = 1.0f / tau;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
     if constexpr (sizeof(T) == 2 && NW <= 4) {
-        // fused path: 4 tables per wave, 2*NW waves
-        constexpr int FW = 2 * NW, HT = 1;
-        const dim3 bf(FW * 64);
+        // fused path: HT hash tiles (4 tables each) per wave, 2*NW/HT waves
+        constexpr int HS = NW >= RACE_HT_SUM ? RACE_HT_SUM : 1, WS = 2 * NW / HS;
+        constexpr int HW = NW >= RACE_HT_WALK ? RACE_HT_WALK : 1, WW = 2 * NW / HW;
         const race::Squash sq = fit_squash(tau, RACE_BF16);
         const dim3 nblk((unsigned)(p.BH * p.nseg));
         const int64_t elems = (int64_t)p.F * race::NCOL;
         const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
         const race::ValSrc<T> vv{V, nullptr, nullptr};
-        LAUNCH(tr, "sum_kv", (race::fused_sum_kernel<T, FW, HT, false, 1>), nblk, bf, K, vv, W,
-               p.L, sq, p.N, (int)p.seg, p.nseg, st, nullptr);
+        LAUNCH(tr, "sum_kv", (race::fused_sum_kernel<T, WS, HS, false, 1>), nblk, dim3(WS * 64), K,
+               vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, nullptr);
         LAUNCH(tr, "scan_kv", race::scan_kernel, sgrid, b256, st, p.nseg, elems, 0);
         if (causal)
-            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, FW, HT, true, false>), nblk, bf, Q, K,
-                   vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
+            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, WW, HW, true, false>), nblk,
+                   dim3(WW * 64), Q, K, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
         else
-            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, FW, HT, false, false>), nblk, bf, Q, K,
-                   vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
+            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, WW, HW, false, false>), nblk,
+                   dim3(WW * 64), Q, K, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
         return;
     }
     LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
@@ -250,9 +268,10 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     const int lp32 = (p.LP + 31) / 32 * 32;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
     if constexpr (sizeof(T) == 2 && NW <= 4) {
-        // fused path: 4 tables per wave, 2*NW waves
-        constexpr int FW = 2 * NW, HT = 1;
-        const dim3 bf(FW * 64);
+        // fused path: HT hash tiles (4 tables each) per wave, 2*NW/HT waves
+        constexpr int HS = NW >= RACE_HT_SUM ? RACE_HT_SUM : 1, WS = 2 * NW / HS;
+        constexpr int HW = NW >= RACE_HT_WALK ? RACE_HT_WALK : 1, WW = 2 * NW / HW;
+        constexpr int HD_ = NW >= RACE_HT_DPSI ? RACE_HT_DPSI : 1, WD = 2 * NW / HD_;
         const race::Squash sq = fit_squash(tau, RACE_BF16);
         const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
         const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
@@ -260,20 +279,20 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
         const int64_t elems = (int64_t)p.F * race::NCOL;
         const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
         // key state S (CxF, for dQ): prefix over segments
-        LAUNCH(tr, "sum_kv_t", (race::fused_sum_kernel<T, FW, HT, false, 2>), nblk, bf, K, vv, W,
-               p.L, sq, p.N, (int)p.seg, p.nseg, nullptr, sS);
+        LAUNCH(tr, "sum_kv_t", (race::fused_sum_kernel<T, WS, HS, false, 2>), nblk, dim3(WS * 64),
+               K, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, nullptr, sS);
         LAUNCH(tr, "scan_kv_t", race::scan_kernel, sgrid, b256, sS, p.nseg, elems, 0);
         // gradient state G (FxC for dV and CxF for dK): suffix over segments
-        LAUNCH(tr, "sum_qd", (race::fused_sum_kernel<T, FW, HT, true, 3>), nblk, bf, Q, vd, W,
-               p.L, sq, p.N, (int)p.seg, p.nseg, sG, sGt);
+        LAUNCH(tr, "sum_qd", (race::fused_sum_kernel<T, WS, HS, true, 3>), nblk, dim3(WS * 64), Q,
+               vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sG, sGt);
         LAUNCH(tr, "scan_qd", race::scan_kernel, sgrid, b256, sG, p.nseg, elems, 1);
         LAUNCH(tr, "scan_qd_t", race::scan_kernel, sgrid, b256, sGt, p.nseg, elems, 1);
-        LAUNCH(tr, "dq", (race::fused_dpsi_kernel<T, FW, HT, CAUSAL != 0, false, true>), nblk, bf,
-               Q, K, vd, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, sS, dQ);
-        LAUNCH(tr, "dk", (race::fused_dpsi_kernel<T, FW, HT, CAUSAL != 0, true, false>), nblk, bf,
-               K, Q, vv, vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sGt, dK);
-        LAUNCH(tr, "dv", (race::fused_walk_kernel<T, FW, HT, CAUSAL != 0, true>), nblk, bf, K, Q,
-               vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sG, dV, nullptr);
+        LAUNCH(tr, "dq", (race::fused_dpsi_kernel<T, WD, HD_, CAUSAL != 0, false, true>), nblk,
+               dim3(WD * 64), Q, K, vd, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, sS, dQ);
+        LAUNCH(tr, "dk", (race::fused_dpsi_kernel<T, WD, HD_, CAUSAL != 0, true, false>), nblk,
+               dim3(WD * 64), K, Q, vv, vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sGt, dK);
+        LAUNCH(tr, "dv", (race::fused_walk_kernel<T, WW, HW, CAUSAL != 0, true>), nblk,
+               dim3(WW * 64), K, Q, vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sG, dV, nullptr);
         return;
     }
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,

@@ -1,0 +1,175 @@
+"""The C ABI without a GPU: loading, exported symbols, argument validation,
+workspace sizing, status strings and the host-fitted squash polynomial.
+
+Every call here returns before the library touches the HIP runtime (the
+documented validation order), so no device is needed.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sketch_attention_soft_amd import build as hip_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "race_attn.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_TAU, E_CHUNK, E_WS, E_HIP = range(8)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build()
+    L = ctypes.CDLL(hip_build.LIB)
+    i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    L.race_attn_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(sz)]
+    L.race_attn_forward.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i32, i64, i32, i32,
+                                    i32, vp, vp, vp, sz, vp]
+    L.race_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, i32, i32,
+                                     i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.race_attn_status_string.argtypes = [i32]
+    L.race_attn_status_string.restype = ctypes.c_char_p
+    L.race_attn_squash_coeffs.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_int)]
+    return L
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(race_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert {"race_attn_forward", "race_attn_backward", "race_attn_workspace_bytes",
+            "race_attn_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_lists_the_header(lib):
+    from sketch_attention_soft_amd import binding
+    assert set(binding.EXPORTS) <= set(header_functions())
+
+
+def ws_bytes(lib, B=1, H=1, N=1024, d=64, L=8, P=4, causal=1, chunk=0, dt=BF16, bwd=0):
+    out = ctypes.c_size_t(0)
+    st = lib.race_attn_workspace_bytes(B, H, N, d, L, P, causal, chunk, dt, bwd,
+                                       ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes(lib):
+    st, f = ws_bytes(lib)
+    assert st == OK and f > 0 and f % 256 == 0
+    st, b = ws_bytes(lib, bwd=1)
+    assert st == OK and b >= f
+    # grows with N and with the table count
+    assert ws_bytes(lib, N=1 << 20)[1] > f
+    assert ws_bytes(lib, L=32)[1] > f
+    # fp32 keeps per-row hash buffers, bf16 (fused) does not
+    assert ws_bytes(lib, dt=F32, N=1 << 16)[1] > ws_bytes(lib, dt=BF16, N=1 << 16)[1]
+    # the 75M-token workload fits comfortably in one GPU's HBM
+    st, b75 = ws_bytes(lib, N=75_000_064, L=16, bwd=1)
+    assert st == OK and b75 < 8 << 30
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
+    (dict(d=32), E_UNSUP), (dict(P=3), E_UNSUP), (dict(L=65), E_UNSUP),
+    (dict(L=33, dt=F32), E_UNSUP), (dict(dt=5), E_UNSUP),
+    (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
+])
+def test_workspace_validation(lib, kw, code):
+    assert ws_bytes(lib, **kw)[0] == code
+
+
+def test_workspace_null(lib):
+    assert lib.race_attn_workspace_bytes(1, 1, 16, 64, 8, 4, 1, 0, BF16, 0, None) == E_NULL
+
+
+FAKE = 0x1000  # never dereferenced: validation fails first
+
+
+def fwd(lib, ptrs=(FAKE,) * 7, L=8, P=4, tau=1.0, causal=1, B=1, H=1, N=64, d=64, dt=BF16,
+        chunk=0, ws_bytes=1 << 30, ws=FAKE * 16):
+    q, k, v, W, o, den, _ = ptrs
+    return lib.race_attn_forward(q, k, v, W, L, P, tau, causal, B, H, N, d, dt, chunk, o, den, ws,
+                                 ws_bytes, None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, ptrs=(None,) + (FAKE,) * 6) == E_NULL
+    assert fwd(lib, ws=None) == E_NULL
+    assert fwd(lib, N=0) == E_SHAPE
+    assert fwd(lib, d=128) == E_UNSUP
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert fwd(lib, tau=bad) == E_TAU
+    assert fwd(lib, chunk=24) == E_CHUNK
+    assert fwd(lib, ws_bytes=16) == E_WS
+    assert fwd(lib, ws=FAKE * 16 + 8) == E_WS  # not 256-byte aligned
+
+
+def test_backward_validation(lib):
+    args = [FAKE] * 7 + [8, 4, 1.0, 1, 1, 1, 64, 64, BF16, 0] + [FAKE] * 3 + [FAKE * 16, 16,
+                                                                            None]
+    assert lib.race_attn_backward(*args) == E_WS
+    a = list(args)
+    a[6] = None  # dO
+    assert lib.race_attn_backward(*a) == E_NULL
+    a = list(args)
+    a[9] = 0.0  # tau
+    a[-2] = 1 << 30
+    assert lib.race_attn_backward(*a) == E_TAU
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(8):
+        s = lib.race_attn_status_string(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.race_attn_status_string(99).decode() == "unknown status"
+
+
+def squash_numpy(coef, deg, v, tau):
+    """fp32 evaluation of the kernels' t = tanh(tanh(v)/tau) from the coefficients."""
+    v = v.astype(np.float32)
+    e = np.exp(np.float32(-2.0) * np.abs(v)).astype(np.float32)
+    if deg < 0:
+        z = (1 - e) / (1 + e)
+        h = np.tanh(z / np.float32(tau))
+    else:
+        y = (np.float32(2) * e - np.float32(1)).astype(np.float32)
+        h = np.full_like(y, np.float32(coef[deg]))
+        for k in range(deg - 1, -1, -1):
+            h = (h * y + np.float32(coef[k])).astype(np.float32)
+    return np.copysign(h, v)
+
+
+@pytest.mark.parametrize("dt,tol", [(BF16, 1e-5), (F32, 2.5e-7)])
+@pytest.mark.parametrize("tau", [0.1, 0.25, 0.5, 1.0, 2.0, 8.0])
+def test_squash_polynomial_against_numpy_tanh(lib, dt, tol, tau):
+    coef = (ctypes.c_float * 17)()
+    deg = ctypes.c_int(0)
+    assert lib.race_attn_squash_coeffs(tau, dt, coef, ctypes.byref(deg)) == OK
+    v = np.concatenate([np.linspace(-12, 12, 200001), [0.0, 1e-30, -1e-30, 1e-6, 40.0]])
+    ref = np.tanh(np.tanh(v) / tau)
+    got = squash_numpy(np.array(coef[:]), deg.value, v, tau)
+    # the kernels' exp is within an ulp of numpy's; allow a few ulps of slack
+    assert np.abs(got - ref).max() <= tol + 4e-7, (deg.value, np.abs(got - ref).max())
+    if tau >= 0.5:
+        assert deg.value > 0  # the polynomial, not the fallback, at the workloads' tau
+
+
+def test_squash_rejects_bad_tau(lib):
+    coef = (ctypes.c_float * 17)()
+    deg = ctypes.c_int(0)
+    assert lib.race_attn_squash_coeffs(0.0, BF16, coef, ctypes.byref(deg)) == E_TAU
+    assert lib.race_attn_squash_coeffs(1.0, BF16, None, ctypes.byref(deg)) == E_NULL
