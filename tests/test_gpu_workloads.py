@@ -1,0 +1,167 @@
+"""Parity at the five workloads' full sizes, in the configuration bench.py times.
+
+* non-causal forward, N = 1024, fp32: every output against the live oracle;
+* causal fwd+bwd, 8 heads x 65536, fp32, segments of 256 tokens: every
+  output of every head against the live oracle;
+* causal fwd+bwd, 4 x 16 heads x 16384, bf16, L = 64: every output of a
+  sample of heads against the live oracle, gradient identities on all heads;
+* causal fwd+bwd, N = 4,194,304, bf16: sampled rows against oracle values
+  written by tests/golden/make_workload_golden.py (inputs checked by digest),
+  gradient identities over the whole sequence;
+* causal fwd+bwd, N = 75,000,000, bf16, L = 16: the causal prefix rows
+  (o, den, dq of a query depend only on earlier tokens) against the live
+  oracle on that prefix; dk, dv through identities over all 75M rows.
+
+Bar: relative Frobenius error 1e-4 (fp32) / 2e-2 (bf16), per head or over
+the sampled rows.
+"""
+import hashlib
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sketch_attention_soft_amd import binding
+from sketch_attention_soft_amd import inputs as I
+from tests.gpu_util import TOL, device_inputs, head_relf, host_inputs, to_host64
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _relf(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _run(w, dx):
+    print(f"[workload] {w.name}: B={w.B} H={w.H} N={w.N} L={w.L} {w.dtype}", flush=True)
+    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], w.tau, w.causal, w.chunk)
+    res = {"o": o, "den": den}
+    if w.backward:
+        dq, dk, dv = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"],
+                                      w.tau, w.causal, w.chunk)
+        res.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return res
+
+
+def _identities(res, dx, tol, rows=1 << 22):
+    """Gradient identities that hold at any size (per head, fp64 on the GPU,
+    in slices of rows): sum_j dv_j = sum_i dO_i and <dq_i, q_i> = <dk_j, k_j> = 0."""
+    N = dx["q"].shape[-2]
+    sdv = sg = 0.0
+    cos = {"dq": 0.0, "dk": 0.0}
+    for r0 in range(0, N, rows):
+        sl = slice(r0, min(N, r0 + rows))
+        sdv = sdv + res["dv"][..., sl, :].double().sum(-2)
+        sg = sg + dx["do"][..., sl, :].double().sum(-2)
+        for gr, x in (("dq", "q"), ("dk", "k")):
+            a, b = res[gr][..., sl, :].double(), dx[x][..., sl, :].double()
+            c = (a * b).sum(-1).abs() / (a.norm(dim=-1) * b.norm(dim=-1) + 1e-30)
+            cos[gr] += c.sum().item()
+    err = ((sdv - sg).norm(dim=-1) / sg.norm(dim=-1)).max().item()
+    print(f"  sum dv vs sum dO: {err:.2e}")
+    assert err <= tol
+    cnt = dx["q"].numel() // dx["q"].shape[-1]
+    for gr in cos:
+        c = cos[gr] / cnt
+        print(f"  mean |<{gr}, x>| / norms: {c:.2e}")
+        assert c <= tol
+
+
+def test_noncausal_fwd_n1k_f32():
+    w = I.WORKLOADS["noncausal_fwd_n1k_f32"]
+    x = I.workload_inputs(w)
+    res = _run(w, device_inputs(x, w.dtype))
+    hx = host_inputs(x, w.dtype)
+    ro, rden = oracle.forward(hx["q"], hx["k"], hx["v"], hx["W"], w.tau, w.causal)
+    e = head_relf(to_host64(res["o"]), ro)
+    print(f"  rel_o={e:.2e}")
+    assert e <= TOL[w.dtype]
+    np.testing.assert_allclose(to_host64(res["den"]), rden, rtol=TOL[w.dtype])
+
+
+@pytest.mark.timeout(600)
+def test_causal_h8_n64k_f32():
+    w = I.WORKLOADS["causal_h8_n64k_f32"]
+    x = I.workload_inputs(w)
+    dx = device_inputs(x, w.dtype)
+    res = _run(w, dx)
+    hx = host_inputs(x, w.dtype)
+    ref = dict(zip(("o", "den", "dq", "dk", "dv"),
+                   oracle.forward_backward(hx["q"], hx["k"], hx["v"], hx["do"], hx["W"], w.tau,
+                                           w.causal)))
+    for n in ("o", "dq", "dk", "dv"):
+        e = head_relf(to_host64(res[n]), ref[n])
+        print(f"  rel_{n}={e:.2e}")
+        assert e <= TOL[w.dtype], (n, e)
+    _identities(res, dx, 1e-4)
+
+
+@pytest.mark.timeout(600)
+def test_causal_b4h16_n16k_bf16():
+    w = I.WORKLOADS["causal_b4h16_n16k_bf16"]
+    x = I.workload_inputs(w)
+    dx = device_inputs(x, w.dtype)
+    res = _run(w, dx)
+    hx = host_inputs(x, w.dtype)
+    heads = [(0, 0), (1, 5), (2, 10), (3, 15)]
+    for b, h in heads:
+        ref = dict(zip(("o", "den", "dq", "dk", "dv"),
+                       oracle.forward_backward(hx["q"][b, h], hx["k"][b, h], hx["v"][b, h],
+                                               hx["do"][b, h], hx["W"], w.tau, w.causal)))
+        for n in ("o", "dq", "dk", "dv"):
+            e = _relf(to_host64(res[n][b, h]), ref[n])
+            print(f"  head ({b},{h}) rel_{n}={e:.2e}")
+            assert e <= TOL[w.dtype], (b, h, n, e)
+    _identities(res, dx, 2e-2)
+
+
+@pytest.mark.timeout(600)
+def test_causal_n4m_bf16():
+    w = I.WORKLOADS["causal_n4m_bf16"]
+    path = os.path.join(GOLDEN, f"{w.name}_rows.npz")
+    gold = np.load(path)
+    x = I.workload_inputs(w)
+    h = hashlib.sha256()
+    for k in ("W", "q", "k", "v", "do"):
+        h.update(np.ascontiguousarray(x[k]).tobytes())
+    assert h.hexdigest() == str(gold["digest"]), "input generator drifted from the stored values"
+    dx = device_inputs(x, w.dtype)
+    del x
+    res = _run(w, dx)
+    rows = torch.from_numpy(gold["rows"]).cuda()
+    for n in ("o", "dq", "dk", "dv"):
+        got = res[n][0, 0].index_select(0, rows).double().cpu().numpy()
+        e = _relf(got, gold[n])
+        print(f"  sampled rel_{n}={e:.2e}")
+        assert e <= TOL[w.dtype], (n, e)
+    got = res["den"][0, 0].index_select(0, rows).double().cpu().numpy()
+    assert _relf(got, gold["den"]) <= TOL[w.dtype]
+    _identities(res, dx, 2e-2)
+
+
+@pytest.mark.timeout(900)
+def test_causal_n75m_bf16():
+    w = I.WORKLOADS["causal_n75m_bf16"]
+    x = I.workload_inputs(w)
+    dx = device_inputs(x, w.dtype)
+    del x
+    res = _run(w, dx)
+    n_p = 16384
+    xp = I.workload_inputs(w, n_rows=n_p)
+    hp = host_inputs(xp, w.dtype)
+    ref = dict(zip(("o", "den", "dq", "dk", "dv"),
+                   oracle.forward_backward(hp["q"], hp["k"], hp["v"], hp["do"], hp["W"], w.tau,
+                                           w.causal)))
+    for n in ("o", "dq"):
+        got = res[n][0, 0, :n_p].double().cpu().numpy()
+        e = _relf(got, ref[n][0, 0])
+        print(f"  prefix rel_{n}={e:.2e}")
+        assert e <= TOL[w.dtype], (n, e)
+    assert _relf(res["den"][0, 0, :n_p].double().cpu().numpy(), ref["den"][0, 0]) <= 2e-2
+    # the last key sees only the last query: dv_{N-1} = (kappa/m) dO_{N-1}, finite
+    assert torch.isfinite(res["dv"]).all() and torch.isfinite(res["dk"]).all()
+    _identities(res, dx, 2e-2)
