@@ -9,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "race_attn.hip")
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("race_common.h", "race_fwd.h", "race_bwd.h")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("race_common.h", "race_fwd.h", "race_bwd.h",
+                                                   "race_squash.h", "race_walk.h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librace_attn.so")
 

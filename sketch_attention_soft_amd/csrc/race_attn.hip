@@ -10,20 +10,8 @@
 
 #include "race_bwd.h"
 #include "race_common.h"
-#include "race_fused.h"
 #include "race_fwd.h"
-
-// Hash tiles (4 tables each) per wave of the fused kernels: 1 gives 2x as
-// many waves with half the registers each.
-#ifndef RACE_HT_SUM
-#define RACE_HT_SUM 1
-#endif
-#ifndef RACE_HT_WALK
-#define RACE_HT_WALK 1
-#endif
-#ifndef RACE_HT_DPSI
-#define RACE_HT_DPSI 1
-#endif
+#include "race_walk.h"
 
 namespace {
 
@@ -120,7 +108,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->b_tk = p->b_tq + p->tb_bytes;
     p->b_s = p->b_tk + p->tb_bytes;
     p->b_gt = p->b_s + p->st_bytes;
-    p->b_g = p->b_gt + p->st_bytes;
+    // the bf16 kernels read the gradient state transposed from its FxC copy
+    p->b_g = p->b_gt + (p->fused ? 0 : p->st_bytes);
     p->b_wt = p->b_g + p->st_bytes;
     p->b_total = p->b_wt + p->wt_bytes;
     return RACE_OK;
@@ -207,6 +196,53 @@ int hash_grid(int64_t rows)
     return (int)(blocks < 16384 ? blocks : 16384);
 }
 
+// walk kernel with the squash polynomial or its direct evaluation
+template <int NW, bool CAUSAL, bool BWD, typename T>
+void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *R,
+                 const T *Wr, const race::ValSrc<T> &vs, const float *W, const Plan &p,
+                 const float *st, T *out, float *den)
+{
+    if constexpr (sizeof(T) == 2) {
+        if (sq.deg >= 0)
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, true>), grid, dim3(NW * 64), R, Wr,
+                   vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, out, den);
+        else
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, false>), grid, dim3(NW * 64), R,
+                   Wr, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, out, den);
+    }
+}
+
+// segment-sum kernel with the squash polynomial or its direct evaluation
+template <int NW, bool DVAL, int LAYOUT, typename T>
+void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *X,
+                const race::ValSrc<T> &vs, const float *W, const Plan &p, float *st_f, float *st_c)
+{
+    if constexpr (sizeof(T) == 2) {
+        if (sq.deg >= 0)
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, LAYOUT, true>), grid, dim3(NW * 64), X, vs,
+                   W, p.L, sq, p.N, (int)p.seg, p.nseg, st_f, st_c);
+        else
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, LAYOUT, false>), grid, dim3(NW * 64), X, vs,
+                   W, p.L, sq, p.N, (int)p.seg, p.nseg, st_f, st_c);
+    }
+}
+
+// gradient kernel with the squash polynomial or its direct evaluation
+template <int NW, bool CAUSAL, bool REVERSE, typename T>
+void launch_grad(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *Xr,
+                 const T *Xw, const race::ValSrc<T> &vr, const race::ValSrc<T> &vw, const float *W,
+                 const Plan &p, const float *st, T *dX)
+{
+    if constexpr (sizeof(T) == 2) {
+        if (sq.deg >= 0)
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true>), grid, dim3(NW * 64), Xr,
+                   Xw, vr, vw, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, dX);
+        else
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false>), grid, dim3(NW * 64), Xr,
+                   Xw, vr, vw, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, dX);
+    }
+}
+
 template <typename T, int NW>
 void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const float *W, float tau,
                     int causal, T *O, float *den, char *ws, const Tracer &tr)
@@ -217,23 +253,19 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     const float inv_tau = 1.0f / tau;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
     if constexpr (sizeof(T) == 2 && NW <= 4) {
-        // fused path: HT hash tiles (4 tables each) per wave, 2*NW/HT waves
-        constexpr int HS = NW >= RACE_HT_SUM ? RACE_HT_SUM : 1, WS = 2 * NW / HS;
-        constexpr int HW = NW >= RACE_HT_WALK ? RACE_HT_WALK : 1, WW = 2 * NW / HW;
+        // bf16 path: 2 NW waves of 4 tables each (16 hyperplanes, 64 features)
+        constexpr int WS = 2 * NW, WW = 2 * NW;
         const race::Squash sq = fit_squash(tau, RACE_BF16);
         const dim3 nblk((unsigned)(p.BH * p.nseg));
         const int64_t elems = (int64_t)p.F * race::NCOL;
         const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
         const race::ValSrc<T> vv{V, nullptr, nullptr};
-        LAUNCH(tr, "sum_kv", (race::fused_sum_kernel<T, WS, HS, false, 1>), nblk, dim3(WS * 64), K,
-               vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, nullptr);
+        launch_sum<WS, false, 1>(tr, "sum_kv", nblk, sq, K, vv, W, p, st, nullptr);
         LAUNCH(tr, "scan_kv", race::scan_kernel, sgrid, b256, st, p.nseg, elems, 0);
         if (causal)
-            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, WW, HW, true, false>), nblk,
-                   dim3(WW * 64), Q, K, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
+            launch_walk<WW, true, false>(tr, "fwd_o", nblk, sq, Q, K, vv, W, p, st, O, den);
         else
-            LAUNCH(tr, "fwd_o", (race::fused_walk_kernel<T, WW, HW, false, false>), nblk,
-                   dim3(WW * 64), Q, K, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, O, den);
+            launch_walk<WW, false, false>(tr, "fwd_o", nblk, sq, Q, K, vv, W, p, st, O, den);
         return;
     }
     LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
@@ -260,18 +292,16 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
 {
     float *tq = reinterpret_cast<float *>(ws + p.b_tq);
     float *tk = reinterpret_cast<float *>(ws + p.b_tk);
-    float *sS = reinterpret_cast<float *>(ws + p.b_s);    // key state, CxF layout
-    float *sGt = reinterpret_cast<float *>(ws + p.b_gt);  // gradient state, CxF layout
+    float *sS = reinterpret_cast<float *>(ws + p.b_s);    // key state (CxF; FxC on the bf16 path)
+    float *sGt = reinterpret_cast<float *>(ws + p.b_gt);  // gradient state, CxF layout (fp32 / L > 32)
     float *sG = reinterpret_cast<float *>(ws + p.b_g);    // gradient state, FxC layout
     char *wt = ws + p.b_wt;
     const float inv_tau = 1.0f / tau;
     const int lp32 = (p.LP + 31) / 32 * 32;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
     if constexpr (sizeof(T) == 2 && NW <= 4) {
-        // fused path: HT hash tiles (4 tables each) per wave, 2*NW/HT waves
-        constexpr int HS = NW >= RACE_HT_SUM ? RACE_HT_SUM : 1, WS = 2 * NW / HS;
-        constexpr int HW = NW >= RACE_HT_WALK ? RACE_HT_WALK : 1, WW = 2 * NW / HW;
-        constexpr int HD_ = NW >= RACE_HT_DPSI ? RACE_HT_DPSI : 1, WD = 2 * NW / HD_;
+        // bf16 path: 2 NW waves of 4 tables each (16 hyperplanes, 64 features)
+        constexpr int WS = 2 * NW, WW = 2 * NW, WD = 2 * NW;
         const race::Squash sq = fit_squash(tau, RACE_BF16);
         const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
         const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
@@ -279,20 +309,14 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
         const int64_t elems = (int64_t)p.F * race::NCOL;
         const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
         // key state S (CxF, for dQ): prefix over segments
-        LAUNCH(tr, "sum_kv_t", (race::fused_sum_kernel<T, WS, HS, false, 2>), nblk, dim3(WS * 64),
-               K, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, nullptr, sS);
+        launch_sum<WS, false, 1>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, sS, nullptr);
         LAUNCH(tr, "scan_kv_t", race::scan_kernel, sgrid, b256, sS, p.nseg, elems, 0);
         // gradient state G (FxC for dV and CxF for dK): suffix over segments
-        LAUNCH(tr, "sum_qd", (race::fused_sum_kernel<T, WS, HS, true, 3>), nblk, dim3(WS * 64), Q,
-               vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sG, sGt);
+        launch_sum<WS, true, 1>(tr, "sum_qd", nblk, sq, Q, vd, W, p, sG, nullptr);
         LAUNCH(tr, "scan_qd", race::scan_kernel, sgrid, b256, sG, p.nseg, elems, 1);
-        LAUNCH(tr, "scan_qd_t", race::scan_kernel, sgrid, b256, sGt, p.nseg, elems, 1);
-        LAUNCH(tr, "dq", (race::fused_dpsi_kernel<T, WD, HD_, CAUSAL != 0, false, true>), nblk,
-               dim3(WD * 64), Q, K, vd, vv, W, p.L, sq, p.N, (int)p.seg, p.nseg, sS, dQ);
-        LAUNCH(tr, "dk", (race::fused_dpsi_kernel<T, WD, HD_, CAUSAL != 0, true, false>), nblk,
-               dim3(WD * 64), K, Q, vv, vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sGt, dK);
-        LAUNCH(tr, "dv", (race::fused_walk_kernel<T, WW, HW, CAUSAL != 0, true>), nblk,
-               dim3(WW * 64), K, Q, vd, W, p.L, sq, p.N, (int)p.seg, p.nseg, sG, dV, nullptr);
+        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, sq, Q, K, vd, vv, W, p, sS, dQ);
+        launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, sq, K, Q, vv, vd, W, p, sG, dK);
+        launch_walk<WW, CAUSAL != 0, true>(tr, "dv", nblk, sq, K, Q, vd, W, p, sG, dV, nullptr);
         return;
     }
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,

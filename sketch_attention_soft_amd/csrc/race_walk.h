@@ -1,0 +1,1037 @@
+// race_walk.h -- block-staged chunk kernels of RACE attention for bf16 rows
+// (gfx950), built so that almost all arithmetic per chunk is MFMA work.
+//
+// Pages: "RACE Attention: A Strictly Linear-Time Attention for Long-Sequence
+// Training", gist.science/zh/paper/2510.04008, technical summary §2.2 (soft
+// hashing, bucket sums, ratio readout) and §2.3 (causal streaming sums); the
+// es page §2 (angular kernel on normalised vectors).
+//
+// Staging.  Each chunk of 32 tokens is loaded once per workgroup: every
+// thread fetches one 16-byte piece of a row (the next chunk's, while the
+// current one is computed) and writes it to LDS, where the eight threads of a
+// row also form its squared norm (dot2 + DPP).  Value rows go to LDS column
+// by column, so that any wave reads them as MFMA operands over tokens.
+//
+// Per wave (4 tables = 16 hyperplanes = 64 features, all in registers):
+//   U^T = W x^T (MFMA, W = W_hi + W_lo) -> lane (table g, token c16) holds
+//   t_0..3 of its table -> the 16 Walsh features of that table are two
+//   token-major K-blocks (slots (g, i) <-> S = 8k + i);
+//   feature-major fragments (K = tokens) come from the token-major ones by a
+//   0/1 selection MFMA, which moves every bf16 value exactly;
+//   intra-chunk scores are formed per wave over its own features and
+//   multiplied into the wave's partial output, so the only cross-wave sum is
+//   the one of the partial outputs.
+// FxC state tile (s, ct): lane (rows 4g + r, column 16 ct + c16) <-> features
+// (table 4w + g, S = 4s + r), stored in global memory as [wave][s][ct][lane][4].
+#pragma once
+#include "race_common.h"
+#include "race_fwd.h"
+#include "race_squash.h"
+
+namespace race {
+
+constexpr int WCT = 32;      // tokens per chunk
+constexpr int XRS = HD + 8;  // staged row stride (bf16 elements)
+constexpr int YCS = WCT + 8; // staged value column stride (tokens)
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    const bf16x2 v = {(bf16)a, (bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bf16x8 pk8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    const u32x4 v = {a, b, c, d};
+    return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x4 pk4(uint32_t a, uint32_t b)
+{
+    const u32x2 v = {a, b};
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
+{
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4 lo4(bf16x8 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+__device__ __forceinline__ bf16x4 hi4(bf16x8 v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
+__device__ __forceinline__ bf16x4 acc2bf4(const floatx4 &a)
+{
+    return pk4(pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3]));
+}
+
+__device__ __forceinline__ void mma32(floatx4 &acc, bf16x8 a, bf16x8 b)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// K = 16 products as 16x16x32 MFMAs with a zero upper half: accumulation
+// chains that mixed v_mfma_f32_16x16x16_bf16 with the 16x16x32 form gave
+// wrong sums on gfx950 in these kernels, so only the 16x16x32 form is used.
+__device__ __forceinline__ void mma16(floatx4 &acc, bf16x4 a, bf16x4 b)
+{
+    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(a, z), cat8(b, z), acc, 0, 0, 0);
+}
+
+// Sums over aligned groups of 8 / 16 lanes (DPP within a row).
+__device__ __forceinline__ float dpp_add(float x, int ctrl_sel)
+{
+    int y;
+    switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false); break;
+    case 1: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false); break;
+    case 2: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false); break;
+    default: y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false); break;
+    }
+    return x + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float sum8(float x)
+{
+    x = dpp_add(x, 0);  // quad_perm [1,0,3,2]
+    x = dpp_add(x, 1);  // quad_perm [2,3,0,1]
+    return dpp_add(x, 2);  // row_half_mirror: the other quad of the 8
+}
+__device__ __forceinline__ float sum16(float x) { return dpp_add(sum8(x), 3); }  // row_ror:8
+
+// ---------------------------------------------------------------------------
+// Staging of raw rows: NS row sets (0: readers, 1: writers) of one chunk,
+// item e -> set e >> 8, token (e >> 3) & 31, columns (e & 7) * 8 .. + 8.
+template <int NTHR, int NS> struct XStage {
+    static constexpr int ITEMS = (NS * WCT * 8 + NTHR - 1) / NTHR;
+    bf16x8 v[ITEMS];
+};
+
+template <int NTHR, int NS>
+__device__ __forceinline__ void xstage_load(const bf16 *__restrict__ r0, const bf16 *__restrict__ r1,
+                                            int64_t tok0, int64_t tend, XStage<NTHR, NS> &xs)
+{
+#pragma unroll
+    for (int it = 0; it < XStage<NTHR, NS>::ITEMS; ++it) {
+        const int e = threadIdx.x + it * NTHR;
+        const int64_t tok = tok0 + ((e >> 3) & (WCT - 1));
+        const bf16 *src = (e >> 8) ? r1 : r0;
+        if (e < NS * WCT * 8 && tok < tend) {
+            xs.v[it] = *reinterpret_cast<const bf16x8 *>(src + tok * HD + (e & 7) * 8);
+        } else {
+            xs.v[it] = pk8(0, 0, 0, 0);
+        }
+    }
+}
+
+// rows -> xb[set][token][XRS]; kb[set][token] = -2 log2(e) / max(|x|, 1e-12)
+template <int NTHR, int NS>
+__device__ __forceinline__ void xstage_store(const XStage<NTHR, NS> &xs, bf16 *xb, float *kb)
+{
+#pragma unroll
+    for (int it = 0; it < XStage<NTHR, NS>::ITEMS; ++it) {
+        const int e = threadIdx.x + it * NTHR;
+        if (e < NS * WCT * 8) {  // uniform per wave
+            const int set = e >> 8, j = (e >> 3) & (WCT - 1);
+            *reinterpret_cast<bf16x8 *>(xb + (set * WCT + j) * XRS + (e & 7) * 8) = xs.v[it];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = (float)xs.v[it][i];
+                ss = fmaf(x, x, ss);
+            }
+            ss = sum8(ss);
+            if ((e & 7) == 0)
+                kb[set * WCT + j] = -2.8853900817779268f * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+        }
+    }
+}
+
+// Staging of value rows y_j: [v | 1] (DVAL = false) or [dO/m | -(dO . o)/m]
+// (DVAL = true), into yc[column][YCS] (token pairs per 32-bit word).
+// Item e < 256 -> tokens 2 (e >> 4) and 2 (e >> 4) + 1, columns (e & 15) * 4 .. + 4.
+template <int NTHR, bool DVAL> struct YStage {
+    static constexpr int ITEMS = (WCT * 8 + NTHR - 1) / NTHR;
+    bf16x4 x[ITEMS][2];
+    bf16x4 o[DVAL ? ITEMS : 1][2];
+    float m[DVAL ? ITEMS : 1][2];
+};
+
+template <int NTHR, bool DVAL>
+__device__ __forceinline__ void ystage_load(const ValSrc<bf16> &src, int64_t tok0, int64_t tend,
+                                            YStage<NTHR, DVAL> &ys)
+{
+#pragma unroll
+    for (int it = 0; it < YStage<NTHR, DVAL>::ITEMS; ++it) {
+        const int e = threadIdx.x + it * NTHR;
+        const int c0 = (e & 15) * 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t tok = tok0 + 2 * ((e >> 4) & 15) + h;
+            const bool ok = e < WCT * 8 && tok < tend;
+            ys.x[it][h] = ok ? *reinterpret_cast<const bf16x4 *>(src.V + tok * HD + c0) : pk4(0, 0);
+            if constexpr (DVAL) {
+                ys.o[it][h] = ok ? *reinterpret_cast<const bf16x4 *>(src.O + tok * HD + c0) : pk4(0, 0);
+                ys.m[it][h] = ok ? src.den[tok] : 1.f;
+            }
+        }
+    }
+}
+
+constexpr int YRS = NCOL + 8;  // token-major value row stride
+
+// yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may be null)
+template <int NTHR, bool DVAL>
+__device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int64_t tok0, int64_t tend,
+                                             bf16 *yc, bf16 *yr = nullptr)
+{
+#pragma unroll
+    for (int it = 0; it < YStage<NTHR, DVAL>::ITEMS; ++it) {
+        const int e = threadIdx.x + it * NTHR;
+        if (e < WCT * 8) {  // uniform per wave
+            const int jp = (e >> 4) & 15, c0 = (e & 15) * 4;
+            float y[2][4], extra[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = tok0 + 2 * jp + h < tend;
+                if constexpr (DVAL) {
+                    float dot = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dot += (float)ys.x[it][h][i] * (float)ys.o[it][h][i];
+                    dot = sum16(dot);
+                    const float inv_m = __builtin_amdgcn_rcpf(ys.m[it][h]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i] * inv_m;
+                    extra[h] = ok ? -dot * inv_m : 0.f;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i];
+                    extra[h] = ok ? 1.f : 0.f;
+                }
+            }
+            if (yc) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<uint32_t *>(yc + (c0 + i) * YCS + 2 * jp) = pk_bf16(y[0][i], y[1][i]);
+                if (c0 == 0) *reinterpret_cast<uint32_t *>(yc + HD * YCS + 2 * jp) = pk_bf16(extra[0], extra[1]);
+            }
+            if (yr) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    *reinterpret_cast<bf16x4 *>(yr + (2 * jp + h) * YRS + c0) =
+                        pk4(pk_bf16(y[h][0], y[h][1]), pk_bf16(y[h][2], y[h][3]));
+                    if (c0 == 0) yr[(2 * jp + h) * YRS + HD] = (bf16)extra[h];
+                }
+            }
+        }
+    }
+}
+
+// value columns HD+1 .. NCOL-1 are zero for every chunk
+template <int NTHR> __device__ __forceinline__ void ystage_zero_pad(bf16 *yc)
+{
+    for (int e = threadIdx.x; e < (NCOL - HD - 1) * WCT / 2; e += NTHR) {
+        const int c = HD + 1 + e / (WCT / 2), jp = e % (WCT / 2);
+        *reinterpret_cast<uint32_t *>(yc + c * YCS + 2 * jp) = 0u;
+    }
+}
+template <int NTHR> __device__ __forceinline__ void yrow_zero_pad(bf16 *yr)
+{
+    for (int e = threadIdx.x; e < (NCOL - HD - 1) * WCT; e += NTHR) {
+        const int c = HD + 1 + e % (NCOL - HD - 1), j = e / (NCOL - HD - 1);
+        yr[j * YRS + c] = (bf16)0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// W rows of this wave's 16 hyperplanes as the A operand of U^T = W x^T.
+struct WRows {
+    bf16x8 hi[2], lo[2];
+};
+
+__device__ __forceinline__ void load_wrows(const float *__restrict__ W, int LP, WRows &wr)
+{
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const int hp = w * 16 + c16;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = hp < LP ? W[hp * HD + kb * 32 + g * 8 + i] : 0.f;
+            wr.hi[kb][i] = (bf16)v;
+            wr.lo[kb][i] = (bf16)(v - (float)wr.hi[kb][i]);
+        }
+}
+
+// t = tanh(tanh(u') / tau), u' = u / |x|, kf = -2 log2(e) / |x|
+template <bool POLY>
+__device__ __forceinline__ float squash_k(float u, float kf, const Squash &sq)
+{
+    const float e = __builtin_amdgcn_exp2f(fabsf(u) * kf);  // exp(-2|u'|)
+    float h;
+    if constexpr (POLY) {
+        constexpr int DEG = SqDeg<bf16>::v;
+        const float y = fmaf(2.f, e, -1.f);
+        h = sq.c[DEG];
+#pragma unroll
+        for (int k = DEG - 1; k >= 0; --k) h = fmaf(h, y, sq.c[k]);
+    } else {
+        const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+        const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
+        h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
+    }
+    return copysignf(h, u);
+}
+
+// t of tables 4w + g (lane (g, c16)) for token 16 tt + c16 of staged set xb
+template <bool POLY>
+__device__ __forceinline__ floatx4 hash_staged(const bf16 *xb, const float *kb, int tt, const WRows &wr,
+                                               const Squash &sq)
+{
+    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+    const int row = tt * 16 + c16;
+    const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + g * 8);
+    const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + 32 + g * 8);
+    floatx4 u = {0.f, 0.f, 0.f, 0.f};
+    mma32(u, wr.hi[0], x0);
+    mma32(u, wr.lo[0], x0);
+    mma32(u, wr.hi[1], x1);
+    mma32(u, wr.lo[1], x1);
+    const float kf = kb[row];
+    floatx4 t;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) t[p] = squash_k<POLY>(u[p], kf, sq);
+    return t;
+}
+
+// token-major Walsh features of one table: lo = S 0..7, hi = S 8..15
+// (q4 = 1/4, or 0 for padding tables)
+__device__ __forceinline__ void walsh_tm(const floatx4 &t, float q4, bf16x8 &lo, bf16x8 &hi)
+{
+    const float a1 = q4 * t[0], a2 = q4 * t[1], a3 = a1 * t[1], b3 = t[2] * t[3];
+    lo = pk8(pk_bf16(q4, a1), pk_bf16(a2, a3), pk_bf16(q4 * t[2], a1 * t[2]),
+             pk_bf16(a2 * t[2], a3 * t[2]));
+    hi = pk8(pk_bf16(q4 * t[3], a1 * t[3]), pk_bf16(a2 * t[3], a3 * t[3]), pk_bf16(q4 * b3, a1 * b3),
+             pk_bf16(a2 * b3, a3 * b3));
+}
+
+// 0/1 selection operand: column rho of FxC row-tile s takes token-major slot
+// (g = rho / 4, i = 4 (s & 1) + rho % 4) of K-block s / 2.
+__device__ __forceinline__ bf16x8 selection(int par)
+{
+    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+    bf16x8 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)((g == (c16 >> 2) && i == 4 * par + (c16 & 3)) ? 1.f : 0.f);
+    return f;
+}
+
+// feature-major fragments of the 4 FxC row tiles over the chunk's 32 tokens
+// (K-slots (g, r) <-> token 4g + r, (g, 4 + r) <-> token 16 + 4g + r)
+__device__ __forceinline__ void feat_major(const bf16x8 (&ptm)[2][2], const bf16x8 (&sel)[2],
+                                           bf16x8 (&pfm)[4])
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        bf16x4 half[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            floatx4 d = {0.f, 0.f, 0.f, 0.f};
+            mma32(d, ptm[tt][s >> 1], sel[s & 1]);
+            half[tt] = acc2bf4(d);
+        }
+        pfm[s] = cat8(half[0], half[1]);
+    }
+}
+
+// value-column operand over the chunk's tokens (same K-slot order as feat_major)
+__device__ __forceinline__ bf16x8 ycol_frag(const bf16 *yc, int col)
+{
+    const int g = lane_id() >> 4;
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(yc + col * YCS + 4 * g);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(yc + col * YCS + 16 + 4 * g);
+    return cat8(a, b);
+}
+
+// ---------------------------------------------------------------------------
+// walk_kernel: reader rows read an FxC state built from writer rows, in
+// chunks of 32 tokens, NW waves of 4 tables each.
+//   BWD = false: readers = queries, writers = keys, y = [v | 1]; token order;
+//                intra mask j <= i; output O = n / m and den = m.
+//   BWD = true:  readers = keys, writers = queries, y = [dO/m | dm]; reverse
+//                order; intra mask j >= i; output dV = n[:, :d].
+template <int NW, bool CAUSAL, bool BWD, bool POLY>
+__global__ __launch_bounds__(NW * 64) void walk_kernel(
+    const bf16 *__restrict__ R, const bf16 *__restrict__ Wr, ValSrc<bf16> vsrc,
+    const float *__restrict__ W, int L, Squash sq, int64_t N, int seg, int64_t nseg,
+    const float *__restrict__ st, bf16 *__restrict__ Out, float *__restrict__ den)
+{
+    constexpr int NTHR = NW * 64;
+    constexpr int NS = CAUSAL ? 2 : 1;
+    constexpr int RSLOTS = 2 * 4 * 64;  // (tile, column tile < 4, lane) partial-output slots
+    constexpr int RIT = (RSLOTS + NTHR - 1) / NTHR;
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[NS * WCT * XRS];
+    __shared__ __attribute__((aligned(16))) float kbuf[NS * WCT];
+    __shared__ __attribute__((aligned(16))) bf16 ycol[CAUSAL ? NCOL * YCS : 8];
+    __shared__ __attribute__((aligned(16))) float red[NW * 2 * NT * 64 * 4];
+    __shared__ __attribute__((aligned(16))) float mbuf[WCT];
+
+    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const bf16 *Rh = R + bh * N * HD;
+    const bf16 *Wh = Wr + bh * N * HD;
+    ValSrc<bf16> vh = vsrc;
+    vh.V += bh * N * HD;
+    if (BWD) {
+        vh.O += bh * N * HD;
+        vh.den += bh * N;
+    }
+    bf16 *Oh = Out + bh * N * HD;
+    float *denh = BWD ? nullptr : den + bh * N;
+
+    WRows wr;
+    load_wrows(W, L * NP, wr);
+    bf16x8 sel[2] = {selection(0), selection(1)};
+    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    floatx4 acc[4][NT];
+    {
+        const float *src = st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+                acc[s][ct] = *reinterpret_cast<const floatx4 *>(src + st_idx(w, s, ct, lane, 4));
+    }
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
+    auto chunk0 = [&](int64_t ci) { return t_begin + (BWD ? nch - 1 - ci : ci) * WCT; };
+
+    XStage<NTHR, NS> xs;
+    YStage<NTHR, BWD> ys;
+    if (CAUSAL) {
+        ystage_zero_pad<NTHR>(ycol);
+        ystage_load<NTHR, BWD>(vh, chunk0(0), t_end, ys);
+    }
+    xstage_load<NTHR, NS>(Rh, Wh, chunk0(0), t_end, xs);
+    xstage_store<NTHR, NS>(xs, xbuf, kbuf);
+    if (nch > 1) xstage_load<NTHR, NS>(Rh, Wh, chunk0(1), t_end, xs);
+    lds_barrier();
+
+    float nsum[RIT][4];
+    int64_t prev0 = 0;
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int64_t tok0 = chunk0(ci);
+        if (CAUSAL) {
+            ystage_store<NTHR, BWD>(ys, tok0, t_end, ycol);
+            if (ci + 1 < nch) ystage_load<NTHR, BWD>(vh, chunk0(ci + 1), t_end, ys);
+        }
+        // hash and Walsh features of this chunk's readers and writers
+        bf16x8 pr[2][2], pfm[4];
+        bf16x4 kA4;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
+        bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const floatx4 t = hash_staged<POLY>(xbuf, kbuf, tt, wr, sq);
+            walsh_tm(t, q4, pr[tt][0], pr[tt][1]);
+        }
+        if (CAUSAL) {
+            bf16x8 pw[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const floatx4 t = hash_staged<POLY>(xbuf + WCT * XRS, kbuf + WCT, tt, wr, sq);
+                walsh_tm(t, q4, pw[tt][0], pw[tt][1]);
+            }
+            // scores^T tiles D[j][i] = psi_w(j) . psi_r(i) over this wave's tables
+            constexpr int TJ[3] = {0, BWD ? 1 : 0, 1}, TI[3] = {0, BWD ? 0 : 1, 1};
+            floatx4 sc[3];
+#pragma unroll
+            for (int pi = 0; pi < 3; ++pi) {
+                sc[pi] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < 2; ++k) mma32(sc[pi], pw[TJ[pi]][k], pr[TI[pi]][k]);
+            }
+            // diagonal tiles: keep j <= i (fwd) or j >= i (bwd); lane (j = 4g + r, i = c16)
+#pragma unroll
+            for (int pi = 0; pi < 3; pi += 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = BWD ? (4 * g + r >= c16) : (4 * g + r <= c16);
+                    sc[pi][r] = keep ? sc[pi][r] : 0.f;
+                }
+            if (BWD) {
+                kA8 = cat8(acc2bf4(sc[0]), acc2bf4(sc[1]));  // reader tile 0: writer tiles 0, 1
+                kA4 = acc2bf4(sc[2]);                        // reader tile 1: writer tile 1
+            } else {
+                kA4 = acc2bf4(sc[0]);                        // reader tile 0: writer tile 0
+                kA8 = cat8(acc2bf4(sc[1]), acc2bf4(sc[2]));  // reader tile 1: writer tiles 0, 1
+            }
+            feat_major(pw, sel, pfm);
+        }
+        lds_barrier();  // #1: value columns of this chunk staged, m of the previous one reduced
+        if (!BWD && ci > 0) {
+#pragma unroll
+            for (int it = 0; it < RIT; ++it) {
+                const int sl = threadIdx.x + it * NTHR;
+                if (sl < RSLOTS) {
+                    const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
+                    const floatx4 m = *reinterpret_cast<const floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
+                        if (tok < t_end)
+                            Oh[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
+                    }
+                }
+            }
+        }
+        if (ci + 1 < nch) {  // the next chunk's rows (xbuf is not read again in this chunk)
+            xstage_store<NTHR, NS>(xs, xbuf, kbuf);
+            if (ci + 2 < nch) xstage_load<NTHR, NS>(Rh, Wh, chunk0(ci + 2), t_end, xs);
+        }
+        floatx4 oacc[2][NT];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) oacc[tt][ct] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            // inter-chunk readout with the state before this chunk
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const bf16x8 sf = cat8(acc2bf4(acc[2 * k][ct]), acc2bf4(acc[2 * k + 1][ct]));
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], pr[tt][k], sf);
+            }
+            if (CAUSAL) {
+                const bf16x8 yb = ycol_frag(ycol, ct * 16 + c16);
+                if (BWD) {
+                    mma32(oacc[0][ct], kA8, yb);
+                    mma16(oacc[1][ct], kA4, hi4(yb));
+                } else {
+                    mma16(oacc[0][ct], kA4, lo4(yb));
+                    mma32(oacc[1][ct], kA8, yb);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+                *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * NT + ct) * 64 + lane) * 4) = oacc[tt][ct];
+        lds_barrier();  // #2: partial outputs of every wave in LDS, next rows staged
+#pragma unroll
+        for (int it = 0; it < RIT; ++it) {
+            const int sl = threadIdx.x + it * NTHR;
+            if (sl < RSLOTS) {
+                const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
+                floatx4 n = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww)
+                    n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * NT + ct) * 64 + ln) * 4);
+                if (BWD) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
+                        if (tok < t_end) Oh[tok * HD + ct * 16 + (ln & 15)] = (bf16)n[r];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) nsum[it][r] = n[r];
+                    if (ct == 0 && (ln & 15) == 0) {
+                        floatx4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ww = 0; ww < NW; ++ww)
+                            m += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * NT + 4) * 64 + ln) * 4);
+                        *reinterpret_cast<floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4)) = m;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int64_t tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
+                            if (tok < t_end) denh[tok] = m[r];
+                        }
+                    }
+                }
+            }
+        }
+        prev0 = tok0;
+    }
+    if (!BWD) {
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < RIT; ++it) {
+            const int sl = threadIdx.x + it * NTHR;
+            if (sl < RSLOTS) {
+                const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
+                const floatx4 m = *reinterpret_cast<const floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
+                    if (tok < t_end)
+                        Oh[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace race
+
+namespace race {
+
+// ---------------------------------------------------------------------------
+// sum_kernel: S_g = sum_{j in segment g} psi(x_j)^T y_j over the segment's
+// writer rows, NW waves of 4 tables each.
+// LAYOUT bit 0: FxC state into st_f, bit 1: CxF state into st_c (same
+// [wave][s][ct][lane][4] blocks; CxF tile (s, ct): lane (rows = value
+// columns 16 ct + 4g + r, column = feature row rho = c16 of tile s)).
+template <int NW, bool DVAL, int LAYOUT, bool POLY>
+__global__ __launch_bounds__(NW * 64) void sum_kernel(
+    const bf16 *__restrict__ X, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
+    int64_t N, int seg, int64_t nseg, float *__restrict__ st_f, float *__restrict__ st_c)
+{
+    constexpr int NTHR = NW * 64;
+    constexpr bool FXC = LAYOUT & 1, CXF = LAYOUT & 2;
+    // double-buffered: chunk c is hashed and summed while chunk c + 1 is staged
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][WCT * XRS];
+    __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
+    __shared__ __attribute__((aligned(16))) bf16 ycol[2][NCOL * YCS];
+
+    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4;
+    const bf16 *Xh = X + bh * N * HD;
+    ValSrc<bf16> vh = vsrc;
+    vh.V += bh * N * HD;
+    if (DVAL) {
+        vh.O += bh * N * HD;
+        vh.den += bh * N;
+    }
+    WRows wr;
+    load_wrows(W, L * NP, wr);
+    const bf16x8 sel[2] = {selection(0), selection(1)};
+    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    floatx4 af[FXC ? 4 : 1][NT], ac[CXF ? 4 : 1][NT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            if (FXC) af[s][ct] = {0.f, 0.f, 0.f, 0.f};
+            if (CXF) ac[s][ct] = {0.f, 0.f, 0.f, 0.f};
+        }
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
+    XStage<NTHR, 1> xs;
+    YStage<NTHR, DVAL> ys;
+    ystage_zero_pad<NTHR>(ycol[0]);
+    ystage_zero_pad<NTHR>(ycol[1]);
+    xstage_load<NTHR, 1>(Xh, Xh, t_begin, t_end, xs);
+    ystage_load<NTHR, DVAL>(vh, t_begin, t_end, ys);
+    xstage_store<NTHR, 1>(xs, xbuf[0], kbuf[0]);
+    ystage_store<NTHR, DVAL>(ys, t_begin, t_end, ycol[0]);
+    if (nch > 1) {
+        xstage_load<NTHR, 1>(Xh, Xh, t_begin + WCT, t_end, xs);
+        ystage_load<NTHR, DVAL>(vh, t_begin + WCT, t_end, ys);
+    }
+    lds_barrier();
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int b = ci & 1;
+        bf16x8 ptm[2][2], pfm[4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const floatx4 t = hash_staged<POLY>(xbuf[b], kbuf[b], tt, wr, sq);
+            walsh_tm(t, q4, ptm[tt][0], ptm[tt][1]);
+        }
+        if (ci + 1 < nch) {  // the other buffers were last read before the previous barrier
+            const int64_t nx = t_begin + (ci + 1) * WCT;
+            xstage_store<NTHR, 1>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            ystage_store<NTHR, DVAL>(ys, nx, t_end, ycol[b ^ 1]);
+            if (ci + 2 < nch) {
+                xstage_load<NTHR, 1>(Xh, Xh, nx + WCT, t_end, xs);
+                ystage_load<NTHR, DVAL>(vh, nx + WCT, t_end, ys);
+            }
+        }
+        feat_major(ptm, sel, pfm);
+        // tokens past t_end have psi_0 = 1/4 but zero value rows
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + (lane & 15));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (FXC) mma32(af[s][ct], pfm[s], yb);
+                if (CXF) mma32(ac[s][ct], yb, pfm[s]);
+            }
+        }
+        lds_barrier();
+    }
+    const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 64 * NCOL);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const int64_t o = blk + st_idx(w, s, ct, lane, 4);
+            if (FXC) *reinterpret_cast<floatx4 *>(st_f + o) = af[s][ct];
+            if (CXF) *reinterpret_cast<floatx4 *>(st_c + o) = ac[s][ct];
+        }
+}
+
+}  // namespace race
+
+namespace race {
+
+// W rows split into bf16 hi + lo, staged once per workgroup: wl[2][hp][XRS]
+// (hyperplanes >= L P are zero); selection operands sl[2][64 lanes][8].
+constexpr int WLR = 128;  // hyperplane rows (L <= 32)
+
+template <int NTHR>
+__device__ __forceinline__ void stage_w(const float *__restrict__ W, int LP, int rows, bf16 *wl, bf16 *sl)
+{
+    for (int e = threadIdx.x; e < rows * HD; e += NTHR) {
+        const int hp = e / HD, c = e % HD;
+        const float v = hp < LP ? W[hp * HD + c] : 0.f;
+        const bf16 hi = (bf16)v;
+        wl[hp * XRS + c] = hi;
+        wl[(rows + hp) * XRS + c] = (bf16)(v - (float)hi);
+    }
+    if (threadIdx.x < 64) {
+        *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
+        *reinterpret_cast<bf16x8 *>(sl + (64 + threadIdx.x) * 8) = selection(1);
+    }
+}
+
+// this wave's projection rows from the staged W (A operand of U^T = W x^T)
+__device__ __forceinline__ void wrows_lds(const bf16 *wl, int rows, WRows &wr)
+{
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const int hp = w * 16 + c16;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        wr.hi[kb] = *reinterpret_cast<const bf16x8 *>(wl + hp * XRS + kb * 32 + g * 8);
+        wr.lo[kb] = *reinterpret_cast<const bf16x8 *>(wl + (rows + hp) * XRS + kb * 32 + g * 8);
+    }
+}
+
+// W^T operand of dxh^T = W^T du^T for dimension tile nt: lane (dim 16 nt + c16, hyperplanes 4g + p)
+__device__ __forceinline__ void wcols_lds(const bf16 *wl, int rows, int nt, bf16x4 &hi, bf16x4 &lo)
+{
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int hp = w * 16 + 4 * g + p;
+        hi[p] = wl[hp * XRS + nt * 16 + c16];
+        lo[p] = wl[(rows + hp) * XRS + nt * 16 + c16];
+    }
+}
+
+// t and dt/du' for the readers of the gradient kernel (u' = u / |x|):
+// dt/du' = ((1 - t^2) / tau) (1 - z^2), z = tanh(|u'|), 1 - z^2 = 4e / (1 + e)^2
+template <bool POLY>
+__device__ __forceinline__ void hash_staged_chain(const bf16 *xb, const float *kb, int tt, const WRows &wr,
+                                                  const Squash &sq, floatx4 &t, floatx4 &c)
+{
+    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+    const int row = tt * 16 + c16;
+    const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + g * 8);
+    const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + 32 + g * 8);
+    floatx4 u = {0.f, 0.f, 0.f, 0.f};
+    mma32(u, wr.hi[0], x0);
+    mma32(u, wr.lo[0], x0);
+    mma32(u, wr.hi[1], x1);
+    mma32(u, wr.lo[1], x1);
+    const float kf = kb[row];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float e = __builtin_amdgcn_exp2f(fabsf(u[p]) * kf);
+        float h;
+        if constexpr (POLY) {
+            constexpr int DEG = SqDeg<bf16>::v;
+            const float y = fmaf(2.f, e, -1.f);
+            h = sq.c[DEG];
+#pragma unroll
+            for (int k = DEG - 1; k >= 0; --k) h = fmaf(h, y, sq.c[k]);
+        } else {
+            const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+            const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
+            h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
+        }
+        const float r = __builtin_amdgcn_rcpf(1.f + e);
+        c[p] = (1.f - h * h) * (4.f * sq.inv_tau) * e * r * r;
+        t[p] = copysignf(h, u[p]);
+    }
+}
+
+// CxF register tiles of a state stored as FxC blocks [wave][s][ct][lane][4]:
+// CxF (s, ct) lane (g, c16) reg r = column 16 ct + 4g + r of feature row c16.
+__device__ __forceinline__ void load_state_cxf(const float *__restrict__ src, floatx4 (&acc)[4][NT])
+{
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[s][ct][r] = src[(((w * 4 + s) * NT + ct) * 64 + (c16 >> 2) * 16 + 4 * g + r) * 4 + (c16 & 3)];
+}
+
+// value-row operand of 16 tokens (token-major): columns 32k + 4g + r (slots
+// r < 4) and 32k + 16 + 4g + r (slots 4 + r), k = 0, 1; plus columns 64 + 4g + r
+__device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)[2], bf16x4 &f4)
+{
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        f8[k] = cat8(*reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 4 * g),
+                     *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 16 + 4 * g));
+    f4 = *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 64 + 4 * g);
+}
+
+// ---------------------------------------------------------------------------
+// grad_kernel: gradient of the reader rows, which read a state built from the
+// writer rows, and back through the readers' hash.
+//   dQ (REVERSE = false): readers = queries with values D = [dO/m | dm],
+//       writers = keys with values [v | 1]; token order; mask j <= i.
+//   dK (REVERSE = true): readers = keys with values [v | 1], writers =
+//       queries with values D; reverse order; mask j >= i.
+// Per chunk: dpsi_r(i)[f] = sum_c S[f][c] y_r(i)[c] + sum_j E[i][j] psi_w(j)[f]
+// with E[i][j] = y_r(i) . y_w(j) (masked), computed transposed (rows f) so
+// that a lane holds all 16 features of its table; S += psi_w^T y_w; then the
+// Walsh gradient, du = dt dt/du', dxh = du W and the normalisation backward.
+template <int NW, bool CAUSAL, bool REVERSE, bool POLY>
+__global__ __launch_bounds__(NW * 64) void grad_kernel(
+    const bf16 *__restrict__ Xr, const bf16 *__restrict__ Xw, ValSrc<bf16> vr_src,
+    ValSrc<bf16> vw_src, const float *__restrict__ W, int L, Squash sq, int64_t N, int seg,
+    int64_t nseg, const float *__restrict__ st, bf16 *__restrict__ dX)
+{
+    constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
+    constexpr int NTHR = NW * 64;
+    constexpr int NS = CAUSAL ? 2 : 1;
+    constexpr int DXS = HD + 4;  // dxh partial row stride (floats)
+    constexpr int NIT = (WCT * 16 + NTHR - 1) / NTHR;
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][NS * WCT * XRS];
+    __shared__ __attribute__((aligned(16))) float kbuf[2][NS * WCT];
+    __shared__ __attribute__((aligned(16))) bf16 yrow_r[WCT * YRS];
+    __shared__ __attribute__((aligned(16))) bf16 yrow_w[CAUSAL ? WCT * YRS : 8];
+    __shared__ __attribute__((aligned(16))) bf16 ycol_w[CAUSAL ? NCOL * YCS : 8];
+    __shared__ __attribute__((aligned(16))) float dxp[NW * WCT * DXS];
+    __shared__ __attribute__((aligned(16))) bf16 wl[2 * NW * 16 * XRS];
+    __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
+
+    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const bf16 *Rh = Xr + bh * N * HD;
+    const bf16 *Wh = Xw + bh * N * HD;
+    ValSrc<bf16> vrh = vr_src, vwh = vw_src;
+    vrh.V += bh * N * HD;
+    vwh.V += bh * N * HD;
+    if (RD) {
+        vrh.O += bh * N * HD;
+        vrh.den += bh * N;
+    } else {
+        vwh.O += bh * N * HD;
+        vwh.den += bh * N;
+    }
+    bf16 *dXh = dX + bh * N * HD;
+
+    constexpr int WROWS = NW * 16;
+    stage_w<NTHR>(W, L * NP, WROWS, wl, sl);
+    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    floatx4 acc[4][NT];  // CxF state
+    load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
+
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
+    auto chunk0 = [&](int64_t ci) { return t_begin + (REVERSE ? nch - 1 - ci : ci) * WCT; };
+
+    XStage<NTHR, NS> xs;
+    YStage<NTHR, RD> ysr;
+    YStage<NTHR, !RD> ysw;
+    yrow_zero_pad<NTHR>(yrow_r);
+    if (CAUSAL) {
+        yrow_zero_pad<NTHR>(yrow_w);
+        ystage_zero_pad<NTHR>(ycol_w);
+        ystage_load<NTHR, !RD>(vwh, chunk0(0), t_end, ysw);
+    }
+    ystage_load<NTHR, RD>(vrh, chunk0(0), t_end, ysr);
+    xstage_load<NTHR, NS>(Rh, Wh, chunk0(0), t_end, xs);
+    xstage_store<NTHR, NS>(xs, xbuf[0], kbuf[0]);
+    if (nch > 1) xstage_load<NTHR, NS>(Rh, Wh, chunk0(1), t_end, xs);
+    lds_barrier();
+
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int b = ci & 1;
+        const int64_t tok0 = chunk0(ci);
+        ystage_store<NTHR, RD>(ysr, tok0, t_end, nullptr, yrow_r);
+        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, tok0, t_end, ycol_w, yrow_w);
+        if (ci + 1 < nch) {
+            ystage_load<NTHR, RD>(vrh, chunk0(ci + 1), t_end, ysr);
+            if (CAUSAL) ystage_load<NTHR, !RD>(vwh, chunk0(ci + 1), t_end, ysw);
+        }
+        floatx4 tr[2], cr[2];
+        bf16x8 pfm[4];
+        {
+            WRows wr;
+            wrows_lds(wl, WROWS, wr);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                hash_staged_chain<POLY>(xbuf[b], kbuf[b], tt, wr, sq, tr[tt], cr[tt]);
+            if (CAUSAL) {
+                bf16x8 pw[2][2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const floatx4 t = hash_staged<POLY>(xbuf[b] + WCT * XRS, kbuf[b] + WCT, tt, wr, sq);
+                    walsh_tm(t, q4, pw[tt][0], pw[tt][1]);
+                }
+                const bf16x8 sel[2] = {*reinterpret_cast<const bf16x8 *>(sl + lane * 8),
+                                       *reinterpret_cast<const bf16x8 *>(sl + (64 + lane) * 8)};
+                feat_major(pw, sel, pfm);
+            }
+        }
+        lds_barrier();  // #1: value rows of this chunk staged
+        if (ci + 1 < nch) {  // the next chunk's rows into the other buffer
+            xstage_store<NTHR, NS>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            if (ci + 2 < nch) xstage_load<NTHR, NS>(Rh, Wh, chunk0(ci + 2), t_end, xs);
+        }
+        // reader value rows as B operands (token-major)
+        bf16x8 yb8[2][2];
+        bf16x4 yb4[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) yrow_frags(yrow_r, tt * 16 + c16, yb8[tt], yb4[tt]);
+        floatx4 dps[4][2];  // dpsi^T tiles (s, tt): lane (rows 4g + r <-> S = 4s + r of table 4w + g, token c16)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) dps[s][tt] = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 eb8;
+        bf16x4 eb4;
+        if (CAUSAL) {
+            // E^T tiles D[j][i] = y_w(j) . y_r(i) over all value columns
+            constexpr int TJ[3] = {0, REVERSE ? 1 : 0, 1}, TI[3] = {0, REVERSE ? 0 : 1, 1};
+            floatx4 et[3];
+#pragma unroll
+            for (int pi = 0; pi < 3; ++pi) et[pi] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj) {
+                bf16x8 wa8[2];
+                bf16x4 wa4;
+                yrow_frags(yrow_w, tj * 16 + c16, wa8, wa4);
+#pragma unroll
+                for (int pi = 0; pi < 3; ++pi) {
+                    if (TJ[pi] != tj) continue;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) mma32(et[pi], wa8[k], yb8[TI[pi]][k]);
+                    mma16(et[pi], wa4, yb4[TI[pi]]);
+                }
+            }
+#pragma unroll
+            for (int pi = 0; pi < 3; pi += 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = REVERSE ? (4 * g + r >= c16) : (4 * g + r <= c16);
+                    et[pi][r] = keep ? et[pi][r] : 0.f;
+                }
+            if (REVERSE) {
+                eb8 = cat8(acc2bf4(et[0]), acc2bf4(et[1]));  // reader tile 0: writer tiles 0, 1
+                eb4 = acc2bf4(et[2]);                        // reader tile 1: writer tile 1
+            } else {
+                eb4 = acc2bf4(et[0]);                        // reader tile 0: writer tile 0
+                eb8 = cat8(acc2bf4(et[1]), acc2bf4(et[2]));  // reader tile 1: writer tiles 0, 1
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // inter-chunk part with the state before this chunk
+            const bf16x8 sa0 = cat8(acc2bf4(acc[s][0]), acc2bf4(acc[s][1]));
+            const bf16x8 sa1 = cat8(acc2bf4(acc[s][2]), acc2bf4(acc[s][3]));
+            const bf16x4 sa2 = acc2bf4(acc[s][4]);
+            // every accumulation chain issues its 16x16x32 products before its
+            // 16x16x16 ones (a 16x16x16 result never feeds a 16x16x32 product)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                mma32(dps[s][tt], sa0, yb8[tt][0]);
+                mma32(dps[s][tt], sa1, yb8[tt][1]);
+            }
+            if (CAUSAL) {
+                if (REVERSE) {
+                    mma32(dps[s][0], pfm[s], eb8);
+                } else {
+                    mma32(dps[s][1], pfm[s], eb8);
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) mma16(dps[s][tt], sa2, yb4[tt]);
+            if (CAUSAL) {
+                if (REVERSE) {
+                    mma16(dps[s][1], hi4(pfm[s]), eb4);
+                } else {
+                    mma16(dps[s][0], lo4(pfm[s]), eb4);
+                }
+            }
+        }
+        if (CAUSAL) {
+            // S += psi_w^T y_w (after every read of the state above)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const bf16x8 ya = ycol_frag(ycol_w, ct * 16 + c16);  // rows = value columns
+#pragma unroll
+                for (int s = 0; s < 4; ++s) mma32(acc[s][ct], ya, pfm[s]);
+            }
+        }
+        // Walsh gradient -> du -> dxh^T partial over this wave's hyperplanes
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float dp[16], dt[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dp[4 * s + r] = dps[s][tt][r];
+            walsh_grad(dp, tr[tt], dt);
+            const bf16x4 du = pk4(pk_bf16(dt[0] * cr[tt][0], dt[1] * cr[tt][1]),
+                                  pk_bf16(dt[2] * cr[tt][2], dt[3] * cr[tt][3]));
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                bf16x4 whi, wlo;
+                wcols_lds(wl, WROWS, nt, whi, wlo);
+                floatx4 xa = {0.f, 0.f, 0.f, 0.f};
+                mma32(xa, cat8(whi, wlo), cat8(du, du));  // (W_hi + W_lo)^T du^T
+                *reinterpret_cast<floatx4 *>(dxp + (w * WCT + tt * 16 + c16) * DXS + nt * 16 + 4 * g) = xa;
+            }
+        }
+        lds_barrier();  // #2: dxh partials of every wave in LDS
+        // sum over waves, then the normalisation backward (16 threads per row)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = threadIdx.x + it * NTHR;
+            const int i = (e >> 4) & (WCT - 1), part = e & 15;
+            floatx4 dh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww)
+                dh += *reinterpret_cast<const floatx4 *>(dxp + (ww * WCT + i) * DXS + part * 4);
+            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[b] + i * XRS + part * 4);
+            float x[4], ss = 0.f, dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[c] = (float)xv[c];
+                ss = fmaf(x[c], x[c], ss);
+                dot = fmaf(dh[c], x[c], dot);
+            }
+            ss = sum16(ss);
+            dot = sum16(dot);
+            const int64_t tok = tok0 + i;
+            if (e < WCT * 16 && tok < t_end) {
+                const float nrm = sqrtf(ss);
+                float rv[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (nrm > 1e-12f) {
+                        const float inv = 1.0f / nrm;
+                        rv[c] = (dh[c] - dot * inv * inv * x[c]) * inv;
+                    } else {
+                        rv[c] = dh[c] * 1e12f;
+                    }
+                }
+                *reinterpret_cast<bf16x4 *>(dXh + tok * HD + part * 4) =
+                    pk4(pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3]));
+            }
+        }
+    }
+}
+
+}  // namespace race
