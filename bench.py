@@ -108,13 +108,15 @@ def main() -> int:
                       dtype=torch.uint8, device=dev)
     wsb = (torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, True),
                        dtype=torch.uint8, device=dev) if w.backward else None)
+    # the forward's key state, kept for the backward (as autograd would)
+    saved = binding.new_saved(q, W, w.causal, w.chunk) if w.backward else None
 
     def step(trf=None, trb=None):
         binding.forward(q, k, v, W, w.tau, w.causal, w.chunk, workspace=wsf, out=(o, den),
-                        trace=trf)
+                        trace=trf, saved=saved)
         if w.backward:
             binding.backward(q, k, v, W, o, den, do, w.tau, w.causal, w.chunk, workspace=wsb,
-                             out=grads, trace=trb)
+                             out=grads, trace=trb, saved=saved)
 
     for _ in range(args.warmup):
         step()

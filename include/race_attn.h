@@ -112,19 +112,36 @@ typedef struct {
     const char *name[RACE_TRACE_MAX];
 } race_trace_t;
 
-/* race_attn_forward / race_attn_backward with optional tracing (trace may
- * be NULL, which is exactly the plain entry point). */
+/* Size, in bytes, of the key-state buffer that race_attn_forward_ex can
+ * save for race_attn_backward_ex (step 3 / zh §2.3: the per-segment prefix
+ * sums of the keys' bucket statistics and the per-head totals, fp32).  0 when
+ * the configuration does not use it (RACE_F32, or L > 32).  Pure host
+ * function. */
+race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P, int causal,
+                                    int chunk, race_dtype_t dt, size_t *bytes);
+
+/* race_attn_forward / race_attn_backward with optional tracing and an
+ * optional saved key state.
+ *   trace: may be NULL.
+ *   saved: device pointer (256-byte aligned, race_attn_saved_bytes bytes,
+ *     owned by the caller) or NULL.  The forward writes the key state there;
+ *     a backward given the same buffer, for the same Q, K, V, W, tau, causal
+ *     and chunk, reads it instead of recomputing it (results are identical).
+ *     Ignored when race_attn_saved_bytes is 0.  A misaligned saved buffer is
+ *     RACE_ERR_WORKSPACE.
+ * With trace = NULL and saved = NULL these are exactly the plain entry
+ * points. */
 race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, const float *W,
                                    int L, int P, float tau, int causal, int B, int H, int64_t N,
                                    int d, race_dtype_t dt, int chunk, void *O, float *den,
-                                   void *workspace, size_t ws_bytes, void *stream,
+                                   void *workspace, size_t ws_bytes, void *stream, void *saved,
                                    race_trace_t *trace);
 race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
                                     const float *W, const void *O, const float *den,
                                     const void *dO, int L, int P, float tau, int causal, int B,
                                     int H, int64_t N, int d, race_dtype_t dt, int chunk, void *dQ,
                                     void *dK, void *dV, void *workspace, size_t ws_bytes,
-                                    void *stream, race_trace_t *trace);
+                                    void *stream, const void *saved, race_trace_t *trace);
 
 /* Diagnostic: the polynomial the kernels use for t = tanh(tanh(v) / tau).
  * With e = exp(-2|v|) and y = 2e - 1, t = sign(v) * sum_k coef[k] y^k for

@@ -19,8 +19,9 @@ STATUS = {
     0: "RACE_OK", 1: "RACE_ERR_NULL", 2: "RACE_ERR_SHAPE", 3: "RACE_ERR_UNSUPPORTED",
     4: "RACE_ERR_TAU", 5: "RACE_ERR_CHUNK", 6: "RACE_ERR_WORKSPACE", 7: "RACE_ERR_HIP",
 }
-EXPORTS = ("race_attn_workspace_bytes", "race_attn_forward", "race_attn_backward",
-           "race_attn_forward_ex", "race_attn_backward_ex", "race_attn_status_string")
+EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forward",
+           "race_attn_backward", "race_attn_forward_ex", "race_attn_backward_ex",
+           "race_attn_status_string")
 TRACE_MAX = 24
 
 
@@ -78,10 +79,13 @@ def lib():
         L.race_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, i32, i32,
                                          i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_backward.restype = i32
+        L.race_attn_saved_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(sz)]
+        L.race_attn_saved_bytes.restype = i32
         tp = ctypes.POINTER(_RaceTrace)
-        L.race_attn_forward_ex.argtypes = L.race_attn_forward.argtypes + [tp]
+        L.race_attn_forward_ex.argtypes = L.race_attn_forward.argtypes + [vp, tp]
         L.race_attn_forward_ex.restype = i32
-        L.race_attn_backward_ex.argtypes = L.race_attn_backward.argtypes + [tp]
+        L.race_attn_backward_ex.argtypes = L.race_attn_backward.argtypes + [vp, tp]
         L.race_attn_backward_ex.restype = i32
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
@@ -110,6 +114,26 @@ def workspace_bytes(B, H, N, d, L, P, causal, chunk, dtype, for_backward) -> int
     return out.value
 
 
+def saved_bytes(B, H, N, d, L, P, causal, chunk, dtype) -> int:
+    """Bytes of the key-state buffer a forward can save for its backward (0: unused)."""
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_saved_bytes(B, H, N, d, L, P, int(causal), chunk, dtype_code(dtype),
+                                       ctypes.byref(out)))
+    return out.value
+
+
+def new_saved(q: torch.Tensor, W: torch.Tensor, causal: bool, chunk: int = 0):
+    """A saved-state buffer for forward(..., saved=) / backward(..., saved=), or None."""
+    B, H, N, d = q.shape
+    L, P, _ = W.shape
+    n = saved_bytes(B, H, N, d, L, P, causal, chunk, q.dtype)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
 def _shape(q: torch.Tensor):
     if q.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
@@ -135,8 +159,9 @@ def _tp(trace):
 
 
 def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None, out=None,
-            trace: Trace | None = None):
-    """RACE attention forward; returns (o, den).  out = (o, den) reuses buffers."""
+            trace: Trace | None = None, saved=None):
+    """RACE attention forward; returns (o, den).  out = (o, den) reuses buffers;
+    saved (from new_saved) receives the key state for the backward."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v)
     if W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous() or W.device != q.device:
@@ -154,13 +179,14 @@ def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None
                                       P, float(tau), int(causal), B, H, N, d,
                                       dtype_code(q.dtype), chunk, o.data_ptr(), den.data_ptr(),
                                       workspace.data_ptr(), workspace.numel(), _stream(),
-                                      _tp(trace)))
+                                      _ptr(saved), _tp(trace)))
     return o, den
 
 
 def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, workspace=None,
-             out=None, trace: Trace | None = None):
-    """RACE attention backward; returns (dq, dk, dv).  out = (dq, dk, dv) reuses buffers."""
+             out=None, trace: Trace | None = None, saved=None):
+    """RACE attention backward; returns (dq, dk, dv).  out = (dq, dk, dv) reuses buffers;
+    saved: the buffer the forward of the same inputs filled, or None."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v, o, do)
     if den.dtype != torch.float32 or den.shape != (B, H, N) or not den.is_contiguous():
@@ -178,7 +204,7 @@ def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, w
                                        float(tau), int(causal), B, H, N, d, dtype_code(q.dtype),
                                        chunk, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                        workspace.data_ptr(), workspace.numel(), _stream(),
-                                       _tp(trace)))
+                                       _ptr(saved), _tp(trace)))
     return dq, dk, dv
 
 
@@ -187,8 +213,10 @@ class RaceAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, W, tau, causal, chunk=0):
-        o, den = forward(q, k, v, W, tau, causal, chunk)
+        saved = new_saved(q, W, causal, chunk)
+        o, den = forward(q, k, v, W, tau, causal, chunk, saved=saved)
         ctx.save_for_backward(q, k, v, W, o, den)
+        ctx.key_state = saved
         ctx.cfg = (tau, causal, chunk)
         return o
 
@@ -196,7 +224,9 @@ class RaceAttention(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, W, o, den = ctx.saved_tensors
         tau, causal, chunk = ctx.cfg
-        dq, dk, dv = backward(q, k, v, W, o, den, do.contiguous(), tau, causal, chunk)
+        dq, dk, dv = backward(q, k, v, W, o, den, do.contiguous(), tau, causal, chunk,
+                              saved=ctx.key_state)
+        ctx.key_state = None
         return dq, dk, dv, None, None, None, None
 
 

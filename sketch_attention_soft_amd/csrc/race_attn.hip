@@ -57,10 +57,12 @@ struct Plan {
     size_t t_bytes;    // forward hash features of Q or K
     size_t tb_bytes;   // backward hash features (t and dt/du) of Q or K
     size_t wt_bytes;   // transposed projection for the backward
+    int scan_groups;   // segment groups of the two-pass scan
+    size_t scan_bytes; // group totals of the scan
     // forward layout
-    size_t f_tq, f_tk, f_st, f_total;
+    size_t f_tq, f_tk, f_st, f_scan, f_total;
     // backward layout
-    size_t b_tq, b_tk, b_s, b_gt, b_g, b_wt, b_total;
+    size_t b_tq, b_tk, b_s, b_gt, b_g, b_wt, b_scan, b_total;
 };
 
 race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
@@ -100,10 +102,15 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->tb_bytes = p->fused ? 0 : align256((size_t)p->rows * L * 2 * race::NP * sizeof(float));
     const int lp32 = (p->LP + 31) / 32 * 32;
     p->wt_bytes = p->fused ? 0 : align256((size_t)race::HD * lp32 * (2 * sizeof(bf16) + sizeof(float)));
+    // groups of at least 16 segments, at most 64 groups
+    const int64_t groups = p->nseg / 16;
+    p->scan_groups = (int)(groups < 1 ? 1 : groups > 64 ? 64 : groups);
+    p->scan_bytes = align256((size_t)p->BH * p->scan_groups * p->F * race::NCOL * sizeof(float));
     p->f_tq = 0;
     p->f_tk = p->f_tq + p->t_bytes;
     p->f_st = p->f_tk + p->t_bytes;
-    p->f_total = p->f_st + p->st_bytes;
+    p->f_scan = p->f_st + p->st_bytes;
+    p->f_total = p->f_scan + p->scan_bytes;
     p->b_tq = 0;
     p->b_tk = p->b_tq + p->tb_bytes;
     p->b_s = p->b_tk + p->tb_bytes;
@@ -111,7 +118,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     // the bf16 kernels read the gradient state transposed from its FxC copy
     p->b_g = p->b_gt + (p->fused ? 0 : p->st_bytes);
     p->b_wt = p->b_g + p->st_bytes;
-    p->b_total = p->b_wt + p->wt_bytes;
+    p->b_scan = p->b_wt + p->wt_bytes;
+    p->b_total = p->b_scan + p->scan_bytes;
     return RACE_OK;
 }
 
@@ -196,6 +204,21 @@ int hash_grid(int64_t rows)
     return (int)(blocks < 16384 ? blocks : 16384);
 }
 
+// exclusive prefix (reverse = 0) or suffix (reverse = 1) of the segment
+// states of every head, plus the head totals
+void launch_scan(const Tracer &tr, const char *name, const Plan &p, float *st, float *tmp,
+                 int reverse)
+{
+    const int64_t elems = (int64_t)p.F * race::NCOL;
+    const dim3 grid((unsigned)((elems + 255) / 256), (unsigned)p.scan_groups, (unsigned)p.BH);
+    tr.begin(name);
+    hipLaunchKernelGGL(race::scan_reduce_kernel, grid, dim3(256), 0, tr.s, st, tmp, p.nseg, elems,
+                       p.scan_groups);
+    hipLaunchKernelGGL(race::scan_apply_kernel, grid, dim3(256), 0, tr.s, st, tmp, p.nseg, elems,
+                       p.scan_groups, reverse);
+    tr.end();
+}
+
 // walk kernel with the squash polynomial or its direct evaluation
 template <int NW, bool CAUSAL, bool BWD, typename T>
 void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *R,
@@ -245,11 +268,13 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const race::Squa
 
 template <typename T, int NW>
 void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const float *W, float tau,
-                    int causal, T *O, float *den, char *ws, const Tracer &tr)
+                    int causal, T *O, float *den, char *ws, float *saved, const Tracer &tr)
 {
     float *tq = reinterpret_cast<float *>(ws + p.f_tq);
     float *tk = reinterpret_cast<float *>(ws + p.f_tk);
-    float *st = reinterpret_cast<float *>(ws + p.f_st);
+    // key state: into the caller's saved buffer when given (bf16 path)
+    float *st = saved ? saved : reinterpret_cast<float *>(ws + p.f_st);
+    float *scan_tmp = reinterpret_cast<float *>(ws + p.f_scan);
     const float inv_tau = 1.0f / tau;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
     if constexpr (sizeof(T) == 2 && NW <= 4) {
@@ -257,11 +282,9 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
         constexpr int WS = 2 * NW, WW = 2 * NW;
         const race::Squash sq = fit_squash(tau, RACE_BF16);
         const dim3 nblk((unsigned)(p.BH * p.nseg));
-        const int64_t elems = (int64_t)p.F * race::NCOL;
-        const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
         const race::ValSrc<T> vv{V, nullptr, nullptr};
         launch_sum<WS, false, 1>(tr, "sum_kv", nblk, sq, K, vv, W, p, st, nullptr);
-        LAUNCH(tr, "scan_kv", race::scan_kernel, sgrid, b256, st, p.nseg, elems, 0);
+        launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
         if (causal)
             launch_walk<WW, true, false>(tr, "fwd_o", nblk, sq, Q, K, vv, W, p, st, O, den);
         else
@@ -274,9 +297,7 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     const dim3 nblk((unsigned)(p.BH * p.nseg));
     LAUNCH(tr, "seg_sum_kv", (race::seg_sum_kernel<T, NW, false, false>), nblk, bw, tk, race::NP,
            vs, p.N, p.L, (int)p.seg, p.nseg, st);
-    const int64_t elems = (int64_t)p.F * race::NCOL;
-    const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
-    LAUNCH(tr, "scan_kv", race::scan_kernel, sgrid, b256, st, p.nseg, elems, 0);
+    launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
     if (causal)
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, true, false>), nblk, bw, tq, tk,
                race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
@@ -288,7 +309,7 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
 template <typename T, int NW, int CAUSAL>
 void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                           const T *O, const float *den, const T *dO, float tau, T *dQ, T *dK,
-                          T *dV, char *ws, const Tracer &tr)
+                          T *dV, char *ws, const float *saved, const Tracer &tr)
 {
     float *tq = reinterpret_cast<float *>(ws + p.b_tq);
     float *tk = reinterpret_cast<float *>(ws + p.b_tk);
@@ -296,6 +317,7 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     float *sGt = reinterpret_cast<float *>(ws + p.b_gt);  // gradient state, CxF layout (fp32 / L > 32)
     float *sG = reinterpret_cast<float *>(ws + p.b_g);    // gradient state, FxC layout
     char *wt = ws + p.b_wt;
+    float *scan_tmp = reinterpret_cast<float *>(ws + p.b_scan);
     const float inv_tau = 1.0f / tau;
     const int lp32 = (p.LP + 31) / 32 * 32;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
@@ -306,15 +328,18 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
         const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
         const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
         const dim3 nblk((unsigned)(p.BH * p.nseg));
-        const int64_t elems = (int64_t)p.F * race::NCOL;
-        const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
-        // key state S (CxF, for dQ): prefix over segments
-        launch_sum<WS, false, 1>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, sS, nullptr);
-        LAUNCH(tr, "scan_kv_t", race::scan_kernel, sgrid, b256, sS, p.nseg, elems, 0);
+        // key state S (FxC, read transposed by dQ): prefix over segments, or
+        // the forward's copy
+        const float *sK = saved;
+        if (!sK) {
+            launch_sum<WS, false, 1>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, sS, nullptr);
+            launch_scan(tr, "scan_kv_t", p, sS, scan_tmp, 0);
+            sK = sS;
+        }
         // gradient state G (FxC for dV and CxF for dK): suffix over segments
         launch_sum<WS, true, 1>(tr, "sum_qd", nblk, sq, Q, vd, W, p, sG, nullptr);
-        LAUNCH(tr, "scan_qd", race::scan_kernel, sgrid, b256, sG, p.nseg, elems, 1);
-        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, sq, Q, K, vd, vv, W, p, sS, dQ);
+        launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
+        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, sq, Q, K, vd, vv, W, p, sK, dQ);
         launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, sq, K, Q, vv, vd, W, p, sG, dK);
         launch_walk<WW, CAUSAL != 0, true>(tr, "dv", nblk, sq, K, Q, vd, W, p, sG, dV, nullptr);
         return;
@@ -328,20 +353,18 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
     const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
     const dim3 nblk((unsigned)(p.BH * p.nseg));
-    const int64_t elems = (int64_t)p.F * race::NCOL;
-    const dim3 sgrid((unsigned)((elems + 255) / 256), (unsigned)p.BH);
     const int ts = 2 * race::NP;
     // key-side state S (CxF, for dQ): prefix over segments
     LAUNCH(tr, "seg_sum_kv_t", (race::seg_sum_kernel<T, NW, true, false>), nblk, bw, tk, ts, vv,
            p.N, p.L, (int)p.seg, p.nseg, sS);
-    LAUNCH(tr, "scan_kv_t", race::scan_kernel, sgrid, b256, sS, p.nseg, elems, 0);
+    launch_scan(tr, "scan_kv_t", p, sS, scan_tmp, 0);
     // query-side gradient states G (CxF for dK, FxC for dV): suffix over segments
     LAUNCH(tr, "seg_sum_qd_t", (race::seg_sum_kernel<T, NW, true, true>), nblk, bw, tq, ts, vd,
            p.N, p.L, (int)p.seg, p.nseg, sGt);
-    LAUNCH(tr, "scan_qd_t", race::scan_kernel, sgrid, b256, sGt, p.nseg, elems, 1);
+    launch_scan(tr, "scan_qd_t", p, sGt, scan_tmp, 1);
     LAUNCH(tr, "seg_sum_qd", (race::seg_sum_kernel<T, NW, false, true>), nblk, bw, tq, ts, vd,
            p.N, p.L, (int)p.seg, p.nseg, sG);
-    LAUNCH(tr, "scan_qd", race::scan_kernel, sgrid, b256, sG, p.nseg, elems, 1);
+    launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
     // dQ: readers Q (values D), writers K (values [v|1]), token order
     LAUNCH(tr, "dpsi_q", (race::dpsi_kernel<T, NW, CAUSAL, false, true>), nblk, bw, Q, tq, tk, vd,
            vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ);
@@ -356,28 +379,29 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
 template <typename T, int NW>
 void launch_backward(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                      const T *O, const float *den, const T *dO, float tau, int causal, T *dQ,
-                     T *dK, T *dV, char *ws, const Tracer &tr)
+                     T *dK, T *dV, char *ws, const float *saved, const Tracer &tr)
 {
     if (causal)
-        launch_backward_body<T, NW, 1>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, tr);
+        launch_backward_body<T, NW, 1>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr);
     else
-        launch_backward_body<T, NW, 0>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, tr);
+        launch_backward_body<T, NW, 0>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr);
 }
 
 template <typename T>
 void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V, const float *W,
-                      float tau, int causal, void *O, float *den, char *ws, const Tracer &tr)
+                      float tau, int causal, void *O, float *den, char *ws, float *saved,
+                      const Tracer &tr)
 {
     auto q = static_cast<const T *>(Q);
     auto k = static_cast<const T *>(K);
     auto v = static_cast<const T *>(V);
     auto o = static_cast<T *>(O);
     switch (p.nw) {
-    case 1: launch_forward<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
-    case 2: launch_forward<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
-    case 4: launch_forward<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+    case 1: launch_forward<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+    case 2: launch_forward<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+    case 4: launch_forward<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
     default:
-        if constexpr (sizeof(T) == 2) launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, tr);
+        if constexpr (sizeof(T) == 2) launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr);
         break;
     }
 }
@@ -386,7 +410,7 @@ template <typename T>
 void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *V,
                        const float *W, const void *O, const float *den, const void *dO,
                        float tau, int causal, void *dQ, void *dK, void *dV, char *ws,
-                       const Tracer &tr)
+                       const float *saved, const Tracer &tr)
 {
     auto q = static_cast<const T *>(Q);
     auto k = static_cast<const T *>(K);
@@ -397,12 +421,12 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     auto dk = static_cast<T *>(dK);
     auto dv = static_cast<T *>(dV);
     switch (p.nw) {
-    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr); break;
-    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr); break;
-    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr); break;
+    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr); break;
+    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr); break;
+    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr); break;
     default:
         if constexpr (sizeof(T) == 2)
-            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, tr);
+            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr);
         break;
     }
 }
@@ -434,10 +458,22 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     return RACE_OK;
 }
 
+race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P, int causal,
+                                    int chunk, race_dtype_t dt, size_t *bytes)
+{
+    (void)causal;
+    if (!bytes) return RACE_ERR_NULL;
+    Plan p;
+    const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    if (st != RACE_OK) return st;
+    *bytes = p.fused ? p.st_bytes : 0;
+    return RACE_OK;
+}
+
 race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, const float *W,
                                    int L, int P, float tau, int causal, int B, int H, int64_t N,
                                    int d, race_dtype_t dt, int chunk, void *O, float *den,
-                                   void *workspace, size_t ws_bytes, void *stream,
+                                   void *workspace, size_t ws_bytes, void *stream, void *saved,
                                    race_trace_t *trace)
 {
     if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
@@ -447,13 +483,15 @@ race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, 
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
+    if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
+    float *sv = p.fused ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
-        dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, tr);
+        dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else
-        dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, tr);
+        dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 
@@ -463,7 +501,7 @@ race_status_t race_attn_forward(const void *Q, const void *K, const void *V, con
                                 void *workspace, size_t ws_bytes, void *stream)
 {
     return race_attn_forward_ex(Q, K, V, W, L, P, tau, causal, B, H, N, d, dt, chunk, O, den,
-                                workspace, ws_bytes, stream, nullptr);
+                                workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
@@ -471,7 +509,7 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
                                     const void *dO, int L, int P, float tau, int causal, int B,
                                     int H, int64_t N, int d, race_dtype_t dt, int chunk, void *dQ,
                                     void *dK, void *dV, void *workspace, size_t ws_bytes,
-                                    void *stream, race_trace_t *trace)
+                                    void *stream, const void *saved, race_trace_t *trace)
 {
     if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !workspace)
         return RACE_ERR_NULL;
@@ -481,13 +519,15 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
+    if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
+    const float *sv = p.fused ? static_cast<const float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
-        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, tr);
+        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr);
     else
-        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, tr);
+        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 
@@ -498,7 +538,7 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
                                  void *workspace, size_t ws_bytes, void *stream)
 {
     return race_attn_backward_ex(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk,
-                                 dQ, dK, dV, workspace, ws_bytes, stream, nullptr);
+                                 dQ, dK, dV, workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg)

@@ -11,8 +11,11 @@
 // Forward pipeline (B*H heads of N tokens, segments of `seg` tokens):
 //   hash_kernel     t = tanh(tanh(W x / |x|) / tau) for every row of Q and K
 //   seg_sum_kernel  per segment g: S_g = sum_{j in g} psi(k_j)^T [v_j | 1]
-//   scan_kernel     exclusive prefix of S_g over the segments of a head, plus
-//                   the head total (used by the non-causal readout)
+//   scan_reduce_kernel / scan_apply_kernel
+//                   exclusive prefix (or suffix) of S_g over the segments of a
+//                   head, plus the head total (used by the non-causal readout),
+//                   in groups of consecutive segments: group totals first,
+//                   then each group rescans from the totals before it
 //   readout_kernel  per segment, in sub-chunks of 16 tokens: the running state
 //                   S (MFMA accumulators) is read by the chunk's queries, the
 //                   causal intra-chunk term tril(psi_Q psi_K^T) [V | 1] is
@@ -30,7 +33,7 @@
 //   "CxF"  tile (ct, ft): rows = value columns, columns = features
 //          lane l holds column 16*ct + 4*(l/16) + r, feature 16*ft + l%16
 // A segment state block in global memory is [wave][8][5][64 lanes][4 floats]
-// in the producing kernel's layout; scan_kernel is layout-agnostic.
+// in the producing kernel's layout; the scan is layout-agnostic.
 #pragma once
 #include "race_common.h"
 
@@ -328,38 +331,72 @@ __global__ __launch_bounds__(NW * 64) void seg_sum_kernel(const float *__restric
             *reinterpret_cast<floatx4 *>(out + st_index(w, a, b, lane)) = acc[a][b];
 }
 
-// scan_kernel: per head, st[g] <- sum of st[g'] over g' < g (reverse = 0) or
-// g' > g (reverse = 1); st[nseg] <- total.
-__global__ __launch_bounds__(256) void scan_kernel(float *__restrict__ st, int64_t nseg,
-                                                   int64_t elems, int reverse)
+// Scan over segments: per head, st[g] <- sum of st[g'] over g' < g
+// (reverse = 0) or g' > g (reverse = 1); st[nseg] <- total.  The segments
+// are split into G groups of consecutive segments; scan_reduce_kernel writes
+// the group totals to tmp[head][G][elems], scan_apply_kernel rescans each
+// group starting from the totals of the groups before (after) it.
+__global__ __launch_bounds__(256) void scan_reduce_kernel(const float *__restrict__ st,
+                                                          float *__restrict__ tmp, int64_t nseg,
+                                                          int64_t elems, int G)
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= elems) return;
-    float *p = st + (int64_t)blockIdx.y * (nseg + 1) * elems + e;
-    float run = 0.f;
+    const int grp = blockIdx.y;
+    const int64_t bh = blockIdx.z;
+    const float *p = st + bh * (nseg + 1) * elems + e;
+    const int64_t s0 = grp * nseg / G, s1 = (grp + 1) * nseg / G;
     constexpr int U = 8;  // loads in flight per thread
+    float sum = 0.f;
+    int64_t g = s0;
+    for (; g + U <= s1; g += U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = p[(g + u) * elems];
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum += v[u];
+    }
+    for (; g < s1; ++g) sum += p[g * elems];
+    tmp[(bh * G + grp) * elems + e] = sum;
+}
+
+__global__ __launch_bounds__(256) void scan_apply_kernel(float *__restrict__ st,
+                                                         const float *__restrict__ tmp,
+                                                         int64_t nseg, int64_t elems, int G,
+                                                         int reverse)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= elems) return;
+    const int grp = blockIdx.y;
+    const int64_t bh = blockIdx.z;
+    float *p = st + bh * (nseg + 1) * elems + e;
+    float run = 0.f;
+    for (int q = 0; q < G; ++q)
+        if (reverse ? q > grp : q < grp) run += tmp[(bh * G + q) * elems + e];
+    const int64_t s0 = grp * nseg / G, s1 = (grp + 1) * nseg / G, n = s1 - s0;
+    constexpr int U = 8;
     int64_t i = 0;
-    for (; i + U <= nseg; i += U) {
+    for (; i + U <= n; i += U) {
         float v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g = reverse ? nseg - 1 - (i + u) : i + u;
+            const int64_t g = reverse ? s1 - 1 - (i + u) : s0 + i + u;
             v[u] = p[g * elems];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g = reverse ? nseg - 1 - (i + u) : i + u;
+            const int64_t g = reverse ? s1 - 1 - (i + u) : s0 + i + u;
             p[g * elems] = run;
             run += v[u];
         }
     }
-    for (; i < nseg; ++i) {
-        const int64_t g = reverse ? nseg - 1 - i : i;
+    for (; i < n; ++i) {
+        const int64_t g = reverse ? s1 - 1 - i : s0 + i;
         const float v = p[g * elems];
         p[g * elems] = run;
         run += v;
     }
-    p[nseg * elems] = run;
+    if (grp == (reverse ? 0 : G - 1)) p[nseg * elems] = run;
 }
 
 // ---------------------------------------------------------------------------

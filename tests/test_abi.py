@@ -90,6 +90,37 @@ def test_workspace_validation(lib, kw, code):
     assert ws_bytes(lib, **kw)[0] == code
 
 
+def test_saved_bytes(lib):
+    fn = lib.race_attn_saved_bytes
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.POINTER(ctypes.c_size_t)]
+    out = ctypes.c_size_t(7)
+    assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, ctypes.byref(out)) == OK
+    assert out.value > 0 and out.value % 256 == 0
+    # one fp32 state of F x 80 per segment plus the head total
+    assert out.value >= 2 * 512 * 80 * 4
+    assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, F32, ctypes.byref(out)) == OK and out.value == 0
+    assert fn(1, 1, 1 << 16, 64, 64, 4, 1, 0, BF16, ctypes.byref(out)) == OK and out.value == 0
+    assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, None) == E_NULL
+    assert fn(1, 1, 0, 64, 32, 4, 1, 0, BF16, ctypes.byref(out)) == E_SHAPE
+
+
+def test_saved_alignment(lib):
+    i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    lib.race_attn_forward_ex.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i32, i64, i32,
+                                         i32, i32, vp, vp, vp, sz, vp, vp, vp]
+    lib.race_attn_backward_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, i32,
+                                          i32, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp, vp, vp]
+    st = lib.race_attn_forward_ex(FAKE, FAKE, FAKE, FAKE, 8, 4, 1.0, 1, 1, 1, 64, 64, BF16, 0, FAKE,
+                                  FAKE, FAKE * 16, 1 << 30, None, FAKE * 16 + 4, None)
+    assert st == E_WS
+    st = lib.race_attn_backward_ex(*([FAKE] * 7), 8, 4, 1.0, 1, 1, 1, 64, 64, BF16, 0, FAKE, FAKE,
+                                   FAKE, FAKE * 16, 1 << 30, None, FAKE * 16 + 4, None)
+    assert st == E_WS
+
+
 def test_workspace_null(lib):
     assert lib.race_attn_workspace_bytes(1, 1, 16, 64, 8, 4, 1, 0, BF16, 0, None) == E_NULL
 
