@@ -112,22 +112,24 @@ typedef struct {
     const char *name[RACE_TRACE_MAX];
 } race_trace_t;
 
-/* Size, in bytes, of the key-state buffer that race_attn_forward_ex can
- * save for race_attn_backward_ex (step 3 / zh §2.3: the per-segment prefix
- * sums of the keys' bucket statistics and the per-head totals, fp32).  0 when
- * the configuration does not use it (RACE_F32, or L > 32).  Pure host
- * function. */
+/* Size, in bytes, of the state that race_attn_forward_ex can save for
+ * race_attn_backward_ex: the per-segment prefix sums of the keys' bucket
+ * statistics with the per-head totals (step 3 / zh §2.3, fp32), and the
+ * squashed projections t of Q and K with their derivatives (steps 1-2, fp16,
+ * 512 bytes per row of Q and of K at L = 32).  0 when the configuration does
+ * not use it (RACE_F32, or L > 32).  Pure host function. */
 race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P, int causal,
                                     int chunk, race_dtype_t dt, size_t *bytes);
 
 /* race_attn_forward / race_attn_backward with optional tracing and an
- * optional saved key state.
+ * optional saved state.
  *   trace: may be NULL.
  *   saved: device pointer (256-byte aligned, race_attn_saved_bytes bytes,
- *     owned by the caller) or NULL.  The forward writes the key state there;
- *     a backward given the same buffer, for the same Q, K, V, W, tau, causal
- *     and chunk, reads it instead of recomputing it (results are identical).
- *     Ignored when race_attn_saved_bytes is 0.  A misaligned saved buffer is
+ *     owned by the caller) or NULL.  The forward writes the state there
+ *     (its outputs are the same either way); a backward given the same
+ *     buffer, for the same Q, K, V, W, tau, causal and chunk, reads it
+ *     instead of recomputing it (the gradients agree to rounding).  Ignored
+ *     when race_attn_saved_bytes is 0.  A misaligned saved buffer is
  *     RACE_ERR_WORKSPACE.
  * With trace = NULL and saved = NULL these are exactly the plain entry
  * points. */

@@ -59,10 +59,14 @@ struct Plan {
     size_t wt_bytes;   // transposed projection for the backward
     int scan_groups;   // segment groups of the two-pass scan
     size_t scan_bytes; // group totals of the scan
-    // forward layout
-    size_t f_tq, f_tk, f_st, f_scan, f_total;
-    // backward layout
-    size_t b_tq, b_tk, b_s, b_gt, b_g, b_wt, b_scan, b_total;
+    int64_t hc_tiles;  // hash-feature cache: 16-token tiles per head (bf16 path)
+    size_t hc_bytes;   // one cache array (t or dt/du' of Q or K), fp16
+    // forward layout (hc: t of K)
+    size_t f_tq, f_tk, f_st, f_hc, f_scan, f_total;
+    // backward layout (hc: t, dt/du' of K then of Q)
+    size_t b_tq, b_tk, b_s, b_gt, b_g, b_wt, b_hc, b_scan, b_total;
+    // saved buffer (bf16 path): key state, then t, dt/du' of K and of Q
+    size_t s_hc, s_total;
 };
 
 race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
@@ -106,11 +110,17 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     const int64_t groups = p->nseg / 16;
     p->scan_groups = (int)(groups < 1 ? 1 : groups > 64 ? 64 : groups);
     p->scan_bytes = align256((size_t)p->BH * p->scan_groups * p->F * race::NCOL * sizeof(float));
+    p->hc_tiles = (N + 31) / 32 * 2;
+    // per 16-token tile: 2 nw waves x 64 lanes x 4 fp16 values
+    p->hc_bytes = p->fused ? align256((size_t)p->BH * p->hc_tiles * (2 * p->nw) * 64 * 4 * 2) : 0;
     p->f_tq = 0;
     p->f_tk = p->f_tq + p->t_bytes;
     p->f_st = p->f_tk + p->t_bytes;
-    p->f_scan = p->f_st + p->st_bytes;
+    p->f_hc = p->f_st + p->st_bytes;
+    p->f_scan = p->f_hc + p->hc_bytes;
     p->f_total = p->f_scan + p->scan_bytes;
+    p->s_hc = p->st_bytes;
+    p->s_total = p->fused ? p->s_hc + 4 * p->hc_bytes : 0;
     p->b_tq = 0;
     p->b_tk = p->b_tq + p->tb_bytes;
     p->b_s = p->b_tk + p->tb_bytes;
@@ -118,7 +128,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     // the bf16 kernels read the gradient state transposed from its FxC copy
     p->b_g = p->b_gt + (p->fused ? 0 : p->st_bytes);
     p->b_wt = p->b_g + p->st_bytes;
-    p->b_scan = p->b_wt + p->wt_bytes;
+    p->b_hc = p->b_wt + p->wt_bytes;
+    p->b_scan = p->b_hc + 4 * p->hc_bytes;
     p->b_total = p->b_scan + p->scan_bytes;
     return RACE_OK;
 }
@@ -219,51 +230,57 @@ void launch_scan(const Tracer &tr, const char *name, const Plan &p, float *st, f
     tr.end();
 }
 
-// walk kernel with the squash polynomial or its direct evaluation
-template <int NW, bool CAUSAL, bool BWD, typename T>
-void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *R,
-                 const T *Wr, const race::ValSrc<T> &vs, const float *W, const Plan &p,
-                 const float *st, T *out, float *den)
+// hash-feature cache arrays (t, dt/du') at base, in units of hc_bytes
+race::HCache hcache(const Plan &p, char *base, int it, int ic)
 {
-    if constexpr (sizeof(T) == 2) {
-        if (sq.deg >= 0)
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, true>), grid, dim3(NW * 64), R, Wr,
-                   vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, out, den);
-        else
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, false>), grid, dim3(NW * 64), R,
-                   Wr, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, out, den);
-    }
+    race::HCache h;
+    h.t = it >= 0 ? reinterpret_cast<_Float16 *>(base + it * p.hc_bytes) : nullptr;
+    h.c = ic >= 0 ? reinterpret_cast<_Float16 *>(base + ic * p.hc_bytes) : nullptr;
+    h.tiles = p.hc_tiles;
+    return h;
 }
 
-// segment-sum kernel with the squash polynomial or its direct evaluation
-template <int NW, bool DVAL, int LAYOUT, typename T>
+// segment sums: hashing (SRC = 0, squash polynomial or direct) or from the cache
+template <int NW, bool DVAL, int SRC, int WR, typename T>
 void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *X,
-                const race::ValSrc<T> &vs, const float *W, const Plan &p, float *st_f, float *st_c)
+                const race::ValSrc<T> &vs, const float *W, const Plan &p, const race::HCache &cin,
+                const race::HCache &cout, float *st)
 {
     if constexpr (sizeof(T) == 2) {
-        if (sq.deg >= 0)
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, LAYOUT, true>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, sq, p.N, (int)p.seg, p.nseg, st_f, st_c);
+        if (SRC == 1 || sq.deg >= 0)
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true>), grid, dim3(NW * 64), X, vs,
+                   W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
         else
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, LAYOUT, false>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, sq, p.N, (int)p.seg, p.nseg, st_f, st_c);
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false>), grid, dim3(NW * 64), X, vs,
+                   W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
     }
 }
 
-// gradient kernel with the squash polynomial or its direct evaluation
-template <int NW, bool CAUSAL, bool REVERSE, typename T>
-void launch_grad(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *Xr,
-                 const T *Xw, const race::ValSrc<T> &vr, const race::ValSrc<T> &vw, const float *W,
-                 const Plan &p, const float *st, T *dX)
+// chunk walk: readers hashed (RSRC = 0) or from the cache, writers from the cache
+template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, typename T>
+void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *R,
+                 const race::ValSrc<T> &vs, const float *W, const Plan &p, const float *st,
+                 const race::HCache &rc, const race::HCache &wc, T *out, float *den)
 {
     if constexpr (sizeof(T) == 2) {
-        if (sq.deg >= 0)
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true>), grid, dim3(NW * 64), Xr,
-                   Xw, vr, vw, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, dX);
+        if (RSRC == 1 || sq.deg >= 0)
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true>), grid,
+                   dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
         else
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false>), grid, dim3(NW * 64), Xr,
-                   Xw, vr, vw, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, dX);
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false>), grid,
+                   dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
     }
+}
+
+template <int NW, bool CAUSAL, bool REVERSE, typename T>
+void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
+                 const race::ValSrc<T> &vr, const race::ValSrc<T> &vw, const float *W,
+                 const Plan &p, const float *st, const race::HCache &rc, const race::HCache &wc,
+                 T *dX)
+{
+    if constexpr (sizeof(T) == 2)
+        LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE>), grid, dim3(NW * 64), Xr, vr, vw,
+               W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX);
 }
 
 template <typename T, int NW>
@@ -283,12 +300,27 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
         const race::Squash sq = fit_squash(tau, RACE_BF16);
         const dim3 nblk((unsigned)(p.BH * p.nseg));
         const race::ValSrc<T> vv{V, nullptr, nullptr};
-        launch_sum<WS, false, 1>(tr, "sum_kv", nblk, sq, K, vv, W, p, st, nullptr);
-        launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
-        if (causal)
-            launch_walk<WW, true, false>(tr, "fwd_o", nblk, sq, Q, K, vv, W, p, st, O, den);
+        // hash features: K (t) in the workspace, or K and Q (t, dt/du') in the saved buffer
+        char *sb = reinterpret_cast<char *>(saved);
+        const race::HCache hk = saved ? hcache(p, sb + p.s_hc, 0, 1) : hcache(p, ws + p.f_hc, 0, -1);
+        const race::HCache hq = saved ? hcache(p, sb + p.s_hc, 2, 3) : hcache(p, nullptr, -1, -1);
+        const race::HCache none = hcache(p, nullptr, -1, -1);
+        if (saved)
+            launch_sum<WS, false, 0, 3>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
         else
-            launch_walk<WW, false, false>(tr, "fwd_o", nblk, sq, Q, K, vv, W, p, st, O, den);
+            launch_sum<WS, false, 0, 1>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
+        launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
+        if (causal) {
+            if (saved)
+                launch_walk<WW, true, false, 0, 3>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+            else
+                launch_walk<WW, true, false, 0, 0>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+        } else {
+            if (saved)
+                launch_walk<WW, false, false, 0, 3>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+            else
+                launch_walk<WW, false, false, 0, 0>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+        }
         return;
     }
     LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
@@ -328,20 +360,31 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
         const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
         const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
         const dim3 nblk((unsigned)(p.BH * p.nseg));
-        // key state S (FxC, read transposed by dQ): prefix over segments, or
-        // the forward's copy
-        const float *sK = saved;
-        if (!sK) {
-            launch_sum<WS, false, 1>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, sS, nullptr);
+        // key state S (FxC, read transposed by dQ) and the hash features of K
+        // and Q (t, dt/du'): the forward's saved copies, or recomputed
+        const float *sK;
+        race::HCache hk, hq;
+        const race::HCache none = hcache(p, nullptr, -1, -1);
+        if (saved) {
+            const char *sb = reinterpret_cast<const char *>(saved);
+            sK = saved;
+            hk = hcache(p, const_cast<char *>(sb) + p.s_hc, 0, 1);
+            hq = hcache(p, const_cast<char *>(sb) + p.s_hc, 2, 3);
+            // gradient state G (FxC; read transposed by dK): suffix over segments
+            launch_sum<WS, true, 1, 0>(tr, "sum_qd", nblk, sq, Q, vd, W, p, hq, none, sG);
+        } else {
+            hk = hcache(p, ws + p.b_hc, 0, 1);
+            hq = hcache(p, ws + p.b_hc, 2, 3);
+            launch_sum<WS, false, 0, 3>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, none, hk, sS);
             launch_scan(tr, "scan_kv_t", p, sS, scan_tmp, 0);
             sK = sS;
+            launch_sum<WS, true, 0, 3>(tr, "sum_qd", nblk, sq, Q, vd, W, p, none, hq, sG);
         }
-        // gradient state G (FxC for dV and CxF for dK): suffix over segments
-        launch_sum<WS, true, 1>(tr, "sum_qd", nblk, sq, Q, vd, W, p, sG, nullptr);
         launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
-        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, sq, Q, K, vd, vv, W, p, sK, dQ);
-        launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, sq, K, Q, vv, vd, W, p, sG, dK);
-        launch_walk<WW, CAUSAL != 0, true>(tr, "dv", nblk, sq, K, Q, vd, W, p, sG, dV, nullptr);
+        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, Q, vd, vv, W, p, sK, hq, hk, dQ);
+        launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, K, vv, vd, W, p, sG, hk, hq, dK);
+        launch_walk<WW, CAUSAL != 0, true, 1, 0>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV,
+                                                 nullptr);
         return;
     }
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,
@@ -466,7 +509,7 @@ race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P
     Plan p;
     const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
-    *bytes = p.fused ? p.st_bytes : 0;
+    *bytes = p.s_total;
     return RACE_OK;
 }
 

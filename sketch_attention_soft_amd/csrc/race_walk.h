@@ -9,8 +9,12 @@
 // Staging.  Each chunk of 32 tokens is loaded once per workgroup: every
 // thread fetches one 16-byte piece of a row (the next chunk's, while the
 // current one is computed) and writes it to LDS, where the eight threads of a
-// row also form its squared norm (dot2 + DPP).  Value rows go to LDS column
-// by column, so that any wave reads them as MFMA operands over tokens.
+// row also form its squared norm.  Value rows go to LDS column by column (and
+// row by row where needed), so that any wave reads them as MFMA operands.
+//
+// Hash-feature cache.  Each row is hashed once per pass: the kernel that
+// hashes it stores t = tanh(tanh(u')/tau) (and dt/du') in fp16 in the
+// kernels' register layout, and later kernels read it instead of hashing.
 //
 // Per wave (4 tables = 16 hyperplanes = 64 features, all in registers):
 //   U^T = W x^T (MFMA, W = W_hi + W_lo) -> lane (table g, token c16) holds
@@ -281,6 +285,49 @@ __device__ __forceinline__ float squash_k(float u, float kf, const Squash &sq)
     return copysignf(h, u);
 }
 
+// 0/1 selection operand: column rho of FxC row-tile s takes token-major slot
+// (g = rho / 4, i = 4 (s & 1) + rho % 4) of K-block s / 2.
+__device__ __forceinline__ bf16x8 selection(int par)
+{
+    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+    bf16x8 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (bf16)((g == (c16 >> 2) && i == 4 * par + (c16 & 3)) ? 1.f : 0.f);
+    return f;
+}
+
+// W rows (hi, lo) of all waves staged once per workgroup, wl[2][NW * 16][XRS],
+// and the two selection operands sl[2][64 lanes][8]
+template <int NW>
+__device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int LP, bf16 *wl, bf16 *sl)
+{
+    for (int e = threadIdx.x; e < NW * 16 * HD; e += NW * 64) {
+        const int hp = e / HD, c = e % HD;
+        const float v = hp < LP ? W[hp * HD + c] : 0.f;
+        const bf16 hi = (bf16)v;
+        wl[hp * XRS + c] = hi;
+        wl[(NW * 16 + hp) * XRS + c] = (bf16)(v - (float)hi);
+    }
+    if (threadIdx.x < 64) {
+        *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
+        *reinterpret_cast<bf16x8 *>(sl + (64 + threadIdx.x) * 8) = selection(1);
+    }
+}
+template <int NW> __device__ __forceinline__ void wrows_lds(const bf16 *wl, WRows &wr)
+{
+    const int lane = lane_id(), g = lane >> 4, hp = wave_id() * 16 + (lane & 15);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        wr.hi[kb] = *reinterpret_cast<const bf16x8 *>(wl + hp * XRS + kb * 32 + g * 8);
+        wr.lo[kb] = *reinterpret_cast<const bf16x8 *>(wl + (NW * 16 + hp) * XRS + kb * 32 + g * 8);
+    }
+}
+__device__ __forceinline__ void sel_lds(const bf16 *sl, bf16x8 (&sel)[2])
+{
+    sel[0] = *reinterpret_cast<const bf16x8 *>(sl + lane_id() * 8);
+    sel[1] = *reinterpret_cast<const bf16x8 *>(sl + (64 + lane_id()) * 8);
+}
+
 // t of tables 4w + g (lane (g, c16)) for token 16 tt + c16 of staged set xb
 template <bool POLY>
 __device__ __forceinline__ floatx4 hash_staged(const bf16 *xb, const float *kb, int tt, const WRows &wr,
@@ -302,6 +349,43 @@ __device__ __forceinline__ floatx4 hash_staged(const bf16 *xb, const float *kb, 
     return t;
 }
 
+// t and dt/du' for the readers of the gradient kernel (u' = u / |x|):
+// dt/du' = ((1 - t^2) / tau) (1 - z^2), z = tanh(|u'|), 1 - z^2 = 4e / (1 + e)^2
+template <bool POLY>
+__device__ __forceinline__ void hash_staged_chain(const bf16 *xb, const float *kb, int tt, const WRows &wr,
+                                                  const Squash &sq, floatx4 &t, floatx4 &c)
+{
+    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+    const int row = tt * 16 + c16;
+    const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + g * 8);
+    const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + 32 + g * 8);
+    floatx4 u = {0.f, 0.f, 0.f, 0.f};
+    mma32(u, wr.hi[0], x0);
+    mma32(u, wr.lo[0], x0);
+    mma32(u, wr.hi[1], x1);
+    mma32(u, wr.lo[1], x1);
+    const float kf = kb[row];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float e = __builtin_amdgcn_exp2f(fabsf(u[p]) * kf);
+        float h;
+        if constexpr (POLY) {
+            constexpr int DEG = SqDeg<bf16>::v;
+            const float y = fmaf(2.f, e, -1.f);
+            h = sq.c[DEG];
+#pragma unroll
+            for (int k = DEG - 1; k >= 0; --k) h = fmaf(h, y, sq.c[k]);
+        } else {
+            const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+            const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
+            h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
+        }
+        const float r = __builtin_amdgcn_rcpf(1.f + e);
+        c[p] = (1.f - h * h) * (4.f * sq.inv_tau) * e * r * r;
+        t[p] = copysignf(h, u[p]);
+    }
+}
+
 // token-major Walsh features of one table: lo = S 0..7, hi = S 8..15
 // (q4 = 1/4, or 0 for padding tables)
 __device__ __forceinline__ void walsh_tm(const floatx4 &t, float q4, bf16x8 &lo, bf16x8 &hi)
@@ -311,17 +395,6 @@ __device__ __forceinline__ void walsh_tm(const floatx4 &t, float q4, bf16x8 &lo,
              pk_bf16(a2 * t[2], a3 * t[2]));
     hi = pk8(pk_bf16(q4 * t[3], a1 * t[3]), pk_bf16(a2 * t[3], a3 * t[3]), pk_bf16(q4 * b3, a1 * b3),
              pk_bf16(a2 * b3, a3 * b3));
-}
-
-// 0/1 selection operand: column rho of FxC row-tile s takes token-major slot
-// (g = rho / 4, i = 4 (s & 1) + rho % 4) of K-block s / 2.
-__device__ __forceinline__ bf16x8 selection(int par)
-{
-    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-    bf16x8 f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (bf16)((g == (c16 >> 2) && i == 4 * par + (c16 & 3)) ? 1.f : 0.f);
-    return f;
 }
 
 // feature-major fragments of the 4 FxC row tiles over the chunk's 32 tokens
@@ -351,6 +424,177 @@ __device__ __forceinline__ bf16x8 ycol_frag(const bf16 *yc, int col)
     return cat8(a, b);
 }
 
+// CxF register tiles of a state stored as FxC blocks [wave][s][ct][lane][4]:
+// CxF (s, ct) lane (g, c16) reg r = column 16 ct + 4g + r of feature row c16.
+__device__ __forceinline__ void load_state_cxf(const float *__restrict__ src, floatx4 (&acc)[4][NT])
+{
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[s][ct][r] = src[(((w * 4 + s) * NT + ct) * 64 + (c16 >> 2) * 16 + 4 * g + r) * 4 + (c16 & 3)];
+}
+
+// value-row operand of 16 tokens (token-major): columns 32k + 4g + r (slots
+// r < 4) and 32k + 16 + 4g + r (slots 4 + r), k = 0, 1; plus columns 64 + 4g + r
+__device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)[2], bf16x4 &f4)
+{
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        f8[k] = cat8(*reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 4 * g),
+                     *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 16 + 4 * g));
+    f4 = *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 64 + 4 * g);
+}
+
+
+// ---------------------------------------------------------------------------
+// Hash-feature cache: fp16 t (and dt/du') of every row, in the kernels'
+// register layout [head][token tile of 16][wave][lane][4]: lane (g, c16) of
+// wave w holds the 4 values of table 4w + g for token 16 * tile + c16.
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+struct HCache {
+    _Float16 *t;    // t values (null: not stored / not read)
+    _Float16 *c;    // dt/du' values (null: not stored / not read)
+    int64_t tiles;  // token tiles per head (2 per 32-token chunk)
+};
+
+template <int NW>
+__device__ __forceinline__ int64_t hc_off(const HCache &h, int64_t bh, int64_t tile)
+{
+    return (((bh * h.tiles + tile) * NW + wave_id()) * 64 + lane_id()) * 4;
+}
+__device__ __forceinline__ halfx4 to_h4(const floatx4 &v)
+{
+    const halfx4 r = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    return r;
+}
+__device__ __forceinline__ floatx4 to_f4(const halfx4 &v)
+{
+    const floatx4 r = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    return r;
+}
+
+// cached values of the two 16-token tiles of the chunk at tok0
+template <int NW>
+__device__ __forceinline__ void hc_load(const _Float16 *__restrict__ p, const HCache &h, int64_t bh,
+                                        int64_t tok0, halfx4 (&v)[2])
+{
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) v[tt] = *reinterpret_cast<const halfx4 *>(p + hc_off<NW>(h, bh, tok0 / 16 + tt));
+}
+
+// ---------------------------------------------------------------------------
+// sum_kernel: S_g = sum_{j in segment g} psi(x_j)^T y_j over the segment's
+// writer rows (FxC state blocks [wave][s][ct][lane][4]).
+//   SRC = 0: the rows X are hashed here; WR bit 0 / bit 1 store their t /
+//            dt/du' into the cache `co`.
+//   SRC = 1: t comes from the cache `ci_` (X is not read).
+template <int NW, bool DVAL, int SRC, int WR, bool POLY>
+__global__ __launch_bounds__(NW * 64) void sum_kernel(
+    const bf16 *__restrict__ X, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
+    int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st)
+{
+    constexpr int NTHR = NW * 64;
+    constexpr bool HASH = SRC == 0;
+    // double-buffered: chunk c is hashed and summed while chunk c + 1 is staged
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][HASH ? WCT * XRS : 8];
+    __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
+    __shared__ __attribute__((aligned(16))) bf16 ycol[2][NCOL * YCS];
+
+    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4;
+    const bf16 *Xh = X + bh * N * HD;
+    ValSrc<bf16> vh = vsrc;
+    vh.V += bh * N * HD;
+    if (DVAL) {
+        vh.O += bh * N * HD;
+        vh.den += bh * N;
+    }
+    WRows wr;
+    if (HASH) load_wrows(W, L * NP, wr);
+    const bf16x8 sel[2] = {selection(0), selection(1)};
+    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    floatx4 af[4][NT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) af[s][ct] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
+    XStage<NTHR, 1> xs;
+    YStage<NTHR, DVAL> ys;
+    halfx4 tc[2];
+    ystage_zero_pad<NTHR>(ycol[0]);
+    ystage_zero_pad<NTHR>(ycol[1]);
+    ystage_load<NTHR, DVAL>(vh, t_begin, t_end, ys);
+    if (HASH) {
+        xstage_load<NTHR, 1>(Xh, Xh, t_begin, t_end, xs);
+        xstage_store<NTHR, 1>(xs, xbuf[0], kbuf[0]);
+    } else {
+        hc_load<NW>(ci_.t, ci_, bh, t_begin, tc);
+    }
+    ystage_store<NTHR, DVAL>(ys, t_begin, t_end, ycol[0]);
+    if (nch > 1) {
+        if (HASH) xstage_load<NTHR, 1>(Xh, Xh, t_begin + WCT, t_end, xs);
+        ystage_load<NTHR, DVAL>(vh, t_begin + WCT, t_end, ys);
+    }
+    lds_barrier();
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int b = ci & 1;
+        const int64_t tok0 = t_begin + ci * WCT;
+        bf16x8 ptm[2][2], pfm[4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            floatx4 t;
+            if constexpr (HASH) {
+                const int64_t o = hc_off<NW>(co, bh, tok0 / 16 + tt);
+                if constexpr ((WR & 2) != 0) {
+                    floatx4 c;
+                    hash_staged_chain<POLY>(xbuf[b], kbuf[b], tt, wr, sq, t, c);
+                    *reinterpret_cast<halfx4 *>(co.c + o) = to_h4(c);
+                } else {
+                    t = hash_staged<POLY>(xbuf[b], kbuf[b], tt, wr, sq);
+                }
+                if constexpr ((WR & 1) != 0) *reinterpret_cast<halfx4 *>(co.t + o) = to_h4(t);
+            } else {
+                t = to_f4(tc[tt]);
+            }
+            walsh_tm(t, q4, ptm[tt][0], ptm[tt][1]);
+        }
+        if (ci + 1 < nch) {  // the other buffers were last read before the previous barrier
+            const int64_t nx = tok0 + WCT;
+            if (HASH) {
+                xstage_store<NTHR, 1>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+                if (ci + 2 < nch) xstage_load<NTHR, 1>(Xh, Xh, nx + WCT, t_end, xs);
+            } else {
+                hc_load<NW>(ci_.t, ci_, bh, nx, tc);
+            }
+            ystage_store<NTHR, DVAL>(ys, nx, t_end, ycol[b ^ 1]);
+            if (ci + 2 < nch) ystage_load<NTHR, DVAL>(vh, nx + WCT, t_end, ys);
+        }
+        feat_major(ptm, sel, pfm);
+        // tokens past t_end have psi_0 = 1/4 but zero value rows
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + (lane & 15));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mma32(af[s][ct], pfm[s], yb);
+        }
+        lds_barrier();
+    }
+    const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 64 * NCOL);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+            *reinterpret_cast<floatx4 *>(st + blk + st_idx(w, s, ct, lane, 4)) = af[s][ct];
+}
+
 // ---------------------------------------------------------------------------
 // walk_kernel: reader rows read an FxC state built from writer rows, in
 // chunks of 32 tokens, NW waves of 4 tables each.
@@ -358,26 +602,29 @@ __device__ __forceinline__ bf16x8 ycol_frag(const bf16 *yc, int col)
 //                intra mask j <= i; output O = n / m and den = m.
 //   BWD = true:  readers = keys, writers = queries, y = [dO/m | dm]; reverse
 //                order; intra mask j >= i; output dV = n[:, :d].
-template <int NW, bool CAUSAL, bool BWD, bool POLY>
+//   Readers: RSRC = 0 hashes the rows R (RWR bit 0 / 1 store t / dt/du' into
+//   the cache rc); RSRC = 1 reads t from rc.  Writers: t from the cache wc.
+template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
-    const bf16 *__restrict__ R, const bf16 *__restrict__ Wr, ValSrc<bf16> vsrc,
-    const float *__restrict__ W, int L, Squash sq, int64_t N, int seg, int64_t nseg,
-    const float *__restrict__ st, bf16 *__restrict__ Out, float *__restrict__ den)
+    const bf16 *__restrict__ R, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
+    int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
+    bf16 *__restrict__ Out, float *__restrict__ den)
 {
     constexpr int NTHR = NW * 64;
-    constexpr int NS = CAUSAL ? 2 : 1;
+    constexpr bool HASH = RSRC == 0;
     constexpr int RSLOTS = 2 * 4 * 64;  // (tile, column tile < 4, lane) partial-output slots
     constexpr int RIT = (RSLOTS + NTHR - 1) / NTHR;
-    __shared__ __attribute__((aligned(16))) bf16 xbuf[NS * WCT * XRS];
-    __shared__ __attribute__((aligned(16))) float kbuf[NS * WCT];
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[HASH ? WCT * XRS : 8];
+    __shared__ __attribute__((aligned(16))) float kbuf[WCT];
     __shared__ __attribute__((aligned(16))) bf16 ycol[CAUSAL ? NCOL * YCS : 8];
     __shared__ __attribute__((aligned(16))) float red[NW * 2 * NT * 64 * 4];
     __shared__ __attribute__((aligned(16))) float mbuf[WCT];
+    __shared__ __attribute__((aligned(16))) bf16 wl[HASH ? 2 * NW * 16 * XRS : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     const bf16 *Rh = R + bh * N * HD;
-    const bf16 *Wh = Wr + bh * N * HD;
     ValSrc<bf16> vh = vsrc;
     vh.V += bh * N * HD;
     if (BWD) {
@@ -387,9 +634,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     bf16 *Oh = Out + bh * N * HD;
     float *denh = BWD ? nullptr : den + bh * N;
 
-    WRows wr;
-    load_wrows(W, L * NP, wr);
-    bf16x8 sel[2] = {selection(0), selection(1)};
+    stage_wrows<NW>(W, L * NP, wl, sl);
     const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
     floatx4 acc[4][NT];
     {
@@ -404,15 +649,21 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
     auto chunk0 = [&](int64_t ci) { return t_begin + (BWD ? nch - 1 - ci : ci) * WCT; };
 
-    XStage<NTHR, NS> xs;
+    XStage<NTHR, 1> xs;
     YStage<NTHR, BWD> ys;
+    halfx4 rt[2], wt[2];
     if (CAUSAL) {
         ystage_zero_pad<NTHR>(ycol);
         ystage_load<NTHR, BWD>(vh, chunk0(0), t_end, ys);
+        hc_load<NW>(wc.t, wc, bh, chunk0(0), wt);
     }
-    xstage_load<NTHR, NS>(Rh, Wh, chunk0(0), t_end, xs);
-    xstage_store<NTHR, NS>(xs, xbuf, kbuf);
-    if (nch > 1) xstage_load<NTHR, NS>(Rh, Wh, chunk0(1), t_end, xs);
+    if (HASH) {
+        xstage_load<NTHR, 1>(Rh, Rh, chunk0(0), t_end, xs);
+        xstage_store<NTHR, 1>(xs, xbuf, kbuf);
+        if (nch > 1) xstage_load<NTHR, 1>(Rh, Rh, chunk0(1), t_end, xs);
+    } else {
+        hc_load<NW>(rc.t, rc, bh, chunk0(0), rt);
+    }
     lds_barrier();
 
     float nsum[RIT][4];
@@ -423,22 +674,36 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             ystage_store<NTHR, BWD>(ys, tok0, t_end, ycol);
             if (ci + 1 < nch) ystage_load<NTHR, BWD>(vh, chunk0(ci + 1), t_end, ys);
         }
-        // hash and Walsh features of this chunk's readers and writers
+        // Walsh features of this chunk's readers and writers
         bf16x8 pr[2][2], pfm[4];
         bf16x4 kA4;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
         bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
+        WRows wr;
+        if (HASH) wrows_lds<NW>(wl, wr);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const floatx4 t = hash_staged<POLY>(xbuf, kbuf, tt, wr, sq);
+            floatx4 t;
+            if constexpr (HASH) {
+                const int64_t o = hc_off<NW>(rc, bh, tok0 / 16 + tt);
+                if constexpr ((RWR & 2) != 0) {
+                    floatx4 c;
+                    hash_staged_chain<POLY>(xbuf, kbuf, tt, wr, sq, t, c);
+                    *reinterpret_cast<halfx4 *>(rc.c + o) = to_h4(c);
+                } else {
+                    t = hash_staged<POLY>(xbuf, kbuf, tt, wr, sq);
+                }
+                if constexpr ((RWR & 1) != 0) *reinterpret_cast<halfx4 *>(rc.t + o) = to_h4(t);
+            } else {
+                t = to_f4(rt[tt]);
+            }
             walsh_tm(t, q4, pr[tt][0], pr[tt][1]);
         }
+        if (!HASH && ci + 1 < nch) hc_load<NW>(rc.t, rc, bh, chunk0(ci + 1), rt);
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const floatx4 t = hash_staged<POLY>(xbuf + WCT * XRS, kbuf + WCT, tt, wr, sq);
-                walsh_tm(t, q4, pw[tt][0], pw[tt][1]);
-            }
+            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
+            if (ci + 1 < nch) hc_load<NW>(wc.t, wc, bh, chunk0(ci + 1), wt);
             // scores^T tiles D[j][i] = psi_w(j) . psi_r(i) over this wave's tables
             constexpr int TJ[3] = {0, BWD ? 1 : 0, 1}, TI[3] = {0, BWD ? 0 : 1, 1};
             floatx4 sc[3];
@@ -463,6 +728,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 kA4 = acc2bf4(sc[0]);                        // reader tile 0: writer tile 0
                 kA8 = cat8(acc2bf4(sc[1]), acc2bf4(sc[2]));  // reader tile 1: writer tiles 0, 1
             }
+            bf16x8 sel[2];
+            sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
         lds_barrier();  // #1: value columns of this chunk staged, m of the previous one reduced
@@ -482,9 +749,9 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 }
             }
         }
-        if (ci + 1 < nch) {  // the next chunk's rows (xbuf is not read again in this chunk)
-            xstage_store<NTHR, NS>(xs, xbuf, kbuf);
-            if (ci + 2 < nch) xstage_load<NTHR, NS>(Rh, Wh, chunk0(ci + 2), t_end, xs);
+        if (HASH && ci + 1 < nch) {  // the next chunk's rows (xbuf is not read again in this chunk)
+            xstage_store<NTHR, 1>(xs, xbuf, kbuf);
+            if (ci + 2 < nch) xstage_load<NTHR, 1>(Rh, Rh, chunk0(ci + 2), t_end, xs);
         }
         floatx4 oacc[2][NT];
 #pragma unroll
@@ -494,12 +761,13 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             // inter-chunk readout with the state before this chunk
+            bf16x8 sf[2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const bf16x8 sf = cat8(acc2bf4(acc[2 * k][ct]), acc2bf4(acc[2 * k + 1][ct]));
+            for (int k = 0; k < 2; ++k) sf[k] = cat8(acc2bf4(acc[2 * k][ct]), acc2bf4(acc[2 * k + 1][ct]));
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], pr[tt][k], sf);
-            }
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], pr[tt][k], sf[k]);
             if (CAUSAL) {
                 const bf16x8 yb = ycol_frag(ycol, ct * 16 + c16);
                 if (BWD) {
@@ -573,216 +841,6 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     }
 }
 
-}  // namespace race
-
-namespace race {
-
-// ---------------------------------------------------------------------------
-// sum_kernel: S_g = sum_{j in segment g} psi(x_j)^T y_j over the segment's
-// writer rows, NW waves of 4 tables each.
-// LAYOUT bit 0: FxC state into st_f, bit 1: CxF state into st_c (same
-// [wave][s][ct][lane][4] blocks; CxF tile (s, ct): lane (rows = value
-// columns 16 ct + 4g + r, column = feature row rho = c16 of tile s)).
-template <int NW, bool DVAL, int LAYOUT, bool POLY>
-__global__ __launch_bounds__(NW * 64) void sum_kernel(
-    const bf16 *__restrict__ X, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
-    int64_t N, int seg, int64_t nseg, float *__restrict__ st_f, float *__restrict__ st_c)
-{
-    constexpr int NTHR = NW * 64;
-    constexpr bool FXC = LAYOUT & 1, CXF = LAYOUT & 2;
-    // double-buffered: chunk c is hashed and summed while chunk c + 1 is staged
-    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][WCT * XRS];
-    __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
-    __shared__ __attribute__((aligned(16))) bf16 ycol[2][NCOL * YCS];
-
-    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
-    const int lane = lane_id(), w = wave_id(), g = lane >> 4;
-    const bf16 *Xh = X + bh * N * HD;
-    ValSrc<bf16> vh = vsrc;
-    vh.V += bh * N * HD;
-    if (DVAL) {
-        vh.O += bh * N * HD;
-        vh.den += bh * N;
-    }
-    WRows wr;
-    load_wrows(W, L * NP, wr);
-    const bf16x8 sel[2] = {selection(0), selection(1)};
-    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
-    floatx4 af[FXC ? 4 : 1][NT], ac[CXF ? 4 : 1][NT];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            if (FXC) af[s][ct] = {0.f, 0.f, 0.f, 0.f};
-            if (CXF) ac[s][ct] = {0.f, 0.f, 0.f, 0.f};
-        }
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
-    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
-    XStage<NTHR, 1> xs;
-    YStage<NTHR, DVAL> ys;
-    ystage_zero_pad<NTHR>(ycol[0]);
-    ystage_zero_pad<NTHR>(ycol[1]);
-    xstage_load<NTHR, 1>(Xh, Xh, t_begin, t_end, xs);
-    ystage_load<NTHR, DVAL>(vh, t_begin, t_end, ys);
-    xstage_store<NTHR, 1>(xs, xbuf[0], kbuf[0]);
-    ystage_store<NTHR, DVAL>(ys, t_begin, t_end, ycol[0]);
-    if (nch > 1) {
-        xstage_load<NTHR, 1>(Xh, Xh, t_begin + WCT, t_end, xs);
-        ystage_load<NTHR, DVAL>(vh, t_begin + WCT, t_end, ys);
-    }
-    lds_barrier();
-    for (int64_t ci = 0; ci < nch; ++ci) {
-        const int b = ci & 1;
-        bf16x8 ptm[2][2], pfm[4];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const floatx4 t = hash_staged<POLY>(xbuf[b], kbuf[b], tt, wr, sq);
-            walsh_tm(t, q4, ptm[tt][0], ptm[tt][1]);
-        }
-        if (ci + 1 < nch) {  // the other buffers were last read before the previous barrier
-            const int64_t nx = t_begin + (ci + 1) * WCT;
-            xstage_store<NTHR, 1>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            ystage_store<NTHR, DVAL>(ys, nx, t_end, ycol[b ^ 1]);
-            if (ci + 2 < nch) {
-                xstage_load<NTHR, 1>(Xh, Xh, nx + WCT, t_end, xs);
-                ystage_load<NTHR, DVAL>(vh, nx + WCT, t_end, ys);
-            }
-        }
-        feat_major(ptm, sel, pfm);
-        // tokens past t_end have psi_0 = 1/4 but zero value rows
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + (lane & 15));
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (FXC) mma32(af[s][ct], pfm[s], yb);
-                if (CXF) mma32(ac[s][ct], yb, pfm[s]);
-            }
-        }
-        lds_barrier();
-    }
-    const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 64 * NCOL);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            const int64_t o = blk + st_idx(w, s, ct, lane, 4);
-            if (FXC) *reinterpret_cast<floatx4 *>(st_f + o) = af[s][ct];
-            if (CXF) *reinterpret_cast<floatx4 *>(st_c + o) = ac[s][ct];
-        }
-}
-
-}  // namespace race
-
-namespace race {
-
-// W rows split into bf16 hi + lo, staged once per workgroup: wl[2][hp][XRS]
-// (hyperplanes >= L P are zero); selection operands sl[2][64 lanes][8].
-constexpr int WLR = 128;  // hyperplane rows (L <= 32)
-
-template <int NTHR>
-__device__ __forceinline__ void stage_w(const float *__restrict__ W, int LP, int rows, bf16 *wl, bf16 *sl)
-{
-    for (int e = threadIdx.x; e < rows * HD; e += NTHR) {
-        const int hp = e / HD, c = e % HD;
-        const float v = hp < LP ? W[hp * HD + c] : 0.f;
-        const bf16 hi = (bf16)v;
-        wl[hp * XRS + c] = hi;
-        wl[(rows + hp) * XRS + c] = (bf16)(v - (float)hi);
-    }
-    if (threadIdx.x < 64) {
-        *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
-        *reinterpret_cast<bf16x8 *>(sl + (64 + threadIdx.x) * 8) = selection(1);
-    }
-}
-
-// this wave's projection rows from the staged W (A operand of U^T = W x^T)
-__device__ __forceinline__ void wrows_lds(const bf16 *wl, int rows, WRows &wr)
-{
-    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    const int hp = w * 16 + c16;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        wr.hi[kb] = *reinterpret_cast<const bf16x8 *>(wl + hp * XRS + kb * 32 + g * 8);
-        wr.lo[kb] = *reinterpret_cast<const bf16x8 *>(wl + (rows + hp) * XRS + kb * 32 + g * 8);
-    }
-}
-
-// W^T operand of dxh^T = W^T du^T for dimension tile nt: lane (dim 16 nt + c16, hyperplanes 4g + p)
-__device__ __forceinline__ void wcols_lds(const bf16 *wl, int rows, int nt, bf16x4 &hi, bf16x4 &lo)
-{
-    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int hp = w * 16 + 4 * g + p;
-        hi[p] = wl[hp * XRS + nt * 16 + c16];
-        lo[p] = wl[(rows + hp) * XRS + nt * 16 + c16];
-    }
-}
-
-// t and dt/du' for the readers of the gradient kernel (u' = u / |x|):
-// dt/du' = ((1 - t^2) / tau) (1 - z^2), z = tanh(|u'|), 1 - z^2 = 4e / (1 + e)^2
-template <bool POLY>
-__device__ __forceinline__ void hash_staged_chain(const bf16 *xb, const float *kb, int tt, const WRows &wr,
-                                                  const Squash &sq, floatx4 &t, floatx4 &c)
-{
-    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-    const int row = tt * 16 + c16;
-    const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + g * 8);
-    const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + 32 + g * 8);
-    floatx4 u = {0.f, 0.f, 0.f, 0.f};
-    mma32(u, wr.hi[0], x0);
-    mma32(u, wr.lo[0], x0);
-    mma32(u, wr.hi[1], x1);
-    mma32(u, wr.lo[1], x1);
-    const float kf = kb[row];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float e = __builtin_amdgcn_exp2f(fabsf(u[p]) * kf);
-        float h;
-        if constexpr (POLY) {
-            constexpr int DEG = SqDeg<bf16>::v;
-            const float y = fmaf(2.f, e, -1.f);
-            h = sq.c[DEG];
-#pragma unroll
-            for (int k = DEG - 1; k >= 0; --k) h = fmaf(h, y, sq.c[k]);
-        } else {
-            const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-            const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
-            h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
-        }
-        const float r = __builtin_amdgcn_rcpf(1.f + e);
-        c[p] = (1.f - h * h) * (4.f * sq.inv_tau) * e * r * r;
-        t[p] = copysignf(h, u[p]);
-    }
-}
-
-// CxF register tiles of a state stored as FxC blocks [wave][s][ct][lane][4]:
-// CxF (s, ct) lane (g, c16) reg r = column 16 ct + 4g + r of feature row c16.
-__device__ __forceinline__ void load_state_cxf(const float *__restrict__ src, floatx4 (&acc)[4][NT])
-{
-    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[s][ct][r] = src[(((w * 4 + s) * NT + ct) * 64 + (c16 >> 2) * 16 + 4 * g + r) * 4 + (c16 & 3)];
-}
-
-// value-row operand of 16 tokens (token-major): columns 32k + 4g + r (slots
-// r < 4) and 32k + 16 + 4g + r (slots 4 + r), k = 0, 1; plus columns 64 + 4g + r
-__device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)[2], bf16x4 &f4)
-{
-    const int g = lane_id() >> 4;
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-        f8[k] = cat8(*reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 4 * g),
-                     *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 16 + 4 * g));
-    f4 = *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 64 + 4 * g);
-}
-
 // ---------------------------------------------------------------------------
 // grad_kernel: gradient of the reader rows, which read a state built from the
 // writer rows, and back through the readers' hash.
@@ -790,34 +848,35 @@ __device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)
 //       writers = keys with values [v | 1]; token order; mask j <= i.
 //   dK (REVERSE = true): readers = keys with values [v | 1], writers =
 //       queries with values D; reverse order; mask j >= i.
+// Reader t and dt/du' come from the cache rc, writer t from wc; the raw
+// reader rows are staged for the normalisation backward.
 // Per chunk: dpsi_r(i)[f] = sum_c S[f][c] y_r(i)[c] + sum_j E[i][j] psi_w(j)[f]
 // with E[i][j] = y_r(i) . y_w(j) (masked), computed transposed (rows f) so
 // that a lane holds all 16 features of its table; S += psi_w^T y_w; then the
 // Walsh gradient, du = dt dt/du', dxh = du W and the normalisation backward.
-template <int NW, bool CAUSAL, bool REVERSE, bool POLY>
+template <int NW, bool CAUSAL, bool REVERSE>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
-    const bf16 *__restrict__ Xr, const bf16 *__restrict__ Xw, ValSrc<bf16> vr_src,
-    ValSrc<bf16> vw_src, const float *__restrict__ W, int L, Squash sq, int64_t N, int seg,
-    int64_t nseg, const float *__restrict__ st, bf16 *__restrict__ dX)
+    const bf16 *__restrict__ Xr, ValSrc<bf16> vr_src, ValSrc<bf16> vw_src,
+    const float *__restrict__ W, int L, int64_t N, int seg, int64_t nseg,
+    const float *__restrict__ st, HCache rc, HCache wc, bf16 *__restrict__ dX)
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
     constexpr int NTHR = NW * 64;
-    constexpr int NS = CAUSAL ? 2 : 1;
     constexpr int DXS = HD + 4;  // dxh partial row stride (floats)
     constexpr int NIT = (WCT * 16 + NTHR - 1) / NTHR;
-    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][NS * WCT * XRS];
-    __shared__ __attribute__((aligned(16))) float kbuf[2][NS * WCT];
+    constexpr int WTS = NW * 16 + 8;  // staged W^T row stride
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][WCT * XRS];
+    __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
     __shared__ __attribute__((aligned(16))) bf16 yrow_r[WCT * YRS];
     __shared__ __attribute__((aligned(16))) bf16 yrow_w[CAUSAL ? WCT * YRS : 8];
     __shared__ __attribute__((aligned(16))) bf16 ycol_w[CAUSAL ? NCOL * YCS : 8];
     __shared__ __attribute__((aligned(16))) float dxp[NW * WCT * DXS];
-    __shared__ __attribute__((aligned(16))) bf16 wl[2 * NW * 16 * XRS];
+    __shared__ __attribute__((aligned(16))) bf16 wt_l[2 * HD * WTS];  // W^T hi, lo: [dim][hyperplane]
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     const bf16 *Rh = Xr + bh * N * HD;
-    const bf16 *Wh = Xw + bh * N * HD;
     ValSrc<bf16> vrh = vr_src, vwh = vw_src;
     vrh.V += bh * N * HD;
     vwh.V += bh * N * HD;
@@ -830,8 +889,18 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     }
     bf16 *dXh = dX + bh * N * HD;
 
-    constexpr int WROWS = NW * 16;
-    stage_w<NTHR>(W, L * NP, WROWS, wl, sl);
+    // W^T (hi, lo) and the selection operands, once per workgroup
+    for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
+        const int hp = e / HD, c = e % HD;
+        const float v = hp < L * NP ? W[hp * HD + c] : 0.f;
+        const bf16 hi = (bf16)v;
+        wt_l[c * WTS + hp] = hi;
+        wt_l[(HD + c) * WTS + hp] = (bf16)(v - (float)hi);
+    }
+    if (threadIdx.x < 64) {
+        *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
+        *reinterpret_cast<bf16x8 *>(sl + (64 + threadIdx.x) * 8) = selection(1);
+    }
     const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
@@ -840,19 +909,23 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
     auto chunk0 = [&](int64_t ci) { return t_begin + (REVERSE ? nch - 1 - ci : ci) * WCT; };
 
-    XStage<NTHR, NS> xs;
+    XStage<NTHR, 1> xs;
     YStage<NTHR, RD> ysr;
     YStage<NTHR, !RD> ysw;
+    halfx4 rt[2], rcv[2], wt[2];
     yrow_zero_pad<NTHR>(yrow_r);
     if (CAUSAL) {
         yrow_zero_pad<NTHR>(yrow_w);
         ystage_zero_pad<NTHR>(ycol_w);
         ystage_load<NTHR, !RD>(vwh, chunk0(0), t_end, ysw);
+        hc_load<NW>(wc.t, wc, bh, chunk0(0), wt);
     }
     ystage_load<NTHR, RD>(vrh, chunk0(0), t_end, ysr);
-    xstage_load<NTHR, NS>(Rh, Wh, chunk0(0), t_end, xs);
-    xstage_store<NTHR, NS>(xs, xbuf[0], kbuf[0]);
-    if (nch > 1) xstage_load<NTHR, NS>(Rh, Wh, chunk0(1), t_end, xs);
+    hc_load<NW>(rc.t, rc, bh, chunk0(0), rt);
+    hc_load<NW>(rc.c, rc, bh, chunk0(0), rcv);
+    xstage_load<NTHR, 1>(Rh, Rh, chunk0(0), t_end, xs);
+    xstage_store<NTHR, 1>(xs, xbuf[0], kbuf[0]);
+    if (nch > 1) xstage_load<NTHR, 1>(Rh, Rh, chunk0(1), t_end, xs);
     lds_barrier();
 
     for (int64_t ci = 0; ci < nch; ++ci) {
@@ -864,30 +937,25 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             ystage_load<NTHR, RD>(vrh, chunk0(ci + 1), t_end, ysr);
             if (CAUSAL) ystage_load<NTHR, !RD>(vwh, chunk0(ci + 1), t_end, ysw);
         }
-        floatx4 tr[2], cr[2];
+        const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
+        if (ci + 1 < nch) {
+            hc_load<NW>(rc.t, rc, bh, chunk0(ci + 1), rt);
+            hc_load<NW>(rc.c, rc, bh, chunk0(ci + 1), rcv);
+        }
         bf16x8 pfm[4];
-        {
-            WRows wr;
-            wrows_lds(wl, WROWS, wr);
+        if (CAUSAL) {
+            bf16x8 pw[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-                hash_staged_chain<POLY>(xbuf[b], kbuf[b], tt, wr, sq, tr[tt], cr[tt]);
-            if (CAUSAL) {
-                bf16x8 pw[2][2];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const floatx4 t = hash_staged<POLY>(xbuf[b] + WCT * XRS, kbuf[b] + WCT, tt, wr, sq);
-                    walsh_tm(t, q4, pw[tt][0], pw[tt][1]);
-                }
-                const bf16x8 sel[2] = {*reinterpret_cast<const bf16x8 *>(sl + lane * 8),
-                                       *reinterpret_cast<const bf16x8 *>(sl + (64 + lane) * 8)};
-                feat_major(pw, sel, pfm);
-            }
+            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
+            if (ci + 1 < nch) hc_load<NW>(wc.t, wc, bh, chunk0(ci + 1), wt);
+            bf16x8 sel[2];
+            sel_lds(sl, sel);
+            feat_major(pw, sel, pfm);
         }
         lds_barrier();  // #1: value rows of this chunk staged
-        if (ci + 1 < nch) {  // the next chunk's rows into the other buffer
-            xstage_store<NTHR, NS>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            if (ci + 2 < nch) xstage_load<NTHR, NS>(Rh, Wh, chunk0(ci + 2), t_end, xs);
+        if (ci + 1 < nch) {  // the next chunk's raw rows into the other buffer
+            xstage_store<NTHR, 1>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            if (ci + 2 < nch) xstage_load<NTHR, 1>(Rh, Rh, chunk0(ci + 2), t_end, xs);
         }
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][2];
@@ -935,33 +1003,26 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 eb8 = cat8(acc2bf4(et[1]), acc2bf4(et[2]));  // reader tile 1: writer tiles 0, 1
             }
         }
+        // inter-chunk part with the state before this chunk (consecutive
+        // products go to the two token tiles' independent accumulators)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            // inter-chunk part with the state before this chunk
-            const bf16x8 sa0 = cat8(acc2bf4(acc[s][0]), acc2bf4(acc[s][1]));
-            const bf16x8 sa1 = cat8(acc2bf4(acc[s][2]), acc2bf4(acc[s][3]));
-            const bf16x4 sa2 = acc2bf4(acc[s][4]);
-            // every accumulation chain issues its 16x16x32 products before its
-            // 16x16x16 ones (a 16x16x16 result never feeds a 16x16x32 product)
+            bf16x8 sa[3];
+            sa[0] = cat8(acc2bf4(acc[s][0]), acc2bf4(acc[s][1]));
+            sa[1] = cat8(acc2bf4(acc[s][2]), acc2bf4(acc[s][3]));
+            sa[2] = cat8(acc2bf4(acc[s][4]), pk4(0, 0));
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                mma32(dps[s][tt], sa0, yb8[tt][0]);
-                mma32(dps[s][tt], sa1, yb8[tt][1]);
-            }
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    mma32(dps[s][tt], sa[k], k < 2 ? yb8[tt][k] : cat8(yb4[tt], pk4(0, 0)));
             if (CAUSAL) {
                 if (REVERSE) {
                     mma32(dps[s][0], pfm[s], eb8);
-                } else {
-                    mma32(dps[s][1], pfm[s], eb8);
-                }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) mma16(dps[s][tt], sa2, yb4[tt]);
-            if (CAUSAL) {
-                if (REVERSE) {
                     mma16(dps[s][1], hi4(pfm[s]), eb4);
                 } else {
                     mma16(dps[s][0], lo4(pfm[s]), eb4);
+                    mma32(dps[s][1], pfm[s], eb8);
                 }
             }
         }
@@ -982,13 +1043,15 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dp[4 * s + r] = dps[s][tt][r];
-            walsh_grad(dp, tr[tt], dt);
-            const bf16x4 du = pk4(pk_bf16(dt[0] * cr[tt][0], dt[1] * cr[tt][1]),
-                                  pk_bf16(dt[2] * cr[tt][2], dt[3] * cr[tt][3]));
+            walsh_grad(dp, to_f4(trh[tt]), dt);
+            const floatx4 cr = to_f4(crh[tt]);
+            const bf16x4 du = pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                bf16x4 whi, wlo;
-                wcols_lds(wl, WROWS, nt, whi, wlo);
+                // W^T operand: lane (dim 16 nt + c16, hyperplanes 16w + 4g .. + 3), hi and lo
+                const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + w * 16 + 4 * g;
+                const bf16x4 whi = *reinterpret_cast<const bf16x4 *>(wrow);
+                const bf16x4 wlo = *reinterpret_cast<const bf16x4 *>(wrow + HD * WTS);
                 floatx4 xa = {0.f, 0.f, 0.f, 0.f};
                 mma32(xa, cat8(whi, wlo), cat8(du, du));  // (W_hi + W_lo)^T du^T
                 *reinterpret_cast<floatx4 *>(dxp + (w * WCT + tt * 16 + c16) * DXS + nt * 16 + 4 * g) = xa;

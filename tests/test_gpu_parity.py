@@ -34,7 +34,7 @@ def _ids(c):
     return "B%dH%dN%dL%d_tau%g_ch%d" % c
 
 
-def _run(dtype, causal, B, H, N, L, tau, chunk, backward):
+def _run(dtype, causal, B, H, N, L, tau, chunk, backward, saved=False):
     if dtype == "f32" and L > 32:
         pytest.skip("fp32 supports L <= 32")
     seed = 7 + N + 31 * L + (1 if causal else 0)
@@ -42,12 +42,13 @@ def _run(dtype, causal, B, H, N, L, tau, chunk, backward):
     dx, hx = device_inputs(x, dtype), host_inputs(x, dtype)
     print(f"[case] {dtype} causal={causal} B={B} H={H} N={N} L={L} tau={tau} chunk={chunk}",
           flush=True)
-    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], tau, causal, chunk)
+    sv = binding.new_saved(dx["q"], dx["W"], causal, chunk) if saved else None
+    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], tau, causal, chunk, saved=sv)
     torch.cuda.synchronize()
     res = {"o": to_host64(o), "den": to_host64(den)}
     if backward:
         dq, dk, dv = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau,
-                                      causal, chunk)
+                                      causal, chunk, saved=sv)
         torch.cuda.synchronize()
         res.update(dq=to_host64(dq), dk=to_host64(dk), dv=to_host64(dv))
         ref = oracle.forward_backward(hx["q"], hx["k"], hx["v"], hx["do"], hx["W"], tau, causal)
@@ -75,8 +76,10 @@ def test_forward_parity(dtype, causal, case):
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_parity(dtype, causal, case):
-    res, ref = _run(dtype, causal, *case, backward=True)
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
+def test_backward_parity(dtype, causal, case, saved):
+    """saved: the backward reads the forward's saved state (as bench.py times it)."""
+    res, ref = _run(dtype, causal, *case, backward=True, saved=saved)
     tol = TOL[dtype]
     # N = 1: every query sees only its own key, so o = v and the exact dQ, dK
     # are zero; the computed values are rounding noise, judged on dV's scale.

@@ -1,12 +1,20 @@
-"""The forward's saved key state: a backward that reads it gives exactly the
-result of one that recomputes it (same kernel, same inputs), through the
-C ABI and through the autograd wrapper."""
+"""The forward's saved state (key-side segment sums and the fp16 hash
+features of Q and K): a backward that reads it agrees with one that
+recomputes it, through the C ABI and through the autograd wrapper.  The
+forward output is unchanged by saving; the gradients agree to rounding (the
+hash features are computed by different kernels), far inside the parity bar.
+"""
 import pytest
 import torch
 
 from sketch_attention_soft_amd import binding
 from sketch_attention_soft_amd import inputs as I
 from tests.gpu_util import device_inputs
+
+
+def _relf(a, b):
+    a, b = a.double(), b.double()
+    return ((a - b).norm() / b.norm().clamp_min(1e-30)).item()
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +44,9 @@ def test_backward_with_saved_state_is_identical(case):
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(den, den2)
     for a, b in zip(got, ref):
-        assert torch.equal(a, b)
+        e = _relf(a, b)
+        print(f"  saved vs recomputed: {e:.2e}")
+        assert e <= 1e-2
 
 
 def test_autograd_wrapper_matches_binding():
@@ -50,4 +60,5 @@ def test_autograd_wrapper_matches_binding():
                                   True)
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), ro)
-    assert torch.equal(q.grad, rq) and torch.equal(k.grad, rk) and torch.equal(v.grad, rv)
+    for a, b in ((q.grad, rq), (k.grad, rk), (v.grad, rv)):
+        assert _relf(a, b) <= 1e-2

@@ -36,14 +36,19 @@ def _relf(a, b):
 
 
 def _run(w, dx):
+    """forward + backward as bench.py times them (the backward reads the
+    forward's saved state)."""
     print(f"[workload] {w.name}: B={w.B} H={w.H} N={w.N} L={w.L} {w.dtype}", flush=True)
-    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], w.tau, w.causal, w.chunk)
+    sv = binding.new_saved(dx["q"], dx["W"], w.causal, w.chunk) if w.backward else None
+    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], w.tau, w.causal, w.chunk,
+                             saved=sv)
     res = {"o": o, "den": den}
     if w.backward:
         dq, dk, dv = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"],
-                                      w.tau, w.causal, w.chunk)
+                                      w.tau, w.causal, w.chunk, saved=sv)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
+    del sv
     return res
 
 
