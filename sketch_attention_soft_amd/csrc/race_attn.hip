@@ -88,11 +88,11 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     const int64_t n16 = (N + 15) / 16 * 16;
     int64_t seg = chunk;
     if (seg == 0) {
-        // about 2048 workgroups in total, segments of 64 .. 8192 tokens
-        const int64_t want = (p->rows + 2047) / 2048;
-        seg = (want + 15) / 16 * 16;
+        // one workgroup per compute unit (MI355X: 256 CUs; every segment
+        // kernel keeps one workgroup per CU resident), segments >= 64 tokens
+        const int64_t want = (p->rows + 255) / 256;
+        seg = (want + 31) / 32 * 32;
         if (seg < 64) seg = 64;
-        if (seg > 8192) seg = 8192;
     }
     if (seg > n16) seg = n16;
     seg = (seg + 31) / 32 * 32;  // whole 32-token sub-chunks per segment
