@@ -109,37 +109,38 @@ template <int NTHR, int NS> struct XStage {
     bf16x8 v[ITEMS];
 };
 
+// Loads are unconditional (rows past tend read the last valid row; the zero
+// fill happens at the store): a prefetch must not sit in a branch, or the
+// wait for it lands right after it is issued.
 template <int NTHR, int NS>
 __device__ __forceinline__ void xstage_load(const bf16 *__restrict__ r0, const bf16 *__restrict__ r1,
-                                            int64_t tok0, int64_t tend, XStage<NTHR, NS> &xs)
+                                            int tok0, int tend, XStage<NTHR, NS> &xs)
 {
 #pragma unroll
     for (int it = 0; it < XStage<NTHR, NS>::ITEMS; ++it) {
-        const int e = threadIdx.x + it * NTHR;
-        const int64_t tok = tok0 + ((e >> 3) & (WCT - 1));
+        const int e = (threadIdx.x + it * NTHR) % (NS * WCT * 8);
+        const int tok = min(tok0 + ((e >> 3) & (WCT - 1)), tend - 1);
         const bf16 *src = (e >> 8) ? r1 : r0;
-        if (e < NS * WCT * 8 && tok < tend) {
-            xs.v[it] = *reinterpret_cast<const bf16x8 *>(src + tok * HD + (e & 7) * 8);
-        } else {
-            xs.v[it] = pk8(0, 0, 0, 0);
-        }
+        xs.v[it] = *reinterpret_cast<const bf16x8 *>(src + tok * HD + (e & 7) * 8);
     }
 }
 
-// rows -> xb[set][token][XRS]; kb[set][token] = -2 log2(e) / max(|x|, 1e-12)
+// rows -> xb[set][token][XRS] (zero past tend); kb[set][token] = -2 log2(e) / max(|x|, 1e-12)
 template <int NTHR, int NS>
-__device__ __forceinline__ void xstage_store(const XStage<NTHR, NS> &xs, bf16 *xb, float *kb)
+__device__ __forceinline__ void xstage_store(const XStage<NTHR, NS> &xs, int tok0, int tend,
+                                             bf16 *xb, float *kb)
 {
 #pragma unroll
     for (int it = 0; it < XStage<NTHR, NS>::ITEMS; ++it) {
         const int e = threadIdx.x + it * NTHR;
         if (e < NS * WCT * 8) {  // uniform per wave
             const int set = e >> 8, j = (e >> 3) & (WCT - 1);
-            *reinterpret_cast<bf16x8 *>(xb + (set * WCT + j) * XRS + (e & 7) * 8) = xs.v[it];
+            const bf16x8 v = tok0 + j < tend ? xs.v[it] : pk8(0, 0, 0, 0);
+            *reinterpret_cast<bf16x8 *>(xb + (set * WCT + j) * XRS + (e & 7) * 8) = v;
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float x = (float)xs.v[it][i];
+                const float x = (float)v[i];
                 ss = fmaf(x, x, ss);
             }
             ss = sum8(ss);
@@ -160,21 +161,20 @@ template <int NTHR, bool DVAL> struct YStage {
 };
 
 template <int NTHR, bool DVAL>
-__device__ __forceinline__ void ystage_load(const ValSrc<bf16> &src, int64_t tok0, int64_t tend,
+__device__ __forceinline__ void ystage_load(const ValSrc<bf16> &src, int tok0, int tend,
                                             YStage<NTHR, DVAL> &ys)
 {
 #pragma unroll
     for (int it = 0; it < YStage<NTHR, DVAL>::ITEMS; ++it) {
-        const int e = threadIdx.x + it * NTHR;
+        const int e = (threadIdx.x + it * NTHR) % (WCT * 8);
         const int c0 = (e & 15) * 4;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int64_t tok = tok0 + 2 * ((e >> 4) & 15) + h;
-            const bool ok = e < WCT * 8 && tok < tend;
-            ys.x[it][h] = ok ? *reinterpret_cast<const bf16x4 *>(src.V + tok * HD + c0) : pk4(0, 0);
+            const int tok = min(tok0 + 2 * ((e >> 4) & 15) + h, tend - 1);
+            ys.x[it][h] = *reinterpret_cast<const bf16x4 *>(src.V + tok * HD + c0);
             if constexpr (DVAL) {
-                ys.o[it][h] = ok ? *reinterpret_cast<const bf16x4 *>(src.O + tok * HD + c0) : pk4(0, 0);
-                ys.m[it][h] = ok ? src.den[tok] : 1.f;
+                ys.o[it][h] = *reinterpret_cast<const bf16x4 *>(src.O + tok * HD + c0);
+                ys.m[it][h] = src.den[tok];
             }
         }
     }
@@ -184,7 +184,7 @@ constexpr int YRS = NCOL + 8;  // token-major value row stride
 
 // yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may be null)
 template <int NTHR, bool DVAL>
-__device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int64_t tok0, int64_t tend,
+__device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int tok0, int tend,
                                              bf16 *yc, bf16 *yr = nullptr)
 {
 #pragma unroll
@@ -195,20 +195,22 @@ __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int64
             float y[2][4], extra[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                // rows past tend were loaded from the last valid row: zero them here
                 const bool ok = tok0 + 2 * jp + h < tend;
                 if constexpr (DVAL) {
                     float dot = 0.f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) dot += (float)ys.x[it][h][i] * (float)ys.o[it][h][i];
                     dot = sum16(dot);
-                    const float inv_m = __builtin_amdgcn_rcpf(ys.m[it][h]);
+                    const float inv_m = ok ? __builtin_amdgcn_rcpf(ys.m[it][h]) : 0.f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i] * inv_m;
-                    extra[h] = ok ? -dot * inv_m : 0.f;
+                    extra[h] = -dot * inv_m;
                 } else {
+                    const float okf = ok ? 1.f : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i];
-                    extra[h] = ok ? 1.f : 0.f;
+                    for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i] * okf;
+                    extra[h] = okf;
                 }
             }
             if (yc) {
@@ -463,10 +465,16 @@ struct HCache {
     int64_t tiles;  // token tiles per head (2 per 32-token chunk)
 };
 
+// first element of the cache of a segment (t_begin: a multiple of 32)
 template <int NW>
-__device__ __forceinline__ int64_t hc_off(const HCache &h, int64_t bh, int64_t tile)
+__device__ __forceinline__ int64_t hc_seg(const HCache &h, int64_t bh, int64_t t_begin)
 {
-    return (((bh * h.tiles + tile) * NW + wave_id()) * 64 + lane_id()) * 4;
+    return (bh * h.tiles + t_begin / 16) * (int64_t)(NW * 64 * 4);
+}
+// offset of this lane's values of tile `tile` (relative to the segment start)
+template <int NW> __device__ __forceinline__ int hc_off(int tile)
+{
+    return ((tile * NW + wave_id()) * 64 + lane_id()) * 4;
 }
 __device__ __forceinline__ halfx4 to_h4(const floatx4 &v)
 {
@@ -479,13 +487,12 @@ __device__ __forceinline__ floatx4 to_f4(const halfx4 &v)
     return r;
 }
 
-// cached values of the two 16-token tiles of the chunk at tok0
+// cached values of the two 16-token tiles of the chunk at tok0 (segment-relative)
 template <int NW>
-__device__ __forceinline__ void hc_load(const _Float16 *__restrict__ p, const HCache &h, int64_t bh,
-                                        int64_t tok0, halfx4 (&v)[2])
+__device__ __forceinline__ void hc_load(const _Float16 *__restrict__ seg, int tok0, halfx4 (&v)[2])
 {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) v[tt] = *reinterpret_cast<const halfx4 *>(p + hc_off<NW>(h, bh, tok0 / 16 + tt));
+    for (int tt = 0; tt < 2; ++tt) v[tt] = *reinterpret_cast<const halfx4 *>(seg + hc_off<NW>(tok0 / 16 + tt));
 }
 
 // ---------------------------------------------------------------------------
@@ -508,13 +515,20 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4;
-    const bf16 *Xh = X + bh * N * HD;
+    // segment-relative row pointers (32-bit offsets in the loop)
+    const int64_t t_begin = sg * seg;
+    const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
+    const int nch = (tend + WCT - 1) / WCT;
+    const bf16 *Xs = X + (bh * N + t_begin) * HD;
     ValSrc<bf16> vh = vsrc;
-    vh.V += bh * N * HD;
+    vh.V += (bh * N + t_begin) * HD;
     if (DVAL) {
-        vh.O += bh * N * HD;
-        vh.den += bh * N;
+        vh.O += (bh * N + t_begin) * HD;
+        vh.den += bh * N + t_begin;
     }
+    const _Float16 *cin_t = HASH ? nullptr : ci_.t + hc_seg<NW>(ci_, bh, t_begin);
+    _Float16 *cout_t = co.t ? co.t + hc_seg<NW>(co, bh, t_begin) : nullptr;
+    _Float16 *cout_c = co.c ? co.c + hc_seg<NW>(co, bh, t_begin) : nullptr;
     WRows wr;
     if (HASH) load_wrows(W, L * NP, wr);
     const bf16x8 sel[2] = {selection(0), selection(1)};
@@ -524,59 +538,55 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) af[s][ct] = {0.f, 0.f, 0.f, 0.f};
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
-    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
     XStage<NTHR, 1> xs;
     YStage<NTHR, DVAL> ys;
     halfx4 tc[2];
     ystage_zero_pad<NTHR>(ycol[0]);
     ystage_zero_pad<NTHR>(ycol[1]);
-    ystage_load<NTHR, DVAL>(vh, t_begin, t_end, ys);
+    ystage_load<NTHR, DVAL>(vh, 0, tend, ys);
+    // chunk starts, clamped to the last chunk (prefetches past the end reload it)
+    auto cstart = [&](int ci) { return min(ci, nch - 1) * WCT; };
     if (HASH) {
-        xstage_load<NTHR, 1>(Xh, Xh, t_begin, t_end, xs);
-        xstage_store<NTHR, 1>(xs, xbuf[0], kbuf[0]);
+        xstage_load<NTHR, 1>(Xs, Xs, 0, tend, xs);
+        xstage_store<NTHR, 1>(xs, 0, tend, xbuf[0], kbuf[0]);
     } else {
-        hc_load<NW>(ci_.t, ci_, bh, t_begin, tc);
+        hc_load<NW>(cin_t, 0, tc);
     }
-    ystage_store<NTHR, DVAL>(ys, t_begin, t_end, ycol[0]);
-    if (nch > 1) {
-        if (HASH) xstage_load<NTHR, 1>(Xh, Xh, t_begin + WCT, t_end, xs);
-        ystage_load<NTHR, DVAL>(vh, t_begin + WCT, t_end, ys);
-    }
+    ystage_store<NTHR, DVAL>(ys, 0, tend, ycol[0]);
+    if (HASH) xstage_load<NTHR, 1>(Xs, Xs, cstart(1), tend, xs);
+    ystage_load<NTHR, DVAL>(vh, cstart(1), tend, ys);
     lds_barrier();
-    for (int64_t ci = 0; ci < nch; ++ci) {
+    for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
-        const int64_t tok0 = t_begin + ci * WCT;
+        const int tok0 = ci * WCT;
         bf16x8 ptm[2][2], pfm[4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             floatx4 t;
             if constexpr (HASH) {
-                const int64_t o = hc_off<NW>(co, bh, tok0 / 16 + tt);
+                const int o = hc_off<NW>(tok0 / 16 + tt);
                 if constexpr ((WR & 2) != 0) {
                     floatx4 c;
                     hash_staged_chain<POLY>(xbuf[b], kbuf[b], tt, wr, sq, t, c);
-                    *reinterpret_cast<halfx4 *>(co.c + o) = to_h4(c);
+                    *reinterpret_cast<halfx4 *>(cout_c + o) = to_h4(c);
                 } else {
                     t = hash_staged<POLY>(xbuf[b], kbuf[b], tt, wr, sq);
                 }
-                if constexpr ((WR & 1) != 0) *reinterpret_cast<halfx4 *>(co.t + o) = to_h4(t);
+                if constexpr ((WR & 1) != 0) *reinterpret_cast<halfx4 *>(cout_t + o) = to_h4(t);
             } else {
                 t = to_f4(tc[tt]);
             }
             walsh_tm(t, q4, ptm[tt][0], ptm[tt][1]);
         }
         if (ci + 1 < nch) {  // the other buffers were last read before the previous barrier
-            const int64_t nx = tok0 + WCT;
-            if (HASH) {
-                xstage_store<NTHR, 1>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-                if (ci + 2 < nch) xstage_load<NTHR, 1>(Xh, Xh, nx + WCT, t_end, xs);
-            } else {
-                hc_load<NW>(ci_.t, ci_, bh, nx, tc);
-            }
-            ystage_store<NTHR, DVAL>(ys, nx, t_end, ycol[b ^ 1]);
-            if (ci + 2 < nch) ystage_load<NTHR, DVAL>(vh, nx + WCT, t_end, ys);
+            if (HASH) xstage_store<NTHR, 1>(xs, tok0 + WCT, tend, xbuf[b ^ 1], kbuf[b ^ 1]);
+            ystage_store<NTHR, DVAL>(ys, tok0 + WCT, tend, ycol[b ^ 1]);
         }
+        if (HASH)
+            xstage_load<NTHR, 1>(Xs, Xs, cstart(ci + 2), tend, xs);
+        else
+            hc_load<NW>(cin_t, cstart(ci + 1), tc);
+        ystage_load<NTHR, DVAL>(vh, cstart(ci + 2), tend, ys);
         feat_major(ptm, sel, pfm);
         // tokens past t_end have psi_0 = 1/4 but zero value rows
 #pragma unroll
@@ -624,15 +634,23 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    const bf16 *Rh = R + bh * N * HD;
+    // segment-relative row pointers (32-bit offsets in the loop)
+    const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
+    const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
+    const int nch = (tend + WCT - 1) / WCT;
+    const bf16 *Rs = R + row0 * HD;
     ValSrc<bf16> vh = vsrc;
-    vh.V += bh * N * HD;
+    vh.V += row0 * HD;
     if (BWD) {
-        vh.O += bh * N * HD;
-        vh.den += bh * N;
+        vh.O += row0 * HD;
+        vh.den += row0;
     }
-    bf16 *Oh = Out + bh * N * HD;
-    float *denh = BWD ? nullptr : den + bh * N;
+    bf16 *Os = Out + row0 * HD;
+    float *dens = BWD ? nullptr : den + row0;
+    const _Float16 *rt_seg = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
+    _Float16 *rt_out = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
+    _Float16 *rc_out = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
+    const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
     stage_wrows<NW>(W, L * NP, wl, sl);
     const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
@@ -645,34 +663,37 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             for (int ct = 0; ct < NT; ++ct)
                 acc[s][ct] = *reinterpret_cast<const floatx4 *>(src + st_idx(w, s, ct, lane, 4));
     }
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
-    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
-    auto chunk0 = [&](int64_t ci) { return t_begin + (BWD ? nch - 1 - ci : ci) * WCT; };
+    // chunk starts in walk order (segment-relative); indices past the last
+    // chunk are clamped (prefetches beyond the end reload the last chunk)
+    auto chunk0 = [&](int ci) {
+        ci = min(ci, nch - 1);
+        return (BWD ? nch - 1 - ci : ci) * WCT;
+    };
 
     XStage<NTHR, 1> xs;
     YStage<NTHR, BWD> ys;
     halfx4 rt[2], wt[2];
     if (CAUSAL) {
         ystage_zero_pad<NTHR>(ycol);
-        ystage_load<NTHR, BWD>(vh, chunk0(0), t_end, ys);
-        hc_load<NW>(wc.t, wc, bh, chunk0(0), wt);
+        ystage_load<NTHR, BWD>(vh, chunk0(0), tend, ys);
+        hc_load<NW>(wt_seg, chunk0(0), wt);
     }
     if (HASH) {
-        xstage_load<NTHR, 1>(Rh, Rh, chunk0(0), t_end, xs);
-        xstage_store<NTHR, 1>(xs, xbuf, kbuf);
-        if (nch > 1) xstage_load<NTHR, 1>(Rh, Rh, chunk0(1), t_end, xs);
+        xstage_load<NTHR, 1>(Rs, Rs, chunk0(0), tend, xs);
+        xstage_store<NTHR, 1>(xs, chunk0(0), tend, xbuf, kbuf);
+        xstage_load<NTHR, 1>(Rs, Rs, chunk0(1), tend, xs);
     } else {
-        hc_load<NW>(rc.t, rc, bh, chunk0(0), rt);
+        hc_load<NW>(rt_seg, chunk0(0), rt);
     }
     lds_barrier();
 
     float nsum[RIT][4];
-    int64_t prev0 = 0;
-    for (int64_t ci = 0; ci < nch; ++ci) {
-        const int64_t tok0 = chunk0(ci);
+    int prev0 = 0;
+    for (int ci = 0; ci < nch; ++ci) {
+        const int tok0 = chunk0(ci);
         if (CAUSAL) {
-            ystage_store<NTHR, BWD>(ys, tok0, t_end, ycol);
-            if (ci + 1 < nch) ystage_load<NTHR, BWD>(vh, chunk0(ci + 1), t_end, ys);
+            ystage_store<NTHR, BWD>(ys, tok0, tend, ycol);
+            ystage_load<NTHR, BWD>(vh, chunk0(ci + 1), tend, ys);
         }
         // Walsh features of this chunk's readers and writers
         bf16x8 pr[2][2], pfm[4];
@@ -684,26 +705,26 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         for (int tt = 0; tt < 2; ++tt) {
             floatx4 t;
             if constexpr (HASH) {
-                const int64_t o = hc_off<NW>(rc, bh, tok0 / 16 + tt);
+                const int o = hc_off<NW>(tok0 / 16 + tt);
                 if constexpr ((RWR & 2) != 0) {
                     floatx4 c;
                     hash_staged_chain<POLY>(xbuf, kbuf, tt, wr, sq, t, c);
-                    *reinterpret_cast<halfx4 *>(rc.c + o) = to_h4(c);
+                    *reinterpret_cast<halfx4 *>(rc_out + o) = to_h4(c);
                 } else {
                     t = hash_staged<POLY>(xbuf, kbuf, tt, wr, sq);
                 }
-                if constexpr ((RWR & 1) != 0) *reinterpret_cast<halfx4 *>(rc.t + o) = to_h4(t);
+                if constexpr ((RWR & 1) != 0) *reinterpret_cast<halfx4 *>(rt_out + o) = to_h4(t);
             } else {
                 t = to_f4(rt[tt]);
             }
             walsh_tm(t, q4, pr[tt][0], pr[tt][1]);
         }
-        if (!HASH && ci + 1 < nch) hc_load<NW>(rc.t, rc, bh, chunk0(ci + 1), rt);
+        if (!HASH) hc_load<NW>(rt_seg, chunk0(ci + 1), rt);
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
-            if (ci + 1 < nch) hc_load<NW>(wc.t, wc, bh, chunk0(ci + 1), wt);
+            hc_load<NW>(wt_seg, chunk0(ci + 1), wt);
             // scores^T tiles D[j][i] = psi_w(j) . psi_r(i) over this wave's tables
             constexpr int TJ[3] = {0, BWD ? 1 : 0, 1}, TI[3] = {0, BWD ? 0 : 1, 1};
             floatx4 sc[3];
@@ -742,16 +763,16 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                     const floatx4 m = *reinterpret_cast<const floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4));
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
-                        if (tok < t_end)
-                            Oh[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
+                        const int tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
+                        if (tok < tend)
+                            Os[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
                     }
                 }
             }
         }
-        if (HASH && ci + 1 < nch) {  // the next chunk's rows (xbuf is not read again in this chunk)
-            xstage_store<NTHR, 1>(xs, xbuf, kbuf);
-            if (ci + 2 < nch) xstage_load<NTHR, 1>(Rh, Rh, chunk0(ci + 2), t_end, xs);
+        if (HASH) {  // the next chunk's rows (xbuf is not read again in this chunk)
+            if (ci + 1 < nch) xstage_store<NTHR, 1>(xs, chunk0(ci + 1), tend, xbuf, kbuf);
+            xstage_load<NTHR, 1>(Rs, Rs, chunk0(ci + 2), tend, xs);
         }
         floatx4 oacc[2][NT];
 #pragma unroll
@@ -799,8 +820,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 if (BWD) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
-                        if (tok < t_end) Oh[tok * HD + ct * 16 + (ln & 15)] = (bf16)n[r];
+                        const int tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
+                        if (tok < tend) Os[tok * HD + ct * 16 + (ln & 15)] = (bf16)n[r];
                     }
                 } else {
 #pragma unroll
@@ -813,8 +834,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                         *reinterpret_cast<floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4)) = m;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const int64_t tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
-                            if (tok < t_end) denh[tok] = m[r];
+                            const int tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
+                            if (tok < tend) dens[tok] = m[r];
                         }
                     }
                 }
@@ -832,9 +853,9 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 const floatx4 m = *reinterpret_cast<const floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
-                    if (tok < t_end)
-                        Oh[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
+                    const int tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
+                    if (tok < tend)
+                        Os[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
                 }
             }
         }
@@ -876,18 +897,25 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    const bf16 *Rh = Xr + bh * N * HD;
+    // segment-relative row pointers (32-bit offsets in the loop)
+    const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
+    const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
+    const int nch = (tend + WCT - 1) / WCT;
+    const bf16 *Rs = Xr + row0 * HD;
     ValSrc<bf16> vrh = vr_src, vwh = vw_src;
-    vrh.V += bh * N * HD;
-    vwh.V += bh * N * HD;
+    vrh.V += row0 * HD;
+    vwh.V += row0 * HD;
     if (RD) {
-        vrh.O += bh * N * HD;
-        vrh.den += bh * N;
+        vrh.O += row0 * HD;
+        vrh.den += row0;
     } else {
-        vwh.O += bh * N * HD;
-        vwh.den += bh * N;
+        vwh.O += row0 * HD;
+        vwh.den += row0;
     }
-    bf16 *dXh = dX + bh * N * HD;
+    bf16 *dXs = dX + row0 * HD;
+    const _Float16 *rt_seg = rc.t + hc_seg<NW>(rc, bh, t_begin);
+    const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
+    const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
     // W^T (hi, lo) and the selection operands, once per workgroup
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
@@ -905,9 +933,10 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
 
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
-    const int64_t nch = (t_end - t_begin + WCT - 1) / WCT;
-    auto chunk0 = [&](int64_t ci) { return t_begin + (REVERSE ? nch - 1 - ci : ci) * WCT; };
+    auto chunk0 = [&](int ci) {
+        ci = min(ci, nch - 1);  // prefetches beyond the end reload the last chunk
+        return (REVERSE ? nch - 1 - ci : ci) * WCT;
+    };
 
     XStage<NTHR, 1> xs;
     YStage<NTHR, RD> ysr;
@@ -917,46 +946,41 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     if (CAUSAL) {
         yrow_zero_pad<NTHR>(yrow_w);
         ystage_zero_pad<NTHR>(ycol_w);
-        ystage_load<NTHR, !RD>(vwh, chunk0(0), t_end, ysw);
-        hc_load<NW>(wc.t, wc, bh, chunk0(0), wt);
+        ystage_load<NTHR, !RD>(vwh, chunk0(0), tend, ysw);
+        hc_load<NW>(wt_seg, chunk0(0), wt);
     }
-    ystage_load<NTHR, RD>(vrh, chunk0(0), t_end, ysr);
-    hc_load<NW>(rc.t, rc, bh, chunk0(0), rt);
-    hc_load<NW>(rc.c, rc, bh, chunk0(0), rcv);
-    xstage_load<NTHR, 1>(Rh, Rh, chunk0(0), t_end, xs);
-    xstage_store<NTHR, 1>(xs, xbuf[0], kbuf[0]);
-    if (nch > 1) xstage_load<NTHR, 1>(Rh, Rh, chunk0(1), t_end, xs);
+    ystage_load<NTHR, RD>(vrh, chunk0(0), tend, ysr);
+    hc_load<NW>(rt_seg, chunk0(0), rt);
+    hc_load<NW>(rc_seg, chunk0(0), rcv);
+    xstage_load<NTHR, 1>(Rs, Rs, chunk0(0), tend, xs);
+    xstage_store<NTHR, 1>(xs, chunk0(0), tend, xbuf[0], kbuf[0]);
+    xstage_load<NTHR, 1>(Rs, Rs, chunk0(1), tend, xs);
     lds_barrier();
 
-    for (int64_t ci = 0; ci < nch; ++ci) {
+    for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
-        const int64_t tok0 = chunk0(ci);
-        ystage_store<NTHR, RD>(ysr, tok0, t_end, nullptr, yrow_r);
-        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, tok0, t_end, ycol_w, yrow_w);
-        if (ci + 1 < nch) {
-            ystage_load<NTHR, RD>(vrh, chunk0(ci + 1), t_end, ysr);
-            if (CAUSAL) ystage_load<NTHR, !RD>(vwh, chunk0(ci + 1), t_end, ysw);
-        }
+        const int tok0 = chunk0(ci);
+        ystage_store<NTHR, RD>(ysr, tok0, tend, nullptr, yrow_r);
+        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, tok0, tend, ycol_w, yrow_w);
+        ystage_load<NTHR, RD>(vrh, chunk0(ci + 1), tend, ysr);
+        if (CAUSAL) ystage_load<NTHR, !RD>(vwh, chunk0(ci + 1), tend, ysw);
         const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
-        if (ci + 1 < nch) {
-            hc_load<NW>(rc.t, rc, bh, chunk0(ci + 1), rt);
-            hc_load<NW>(rc.c, rc, bh, chunk0(ci + 1), rcv);
-        }
+        hc_load<NW>(rt_seg, chunk0(ci + 1), rt);
+        hc_load<NW>(rc_seg, chunk0(ci + 1), rcv);
         bf16x8 pfm[4];
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
-            if (ci + 1 < nch) hc_load<NW>(wc.t, wc, bh, chunk0(ci + 1), wt);
+            hc_load<NW>(wt_seg, chunk0(ci + 1), wt);
             bf16x8 sel[2];
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
         lds_barrier();  // #1: value rows of this chunk staged
-        if (ci + 1 < nch) {  // the next chunk's raw rows into the other buffer
-            xstage_store<NTHR, 1>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            if (ci + 2 < nch) xstage_load<NTHR, 1>(Rh, Rh, chunk0(ci + 2), t_end, xs);
-        }
+        // the next chunk's raw rows into the other buffer
+        if (ci + 1 < nch) xstage_store<NTHR, 1>(xs, chunk0(ci + 1), tend, xbuf[b ^ 1], kbuf[b ^ 1]);
+        xstage_load<NTHR, 1>(Rs, Rs, chunk0(ci + 2), tend, xs);
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][2];
         bf16x4 yb4[2];
@@ -1077,8 +1101,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             }
             ss = sum16(ss);
             dot = sum16(dot);
-            const int64_t tok = tok0 + i;
-            if (e < WCT * 16 && tok < t_end) {
+            const int tok = tok0 + i;
+            if (e < WCT * 16 && tok < tend) {
                 const float nrm = sqrtf(ss);
                 float rv[4];
 #pragma unroll
@@ -1090,7 +1114,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                         rv[c] = dh[c] * 1e12f;
                     }
                 }
-                *reinterpret_cast<bf16x4 *>(dXh + tok * HD + part * 4) =
+                *reinterpret_cast<bf16x4 *>(dXs + tok * HD + part * 4) =
                     pk4(pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3]));
             }
         }
