@@ -18,6 +18,9 @@ import os
 import sys
 import time
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
 METRIC = "RACE attn fwd+bwd tokens/s at N=4M causal d=64; % of MFMA/HBM roofline"
 
 # MI355X published peaks
@@ -62,14 +65,46 @@ def algorithmic_per_token(w):
     return fwd_flops + bwd_flops, 12 * d * e + 8, per_kernel
 
 
+def kernel_sources_digest() -> str:
+    """sha256 over the kernel sources (file names and bytes, sorted by name)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(HERE, "sketch_attention_soft_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str) -> dict:
+    """HBM bytes per launch from the committed counter summary of this workload,
+    or {} when it is missing or was taken on other kernel sources."""
+    path = os.path.join(HERE, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    out, digest = {}, None
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) >= 3 and parts[0] == "traffic":
+                out[parts[1]] = float(parts[2])
+            elif len(parts) == 2 and parts[0] == "source_sha256":
+                digest = parts[1]
+    return out if digest == kernel_sources_digest() else {}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="causal_n4m_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=262144,
+    ap.add_argument("--cpu-tokens", type=int, default=524288,
                     help="tokens of the workload's first head timed on the oracle (0: skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -78,6 +113,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return 0
 
     from sketch_attention_soft_amd import binding
     from sketch_attention_soft_amd import inputs as I
@@ -151,8 +196,10 @@ def main() -> int:
     achieved = per_kernel.get(dom, 0) * tokens / (dom_ms * 1e-3) / 1e12
     t_mfma = flops_tok * tokens / (peak * 1e12) * 1e3
     t_hbm = bytes_tok * tokens / (PEAK_HBM_GBS * 1e9) * 1e3
+    traffic = measured_traffic(w.name).get(dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 5), "traffic": None, "kernel": dom,
+                "frac": round(achieved / peak, 5),
+                "traffic": round(traffic) if traffic is not None else None, "kernel": dom,
                 "kernel_ms": round(dom_ms, 4)}
 
     cpu = None
