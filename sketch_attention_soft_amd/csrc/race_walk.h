@@ -11,6 +11,8 @@
 // current one is computed) and writes it to LDS, where the eight threads of a
 // row also form its squared norm.  Value rows go to LDS column by column (and
 // row by row where needed), so that any wave reads them as MFMA operands.
+// All chunk loads and stores go through buffer resources sized to the chunk's
+// valid rows, so ragged ends need neither clamping nor branches.
 //
 // Hash-feature cache.  Each row is hashed once per pass: the kernel that
 // hashes it stores t = tanh(tanh(u')/tau) (and dt/du') in fp16 in the
@@ -102,41 +104,79 @@ __device__ __forceinline__ float sum8(float x)
 __device__ __forceinline__ float sum16(float x) { return dpp_add(sum8(x), 3); }  // row_ror:8
 
 // ---------------------------------------------------------------------------
-// Staging of raw rows: NS row sets (0: readers, 1: writers) of one chunk,
-// item e -> set e >> 8, token (e >> 3) & 31, columns (e & 7) * 8 .. + 8.
-template <int NTHR, int NS> struct XStage {
-    static constexpr int ITEMS = (NS * WCT * 8 + NTHR - 1) / NTHR;
-    bf16x8 v[ITEMS];
+// Buffer resources.  The rows of one chunk are addressed through a resource
+// whose base is the chunk's first row and whose size covers its valid rows
+// only: loads past the size return zeros and stores past it are dropped.  So
+// the loop needs no clamping and no per-row branches, lane offsets are loop
+// constants, and the chunk position lives in scalar registers.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int bytes)
+{
+    // the arguments are wave-uniform; reading them through the first lane
+    // keeps the descriptor in scalar registers whichever unit computed them
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    // dword 3: 32-bit data format, the raw-buffer setting of this GPU family
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(lo | (hi << 32)), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+constexpr int OOB = 0x7ffffff0;  // a lane offset past every resource: the access is skipped
+
+__device__ __forceinline__ u32x4 bld128(Rsrc r, int off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+__device__ __forceinline__ u32x2 bld64(Rsrc r, int off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+__device__ __forceinline__ float bldf(Rsrc r, int off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bst64(u32x2 v, Rsrc r, int off) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0); }
+__device__ __forceinline__ void bstf(float v, Rsrc r, int off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+// A chunk of a segment: first token (segment-relative) and valid rows (0 for
+// chunk indices past the end, whose accesses are all skipped).
+struct Chunk {
+    int tok0, nv;
+};
+// rows of a [token][HD] bf16 array
+__device__ __forceinline__ Rsrc row_res(const bf16 *seg_rows, const Chunk &c)
+{
+    return make_rsrc(seg_rows + c.tok0 * HD, c.nv * HD * 2);
+}
+
+// ---------------------------------------------------------------------------
+// Staging of raw rows of one chunk: item e = threadIdx.x + it NTHR (< 256)
+// -> token e >> 3, columns (e & 7) * 8 .. + 8 (byte offset 16 e).
+template <int NTHR> struct XStage {
+    static constexpr int ITEMS = (WCT * 8 + NTHR - 1) / NTHR;
+    u32x4 v[ITEMS];
 };
 
-// Loads are unconditional (rows past tend read the last valid row; the zero
-// fill happens at the store): a prefetch must not sit in a branch, or the
-// wait for it lands right after it is issued.
-template <int NTHR, int NS>
-__device__ __forceinline__ void xstage_load(const bf16 *__restrict__ r0, const bf16 *__restrict__ r1,
-                                            int tok0, int tend, XStage<NTHR, NS> &xs)
+template <int NTHR>
+__device__ __forceinline__ void xstage_load(Rsrc r, XStage<NTHR> &xs)
 {
 #pragma unroll
-    for (int it = 0; it < XStage<NTHR, NS>::ITEMS; ++it) {
-        const int e = (threadIdx.x + it * NTHR) % (NS * WCT * 8);
-        const int tok = min(tok0 + ((e >> 3) & (WCT - 1)), tend - 1);
-        const bf16 *src = (e >> 8) ? r1 : r0;
-        xs.v[it] = *reinterpret_cast<const bf16x8 *>(src + tok * HD + (e & 7) * 8);
+    for (int it = 0; it < XStage<NTHR>::ITEMS; ++it) {
+        const int e = threadIdx.x + it * NTHR;
+        xs.v[it] = bld128(r, e < WCT * 8 ? e * 16 : OOB);
     }
 }
 
-// rows -> xb[set][token][XRS] (zero past tend); kb[set][token] = -2 log2(e) / max(|x|, 1e-12)
-template <int NTHR, int NS>
-__device__ __forceinline__ void xstage_store(const XStage<NTHR, NS> &xs, int tok0, int tend,
-                                             bf16 *xb, float *kb)
+// rows -> xb[token][XRS] (rows past the chunk's end were loaded as zeros);
+// kb[token] = -2 log2(e) / max(|x|, 1e-12) (NORM2: the squared norm |x|^2)
+template <int NTHR, bool NORM2 = false>
+__device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, float *kb)
 {
 #pragma unroll
-    for (int it = 0; it < XStage<NTHR, NS>::ITEMS; ++it) {
+    for (int it = 0; it < XStage<NTHR>::ITEMS; ++it) {
         const int e = threadIdx.x + it * NTHR;
-        if (e < NS * WCT * 8) {  // uniform per wave
-            const int set = e >> 8, j = (e >> 3) & (WCT - 1);
-            const bf16x8 v = tok0 + j < tend ? xs.v[it] : pk8(0, 0, 0, 0);
-            *reinterpret_cast<bf16x8 *>(xb + (set * WCT + j) * XRS + (e & 7) * 8) = v;
+        if (e < WCT * 8) {  // uniform per wave
+            const int j = e >> 3;
+            const bf16x8 v = __builtin_bit_cast(bf16x8, xs.v[it]);
+            *reinterpret_cast<bf16x8 *>(xb + j * XRS + (e & 7) * 8) = v;
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -145,36 +185,54 @@ __device__ __forceinline__ void xstage_store(const XStage<NTHR, NS> &xs, int tok
             }
             ss = sum8(ss);
             if ((e & 7) == 0)
-                kb[set * WCT + j] = -2.8853900817779268f * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+                kb[j] = NORM2 ? ss : -2.8853900817779268f * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
         }
     }
 }
 
 // Staging of value rows y_j: [v | 1] (DVAL = false) or [dO/m | -(dO . o)/m]
-// (DVAL = true), into yc[column][YCS] (token pairs per 32-bit word).
-// Item e < 256 -> tokens 2 (e >> 4) and 2 (e >> 4) + 1, columns (e & 15) * 4 .. + 4.
+// (DVAL = true).  Item e < 256 -> tokens 2 (e >> 4) and 2 (e >> 4) + 1,
+// columns (e & 15) * 4 .. + 4.
+struct YRes {
+    Rsrc v, o, d;
+};
+template <bool DVAL>
+__device__ __forceinline__ YRes yres(const ValSrc<bf16> &s, const Chunk &c)
+{
+    YRes r;
+    r.v = row_res(s.V, c);
+    if constexpr (DVAL) {
+        r.o = row_res(s.O, c);
+        r.d = make_rsrc(s.den + c.tok0, c.nv * 4);
+    } else {
+        r.o = r.v;
+        r.d = r.v;
+    }
+    return r;
+}
+
 template <int NTHR, bool DVAL> struct YStage {
     static constexpr int ITEMS = (WCT * 8 + NTHR - 1) / NTHR;
-    bf16x4 x[ITEMS][2];
-    bf16x4 o[DVAL ? ITEMS : 1][2];
+    u32x2 x[ITEMS][2];
+    u32x2 o[DVAL ? ITEMS : 1][2];
     float m[DVAL ? ITEMS : 1][2];
 };
 
 template <int NTHR, bool DVAL>
-__device__ __forceinline__ void ystage_load(const ValSrc<bf16> &src, int tok0, int tend,
-                                            YStage<NTHR, DVAL> &ys)
+__device__ __forceinline__ void ystage_load(const YRes &r, YStage<NTHR, DVAL> &ys)
 {
 #pragma unroll
     for (int it = 0; it < YStage<NTHR, DVAL>::ITEMS; ++it) {
-        const int e = (threadIdx.x + it * NTHR) % (WCT * 8);
-        const int c0 = (e & 15) * 4;
+        const int e = threadIdx.x + it * NTHR;
+        const bool act = e < WCT * 8;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int tok = min(tok0 + 2 * ((e >> 4) & 15) + h, tend - 1);
-            ys.x[it][h] = *reinterpret_cast<const bf16x4 *>(src.V + tok * HD + c0);
+            const int tok = 2 * (e >> 4) + h;
+            const int off = act ? tok * (HD * 2) + (e & 15) * 8 : OOB;
+            ys.x[it][h] = bld64(r.v, off);
             if constexpr (DVAL) {
-                ys.o[it][h] = *reinterpret_cast<const bf16x4 *>(src.O + tok * HD + c0);
-                ys.m[it][h] = src.den[tok];
+                ys.o[it][h] = bld64(r.o, off);
+                ys.m[it][h] = bldf(r.d, act ? tok * 4 : OOB);
             }
         }
     }
@@ -182,35 +240,37 @@ __device__ __forceinline__ void ystage_load(const ValSrc<bf16> &src, int tok0, i
 
 constexpr int YRS = NCOL + 8;  // token-major value row stride
 
-// yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may be null)
+// yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may
+// be null); nv = valid rows of the chunk (the others are staged as zeros)
 template <int NTHR, bool DVAL>
-__device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int tok0, int tend,
-                                             bf16 *yc, bf16 *yr = nullptr)
+__device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int nv, bf16 *yc,
+                                             bf16 *yr = nullptr)
 {
 #pragma unroll
     for (int it = 0; it < YStage<NTHR, DVAL>::ITEMS; ++it) {
         const int e = threadIdx.x + it * NTHR;
         if (e < WCT * 8) {  // uniform per wave
-            const int jp = (e >> 4) & 15, c0 = (e & 15) * 4;
+            const int jp = e >> 4, c0 = (e & 15) * 4;
             float y[2][4], extra[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                // rows past tend were loaded from the last valid row: zero them here
-                const bool ok = tok0 + 2 * jp + h < tend;
+                const bool ok = 2 * jp + h < nv;
+                const bf16x4 xv = __builtin_bit_cast(bf16x4, ys.x[it][h]);
                 if constexpr (DVAL) {
+                    const bf16x4 ov = __builtin_bit_cast(bf16x4, ys.o[it][h]);
                     float dot = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dot += (float)ys.x[it][h][i] * (float)ys.o[it][h][i];
+                    for (int i = 0; i < 4; ++i) dot = fmaf((float)xv[i], (float)ov[i], dot);
                     dot = sum16(dot);
+                    // rows past the end read m = 0: their D row is zero
                     const float inv_m = ok ? __builtin_amdgcn_rcpf(ys.m[it][h]) : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i] * inv_m;
+                    for (int i = 0; i < 4; ++i) y[h][i] = (float)xv[i] * inv_m;
                     extra[h] = -dot * inv_m;
                 } else {
-                    const float okf = ok ? 1.f : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[h][i] = (float)ys.x[it][h][i] * okf;
-                    extra[h] = okf;
+                    for (int i = 0; i < 4; ++i) y[h][i] = (float)xv[i];
+                    extra[h] = ok ? 1.f : 0.f;
                 }
             }
             if (yc) {
@@ -453,6 +513,7 @@ __device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)
 }
 
 
+
 // ---------------------------------------------------------------------------
 // Hash-feature cache: fp16 t (and dt/du') of every row, in the kernels'
 // register layout [head][token tile of 16][wave][lane][4]: lane (g, c16) of
@@ -471,10 +532,16 @@ __device__ __forceinline__ int64_t hc_seg(const HCache &h, int64_t bh, int64_t t
 {
     return (bh * h.tiles + t_begin / 16) * (int64_t)(NW * 64 * 4);
 }
-// offset of this lane's values of tile `tile` (relative to the segment start)
-template <int NW> __device__ __forceinline__ int hc_off(int tile)
+// the two tiles of a chunk (tiles past its valid rows are skipped)
+template <int NW>
+__device__ __forceinline__ Rsrc hc_res(const _Float16 *seg, const Chunk &c)
 {
-    return ((tile * NW + wave_id()) * 64 + lane_id()) * 4;
+    return make_rsrc(seg + (c.tok0 / 16) * (NW * 64 * 4), (c.nv + 15) / 16 * (NW * 64 * 8));
+}
+// byte offset of this lane's 4 values in tile tt of the chunk
+template <int NW> __device__ __forceinline__ int hc_lane(int tt)
+{
+    return ((tt * NW + wave_id()) * 64 + lane_id()) * 8;
 }
 __device__ __forceinline__ halfx4 to_h4(const floatx4 &v)
 {
@@ -486,13 +553,16 @@ __device__ __forceinline__ floatx4 to_f4(const halfx4 &v)
     const floatx4 r = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
     return r;
 }
-
-// cached values of the two 16-token tiles of the chunk at tok0 (segment-relative)
 template <int NW>
-__device__ __forceinline__ void hc_load(const _Float16 *__restrict__ seg, int tok0, halfx4 (&v)[2])
+__device__ __forceinline__ void hc_load(Rsrc r, halfx4 (&v)[2])
 {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) v[tt] = *reinterpret_cast<const halfx4 *>(seg + hc_off<NW>(tok0 / 16 + tt));
+    for (int tt = 0; tt < 2; ++tt) v[tt] = __builtin_bit_cast(halfx4, bld64(r, hc_lane<NW>(tt)));
+}
+template <int NW>
+__device__ __forceinline__ void hc_store(Rsrc r, int tt, const floatx4 &v)
+{
+    bst64(__builtin_bit_cast(u32x2, to_h4(v)), r, hc_lane<NW>(tt));
 }
 
 // ---------------------------------------------------------------------------
@@ -515,16 +585,16 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4;
-    // segment-relative row pointers (32-bit offsets in the loop)
-    const int64_t t_begin = sg * seg;
+    // segment-relative row pointers; chunk positions go into buffer resources
+    const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const bf16 *Xs = X + (bh * N + t_begin) * HD;
+    const bf16 *Xs = X + row0 * HD;
     ValSrc<bf16> vh = vsrc;
-    vh.V += (bh * N + t_begin) * HD;
+    vh.V += row0 * HD;
     if (DVAL) {
-        vh.O += (bh * N + t_begin) * HD;
-        vh.den += bh * N + t_begin;
+        vh.O += row0 * HD;
+        vh.den += row0;
     }
     const _Float16 *cin_t = HASH ? nullptr : ci_.t + hc_seg<NW>(ci_, bh, t_begin);
     _Float16 *cout_t = co.t ? co.t + hc_seg<NW>(co, bh, t_begin) : nullptr;
@@ -538,57 +608,62 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) af[s][ct] = {0.f, 0.f, 0.f, 0.f};
-    XStage<NTHR, 1> xs;
+    auto chunk = [&](int ci) -> Chunk {
+        if (ci >= nch) return Chunk{0, 0};
+        return Chunk{ci * WCT, min(WCT, tend - ci * WCT)};
+    };
+    XStage<NTHR> xs;
     YStage<NTHR, DVAL> ys;
     halfx4 tc[2];
     ystage_zero_pad<NTHR>(ycol[0]);
     ystage_zero_pad<NTHR>(ycol[1]);
-    ystage_load<NTHR, DVAL>(vh, 0, tend, ys);
-    // chunk starts, clamped to the last chunk (prefetches past the end reload it)
-    auto cstart = [&](int ci) { return min(ci, nch - 1) * WCT; };
+    const Chunk c0 = chunk(0), c1 = chunk(1);
+    ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c0), ys);
     if (HASH) {
-        xstage_load<NTHR, 1>(Xs, Xs, 0, tend, xs);
-        xstage_store<NTHR, 1>(xs, 0, tend, xbuf[0], kbuf[0]);
+        xstage_load<NTHR>(row_res(Xs, c0), xs);
+        xstage_store<NTHR>(xs, xbuf[0], kbuf[0]);
     } else {
-        hc_load<NW>(cin_t, 0, tc);
+        hc_load<NW>(hc_res<NW>(cin_t, c0), tc);
     }
-    ystage_store<NTHR, DVAL>(ys, 0, tend, ycol[0]);
-    if (HASH) xstage_load<NTHR, 1>(Xs, Xs, cstart(1), tend, xs);
-    ystage_load<NTHR, DVAL>(vh, cstart(1), tend, ys);
+    ystage_store<NTHR, DVAL>(ys, c0.nv, ycol[0]);
+    if (HASH) xstage_load<NTHR>(row_res(Xs, c1), xs);
+    ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c1), ys);
     lds_barrier();
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
-        const int tok0 = ci * WCT;
+        const Chunk cc = chunk(ci);
         bf16x8 ptm[2][2], pfm[4];
+        Rsrc rto, rco;
+        if constexpr (HASH && (WR & 1) != 0) rto = hc_res<NW>(cout_t, cc);
+        if constexpr (HASH && (WR & 2) != 0) rco = hc_res<NW>(cout_c, cc);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             floatx4 t;
             if constexpr (HASH) {
-                const int o = hc_off<NW>(tok0 / 16 + tt);
                 if constexpr ((WR & 2) != 0) {
                     floatx4 c;
                     hash_staged_chain<POLY>(xbuf[b], kbuf[b], tt, wr, sq, t, c);
-                    *reinterpret_cast<halfx4 *>(cout_c + o) = to_h4(c);
+                    hc_store<NW>(rco, tt, c);
                 } else {
                     t = hash_staged<POLY>(xbuf[b], kbuf[b], tt, wr, sq);
                 }
-                if constexpr ((WR & 1) != 0) *reinterpret_cast<halfx4 *>(cout_t + o) = to_h4(t);
+                if constexpr ((WR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
                 t = to_f4(tc[tt]);
             }
             walsh_tm(t, q4, ptm[tt][0], ptm[tt][1]);
         }
         if (ci + 1 < nch) {  // the other buffers were last read before the previous barrier
-            if (HASH) xstage_store<NTHR, 1>(xs, tok0 + WCT, tend, xbuf[b ^ 1], kbuf[b ^ 1]);
-            ystage_store<NTHR, DVAL>(ys, tok0 + WCT, tend, ycol[b ^ 1]);
+            if (HASH) xstage_store<NTHR>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            ystage_store<NTHR, DVAL>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
         }
         if (HASH)
-            xstage_load<NTHR, 1>(Xs, Xs, cstart(ci + 2), tend, xs);
+            xstage_load<NTHR>(row_res(Xs, chunk(ci + 2)), xs);
         else
-            hc_load<NW>(cin_t, cstart(ci + 1), tc);
-        ystage_load<NTHR, DVAL>(vh, cstart(ci + 2), tend, ys);
+            hc_load<NW>(hc_res<NW>(cin_t, chunk(ci + 1)), tc);
+        ystage_load<NTHR, DVAL>(yres<DVAL>(vh, chunk(ci + 2)), ys);
         feat_major(ptm, sel, pfm);
-        // tokens past t_end have psi_0 = 1/4 but zero value rows
+        // tokens past the end have psi_0 = 1/4 but zero value rows
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + (lane & 15));
@@ -614,6 +689,9 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 //                order; intra mask j >= i; output dV = n[:, :d].
 //   Readers: RSRC = 0 hashes the rows R (RWR bit 0 / 1 store t / dt/du' into
 //   the cache rc); RSRC = 1 reads t from rc.  Writers: t from the cache wc.
+// Outputs are formed transposed (value columns x tokens: the state and value
+// operands are the A side of the MFMAs), so that a lane ends up with four
+// consecutive columns of one token.
 template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const bf16 *__restrict__ R, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
@@ -622,7 +700,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = RSRC == 0;
-    constexpr int RSLOTS = 2 * 4 * 64;  // (tile, column tile < 4, lane) partial-output slots
+    constexpr int RSLOTS = 2 * 4 * 64;  // (token tile, value column tile < 4, lane) output slots
     constexpr int RIT = (RSLOTS + NTHR - 1) / NTHR;
     __shared__ __attribute__((aligned(16))) bf16 xbuf[HASH ? WCT * XRS : 8];
     __shared__ __attribute__((aligned(16))) float kbuf[WCT];
@@ -634,7 +712,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    // segment-relative row pointers (32-bit offsets in the loop)
+    // segment-relative row pointers; chunk positions go into buffer resources
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
@@ -648,8 +726,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     bf16 *Os = Out + row0 * HD;
     float *dens = BWD ? nullptr : den + row0;
     const _Float16 *rt_seg = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
-    _Float16 *rt_out = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
-    _Float16 *rc_out = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
+    const _Float16 *rc_seg = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
     stage_wrows<NW>(W, L * NP, wl, sl);
@@ -663,37 +740,44 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             for (int ct = 0; ct < NT; ++ct)
                 acc[s][ct] = *reinterpret_cast<const floatx4 *>(src + st_idx(w, s, ct, lane, 4));
     }
-    // chunk starts in walk order (segment-relative); indices past the last
-    // chunk are clamped (prefetches beyond the end reload the last chunk)
-    auto chunk0 = [&](int ci) {
-        ci = min(ci, nch - 1);
-        return (BWD ? nch - 1 - ci : ci) * WCT;
+    // chunks in walk order
+    auto chunk = [&](int ci) -> Chunk {
+        if (ci >= nch) return Chunk{0, 0};
+        const int t0 = (BWD ? nch - 1 - ci : ci) * WCT;
+        return Chunk{t0, min(WCT, tend - t0)};
     };
 
-    XStage<NTHR, 1> xs;
+    XStage<NTHR> xs;
     YStage<NTHR, BWD> ys;
     halfx4 rt[2], wt[2];
+    const Chunk c0 = chunk(0);
     if (CAUSAL) {
         ystage_zero_pad<NTHR>(ycol);
-        ystage_load<NTHR, BWD>(vh, chunk0(0), tend, ys);
-        hc_load<NW>(wt_seg, chunk0(0), wt);
+        ystage_load<NTHR, BWD>(yres<BWD>(vh, c0), ys);
+        hc_load<NW>(hc_res<NW>(wt_seg, c0), wt);
     }
     if (HASH) {
-        xstage_load<NTHR, 1>(Rs, Rs, chunk0(0), tend, xs);
-        xstage_store<NTHR, 1>(xs, chunk0(0), tend, xbuf, kbuf);
-        xstage_load<NTHR, 1>(Rs, Rs, chunk0(1), tend, xs);
+        xstage_load<NTHR>(row_res(Rs, c0), xs);
+        xstage_store<NTHR>(xs, xbuf, kbuf);
+        xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
     } else {
-        hc_load<NW>(rt_seg, chunk0(0), rt);
+        hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     }
     lds_barrier();
 
+    // this thread's output slots: token tile, column tile, lane (g, c16)
+    auto out_off = [&](int it) {
+        const int sl = threadIdx.x + it * NTHR;
+        const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
+        return (tt * 16 + (ln & 15)) * (HD * 2) + (16 * ct + 4 * (ln >> 4)) * 2;
+    };
     float nsum[RIT][4];
-    int prev0 = 0;
+    Chunk prev = c0;
     for (int ci = 0; ci < nch; ++ci) {
-        const int tok0 = chunk0(ci);
+        const Chunk cc = chunk(ci), cn = chunk(ci + 1);
         if (CAUSAL) {
-            ystage_store<NTHR, BWD>(ys, tok0, tend, ycol);
-            ystage_load<NTHR, BWD>(vh, chunk0(ci + 1), tend, ys);
+            ystage_store<NTHR, BWD>(ys, cc.nv, ycol);
+            ystage_load<NTHR, BWD>(yres<BWD>(vh, cn), ys);
         }
         // Walsh features of this chunk's readers and writers
         bf16x8 pr[2][2], pfm[4];
@@ -701,30 +785,32 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
         WRows wr;
         if (HASH) wrows_lds<NW>(wl, wr);
+        Rsrc rto, rco;
+        if constexpr (HASH && (RWR & 1) != 0) rto = hc_res<NW>(rt_seg, cc);
+        if constexpr (HASH && (RWR & 2) != 0) rco = hc_res<NW>(rc_seg, cc);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             floatx4 t;
             if constexpr (HASH) {
-                const int o = hc_off<NW>(tok0 / 16 + tt);
                 if constexpr ((RWR & 2) != 0) {
                     floatx4 c;
                     hash_staged_chain<POLY>(xbuf, kbuf, tt, wr, sq, t, c);
-                    *reinterpret_cast<halfx4 *>(rc_out + o) = to_h4(c);
+                    hc_store<NW>(rco, tt, c);
                 } else {
                     t = hash_staged<POLY>(xbuf, kbuf, tt, wr, sq);
                 }
-                if constexpr ((RWR & 1) != 0) *reinterpret_cast<halfx4 *>(rt_out + o) = to_h4(t);
+                if constexpr ((RWR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
                 t = to_f4(rt[tt]);
             }
             walsh_tm(t, q4, pr[tt][0], pr[tt][1]);
         }
-        if (!HASH) hc_load<NW>(rt_seg, chunk0(ci + 1), rt);
+        if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, cn), rt);
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
-            hc_load<NW>(wt_seg, chunk0(ci + 1), wt);
+            hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             // scores^T tiles D[j][i] = psi_w(j) . psi_r(i) over this wave's tables
             constexpr int TJ[3] = {0, BWD ? 1 : 0, 1}, TI[3] = {0, BWD ? 0 : 1, 1};
             floatx4 sc[3];
@@ -755,25 +841,24 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         }
         lds_barrier();  // #1: value columns of this chunk staged, m of the previous one reduced
         if (!BWD && ci > 0) {
+            // outputs of the previous chunk: o = n / m
+            const Rsrc ro = row_res(Os, prev);
 #pragma unroll
             for (int it = 0; it < RIT; ++it) {
                 const int sl = threadIdx.x + it * NTHR;
                 if (sl < RSLOTS) {
-                    const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
-                    const floatx4 m = *reinterpret_cast<const floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
-                        if (tok < tend)
-                            Os[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
-                    }
+                    const float inv = __builtin_amdgcn_rcpf(mbuf[(sl >> 8) * 16 + (sl & 15)]);
+                    const u32x2 v = {pk_bf16(nsum[it][0] * inv, nsum[it][1] * inv),
+                                     pk_bf16(nsum[it][2] * inv, nsum[it][3] * inv)};
+                    bst64(v, ro, out_off(it));
                 }
             }
         }
         if (HASH) {  // the next chunk's rows (xbuf is not read again in this chunk)
-            if (ci + 1 < nch) xstage_store<NTHR, 1>(xs, chunk0(ci + 1), tend, xbuf, kbuf);
-            xstage_load<NTHR, 1>(Rs, Rs, chunk0(ci + 2), tend, xs);
+            if (ci + 1 < nch) xstage_store<NTHR>(xs, xbuf, kbuf);
+            xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         }
+        // O^T tiles (tt, ct): lane (columns 16 ct + 4g + r, token 16 tt + c16)
         floatx4 oacc[2][NT];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
@@ -788,15 +873,15 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 #pragma unroll
             for (int k = 0; k < 2; ++k)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], pr[tt][k], sf[k]);
+                for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], sf[k], pr[tt][k]);
             if (CAUSAL) {
                 const bf16x8 yb = ycol_frag(ycol, ct * 16 + c16);
                 if (BWD) {
-                    mma32(oacc[0][ct], kA8, yb);
-                    mma16(oacc[1][ct], kA4, hi4(yb));
+                    mma32(oacc[0][ct], yb, kA8);
+                    mma16(oacc[1][ct], hi4(yb), kA4);
                 } else {
-                    mma16(oacc[0][ct], kA4, lo4(yb));
-                    mma32(oacc[1][ct], kA8, yb);
+                    mma16(oacc[0][ct], lo4(yb), kA4);
+                    mma32(oacc[1][ct], yb, kA8);
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
@@ -808,6 +893,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             for (int ct = 0; ct < NT; ++ct)
                 *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * NT + ct) * 64 + lane) * 4) = oacc[tt][ct];
         lds_barrier();  // #2: partial outputs of every wave in LDS, next rows staged
+        const Rsrc ro = row_res(Os, cc);
 #pragma unroll
         for (int it = 0; it < RIT; ++it) {
             const int sl = threadIdx.x + it * NTHR;
@@ -818,45 +904,35 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 for (int ww = 0; ww < NW; ++ww)
                     n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * NT + ct) * 64 + ln) * 4);
                 if (BWD) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
-                        if (tok < tend) Os[tok * HD + ct * 16 + (ln & 15)] = (bf16)n[r];
-                    }
+                    const u32x2 v = {pk_bf16(n[0], n[1]), pk_bf16(n[2], n[3])};
+                    bst64(v, ro, out_off(it));
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) nsum[it][r] = n[r];
-                    if (ct == 0 && (ln & 15) == 0) {
-                        floatx4 m = {0.f, 0.f, 0.f, 0.f};
+                    if (ct == 0 && ln < 16) {
+                        // the count column (64) is row 0 of column tile 4: lanes 0..15, register 0
+                        float m = 0.f;
 #pragma unroll
-                        for (int ww = 0; ww < NW; ++ww)
-                            m += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * NT + 4) * 64 + ln) * 4);
-                        *reinterpret_cast<floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4)) = m;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int tok = tok0 + tt * 16 + 4 * (ln >> 4) + r;
-                            if (tok < tend) dens[tok] = m[r];
-                        }
+                        for (int ww = 0; ww < NW; ++ww) m += red[(((ww * 2 + tt) * NT + 4) * 64 + ln) * 4];
+                        mbuf[tt * 16 + ln] = m;
+                        bstf(m, make_rsrc(dens + cc.tok0, cc.nv * 4), (tt * 16 + ln) * 4);
                     }
                 }
             }
         }
-        prev0 = tok0;
+        prev = cc;
     }
     if (!BWD) {
         lds_barrier();
+        const Rsrc ro = row_res(Os, prev);
 #pragma unroll
         for (int it = 0; it < RIT; ++it) {
             const int sl = threadIdx.x + it * NTHR;
             if (sl < RSLOTS) {
-                const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
-                const floatx4 m = *reinterpret_cast<const floatx4 *>(mbuf + tt * 16 + 4 * (ln >> 4));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = prev0 + tt * 16 + 4 * (ln >> 4) + r;
-                    if (tok < tend)
-                        Os[tok * HD + ct * 16 + (ln & 15)] = (bf16)(nsum[it][r] * __builtin_amdgcn_rcpf(m[r]));
-                }
+                const float inv = __builtin_amdgcn_rcpf(mbuf[(sl >> 8) * 16 + (sl & 15)]);
+                const u32x2 v = {pk_bf16(nsum[it][0] * inv, nsum[it][1] * inv),
+                                 pk_bf16(nsum[it][2] * inv, nsum[it][3] * inv)};
+                bst64(v, ro, out_off(it));
             }
         }
     }
@@ -897,7 +973,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    // segment-relative row pointers (32-bit offsets in the loop)
+    // segment-relative row pointers; chunk positions go into buffer resources
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
@@ -933,54 +1009,56 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
 
-    auto chunk0 = [&](int ci) {
-        ci = min(ci, nch - 1);  // prefetches beyond the end reload the last chunk
-        return (REVERSE ? nch - 1 - ci : ci) * WCT;
+    auto chunk = [&](int ci) -> Chunk {
+        if (ci >= nch) return Chunk{0, 0};
+        const int t0 = (REVERSE ? nch - 1 - ci : ci) * WCT;
+        return Chunk{t0, min(WCT, tend - t0)};
     };
 
-    XStage<NTHR, 1> xs;
+    XStage<NTHR> xs;
     YStage<NTHR, RD> ysr;
     YStage<NTHR, !RD> ysw;
     halfx4 rt[2], rcv[2], wt[2];
+    const Chunk c0 = chunk(0);
     yrow_zero_pad<NTHR>(yrow_r);
     if (CAUSAL) {
         yrow_zero_pad<NTHR>(yrow_w);
         ystage_zero_pad<NTHR>(ycol_w);
-        ystage_load<NTHR, !RD>(vwh, chunk0(0), tend, ysw);
-        hc_load<NW>(wt_seg, chunk0(0), wt);
+        ystage_load<NTHR, !RD>(yres<!RD>(vwh, c0), ysw);
+        hc_load<NW>(hc_res<NW>(wt_seg, c0), wt);
     }
-    ystage_load<NTHR, RD>(vrh, chunk0(0), tend, ysr);
-    hc_load<NW>(rt_seg, chunk0(0), rt);
-    hc_load<NW>(rc_seg, chunk0(0), rcv);
-    xstage_load<NTHR, 1>(Rs, Rs, chunk0(0), tend, xs);
-    xstage_store<NTHR, 1>(xs, chunk0(0), tend, xbuf[0], kbuf[0]);
-    xstage_load<NTHR, 1>(Rs, Rs, chunk0(1), tend, xs);
+    ystage_load<NTHR, RD>(yres<RD>(vrh, c0), ysr);
+    hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
+    hc_load<NW>(hc_res<NW>(rc_seg, c0), rcv);
+    xstage_load<NTHR>(row_res(Rs, c0), xs);
+    xstage_store<NTHR, true>(xs, xbuf[0], kbuf[0]);
+    xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
     lds_barrier();
 
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
-        const int tok0 = chunk0(ci);
-        ystage_store<NTHR, RD>(ysr, tok0, tend, nullptr, yrow_r);
-        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, tok0, tend, ycol_w, yrow_w);
-        ystage_load<NTHR, RD>(vrh, chunk0(ci + 1), tend, ysr);
-        if (CAUSAL) ystage_load<NTHR, !RD>(vwh, chunk0(ci + 1), tend, ysw);
+        const Chunk cc = chunk(ci), cn = chunk(ci + 1);
+        ystage_store<NTHR, RD>(ysr, cc.nv, nullptr, yrow_r);
+        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, cc.nv, ycol_w, yrow_w);
+        ystage_load<NTHR, RD>(yres<RD>(vrh, cn), ysr);
+        if (CAUSAL) ystage_load<NTHR, !RD>(yres<!RD>(vwh, cn), ysw);
         const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
-        hc_load<NW>(rt_seg, chunk0(ci + 1), rt);
-        hc_load<NW>(rc_seg, chunk0(ci + 1), rcv);
+        hc_load<NW>(hc_res<NW>(rt_seg, cn), rt);
+        hc_load<NW>(hc_res<NW>(rc_seg, cn), rcv);
         bf16x8 pfm[4];
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
-            hc_load<NW>(wt_seg, chunk0(ci + 1), wt);
+            hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             bf16x8 sel[2];
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
         lds_barrier();  // #1: value rows of this chunk staged
         // the next chunk's raw rows into the other buffer
-        if (ci + 1 < nch) xstage_store<NTHR, 1>(xs, chunk0(ci + 1), tend, xbuf[b ^ 1], kbuf[b ^ 1]);
-        xstage_load<NTHR, 1>(Rs, Rs, chunk0(ci + 2), tend, xs);
+        if (ci + 1 < nch) xstage_store<NTHR, true>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+        xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][2];
         bf16x4 yb4[2];
@@ -1082,7 +1160,9 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             }
         }
         lds_barrier();  // #2: dxh partials of every wave in LDS
-        // sum over waves, then the normalisation backward (16 threads per row)
+        // sum over waves, then the normalisation backward (16 threads per row):
+        // dx = (dxh - x (x . dxh) / |x|^2) / |x| for |x| > 1e-12, else dxh 1e12
+        const Rsrc rdx = row_res(dXs, cc);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = threadIdx.x + it * NTHR;
@@ -1092,31 +1172,21 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             for (int ww = 0; ww < NW; ++ww)
                 dh += *reinterpret_cast<const floatx4 *>(dxp + (ww * WCT + i) * DXS + part * 4);
             const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[b] + i * XRS + part * 4);
-            float x[4], ss = 0.f, dot = 0.f;
+            float x[4], dot = 0.f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 x[c] = (float)xv[c];
-                ss = fmaf(x[c], x[c], ss);
                 dot = fmaf(dh[c], x[c], dot);
             }
-            ss = sum16(ss);
             dot = sum16(dot);
-            const int tok = tok0 + i;
-            if (e < WCT * 16 && tok < tend) {
-                const float nrm = sqrtf(ss);
-                float rv[4];
+            const float ss = kbuf[b][i];
+            const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+            const float coef = ss > 1e-24f ? dot * inv * inv : 0.f;
+            float rv[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (nrm > 1e-12f) {
-                        const float inv = 1.0f / nrm;
-                        rv[c] = (dh[c] - dot * inv * inv * x[c]) * inv;
-                    } else {
-                        rv[c] = dh[c] * 1e12f;
-                    }
-                }
-                *reinterpret_cast<bf16x4 *>(dXs + tok * HD + part * 4) =
-                    pk4(pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3]));
-            }
+            for (int c = 0; c < 4; ++c) rv[c] = (dh[c] - coef * x[c]) * inv;
+            const u32x2 v = {pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3])};
+            bst64(v, rdx, i * (HD * 2) + part * 8);
         }
     }
 }
