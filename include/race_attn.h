@@ -145,14 +145,21 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
                                     void *dK, void *dV, void *workspace, size_t ws_bytes,
                                     void *stream, const void *saved, race_trace_t *trace);
 
-/* Diagnostic: the polynomial the kernels use for t = tanh(tanh(v) / tau).
- * With e = exp(-2|v|) and y = 2e - 1, t = sign(v) * sum_k coef[k] y^k for
- * k = 0 .. *deg (Chebyshev interpolation of tanh(((1-e)/(1+e))/tau) on
- * e in [0, 1], fitted in fp64 on the host to the accuracy the dtype needs).
- * coef receives RACE_SQUASH_MAXDEG + 1 floats; *deg = -1 means the kernels
- * evaluate the function directly instead. */
+/* Diagnostic: the polynomials the bf16 kernels use for the squash
+ * t = tanh(tanh(v) / tau) and its derivative dt/dv (steps 1-2; zh §2.2).
+ * With e = exp(-2|v|) and y = 2e - 1, the kernels evaluate
+ *   t = sign(v) |sum_k coef[k] y^k|      (race_attn_squash_coeffs)
+ *   dt/dv = sum_k coef[k] y^k            (race_attn_squash_deriv_coeffs)
+ * for k = 0 .. *deg, in fp16 arithmetic (y rounded from fp32, fused
+ * multiply-adds), with fp16 coefficients (returned exactly as floats): a
+ * Chebyshev interpolation on e in [0, 1] fitted in fp64 on the host and kept
+ * when its fp16 evaluation stays within 1.5e-3 of t and 1.5e-3 max(1, 1/tau)
+ * of dt/dv.  coef receives RACE_SQUASH_MAXDEG + 1 floats (zeros past *deg).
+ * *deg = -1 means the kernels evaluate the functions directly in fp32 (always
+ * so for RACE_F32).  Pure host functions. */
 #define RACE_SQUASH_MAXDEG 16
 race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
+race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
 
 /* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);

@@ -5,6 +5,7 @@
 // mutable state.
 #include "race_attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -135,37 +136,54 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
 }
 
 // h(e) = tanh(((1 - e)/(1 + e)) / tau) on e in [0, 1], the outer tanh of
-// t = tanh(tanh(v) / tau) written through e = exp(-2|v|).
+// t = tanh(tanh(v) / tau) written through e = exp(-2|v|); g(e) = dt/dv there,
+// ((1 - h^2) / tau) (1 - z^2) with z = (1 - e)/(1 + e) = tanh(|v|).
 double squash_ref(double e, double tau) { return std::tanh(((1.0 - e) / (1.0 + e)) / tau); }
-
-// Chebyshev interpolation of h at the Chebyshev nodes of y = 2e - 1, in fp64,
-// at the kernels' fixed degree for the dtype, converted to monomial
-// coefficients in y.  Kept when its fp32 Horner evaluation stays within the
-// dtype's target on a dense grid; otherwise deg = -1 (direct evaluation).
-race::Squash fit_squash(float tau, race_dtype_t dt)
+double squash_deriv_ref(double e, double tau)
 {
-    race::Squash sq;
-    std::memset(&sq, 0, sizeof sq);
-    sq.inv_tau = 1.0f / tau;
-    sq.deg = -1;
-    const double target = dt == RACE_BF16 ? 1e-5 : 2.5e-7;
-    const int deg = dt == RACE_BF16 ? race::SqDeg<bf16>::v : race::SqDeg<float>::v;
-    constexpr int NG = 4001;
+    const double z = (1.0 - e) / (1.0 + e), h = std::tanh(z / tau);
+    return (1.0 - h * h) / tau * (1.0 - z * z);
+}
+
+// x rounded to the nearest fp16 value (ties to even; fp16 normals have 11
+// significant bits, subnormals a quantum of 2^-24)
+double round_f16(double x)
+{
+    if (x == 0.0 || !std::isfinite(x)) return x;
+    int ex;
+    std::frexp(x, &ex);
+    const double q = std::ldexp(1.0, std::max(ex - 11, -24));
+    return std::nearbyint(x / q) * q;
+}
+
+// IEEE binary16 bits of a value that is exactly representable in fp16
+uint32_t f16_bits(double v)
+{
+    uint32_t sign = std::signbit(v) ? 0x8000u : 0u;
+    v = std::fabs(v);
+    if (v == 0.0) return sign;
+    int ex;
+    const double m = std::frexp(v, &ex);  // v = m 2^ex, m in [0.5, 1)
+    const int be = ex - 1 + 15;           // biased exponent of 1.f x 2^(ex - 1)
+    if (be >= 1) return sign | ((uint32_t)be << 10) | (uint32_t)std::lround((2.0 * m - 1.0) * 1024.0);
+    return sign | (uint32_t)std::lround(v * 16777216.0);  // subnormal: v / 2^-24
+}
+
+// Chebyshev interpolation of f(., tau) at the Chebyshev nodes of y = 2e - 1,
+// in fp64, converted to monomial coefficients in y.
+void cheb_mono(double (*f)(double, double), double tau, int deg, double *mono)
+{
     const int n = deg + 1;
     double fk[race::MAXDEG + 1], a[race::MAXDEG + 1];
-    for (int k = 0; k < n; ++k) {
-        const double y = std::cos(M_PI * (k + 0.5) / n);
-        fk[k] = squash_ref(0.5 * (y + 1.0), tau);
-    }
+    for (int k = 0; k < n; ++k) fk[k] = f(0.5 * (std::cos(M_PI * (k + 0.5) / n) + 1.0), tau);
     for (int j = 0; j < n; ++j) {
         double sum = 0.0;
         for (int k = 0; k < n; ++k) sum += fk[k] * std::cos(M_PI * j * (k + 0.5) / n);
         a[j] = (j == 0 ? 1.0 : 2.0) * sum / n;
     }
-    // sum_j a_j T_j(y) in the monomial basis: T_0 = 1, T_1 = y,
-    // T_{j+1} = 2y T_j - T_{j-1}
-    double mono[race::MAXDEG + 1] = {0}, tm1[race::MAXDEG + 2] = {0}, t0[race::MAXDEG + 2] = {0},
-           t1[race::MAXDEG + 2] = {0};
+    // T_0 = 1, T_1 = y, T_{j+1} = 2y T_j - T_{j-1}
+    double tm1[race::MAXDEG + 2] = {0}, t0[race::MAXDEG + 2] = {0}, t1[race::MAXDEG + 2] = {0};
+    for (int i = 0; i <= deg; ++i) mono[i] = 0.0;
     t0[0] = 1.0;
     for (int j = 0; j < n; ++j) {
         for (int i = 0; i <= j; ++i) mono[i] += a[j] * t0[i];
@@ -178,21 +196,60 @@ race::Squash fit_squash(float tau, race_dtype_t dt)
             t0[i] = t1[i];
         }
     }
-    float c[race::MAXDEG + 1];
-    for (int i = 0; i <= deg; ++i) c[i] = (float)mono[i];
-    double err = 0.0;
+}
+
+// The bf16 kernels' squash: |t| and dt/dv as degree-DEG16 polynomials in
+// y = 2e - 1 with fp16 coefficients, evaluated in fp16 (Horner with fused
+// multiply-adds, y rounded from fp32).  The fit is kept when that evaluation,
+// emulated here on a dense grid, is within 1.5e-3 of t and within
+// 1.5e-3 max(1, 1/tau) of dt/dv (fp16 keeps t to 2.4e-4 and the bf16 Walsh
+// features to 2e-3 relative anyway); otherwise deg = -1 and the kernels
+// evaluate both functions directly in fp32.  The fp32 kernels always
+// evaluate directly.
+race::Squash fit_squash(float tau, race_dtype_t dt)
+{
+    race::Squash sq;
+    std::memset(&sq, 0, sizeof sq);
+    sq.inv_tau = 1.0f / tau;
+    sq.deg = -1;
+    if (dt != RACE_BF16) return sq;
+    constexpr int D = race::DEG16;
+    double mt[race::MAXDEG + 1], mc[race::MAXDEG + 1];
+    cheb_mono(squash_ref, tau, D, mt);
+    cheb_mono(squash_deriv_ref, tau, D, mc);
+    for (int i = 0; i <= D; ++i) {
+        mt[i] = round_f16(mt[i]);
+        mc[i] = round_f16(mc[i]);
+    }
+    constexpr int NG = 4001;
+    double et = 0.0, ec = 0.0;
     for (int k = 0; k < NG; ++k) {
         const double e = (double)k / (NG - 1);
-        const float y = 2.0f * (float)e - 1.0f;
-        float h = c[deg];
-        for (int i = deg - 1; i >= 0; --i) h = std::fma(h, y, c[i]);
-        err = std::fmax(err, std::fabs((double)h - squash_ref(e, tau)));
+        const double y = round_f16((double)std::fma(2.0f, (float)e, -1.0f));
+        double h = mt[D], c = mc[D];
+        for (int i = D - 1; i >= 0; --i) {
+            h = round_f16(h * y + mt[i]);
+            c = round_f16(c * y + mc[i]);
+        }
+        et = std::fmax(et, std::fabs(std::fabs(h) - squash_ref(e, tau)));
+        ec = std::fmax(ec, std::fabs(c - squash_deriv_ref(e, tau)));
     }
-    if (err <= target) {
-        for (int i = 0; i <= deg; ++i) sq.c[i] = c[i];
-        sq.deg = deg;
+    if (et <= 1.5e-3 && ec <= 1.5e-3 * std::fmax(1.0, 1.0 / tau)) {
+        for (int i = 0; i <= D; ++i) {
+            sq.t16[i] = f16_bits(mt[i]) * 0x10001u;
+            sq.c16[i] = f16_bits(mc[i]) * 0x10001u;
+        }
+        sq.deg = D;
     }
     return sq;
+}
+
+// value of an fp16 pair's low half
+double f16_value(uint32_t bits)
+{
+    const uint32_t b = bits & 0xffffu, e = (b >> 10) & 31u, m = b & 1023u;
+    const double v = e == 0 ? std::ldexp((double)m, -24) : std::ldexp(1.0 + m / 1024.0, (int)e - 15);
+    return (b & 0x8000u) ? -v : v;
 }
 
 race_status_t check_tau(float tau)
@@ -584,16 +641,27 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
                                  dQ, dK, dV, workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
-race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg)
+static race_status_t squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg, bool deriv)
 {
     if (!coef || !deg) return RACE_ERR_NULL;
     race_status_t st = check_tau(tau);
     if (st != RACE_OK) return st;
     if (dt != RACE_F32 && dt != RACE_BF16) return RACE_ERR_UNSUPPORTED;
     const race::Squash sq = fit_squash(tau, dt);
-    for (int i = 0; i <= race::MAXDEG; ++i) coef[i] = sq.c[i];
+    for (int i = 0; i <= race::MAXDEG; ++i)
+        coef[i] = (sq.deg >= 0 && i <= sq.deg) ? (float)f16_value(deriv ? sq.c16[i] : sq.t16[i]) : 0.f;
     *deg = sq.deg;
     return RACE_OK;
+}
+
+race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg)
+{
+    return squash_coeffs(tau, dt, coef, deg, false);
+}
+
+race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *coef, int *deg)
+{
+    return squash_coeffs(tau, dt, coef, deg, true);
 }
 
 const char *race_attn_status_string(race_status_t status)

@@ -10,18 +10,16 @@
 
 namespace race {
 
-constexpr int MAXDEG = 16;
+constexpr int MAXDEG = 16;  // coefficient slots reported by the diagnostic entry points
+constexpr int DEG16 = 6;    // degree of the fp16 squash polynomials
 
-// Polynomial degree of the squash per storage type (enough for its accuracy
-// target at the temperatures in use; the host falls back to direct
-// evaluation, deg < 0, when the fit misses the target).
-template <typename T> struct SqDeg;
-template <> struct SqDeg<bf16> { static constexpr int v = 8; };
-template <> struct SqDeg<float> { static constexpr int v = 12; };
-
+// t = tanh(tanh(u') / tau) and dt/du' as polynomials in y = 2 exp(-2|u'|) - 1,
+// evaluated by the bf16 kernels in fp16 pairs (deg < 0: the host fit missed
+// its accuracy target and the kernels evaluate the functions directly).
 struct Squash {
-    float c[MAXDEG + 1];  // monomial coefficients in y = 2e - 1
-    int deg;              // < 0: direct evaluation
+    uint32_t t16[DEG16 + 1];  // fp16 coefficients of |t|, each in both halves
+    uint32_t c16[DEG16 + 1];  // fp16 coefficients of dt/du'
+    int deg;
     float inv_tau;
 };
 

@@ -43,6 +43,18 @@ constexpr int YCS = WCT + 8; // staged value column stride (tokens)
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ halfx4 to_h4(const floatx4 &v)
+{
+    const halfx4 r = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    return r;
+}
+__device__ __forceinline__ floatx4 to_f4(const halfx4 &v)
+{
+    const floatx4 r = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    return r;
+}
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
 {
@@ -135,6 +147,10 @@ __device__ __forceinline__ void bstf(float v, Rsrc r, int off)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
+
+// Keeps the loads issued above it in place: the scheduler would otherwise
+// sink prefetches towards the end of the loop body, next to their first use.
+__device__ __forceinline__ void pin_loads() { __builtin_amdgcn_sched_barrier(0); }
 
 // A chunk of a segment: first token (segment-relative) and valid rows (0 for
 // chunk indices past the end, whose accesses are all skipped).
@@ -327,26 +343,6 @@ __device__ __forceinline__ void load_wrows(const float *__restrict__ W, int LP, 
         }
 }
 
-// t = tanh(tanh(u') / tau), u' = u / |x|, kf = -2 log2(e) / |x|
-template <bool POLY>
-__device__ __forceinline__ float squash_k(float u, float kf, const Squash &sq)
-{
-    const float e = __builtin_amdgcn_exp2f(fabsf(u) * kf);  // exp(-2|u'|)
-    float h;
-    if constexpr (POLY) {
-        constexpr int DEG = SqDeg<bf16>::v;
-        const float y = fmaf(2.f, e, -1.f);
-        h = sq.c[DEG];
-#pragma unroll
-        for (int k = DEG - 1; k >= 0; --k) h = fmaf(h, y, sq.c[k]);
-    } else {
-        const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-        const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
-        h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
-    }
-    return copysignf(h, u);
-}
-
 // 0/1 selection operand: column rho of FxC row-tile s takes token-major slot
 // (g = rho / 4, i = 4 (s & 1) + rho % 4) of K-block s / 2.
 __device__ __forceinline__ bf16x8 selection(int par)
@@ -390,32 +386,34 @@ __device__ __forceinline__ void sel_lds(const bf16 *sl, bf16x8 (&sel)[2])
     sel[1] = *reinterpret_cast<const bf16x8 *>(sl + (64 + lane_id()) * 8);
 }
 
-// t of tables 4w + g (lane (g, c16)) for token 16 tt + c16 of staged set xb
-template <bool POLY>
-__device__ __forceinline__ floatx4 hash_staged(const bf16 *xb, const float *kb, int tt, const WRows &wr,
-                                               const Squash &sq)
+// Squash of the projections u of tables 4w + g (lane (g, c16)) for token
+// 16 tt + c16 of the staged rows xb: t = tanh(tanh(u') / tau) with u' = u / |x|,
+// and with CHAIN also dt/du' = ((1 - t^2) / tau) (1 - z^2), z = tanh(|u'|),
+// 1 - z^2 = 4e / (1 + e)^2, e = exp(-2|u'|) = exp2(|u| kb).  Both are returned
+// in fp16, the precision the hash-feature cache keeps.
+//   POLY: |t| and dt/du' as degree-DEG16 polynomials in y = 2e - 1, evaluated
+//         in fp16 pairs (two values per instruction); the sign of u is copied
+//         onto the pair's sign bits.
+//   else: the functions themselves in fp32.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2v horner16(const uint32_t (&cf)[DEG16 + 1], half2v y)
 {
-    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-    const int row = tt * 16 + c16;
-    const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + g * 8);
-    const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(xb + row * XRS + 32 + g * 8);
-    floatx4 u = {0.f, 0.f, 0.f, 0.f};
-    mma32(u, wr.hi[0], x0);
-    mma32(u, wr.lo[0], x0);
-    mma32(u, wr.hi[1], x1);
-    mma32(u, wr.lo[1], x1);
-    const float kf = kb[row];
-    floatx4 t;
+    half2v h = __builtin_bit_cast(half2v, cf[DEG16]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) t[p] = squash_k<POLY>(u[p], kf, sq);
-    return t;
+    for (int k = DEG16 - 1; k >= 0; --k) h = __builtin_elementwise_fma(h, y, __builtin_bit_cast(half2v, cf[k]));
+    return h;
+}
+// the sign bits of a and b in the sign bits of an fp16 pair (low, high)
+__device__ __forceinline__ uint32_t sign_pair(float a, float b)
+{
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07000300u) &
+           0x80008000u;
 }
 
-// t and dt/du' for the readers of the gradient kernel (u' = u / |x|):
-// dt/du' = ((1 - t^2) / tau) (1 - z^2), z = tanh(|u'|), 1 - z^2 = 4e / (1 + e)^2
-template <bool POLY>
-__device__ __forceinline__ void hash_staged_chain(const bf16 *xb, const float *kb, int tt, const WRows &wr,
-                                                  const Squash &sq, floatx4 &t, floatx4 &c)
+template <bool POLY, bool CHAIN>
+__device__ __forceinline__ void hash_staged(const bf16 *xb, const float *kb, int tt, const WRows &wr,
+                                            const Squash &sq, halfx4 &t, halfx4 &c)
 {
     const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
     const int row = tt * 16 + c16;
@@ -427,24 +425,39 @@ __device__ __forceinline__ void hash_staged_chain(const bf16 *xb, const float *k
     mma32(u, wr.hi[1], x1);
     mma32(u, wr.lo[1], x1);
     const float kf = kb[row];
+    if constexpr (POLY) {
+        uint32_t tp[2], cp[2];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float e = __builtin_amdgcn_exp2f(fabsf(u[p]) * kf);
-        float h;
-        if constexpr (POLY) {
-            constexpr int DEG = SqDeg<bf16>::v;
-            const float y = fmaf(2.f, e, -1.f);
-            h = sq.c[DEG];
+        for (int q = 0; q < 2; ++q) {
+            const float e0 = __builtin_amdgcn_exp2f(fabsf(u[2 * q]) * kf);
+            const float e1 = __builtin_amdgcn_exp2f(fabsf(u[2 * q + 1]) * kf);
+            const half2v y = {(_Float16)fmaf(2.f, e0, -1.f), (_Float16)fmaf(2.f, e1, -1.f)};
+            const uint32_t h = __builtin_bit_cast(uint32_t, horner16(sq.t16, y));
+            tp[q] = (h & 0x7fff7fffu) | sign_pair(u[2 * q], u[2 * q + 1]);
+            if constexpr (CHAIN) cp[q] = __builtin_bit_cast(uint32_t, horner16(sq.c16, y));
+        }
+        const u32x2 tv = {tp[0], tp[1]};
+        t = __builtin_bit_cast(halfx4, tv);
+        if constexpr (CHAIN) {
+            const u32x2 cv = {cp[0], cp[1]};
+            c = __builtin_bit_cast(halfx4, cv);
+        }
+    } else {
+        floatx4 tf, cf;
 #pragma unroll
-            for (int k = DEG - 1; k >= 0; --k) h = fmaf(h, y, sq.c[k]);
-        } else {
+        for (int p = 0; p < 4; ++p) {
+            const float e = __builtin_amdgcn_exp2f(fabsf(u[p]) * kf);
             const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
             const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
-            h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
+            const float h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
+            tf[p] = copysignf(h, u[p]);
+            if constexpr (CHAIN) {
+                const float r = __builtin_amdgcn_rcpf(1.f + e);
+                cf[p] = (1.f - h * h) * (4.f * sq.inv_tau) * e * r * r;
+            }
         }
-        const float r = __builtin_amdgcn_rcpf(1.f + e);
-        c[p] = (1.f - h * h) * (4.f * sq.inv_tau) * e * r * r;
-        t[p] = copysignf(h, u[p]);
+        t = to_h4(tf);
+        if constexpr (CHAIN) c = to_h4(cf);
     }
 }
 
@@ -518,7 +531,6 @@ __device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)
 // Hash-feature cache: fp16 t (and dt/du') of every row, in the kernels'
 // register layout [head][token tile of 16][wave][lane][4]: lane (g, c16) of
 // wave w holds the 4 values of table 4w + g for token 16 * tile + c16.
-typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 
 struct HCache {
     _Float16 *t;    // t values (null: not stored / not read)
@@ -543,16 +555,6 @@ template <int NW> __device__ __forceinline__ int hc_lane(int tt)
 {
     return ((tt * NW + wave_id()) * 64 + lane_id()) * 8;
 }
-__device__ __forceinline__ halfx4 to_h4(const floatx4 &v)
-{
-    const halfx4 r = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    return r;
-}
-__device__ __forceinline__ floatx4 to_f4(const halfx4 &v)
-{
-    const floatx4 r = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-    return r;
-}
 template <int NW>
 __device__ __forceinline__ void hc_load(Rsrc r, halfx4 (&v)[2])
 {
@@ -560,9 +562,9 @@ __device__ __forceinline__ void hc_load(Rsrc r, halfx4 (&v)[2])
     for (int tt = 0; tt < 2; ++tt) v[tt] = __builtin_bit_cast(halfx4, bld64(r, hc_lane<NW>(tt)));
 }
 template <int NW>
-__device__ __forceinline__ void hc_store(Rsrc r, int tt, const floatx4 &v)
+__device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 {
-    bst64(__builtin_bit_cast(u32x2, to_h4(v)), r, hc_lane<NW>(tt));
+    bst64(__builtin_bit_cast(u32x2, v), r, hc_lane<NW>(tt));
 }
 
 // ---------------------------------------------------------------------------
@@ -632,36 +634,36 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const Chunk cc = chunk(ci);
+        // stage chunk ci + 1 (loaded one iteration ago) into the other buffers,
+        // which were last read before the previous barrier, then prefetch ci + 2
+        if (ci + 1 < nch) {
+            if (HASH) xstage_store<NTHR>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            ystage_store<NTHR, DVAL>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
+        }
+        const halfx4 tcur[2] = {tc[0], tc[1]};
+        if (HASH)
+            xstage_load<NTHR>(row_res(Xs, chunk(ci + 2)), xs);
+        else
+            hc_load<NW>(hc_res<NW>(cin_t, chunk(ci + 1)), tc);
+        ystage_load<NTHR, DVAL>(yres<DVAL>(vh, chunk(ci + 2)), ys);
+        if (!HASH) pin_loads();
         bf16x8 ptm[2][2], pfm[4];
         Rsrc rto, rco;
         if constexpr (HASH && (WR & 1) != 0) rto = hc_res<NW>(cout_t, cc);
         if constexpr (HASH && (WR & 2) != 0) rco = hc_res<NW>(cout_c, cc);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            floatx4 t;
+            halfx4 t;
             if constexpr (HASH) {
-                if constexpr ((WR & 2) != 0) {
-                    floatx4 c;
-                    hash_staged_chain<POLY>(xbuf[b], kbuf[b], tt, wr, sq, t, c);
-                    hc_store<NW>(rco, tt, c);
-                } else {
-                    t = hash_staged<POLY>(xbuf[b], kbuf[b], tt, wr, sq);
-                }
+                halfx4 c;
+                hash_staged<POLY, (WR & 2) != 0>(xbuf[b], kbuf[b], tt, wr, sq, t, c);
+                if constexpr ((WR & 2) != 0) hc_store<NW>(rco, tt, c);
                 if constexpr ((WR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
-                t = to_f4(tc[tt]);
+                t = tcur[tt];
             }
-            walsh_tm(t, q4, ptm[tt][0], ptm[tt][1]);
+            walsh_tm(to_f4(t), q4, ptm[tt][0], ptm[tt][1]);
         }
-        if (ci + 1 < nch) {  // the other buffers were last read before the previous barrier
-            if (HASH) xstage_store<NTHR>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            ystage_store<NTHR, DVAL>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
-        }
-        if (HASH)
-            xstage_load<NTHR>(row_res(Xs, chunk(ci + 2)), xs);
-        else
-            hc_load<NW>(hc_res<NW>(cin_t, chunk(ci + 1)), tc);
-        ystage_load<NTHR, DVAL>(yres<DVAL>(vh, chunk(ci + 2)), ys);
         feat_major(ptm, sel, pfm);
         // tokens past the end have psi_0 = 1/4 but zero value rows
 #pragma unroll
@@ -790,20 +792,16 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         if constexpr (HASH && (RWR & 2) != 0) rco = hc_res<NW>(rc_seg, cc);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            floatx4 t;
+            halfx4 t;
             if constexpr (HASH) {
-                if constexpr ((RWR & 2) != 0) {
-                    floatx4 c;
-                    hash_staged_chain<POLY>(xbuf, kbuf, tt, wr, sq, t, c);
-                    hc_store<NW>(rco, tt, c);
-                } else {
-                    t = hash_staged<POLY>(xbuf, kbuf, tt, wr, sq);
-                }
+                halfx4 c;
+                hash_staged<POLY, (RWR & 2) != 0>(xbuf, kbuf, tt, wr, sq, t, c);
+                if constexpr ((RWR & 2) != 0) hc_store<NW>(rco, tt, c);
                 if constexpr ((RWR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
-                t = to_f4(rt[tt]);
+                t = rt[tt];
             }
-            walsh_tm(t, q4, pr[tt][0], pr[tt][1]);
+            walsh_tm(to_f4(t), q4, pr[tt][0], pr[tt][1]);
         }
         if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, cn), rt);
         if (CAUSAL) {

@@ -35,8 +35,8 @@ def lib():
                                      i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.race_attn_status_string.argtypes = [i32]
     L.race_attn_status_string.restype = ctypes.c_char_p
-    L.race_attn_squash_coeffs.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_float),
-                                          ctypes.POINTER(ctypes.c_int)]
+    for fn in (L.race_attn_squash_coeffs, L.race_attn_squash_deriv_coeffs):
+        fn.argtypes = [f32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]
     return L
 
 
@@ -170,34 +170,64 @@ def test_status_strings(lib):
     assert lib.race_attn_status_string(99).decode() == "unknown status"
 
 
-def squash_numpy(coef, deg, v, tau):
-    """fp32 evaluation of the kernels' t = tanh(tanh(v)/tau) from the coefficients."""
+def f16_eval(coef, deg, v):
+    """The kernels' fp16 evaluation: y = 2 exp(-2|v|) - 1 formed in fp32 and
+    rounded to fp16, then Horner with fused multiply-adds rounded to fp16."""
     v = v.astype(np.float32)
     e = np.exp(np.float32(-2.0) * np.abs(v)).astype(np.float32)
-    if deg < 0:
-        z = (1 - e) / (1 + e)
-        h = np.tanh(z / np.float32(tau))
-    else:
-        y = (np.float32(2) * e - np.float32(1)).astype(np.float32)
-        h = np.full_like(y, np.float32(coef[deg]))
-        for k in range(deg - 1, -1, -1):
-            h = (h * y + np.float32(coef[k])).astype(np.float32)
-    return np.copysign(h, v)
+    y = (np.float32(2) * e - np.float32(1)).astype(np.float32).astype(np.float16).astype(np.float64)
+    c = np.asarray(coef, dtype=np.float64)
+    assert np.all(c.astype(np.float16).astype(np.float64) == c)  # fp16 coefficients
+    h = np.full_like(y, c[deg])
+    for k in range(deg - 1, -1, -1):
+        h = (h * y + c[k]).astype(np.float16).astype(np.float64)
+    return h
 
 
-@pytest.mark.parametrize("dt,tol", [(BF16, 1e-5), (F32, 2.5e-7)])
-@pytest.mark.parametrize("tau", [0.1, 0.25, 0.5, 1.0, 2.0, 8.0])
-def test_squash_polynomial_against_numpy_tanh(lib, dt, tol, tau):
+def coeffs(lib, fn, tau, dt):
     coef = (ctypes.c_float * 17)()
     deg = ctypes.c_int(0)
-    assert lib.race_attn_squash_coeffs(tau, dt, coef, ctypes.byref(deg)) == OK
-    v = np.concatenate([np.linspace(-12, 12, 200001), [0.0, 1e-30, -1e-30, 1e-6, 40.0]])
-    ref = np.tanh(np.tanh(v) / tau)
-    got = squash_numpy(np.array(coef[:]), deg.value, v, tau)
-    # the kernels' exp is within an ulp of numpy's; allow a few ulps of slack
-    assert np.abs(got - ref).max() <= tol + 4e-7, (deg.value, np.abs(got - ref).max())
+    assert fn(tau, dt, coef, ctypes.byref(deg)) == OK
+    return np.array(coef[:], dtype=np.float64), deg.value
+
+
+V_GRID = np.concatenate([np.linspace(-12, 12, 200001), [0.0, 1e-30, -1e-30, 1e-6, 40.0]])
+
+
+@pytest.mark.parametrize("tau", [0.1, 0.25, 0.5, 1.0, 2.0, 8.0])
+def test_squash_polynomial_against_numpy_tanh(lib, tau):
+    coef, deg = coeffs(lib, lib.race_attn_squash_coeffs, tau, BF16)
     if tau >= 0.5:
-        assert deg.value > 0  # the polynomial, not the fallback, at the workloads' tau
+        assert deg > 0  # the polynomial, not the fallback, at the workloads' tau
+    if deg < 0:
+        return
+    ref = np.tanh(np.tanh(V_GRID) / tau)
+    got = np.copysign(np.abs(f16_eval(coef, deg, V_GRID)), V_GRID)
+    assert np.abs(got - ref).max() <= 1.5e-3 + 1e-6, (deg, np.abs(got - ref).max())
+
+
+@pytest.mark.parametrize("tau", [0.1, 0.25, 0.5, 1.0, 2.0, 8.0])
+def test_squash_derivative_against_numpy(lib, tau):
+    coef, deg = coeffs(lib, lib.race_attn_squash_deriv_coeffs, tau, BF16)
+    tdeg = coeffs(lib, lib.race_attn_squash_coeffs, tau, BF16)[1]
+    assert deg == tdeg
+    if deg < 0:
+        return
+    z = np.tanh(V_GRID)
+    t = np.tanh(z / tau)
+    ref = (1 - t * t) / tau * (1 - z * z)  # d/dv tanh(tanh(v) / tau)
+    # the same derivative by central differences of the closed form
+    h = 1e-5
+    fd = (np.tanh(np.tanh(V_GRID + h) / tau) - np.tanh(np.tanh(V_GRID - h) / tau)) / (2 * h)
+    assert np.abs(fd - ref).max() < 1e-8
+    got = f16_eval(coef, deg, V_GRID)
+    assert np.abs(got - ref).max() <= 1.5e-3 * max(1.0, 1.0 / tau) + 1e-6
+
+
+def test_squash_f32_is_direct(lib):
+    for fn in (lib.race_attn_squash_coeffs, lib.race_attn_squash_deriv_coeffs):
+        coef, deg = coeffs(lib, fn, 1.0, F32)
+        assert deg == -1 and not coef.any()
 
 
 def test_squash_rejects_bad_tau(lib):
