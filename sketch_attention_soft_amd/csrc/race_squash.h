@@ -30,26 +30,23 @@ __device__ __forceinline__ int64_t st_idx(int w, int a, int ct, int lane, int at
     return ((((int64_t)w * at + a) * NT + ct) * 64 + lane) * 4;
 }
 
-// dt_p = d(sum_S dpsi_S psi_S)/dt_p for one table: the multilinear polynomial
-// with coefficients dpsi_{S u p}, S over the other three bits, evaluated at t.
+// Gradient of the Walsh features of one table: with
+// P(t) = sum_S dpsi_S prod_{p in S} t_p (the features without their common
+// factor 1/4), dt[p] = dP/dt_p.  P is multilinear: contracting t_3, then t_2
+// and t_1, yields the four partial derivatives in 24 fused multiply-adds.
 __device__ __forceinline__ void walsh_grad(const float dp[16], const floatx4 &t, float dt[4])
 {
+    float a[8], c[4], b[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        int o[3], n = 0;
+    for (int i = 0; i < 8; ++i) a[i] = fmaf(t[3], dp[i + 8], dp[i]);  // P with t_3 contracted
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            if (b != p) o[n++] = b;
-        float m[4];
+    for (int i = 0; i < 4; ++i) c[i] = fmaf(t[2], dp[i + 12], dp[i + 8]);
+    dt[3] = fmaf(t[0], fmaf(t[1], c[3], c[1]), fmaf(t[1], c[2], c[0]));
+    dt[2] = fmaf(t[0], fmaf(t[1], a[7], a[5]), fmaf(t[1], a[6], a[4]));
 #pragma unroll
-        for (int yz = 0; yz < 4; ++yz) {
-            const int base = (1 << p) | ((yz & 1) << o[1]) | ((yz >> 1) << o[2]);
-            m[yz] = fmaf(t[o[0]], dp[base | (1 << o[0])], dp[base]);
-        }
-        const float n0 = fmaf(t[o[1]], m[1], m[0]);
-        const float n1 = fmaf(t[o[1]], m[3], m[2]);
-        dt[p] = 0.25f * fmaf(t[o[2]], n1, n0);
-    }
+    for (int i = 0; i < 4; ++i) b[i] = fmaf(t[2], a[i + 4], a[i]);  // then t_2
+    dt[1] = fmaf(t[0], b[3], b[2]);
+    dt[0] = fmaf(t[1], b[3], b[1]);
 }
 
 }  // namespace race

@@ -86,15 +86,6 @@ __device__ __forceinline__ void mma32(floatx4 &acc, bf16x8 a, bf16x8 b)
 {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
-// K = 16 products as 16x16x32 MFMAs with a zero upper half: accumulation
-// chains that mixed v_mfma_f32_16x16x16_bf16 with the 16x16x32 form gave
-// wrong sums on gfx950 in these kernels, so only the 16x16x32 form is used.
-__device__ __forceinline__ void mma16(floatx4 &acc, bf16x4 a, bf16x4 b)
-{
-    const bf16x4 z = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(a, z), cat8(b, z), acc, 0, 0, 0);
-}
-
 // Sums over aligned groups of 8 / 16 lanes (DPP within a row).
 __device__ __forceinline__ float dpp_add(float x, int ctrl_sel)
 {
@@ -254,7 +245,10 @@ __device__ __forceinline__ void ystage_load(const YRes &r, YStage<NTHR, DVAL> &y
     }
 }
 
-constexpr int YRS = NCOL + 8;  // token-major value row stride
+// token-major value rows: columns 0 .. NCOL + 15 (three K = 32 operand groups,
+// zero past column HD) and 8 of padding
+constexpr int YRC = NCOL + 16;
+constexpr int YRS = YRC + 8;
 
 // yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may
 // be null); nv = valid rows of the chunk (the others are staged as zeros)
@@ -317,8 +311,8 @@ template <int NTHR> __device__ __forceinline__ void ystage_zero_pad(bf16 *yc)
 }
 template <int NTHR> __device__ __forceinline__ void yrow_zero_pad(bf16 *yr)
 {
-    for (int e = threadIdx.x; e < (NCOL - HD - 1) * WCT; e += NTHR) {
-        const int c = HD + 1 + e % (NCOL - HD - 1), j = e / (NCOL - HD - 1);
+    for (int e = threadIdx.x; e < (YRC - HD - 1) * WCT; e += NTHR) {
+        const int c = HD + 1 + e % (YRC - HD - 1), j = e / (YRC - HD - 1);
         yr[j * YRS + c] = (bf16)0.f;
     }
 }
@@ -514,15 +508,14 @@ __device__ __forceinline__ void load_state_cxf(const float *__restrict__ src, fl
 }
 
 // value-row operand of 16 tokens (token-major): columns 32k + 4g + r (slots
-// r < 4) and 32k + 16 + 4g + r (slots 4 + r), k = 0, 1; plus columns 64 + 4g + r
-__device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)[2], bf16x4 &f4)
+// r < 4) and 32k + 16 + 4g + r (slots 4 + r), k = 0, 1, 2 (zero past column HD)
+__device__ __forceinline__ void yrow_frags(const bf16 *yr, int row, bf16x8 (&f8)[3])
 {
     const int g = lane_id() >> 4;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 3; ++k)
         f8[k] = cat8(*reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 4 * g),
                      *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 32 * k + 16 + 4 * g));
-    f4 = *reinterpret_cast<const bf16x4 *>(yr + row * YRS + 64 + 4 * g);
 }
 
 
@@ -783,7 +776,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         }
         // Walsh features of this chunk's readers and writers
         bf16x8 pr[2][2], pfm[4];
-        bf16x4 kA4;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
+        bf16x8 kA1;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
         bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
         WRows wr;
         if (HASH) wrows_lds<NW>(wl, wr);
@@ -826,11 +819,13 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                     const bool keep = BWD ? (4 * g + r >= c16) : (4 * g + r <= c16);
                     sc[pi][r] = keep ? sc[pi][r] : 0.f;
                 }
+            // operands over both writer tiles (the masked-out tile is zero)
+            const bf16x4 z4 = pk4(0, 0);
             if (BWD) {
                 kA8 = cat8(acc2bf4(sc[0]), acc2bf4(sc[1]));  // reader tile 0: writer tiles 0, 1
-                kA4 = acc2bf4(sc[2]);                        // reader tile 1: writer tile 1
+                kA1 = cat8(z4, acc2bf4(sc[2]));              // reader tile 1: writer tile 1
             } else {
-                kA4 = acc2bf4(sc[0]);                        // reader tile 0: writer tile 0
+                kA1 = cat8(acc2bf4(sc[0]), z4);              // reader tile 0: writer tile 0
                 kA8 = cat8(acc2bf4(sc[1]), acc2bf4(sc[2]));  // reader tile 1: writer tiles 0, 1
             }
             bf16x8 sel[2];
@@ -874,13 +869,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], sf[k], pr[tt][k]);
             if (CAUSAL) {
                 const bf16x8 yb = ycol_frag(ycol, ct * 16 + c16);
-                if (BWD) {
-                    mma32(oacc[0][ct], yb, kA8);
-                    mma16(oacc[1][ct], hi4(yb), kA4);
-                } else {
-                    mma16(oacc[0][ct], lo4(yb), kA4);
-                    mma32(oacc[1][ct], yb, kA8);
-                }
+                mma32(oacc[0][ct], yb, BWD ? kA8 : kA1);
+                mma32(oacc[1][ct], yb, BWD ? kA1 : kA8);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
             }
@@ -897,9 +887,9 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             const int sl = threadIdx.x + it * NTHR;
             if (sl < RSLOTS) {
                 const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
-                floatx4 n = {0.f, 0.f, 0.f, 0.f};
+                floatx4 n = *reinterpret_cast<const floatx4 *>(red + ((tt * NT + ct) * 64 + ln) * 4);
 #pragma unroll
-                for (int ww = 0; ww < NW; ++ww)
+                for (int ww = 1; ww < NW; ++ww)
                     n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * NT + ct) * 64 + ln) * 4);
                 if (BWD) {
                     const u32x2 v = {pk_bf16(n[0], n[1]), pk_bf16(n[2], n[3])};
@@ -909,9 +899,9 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                     for (int r = 0; r < 4; ++r) nsum[it][r] = n[r];
                     if (ct == 0 && ln < 16) {
                         // the count column (64) is row 0 of column tile 4: lanes 0..15, register 0
-                        float m = 0.f;
+                        float m = red[((tt * NT + 4) * 64 + ln) * 4];
 #pragma unroll
-                        for (int ww = 0; ww < NW; ++ww) m += red[(((ww * 2 + tt) * NT + 4) * 64 + ln) * 4];
+                        for (int ww = 1; ww < NW; ++ww) m += red[(((ww * 2 + tt) * NT + 4) * 64 + ln) * 4];
                         mbuf[tt * 16 + ln] = m;
                         bstf(m, make_rsrc(dens + cc.tok0, cc.nv * 4), (tt * 16 + ln) * 4);
                     }
@@ -957,15 +947,16 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
     constexpr int NTHR = NW * 64;
-    constexpr int DXS = HD + 4;  // dxh partial row stride (floats)
-    constexpr int NIT = (WCT * 16 + NTHR - 1) / NTHR;
+    constexpr int DUS = NW * 16 + 8;  // du row stride (bf16)
+    constexpr int TPWV = 8 / NW;      // dxh tiles per wave
     constexpr int WTS = NW * 16 + 8;  // staged W^T row stride
     __shared__ __attribute__((aligned(16))) bf16 xbuf[2][WCT * XRS];
     __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
     __shared__ __attribute__((aligned(16))) bf16 yrow_r[WCT * YRS];
     __shared__ __attribute__((aligned(16))) bf16 yrow_w[CAUSAL ? WCT * YRS : 8];
     __shared__ __attribute__((aligned(16))) bf16 ycol_w[CAUSAL ? NCOL * YCS : 8];
-    __shared__ __attribute__((aligned(16))) float dxp[NW * WCT * DXS];
+    __shared__ __attribute__((aligned(16))) bf16 du_l[WCT * DUS];
+    __shared__ __attribute__((aligned(16))) float dotp[WCT * 16];  // partial x . dxh [token][nt][g]
     __shared__ __attribute__((aligned(16))) bf16 wt_l[2 * HD * WTS];  // W^T hi, lo: [dim][hyperplane]
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
 
@@ -991,10 +982,11 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
-    // W^T (hi, lo) and the selection operands, once per workgroup
+    // W^T (hi, lo) and the selection operands, once per workgroup; W^T carries
+    // the factor 1/4 of the Walsh features (exact), which walsh_grad leaves out
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
         const int hp = e / HD, c = e % HD;
-        const float v = hp < L * NP ? W[hp * HD + c] : 0.f;
+        const float v = hp < L * NP ? 0.25f * W[hp * HD + c] : 0.f;
         const bf16 hi = (bf16)v;
         wt_l[c * WTS + hp] = hi;
         wt_l[(HD + c) * WTS + hp] = (bf16)(v - (float)hi);
@@ -1033,6 +1025,37 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
     lds_barrier();
 
+    // the previous chunk's dxh tiles, finished one barrier later (when the
+    // partial dots of every wave are in LDS): the normalisation backward
+    // dx = (dxh - x (x . dxh) / |x|^2) / |x| for |x| > 1e-12, else dxh 1e12
+    floatx4 dxh[TPWV];
+    bf16x4 xkeep[TPWV];
+    float sskeep[TPWV];
+    bool have_prev = false;
+    Chunk prev = c0;
+    auto finish_prev = [&]() {
+        if (!have_prev) return;
+        const Rsrc rdx = row_res(dXs, prev);
+#pragma unroll
+        for (int i = 0; i < TPWV; ++i) {
+            const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
+            float dot = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(dotp + tok * 16 + 4 * q);
+                dot += (v[0] + v[1]) + (v[2] + v[3]);
+            }
+            const float ss = sskeep[i];
+            const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+            const float coef = ss > 1e-24f ? dot * inv * inv : 0.f;
+            float rv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rv[r] = (dxh[i][r] - coef * (float)xkeep[i][r]) * inv;
+            const u32x2 v = {pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3])};
+            bst64(v, rdx, tok * (HD * 2) + (nt * 16 + 4 * g) * 2);
+        }
+    };
+
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
@@ -1053,22 +1076,21 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
-        lds_barrier();  // #1: value rows of this chunk staged
+        lds_barrier();  // #1: value rows of this chunk staged, partial dots of the previous one
+        finish_prev();
         // the next chunk's raw rows into the other buffer
         if (ci + 1 < nch) xstage_store<NTHR, true>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
         xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         // reader value rows as B operands (token-major)
-        bf16x8 yb8[2][2];
-        bf16x4 yb4[2];
+        bf16x8 yb8[2][3];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) yrow_frags(yrow_r, tt * 16 + c16, yb8[tt], yb4[tt]);
+        for (int tt = 0; tt < 2; ++tt) yrow_frags(yrow_r, tt * 16 + c16, yb8[tt]);
         floatx4 dps[4][2];  // dpsi^T tiles (s, tt): lane (rows 4g + r <-> S = 4s + r of table 4w + g, token c16)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) dps[s][tt] = {0.f, 0.f, 0.f, 0.f};
-        bf16x8 eb8;
-        bf16x4 eb4;
+        bf16x8 eb8, eb1;
         if (CAUSAL) {
             // E^T tiles D[j][i] = y_w(j) . y_r(i) over all value columns
             constexpr int TJ[3] = {0, REVERSE ? 1 : 0, 1}, TI[3] = {0, REVERSE ? 0 : 1, 1};
@@ -1077,15 +1099,13 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             for (int pi = 0; pi < 3; ++pi) et[pi] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tj = 0; tj < 2; ++tj) {
-                bf16x8 wa8[2];
-                bf16x4 wa4;
-                yrow_frags(yrow_w, tj * 16 + c16, wa8, wa4);
+                bf16x8 wa8[3];
+                yrow_frags(yrow_w, tj * 16 + c16, wa8);
 #pragma unroll
                 for (int pi = 0; pi < 3; ++pi) {
                     if (TJ[pi] != tj) continue;
 #pragma unroll
-                    for (int k = 0; k < 2; ++k) mma32(et[pi], wa8[k], yb8[TI[pi]][k]);
-                    mma16(et[pi], wa4, yb4[TI[pi]]);
+                    for (int k = 0; k < 3; ++k) mma32(et[pi], wa8[k], yb8[TI[pi]][k]);
                 }
             }
 #pragma unroll
@@ -1095,11 +1115,13 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                     const bool keep = REVERSE ? (4 * g + r >= c16) : (4 * g + r <= c16);
                     et[pi][r] = keep ? et[pi][r] : 0.f;
                 }
+            // operands over both writer tiles (the masked-out tile is zero)
+            const bf16x4 z4 = pk4(0, 0);
             if (REVERSE) {
                 eb8 = cat8(acc2bf4(et[0]), acc2bf4(et[1]));  // reader tile 0: writer tiles 0, 1
-                eb4 = acc2bf4(et[2]);                        // reader tile 1: writer tile 1
+                eb1 = cat8(z4, acc2bf4(et[2]));              // reader tile 1: writer tile 1
             } else {
-                eb4 = acc2bf4(et[0]);                        // reader tile 0: writer tile 0
+                eb1 = cat8(acc2bf4(et[0]), z4);              // reader tile 0: writer tile 0
                 eb8 = cat8(acc2bf4(et[1]), acc2bf4(et[2]));  // reader tile 1: writer tiles 0, 1
             }
         }
@@ -1110,20 +1132,16 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             bf16x8 sa[3];
             sa[0] = cat8(acc2bf4(acc[s][0]), acc2bf4(acc[s][1]));
             sa[1] = cat8(acc2bf4(acc[s][2]), acc2bf4(acc[s][3]));
-            sa[2] = cat8(acc2bf4(acc[s][4]), pk4(0, 0));
+            // columns 80 .. 95 of the value rows are zero: any finite upper half
+            const bf16x4 s4 = acc2bf4(acc[s][4]);
+            sa[2] = cat8(s4, s4);
 #pragma unroll
             for (int k = 0; k < 3; ++k)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-                    mma32(dps[s][tt], sa[k], k < 2 ? yb8[tt][k] : cat8(yb4[tt], pk4(0, 0)));
+                for (int tt = 0; tt < 2; ++tt) mma32(dps[s][tt], sa[k], yb8[tt][k]);
             if (CAUSAL) {
-                if (REVERSE) {
-                    mma32(dps[s][0], pfm[s], eb8);
-                    mma16(dps[s][1], hi4(pfm[s]), eb4);
-                } else {
-                    mma16(dps[s][0], lo4(pfm[s]), eb4);
-                    mma32(dps[s][1], pfm[s], eb8);
-                }
+                mma32(dps[s][0], pfm[s], REVERSE ? eb8 : eb1);
+                mma32(dps[s][1], pfm[s], REVERSE ? eb1 : eb8);
             }
         }
         if (CAUSAL) {
@@ -1135,7 +1153,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], ya, pfm[s]);
             }
         }
-        // Walsh gradient -> du -> dxh^T partial over this wave's hyperplanes
+        // Walsh gradient -> du of this wave's 16 hyperplanes (token-major, LDS)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             float dp[16], dt[4];
@@ -1145,48 +1163,38 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 for (int r = 0; r < 4; ++r) dp[4 * s + r] = dps[s][tt][r];
             walsh_grad(dp, to_f4(trh[tt]), dt);
             const floatx4 cr = to_f4(crh[tt]);
-            const bf16x4 du = pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                // W^T operand: lane (dim 16 nt + c16, hyperplanes 16w + 4g .. + 3), hi and lo
-                const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + w * 16 + 4 * g;
-                const bf16x4 whi = *reinterpret_cast<const bf16x4 *>(wrow);
-                const bf16x4 wlo = *reinterpret_cast<const bf16x4 *>(wrow + HD * WTS);
-                floatx4 xa = {0.f, 0.f, 0.f, 0.f};
-                mma32(xa, cat8(whi, wlo), cat8(du, du));  // (W_hi + W_lo)^T du^T
-                *reinterpret_cast<floatx4 *>(dxp + (w * WCT + tt * 16 + c16) * DXS + nt * 16 + 4 * g) = xa;
-            }
+            *reinterpret_cast<bf16x4 *>(du_l + (tt * 16 + c16) * DUS + w * 16 + 4 * g) =
+                pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
         }
-        lds_barrier();  // #2: dxh partials of every wave in LDS
-        // sum over waves, then the normalisation backward (16 threads per row):
-        // dx = (dxh - x (x . dxh) / |x|^2) / |x| for |x| > 1e-12, else dxh 1e12
-        const Rsrc rdx = row_res(dXs, cc);
+        lds_barrier();  // #2: du of every wave in LDS
+        // dxh^T tiles (tt, nt) over all hyperplanes (W^T hi + lo); tile
+        // (tt, nt) = wave + NW i.  Lane (g, c16): token 16 tt + c16, dims
+        // 16 nt + 4g + r; the partial dot with x of those 4 dims goes to LDS.
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int e = threadIdx.x + it * NTHR;
-            const int i = (e >> 4) & (WCT - 1), part = e & 15;
-            floatx4 dh = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < TPWV; ++i) {
+            const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
+            floatx4 xa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww)
-                dh += *reinterpret_cast<const floatx4 *>(dxp + (ww * WCT + i) * DXS + part * 4);
-            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[b] + i * XRS + part * 4);
-            float x[4], dot = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                x[c] = (float)xv[c];
-                dot = fmaf(dh[c], x[c], dot);
+            for (int k = 0; k < NW / 2; ++k) {
+                const bf16x8 dub = *reinterpret_cast<const bf16x8 *>(du_l + tok * DUS + 32 * k + 8 * g);
+                const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + 32 * k + 8 * g;
+                mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow), dub);
+                mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow + HD * WTS), dub);
             }
-            dot = sum16(dot);
-            const float ss = kbuf[b][i];
-            const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
-            const float coef = ss > 1e-24f ? dot * inv * inv : 0.f;
-            float rv[4];
+            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[b] + tok * XRS + nt * 16 + 4 * g);
+            float dot = 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) rv[c] = (dh[c] - coef * x[c]) * inv;
-            const u32x2 v = {pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3])};
-            bst64(v, rdx, i * (HD * 2) + part * 8);
+            for (int r = 0; r < 4; ++r) dot = fmaf(xa[r], (float)xv[r], dot);
+            dotp[tok * 16 + nt * 4 + g] = dot;
+            dxh[i] = xa;
+            xkeep[i] = xv;
+            sskeep[i] = kbuf[b][tok];
         }
+        have_prev = true;
+        prev = cc;
     }
+    lds_barrier();
+    finish_prev();
 }
 
 }  // namespace race
