@@ -797,6 +797,27 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             walsh_tm(to_f4(t), q4, pr[tt][0], pr[tt][1]);
         }
         if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, cn), rt);
+        lds_barrier();  // #1: value columns of this chunk staged, m of the previous one reduced
+        if (!BWD && ci > 0) {
+            // outputs of the previous chunk: o = n / m
+            const Rsrc ro = row_res(Os, prev);
+#pragma unroll
+            for (int it = 0; it < RIT; ++it) {
+                const int sl = threadIdx.x + it * NTHR;
+                if (sl < RSLOTS) {
+                    const float inv = __builtin_amdgcn_rcpf(mbuf[(sl >> 8) * 16 + (sl & 15)]);
+                    const u32x2 v = {pk_bf16(nsum[it][0] * inv, nsum[it][1] * inv),
+                                     pk_bf16(nsum[it][2] * inv, nsum[it][3] * inv)};
+                    bst64(v, ro, out_off(it));
+                }
+            }
+        }
+        if (HASH) {  // the next chunk's rows (xbuf is not read again in this chunk)
+            if (ci + 1 < nch) xstage_store<NTHR>(xs, xbuf, kbuf);
+            xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
+        }
+        // writer features, masked scores and feature-major operands after the
+        // barrier, next to the MFMA-bound products that consume them
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
@@ -831,25 +852,6 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             bf16x8 sel[2];
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
-        }
-        lds_barrier();  // #1: value columns of this chunk staged, m of the previous one reduced
-        if (!BWD && ci > 0) {
-            // outputs of the previous chunk: o = n / m
-            const Rsrc ro = row_res(Os, prev);
-#pragma unroll
-            for (int it = 0; it < RIT; ++it) {
-                const int sl = threadIdx.x + it * NTHR;
-                if (sl < RSLOTS) {
-                    const float inv = __builtin_amdgcn_rcpf(mbuf[(sl >> 8) * 16 + (sl & 15)]);
-                    const u32x2 v = {pk_bf16(nsum[it][0] * inv, nsum[it][1] * inv),
-                                     pk_bf16(nsum[it][2] * inv, nsum[it][3] * inv)};
-                    bst64(v, ro, out_off(it));
-                }
-            }
-        }
-        if (HASH) {  // the next chunk's rows (xbuf is not read again in this chunk)
-            if (ci + 1 < nch) xstage_store<NTHR>(xs, xbuf, kbuf);
-            xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         }
         // O^T tiles (tt, ct): lane (columns 16 ct + 4g + r, token 16 tt + c16)
         floatx4 oacc[2][NT];
