@@ -261,27 +261,43 @@ __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int n
         const int e = threadIdx.x + it * NTHR;
         if (e < WCT * 8) {  // uniform per wave
             const int jp = e >> 4, c0 = (e & 15) * 4;
+            if constexpr (!DVAL) {
+                // [v | 1]: the loaded bf16 bits are staged as they are; the column
+                // layout pairs tokens 2jp, 2jp + 1 of each column by byte permutes
+                if (yc) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<uint32_t *>(yc + (c0 + i) * YCS + 2 * jp) =
+                            __builtin_amdgcn_perm(ys.x[it][1][i >> 1], ys.x[it][0][i >> 1],
+                                                  (i & 1) ? 0x07060302u : 0x05040100u);
+                    if (c0 == 0)
+                        *reinterpret_cast<uint32_t *>(yc + HD * YCS + 2 * jp) =
+                            pk_bf16(2 * jp < nv ? 1.f : 0.f, 2 * jp + 1 < nv ? 1.f : 0.f);
+                }
+                if (yr) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        *reinterpret_cast<u32x2 *>(yr + (2 * jp + h) * YRS + c0) = ys.x[it][h];
+                        if (c0 == 0) yr[(2 * jp + h) * YRS + HD] = (bf16)(2 * jp + h < nv ? 1.f : 0.f);
+                    }
+                }
+                continue;
+            }
             float y[2][4], extra[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool ok = 2 * jp + h < nv;
                 const bf16x4 xv = __builtin_bit_cast(bf16x4, ys.x[it][h]);
-                if constexpr (DVAL) {
-                    const bf16x4 ov = __builtin_bit_cast(bf16x4, ys.o[it][h]);
-                    float dot = 0.f;
+                const bf16x4 ov = __builtin_bit_cast(bf16x4, ys.o[it][h]);
+                float dot = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dot = fmaf((float)xv[i], (float)ov[i], dot);
-                    dot = sum16(dot);
-                    // rows past the end read m = 0: their D row is zero
-                    const float inv_m = ok ? __builtin_amdgcn_rcpf(ys.m[it][h]) : 0.f;
+                for (int i = 0; i < 4; ++i) dot = fmaf((float)xv[i], (float)ov[i], dot);
+                dot = sum16(dot);
+                // rows past the end read m = 0: their D row is zero
+                const float inv_m = ok ? __builtin_amdgcn_rcpf(ys.m[it][h]) : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) y[h][i] = (float)xv[i] * inv_m;
-                    extra[h] = -dot * inv_m;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) y[h][i] = (float)xv[i];
-                    extra[h] = ok ? 1.f : 0.f;
-                }
+                for (int i = 0; i < 4; ++i) y[h][i] = (float)xv[i] * inv_m;
+                extra[h] = -dot * inv_m;
             }
             if (yc) {
 #pragma unroll
