@@ -716,7 +716,9 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     __shared__ __attribute__((aligned(16))) bf16 xbuf[HASH ? WCT * XRS : 8];
     __shared__ __attribute__((aligned(16))) float kbuf[WCT];
     __shared__ __attribute__((aligned(16))) bf16 ycol[CAUSAL ? NCOL * YCS : 8];
-    __shared__ __attribute__((aligned(16))) float red[NW * 2 * NT * 64 * 4];
+    // partial outputs of every wave: value columns (4 tiles) and the count column
+    __shared__ __attribute__((aligned(16))) float red[NW * 2 * 4 * 64 * 4];
+    __shared__ __attribute__((aligned(16))) float redm[NW * 2 * 64];
     __shared__ __attribute__((aligned(16))) float mbuf[WCT];
     __shared__ __attribute__((aligned(16))) bf16 wl[HASH ? 2 * NW * 16 * XRS : 8];
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
@@ -894,10 +896,14 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             }
         }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct)
-                *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * NT + ct) * 64 + lane) * 4) = oacc[tt][ct];
+            for (int ct = 0; ct < 4; ++ct)
+                *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * 4 + ct) * 64 + lane) * 4) = oacc[tt][ct];
+            // the count column (64) is row 0 of column tile 4: register 0 of lanes
+            // 0..15 (the other lanes' values are not read)
+            redm[(w * 2 + tt) * 64 + lane] = oacc[tt][4][0];
+        }
         lds_barrier();  // #2: partial outputs of every wave in LDS, next rows staged
         const Rsrc ro = row_res(Os, cc);
 #pragma unroll
@@ -905,10 +911,10 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             const int sl = threadIdx.x + it * NTHR;
             if (sl < RSLOTS) {
                 const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
-                floatx4 n = *reinterpret_cast<const floatx4 *>(red + ((tt * NT + ct) * 64 + ln) * 4);
+                floatx4 n = *reinterpret_cast<const floatx4 *>(red + ((tt * 4 + ct) * 64 + ln) * 4);
 #pragma unroll
                 for (int ww = 1; ww < NW; ++ww)
-                    n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * NT + ct) * 64 + ln) * 4);
+                    n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * 4 + ct) * 64 + ln) * 4);
                 if (BWD) {
                     const u32x2 v = {pk_bf16(n[0], n[1]), pk_bf16(n[2], n[3])};
                     bst64(v, ro, out_off(it));
@@ -916,10 +922,9 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) nsum[it][r] = n[r];
                     if (ct == 0 && ln < 16) {
-                        // the count column (64) is row 0 of column tile 4: lanes 0..15, register 0
-                        float m = red[((tt * NT + 4) * 64 + ln) * 4];
+                        float m = redm[tt * 64 + ln];
 #pragma unroll
-                        for (int ww = 1; ww < NW; ++ww) m += red[(((ww * 2 + tt) * NT + 4) * 64 + ln) * 4];
+                        for (int ww = 1; ww < NW; ++ww) m += redm[(ww * 2 + tt) * 64 + ln];
                         mbuf[tt * 16 + ln] = m;
                         bstf(m, make_rsrc(dens + cc.tok0, cc.nv * 4), (tt * 16 + ln) * 4);
                     }
