@@ -980,7 +980,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     __shared__ __attribute__((aligned(16))) bf16 ycol_w[CAUSAL ? NCOL * YCS : 8];
     __shared__ __attribute__((aligned(16))) bf16 du_l[WCT * DUS];
     __shared__ __attribute__((aligned(16))) float dotp[WCT * 16];  // partial x . dxh [token][nt][g]
-    __shared__ __attribute__((aligned(16))) bf16 wt_l[2 * HD * WTS];  // W^T hi, lo: [dim][hyperplane]
+    __shared__ __attribute__((aligned(16))) bf16 wt_l[HD * WTS];  // W^T (bf16): [dim][hyperplane]
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
@@ -1005,14 +1005,13 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
-    // W^T (hi, lo) and the selection operands, once per workgroup; W^T carries
-    // the factor 1/4 of the Walsh features (exact), which walsh_grad leaves out
+    // W^T and the selection operands, once per workgroup.  dxh = du W takes W
+    // in bf16, the precision of du itself (the forward projection keeps W to
+    // about 16 bits as bf16 hi + lo); W^T carries the factor 1/4 of the Walsh
+    // features (exact), which walsh_grad leaves out.
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
         const int hp = e / HD, c = e % HD;
-        const float v = hp < L * NP ? 0.25f * W[hp * HD + c] : 0.f;
-        const bf16 hi = (bf16)v;
-        wt_l[c * WTS + hp] = hi;
-        wt_l[(HD + c) * WTS + hp] = (bf16)(v - (float)hi);
+        wt_l[c * WTS + hp] = (bf16)(hp < L * NP ? 0.25f * W[hp * HD + c] : 0.f);
     }
     if (threadIdx.x < 64) {
         *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
@@ -1190,7 +1189,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
         }
         lds_barrier();  // #2: du of every wave in LDS
-        // dxh^T tiles (tt, nt) over all hyperplanes (W^T hi + lo); tile
+        // dxh^T tiles (tt, nt) over all hyperplanes; tile
         // (tt, nt) = wave + NW i.  Lane (g, c16): token 16 tt + c16, dims
         // 16 nt + 4g + r; the partial dot with x of those 4 dims goes to LDS.
 #pragma unroll
@@ -1202,7 +1201,6 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 const bf16x8 dub = *reinterpret_cast<const bf16x8 *>(du_l + tok * DUS + 32 * k + 8 * g);
                 const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + 32 * k + 8 * g;
                 mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow), dub);
-                mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow + HD * WTS), dub);
             }
             const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[b] + tok * XRS + nt * 16 + 4 * g);
             float dot = 0.f;
