@@ -743,6 +743,11 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
     stage_wrows<NW>(W, L * NP, wl, sl);
+    WRows wr;  // this wave's W rows (hi, lo), kept in registers
+    if (HASH) {
+        __syncthreads();
+        wrows_lds<NW>(wl, wr);
+    }
     const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
     floatx4 acc[4][NT];
     {
@@ -796,8 +801,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         bf16x8 pr[2][2], pfm[4];
         bf16x8 kA1;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
         bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
-        WRows wr;
-        if (HASH) wrows_lds<NW>(wl, wr);
+
         Rsrc rto, rco;
         if constexpr (HASH && (RWR & 1) != 0) rto = hc_res<NW>(rt_seg, cc);
         if constexpr (HASH && (RWR & 2) != 0) rco = hc_res<NW>(rc_seg, cc);
