@@ -899,6 +899,14 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
             }
         }
+        // ask the scheduler to interleave the products with the vector work of
+        // this block (writer features, score masks, state conversions): one
+        // MFMA, then up to three VALU instructions, which co-issue with it
+#pragma unroll
+        for (int i = 0; i < 40; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
