@@ -148,6 +148,20 @@ __device__ __forceinline__ void pin_loads() { __builtin_amdgcn_sched_barrier(0);
 struct Chunk {
     int tok0, nv;
 };
+
+// chunk loop unrolled by two so that the parity of the chunk, which selects a
+// double buffer, is a compile-time constant: body(ci, Par<ci & 1>{})
+template <int P> struct Par {
+    static constexpr int v = P;
+};
+template <class F>
+__device__ __forceinline__ void for_chunks2(int n, F &&body)
+{
+    for (int ci = 0; ci < n; ci += 2) {
+        body(ci, Par<0>{});
+        if (ci + 1 < n) body(ci + 1, Par<1>{});
+    }
+}
 // rows of a [token][HD] bf16 array
 __device__ __forceinline__ Rsrc row_res(const bf16 *seg_rows, const Chunk &c)
 {
@@ -364,10 +378,9 @@ __device__ __forceinline__ bf16x8 selection(int par)
     return f;
 }
 
-// W rows (hi, lo) of all waves staged once per workgroup, wl[2][NW * 16][XRS],
-// and the two selection operands sl[2][64 lanes][8]
+// W rows (hi, lo) of all waves staged once per workgroup, wl[2][NW * 16][XRS]
 template <int NW>
-__device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int LP, bf16 *wl, bf16 *sl)
+__device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int LP, bf16 *wl)
 {
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NW * 64) {
         const int hp = e / HD, c = e % HD;
@@ -376,6 +389,10 @@ __device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int LP,
         wl[hp * XRS + c] = hi;
         wl[(NW * 16 + hp) * XRS + c] = (bf16)(v - (float)hi);
     }
+}
+// the two selection operands, sl[2][64 lanes][8]
+__device__ __forceinline__ void stage_sel(bf16 *sl)
+{
     if (threadIdx.x < 64) {
         *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
         *reinterpret_cast<bf16x8 *>(sl + (64 + threadIdx.x) * 8) = selection(1);
@@ -640,8 +657,8 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     if (HASH) xstage_load<NTHR>(row_res(Xs, c1), xs);
     ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c1), ys);
     lds_barrier();
-    for (int ci = 0; ci < nch; ++ci) {
-        const int b = ci & 1;
+    for_chunks2(nch, [&](int ci, auto par) {
+        constexpr int b = decltype(par)::v;
         const Chunk cc = chunk(ci);
         // stage chunk ci + 1 (loaded one iteration ago) into the other buffers,
         // which were last read before the previous barrier, then prefetch ci + 2
@@ -682,7 +699,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
             for (int s = 0; s < 4; ++s) mma32(af[s][ct], pfm[s], yb);
         }
         lds_barrier();
-    }
+    });
     const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 64 * NCOL);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -703,6 +720,9 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // Outputs are formed transposed (value columns x tokens: the state and value
 // operands are the A side of the MFMAs), so that a lane ends up with four
 // consecutive columns of one token.
+// One barrier per chunk: staging buffers and the partial outputs are double
+// buffered, and the partial outputs of chunk c are summed after the barrier
+// of chunk c + 1, beside that chunk's products.
 template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const bf16 *__restrict__ R, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
@@ -713,15 +733,15 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     constexpr bool HASH = RSRC == 0;
     constexpr int RSLOTS = 2 * 4 * 64;  // (token tile, value column tile < 4, lane) output slots
     constexpr int RIT = (RSLOTS + NTHR - 1) / NTHR;
-    __shared__ __attribute__((aligned(16))) bf16 xbuf[HASH ? WCT * XRS : 8];
-    __shared__ __attribute__((aligned(16))) float kbuf[WCT];
-    __shared__ __attribute__((aligned(16))) bf16 ycol[CAUSAL ? NCOL * YCS : 8];
-    // partial outputs of every wave: value columns (4 tiles) and the count column
-    __shared__ __attribute__((aligned(16))) float red[NW * 2 * 4 * 64 * 4];
-    __shared__ __attribute__((aligned(16))) float redm[NW * 2 * 64];
-    __shared__ __attribute__((aligned(16))) float mbuf[WCT];
-    __shared__ __attribute__((aligned(16))) bf16 wl[HASH ? 2 * NW * 16 * XRS : 8];
+    constexpr int REDN = NW * 2 * 4 * 64 * 4;  // partial outputs: value columns (4 tiles) of every wave
+    constexpr int REDM = NW * 2 * 64;          // and their count column
+    __shared__ __attribute__((aligned(16))) bf16 xbuf[2][HASH ? WCT * XRS : 8];
+    __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
+    __shared__ __attribute__((aligned(16))) bf16 ycol[2][CAUSAL ? NCOL * YCS : 8];
+    // [2][REDN + REDM]; before the loop the forward's W rows are staged here
+    __shared__ __attribute__((aligned(16))) float red[2 * (REDN + REDM)];
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
+    static_assert(!HASH || 2 * NW * 16 * XRS * 2 <= 2 * (REDN + REDM) * 4, "W rows fit the partial-output buffer");
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
@@ -742,12 +762,12 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const _Float16 *rc_seg = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
-    stage_wrows<NW>(W, L * NP, wl, sl);
-    WRows wr;  // this wave's W rows (hi, lo), kept in registers
-    if (HASH) {
-        __syncthreads();
-        wrows_lds<NW>(wl, wr);
-    }
+    WRows wr;  // the forward's W rows (hi, lo), kept in registers
+    if (HASH) stage_wrows<NW>(W, L * NP, reinterpret_cast<bf16 *>(red));
+    stage_sel(sl);
+    __syncthreads();
+    // red is next written after two more barriers
+    if (HASH) wrows_lds<NW>(reinterpret_cast<const bf16 *>(red), wr);
     const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
     floatx4 acc[4][NT];
     {
@@ -770,76 +790,112 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     halfx4 rt[2], wt[2];
     const Chunk c0 = chunk(0);
     if (CAUSAL) {
-        ystage_zero_pad<NTHR>(ycol);
+        ystage_zero_pad<NTHR>(ycol[0]);
+        ystage_zero_pad<NTHR>(ycol[1]);
         ystage_load<NTHR, BWD>(yres<BWD>(vh, c0), ys);
         hc_load<NW>(hc_res<NW>(wt_seg, c0), wt);
     }
     if (HASH) {
         xstage_load<NTHR>(row_res(Rs, c0), xs);
-        xstage_store<NTHR>(xs, xbuf, kbuf);
+        xstage_store<NTHR>(xs, xbuf[0], kbuf[0]);
         xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
     } else {
         hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     }
     lds_barrier();
 
-    // this thread's output slots: token tile, column tile, lane (g, c16)
-    auto out_off = [&](int it) {
-        const int sl = threadIdx.x + it * NTHR;
-        const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
-        return (tt * 16 + (ln & 15)) * (HD * 2) + (16 * ct + 4 * (ln >> 4)) * 2;
-    };
-    float nsum[RIT][4];
-    Chunk prev = c0;
-    for (int ci = 0; ci < nch; ++ci) {
-        const Chunk cc = chunk(ci), cn = chunk(ci + 1);
-        if (CAUSAL) {
-            ystage_store<NTHR, BWD>(ys, cc.nv, ycol);
-            ystage_load<NTHR, BWD>(yres<BWD>(vh, cn), ys);
-        }
-        // Walsh features of this chunk's readers and writers
-        bf16x8 pr[2][2], pfm[4];
-        bf16x8 kA1;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
-        bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
-
+    // Walsh features of chunk ci's readers: hashed from the rows staged in
+    // buffer xb (storing t and dt/du' to the cache as asked), or from the
+    // cached t of the chunk (rt, which then takes the next chunk's t)
+    auto reader_feats = [&](int ci, const bf16 *xb, const float *kb, bf16x8 (&pr)[2][2]) {
+        const Chunk c = chunk(ci);
         Rsrc rto, rco;
-        if constexpr (HASH && (RWR & 1) != 0) rto = hc_res<NW>(rt_seg, cc);
-        if constexpr (HASH && (RWR & 2) != 0) rco = hc_res<NW>(rc_seg, cc);
+        if constexpr (HASH && (RWR & 1) != 0) rto = hc_res<NW>(rt_seg, c);
+        if constexpr (HASH && (RWR & 2) != 0) rco = hc_res<NW>(rc_seg, c);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             halfx4 t;
             if constexpr (HASH) {
-                halfx4 c;
-                hash_staged<POLY, (RWR & 2) != 0>(xbuf, kbuf, tt, wr, sq, t, c);
-                if constexpr ((RWR & 2) != 0) hc_store<NW>(rco, tt, c);
+                halfx4 cd;
+                hash_staged<POLY, (RWR & 2) != 0>(xb, kb, tt, wr, sq, t, cd);
+                if constexpr ((RWR & 2) != 0) hc_store<NW>(rco, tt, cd);
                 if constexpr ((RWR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
                 t = rt[tt];
             }
             walsh_tm(to_f4(t), q4, pr[tt][0], pr[tt][1]);
         }
-        if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, cn), rt);
-        lds_barrier();  // #1: value columns of this chunk staged, m of the previous one reduced
-        if (!BWD && ci > 0) {
-            // outputs of the previous chunk: o = n / m
-            const Rsrc ro = row_res(Os, prev);
+        if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, chunk(ci + 1)), rt);
+    };
+    // Reader features from the cache are formed one chunk ahead, beside the
+    // products of the chunk before (this helps there but not where the rows
+    // are hashed, which happens before the chunk's barrier)
+    constexpr bool PIPE = !HASH;
+    bf16x8 prc[2][2];  // reader features of the current chunk
+    if constexpr (PIPE) reader_feats(0, xbuf[0], kbuf[0], prc);
+
+    // Sum of the partial outputs of chunk c (buffer c & 1) and its output
+    // rows: O = n / m (m formed per token from the count column) and den = m,
+    // or dV = n.  Thread slot: token tile tt, column tile ct, lane (g, c16).
+    auto finish = [&](int ci, int pb) {
+        const Chunk c = chunk(ci);
+        const float *rn = red + pb * (REDN + REDM), *rm = rn + REDN;
+        const Rsrc ro = row_res(Os, c);
 #pragma unroll
-            for (int it = 0; it < RIT; ++it) {
-                const int sl = threadIdx.x + it * NTHR;
-                if (sl < RSLOTS) {
-                    const float inv = __builtin_amdgcn_rcpf(mbuf[(sl >> 8) * 16 + (sl & 15)]);
-                    const u32x2 v = {pk_bf16(nsum[it][0] * inv, nsum[it][1] * inv),
-                                     pk_bf16(nsum[it][2] * inv, nsum[it][3] * inv)};
-                    bst64(v, ro, out_off(it));
+        for (int it = 0; it < RIT; ++it) {
+            const int sl_ = threadIdx.x + it * NTHR;
+            // branch-free where every slot is taken, so that this joins the
+            // block of the products
+            if (RSLOTS % NTHR == 0 || sl_ < RSLOTS) {
+                const int tt = sl_ >> 8, ct = (sl_ >> 6) & 3, ln = sl_ & 63;
+                floatx4 n = *reinterpret_cast<const floatx4 *>(rn + ((tt * 4 + ct) * 64 + ln) * 4);
+#pragma unroll
+                for (int ww = 1; ww < NW; ++ww)
+                    n += *reinterpret_cast<const floatx4 *>(rn + (((ww * 2 + tt) * 4 + ct) * 64 + ln) * 4);
+                const int off = (tt * 16 + (ln & 15)) * (HD * 2) + (16 * ct + 4 * (ln >> 4)) * 2;
+                if (BWD) {
+                    bst64(u32x2{pk_bf16(n[0], n[1]), pk_bf16(n[2], n[3])}, ro, off);
+                } else {
+                    float m = rm[tt * 64 + (ln & 15)];
+#pragma unroll
+                    for (int ww = 1; ww < NW; ++ww) m += rm[(ww * 2 + tt) * 64 + (ln & 15)];
+                    const float inv = __builtin_amdgcn_rcpf(m);
+                    bst64(u32x2{pk_bf16(n[0] * inv, n[1] * inv), pk_bf16(n[2] * inv, n[3] * inv)}, ro, off);
+                    bstf(m, make_rsrc(dens + c.tok0, c.nv * 4), (ct == 0 && ln < 16) ? (tt * 16 + ln) * 4 : OOB);
                 }
             }
         }
-        if (HASH) {  // the next chunk's rows (xbuf is not read again in this chunk)
-            if (ci + 1 < nch) xstage_store<NTHR>(xs, xbuf, kbuf);
+    };
+
+    for_chunks2(nch, [&](int ci, auto par) {
+        constexpr int b = decltype(par)::v;
+        const Chunk cc = chunk(ci), cn = chunk(ci + 1);
+        if (CAUSAL) {
+            ystage_store<NTHR, BWD>(ys, cc.nv, ycol[b]);
+            ystage_load<NTHR, BWD>(yres<BWD>(vh, cn), ys);
+        }
+        bf16x8 pr[2][2];
+        if constexpr (PIPE) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) pr[tt][k] = prc[tt][k];
+        } else {
+            reader_feats(ci, xbuf[b], kbuf[b], pr);
+        }
+        bf16x8 pfm[4];
+        bf16x8 kA1;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
+        bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
+        if (HASH) {  // the next chunk's rows into the other buffer (last read before the previous barrier)
+            if (ci + 1 < nch) xstage_store<NTHR>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
             xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         }
-        // writer features, masked scores and feature-major operands after the
-        // barrier, next to the MFMA-bound products that consume them
+        lds_barrier();  // value columns and next rows staged; partial outputs of chunk ci - 1 in LDS
+        // the next chunk's reader features, computed beside this chunk's
+        // products (past the last chunk: nothing is read or stored)
+        if constexpr (PIPE) reader_feats(ci + 1, xbuf[b ^ 1], kbuf[b ^ 1], prc);
+        // writer features, masked scores and feature-major operands, next to
+        // the MFMA-bound products that consume them
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
@@ -892,7 +948,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], sf[k], pr[tt][k]);
             if (CAUSAL) {
-                const bf16x8 yb = ycol_frag(ycol, ct * 16 + c16);
+                const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + c16);
                 mma32(oacc[0][ct], yb, BWD ? kA8 : kA1);
                 mma32(oacc[1][ct], yb, BWD ? kA1 : kA8);
 #pragma unroll
@@ -907,57 +963,21 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
+        if (ci > 0) finish(ci - 1, b ^ 1);
+        float *rn = red + b * (REDN + REDM), *rm = rn + REDN;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
-                *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * 4 + ct) * 64 + lane) * 4) = oacc[tt][ct];
+                *reinterpret_cast<floatx4 *>(rn + (((w * 2 + tt) * 4 + ct) * 64 + lane) * 4) = oacc[tt][ct];
             // the count column (64) is row 0 of column tile 4: register 0 of lanes
             // 0..15 (the other lanes' values are not read)
-            redm[(w * 2 + tt) * 64 + lane] = oacc[tt][4][0];
+            if (!BWD) rm[(w * 2 + tt) * 64 + lane] = oacc[tt][4][0];
         }
-        lds_barrier();  // #2: partial outputs of every wave in LDS, next rows staged
-        const Rsrc ro = row_res(Os, cc);
-#pragma unroll
-        for (int it = 0; it < RIT; ++it) {
-            const int sl = threadIdx.x + it * NTHR;
-            if (sl < RSLOTS) {
-                const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63;
-                floatx4 n = *reinterpret_cast<const floatx4 *>(red + ((tt * 4 + ct) * 64 + ln) * 4);
-#pragma unroll
-                for (int ww = 1; ww < NW; ++ww)
-                    n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * 4 + ct) * 64 + ln) * 4);
-                if (BWD) {
-                    const u32x2 v = {pk_bf16(n[0], n[1]), pk_bf16(n[2], n[3])};
-                    bst64(v, ro, out_off(it));
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) nsum[it][r] = n[r];
-                    if (ct == 0 && ln < 16) {
-                        float m = redm[tt * 64 + ln];
-#pragma unroll
-                        for (int ww = 1; ww < NW; ++ww) m += redm[(ww * 2 + tt) * 64 + ln];
-                        mbuf[tt * 16 + ln] = m;
-                        bstf(m, make_rsrc(dens + cc.tok0, cc.nv * 4), (tt * 16 + ln) * 4);
-                    }
-                }
-            }
-        }
-        prev = cc;
-    }
-    if (!BWD) {
+    });
+    if (nch > 0) {
         lds_barrier();
-        const Rsrc ro = row_res(Os, prev);
-#pragma unroll
-        for (int it = 0; it < RIT; ++it) {
-            const int sl = threadIdx.x + it * NTHR;
-            if (sl < RSLOTS) {
-                const float inv = __builtin_amdgcn_rcpf(mbuf[(sl >> 8) * 16 + (sl & 15)]);
-                const u32x2 v = {pk_bf16(nsum[it][0] * inv, nsum[it][1] * inv),
-                                 pk_bf16(nsum[it][2] * inv, nsum[it][3] * inv)};
-                bst64(v, ro, out_off(it));
-            }
-        }
+        finish(nch - 1, (nch - 1) & 1);
     }
 }
 
@@ -985,14 +1005,16 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     constexpr int DUS = NW * 16 + 8;  // du row stride (bf16)
     constexpr int TPWV = 8 / NW;      // dxh tiles per wave
     constexpr int WTS = NW * 16 + 8;  // staged W^T row stride
+    // staging buffers, du and the partial dots are double buffered: one
+    // barrier per chunk
     __shared__ __attribute__((aligned(16))) bf16 xbuf[2][WCT * XRS];
     __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
-    __shared__ __attribute__((aligned(16))) bf16 yrow_r[WCT * YRS];
-    __shared__ __attribute__((aligned(16))) bf16 yrow_w[CAUSAL ? WCT * YRS : 8];
-    __shared__ __attribute__((aligned(16))) bf16 ycol_w[CAUSAL ? NCOL * YCS : 8];
-    __shared__ __attribute__((aligned(16))) bf16 du_l[WCT * DUS];
-    __shared__ __attribute__((aligned(16))) float dotp[WCT * 16];  // partial x . dxh [token][nt][g]
-    __shared__ __attribute__((aligned(16))) bf16 wt_l[HD * WTS];  // W^T (bf16): [dim][hyperplane]
+    __shared__ __attribute__((aligned(16))) bf16 yrow_r[2][WCT * YRS];
+    __shared__ __attribute__((aligned(16))) bf16 yrow_w[2][CAUSAL ? WCT * YRS : 8];
+    __shared__ __attribute__((aligned(16))) bf16 ycol_w[2][CAUSAL ? NCOL * YCS : 8];
+    __shared__ __attribute__((aligned(16))) bf16 du_l[2][WCT * DUS];
+    __shared__ __attribute__((aligned(16))) float dotp[2][WCT * 16];  // partial x . dxh [token][nt][g]
+    __shared__ __attribute__((aligned(16))) bf16 wt_l[HD * WTS];     // W^T (bf16): [dim][hyperplane]
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
@@ -1025,16 +1047,13 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         const int hp = e / HD, c = e % HD;
         wt_l[c * WTS + hp] = (bf16)(hp < L * NP ? 0.25f * W[hp * HD + c] : 0.f);
     }
-    if (threadIdx.x < 64) {
-        *reinterpret_cast<bf16x8 *>(sl + threadIdx.x * 8) = selection(0);
-        *reinterpret_cast<bf16x8 *>(sl + (64 + threadIdx.x) * 8) = selection(1);
-    }
+    stage_sel(sl);
     const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
 
     auto chunk = [&](int ci) -> Chunk {
-        if (ci >= nch) return Chunk{0, 0};
+        if (ci < 0 || ci >= nch) return Chunk{0, 0};
         const int t0 = (REVERSE ? nch - 1 - ci : ci) * WCT;
         return Chunk{t0, min(WCT, tend - t0)};
     };
@@ -1044,10 +1063,15 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     YStage<NTHR, !RD> ysw;
     halfx4 rt[2], rcv[2], wt[2];
     const Chunk c0 = chunk(0);
-    yrow_zero_pad<NTHR>(yrow_r);
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+        yrow_zero_pad<NTHR>(yrow_r[pb]);
+        if (CAUSAL) {
+            yrow_zero_pad<NTHR>(yrow_w[pb]);
+            ystage_zero_pad<NTHR>(ycol_w[pb]);
+        }
+    }
     if (CAUSAL) {
-        yrow_zero_pad<NTHR>(yrow_w);
-        ystage_zero_pad<NTHR>(ycol_w);
         ystage_load<NTHR, !RD>(yres<!RD>(vwh, c0), ysw);
         hc_load<NW>(hc_res<NW>(wt_seg, c0), wt);
     }
@@ -1055,28 +1079,47 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     hc_load<NW>(hc_res<NW>(rc_seg, c0), rcv);
     xstage_load<NTHR>(row_res(Rs, c0), xs);
-    xstage_store<NTHR, true>(xs, xbuf[0], kbuf[0]);
-    xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
-    lds_barrier();
 
-    // the previous chunk's dxh tiles, finished one barrier later (when the
-    // partial dots of every wave are in LDS): the normalisation backward
-    // dx = (dxh - x (x . dxh) / |x|^2) / |x| for |x| > 1e-12, else dxh 1e12
+    // dxh = du W of chunk ci (du in buffer pb) for this wave's tiles; the
+    // partial dots with x go to dotp[pb], dxh, x and |x|^2 stay in registers
+    // until every wave's dots are in LDS.  Tile (tt, nt) = wave + NW i; lane
+    // (g, c16): token 16 tt + c16, dims 16 nt + 4g + r.
     floatx4 dxh[TPWV];
     bf16x4 xkeep[TPWV];
     float sskeep[TPWV];
-    bool have_prev = false;
-    Chunk prev = c0;
-    auto finish_prev = [&]() {
-        if (!have_prev) return;
-        const Rsrc rdx = row_res(dXs, prev);
+    auto dxh_tiles = [&](int pb) {
+#pragma unroll
+        for (int i = 0; i < TPWV; ++i) {
+            const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
+            floatx4 xa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < NW / 2; ++k) {
+                const bf16x8 dub = *reinterpret_cast<const bf16x8 *>(du_l[pb] + tok * DUS + 32 * k + 8 * g);
+                const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + 32 * k + 8 * g;
+                mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow), dub);
+            }
+            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[pb] + tok * XRS + nt * 16 + 4 * g);
+            float dot = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dot = fmaf(xa[r], (float)xv[r], dot);
+            dotp[pb][tok * 16 + nt * 4 + g] = dot;
+            dxh[i] = xa;
+            xkeep[i] = xv;
+            sskeep[i] = kbuf[pb][tok];
+        }
+    };
+    // the normalisation backward of chunk ci from the registers above and the
+    // dots in dotp[pb]: dx = (dxh - x (x . dxh) / |x|^2) / |x| for
+    // |x| > 1e-12, else dxh 1e12
+    auto finish = [&](int ci, int pb) {
+        const Rsrc rdx = row_res(dXs, chunk(ci));
 #pragma unroll
         for (int i = 0; i < TPWV; ++i) {
             const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
             float dot = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(dotp + tok * 16 + 4 * q);
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(dotp[pb] + tok * 16 + 4 * q);
                 dot += (v[0] + v[1]) + (v[2] + v[3]);
             }
             const float ss = sskeep[i];
@@ -1090,11 +1133,15 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         }
     };
 
+    // Chunk ci: its value rows are staged before the barrier; after it, the
+    // normalisation backward of chunk ci - 2 (whose dots are complete), chunk
+    // ci's rows and products, and last dxh of chunk ci - 1 (whose du is
+    // complete).
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
-        ystage_store<NTHR, RD>(ysr, cc.nv, nullptr, yrow_r);
-        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, cc.nv, ycol_w, yrow_w);
+        ystage_store<NTHR, RD>(ysr, cc.nv, nullptr, yrow_r[b]);
+        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, cc.nv, ycol_w[b], yrow_w[b]);
         ystage_load<NTHR, RD>(yres<RD>(vrh, cn), ysr);
         if (CAUSAL) ystage_load<NTHR, !RD>(yres<!RD>(vwh, cn), ysw);
         const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
@@ -1110,15 +1157,15 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
-        lds_barrier();  // #1: value rows of this chunk staged, partial dots of the previous one
-        finish_prev();
-        // the next chunk's raw rows into the other buffer
-        if (ci + 1 < nch) xstage_store<NTHR, true>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-        xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
+        lds_barrier();  // value rows of this chunk; du and rows of ci - 1; dots of ci - 2
+        if (ci >= 2) finish(ci - 2, b);
+        // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
+        xstage_store<NTHR, true>(xs, xbuf[b], kbuf[b]);
+        xstage_load<NTHR>(row_res(Rs, cn), xs);
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][3];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) yrow_frags(yrow_r, tt * 16 + c16, yb8[tt]);
+        for (int tt = 0; tt < 2; ++tt) yrow_frags(yrow_r[b], tt * 16 + c16, yb8[tt]);
         floatx4 dps[4][2];  // dpsi^T tiles (s, tt): lane (rows 4g + r <-> S = 4s + r of table 4w + g, token c16)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -1134,7 +1181,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 #pragma unroll
             for (int tj = 0; tj < 2; ++tj) {
                 bf16x8 wa8[3];
-                yrow_frags(yrow_w, tj * 16 + c16, wa8);
+                yrow_frags(yrow_w[b], tj * 16 + c16, wa8);
 #pragma unroll
                 for (int pi = 0; pi < 3; ++pi) {
                     if (TJ[pi] != tj) continue;
@@ -1182,7 +1229,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             // S += psi_w^T y_w (after every read of the state above)
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                const bf16x8 ya = ycol_frag(ycol_w, ct * 16 + c16);  // rows = value columns
+                const bf16x8 ya = ycol_frag(ycol_w[b], ct * 16 + c16);  // rows = value columns
 #pragma unroll
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], ya, pfm[s]);
             }
@@ -1197,37 +1244,19 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 for (int r = 0; r < 4; ++r) dp[4 * s + r] = dps[s][tt][r];
             walsh_grad(dp, to_f4(trh[tt]), dt);
             const floatx4 cr = to_f4(crh[tt]);
-            *reinterpret_cast<bf16x4 *>(du_l + (tt * 16 + c16) * DUS + w * 16 + 4 * g) =
+            *reinterpret_cast<bf16x4 *>(du_l[b] + (tt * 16 + c16) * DUS + w * 16 + 4 * g) =
                 pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
         }
-        lds_barrier();  // #2: du of every wave in LDS
-        // dxh^T tiles (tt, nt) over all hyperplanes; tile
-        // (tt, nt) = wave + NW i.  Lane (g, c16): token 16 tt + c16, dims
-        // 16 nt + 4g + r; the partial dot with x of those 4 dims goes to LDS.
-#pragma unroll
-        for (int i = 0; i < TPWV; ++i) {
-            const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
-            floatx4 xa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < NW / 2; ++k) {
-                const bf16x8 dub = *reinterpret_cast<const bf16x8 *>(du_l + tok * DUS + 32 * k + 8 * g);
-                const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + 32 * k + 8 * g;
-                mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow), dub);
-            }
-            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[b] + tok * XRS + nt * 16 + 4 * g);
-            float dot = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dot = fmaf(xa[r], (float)xv[r], dot);
-            dotp[tok * 16 + nt * 4 + g] = dot;
-            dxh[i] = xa;
-            xkeep[i] = xv;
-            sskeep[i] = kbuf[b][tok];
-        }
-        have_prev = true;
-        prev = cc;
+        if (ci >= 1) dxh_tiles(b ^ 1);
     }
-    lds_barrier();
-    finish_prev();
+    if (nch > 0) {
+        const int pl = (nch - 1) & 1;  // buffers of the last chunk
+        lds_barrier();
+        if (nch >= 2) finish(nch - 2, pl ^ 1);
+        dxh_tiles(pl);
+        lds_barrier();
+        finish(nch - 1, pl);
+    }
 }
 
 }  // namespace race
