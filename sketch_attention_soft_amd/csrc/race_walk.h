@@ -780,7 +780,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     }
     // chunks in walk order
     auto chunk = [&](int ci) -> Chunk {
-        if (ci >= nch) return Chunk{0, 0};
+        if (ci < 0 || ci >= nch) return Chunk{0, 0};
         const int t0 = (BWD ? nch - 1 - ci : ci) * WCT;
         return Chunk{t0, min(WCT, tend - t0)};
     };
@@ -891,6 +891,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         }
         lds_barrier();  // value columns and next rows staged; partial outputs of chunk ci - 1 in LDS
+        finish(ci - 1, b ^ 1);  // (none before the first chunk: its stores are dropped)
+        __builtin_amdgcn_sched_barrier(0);
         // the next chunk's reader features, computed beside this chunk's
         // products (past the last chunk: nothing is read or stored)
         if constexpr (PIPE) reader_feats(ci + 1, xbuf[b ^ 1], kbuf[b ^ 1], prc);
@@ -963,7 +965,6 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
-        if (ci > 0) finish(ci - 1, b ^ 1);
         float *rn = red + b * (REDN + REDM), *rm = rn + REDN;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1158,7 +1159,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             feat_major(pw, sel, pfm);
         }
         lds_barrier();  // value rows of this chunk; du and rows of ci - 1; dots of ci - 2
-        if (ci >= 2) finish(ci - 2, b);
+        finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
         // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
         xstage_store<NTHR, true>(xs, xbuf[b], kbuf[b]);
         xstage_load<NTHR>(row_res(Rs, cn), xs);
@@ -1247,7 +1248,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             *reinterpret_cast<bf16x4 *>(du_l[b] + (tt * 16 + c16) * DUS + w * 16 + 4 * g) =
                 pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
         }
-        if (ci >= 1) dxh_tiles(b ^ 1);
+        dxh_tiles(b ^ 1);  // (before the first chunk: unused values)
     }
     if (nch > 0) {
         const int pl = (nch - 1) & 1;  // buffers of the last chunk
