@@ -488,14 +488,17 @@ __device__ __forceinline__ void hash_staged(const bf16 *xb, const float *kb, int
     }
 }
 
-// token-major Walsh features of one table: lo = S 0..7, hi = S 8..15
-// (q4 = 1/4, or 0 for padding tables)
-__device__ __forceinline__ void walsh_tm(const floatx4 &t, float q4, bf16x8 &lo, bf16x8 &hi)
+// token-major Walsh features of one table, q prod_{p in S} t_p: lo = S 0..7,
+// hi = S 8..15.  The features are 1/4 prod t_p; the kernels form reader
+// features with q = 1 and writer features with q = 1/16 (0 for padding
+// tables), which gives every score and state product its factor 1/16 exactly
+// (powers of two) and saves the reader side four products.
+__device__ __forceinline__ void walsh_tm(const floatx4 &t, float q, bf16x8 &lo, bf16x8 &hi)
 {
-    const float a1 = q4 * t[0], a2 = q4 * t[1], a3 = a1 * t[1], b3 = t[2] * t[3];
-    lo = pk8(pk_bf16(q4, a1), pk_bf16(a2, a3), pk_bf16(q4 * t[2], a1 * t[2]),
+    const float a1 = q * t[0], a2 = q * t[1], a3 = a1 * t[1], b3 = t[2] * t[3];
+    lo = pk8(pk_bf16(q, a1), pk_bf16(a2, a3), pk_bf16(q * t[2], a1 * t[2]),
              pk_bf16(a2 * t[2], a3 * t[2]));
-    hi = pk8(pk_bf16(q4 * t[3], a1 * t[3]), pk_bf16(a2 * t[3], a3 * t[3]), pk_bf16(q4 * b3, a1 * b3),
+    hi = pk8(pk_bf16(q * t[3], a1 * t[3]), pk_bf16(a2 * t[3], a3 * t[3]), pk_bf16(q * b3, a1 * b3),
              pk_bf16(a2 * b3, a3 * b3));
 }
 
@@ -630,7 +633,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     WRows wr;
     if (HASH) load_wrows(W, L * NP, wr);
     const bf16x8 sel[2] = {selection(0), selection(1)};
-    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
     floatx4 af[4][NT];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -688,7 +691,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
             } else {
                 t = tcur[tt];
             }
-            walsh_tm(to_f4(t), q4, ptm[tt][0], ptm[tt][1]);
+            walsh_tm(to_f4(t), qw, ptm[tt][0], ptm[tt][1]);
         }
         feat_major(ptm, sel, pfm);
         // tokens past the end have psi_0 = 1/4 but zero value rows
@@ -768,7 +771,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     __syncthreads();
     // red is next written after two more barriers
     if (HASH) wrows_lds<NW>(reinterpret_cast<const bf16 *>(red), wr);
-    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
     floatx4 acc[4][NT];
     {
         const float *src = st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL);
@@ -823,7 +826,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             } else {
                 t = rt[tt];
             }
-            walsh_tm(to_f4(t), q4, pr[tt][0], pr[tt][1]);
+            walsh_tm(to_f4(t), 1.f, pr[tt][0], pr[tt][1]);
         }
         if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, chunk(ci + 1)), rt);
     };
@@ -901,7 +904,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
+            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), qw, pw[tt][0], pw[tt][1]);
             hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             // scores^T tiles D[j][i] = psi_w(j) . psi_r(i) over this wave's tables
             constexpr int TJ[3] = {0, BWD ? 1 : 0, 1}, TI[3] = {0, BWD ? 0 : 1, 1};
@@ -1042,14 +1045,16 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 
     // W^T and the selection operands, once per workgroup.  dxh = du W takes W
     // in bf16, the precision of du itself (the forward projection keeps W to
-    // about 16 bits as bf16 hi + lo); W^T carries the factor 1/4 of the Walsh
-    // features (exact), which walsh_grad leaves out.
+    // about 16 bits as bf16 hi + lo).  With writer features scaled by 1/16 and
+    // reader features by 1, the products below give the gradient with respect
+    // to the unscaled reader features prod t_p, so that walsh_grad yields dt
+    // itself.
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
         const int hp = e / HD, c = e % HD;
-        wt_l[c * WTS + hp] = (bf16)(hp < L * NP ? 0.25f * W[hp * HD + c] : 0.f);
+        wt_l[c * WTS + hp] = (bf16)(hp < L * NP ? W[hp * HD + c] : 0.f);
     }
     stage_sel(sl);
-    const float q4 = (4 * w + g < L) ? 0.25f : 0.f;
+    const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
 
@@ -1152,7 +1157,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), q4, pw[tt][0], pw[tt][1]);
+            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), qw, pw[tt][0], pw[tt][1]);
             hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             bf16x8 sel[2];
             sel_lds(sl, sel);
