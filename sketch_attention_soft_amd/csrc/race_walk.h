@@ -176,24 +176,34 @@ template <int NTHR> struct XStage {
     u32x4 v[ITEMS];
 };
 
-template <int NTHR>
+// Row piece of this thread.  UP (the gradient kernels, whose value rows cost
+// the most) with 512 threads: the rows go to the upper four waves, so that the
+// value rows (items of the lower four) and the rows are staged by different
+// waves of each SIMD.
+template <int NTHR, bool UP> __device__ __forceinline__ int xitem(int it)
+{
+    return (UP && NTHR == 512 ? (int)threadIdx.x ^ 256 : (int)threadIdx.x) + it * NTHR;
+}
+
+template <int NTHR, bool UP = false>
 __device__ __forceinline__ void xstage_load(Rsrc r, XStage<NTHR> &xs)
 {
 #pragma unroll
     for (int it = 0; it < XStage<NTHR>::ITEMS; ++it) {
-        const int e = threadIdx.x + it * NTHR;
+        const int e = xitem<NTHR, UP>(it);
         xs.v[it] = bld128(r, e < WCT * 8 ? e * 16 : OOB);
     }
 }
 
 // rows -> xb[token][XRS] (rows past the chunk's end were loaded as zeros);
-// kb[token] = -2 log2(e) / max(|x|, 1e-12) (NORM2: the squared norm |x|^2)
+// kb[token] = -2 log2(e) / max(|x|, 1e-12) (NORM2: the squared norm |x|^2;
+// the pieces are those of xstage_load<NTHR, NORM2>)
 template <int NTHR, bool NORM2 = false>
 __device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, float *kb)
 {
 #pragma unroll
     for (int it = 0; it < XStage<NTHR>::ITEMS; ++it) {
-        const int e = threadIdx.x + it * NTHR;
+        const int e = xitem<NTHR, NORM2>(it);
         if (e < WCT * 8) {  // uniform per wave
             const int j = e >> 3;
             const bf16x8 v = __builtin_bit_cast(bf16x8, xs.v[it]);
@@ -1084,7 +1094,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     ystage_load<NTHR, RD>(yres<RD>(vrh, c0), ysr);
     hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     hc_load<NW>(hc_res<NW>(rc_seg, c0), rcv);
-    xstage_load<NTHR>(row_res(Rs, c0), xs);
+    xstage_load<NTHR, true>(row_res(Rs, c0), xs);
 
     // dxh = du W of chunk ci (du in buffer pb) for this wave's tiles; the
     // partial dots with x go to dotp[pb], dxh, x and |x|^2 stay in registers
@@ -1167,7 +1177,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
         // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
         xstage_store<NTHR, true>(xs, xbuf[b], kbuf[b]);
-        xstage_load<NTHR>(row_res(Rs, cn), xs);
+        xstage_load<NTHR, true>(row_res(Rs, cn), xs);
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][3];
 #pragma unroll
