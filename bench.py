@@ -105,6 +105,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters), then exit")
+    ap.add_argument("--stream", action="store_true",
+                    help="time the streaming state entry points instead (decode of one token "
+                         "per head over 64 heads, bulk state_add of the 4M-token head)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -126,6 +129,9 @@ def main() -> int:
 
     from sketch_attention_soft_amd import binding
     from sketch_attention_soft_amd import inputs as I
+
+    if args.stream:
+        return stream_bench(args, binding, I, np, torch)
 
     w = I.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
@@ -234,6 +240,87 @@ def main() -> int:
                           "frac": round(max(t_mfma, t_hbm) / ms, 5)},
         "kernels_ms": {k2: round(v2, 4) for k2, v2 in kern.items()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def stream_bench(args, binding, I, np, torch) -> int:
+    """One JSON line for the streaming state API (race_attn_decode,
+    race_attn_state_add).  Decode: 4 x 16 heads, one token each per call, the
+    state of a 2048-token prefix; bound by reading and writing the fp32 state
+    (F x 65 floats per head), so its roofline is HBM bytes per call / time.
+    Bulk add: the 4,194,304-token head of causal_n4m_bf16; fp32 vector
+    arithmetic, 2 F (d + 1) + 2 d L P flops per token (update and
+    projection), against the fp32 vector peak."""
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L, P, d, tau = 32, 4, 64, 1.0
+    F = L << P
+
+    def put(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timed(fn, iters, warm):
+        for _ in range(warm):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    # decode: 64 heads, one token per head per call
+    B, H, N0 = 4, 16, 2048
+    x = I.make_inputs(B, H, N0 + 1, d, L, P, "bf16", 4242, with_grad=False)
+    q, k, v = (put(x[n]) for n in ("q", "k", "v"))
+    W = torch.from_numpy(x["W"]).to(dev)
+    st = binding.new_state(B, H, d, L, P, dev)
+    binding.state_add(st, k[:, :, :N0].contiguous(), v[:, :, :N0].contiguous(), W, tau)
+    q1, k1, v1 = (t[:, :, N0:].contiguous() for t in (q, k, v))
+    o1 = torch.empty_like(q1)
+    den1 = torch.empty((B, H, 1), dtype=torch.float32, device=dev)
+    ms_dec = timed(lambda: binding.decode(st, q1, k1, v1, W, tau, out=(o1, den1)),
+                   max(args.steps, 10) * 10, args.warmup + 5)
+    bytes_dec = 2 * B * H * F * (d + 1) * 4 + 4 * B * H * d * 2 + B * H * 4
+    gbs = bytes_dec / (ms_dec * 1e-3) / 1e9
+
+    # bulk add of the headline head
+    w = I.WORKLOADS["causal_n4m_bf16"]
+    xa = I.workload_inputs(w, with_grad=False)
+    ka, va = put(xa["k"]), put(xa["v"])
+    Wa = torch.from_numpy(xa["W"]).to(dev)
+    del xa
+    sa = binding.new_state(1, 1, d, L, P, dev)
+    ws = torch.empty(binding.state_add_workspace_bytes(1, 1, w.N, d, L, P), dtype=torch.uint8,
+                     device=dev)
+    ms_add = timed(lambda: binding.state_add(sa, ka, va, Wa, tau, workspace=ws), max(args.steps, 3),
+                   1)
+    flops_tok = 2 * F * (d + 1) + 2 * d * L * P
+    tflops = flops_tok * w.N / (ms_add * 1e-3) / 1e12
+
+    line = {
+        "metric": "RACE streaming decode tokens/s (64 heads x 1 token, L=32, d=64, bf16 rows, "
+                  "fp32 state); % of HBM roofline",
+        "value": round(B * H / (ms_dec * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": max(args.steps, 10) * 10, "warmup": args.warmup + 5,
+        "ms_per_step": round(ms_dec, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Philox N(0,1); Q, K rows L2-normalised)",
+        "config": {"workload": "decode_64h_1tok_L32", "B": B, "H": H, "prefix": N0, "L": L,
+                   "P": P, "d": d, "tau": tau},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 5), "traffic": None,
+                     "kernel": "stream_kernel (decode)", "bytes_per_call": bytes_dec},
+        "state_add": {"workload": w.name, "tokens": w.N, "ms": round(ms_add, 4),
+                      "tokens_per_s": round(w.N / (ms_add * 1e-3), 1),
+                      "roofline": {"bound": "alu", "achieved": round(tflops, 3),
+                                   "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                                   "frac": round(tflops / PEAK_TFLOPS["f32"], 5),
+                                   "flops_per_token": flops_tok}},
     }
     print(json.dumps(line), flush=True)
     return 0

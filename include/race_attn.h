@@ -162,6 +162,62 @@ race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, i
 race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
 
 /* Static, NUL-terminated description of a status code. */
+/* Streaming state (inference).  The causal recurrence of step 5 keeps running
+ * bucket sums and reads them at every step (zh §2.3: each step costs the same
+ * however long the prefix), so a head can be carried as a fixed-size state
+ * that tokens are appended to and read from, one step at a time.
+ *
+ * State of one head: fp32 S[F][d + 1], F = 16 L, row f = 16 l + s:
+ *   S[f][c] = sum_j psi_f(k_j) v_j[c] for c < d,  S[f][d] = sum_j psi_f(k_j),
+ *   psi_{16 l + s}(x) = 1/4 prod_{p in s} t_lp(x),  t_lp = tanh(z_lp / tau),
+ * over the keys j appended so far, where s is a subset of the table's P = 4
+ * hyperplanes (bit p of s set when p is in it).  The corner weights of step 2
+ * are phi_lr = prod_p (1 + c_rp t_lp) / 2, so psi_l is their Walsh-Hadamard
+ * transform, psi(q).psi(k) = phi(q).phi(k), and S holds the bucket sums A_l,
+ * B_l of step 3 in that basis.  A readout is [n | m] = sum_f psi_f(q) S[f][:],
+ * o = n / m, den = m (step 4).  The states of all heads are one contiguous
+ * device array [B][H][F][d + 1], owned by the caller; all zeros is the empty
+ * prefix.  These entry points compute in fp32 (t with tanhf) whatever dt is.
+ * Supported as above (d = 64, P = 4, L <= 64) and B * H <= 65535; N or T = 0
+ * is a no-op (the row pointers may then be NULL; W and state may not).  Calls
+ * that write one state must not overlap. */
+
+/* Bytes of the states of B * H heads (F * (d + 1) floats each).  Pure host
+ * function. */
+race_status_t race_attn_state_bytes(int B, int H, int d, int L, int P, size_t *bytes);
+
+/* Workspace bytes that race_attn_state_add needs for N tokens per head (0 for
+ * N = 0).  Pure host function. */
+race_status_t race_attn_state_add_workspace_bytes(int B, int H, int64_t N, int d, int L, int P,
+                                                  size_t *bytes);
+
+/* Appends N tokens per head to the states: state += sum_j psi(k_j)^T [v_j | 1]
+ * for the rows of K, V ([B][H][N][d], type dt).  The tokens are summed in
+ * blocks in parallel and the block sums added to the state in block order
+ * (the result does not depend on the launch).  workspace: 256-byte aligned,
+ * race_attn_state_add_workspace_bytes bytes, scratch. */
+race_status_t race_attn_state_add(const void *K, const void *V, const float *W, int L, int P,
+                                  float tau, int B, int H, int64_t N, int d, race_dtype_t dt,
+                                  float *state, void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode step: appends T tokens per head in order and returns their causal
+ * outputs; token i reads the state after its own key is added (step 5: keys
+ * j <= i).  Q, K, V: [B][H][T][d] (type dt); O: [B][H][T][d] (type dt); den:
+ * fp32 [B][H][T].  Started from the empty state, a call over a sequence gives
+ * the rows of race_attn_forward with causal = 1; started from
+ * race_attn_state_add of a prefix, the rows that follow it. */
+race_status_t race_attn_decode(const void *Q, const void *K, const void *V, const float *W,
+                               int L, int P, float tau, int B, int H, int64_t T, int d,
+                               race_dtype_t dt, float *state, void *O, float *den, void *stream);
+
+/* Readout without appending: o_i = n_i / m_i with [n_i | m_i] = psi(q_i) S
+ * for the T rows of Q ([B][H][T][d]); the state is only read.  Over the
+ * state of a key set this is race_attn_forward with causal = 0 on those keys.
+ * A state with no keys gives m = 0 and non-finite o. */
+race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int P, float tau,
+                                      int B, int H, int64_t T, int d, race_dtype_t dt,
+                                      const float *state, void *O, float *den, void *stream);
+
 const char *race_attn_status_string(race_status_t status);
 
 #ifdef __cplusplus

@@ -144,3 +144,35 @@ def forward_backward(q, k, v, g, W, tau: float, causal: bool):
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(W), L, P, float(tau), int(causal), BH, N, d,
         _ptr(o), _ptr(den), _ptr(dq), _ptr(dk), _ptr(dv)), "forward_backward")
     return o, den, dq, dk, dv
+
+
+def bucket_sums(k, v, W, tau: float):
+    """Per-table bucket sums of the keys of one head ([zh] §2.2 bucket
+    aggregation): A[l, r] = sum_j phi_lr(k_j) and B[l, r, :] = sum_j
+    phi_lr(k_j) v_j, returned together as AB[l, r, :d] = B and AB[l, r, d] = A
+    (fp64, k and v [N, d])."""
+    k, v = _f64(k), _f64(v)
+    phi, _ = soft_hash(k, W, tau)                      # [N, L, R]
+    yv = np.concatenate([v, np.ones((v.shape[0], 1))], axis=1)
+    return np.einsum("jlr,jc->lrc", phi, yv)
+
+
+def walsh_state(k, v, W, tau: float):
+    """The streaming state of one head after the keys k (values v), in the
+    Walsh basis of each table: S[16 l + s, :] = 1/4 sum_r chi_s(r) AB[l, r, :]
+    with chi_s(r) = prod_{p in s} c_rp and AB from bucket_sums.  Since the
+    corner weights are phi_lr = prod_p (1 + c_rp t_lp) / 2 (pin P-2),
+    1/4 sum_r chi_s(r) phi_lr = 1/4 prod_{p in s} t_lp: S is the sum over the
+    keys of those products times [v | 1].  Returns [L * R, d + 1] fp64.
+
+    The readout of step 7 ([zh] §2.2) from it, sum_l phi_l(q)^T AB_l, equals
+    psi(q) S with psi_{16 l + s}(q) = 1/4 sum_r chi_s(r) phi_lr(q), because
+    sum_s chi_s(r) chi_s(r') = R [r == r']."""
+    AB = bucket_sums(k, v, W, tau)                     # [L, R, d + 1]
+    L, R, C = AB.shape
+    P = R.bit_length() - 1
+    r = np.arange(R)
+    c = np.where(((r[:, None] >> np.arange(P)[None, :]) & 1) == 1, 1.0, -1.0)   # [R, P]
+    s_bits = ((np.arange(R)[:, None] >> np.arange(P)[None, :]) & 1) == 1        # [S, P]
+    chi = np.prod(np.where(s_bits[:, None, :], c[None, :, :], 1.0), axis=2)     # [S, R]
+    return (0.25 * np.einsum("sr,lrc->lsc", chi, AB)).reshape(L * R, C)

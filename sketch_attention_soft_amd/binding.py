@@ -21,7 +21,9 @@ STATUS = {
 }
 EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forward",
            "race_attn_backward", "race_attn_forward_ex", "race_attn_backward_ex",
-           "race_attn_status_string")
+           "race_attn_squash_coeffs", "race_attn_squash_deriv_coeffs",
+           "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
+           "race_attn_decode", "race_attn_state_readout", "race_attn_status_string")
 TRACE_MAX = 24
 
 
@@ -87,6 +89,20 @@ def lib():
         L.race_attn_forward_ex.restype = i32
         L.race_attn_backward_ex.argtypes = L.race_attn_backward.argtypes + [vp, tp]
         L.race_attn_backward_ex.restype = i32
+        L.race_attn_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.race_attn_state_bytes.restype = i32
+        L.race_attn_state_add_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32,
+                                                          ctypes.POINTER(sz)]
+        L.race_attn_state_add_workspace_bytes.restype = i32
+        L.race_attn_state_add.argtypes = [vp, vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
+                                          vp, sz, vp]
+        L.race_attn_state_add.restype = i32
+        L.race_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
+                                       vp, vp, vp]
+        L.race_attn_decode.restype = i32
+        L.race_attn_state_readout.argtypes = [vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
+                                              vp, vp, vp]
+        L.race_attn_state_readout.restype = i32
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -232,3 +248,86 @@ class RaceAttention(torch.autograd.Function):
 
 def race_attention(q, k, v, W, tau: float = 1.0, causal: bool = True, chunk: int = 0):
     return RaceAttention.apply(q, k, v, W, tau, causal, chunk)
+
+
+# ---------------------------------------------------------------------------
+# Streaming state (race_attn_state_* / race_attn_decode in include/race_attn.h)
+
+def _check_w(W, ref):
+    if W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous() or W.device != ref.device:
+        raise ValueError("W must be a contiguous fp32 [L, P, d] tensor on the same device")
+    return W.shape[0], W.shape[1]
+
+
+def state_bytes(B, H, d, L, P) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_state_bytes(B, H, d, L, P, ctypes.byref(out)))
+    return out.value
+
+
+def new_state(B, H, d, L, P, device) -> torch.Tensor:
+    """Zeroed states [B, H, 16 L, d + 1] (fp32): the empty prefix of every head."""
+    state_bytes(B, H, d, L, P)  # validates the shape
+    return torch.zeros((B, H, L << P, d + 1), dtype=torch.float32, device=device)
+
+
+def _check_state(state, B, H, d, L, P, ref):
+    if (state.dtype != torch.float32 or state.shape != (B, H, L << P, d + 1)
+            or not state.is_contiguous() or state.device != ref.device):
+        raise ValueError("state must be a contiguous fp32 [B, H, 16 L, d + 1] tensor")
+
+
+def state_add_workspace_bytes(B, H, N, d, L, P) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().race_attn_state_add_workspace_bytes(B, H, N, d, L, P, ctypes.byref(out)))
+    return out.value
+
+
+def state_add(state, k, v, W, tau: float, workspace=None):
+    """state += the sums of the rows of k, v ([B, H, N, d]); returns state."""
+    B, H, N, d = _shape(k)
+    _check_tensors(k, v)
+    L, P = _check_w(W, k)
+    _check_state(state, B, H, d, L, P, k)
+    nbytes = state_add_workspace_bytes(B, H, N, d, L, P)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    _check(lib().race_attn_state_add(k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P, float(tau),
+                                     B, H, N, d, dtype_code(k.dtype), state.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream()))
+    return state
+
+
+def decode(state, q, k, v, W, tau: float, out=None):
+    """Appends the T tokens of q, k, v ([B, H, T, d]) to state in order; returns
+    their causal outputs (o, den)."""
+    B, H, T, d = _shape(q)
+    _check_tensors(q, k, v)
+    L, P = _check_w(W, q)
+    _check_state(state, B, H, d, L, P, q)
+    if out is None:
+        o = torch.empty_like(q)
+        den = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    else:
+        o, den = out
+    _check(lib().race_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P,
+                                  float(tau), B, H, T, d, dtype_code(q.dtype), state.data_ptr(),
+                                  o.data_ptr(), den.data_ptr(), _stream()))
+    return o, den
+
+
+def state_readout(state, q, W, tau: float, out=None):
+    """Readout of the rows of q ([B, H, T, d]) from state (not modified): (o, den)."""
+    B, H, T, d = _shape(q)
+    _check_tensors(q)
+    L, P = _check_w(W, q)
+    _check_state(state, B, H, d, L, P, q)
+    if out is None:
+        o = torch.empty_like(q)
+        den = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    else:
+        o, den = out
+    _check(lib().race_attn_state_readout(q.data_ptr(), W.data_ptr(), L, P, float(tau), B, H, T,
+                                         d, dtype_code(q.dtype), state.data_ptr(), o.data_ptr(),
+                                         den.data_ptr(), _stream()))
+    return o, den

@@ -12,6 +12,7 @@
 #include "race_bwd.h"
 #include "race_common.h"
 #include "race_fwd.h"
+#include "race_stream.h"
 #include "race_walk.h"
 
 namespace {
@@ -541,6 +542,57 @@ race_status_t check_trace(race_trace_t *trace)
     return RACE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Streaming state (race_stream.h)
+
+struct StreamPlan {
+    int BH, L, F, fpt, nthr;
+    int64_t elems;  // floats of one head's state
+};
+
+race_status_t stream_plan(int B, int H, int64_t N, int d, int L, int P, race_dtype_t dt,
+                          StreamPlan *sp)
+{
+    if (B < 1 || H < 1 || N < 0 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
+    if (d != race::HD || P != race::NP || L > 64) return RACE_ERR_UNSUPPORTED;
+    if (dt != RACE_F32 && dt != RACE_BF16) return RACE_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > 65535) return RACE_ERR_UNSUPPORTED;  // heads go to the second grid dimension
+    if (N > ((int64_t)1 << 62) / (BH * race::HD)) return RACE_ERR_SHAPE;
+    sp->BH = (int)BH;
+    sp->L = L;
+    sp->F = L * race::NR;
+    sp->fpt = sp->F > 256 ? 64 : 32;
+    sp->nthr = 64 * ((sp->F + sp->fpt - 1) / sp->fpt);  // one wave per feature group
+    sp->elems = (int64_t)sp->F * race::S_C;
+    return RACE_OK;
+}
+
+// token blocks per head for the parallel modes: about 1024 workgroups in all,
+// at least 64 tokens per block
+int64_t stream_blocks(const StreamPlan &sp, int64_t N)
+{
+    const int64_t want = (1024 + sp.BH - 1) / sp.BH;
+    return std::max<int64_t>(1, std::min<int64_t>(want, (N + 63) / 64));
+}
+
+template <typename T, int MODE>
+void launch_stream(const StreamPlan &sp, const void *Q, const void *K, const void *V,
+                   const float *W, float tau, int64_t N, int64_t nblk, float *state, float *part,
+                   void *O, float *den, hipStream_t s)
+{
+    const int64_t blk = (N + nblk - 1) / nblk;
+    const dim3 grid((unsigned)nblk, (unsigned)sp.BH);
+    // 32 or 64 features per wave; up to 8 waves (256 registers per lane), or
+    // 16 for L > 32 (128 registers)
+    auto k = sp.fpt == 32       ? race::stream_kernel<T, MODE, 32, 512>
+             : sp.nthr <= 512   ? race::stream_kernel<T, MODE, 64, 512>
+                                : race::stream_kernel<T, MODE, 64, 1024>;
+    hipLaunchKernelGGL(k, grid, dim3(sp.nthr), 0, s, static_cast<const T *>(Q),
+                       static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, 1.f / tau,
+                       N, blk, state, part, static_cast<T *>(O), den);
+}
+
 }  // namespace
 
 extern "C" {
@@ -662,6 +714,100 @@ race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, i
 race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *coef, int *deg)
 {
     return squash_coeffs(tau, dt, coef, deg, true);
+}
+
+race_status_t race_attn_state_bytes(int B, int H, int d, int L, int P, size_t *bytes)
+{
+    if (!bytes) return RACE_ERR_NULL;
+    StreamPlan sp;
+    race_status_t st = stream_plan(B, H, 1, d, L, P, RACE_F32, &sp);
+    if (st != RACE_OK) return st;
+    *bytes = (size_t)sp.BH * sp.elems * sizeof(float);
+    return RACE_OK;
+}
+
+race_status_t race_attn_state_add_workspace_bytes(int B, int H, int64_t N, int d, int L, int P,
+                                                  size_t *bytes)
+{
+    if (!bytes) return RACE_ERR_NULL;
+    StreamPlan sp;
+    race_status_t st = stream_plan(B, H, N, d, L, P, RACE_F32, &sp);
+    if (st != RACE_OK) return st;
+    *bytes = N == 0 ? 0 : (size_t)sp.BH * stream_blocks(sp, N) * sp.elems * sizeof(float);
+    return RACE_OK;
+}
+
+race_status_t race_attn_state_add(const void *K, const void *V, const float *W, int L, int P,
+                                  float tau, int B, int H, int64_t N, int d, race_dtype_t dt,
+                                  float *state, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!W || !state) return RACE_ERR_NULL;
+    StreamPlan sp;
+    race_status_t st = stream_plan(B, H, N, d, L, P, dt, &sp);
+    if (st != RACE_OK) return st;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if (N == 0) return RACE_OK;  // the row pointers may be NULL then
+    if (!K || !V) return RACE_ERR_NULL;
+    const int64_t nblk = stream_blocks(sp, N);
+    if (!workspace) return RACE_ERR_NULL;
+    if (ws_bytes < (size_t)sp.BH * nblk * sp.elems * sizeof(float) || ((uintptr_t)workspace & 255))
+        return RACE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *part = static_cast<float *>(workspace);
+    (void)hipGetLastError();
+    if (dt == RACE_BF16)
+        launch_stream<bf16, race::SM_ADD>(sp, nullptr, K, V, W, tau, N, nblk, state, part, nullptr,
+                                          nullptr, s);
+    else
+        launch_stream<float, race::SM_ADD>(sp, nullptr, K, V, W, tau, N, nblk, state, part,
+                                           nullptr, nullptr, s);
+    hipLaunchKernelGGL(race::stream_reduce_kernel, dim3((unsigned)((sp.elems + 255) / 256), sp.BH),
+                       dim3(256), 0, s, part, (int)nblk, sp.elems, state);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_decode(const void *Q, const void *K, const void *V, const float *W,
+                               int L, int P, float tau, int B, int H, int64_t T, int d,
+                               race_dtype_t dt, float *state, void *O, float *den, void *stream)
+{
+    if (!W || !state) return RACE_ERR_NULL;
+    StreamPlan sp;
+    race_status_t st = stream_plan(B, H, T, d, L, P, dt, &sp);
+    if (st != RACE_OK) return st;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if (T == 0) return RACE_OK;  // the row pointers may be NULL then
+    if (!Q || !K || !V || !O || !den) return RACE_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (dt == RACE_BF16)
+        launch_stream<bf16, race::SM_DECODE>(sp, Q, K, V, W, tau, T, 1, state, nullptr, O, den, s);
+    else
+        launch_stream<float, race::SM_DECODE>(sp, Q, K, V, W, tau, T, 1, state, nullptr, O, den, s);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int P, float tau,
+                                      int B, int H, int64_t T, int d, race_dtype_t dt,
+                                      const float *state, void *O, float *den, void *stream)
+{
+    if (!W || !state) return RACE_ERR_NULL;
+    StreamPlan sp;
+    race_status_t st = stream_plan(B, H, T, d, L, P, dt, &sp);
+    if (st != RACE_OK) return st;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if (T == 0) return RACE_OK;  // the row pointers may be NULL then
+    if (!Q || !O || !den) return RACE_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *sv = const_cast<float *>(state);  // read only in this mode
+    (void)hipGetLastError();
+    const int64_t nblk = stream_blocks(sp, T);
+    if (dt == RACE_BF16)
+        launch_stream<bf16, race::SM_READOUT>(sp, Q, nullptr, nullptr, W, tau, T, nblk, sv,
+                                              nullptr, O, den, s);
+    else
+        launch_stream<float, race::SM_READOUT>(sp, Q, nullptr, nullptr, W, tau, T, nblk, sv,
+                                               nullptr, O, den, s);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 
 const char *race_attn_status_string(race_status_t status)

@@ -1,0 +1,213 @@
+// race_stream.h -- the streaming form of RACE attention (gfx950): a persistent
+// per-head state that tokens are appended to and read from, for inference
+// (decode) after a prompt.
+//
+// Pages: "RACE Attention: A Strictly Linear-Time Attention for Long-Sequence
+// Training", gist.science/zh/paper/2510.04008, technical summary §2.3 (causal
+// mode keeps running bucket sums and reads them at every step, so each step
+// costs the same however long the prefix) and §2.2 (bucket sums A and B, the
+// ratio readout).
+//
+// State of one head: S[f][c] for f < F = 16 L, c <= d (fp32, [F][d + 1]):
+//   S[f][c] = sum_j psi_f(k_j) v_j[c] (c < d),  S[f][d] = sum_j psi_f(k_j),
+//   psi_{16 l + s}(x) = 1/4 prod_{p in s} t_{lp}(x)  (s: a subset of the
+//   table's 4 hyperplanes, bit p set when p is in it),
+//   t_{lp}(x) = tanh(tanh(<w_lp, x / max(|x|, 1e-12)>) / tau).
+// The corner weights of the pages are phi_lr = prod_p (1 + c_rp t_lp) / 2, so
+// psi is their Walsh-Hadamard transform and psi(q).psi(k) = phi(q).phi(k): S
+// holds the pages' bucket sums A and B in that basis, and a readout is
+// [n | m] = psi(q) S, o = n / m, den = m.
+//
+// One kernel in three modes, over the tokens [b blk, (b + 1) blk) of a head:
+//   ADD      S_b = sum over the block (from zero), to a partial buffer; the
+//            partials are then added to the state in block order.
+//   DECODE   token by token: S += psi(k_i)^T [v_i | 1], then o_i from
+//            psi(q_i) S (one workgroup per head, the causal recurrence).
+//   READOUT  o_i from psi(q_i) S for a fixed S (no append).
+// Wave g of a workgroup owns the features [g FPT, (g + 1) FPT): lane c keeps
+// S[f][c] of those features in registers for the whole block, and the count
+// column S[f][d] is spread over the wave's lanes (feature g FPT + 64 z + lane
+// in slot z).  Tokens go in tiles of TT: rows staged in LDS, projections and
+// features of the tile in LDS, then every wave applies the tile to its slice
+// of S.  The per-token work is the F x (d + 1) update and readout, in fp32
+// vector arithmetic; the state (133 KB per head at L = 32) is read and
+// written once per call.
+#pragma once
+#include "race_common.h"
+
+namespace race {
+
+constexpr int SM_ADD = 0, SM_DECODE = 1, SM_READOUT = 2;
+constexpr int S_TT = 8;          // tokens per tile
+constexpr int S_C = HD + 1;      // state columns
+constexpr int S_FMAX = 1024;     // features, L <= 64
+constexpr int S_LPMAX = 256;     // hyperplanes, L <= 64
+constexpr int S_MAXW = 16;       // waves (feature groups) per workgroup
+
+template <typename T> __device__ __forceinline__ float sload(const T *p) { return (float)*p; }
+
+template <typename T, int MODE, int FPT, int MAXT>
+__global__ __launch_bounds__(MAXT) void stream_kernel(
+    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
+    const float *__restrict__ W, int L, float inv_tau, int64_t N, int64_t blk,
+    float *__restrict__ state, float *__restrict__ part, T *__restrict__ O, float *__restrict__ den)
+{
+    constexpr bool UPD = MODE != SM_READOUT, RD = MODE != SM_ADD;
+    constexpr int ZP = (FPT + 63) / 64;         // count-column slots per lane
+    __shared__ float xr[2][S_TT][HD];           // staged q (0) and k (1) rows
+    __shared__ float yv[S_TT][HD];              // staged v rows
+    __shared__ float inrm[2][S_TT];             // 1 / max(|x|, 1e-12)
+    __shared__ float tv[2][S_TT][S_LPMAX];      // squashed projections t
+    __shared__ float ps[2][S_TT][S_FMAX];       // features psi (zero past F)
+    __shared__ float pn[S_TT][S_MAXW][HD];      // partial readouts n of the waves
+    __shared__ float pm[S_TT][S_MAXW];          // and of m
+
+    const int LP = L * NP, F = L * NR;
+    const int QN = (F + FPT - 1) / FPT;
+    const int nthr = blockDim.x, tid = threadIdx.x;
+    const int c = tid & 63, grp = tid >> 6, f0 = grp * FPT;
+    const int64_t bh = blockIdx.y;
+    const int64_t t_begin = (int64_t)blockIdx.x * blk, t_end = min(N, t_begin + blk);
+    const int64_t row0 = bh * N;
+    float *sh = state + bh * (int64_t)F * S_C;
+
+    float S[FPT], Z[ZP];
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) S[i] = (MODE != SM_ADD && f0 + i < F) ? sh[(int64_t)(f0 + i) * S_C + c] : 0.f;
+#pragma unroll
+    for (int z = 0; z < ZP; ++z) {
+        const int f = f0 + 64 * z + c;
+        Z[z] = (MODE != SM_ADD && 64 * z + c < FPT && f < F) ? sh[(int64_t)f * S_C + HD] : 0.f;
+    }
+
+    for (int64_t tile = t_begin; tile < t_end; tile += S_TT) {
+        const int nt = (int)min<int64_t>(S_TT, t_end - tile);
+        // rows of the tile (zeros past the end)
+        for (int e = tid; e < S_TT * HD; e += nthr) {
+            const int t = e / HD, k = e % HD;
+            float q = 0.f, kk = 0.f, v = 0.f;
+            if (t < nt) {
+                const int64_t off = (row0 + tile + t) * HD + k;
+                if (RD) q = sload(Q + off);
+                if (UPD) {
+                    kk = sload(K + off);
+                    v = sload(V + off);
+                }
+            }
+            xr[0][t][k] = q;
+            xr[1][t][k] = kk;
+            yv[t][k] = v;
+        }
+        __syncthreads();
+        if (tid < 2 * S_TT) {
+            const int side = tid / S_TT, t = tid % S_TT;
+            if ((side == 0 && RD) || (side == 1 && UPD)) {
+                float ss = 0.f;
+                for (int k = 0; k < HD; ++k) ss = fmaf(xr[side][t][k], xr[side][t][k], ss);
+                inrm[side][t] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+            }
+        }
+        __syncthreads();
+        // projections: thread (side, h) for all tokens of the tile
+        for (int j = tid; j < 2 * LP; j += nthr) {
+            const int side = j / LP, h = j % LP;
+            if ((side == 0 && !RD) || (side == 1 && !UPD)) continue;
+            float u[S_TT];
+#pragma unroll
+            for (int t = 0; t < S_TT; ++t) u[t] = 0.f;
+            const float *wr = W + (int64_t)h * HD;
+#pragma unroll 4
+            for (int k = 0; k < HD; ++k) {
+                const float wk = wr[k];
+#pragma unroll
+                for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < S_TT; ++t) tv[side][t][h] = tanhf(tanhf(u[t] * inrm[side][t]) * inv_tau);
+        }
+        __syncthreads();
+        // features, zero past F up to the waves' end
+        for (int e = tid; e < 2 * S_TT * QN * FPT; e += nthr) {
+            const int side = e / (S_TT * QN * FPT), r = e % (S_TT * QN * FPT);
+            const int t = r / (QN * FPT), f = r % (QN * FPT);
+            if ((side == 0 && !RD) || (side == 1 && !UPD)) continue;
+            float p = 0.f;
+            if (f < F) {
+                const float *tl = &tv[side][t][(f >> 4) * NP];
+                p = 0.25f;
+#pragma unroll
+                for (int b = 0; b < NP; ++b)
+                    if ((f >> b) & 1) p *= tl[b];
+            }
+            ps[side][t][f] = p;
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int t = 0; t < nt; ++t) {
+            if (UPD) {
+                const float y = yv[t][c];
+#pragma unroll
+                for (int i = 0; i < FPT; ++i) S[i] = fmaf(ps[1][t][f0 + i], y, S[i]);
+#pragma unroll
+                for (int z = 0; z < ZP; ++z)
+                    if (64 * z + c < FPT) Z[z] += ps[1][t][f0 + 64 * z + c];
+            }
+            if (RD) {
+                float n = 0.f, m = 0.f;
+#pragma unroll
+                for (int i = 0; i < FPT; ++i) n = fmaf(ps[0][t][f0 + i], S[i], n);
+#pragma unroll
+                for (int z = 0; z < ZP; ++z)
+                    if (64 * z + c < FPT) m = fmaf(ps[0][t][f0 + 64 * z + c], Z[z], m);
+                pn[t][grp][c] = n;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) m += __shfl_xor(m, o, 64);
+                if (c == 0) pm[t][grp] = m;
+            }
+        }
+        __syncthreads();
+        if (RD) {
+            for (int e = tid; e < nt * S_C; e += nthr) {
+                const int t = e / S_C, col = e % S_C;
+                float n = 0.f, m = 0.f;
+                for (int g = 0; g < QN; ++g) {
+                    if (col < HD) n += pn[t][g][col];
+                    m += pm[t][g];
+                }
+                const int64_t row = row0 + tile + t;
+                if (col < HD)
+                    O[row * HD + col] = (T)(n / m);
+                else
+                    den[row] = m;
+            }
+        }
+        __syncthreads();  // the tile's LDS is rewritten next
+    }
+    if (MODE != SM_READOUT) {
+        float *dst = MODE == SM_DECODE ? sh : part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * S_C;
+#pragma unroll
+        for (int i = 0; i < FPT; ++i)
+            if (f0 + i < F) dst[(int64_t)(f0 + i) * S_C + c] = S[i];
+#pragma unroll
+        for (int z = 0; z < ZP; ++z) {
+            const int f = f0 + 64 * z + c;
+            if (64 * z + c < FPT && f < F) dst[(int64_t)f * S_C + HD] = Z[z];
+        }
+    }
+}
+
+// state[head] += sum over the blocks b = 0, 1, ... of part[head][b] (in that
+// order, so the result does not depend on the launch)
+__global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part, int nblk,
+                                                            int64_t elems, float *__restrict__ state)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= elems) return;
+    const int64_t bh = blockIdx.y;
+    float acc = state[bh * elems + e];
+    const float *p = part + bh * (int64_t)nblk * elems + e;
+    for (int b = 0; b < nblk; ++b) acc += p[(int64_t)b * elems];
+    state[bh * elems + e] = acc;
+}
+
+}  // namespace race

@@ -235,3 +235,75 @@ def test_squash_rejects_bad_tau(lib):
     deg = ctypes.c_int(0)
     assert lib.race_attn_squash_coeffs(0.0, BF16, coef, ctypes.byref(deg)) == E_TAU
     assert lib.race_attn_squash_coeffs(1.0, BF16, None, ctypes.byref(deg)) == E_NULL
+
+
+# ---------------------------------------------------------------------------
+# Streaming state entry points (validation and sizes only: no kernel runs)
+
+def _stream_lib(lib):
+    i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    lib.race_attn_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.race_attn_state_add_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32,
+                                                        ctypes.POINTER(sz)]
+    lib.race_attn_state_add.argtypes = [vp, vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
+                                        vp, sz, vp]
+    lib.race_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
+                                     vp, vp, vp]
+    lib.race_attn_state_readout.argtypes = [vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
+                                            vp, vp, vp]
+    return lib
+
+
+def test_state_bytes(lib):
+    L = _stream_lib(lib)
+    out = ctypes.c_size_t(0)
+    # [B][H][16 L][d + 1] fp32
+    assert L.race_attn_state_bytes(2, 3, 64, 32, 4, ctypes.byref(out)) == OK
+    assert out.value == 2 * 3 * 512 * 65 * 4
+    assert L.race_attn_state_bytes(1, 1, 64, 5, 4, ctypes.byref(out)) == OK
+    assert out.value == 80 * 65 * 4
+    assert L.race_attn_state_bytes(1, 1, 64, 32, 4, None) == E_NULL
+    for args, code in (((0, 1, 64, 8, 4), E_SHAPE), ((1, 1, 32, 8, 4), E_UNSUP),
+                       ((1, 1, 64, 8, 3), E_UNSUP), ((1, 1, 64, 65, 4), E_UNSUP),
+                       ((1, 1, 64, 0, 4), E_SHAPE), ((65536, 1, 64, 8, 4), E_UNSUP)):
+        assert L.race_attn_state_bytes(*args, ctypes.byref(out)) == code, args
+
+
+def test_state_add_workspace(lib):
+    L = _stream_lib(lib)
+    out = ctypes.c_size_t(7)
+    assert L.race_attn_state_add_workspace_bytes(1, 1, 0, 64, 32, 4, ctypes.byref(out)) == OK
+    assert out.value == 0
+    # block partials of one state each, at most about 1024 blocks in all
+    assert L.race_attn_state_add_workspace_bytes(1, 1, 1 << 22, 64, 32, 4, ctypes.byref(out)) == OK
+    assert out.value == 1024 * 512 * 65 * 4
+    assert L.race_attn_state_add_workspace_bytes(64, 1, 100, 64, 32, 4, ctypes.byref(out)) == OK
+    assert out.value == 64 * 2 * 512 * 65 * 4
+    assert L.race_attn_state_add_workspace_bytes(1, 1, -1, 64, 32, 4, ctypes.byref(out)) == E_SHAPE
+
+
+def test_stream_validation(lib):
+    L = _stream_lib(lib)
+    F = FAKE
+    # state_add: nulls, tau, dtype, workspace size and alignment
+    assert L.race_attn_state_add(None, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, F, F, 1 << 30, None) == E_NULL
+    assert L.race_attn_state_add(F, F, None, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, F, 1 << 30, None) == E_NULL
+    assert L.race_attn_state_add(F, F, F, 8, 4, 0.0, 1, 1, 64, 64, BF16, F, F, 1 << 30, None) == E_TAU
+    assert L.race_attn_state_add(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, 7, F, F, 1 << 30, None) == E_UNSUP
+    assert L.race_attn_state_add(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, F, F, 16, None) == E_WS
+    assert L.race_attn_state_add(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, F, F + 4, 1 << 30, None) == E_WS
+    assert L.race_attn_state_add(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, F, None, 1 << 30, None) == E_NULL
+    # N = 0 is a no-op that needs no workspace
+    assert L.race_attn_state_add(F, F, F, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, None, 0, None) == OK
+    # decode / readout
+    assert L.race_attn_decode(F, F, F, F, 8, 4, 1.0, 1, 1, 4, 64, BF16, None, F, F, None) == E_NULL
+    assert L.race_attn_decode(F, F, F, F, 8, 4, float("nan"), 1, 1, 4, 64, BF16, F, F, F, None) == E_TAU
+    assert L.race_attn_decode(F, F, F, F, 8, 4, 1.0, 1, 1, -1, 64, BF16, F, F, F, None) == E_SHAPE
+    assert L.race_attn_decode(F, F, F, F, 8, 4, 1.0, 1, 1, 4, 128, BF16, F, F, F, None) == E_UNSUP
+    assert L.race_attn_decode(None, None, None, F, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, None, None, None) == OK
+    assert L.race_attn_decode(F, None, F, F, 8, 4, 1.0, 1, 1, 3, 64, BF16, F, F, F, None) == E_NULL
+    assert L.race_attn_state_readout(F, F, 8, 4, 1.0, 1, 1, 4, 64, BF16, F, None, F, None) == E_NULL
+    assert L.race_attn_state_readout(F, F, 8, 5, 1.0, 1, 1, 4, 64, BF16, F, F, F, None) == E_UNSUP
+    assert L.race_attn_state_readout(None, F, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, None, None, None) == OK
+    assert L.race_attn_state_readout(F, F, 8, 4, 1.0, 1, 1, 2, 64, BF16, None, F, F, None) == E_NULL
