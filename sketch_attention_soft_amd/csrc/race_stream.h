@@ -38,29 +38,35 @@
 namespace race {
 
 constexpr int SM_ADD = 0, SM_DECODE = 1, SM_READOUT = 2;
-constexpr int S_TT = 8;          // tokens per tile
 constexpr int S_C = HD + 1;      // state columns
-constexpr int S_FMAX = 1024;     // features, L <= 64
-constexpr int S_LPMAX = 256;     // hyperplanes, L <= 64
-constexpr int S_MAXW = 16;       // waves (feature groups) per workgroup
+constexpr int S_XS = HD + 1;     // LDS row stride of staged rows and W (odd: no bank conflicts)
 
 template <typename T> __device__ __forceinline__ float sload(const T *p) { return (float)*p; }
 
+// MAXT threads = MAXT / 64 waves of FPT features: F <= FMAX = FPT MAXT / 64
+// and L P <= FMAX P / 16 (the launch picks the instance that fits).  Tiles
+// of S_TT tokens.
 template <typename T, int MODE, int FPT, int MAXT>
-__global__ __launch_bounds__(MAXT) void stream_kernel(
+__global__ __launch_bounds__(MAXT)
+__attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) void stream_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
     const float *__restrict__ W, int L, float inv_tau, int64_t N, int64_t blk,
     float *__restrict__ state, float *__restrict__ part, T *__restrict__ O, float *__restrict__ den)
 {
     constexpr bool UPD = MODE != SM_READOUT, RD = MODE != SM_ADD;
-    constexpr int ZP = (FPT + 63) / 64;         // count-column slots per lane
-    __shared__ float xr[2][S_TT][HD];           // staged q (0) and k (1) rows
-    __shared__ float yv[S_TT][HD];              // staged v rows
-    __shared__ float inrm[2][S_TT];             // 1 / max(|x|, 1e-12)
-    __shared__ float tv[2][S_TT][S_LPMAX];      // squashed projections t
-    __shared__ float ps[2][S_TT][S_FMAX];       // features psi (zero past F)
-    __shared__ float pn[S_TT][S_MAXW][HD];      // partial readouts n of the waves
-    __shared__ float pm[S_TT][S_MAXW];          // and of m
+    constexpr int NS = (UPD ? 1 : 0) + (RD ? 1 : 0);  // row sides: queries (if RD), then keys (if UPD)
+    constexpr int KS = RD ? 1 : 0;                     // side of the keys
+    constexpr int NWV = MAXT / 64, FMAX = FPT * NWV, LPMAX = FMAX / NR * NP;
+    constexpr int ZP = (FPT + 63) / 64;                // count-column slots per lane
+    constexpr int S_TT = NS == 2 && FMAX > 512 ? 4 : 8;  // tokens per tile (LDS of L > 32 decode)
+    __shared__ float wl[MODE != SM_DECODE ? LPMAX * S_XS : 1];  // W rows
+    __shared__ float xr[NS][S_TT][S_XS];               // staged rows
+    __shared__ float yv[UPD ? S_TT : 1][HD];           // staged v rows
+    __shared__ float inrm[NS][S_TT];                   // 1 / max(|x|, 1e-12)
+    __shared__ float tv[NS][S_TT][LPMAX];              // squashed projections t
+    __shared__ float ps[NS][S_TT][FMAX];               // features psi (zero past F)
+    __shared__ float pn[RD ? S_TT : 1][NWV][HD];       // partial readouts n of the waves
+    __shared__ float pm[RD ? S_TT : 1][NWV];           // and of m
 
     const int LP = L * NP, F = L * NR;
     const int QN = (F + FPT - 1) / FPT;
@@ -71,6 +77,11 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(
     const int64_t row0 = bh * N;
     float *sh = state + bh * (int64_t)F * S_C;
 
+    // W rows in LDS for the parallel modes; decode (mostly a few tokens) reads
+    // them from global memory instead of waiting for the staging
+    constexpr bool wlds = MODE != SM_DECODE;
+    if (wlds)
+        for (int e = tid; e < LP * HD; e += nthr) wl[(e / HD) * S_XS + e % HD] = W[e];
     float S[FPT], Z[ZP];
 #pragma unroll
     for (int i = 0; i < FPT; ++i) S[i] = (MODE != SM_ADD && f0 + i < F) ? sh[(int64_t)(f0 + i) * S_C + c] : 0.f;
@@ -94,43 +105,53 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(
                     v = sload(V + off);
                 }
             }
-            xr[0][t][k] = q;
-            xr[1][t][k] = kk;
-            yv[t][k] = v;
+            if (RD) xr[0][t][k] = q;
+            if (UPD) {
+                xr[KS][t][k] = kk;
+                yv[t][k] = v;
+            }
         }
         __syncthreads();
-        if (tid < 2 * S_TT) {
-            const int side = tid / S_TT, t = tid % S_TT;
-            if ((side == 0 && RD) || (side == 1 && UPD)) {
-                float ss = 0.f;
-                for (int k = 0; k < HD; ++k) ss = fmaf(xr[side][t][k], xr[side][t][k], ss);
-                inrm[side][t] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
-            }
+        // squared norms: wave w takes rows w, w + NWV, ...; lane k one element
+        for (int r = grp; r < NS * nt; r += nthr >> 6) {
+            const int side = r / nt, t = r % nt;
+            float ss = xr[side][t][c] * xr[side][t][c];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+            if (c == 0) inrm[side][t] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
         }
         __syncthreads();
         // projections: thread (side, h) for all tokens of the tile
-        for (int j = tid; j < 2 * LP; j += nthr) {
+        for (int j = tid; j < NS * LP; j += nthr) {
             const int side = j / LP, h = j % LP;
-            if ((side == 0 && !RD) || (side == 1 && !UPD)) continue;
             float u[S_TT];
 #pragma unroll
             for (int t = 0; t < S_TT; ++t) u[t] = 0.f;
-            const float *wr = W + (int64_t)h * HD;
-#pragma unroll 4
-            for (int k = 0; k < HD; ++k) {
-                const float wk = wr[k];
+            if constexpr (wlds) {
+#pragma unroll 8
+                for (int k = 0; k < HD; ++k) {
+                    const float wk = wl[h * S_XS + k];
 #pragma unroll
-                for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
+                    for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
+                }
+            } else {
+                const float *wg = W + (int64_t)h * HD;
+#pragma unroll 4
+                for (int k = 0; k < HD; ++k) {
+                    const float wk = wg[k];
+#pragma unroll
+                    for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
+                }
             }
 #pragma unroll
-            for (int t = 0; t < S_TT; ++t) tv[side][t][h] = tanhf(tanhf(u[t] * inrm[side][t]) * inv_tau);
+            for (int t = 0; t < S_TT; ++t)
+                if (t < nt) tv[side][t][h] = tanhf(tanhf(u[t] * inrm[side][t]) * inv_tau);
         }
         __syncthreads();
-        // features, zero past F up to the waves' end
-        for (int e = tid; e < 2 * S_TT * QN * FPT; e += nthr) {
-            const int side = e / (S_TT * QN * FPT), r = e % (S_TT * QN * FPT);
+        // features of the tile's tokens, zero past F up to the waves' end
+        for (int e = tid; e < NS * nt * QN * FPT; e += nthr) {
+            const int side = e / (nt * QN * FPT), r = e % (nt * QN * FPT);
             const int t = r / (QN * FPT), f = r % (QN * FPT);
-            if ((side == 0 && !RD) || (side == 1 && !UPD)) continue;
             float p = 0.f;
             if (f < F) {
                 const float *tl = &tv[side][t][(f >> 4) * NP];
@@ -147,10 +168,10 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(
             if (UPD) {
                 const float y = yv[t][c];
 #pragma unroll
-                for (int i = 0; i < FPT; ++i) S[i] = fmaf(ps[1][t][f0 + i], y, S[i]);
+                for (int i = 0; i < FPT; ++i) S[i] = fmaf(ps[KS][t][f0 + i], y, S[i]);
 #pragma unroll
                 for (int z = 0; z < ZP; ++z)
-                    if (64 * z + c < FPT) Z[z] += ps[1][t][f0 + 64 * z + c];
+                    if (64 * z + c < FPT) Z[z] += ps[KS][t][f0 + 64 * z + c];
             }
             if (RD) {
                 float n = 0.f, m = 0.f;
@@ -180,8 +201,8 @@ __global__ __launch_bounds__(MAXT) void stream_kernel(
                 else
                     den[row] = m;
             }
+            __syncthreads();  // the tile's LDS is rewritten next
         }
-        __syncthreads();  // the tile's LDS is rewritten next
     }
     if (MODE != SM_READOUT) {
         float *dst = MODE == SM_DECODE ? sh : part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * S_C;
