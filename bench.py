@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
-def algorithmic_per_token(w):
+def algorithmic_per_token(w, dw: bool = False):
     """Algorithmic work of the method per token (one (b, h) row).
 
     flops: projections 2 d L P per hashed row (Q and K in the forward; again
@@ -36,6 +36,8 @@ def algorithmic_per_token(w):
     backward), sketch and readout 2 F (d+1) each, the query-side gradient
     2 F (d+1), the gradient sketch 2 F (d+1), dV and dphi(k) 2 F d each.
     bytes: one read of every input and one write of every output per pass.
+    dw: the backward also forms the projection gradient, 2 d L P per row of Q
+    (in dq) and of K (in dk).
     """
     d, L, P = w.d, w.L, w.P
     F, d1 = L * (1 << P), d + 1
@@ -58,8 +60,11 @@ def algorithmic_per_token(w):
         "dpsi_q": 2 * F * d1 + proj, "dpsi_k": 2 * F * d + proj,
         "readout_dv": 2 * F * d,
     }
+    if dw:
+        per_kernel["dq"] += proj
+        per_kernel["dk"] += proj
     fwd_flops = 4 * d * L * P + 4 * F * d1
-    bwd_flops = 8 * d * L * P + 4 * F * d1 + 4 * F * d
+    bwd_flops = 8 * d * L * P + 4 * F * d1 + 4 * F * d + (4 * d * L * P if dw else 0)
     if not w.backward:
         return fwd_flops, 4 * d * e + 4, per_kernel
     return fwd_flops + bwd_flops, 12 * d * e + 8, per_kernel
@@ -105,6 +110,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters), then exit")
+    ap.add_argument("--dw", action="store_true",
+                    help="the backward also returns the projection gradient dW "
+                         "(race_attn_backward_dw, learned hyperplanes)")
     ap.add_argument("--stream", action="store_true",
                     help="time the streaming state entry points instead (decode of one token "
                          "per head over 64 heads, bulk state_add of the 4M-token head)")
@@ -157,7 +165,8 @@ def main() -> int:
     grads = tuple(torch.empty_like(q) for _ in range(3)) if w.backward else None
     wsf = torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, False),
                       dtype=torch.uint8, device=dev)
-    wsb = (torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, True),
+    wsb = (torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt,
+                                               2 if args.dw else 1),
                        dtype=torch.uint8, device=dev) if w.backward else None)
     # the forward's key state, kept for the backward (as autograd would)
     saved = binding.new_saved(q, W, w.causal, w.chunk) if w.backward else None
@@ -167,7 +176,7 @@ def main() -> int:
                         trace=trf, saved=saved)
         if w.backward:
             binding.backward(q, k, v, W, o, den, do, w.tau, w.causal, w.chunk, workspace=wsb,
-                             out=grads, trace=trb, saved=saved)
+                             out=grads, trace=trb, saved=saved, dw=args.dw)
 
     for _ in range(args.warmup):
         step()
@@ -195,14 +204,15 @@ def main() -> int:
                 continue
             for name, t in tr.results():
                 kern[name] = kern.get(name, 0.0) + t / args.steps
-    flops_tok, bytes_tok, per_kernel = algorithmic_per_token(w)
+    flops_tok, bytes_tok, per_kernel = algorithmic_per_token(w, args.dw)
     dom = max(kern, key=kern.get)
     dom_ms = kern[dom]
     peak = PEAK_TFLOPS[w.dtype]
     achieved = per_kernel.get(dom, 0) * tokens / (dom_ms * 1e-3) / 1e12
     t_mfma = flops_tok * tokens / (peak * 1e12) * 1e3
     t_hbm = bytes_tok * tokens / (PEAK_HBM_GBS * 1e9) * 1e3
-    traffic = measured_traffic(w.name).get(dom)
+    # the counters were taken on the plain backward
+    traffic = None if args.dw else measured_traffic(w.name).get(dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 5),
                 "traffic": round(traffic) if traffic is not None else None, "kernel": dom,
@@ -234,7 +244,8 @@ def main() -> int:
         "data": "synthetic (seeded Philox N(0,1); Q, K rows L2-normalised)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "L": w.L,
                    "P": w.P, "tau": w.tau, "causal": w.causal,
-                   "passes": "fwd+bwd" if w.backward else "fwd", "chunk": w.chunk},
+                   "passes": ("fwd+bwd+dW" if args.dw else "fwd+bwd") if w.backward else "fwd",
+                   "chunk": w.chunk},
         "roofline": roofline,
         "step_roofline": {"t_mfma_ms": round(t_mfma, 4), "t_hbm_ms": round(t_hbm, 4),
                           "frac": round(max(t_mfma, t_hbm) / ms, 5)},

@@ -72,9 +72,11 @@ typedef enum {
 
 typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
 
-/* Workspace size, in bytes, that race_attn_forward (for_backward = 0) or
- * race_attn_backward (for_backward = 1) needs for this problem.  Pure host
- * function; `bytes` (host pointer) receives the size. */
+/* Workspace size, in bytes, that race_attn_forward (for_backward = 0),
+ * race_attn_backward (for_backward = 1) or race_attn_backward_dw
+ * (for_backward = 2; RACE_ERR_UNSUPPORTED where that entry point is) needs
+ * for this problem.  Pure host function; `bytes` (host pointer) receives the
+ * size. */
 race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, int P,
                                         int causal, int chunk, race_dtype_t dt,
                                         int for_backward, size_t *bytes);
@@ -162,6 +164,22 @@ race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, i
 race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
 
 /* Static, NUL-terminated description of a status code. */
+/* race_attn_backward_ex that also returns the gradient of the projection,
+ * for learned hyperplanes: dW = sum over the rows x of Q and K (every batch
+ * and head) of dLoss/du (x / max(|x|, 1e-12))^T, u = W x_hat (step 1), into
+ * dW (device, fp32 [L][P][d], overwritten).  dQ, dK and dV are the same as
+ * race_attn_backward_ex's.  The per-workgroup sums are added in a fixed order,
+ * so the result does not depend on the launch.  Supported for RACE_BF16 with
+ * L <= 32 (RACE_ERR_UNSUPPORTED otherwise); workspace: race_attn_workspace_bytes
+ * with for_backward = 2. */
+race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
+                                    const float *W, const void *O, const float *den,
+                                    const void *dO, int L, int P, float tau, int causal, int B,
+                                    int H, int64_t N, int d, race_dtype_t dt, int chunk, void *dQ,
+                                    void *dK, void *dV, float *dW, void *workspace,
+                                    size_t ws_bytes, void *stream, const void *saved,
+                                    race_trace_t *trace);
+
 /* Streaming state (inference).  The causal recurrence of step 5 keeps running
  * bucket sums and reads them at every step (zh §2.3: each step costs the same
  * however long the prefix), so a head can be carried as a fixed-size state

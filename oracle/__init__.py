@@ -59,6 +59,8 @@ def _load():
         lib.race_oracle_forward_backward.argtypes = [dp, dp, dp, dp, dp, c_int, c_int, c_dbl,
                                                      c_int, i64, i64, c_int, dp, dp, dp, dp, dp]
         lib.race_oracle_forward_backward.restype = c_int
+        lib.race_oracle_forward_backward_w.argtypes = lib.race_oracle_forward_backward.argtypes + [dp]
+        lib.race_oracle_forward_backward_w.restype = c_int
         _lib = lib
     return _lib
 
@@ -123,11 +125,12 @@ def forward(q, k, v, W, tau: float, causal: bool, hard: bool = False):
     return o, den
 
 
-def forward_backward(q, k, v, g, W, tau: float, causal: bool):
+def forward_backward(q, k, v, g, W, tau: float, causal: bool, with_dw: bool = False):
     """Forward plus the exact backward for upstream gradient g = dL/do.
 
-    Returns (o, den, dq, dk, dv), all fp64.  The backward uses this call's own
-    forward results only.
+    Returns (o, den, dq, dk, dv), all fp64, and with with_dw also dW [L, P, d],
+    the gradient of the projection (summed over every head and over the rows of
+    q and k).  The backward uses this call's own forward results only.
     """
     q, k, v, g, W = _f64(q), _f64(k), _f64(v), _f64(g), _f64(W)
     assert q.shape == k.shape == v.shape == g.shape and q.ndim >= 2
@@ -140,10 +143,12 @@ def forward_backward(q, k, v, g, W, tau: float, causal: bool):
     dq = np.empty(q.shape)
     dk = np.empty(q.shape)
     dv = np.empty(q.shape)
-    _check(_load().race_oracle_forward_backward(
+    dW = np.empty((L, P, d)) if with_dw else None
+    _check(_load().race_oracle_forward_backward_w(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(W), L, P, float(tau), int(causal), BH, N, d,
-        _ptr(o), _ptr(den), _ptr(dq), _ptr(dk), _ptr(dv)), "forward_backward")
-    return o, den, dq, dk, dv
+        _ptr(o), _ptr(den), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW) if with_dw else None),
+        "forward_backward")
+    return (o, den, dq, dk, dv, dW) if with_dw else (o, den, dq, dk, dv)
 
 
 def bucket_sums(k, v, W, tau: float):

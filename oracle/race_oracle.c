@@ -33,7 +33,9 @@
  *      ([zh] §2.3);
  *   9. the backward pass is the exact derivative of steps 1-8 (the pages
  *      state the method is differentiable end to end, [es] §2 item 3, [fr]
- *      §3 item 3); the chain rule is written out in backward_* below.
+ *      §3 item 3); the chain rule is written out in backward_* below, and
+ *      optionally continued to the projection W of step 2 (for learned
+ *      hyperplanes; the pages draw W at random and keep it fixed).
  *
  * Parallelism never reorders arithmetic: every running sum is updated in
  * token order and every dot product is summed in index order.  Threads only
@@ -302,22 +304,46 @@ static void row_sweep(int F, int ncol, int n, int rev, const double *a, const do
     }
 }
 
-/* Backward of steps 1-5 for every row of a block. */
-static void block_hash_backward(const headp *hp, const double *x, int64_t b0, int n,
-                                const double *dphi, double *dx)
+/* Backward of steps 1-5 for every row of a block.  With dW (may be NULL), also
+ * the gradient of the projection u = W x_hat (step 2):
+ * dW[lp][t] += sum over the block's rows, in row order, of du_lp xhat_t. */
+static int block_hash_backward(const headp *hp, const double *x, int64_t b0, int n,
+                               const double *dphi, double *dx, double *dW)
 {
     const int d = hp->d, F = hp->h.F, LP = hp->h.L * hp->h.P;
+    double *dus = NULL, *xhs = NULL;
+    if (dW) {
+        dus = malloc(sizeof(double) * (size_t)n * LP);
+        xhs = malloc(sizeof(double) * (size_t)n * d);
+        if (!dus || !xhs) { free(dus); free(xhs); return ORC_ENOMEM; }
+    }
 #pragma omp parallel
     {
         double *xh = malloc(sizeof(double) * d), *z = malloc(sizeof(double) * LP);
         double *ph = malloc(sizeof(double) * F), *du = malloc(sizeof(double) * LP);
         double *dxh = malloc(sizeof(double) * d);
 #pragma omp for schedule(static)
-        for (int i = 0; i < n; ++i)
+        for (int i = 0; i < n; ++i) {
             hash_row_backward(&hp->h, x + (b0 + i) * d, dphi + (size_t)i * F,
                               dx + (b0 + i) * d, xh, z, ph, du, dxh);
+            if (dus) {
+                memcpy(dus + (size_t)i * LP, du, sizeof(double) * LP);
+                memcpy(xhs + (size_t)i * d, xh, sizeof(double) * d);
+            }
+        }
         free(xh); free(z); free(ph); free(du); free(dxh);
     }
+    if (dW) {
+#pragma omp parallel for schedule(static)
+        for (int lp = 0; lp < LP; ++lp)
+            for (int i = 0; i < n; ++i) {
+                const double g = dus[(size_t)i * LP + lp];
+                for (int t = 0; t < d; ++t) dW[(size_t)lp * d + t] += g * xhs[(size_t)i * d + t];
+            }
+        free(dus);
+        free(xhs);
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -364,7 +390,7 @@ static int forward_head(const headp *hp, double *o, double *den)
  *   dv_j      = (G_j[:, :d])^T phi(k_j)
  *   dphi(k_j) = G_j [v_j | 1]
  * then the hash backward for dq and dk. */
-static int backward_head(const headp *hp, double *dq, double *dk, double *dv)
+static int backward_head(const headp *hp, double *dq, double *dk, double *dv, double *dW)
 {
     const int d = hp->d, d1 = hp->d1, F = hp->h.F;
     const int64_t N = hp->N;
@@ -384,7 +410,11 @@ static int backward_head(const headp *hp, double *dq, double *dk, double *dv)
         const int n = (int)(N - b0 < BLK ? N - b0 : BLK);
         fill_block(hp, b0, n, 0, causal, 1, &bb);
         row_sweep(F, d1, n, 0, bb.phk, bb.v1, bb.D, M, bb.out, causal, 1);
-        block_hash_backward(hp, hp->q, b0, n, bb.out, dq);
+        if (block_hash_backward(hp, hp->q, b0, n, bb.out, dq, dW)) {
+            free(M);
+            free_block(&bb);
+            return ORC_ENOMEM;
+        }
     }
 
     /* key side, dphi(k): state [d1][F] of queries, swept in reverse, read with [v|1] */
@@ -400,7 +430,11 @@ static int backward_head(const headp *hp, double *dq, double *dk, double *dv)
         const int n = (int)(e - b0);
         fill_block(hp, b0, n, causal, 0, causal, &bb);
         row_sweep(F, d1, n, 1, bb.phq, bb.D, bb.v1, M, bb.out, causal, 1);
-        block_hash_backward(hp, hp->k, b0, n, bb.out, dk);
+        if (block_hash_backward(hp, hp->k, b0, n, bb.out, dk, dW)) {
+            free(M);
+            free_block(&bb);
+            return ORC_ENOMEM;
+        }
     }
 
     /* key side, dv: state [d][F] of queries (value columns of D only) */
@@ -497,13 +531,16 @@ int race_oracle_forward(const double *q, const double *k, const double *v, const
 }
 
 /* Forward and backward together: the backward uses this call's own forward
- * results, never values supplied from outside. */
-int race_oracle_forward_backward(const double *q, const double *k, const double *v,
-                                 const double *g, const double *W, int L, int P, double tau,
-                                 int causal, int64_t BH, int64_t N, int d, double *o,
-                                 double *den, double *dq, double *dk, double *dv)
+ * results, never values supplied from outside.  dW (may be NULL): the
+ * gradient of the projection, [L][P][d], summed over every head and over the
+ * rows of q and of k. */
+int race_oracle_forward_backward_w(const double *q, const double *k, const double *v,
+                                   const double *g, const double *W, int L, int P, double tau,
+                                   int causal, int64_t BH, int64_t N, int d, double *o,
+                                   double *den, double *dq, double *dk, double *dv, double *dW)
 {
     if (check_args(BH, N, d, L, P, tau, 0)) return ORC_EINVAL;
+    if (dW) memset(dW, 0, sizeof(double) * (size_t)L * P * d);
     headp hp;
     memset(&hp, 0, sizeof hp);
     make_hashp(&hp.h, d, L, P, tau, 0, W);
@@ -514,8 +551,17 @@ int race_oracle_forward_backward(const double *q, const double *k, const double 
         int err = forward_head(&hp, o + off, den + bh * N);
         if (err) return err;
         hp.o = o + off; hp.m = den + bh * N;
-        err = backward_head(&hp, dq + off, dk + off, dv + off);
+        err = backward_head(&hp, dq + off, dk + off, dv + off, dW);
         if (err) return err;
     }
     return ORC_OK;
+}
+
+int race_oracle_forward_backward(const double *q, const double *k, const double *v,
+                                 const double *g, const double *W, int L, int P, double tau,
+                                 int causal, int64_t BH, int64_t N, int d, double *o,
+                                 double *den, double *dq, double *dk, double *dv)
+{
+    return race_oracle_forward_backward_w(q, k, v, g, W, L, P, tau, causal, BH, N, d, o, den, dq,
+                                          dk, dv, NULL);
 }

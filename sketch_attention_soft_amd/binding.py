@@ -21,6 +21,7 @@ STATUS = {
 }
 EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forward",
            "race_attn_backward", "race_attn_forward_ex", "race_attn_backward_ex",
+           "race_attn_backward_dw",
            "race_attn_squash_coeffs", "race_attn_squash_deriv_coeffs",
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
            "race_attn_decode", "race_attn_state_readout", "race_attn_status_string")
@@ -89,6 +90,9 @@ def lib():
         L.race_attn_forward_ex.restype = i32
         L.race_attn_backward_ex.argtypes = L.race_attn_backward.argtypes + [vp, tp]
         L.race_attn_backward_ex.restype = i32
+        L.race_attn_backward_dw.argtypes = (L.race_attn_backward.argtypes[:20] + [vp]
+                                            + L.race_attn_backward.argtypes[20:] + [vp, tp])
+        L.race_attn_backward_dw.restype = i32
         L.race_attn_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_state_bytes.restype = i32
         L.race_attn_state_add_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32,
@@ -200,8 +204,9 @@ def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None
 
 
 def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, workspace=None,
-             out=None, trace: Trace | None = None, saved=None):
-    """RACE attention backward; returns (dq, dk, dv).  out = (dq, dk, dv) reuses buffers;
+             out=None, trace: Trace | None = None, saved=None, dw: bool = False):
+    """RACE attention backward; returns (dq, dk, dv), and dW last with dw=True
+    (race_attn_backward_dw: bf16, L <= 32).  out = (dq, dk, dv) reuses buffers;
     saved: the buffer the forward of the same inputs filled, or None."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v, o, do)
@@ -212,9 +217,17 @@ def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, w
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     else:
         dq, dk, dv = out
-    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, True)
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, 2 if dw else 1)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if dw:
+        gW = torch.empty_like(W)
+        _check(lib().race_attn_backward_dw(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), o.data_ptr(), den.data_ptr(),
+            do.data_ptr(), L, P, float(tau), int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), gW.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), _stream(), _ptr(saved), _tp(trace)))
+        return dq, dk, dv, gW
     _check(lib().race_attn_backward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
                                        o.data_ptr(), den.data_ptr(), do.data_ptr(), L, P,
                                        float(tau), int(causal), B, H, N, d, dtype_code(q.dtype),
@@ -225,7 +238,8 @@ def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, w
 
 
 class RaceAttention(torch.autograd.Function):
-    """Autograd wrapper: o = race_attention(q, k, v); W is a fixed projection."""
+    """Autograd wrapper: o = race_attention(q, k, v, W).  W gets a gradient when
+    it requires one (learned hyperplanes; bf16 inputs with L <= 32)."""
 
     @staticmethod
     def forward(ctx, q, k, v, W, tau, causal, chunk=0):
@@ -240,14 +254,35 @@ class RaceAttention(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, W, o, den = ctx.saved_tensors
         tau, causal, chunk = ctx.cfg
-        dq, dk, dv = backward(q, k, v, W, o, den, do.contiguous(), tau, causal, chunk,
-                              saved=ctx.key_state)
+        grads = backward(q, k, v, W, o, den, do.contiguous(), tau, causal, chunk,
+                         saved=ctx.key_state, dw=ctx.needs_input_grad[3])
         ctx.key_state = None
-        return dq, dk, dv, None, None, None, None
+        dW = grads[3] if ctx.needs_input_grad[3] else None
+        return grads[0], grads[1], grads[2], dW, None, None, None
 
 
 def race_attention(q, k, v, W, tau: float = 1.0, causal: bool = True, chunk: int = 0):
     return RaceAttention.apply(q, k, v, W, tau, causal, chunk)
+
+
+class RaceAttentionLayer(torch.nn.Module):
+    """Drop-in attention core on [B, H, N, d] tensors: o = race_attention(q, k, v, W)
+    with W [L, P, d] drawn from N(0, 1) (the pages' random hyperplanes), kept as a
+    buffer, or as a parameter with learn_projection=True (bf16, L <= 32)."""
+
+    def __init__(self, d: int = 64, L: int = 32, P: int = 4, tau: float = 1.0,
+                 causal: bool = True, chunk: int = 0, learn_projection: bool = False,
+                 generator: torch.Generator | None = None):
+        super().__init__()
+        W = torch.randn((L, P, d), generator=generator, dtype=torch.float32)
+        if learn_projection:
+            self.W = torch.nn.Parameter(W)
+        else:
+            self.register_buffer("W", W)
+        self.tau, self.causal, self.chunk = tau, causal, chunk
+
+    def forward(self, q, k, v):
+        return RaceAttention.apply(q, k, v, self.W.contiguous(), self.tau, self.causal, self.chunk)
 
 
 # ---------------------------------------------------------------------------

@@ -67,6 +67,7 @@ struct Plan {
     size_t f_tq, f_tk, f_st, f_hc, f_scan, f_total;
     // backward layout (hc: t, dt/du' of K then of Q)
     size_t b_tq, b_tk, b_s, b_gt, b_g, b_wt, b_hc, b_scan, b_total;
+    size_t b_dw, dw_total;  // backward with dW (bf16, L <= 32): partials after b_total
     // saved buffer (bf16 path): key state, then t, dt/du' of K and of Q
     size_t s_hc, s_total;
 };
@@ -133,6 +134,11 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->b_hc = p->b_wt + p->wt_bytes;
     p->b_scan = p->b_hc + 4 * p->hc_bytes;
     p->b_total = p->b_scan + p->scan_bytes;
+    // backward with dW: one [hyperplane rows][d] fp32 block per workgroup of dQ and of dK
+    p->b_dw = p->b_total;
+    p->dw_total = p->fused ? p->b_dw + align256((size_t)2 * p->BH * p->nseg * (2 * p->nw * 16) *
+                                                race::HD * sizeof(float))
+                           : 0;
     return RACE_OK;
 }
 
@@ -334,11 +340,16 @@ template <int NW, bool CAUSAL, bool REVERSE, typename T>
 void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
                  const race::ValSrc<T> &vr, const race::ValSrc<T> &vw, const float *W,
                  const Plan &p, const float *st, const race::HCache &rc, const race::HCache &wc,
-                 T *dX)
+                 T *dX, float *dwp)
 {
-    if constexpr (sizeof(T) == 2)
-        LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE>), grid, dim3(NW * 64), Xr, vr, vw,
-               W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX);
+    if constexpr (sizeof(T) == 2) {
+        if (dwp)
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true>), grid, dim3(NW * 64), Xr,
+                   vr, vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp);
+        else
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE>), grid, dim3(NW * 64), Xr, vr,
+                   vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr);
+    }
 }
 
 template <typename T, int NW>
@@ -399,7 +410,7 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
 template <typename T, int NW, int CAUSAL>
 void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                           const T *O, const float *den, const T *dO, float tau, T *dQ, T *dK,
-                          T *dV, char *ws, const float *saved, const Tracer &tr)
+                          T *dV, char *ws, const float *saved, const Tracer &tr, float *dW)
 {
     float *tq = reinterpret_cast<float *>(ws + p.b_tq);
     float *tk = reinterpret_cast<float *>(ws + p.b_tk);
@@ -439,8 +450,15 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
             launch_sum<WS, true, 0, 3>(tr, "sum_qd", nblk, sq, Q, vd, W, p, none, hq, sG);
         }
         launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
-        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, Q, vd, vv, W, p, sK, hq, hk, dQ);
-        launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, K, vv, vd, W, p, sG, hk, hq, dK);
+        // dW (when asked): partial sums of the dQ and dK workgroups, then their sum
+        float *dwp = dW ? reinterpret_cast<float *>(ws + p.b_dw) : nullptr;
+        const int64_t dwb = p.BH * p.nseg * (int64_t)(WD * 16 * race::HD);
+        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, Q, vd, vv, W, p, sK, hq, hk, dQ, dwp);
+        launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, K, vv, vd, W, p, sG, hk, hq, dK,
+                                           dwp ? dwp + dwb : nullptr);
+        if (dW)
+            LAUNCH(tr, "dw_reduce", race::dw_reduce_kernel, dim3((p.LP * race::HD + 31) / 32),
+                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, dW);
         launch_walk<WW, CAUSAL != 0, true, 1, 0>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV,
                                                  nullptr);
         return;
@@ -480,12 +498,12 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
 template <typename T, int NW>
 void launch_backward(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                      const T *O, const float *den, const T *dO, float tau, int causal, T *dQ,
-                     T *dK, T *dV, char *ws, const float *saved, const Tracer &tr)
+                     T *dK, T *dV, char *ws, const float *saved, const Tracer &tr, float *dW)
 {
     if (causal)
-        launch_backward_body<T, NW, 1>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr);
+        launch_backward_body<T, NW, 1>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
     else
-        launch_backward_body<T, NW, 0>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr);
+        launch_backward_body<T, NW, 0>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
 }
 
 template <typename T>
@@ -511,7 +529,7 @@ template <typename T>
 void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *V,
                        const float *W, const void *O, const float *den, const void *dO,
                        float tau, int causal, void *dQ, void *dK, void *dV, char *ws,
-                       const float *saved, const Tracer &tr)
+                       const float *saved, const Tracer &tr, float *dW)
 {
     auto q = static_cast<const T *>(Q);
     auto k = static_cast<const T *>(K);
@@ -522,12 +540,12 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     auto dk = static_cast<T *>(dK);
     auto dv = static_cast<T *>(dV);
     switch (p.nw) {
-    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr); break;
-    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr); break;
-    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr); break;
+    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
     default:
         if constexpr (sizeof(T) == 2)
-            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr);
+            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW);
         break;
     }
 }
@@ -606,7 +624,8 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     Plan p;
     const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
-    *bytes = for_backward ? p.b_total : p.f_total;
+    if (for_backward == 2 && !p.fused) return RACE_ERR_UNSUPPORTED;
+    *bytes = for_backward == 2 ? p.dw_total : for_backward ? p.b_total : p.f_total;
     return RACE_OK;
 }
 
@@ -677,9 +696,35 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
-        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr);
+        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
     else
-        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr);
+        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
+                                    const float *W, const void *O, const float *den,
+                                    const void *dO, int L, int P, float tau, int causal, int B,
+                                    int H, int64_t N, int d, race_dtype_t dt, int chunk, void *dQ,
+                                    void *dK, void *dV, float *dW, void *workspace,
+                                    size_t ws_bytes, void *stream, const void *saved,
+                                    race_trace_t *trace)
+{
+    if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !dW || !workspace)
+        return RACE_ERR_NULL;
+    Plan p;
+    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    if (st != RACE_OK) return st;
+    if (!p.fused) return RACE_ERR_UNSUPPORTED;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if ((st = check_ws(p, p.dw_total, workspace, ws_bytes)) != RACE_OK) return st;
+    if ((st = check_trace(trace)) != RACE_OK) return st;
+    if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
+    const Tracer tr{trace, static_cast<hipStream_t>(stream)};
+    (void)hipGetLastError();
+    dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV,
+                            static_cast<char *>(workspace), static_cast<const float *>(saved), tr,
+                            dW);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 

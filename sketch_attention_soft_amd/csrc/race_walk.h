@@ -530,6 +530,17 @@ __device__ __forceinline__ void feat_major(const bf16x8 (&ptm)[2][2], const bf16
     }
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte reads of lanes 4j + i / 4,
+// j = 0..3 (four consecutive 16-bit values read by four lanes become one
+// lane's four values).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr16(const bf16 *p)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p)));
+}
+
 // value-column operand over the chunk's tokens (same K-slot order as feat_major)
 __device__ __forceinline__ bf16x8 ycol_frag(const bf16 *yc, int col)
 {
@@ -1008,11 +1019,17 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 // with E[i][j] = y_r(i) . y_w(j) (masked), computed transposed (rows f) so
 // that a lane holds all 16 features of its table; S += psi_w^T y_w; then the
 // Walsh gradient, du = dt dt/du', dxh = du W and the normalisation backward.
-template <int NW, bool CAUSAL, bool REVERSE>
+// DW: also the gradient of the projection, dW = sum over the reader rows of
+// du x_hat^T: per chunk and wave, [16 hyperplanes x 32 tokens] x [32 tokens x
+// 64 dims] on MFMA (both operands read transposed from du and the staged
+// rows), summed in LDS, and the workgroup's sum written to dwp[workgroup]
+// ([NW * 16][64] fp32) for a reduction over segments.
+template <int NW, bool CAUSAL, bool REVERSE, bool DW = false>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const bf16 *__restrict__ Xr, ValSrc<bf16> vr_src, ValSrc<bf16> vw_src,
     const float *__restrict__ W, int L, int64_t N, int seg, int64_t nseg,
-    const float *__restrict__ st, HCache rc, HCache wc, bf16 *__restrict__ dX)
+    const float *__restrict__ st, HCache rc, HCache wc, bf16 *__restrict__ dX,
+    float *__restrict__ dwp)
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
     constexpr int NTHR = NW * 64;
@@ -1029,6 +1046,9 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     __shared__ __attribute__((aligned(16))) bf16 du_l[2][WCT * DUS];
     __shared__ __attribute__((aligned(16))) float dotp[2][WCT * 16];  // partial x . dxh [token][nt][g]
     __shared__ __attribute__((aligned(16))) bf16 wt_l[HD * WTS];     // W^T (bf16): [dim][hyperplane]
+    // this block's dW as [hyperplane / 4][column][hyperplane % 4]: a lane's
+    // four accumulator values are one 16-byte word (each wave owns its rows)
+    __shared__ __attribute__((aligned(16))) float dwl[DW ? NW * 16 * HD : 4];
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
@@ -1063,6 +1083,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         const int hp = e / HD, c = e % HD;
         wt_l[c * WTS + hp] = (bf16)(hp < L * NP ? W[hp * HD + c] : 0.f);
     }
+    if constexpr (DW)
+        for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) dwl[e] = 0.f;
     stage_sel(sl);
     const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
     floatx4 acc[4][NT];  // CxF state
@@ -1122,6 +1144,29 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             dxh[i] = xa;
             xkeep[i] = xv;
             sskeep[i] = kbuf[pb][tok];
+        }
+    };
+    // dW of chunk ci's rows (du in buffer pb, rows in xbuf[pb]): A = du^T
+    // scaled per token by 1 / max(|x|, 1e-12) (x_hat = x / that), K-slot
+    // (g, j) <-> token 8g + j for both operands
+    auto dw_tiles = [&](int pb) {
+        const int tq = c16 & 3, tj = c16 >> 2;
+        const bf16 *da = du_l[pb] + (8 * g + tj) * DUS + w * 16 + 4 * tq;
+        bf16x8 a = cat8(lds_tr16(da), lds_tr16(da + 4 * DUS));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float ss = kbuf[pb][8 * g + j];
+            a[j] = (bf16)((float)a[j] * __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f)));
+        }
+        const bf16 *xa = xbuf[pb] + (8 * g + tj) * XRS + 4 * tq;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const bf16x8 bx = cat8(lds_tr16(xa + 16 * nt), lds_tr16(xa + 16 * nt + 4 * XRS));
+            // rows 4g + r of this wave's 16, column 16 nt + c16
+            floatx4 *acc4 = reinterpret_cast<floatx4 *>(dwl + ((w * 4 + g) * HD + 16 * nt + c16) * 4);
+            floatx4 v = *acc4;
+            mma32(v, a, bx);
+            *acc4 = v;
         }
     };
     // the normalisation backward of chunk ci from the registers above and the
@@ -1264,14 +1309,52 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
         }
         dxh_tiles(b ^ 1);  // (before the first chunk: unused values)
+        if constexpr (DW) {
+            if (ci >= 1) dw_tiles(b ^ 1);
+        }
     }
     if (nch > 0) {
         const int pl = (nch - 1) & 1;  // buffers of the last chunk
         lds_barrier();
         if (nch >= 2) finish(nch - 2, pl ^ 1);
         dxh_tiles(pl);
+        if constexpr (DW) dw_tiles(pl);
         lds_barrier();
         finish(nch - 1, pl);
+    }
+    if constexpr (DW) {
+        __syncthreads();
+        float *dst = dwp + blockIdx.x * (int64_t)(NW * 16 * HD);
+        for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
+            const int hp = e / HD, col = e % HD;
+            dst[e] = dwl[((hp >> 2) * HD + col) * 4 + (hp & 3)];
+        }
+    }
+}
+
+// dW[hp][c] = sum over the nparts partial blocks [rows][HD] for hp < LP; rows
+// >= LP of the blocks (padding hyperplanes) are zero.  A workgroup takes 32
+// consecutive entries; its 8 thread groups sum every 8th block (in order),
+// then the 8 group sums are added in group order (a fixed order, whatever the
+// launch).
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int64_t nparts,
+                                                        int rows, int LP, float *__restrict__ dW)
+{
+    __shared__ float gs[8][32];
+    const int grp = threadIdx.x >> 5, j = threadIdx.x & 31;
+    const int e = blockIdx.x * 32 + j;
+    float acc = 0.f;
+    if (e < LP * HD) {
+        const float *p = part + e;
+        for (int64_t b = grp; b < nparts; b += 8) acc += p[b * (int64_t)rows * HD];
+    }
+    gs[grp][j] = acc;
+    __syncthreads();
+    if (grp == 0 && e < LP * HD) {
+        float t = gs[0][j];
+#pragma unroll
+        for (int g2 = 1; g2 < 8; ++g2) t += gs[g2][j];
+        dW[e] = t;
     }
 }
 

@@ -307,3 +307,29 @@ def test_stream_validation(lib):
     assert L.race_attn_state_readout(F, F, 8, 5, 1.0, 1, 1, 4, 64, BF16, F, F, F, None) == E_UNSUP
     assert L.race_attn_state_readout(None, F, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, None, None, None) == OK
     assert L.race_attn_state_readout(F, F, 8, 4, 1.0, 1, 1, 2, 64, BF16, None, F, F, None) == E_NULL
+
+
+def test_backward_dw_validation(lib):
+    i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    fn = lib.race_attn_backward_dw
+    fn.argtypes = [vp] * 7 + [i32, i32, f32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, vp,
+                              vp, sz, vp, vp, vp]
+    F = FAKE
+    # the workspace with dW is larger than the plain backward's, bf16 with L <= 32 only
+    st1, b1 = ws_bytes(lib, L=32, bwd=1)
+    st2, b2 = ws_bytes(lib, L=32, bwd=2)
+    assert st1 == OK and st2 == OK and b2 > b1
+    assert ws_bytes(lib, L=32, dt=F32, bwd=2)[0] == E_UNSUP
+    assert ws_bytes(lib, L=64, bwd=2)[0] == E_UNSUP
+    args = [F] * 7 + [32, 4, 1.0, 1, 1, 1, 1024, 64, BF16, 0, F, F, F, F, F * 16, 1 << 40, None,
+                      None, None]
+    bad = list(args)
+    bad[20] = None  # dW
+    assert fn(*bad) == E_NULL
+    bad = list(args)
+    bad[15] = F32
+    assert fn(*bad) == E_UNSUP
+    bad = list(args)
+    bad[22] = 16  # workspace too small
+    assert fn(*bad) == E_WS

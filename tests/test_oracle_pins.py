@@ -382,3 +382,39 @@ def test_p13_walsh_readout_is_the_non_causal_forward():
     o, den = oracle.forward(qq, k, v, W, tau, False)
     np.testing.assert_allclose(nm[:, d], den[:M], rtol=1e-11)
     np.testing.assert_allclose(nm[:, :d] / nm[:, d:], o[:M], rtol=1e-10, atol=1e-12)
+
+
+# -- P-14: the projection gradient dW against finite differences of the
+# oracle's forward and of the independent closed form (tests/quadratic_ref.py)
+@pytest.mark.parametrize("P,tau,causal", [(4, 1.0, True), (3, 0.6, False), (2, 1.3, True)])
+def test_p14_dw_finite_differences(P, tau, causal):
+    rng = np.random.default_rng(80 + P)
+    B, H, N, d, L = 1, 2, 9, 5, 2
+    q = rng.standard_normal((B, H, N, d)) * 1.4
+    k = rng.standard_normal((B, H, N, d)) * 0.7
+    v, g = rng.standard_normal((B, H, N, d)), rng.standard_normal((B, H, N, d))
+    W = rng.standard_normal((L, P, d))
+    out = oracle.forward_backward(q, k, v, g, W, tau, causal, with_dw=True)
+    dW = out[5]
+    assert dW.shape == (L, P, d)
+    # the other gradients are unchanged by asking for dW
+    for a, b in zip(out[:5], oracle.forward_backward(q, k, v, g, W, tau, causal)):
+        assert np.array_equal(a, b)
+    h = 1e-6
+
+    def loss(WW, closed=False):
+        if closed:
+            o = np.stack([np.stack([qr.soft_race_attention(q[0, i], k[0, i], v[0, i], WW, tau,
+                                                           causal)[0] for i in range(H)])])
+        else:
+            o = oracle.forward(q, k, v, WW, tau, causal)[0]
+        return float((g * o).sum())
+
+    for closed in (False, True):
+        num = np.zeros_like(W)
+        for idx in np.ndindex(W.shape):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[idx] += h
+            Wm[idx] -= h
+            num[idx] = (loss(Wp, closed) - loss(Wm, closed)) / (2 * h)
+        assert _relf(dW, num) < 1e-6, (closed, _relf(dW, num))
