@@ -113,6 +113,8 @@ def main() -> int:
     ap.add_argument("--dw", action="store_true",
                     help="the backward also returns the projection gradient dW "
                          "(race_attn_backward_dw, learned hyperplanes)")
+    ap.add_argument("--hard", action="store_true",
+                    help="time the hard-hash forward (race_attn_forward_hard) on the workload")
     ap.add_argument("--stream", action="store_true",
                     help="time the streaming state entry points instead (decode of one token "
                          "per head over 64 heads, bulk state_add of the 4M-token head)")
@@ -140,6 +142,8 @@ def main() -> int:
 
     if args.stream:
         return stream_bench(args, binding, I, np, torch)
+    if args.hard:
+        return hard_bench(args, binding, I, np, torch)
 
     w = I.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
@@ -251,6 +255,68 @@ def main() -> int:
                           "frac": round(max(t_mfma, t_hbm) / ms, 5)},
         "kernels_ms": {k2: round(v2, 4) for k2, v2 in kern.items()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def hard_bench(args, binding, I, np, torch) -> int:
+    """One JSON line for the hard-hash forward on the workload (forward only:
+    the hash has no gradient).  Its algorithmic bytes are one read of Q, K, V
+    and one write of O and den; the step runs the same chunked kernels as the
+    soft forward with t = +-1, so it is reported against HBM and MFMA both."""
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    x = I.workload_inputs(w, with_grad=False)
+
+    def put(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = put(x["q"]), put(x["k"]), put(x["v"])
+    W = torch.from_numpy(x["W"]).to(dev)
+    del x
+    B, H, N, d = q.shape
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.empty_like(q)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, False),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.forward_hard(q, k, v, W, w.causal, w.chunk, workspace=ws, out=(o, den))
+
+    for _ in range(args.warmup):
+        step()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    e = 2 if w.dtype == "bf16" else 4
+    bytes_tok = 4 * d * e + 4
+    import dataclasses
+    fwd_flops_tok = algorithmic_per_token(dataclasses.replace(w, backward=False))[0]
+    gbs = bytes_tok * w.tokens / (ms * 1e-3) / 1e9
+    tfl = fwd_flops_tok * w.tokens / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "RACE hard-hash attention forward tokens/s (true bucket counts)",
+        "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Philox N(0,1); Q, K rows L2-normalised)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "L": w.L,
+                   "P": w.P, "causal": w.causal, "passes": "fwd (hard hash)", "chunk": w.chunk},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 5), "traffic": None,
+                     "kernel": "whole forward (sum_kv, scan, fwd_o)", "bytes_per_token": bytes_tok},
+        "mfma": {"achieved": round(tfl, 3), "peak": PEAK_TFLOPS["bf16" if w.dtype == "bf16" else "f32"],
+                 "unit": "TFLOP/s", "flops_per_token": fwd_flops_tok},
     }
     print(json.dumps(line), flush=True)
     return 0

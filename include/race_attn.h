@@ -89,6 +89,18 @@ race_status_t race_attn_forward(const void *Q, const void *K, const void *V, con
                                 int d, race_dtype_t dt, int chunk, void *O, float *den,
                                 void *workspace, size_t ws_bytes, void *stream);
 
+/* Forward pass with hard hashing: each row falls in exactly one corner per
+ * table, r_l(x) = sum_p [z_lp >= 0] 2^p, and the bucket sums of steps 3-5 are
+ * true counts and value sums (the tau -> 0 limit of step 2: the original RACE
+ * sketch and YOSO-style attention the pages contrast soft hashing with, zh
+ * §2.2 and §3).  o_i = sum_l B_l[r_l(q_i)] / sum_l A_l[r_l(q_i)] over keys
+ * j <= i (causal) or all keys.  No tau; otherwise as race_attn_forward (same
+ * workspace size).  Inference only: the hash has no gradient. */
+race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
+                                     const float *W, int L, int P, int causal, int B, int H,
+                                     int64_t N, int d, race_dtype_t dt, int chunk, void *O,
+                                     float *den, void *workspace, size_t ws_bytes, void *stream);
+
 /* Backward pass: the exact gradient of the forward (the pages state the
  * method is differentiable end to end, es §2 item 3, fr §3 item 3).  Given
  * Q, K, V, W, the forward's O and den, and dO = dLoss/dO, writes dQ, dK, dV

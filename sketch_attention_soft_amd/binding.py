@@ -21,7 +21,7 @@ STATUS = {
 }
 EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forward",
            "race_attn_backward", "race_attn_forward_ex", "race_attn_backward_ex",
-           "race_attn_backward_dw",
+           "race_attn_backward_dw", "race_attn_forward_hard",
            "race_attn_squash_coeffs", "race_attn_squash_deriv_coeffs",
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
            "race_attn_decode", "race_attn_state_readout", "race_attn_status_string")
@@ -82,6 +82,9 @@ def lib():
         L.race_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32, i32, i32,
                                          i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.race_attn_backward.restype = i32
+        L.race_attn_forward_hard.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32,
+                                             i32, i32, vp, vp, vp, sz, vp]
+        L.race_attn_forward_hard.restype = i32
         L.race_attn_saved_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32,
                                             ctypes.POINTER(sz)]
         L.race_attn_saved_bytes.restype = i32
@@ -200,6 +203,26 @@ def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None
                                       dtype_code(q.dtype), chunk, o.data_ptr(), den.data_ptr(),
                                       workspace.data_ptr(), workspace.numel(), _stream(),
                                       _ptr(saved), _tp(trace)))
+    return o, den
+
+
+def forward_hard(q, k, v, W, causal: bool, chunk: int = 0, workspace=None, out=None):
+    """Hard-hash forward (one bucket per table and row, true counts): (o, den)."""
+    B, H, N, d = _shape(q)
+    _check_tensors(q, k, v)
+    L, P = _check_w(W, q)
+    if out is None:
+        o = torch.empty_like(q)
+        den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, den = out
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().race_attn_forward_hard(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L,
+                                        P, int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
+                                        o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel(), _stream()))
     return o, den
 
 

@@ -251,6 +251,19 @@ race::Squash fit_squash(float tau, race_dtype_t dt)
     return sq;
 }
 
+// Hard hashing (the tau -> 0 limit, t = sign(u), +1 at 0) in the polynomial
+// form the bf16 kernels evaluate: |t| = 1 (the constant polynomial) with the
+// sign of u, and dt/du' = 0.
+race::Squash hard_squash()
+{
+    race::Squash sq;
+    std::memset(&sq, 0, sizeof sq);
+    sq.inv_tau = 0.f;
+    sq.deg = race::DEG16;
+    sq.t16[0] = f16_bits(1.0) * 0x10001u;
+    return sq;
+}
+
 // value of an fp16 pair's low half
 double f16_value(uint32_t bits)
 {
@@ -361,12 +374,14 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     // key state: into the caller's saved buffer when given (bf16 path)
     float *st = saved ? saved : reinterpret_cast<float *>(ws + p.f_st);
     float *scan_tmp = reinterpret_cast<float *>(ws + p.f_scan);
-    const float inv_tau = 1.0f / tau;
+    // tau = 0 (race_attn_forward_hard only): hard hashing
+    const bool hard = tau == 0.f;
+    const float inv_tau = hard ? 0.f : 1.0f / tau;
     const dim3 hg(hash_grid(p.rows)), b256(256), bw(NW * 64);
     if constexpr (sizeof(T) == 2 && NW <= 4) {
         // bf16 path: 2 NW waves of 4 tables each (16 hyperplanes, 64 features)
         constexpr int WS = 2 * NW, WW = 2 * NW;
-        const race::Squash sq = fit_squash(tau, RACE_BF16);
+        const race::Squash sq = hard ? hard_squash() : fit_squash(tau, RACE_BF16);
         const dim3 nblk((unsigned)(p.BH * p.nseg));
         const race::ValSrc<T> vv{V, nullptr, nullptr};
         // hash features: K (t) in the workspace, or K and Q (t, dt/du') in the saved buffer
@@ -663,6 +678,26 @@ race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, 
         dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else
         dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
+                                     const float *W, int L, int P, int causal, int B, int H,
+                                     int64_t N, int d, race_dtype_t dt, int chunk, void *O,
+                                     float *den, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
+    Plan p;
+    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    if (st != RACE_OK) return st;
+    if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
+    const Tracer tr{nullptr, static_cast<hipStream_t>(stream)};
+    (void)hipGetLastError();
+    char *ws = static_cast<char *>(workspace);
+    if (dt == RACE_BF16)
+        dispatch_forward<bf16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+    else
+        dispatch_forward<float>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 

@@ -50,6 +50,7 @@ template <typename T> struct ValSrc {
 
 // ---------------------------------------------------------------------------
 // hash_kernel: per row x of X and table l, t[p] = tanh(tanh(u_p / |x|) / tau)
+// (inv_tau = 0: hard hashing, t[p] = +1 if u_p >= 0 else -1, the tau -> 0 limit)
 // with u = W x (raw row; |x| clamped at 1e-12).  U^T = W X^T on MFMA
 // (M = hyperplanes, N = 16 rows, K = d); bf16 inputs use W = W_hi + W_lo.
 // CHAIN also stores dt/du = ((1 - t^2)/tau) (1 - z^2), z = tanh(u / |x|),
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(256) void hash_kernel(const T *__restrict__ X, int6
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float z = tanhf(acc[r] * inv_norm);
-                    t[r] = tanhf(z * inv_tau);
+                    // inv_tau = 0: hard hashing, the tau -> 0 limit t = sign(z) (+1 at 0)
+                    t[r] = inv_tau == 0.f ? (acc[r] >= 0.f ? 1.f : -1.f) : tanhf(z * inv_tau);
                     sd[r] = (1.f - t[r] * t[r]) * inv_tau * (1.f - z * z);
                 }
                 float *dst = tout + (row * L + l) * TS;

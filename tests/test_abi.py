@@ -333,3 +333,14 @@ def test_backward_dw_validation(lib):
     bad = list(args)
     bad[22] = 16  # workspace too small
     assert fn(*bad) == E_WS
+
+
+def test_forward_hard_validation(lib):
+    i32, i64, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    fn = lib.race_attn_forward_hard
+    fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, sz, vp]
+    F = FAKE
+    assert fn(None, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_NULL
+    assert fn(F, F, F, F, 8, 3, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
+    assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 17, F, F, F, 1 << 30, None) == E_CHUNK
+    assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F * 16, 16, None) == E_WS
