@@ -21,7 +21,10 @@
  *
  * Conventions shared by every entry point
  *   - Q, K, V, O, dO, dQ, dK, dV: device pointers to contiguous [B][H][N][d]
- *     tensors of type `dt` (RACE_F32: float, RACE_BF16: bfloat16 bits).
+ *     tensors of type `dt` (RACE_F32: float, RACE_BF16: bfloat16 bits,
+ *     RACE_F16: IEEE half bits).  RACE_F16 rows are read exactly, staged
+ *     and multiplied as bf16 like RACE_BF16 rows (the matrix-core operands
+ *     of both are bf16, with fp32 sums) and the outputs are rounded to fp16.
  *   - W: device pointer, contiguous fp32 [L][P][d], shared by every (b, h).
  *   - den: device pointer, fp32 [B][H][N]: the readout denominator
  *     m_i = sum_l phi_l(q_i)^T A_l of every row, written by the forward and
@@ -33,7 +36,8 @@
  *     after enqueueing, without synchronising.  The library never allocates,
  *     frees or synchronises, keeps no global mutable state and is safe to
  *     call from several threads.
- *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32),
+ *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32 and
+ *     RACE_F16),
  *     any B, H, N >= 1 (int64 offsets), tau finite and > 0.
  *   - chunk: tokens per scan segment, 0 = the library chooses; otherwise a
  *     multiple of 16.  It changes only the order of the floating-point sums.
@@ -70,7 +74,7 @@ typedef enum {
     RACE_ERR_HIP = 7
 } race_status_t;
 
-typedef enum { RACE_F32 = 0, RACE_BF16 = 1 } race_dtype_t;
+typedef enum { RACE_F32 = 0, RACE_BF16 = 1, RACE_F16 = 2 } race_dtype_t;
 
 /* Workspace size, in bytes, that race_attn_forward (for_backward = 0),
  * race_attn_backward (for_backward = 1) or race_attn_backward_dw
@@ -95,7 +99,10 @@ race_status_t race_attn_forward(const void *Q, const void *K, const void *V, con
  * sketch and YOSO-style attention the pages contrast soft hashing with, zh
  * §2.2 and §3).  o_i = sum_l B_l[r_l(q_i)] / sum_l A_l[r_l(q_i)] over keys
  * j <= i (causal) or all keys.  No tau; otherwise as race_attn_forward (same
- * workspace size).  Inference only: the hash has no gradient. */
+ * workspace size).  Inference only: the hash has no gradient.  A query that
+ * collides with no visible key gets den = 0 and a non-finite o (0 / 0).  The
+ * corner of a RACE_BF16 / RACE_F16 row is decided on its bf16 value (the
+ * matrix-core operand), with W to about 16 bits. */
 race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
                                      const float *W, int L, int P, int causal, int B, int H,
                                      int64_t N, int d, race_dtype_t dt, int chunk, void *O,
@@ -159,7 +166,8 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
                                     void *dK, void *dV, void *workspace, size_t ws_bytes,
                                     void *stream, const void *saved, race_trace_t *trace);
 
-/* Diagnostic: the polynomials the bf16 kernels use for the squash
+/* Diagnostic: the polynomials the bf16 kernels (RACE_BF16 and RACE_F16 rows)
+ * use for the squash
  * t = tanh(tanh(v) / tau) and its derivative dt/dv (steps 1-2; zh §2.2).
  * With e = exp(-2|v|) and y = 2e - 1, the kernels evaluate
  *   t = sign(v) |sum_k coef[k] y^k|      (race_attn_squash_coeffs)
@@ -175,14 +183,13 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
 race_status_t race_attn_squash_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
 race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *coef, int *deg);
 
-/* Static, NUL-terminated description of a status code. */
 /* race_attn_backward_ex that also returns the gradient of the projection,
  * for learned hyperplanes: dW = sum over the rows x of Q and K (every batch
  * and head) of dLoss/du (x / max(|x|, 1e-12))^T, u = W x_hat (step 1), into
  * dW (device, fp32 [L][P][d], overwritten).  dQ, dK and dV are the same as
  * race_attn_backward_ex's.  The per-workgroup sums are added in a fixed order,
- * so the result does not depend on the launch.  Supported for RACE_BF16 with
- * L <= 32 (RACE_ERR_UNSUPPORTED otherwise); workspace: race_attn_workspace_bytes
+ * so the result does not depend on the launch.  Supported for RACE_BF16 and
+ * RACE_F16 with L <= 32 (RACE_ERR_UNSUPPORTED otherwise); workspace: race_attn_workspace_bytes
  * with for_backward = 2. */
 race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
                                     const float *W, const void *O, const float *den,
@@ -248,6 +255,7 @@ race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int 
                                       int B, int H, int64_t T, int d, race_dtype_t dt,
                                       const float *state, void *O, float *den, void *stream);
 
+/* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);
 
 #ifdef __cplusplus

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librace_attn.so")
 
-RACE_F32, RACE_BF16 = 0, 1
+RACE_F32, RACE_BF16, RACE_F16 = 0, 1, 2
 STATUS = {
     0: "RACE_OK", 1: "RACE_ERR_NULL", 2: "RACE_ERR_SHAPE", 3: "RACE_ERR_UNSUPPORTED",
     4: "RACE_ERR_TAU", 5: "RACE_ERR_CHUNK", 6: "RACE_ERR_WORKSPACE", 7: "RACE_ERR_HIP",
@@ -126,6 +126,8 @@ def dtype_code(dtype: torch.dtype) -> int:
         return RACE_F32
     if dtype == torch.bfloat16:
         return RACE_BF16
+    if dtype == torch.float16:
+        return RACE_F16
     raise TypeError(f"unsupported dtype {dtype}")
 
 

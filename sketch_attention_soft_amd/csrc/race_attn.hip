@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "race_bwd.h"
 #include "race_common.h"
@@ -77,9 +78,9 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
 {
     if (B < 1 || H < 1 || N < 1 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
-    if (dt != RACE_F32 && dt != RACE_BF16) return RACE_ERR_UNSUPPORTED;
+    if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     if (d != race::HD || P != race::NP) return RACE_ERR_UNSUPPORTED;
-    if (L > 64 || (dt == RACE_F32 && L > 32)) return RACE_ERR_UNSUPPORTED;
+    if (L > 64 || (dt != RACE_BF16 && L > 32)) return RACE_ERR_UNSUPPORTED;
     if (chunk < 0 || chunk % race::CH != 0) return RACE_ERR_CHUNK;
     p->BH = (int64_t)B * H;
     p->N = N;
@@ -102,7 +103,7 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->seg = seg;
     p->nseg = (N + seg - 1) / seg;
     if (p->BH * p->nseg > 0x7fffffffLL) return RACE_ERR_SHAPE;
-    p->fused = dt == RACE_BF16 && L <= 32;
+    p->fused = (dt == RACE_BF16 || dt == RACE_F16) && L <= 32;
     p->st_bytes = align256((size_t)p->BH * (p->nseg + 1) * p->F * race::NCOL * sizeof(float));
     // the fused kernels keep hash features on chip: no per-row buffers
     p->t_bytes = p->fused ? 0 : align256((size_t)p->rows * L * race::NP * sizeof(float));
@@ -325,10 +326,10 @@ void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squas
 {
     if constexpr (sizeof(T) == 2) {
         if (SRC == 1 || sq.deg >= 0)
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true>), grid, dim3(NW * 64), X, vs,
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T>), grid, dim3(NW * 64), X, vs,
                    W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
         else
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false>), grid, dim3(NW * 64), X, vs,
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T>), grid, dim3(NW * 64), X, vs,
                    W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
     }
 }
@@ -341,10 +342,10 @@ void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squa
 {
     if constexpr (sizeof(T) == 2) {
         if (RSRC == 1 || sq.deg >= 0)
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true>), grid,
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T>), grid,
                    dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
         else
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false>), grid,
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T>), grid,
                    dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
     }
 }
@@ -357,10 +358,10 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
 {
     if constexpr (sizeof(T) == 2) {
         if (dwp)
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true>), grid, dim3(NW * 64), Xr,
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T>), grid, dim3(NW * 64), Xr,
                    vr, vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp);
         else
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE>), grid, dim3(NW * 64), Xr, vr,
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T>), grid, dim3(NW * 64), Xr, vr,
                    vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr);
     }
 }
@@ -407,6 +408,7 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
         }
         return;
     }
+    if constexpr (!std::is_same<T, _Float16>::value) {  // fp16 rows: the fused path only
     LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
     LAUNCH(tr, "hash_k", (race::hash_kernel<T, false>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
     const race::ValSrc<T> vs{V, nullptr, nullptr};
@@ -420,6 +422,7 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     else
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, false, false>), nblk, bw, tq, tk,
                race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
+    }
 }
 
 template <typename T, int NW, int CAUSAL>
@@ -478,6 +481,7 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
                                                  nullptr);
         return;
     }
+    if constexpr (!std::is_same<T, _Float16>::value) {  // fp16 rows: the fused path only
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,
            p.LP, lp32, wt);
     LAUNCH(tr, "hash_q_chain", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L,
@@ -508,6 +512,7 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     // dV: keys read the FxC gradient state, reverse order
     LAUNCH(tr, "readout_dv", (race::readout_kernel<T, NW, CAUSAL != 0, true>), nblk, bw, tk, tq,
            ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr);
+    }
 }
 
 template <typename T, int NW>
@@ -535,7 +540,8 @@ void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V
     case 2: launch_forward<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
     case 4: launch_forward<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
     default:
-        if constexpr (sizeof(T) == 2) launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr);
+        if constexpr (std::is_same<T, bf16>::value)
+            launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr);
         break;
     }
 }
@@ -559,7 +565,7 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
     case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
     default:
-        if constexpr (sizeof(T) == 2)
+        if constexpr (std::is_same<T, bf16>::value)
             launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW);
         break;
     }
@@ -588,7 +594,7 @@ race_status_t stream_plan(int B, int H, int64_t N, int d, int L, int P, race_dty
 {
     if (B < 1 || H < 1 || N < 0 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
     if (d != race::HD || P != race::NP || L > 64) return RACE_ERR_UNSUPPORTED;
-    if (dt != RACE_F32 && dt != RACE_BF16) return RACE_ERR_UNSUPPORTED;
+    if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH > 65535) return RACE_ERR_UNSUPPORTED;  // heads go to the second grid dimension
     if (N > ((int64_t)1 << 62) / (BH * race::HD)) return RACE_ERR_SHAPE;
@@ -676,6 +682,8 @@ race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, 
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
         dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
+    else if (dt == RACE_F16)
+        dispatch_forward<_Float16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else
         dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
@@ -696,6 +704,8 @@ race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
         dispatch_forward<bf16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+    else if (dt == RACE_F16)
+        dispatch_forward<_Float16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
     else
         dispatch_forward<float>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
@@ -732,6 +742,8 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
     char *ws = static_cast<char *>(workspace);
     if (dt == RACE_BF16)
         dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
+    else if (dt == RACE_F16)
+        dispatch_backward<_Float16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
     else
         dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
@@ -757,9 +769,12 @@ race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
     if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
-    dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV,
-                            static_cast<char *>(workspace), static_cast<const float *>(saved), tr,
-                            dW);
+    char *ws = static_cast<char *>(workspace);
+    const float *sv = static_cast<const float *>(saved);
+    if (dt == RACE_F16)
+        dispatch_backward<_Float16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
+    else
+        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 
@@ -778,8 +793,9 @@ static race_status_t squash_coeffs(float tau, race_dtype_t dt, float *coef, int 
     if (!coef || !deg) return RACE_ERR_NULL;
     race_status_t st = check_tau(tau);
     if (st != RACE_OK) return st;
-    if (dt != RACE_F32 && dt != RACE_BF16) return RACE_ERR_UNSUPPORTED;
-    const race::Squash sq = fit_squash(tau, dt);
+    if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
+    // fp16 rows take the bf16 path's squash (its operands are bf16)
+    const race::Squash sq = fit_squash(tau, dt == RACE_F16 ? RACE_BF16 : dt);
     for (int i = 0; i <= race::MAXDEG; ++i)
         coef[i] = (sq.deg >= 0 && i <= sq.deg) ? (float)f16_value(deriv ? sq.c16[i] : sq.t16[i]) : 0.f;
     *deg = sq.deg;
@@ -838,6 +854,9 @@ race_status_t race_attn_state_add(const void *K, const void *V, const float *W, 
     if (dt == RACE_BF16)
         launch_stream<bf16, race::SM_ADD>(sp, nullptr, K, V, W, tau, N, nblk, state, part, nullptr,
                                           nullptr, s);
+    else if (dt == RACE_F16)
+        launch_stream<_Float16, race::SM_ADD>(sp, nullptr, K, V, W, tau, N, nblk, state, part,
+                                              nullptr, nullptr, s);
     else
         launch_stream<float, race::SM_ADD>(sp, nullptr, K, V, W, tau, N, nblk, state, part,
                                            nullptr, nullptr, s);
@@ -861,6 +880,8 @@ race_status_t race_attn_decode(const void *Q, const void *K, const void *V, cons
     (void)hipGetLastError();
     if (dt == RACE_BF16)
         launch_stream<bf16, race::SM_DECODE>(sp, Q, K, V, W, tau, T, 1, state, nullptr, O, den, s);
+    else if (dt == RACE_F16)
+        launch_stream<_Float16, race::SM_DECODE>(sp, Q, K, V, W, tau, T, 1, state, nullptr, O, den, s);
     else
         launch_stream<float, race::SM_DECODE>(sp, Q, K, V, W, tau, T, 1, state, nullptr, O, den, s);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
@@ -884,6 +905,9 @@ race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int 
     if (dt == RACE_BF16)
         launch_stream<bf16, race::SM_READOUT>(sp, Q, nullptr, nullptr, W, tau, T, nblk, sv,
                                               nullptr, O, den, s);
+    else if (dt == RACE_F16)
+        launch_stream<_Float16, race::SM_READOUT>(sp, Q, nullptr, nullptr, W, tau, T, nblk, sv,
+                                                  nullptr, O, den, s);
     else
         launch_stream<float, race::SM_READOUT>(sp, Q, nullptr, nullptr, W, tau, T, nblk, sv,
                                                nullptr, O, den, s);

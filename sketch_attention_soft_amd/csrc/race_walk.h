@@ -61,6 +61,40 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
     const bf16x2 v = {(bf16)a, (bf16)b};
     return __builtin_bit_cast(uint32_t, v);
 }
+typedef _Float16 f16;
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Rows in global memory are bf16 or fp16 (IO); what is staged in LDS and
+// every MFMA operand is bf16.  One 32-bit word holds two row elements:
+// io_lo / io_hi give them as floats (exact), io_bf16w as bf16 bits (as they
+// are for bf16 rows, rounded to nearest even for fp16 rows), and pk_io packs
+// two floats as IO (round to nearest even).
+template <typename IO> constexpr bool is_bf16 = false;
+template <> constexpr bool is_bf16<bf16> = true;
+template <typename IO> __device__ __forceinline__ float io_lo(uint32_t w)
+{
+    if constexpr (is_bf16<IO>) return __builtin_bit_cast(float, w << 16);
+    else return (float)__builtin_bit_cast(half2v, w)[0];
+}
+template <typename IO> __device__ __forceinline__ float io_hi(uint32_t w)
+{
+    if constexpr (is_bf16<IO>) return __builtin_bit_cast(float, w & 0xffff0000u);
+    else return (float)__builtin_bit_cast(half2v, w)[1];
+}
+template <typename IO> __device__ __forceinline__ uint32_t io_bf16w(uint32_t w)
+{
+    if constexpr (is_bf16<IO>) return w;
+    else return pk_bf16(io_lo<IO>(w), io_hi<IO>(w));
+}
+template <typename IO> __device__ __forceinline__ uint32_t pk_io(float a, float b)
+{
+    if constexpr (is_bf16<IO>) {
+        return pk_bf16(a, b);
+    } else {
+        const half2v v = {(f16)a, (f16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
 __device__ __forceinline__ bf16x8 pk8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
 {
     const u32x4 v = {a, b, c, d};
@@ -162,8 +196,8 @@ __device__ __forceinline__ void for_chunks2(int n, F &&body)
         if (ci + 1 < n) body(ci + 1, Par<1>{});
     }
 }
-// rows of a [token][HD] bf16 array
-__device__ __forceinline__ Rsrc row_res(const bf16 *seg_rows, const Chunk &c)
+// rows of a [token][HD] array of 16-bit elements
+template <typename IO> __device__ __forceinline__ Rsrc row_res(const IO *seg_rows, const Chunk &c)
 {
     return make_rsrc(seg_rows + c.tok0 * HD, c.nv * HD * 2);
 }
@@ -198,7 +232,7 @@ __device__ __forceinline__ void xstage_load(Rsrc r, XStage<NTHR> &xs)
 // rows -> xb[token][XRS] (rows past the chunk's end were loaded as zeros);
 // kb[token] = -2 log2(e) / max(|x|, 1e-12) (NORM2: the squared norm |x|^2;
 // the pieces are those of xstage_load<NTHR, NORM2>)
-template <int NTHR, bool NORM2 = false>
+template <int NTHR, bool NORM2, typename IO>
 __device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, float *kb)
 {
 #pragma unroll
@@ -206,13 +240,27 @@ __device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, f
         const int e = xitem<NTHR, NORM2>(it);
         if (e < WCT * 8) {  // uniform per wave
             const int j = e >> 3;
-            const bf16x8 v = __builtin_bit_cast(bf16x8, xs.v[it]);
-            *reinterpret_cast<bf16x8 *>(xb + j * XRS + (e & 7) * 8) = v;
             float ss = 0.f;
+            if constexpr (is_bf16<IO>) {
+                const bf16x8 v = __builtin_bit_cast(bf16x8, xs.v[it]);
+                *reinterpret_cast<bf16x8 *>(xb + j * XRS + (e & 7) * 8) = v;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float x = (float)v[i];
-                ss = fmaf(x, x, ss);
+                for (int i = 0; i < 8; ++i) {
+                    const float x = (float)v[i];
+                    ss = fmaf(x, x, ss);
+                }
+            } else {
+                // the norm from the exact values, the staged row rounded to bf16
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[2 * i] = io_lo<IO>(xs.v[it][i]);
+                    x[2 * i + 1] = io_hi<IO>(xs.v[it][i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+                *reinterpret_cast<bf16x8 *>(xb + j * XRS + (e & 7) * 8) =
+                    pk8(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7]));
             }
             ss = sum8(ss);
             if ((e & 7) == 0)
@@ -227,8 +275,8 @@ __device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, f
 struct YRes {
     Rsrc v, o, d;
 };
-template <bool DVAL>
-__device__ __forceinline__ YRes yres(const ValSrc<bf16> &s, const Chunk &c)
+template <bool DVAL, typename IO>
+__device__ __forceinline__ YRes yres(const ValSrc<IO> &s, const Chunk &c)
 {
     YRes r;
     r.v = row_res(s.V, c);
@@ -276,7 +324,7 @@ constexpr int YRS = YRC + 8;
 
 // yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may
 // be null); nv = valid rows of the chunk (the others are staged as zeros)
-template <int NTHR, bool DVAL>
+template <int NTHR, bool DVAL, typename IO>
 __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int nv, bf16 *yc,
                                              bf16 *yr = nullptr)
 {
@@ -286,13 +334,18 @@ __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int n
         if (e < WCT * 8) {  // uniform per wave
             const int jp = e >> 4, c0 = (e & 15) * 4;
             if constexpr (!DVAL) {
-                // [v | 1]: the loaded bf16 bits are staged as they are; the column
-                // layout pairs tokens 2jp, 2jp + 1 of each column by byte permutes
+                // [v | 1]: the loaded bits are staged as they are (bf16 rows) or
+                // rounded to bf16; the column layout pairs tokens 2jp, 2jp + 1 of
+                // each column by byte permutes
+                u32x2 yx[2] = {ys.x[it][0], ys.x[it][1]};
+                if constexpr (!is_bf16<IO>)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) yx[h] = u32x2{io_bf16w<IO>(yx[h][0]), io_bf16w<IO>(yx[h][1])};
                 if (yc) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         *reinterpret_cast<uint32_t *>(yc + (c0 + i) * YCS + 2 * jp) =
-                            __builtin_amdgcn_perm(ys.x[it][1][i >> 1], ys.x[it][0][i >> 1],
+                            __builtin_amdgcn_perm(yx[1][i >> 1], yx[0][i >> 1],
                                                   (i & 1) ? 0x07060302u : 0x05040100u);
                     if (c0 == 0)
                         *reinterpret_cast<uint32_t *>(yc + HD * YCS + 2 * jp) =
@@ -301,7 +354,7 @@ __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int n
                 if (yr) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        *reinterpret_cast<u32x2 *>(yr + (2 * jp + h) * YRS + c0) = ys.x[it][h];
+                        *reinterpret_cast<u32x2 *>(yr + (2 * jp + h) * YRS + c0) = yx[h];
                         if (c0 == 0) yr[(2 * jp + h) * YRS + HD] = (bf16)(2 * jp + h < nv ? 1.f : 0.f);
                     }
                 }
@@ -311,16 +364,22 @@ __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int n
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool ok = 2 * jp + h < nv;
-                const bf16x4 xv = __builtin_bit_cast(bf16x4, ys.x[it][h]);
-                const bf16x4 ov = __builtin_bit_cast(bf16x4, ys.o[it][h]);
+                float xv[4], ov[4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    xv[2 * i] = io_lo<IO>(ys.x[it][h][i]);
+                    xv[2 * i + 1] = io_hi<IO>(ys.x[it][h][i]);
+                    ov[2 * i] = io_lo<IO>(ys.o[it][h][i]);
+                    ov[2 * i + 1] = io_hi<IO>(ys.o[it][h][i]);
+                }
                 float dot = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dot = fmaf((float)xv[i], (float)ov[i], dot);
+                for (int i = 0; i < 4; ++i) dot = fmaf(xv[i], ov[i], dot);
                 dot = sum16(dot);
                 // rows past the end read m = 0: their D row is zero
                 const float inv_m = ok ? __builtin_amdgcn_rcpf(ys.m[it][h]) : 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) y[h][i] = (float)xv[i] * inv_m;
+                for (int i = 0; i < 4; ++i) y[h][i] = xv[i] * inv_m;
                 extra[h] = -dot * inv_m;
             }
             if (yc) {
@@ -432,8 +491,6 @@ __device__ __forceinline__ void sel_lds(const bf16 *sl, bf16x8 (&sel)[2])
 //         in fp16 pairs (two values per instruction); the sign of u is copied
 //         onto the pair's sign bits.
 //   else: the functions themselves in fp32.
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ half2v horner16(const uint32_t (&cf)[DEG16 + 1], half2v y)
 {
     half2v h = __builtin_bit_cast(half2v, cf[DEG16]);
@@ -623,9 +680,9 @@ __device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 //   SRC = 0: the rows X are hashed here; WR bit 0 / bit 1 store their t /
 //            dt/du' into the cache `co`.
 //   SRC = 1: t comes from the cache `ci_` (X is not read).
-template <int NW, bool DVAL, int SRC, int WR, bool POLY>
+template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO>
 __global__ __launch_bounds__(NW * 64) void sum_kernel(
-    const bf16 *__restrict__ X, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
+    const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, Squash sq,
     int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st)
 {
     constexpr int NTHR = NW * 64;
@@ -641,8 +698,8 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const bf16 *Xs = X + row0 * HD;
-    ValSrc<bf16> vh = vsrc;
+    const IO *Xs = X + row0 * HD;
+    ValSrc<IO> vh = vsrc;
     vh.V += row0 * HD;
     if (DVAL) {
         vh.O += row0 * HD;
@@ -673,11 +730,11 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c0), ys);
     if (HASH) {
         xstage_load<NTHR>(row_res(Xs, c0), xs);
-        xstage_store<NTHR>(xs, xbuf[0], kbuf[0]);
+        xstage_store<NTHR, false, IO>(xs, xbuf[0], kbuf[0]);
     } else {
         hc_load<NW>(hc_res<NW>(cin_t, c0), tc);
     }
-    ystage_store<NTHR, DVAL>(ys, c0.nv, ycol[0]);
+    ystage_store<NTHR, DVAL, IO>(ys, c0.nv, ycol[0]);
     if (HASH) xstage_load<NTHR>(row_res(Xs, c1), xs);
     ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c1), ys);
     lds_barrier();
@@ -687,8 +744,8 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
         // stage chunk ci + 1 (loaded one iteration ago) into the other buffers,
         // which were last read before the previous barrier, then prefetch ci + 2
         if (ci + 1 < nch) {
-            if (HASH) xstage_store<NTHR>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            ystage_store<NTHR, DVAL>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
+            if (HASH) xstage_store<NTHR, false, IO>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            ystage_store<NTHR, DVAL, IO>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
         }
         const halfx4 tcur[2] = {tc[0], tc[1]};
         if (HASH)
@@ -747,11 +804,11 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // One barrier per chunk: staging buffers and the partial outputs are double
 // buffered, and the partial outputs of chunk c are summed after the barrier
 // of chunk c + 1, beside that chunk's products.
-template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY>
+template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
-    const bf16 *__restrict__ R, ValSrc<bf16> vsrc, const float *__restrict__ W, int L, Squash sq,
+    const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
-    bf16 *__restrict__ Out, float *__restrict__ den)
+    IO *__restrict__ Out, float *__restrict__ den)
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = RSRC == 0;
@@ -773,14 +830,14 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const bf16 *Rs = R + row0 * HD;
-    ValSrc<bf16> vh = vsrc;
+    const IO *Rs = R + row0 * HD;
+    ValSrc<IO> vh = vsrc;
     vh.V += row0 * HD;
     if (BWD) {
         vh.O += row0 * HD;
         vh.den += row0;
     }
-    bf16 *Os = Out + row0 * HD;
+    IO *Os = Out + row0 * HD;
     float *dens = BWD ? nullptr : den + row0;
     const _Float16 *rt_seg = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
     const _Float16 *rc_seg = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
@@ -821,7 +878,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     }
     if (HASH) {
         xstage_load<NTHR>(row_res(Rs, c0), xs);
-        xstage_store<NTHR>(xs, xbuf[0], kbuf[0]);
+        xstage_store<NTHR, false, IO>(xs, xbuf[0], kbuf[0]);
         xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
     } else {
         hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
@@ -878,13 +935,13 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                     n += *reinterpret_cast<const floatx4 *>(rn + (((ww * 2 + tt) * 4 + ct) * 64 + ln) * 4);
                 const int off = (tt * 16 + (ln & 15)) * (HD * 2) + (16 * ct + 4 * (ln >> 4)) * 2;
                 if (BWD) {
-                    bst64(u32x2{pk_bf16(n[0], n[1]), pk_bf16(n[2], n[3])}, ro, off);
+                    bst64(u32x2{pk_io<IO>(n[0], n[1]), pk_io<IO>(n[2], n[3])}, ro, off);
                 } else {
                     float m = rm[tt * 64 + (ln & 15)];
 #pragma unroll
                     for (int ww = 1; ww < NW; ++ww) m += rm[(ww * 2 + tt) * 64 + (ln & 15)];
                     const float inv = __builtin_amdgcn_rcpf(m);
-                    bst64(u32x2{pk_bf16(n[0] * inv, n[1] * inv), pk_bf16(n[2] * inv, n[3] * inv)}, ro, off);
+                    bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
                     bstf(m, make_rsrc(dens + c.tok0, c.nv * 4), (ct == 0 && ln < 16) ? (tt * 16 + ln) * 4 : OOB);
                 }
             }
@@ -895,7 +952,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         constexpr int b = decltype(par)::v;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
         if (CAUSAL) {
-            ystage_store<NTHR, BWD>(ys, cc.nv, ycol[b]);
+            ystage_store<NTHR, BWD, IO>(ys, cc.nv, ycol[b]);
             ystage_load<NTHR, BWD>(yres<BWD>(vh, cn), ys);
         }
         bf16x8 pr[2][2];
@@ -911,7 +968,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         bf16x8 kA1;   // single-tile scores (fwd: reader tile 0, bwd: reader tile 1)
         bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
         if (HASH) {  // the next chunk's rows into the other buffer (last read before the previous barrier)
-            if (ci + 1 < nch) xstage_store<NTHR>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
+            if (ci + 1 < nch) xstage_store<NTHR, false, IO>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
             xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
         }
         lds_barrier();  // value columns and next rows staged; partial outputs of chunk ci - 1 in LDS
@@ -1024,11 +1081,11 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 // 64 dims] on MFMA (both operands read transposed from du and the staged
 // rows), summed in LDS, and the workgroup's sum written to dwp[workgroup]
 // ([NW * 16][64] fp32) for a reduction over segments.
-template <int NW, bool CAUSAL, bool REVERSE, bool DW = false>
+template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
-    const bf16 *__restrict__ Xr, ValSrc<bf16> vr_src, ValSrc<bf16> vw_src,
+    const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
     const float *__restrict__ W, int L, int64_t N, int seg, int64_t nseg,
-    const float *__restrict__ st, HCache rc, HCache wc, bf16 *__restrict__ dX,
+    const float *__restrict__ st, HCache rc, HCache wc, IO *__restrict__ dX,
     float *__restrict__ dwp)
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
@@ -1057,8 +1114,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const bf16 *Rs = Xr + row0 * HD;
-    ValSrc<bf16> vrh = vr_src, vwh = vw_src;
+    const IO *Rs = Xr + row0 * HD;
+    ValSrc<IO> vrh = vr_src, vwh = vw_src;
     vrh.V += row0 * HD;
     vwh.V += row0 * HD;
     if (RD) {
@@ -1068,7 +1125,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         vwh.O += row0 * HD;
         vwh.den += row0;
     }
-    bf16 *dXs = dX + row0 * HD;
+    IO *dXs = dX + row0 * HD;
     const _Float16 *rt_seg = rc.t + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
@@ -1189,7 +1246,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             float rv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) rv[r] = (dxh[i][r] - coef * (float)xkeep[i][r]) * inv;
-            const u32x2 v = {pk_bf16(rv[0], rv[1]), pk_bf16(rv[2], rv[3])};
+            const u32x2 v = {pk_io<IO>(rv[0], rv[1]), pk_io<IO>(rv[2], rv[3])};
             bst64(v, rdx, tok * (HD * 2) + (nt * 16 + 4 * g) * 2);
         }
     };
@@ -1201,8 +1258,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
-        ystage_store<NTHR, RD>(ysr, cc.nv, nullptr, yrow_r[b]);
-        if (CAUSAL) ystage_store<NTHR, !RD>(ysw, cc.nv, ycol_w[b], yrow_w[b]);
+        ystage_store<NTHR, RD, IO>(ysr, cc.nv, nullptr, yrow_r[b]);
+        if (CAUSAL) ystage_store<NTHR, !RD, IO>(ysw, cc.nv, ycol_w[b], yrow_w[b]);
         ystage_load<NTHR, RD>(yres<RD>(vrh, cn), ysr);
         if (CAUSAL) ystage_load<NTHR, !RD>(yres<!RD>(vwh, cn), ysw);
         const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
@@ -1221,7 +1278,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         lds_barrier();  // value rows of this chunk; du and rows of ci - 1; dots of ci - 2
         finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
         // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
-        xstage_store<NTHR, true>(xs, xbuf[b], kbuf[b]);
+        xstage_store<NTHR, true, IO>(xs, xbuf[b], kbuf[b]);
         xstage_load<NTHR, true>(row_res(Rs, cn), xs);
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][3];

@@ -3,8 +3,8 @@
 This module is shared by the tests, the benchmark and the smoke check, and it
 feeds both the HIP path and the oracle the same bytes.  It holds none of the
 method's arithmetic: only random draws, the per-row L2 normalisation that the
-input recipe applies to Q and K, rounding to the storage dtype, and bf16 bit
-conversions.
+input recipe applies to Q and K, rounding to the storage dtype, and bf16 / fp16
+bit conversions.
 
 Recipe (one counter-based Philox stream per tensor, fixed order W, Q, K, V,
 dO; rows generated in blocks of ``ROWS_PER_BLOCK`` so that any block can be
@@ -12,7 +12,7 @@ reproduced on its own):
 
 * every tensor is drawn i.i.d. N(0, 1) in fp32;
 * rows of Q and K are L2-normalised in fp64, rounded to fp32, and for bf16
-  workloads rounded again to bf16 with round-to-nearest-even;
+  or fp16 workloads rounded again to that type with round-to-nearest-even;
 * V and dO are rounded to the storage dtype the same way;
 * W[L, P, d] stays fp32;
 * the counter of block b of stream s is (0, b, 0, 0) under key
@@ -42,7 +42,7 @@ class Workload:
     P: int
     tau: float
     causal: bool
-    dtype: str  # "f32" or "bf16": storage type of Q, K, V, O, dO, dQ, dK, dV
+    dtype: str  # "f32", "bf16" or "f16": storage type of Q, K, V, O, dO, dQ, dK, dV
     backward: bool
     chunk: int  # 0: the library chooses
     seed: int
@@ -81,9 +81,11 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact fp64 value of a stored tensor (fp32 array or bf16 bits)."""
+    """Exact fp64 value of a stored tensor (fp32 array, bf16 or fp16 bits)."""
     if dtype == "bf16":
         return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
@@ -109,7 +111,11 @@ def _rows(seed: int, stream: int, r0: int, r1: int, d: int, normalise: bool) -> 
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":  # IEEE half, round-to-nearest-even (numpy's cast)
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    return x
 
 
 def make_w(seed: int, L: int, P: int, d: int) -> np.ndarray:
@@ -127,7 +133,7 @@ def make_tensor(seed: int, stream: int, BH: int, N: int, d: int, dtype: str,
     """
     n = N if n_rows is None else n_rows
     normalise = stream in (STREAM_Q, STREAM_K)
-    out = np.empty((BH, n, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty((BH, n, d), dtype=np.uint16 if dtype in ("bf16", "f16") else np.float32)
     jobs = []
     for h in range(BH):
         for r in range(0, n, ROWS_PER_BLOCK):

@@ -8,12 +8,14 @@ import torch
 from sketch_attention_soft_amd import inputs as I
 
 # parity bar: max over heads of the relative Frobenius error
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
 
 
 def to_device(a: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.float16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 

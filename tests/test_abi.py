@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "race_attn.h")
 
 OK, E_NULL, E_SHAPE, E_UNSUP, E_TAU, E_CHUNK, E_WS, E_HIP = range(8)
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 
 @pytest.fixture(scope="module")
@@ -75,6 +75,9 @@ def test_workspace_sizes(lib):
     assert ws_bytes(lib, L=32)[1] > f
     # fp32 keeps per-row hash buffers, bf16 (fused) does not
     assert ws_bytes(lib, dt=F32, N=1 << 16)[1] > ws_bytes(lib, dt=BF16, N=1 << 16)[1]
+    # fp16 rows take the bf16 (fused) path: the same workspace
+    for bwd in (0, 1, 2):
+        assert ws_bytes(lib, dt=F16, L=32, bwd=bwd) == ws_bytes(lib, dt=BF16, L=32, bwd=bwd)
     # the 75M-token workload fits comfortably in one GPU's HBM: segment states
     # plus four fp16 hash-feature arrays (t, dt/du' of Q and K), 512 B per row
     st, b75 = ws_bytes(lib, N=75_000_064, L=16, bwd=1)
@@ -84,7 +87,7 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
     (dict(d=32), E_UNSUP), (dict(P=3), E_UNSUP), (dict(L=65), E_UNSUP),
-    (dict(L=33, dt=F32), E_UNSUP), (dict(dt=5), E_UNSUP),
+    (dict(L=33, dt=F32), E_UNSUP), (dict(L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
     (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
 ])
 def test_workspace_validation(lib, kw, code):
@@ -102,6 +105,11 @@ def test_saved_bytes(lib):
     # one fp32 state of F x 80 per segment plus the head total
     assert out.value >= 2 * 512 * 80 * 4
     assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, F32, ctypes.byref(out)) == OK and out.value == 0
+    # fp16 rows save the same state as bf16 rows
+    o16, ob = ctypes.c_size_t(0), ctypes.c_size_t(1)
+    assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, F16, ctypes.byref(o16)) == OK
+    assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, ctypes.byref(ob)) == OK
+    assert o16.value == ob.value > 0
     assert fn(1, 1, 1 << 16, 64, 64, 4, 1, 0, BF16, ctypes.byref(out)) == OK and out.value == 0
     assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, None) == E_NULL
     assert fn(1, 1, 0, 64, 32, 4, 1, 0, BF16, ctypes.byref(out)) == E_SHAPE

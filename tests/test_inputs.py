@@ -45,3 +45,19 @@ def test_workloads_table():
     assert I.WORKLOADS["causal_h8_n64k_f32"].chunk == 256
     assert I.WORKLOADS["noncausal_fwd_n1k_f32"].backward is False
     assert len({w.seed for w in I.WORKLOADS.values()}) == len(I.WORKLOADS)
+
+
+def test_f16_storage_matches_torch():
+    # fp16 workloads store IEEE half bits rounded to nearest even, as torch does
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 100,
+                        np.array([0.0, -0.0, 1.0, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 6e-8], np.float32)])
+    ours = I._store(x, "f16")
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert ours.dtype == np.uint16 and np.array_equal(ours, ref)
+    assert np.array_equal(I.to_f64(ours, "f16"), torch.from_numpy(x).to(torch.float16).double().numpy())
+    f = I.make_inputs(1, 1, 500, 64, 8, 4, "f16", seed=9)
+    g = I.make_inputs(1, 1, 500, 64, 8, 4, "f32", seed=9)
+    for k in ("q", "k", "v", "do"):
+        assert f[k].dtype == np.uint16
+        assert np.array_equal(I.to_f64(f[k], "f16"), g[k].astype(np.float16).astype(np.float64))
