@@ -37,7 +37,9 @@
  *     frees or synchronises, keeps no global mutable state and is safe to
  *     call from several threads.
  *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32 and
- *     RACE_F16),
+ *     RACE_F16); also d = 32 for RACE_BF16 and RACE_F16 with L <= 32 (the
+ *     rows are zero-padded to 64 columns on chip: the same work per token as
+ *     d = 64, half the memory traffic),
  *     any B, H, N >= 1 (int64 offsets), tau finite and > 0.
  *   - chunk: tokens per scan segment, 0 = the library chooses; otherwise a
  *     multiple of 16.  It changes only the order of the floating-point sums.
@@ -215,7 +217,7 @@ race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
  * o = n / m, den = m (step 4).  The states of all heads are one contiguous
  * device array [B][H][F][d + 1], owned by the caller; all zeros is the empty
  * prefix.  These entry points compute in fp32 (t with tanhf) whatever dt is.
- * Supported as above (d = 64, P = 4, L <= 64) and B * H <= 65535; N or T = 0
+ * Supported for 1 <= d <= 64, P = 4, L <= 64 and B * H <= 65535; N or T = 0
  * is a no-op (the row pointers may then be NULL; W and state may not).  Calls
  * that write one state must not overlap. */
 

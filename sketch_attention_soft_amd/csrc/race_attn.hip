@@ -54,6 +54,7 @@ struct Tracer {
 struct Plan {
     int64_t BH, N, rows;
     int L, nw, F, LP;
+    int d;             // head dimension (64, or 32 on the fused path)
     bool fused;        // bf16 and L <= 32: kernels hash their own rows
     int64_t seg, nseg;
     size_t st_bytes;   // one set of segment states (nseg + 1 per head)
@@ -79,10 +80,13 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     if (B < 1 || H < 1 || N < 1 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
-    if (d != race::HD || P != race::NP) return RACE_ERR_UNSUPPORTED;
+    if (P != race::NP) return RACE_ERR_UNSUPPORTED;
     if (L > 64 || (dt != RACE_BF16 && L > 32)) return RACE_ERR_UNSUPPORTED;
+    // d = 64, or d = 32 on the fused path (16-bit rows, L <= 32)
+    if (d != race::HD && !(d == 32 && dt != RACE_F32 && L <= 32)) return RACE_ERR_UNSUPPORTED;
     if (chunk < 0 || chunk % race::CH != 0) return RACE_ERR_CHUNK;
     p->BH = (int64_t)B * H;
+    p->d = d;
     p->N = N;
     p->rows = p->BH * N;
     p->L = L;
@@ -319,38 +323,38 @@ race::HCache hcache(const Plan &p, char *base, int it, int ic)
 }
 
 // segment sums: hashing (SRC = 0, squash polynomial or direct) or from the cache
-template <int NW, bool DVAL, int SRC, int WR, typename T>
+template <int NW, bool DVAL, int SRC, int WR, int D, typename T>
 void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *X,
                 const race::ValSrc<T> &vs, const float *W, const Plan &p, const race::HCache &cin,
                 const race::HCache &cout, float *st)
 {
     if constexpr (sizeof(T) == 2) {
         if (SRC == 1 || sq.deg >= 0)
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T>), grid, dim3(NW * 64), X, vs,
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T, D>), grid, dim3(NW * 64), X, vs,
                    W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
         else
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T>), grid, dim3(NW * 64), X, vs,
+            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T, D>), grid, dim3(NW * 64), X, vs,
                    W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
     }
 }
 
 // chunk walk: readers hashed (RSRC = 0) or from the cache, writers from the cache
-template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, typename T>
+template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, int D, typename T>
 void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squash &sq, const T *R,
                  const race::ValSrc<T> &vs, const float *W, const Plan &p, const float *st,
                  const race::HCache &rc, const race::HCache &wc, T *out, float *den)
 {
     if constexpr (sizeof(T) == 2) {
         if (RSRC == 1 || sq.deg >= 0)
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T>), grid,
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D>), grid,
                    dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
         else
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T>), grid,
+            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D>), grid,
                    dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
     }
 }
 
-template <int NW, bool CAUSAL, bool REVERSE, typename T>
+template <int NW, bool CAUSAL, bool REVERSE, int D, typename T>
 void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
                  const race::ValSrc<T> &vr, const race::ValSrc<T> &vw, const float *W,
                  const Plan &p, const float *st, const race::HCache &rc, const race::HCache &wc,
@@ -358,15 +362,16 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
 {
     if constexpr (sizeof(T) == 2) {
         if (dwp)
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T>), grid, dim3(NW * 64), Xr,
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D>), grid, dim3(NW * 64), Xr,
                    vr, vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp);
         else
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T>), grid, dim3(NW * 64), Xr, vr,
+            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D>), grid, dim3(NW * 64), Xr, vr,
                    vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr);
     }
 }
 
-template <typename T, int NW>
+// D = d: 64, or 32 on the fused path (bf16 / fp16 rows, L <= 32)
+template <typename T, int NW, int D>
 void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const float *W, float tau,
                     int causal, T *O, float *den, char *ws, float *saved, const Tracer &tr)
 {
@@ -391,24 +396,24 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
         const race::HCache hq = saved ? hcache(p, sb + p.s_hc, 2, 3) : hcache(p, nullptr, -1, -1);
         const race::HCache none = hcache(p, nullptr, -1, -1);
         if (saved)
-            launch_sum<WS, false, 0, 3>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
+            launch_sum<WS, false, 0, 3, D>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
         else
-            launch_sum<WS, false, 0, 1>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
+            launch_sum<WS, false, 0, 1, D>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
         launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
         if (causal) {
             if (saved)
-                launch_walk<WW, true, false, 0, 3>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+                launch_walk<WW, true, false, 0, 3, D>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
             else
-                launch_walk<WW, true, false, 0, 0>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+                launch_walk<WW, true, false, 0, 0, D>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
         } else {
             if (saved)
-                launch_walk<WW, false, false, 0, 3>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+                launch_walk<WW, false, false, 0, 3, D>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
             else
-                launch_walk<WW, false, false, 0, 0>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
+                launch_walk<WW, false, false, 0, 0, D>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O, den);
         }
         return;
     }
-    if constexpr (!std::is_same<T, _Float16>::value) {  // fp16 rows: the fused path only
+    if constexpr (!std::is_same<T, _Float16>::value && D == race::HD) {  // fp16 rows, d = 32: fused path only
     LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
     LAUNCH(tr, "hash_k", (race::hash_kernel<T, false>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
     const race::ValSrc<T> vs{V, nullptr, nullptr};
@@ -425,7 +430,7 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     }
 }
 
-template <typename T, int NW, int CAUSAL>
+template <typename T, int NW, int CAUSAL, int D>
 void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                           const T *O, const float *den, const T *dO, float tau, T *dQ, T *dK,
                           T *dV, char *ws, const float *saved, const Tracer &tr, float *dW)
@@ -458,30 +463,30 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
             hk = hcache(p, const_cast<char *>(sb) + p.s_hc, 0, 1);
             hq = hcache(p, const_cast<char *>(sb) + p.s_hc, 2, 3);
             // gradient state G (FxC; read transposed by dK): suffix over segments
-            launch_sum<WS, true, 1, 0>(tr, "sum_qd", nblk, sq, Q, vd, W, p, hq, none, sG);
+            launch_sum<WS, true, 1, 0, D>(tr, "sum_qd", nblk, sq, Q, vd, W, p, hq, none, sG);
         } else {
             hk = hcache(p, ws + p.b_hc, 0, 1);
             hq = hcache(p, ws + p.b_hc, 2, 3);
-            launch_sum<WS, false, 0, 3>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, none, hk, sS);
+            launch_sum<WS, false, 0, 3, D>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, none, hk, sS);
             launch_scan(tr, "scan_kv_t", p, sS, scan_tmp, 0);
             sK = sS;
-            launch_sum<WS, true, 0, 3>(tr, "sum_qd", nblk, sq, Q, vd, W, p, none, hq, sG);
+            launch_sum<WS, true, 0, 3, D>(tr, "sum_qd", nblk, sq, Q, vd, W, p, none, hq, sG);
         }
         launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
         // dW (when asked): partial sums of the dQ and dK workgroups, then their sum
         float *dwp = dW ? reinterpret_cast<float *>(ws + p.b_dw) : nullptr;
         const int64_t dwb = p.BH * p.nseg * (int64_t)(WD * 16 * race::HD);
-        launch_grad<WD, CAUSAL != 0, false>(tr, "dq", nblk, Q, vd, vv, W, p, sK, hq, hk, dQ, dwp);
-        launch_grad<WD, CAUSAL != 0, true>(tr, "dk", nblk, K, vv, vd, W, p, sG, hk, hq, dK,
+        launch_grad<WD, CAUSAL != 0, false, D>(tr, "dq", nblk, Q, vd, vv, W, p, sK, hq, hk, dQ, dwp);
+        launch_grad<WD, CAUSAL != 0, true, D>(tr, "dk", nblk, K, vv, vd, W, p, sG, hk, hq, dK,
                                            dwp ? dwp + dwb : nullptr);
         if (dW)
             LAUNCH(tr, "dw_reduce", race::dw_reduce_kernel, dim3((p.LP * race::HD + 31) / 32),
-                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, dW);
-        launch_walk<WW, CAUSAL != 0, true, 1, 0>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV,
+                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, D, dW);
+        launch_walk<WW, CAUSAL != 0, true, 1, 0, D>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV,
                                                  nullptr);
         return;
     }
-    if constexpr (!std::is_same<T, _Float16>::value) {  // fp16 rows: the fused path only
+    if constexpr (!std::is_same<T, _Float16>::value && D == race::HD) {  // fp16 rows, d = 32: fused path only
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,
            p.LP, lp32, wt);
     LAUNCH(tr, "hash_q_chain", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L,
@@ -515,15 +520,15 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     }
 }
 
-template <typename T, int NW>
+template <typename T, int NW, int D>
 void launch_backward(const Plan &p, const T *Q, const T *K, const T *V, const float *W,
                      const T *O, const float *den, const T *dO, float tau, int causal, T *dQ,
                      T *dK, T *dV, char *ws, const float *saved, const Tracer &tr, float *dW)
 {
     if (causal)
-        launch_backward_body<T, NW, 1>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
+        launch_backward_body<T, NW, 1, D>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
     else
-        launch_backward_body<T, NW, 0>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
+        launch_backward_body<T, NW, 0, D>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
 }
 
 template <typename T>
@@ -535,13 +540,24 @@ void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V
     auto k = static_cast<const T *>(K);
     auto v = static_cast<const T *>(V);
     auto o = static_cast<T *>(O);
+    if constexpr (sizeof(T) == 2) {
+        if (p.d == 32) {  // the fused path only (L <= 32)
+            switch (p.nw) {
+            case 1: launch_forward<T, 1, 32>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+            case 2: launch_forward<T, 2, 32>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+            default: launch_forward<T, 4, 32>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+            }
+            return;
+        }
+    }
+    constexpr int D = race::HD;
     switch (p.nw) {
-    case 1: launch_forward<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
-    case 2: launch_forward<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
-    case 4: launch_forward<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+    case 1: launch_forward<T, 1, D>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+    case 2: launch_forward<T, 2, D>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+    case 4: launch_forward<T, 4, D>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
     default:
         if constexpr (std::is_same<T, bf16>::value)
-            launch_forward<T, 8>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr);
+            launch_forward<T, 8, D>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr);
         break;
     }
 }
@@ -560,13 +576,24 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     auto dq = static_cast<T *>(dQ);
     auto dk = static_cast<T *>(dK);
     auto dv = static_cast<T *>(dV);
+    if constexpr (sizeof(T) == 2) {
+        if (p.d == 32) {  // the fused path only (L <= 32)
+            switch (p.nw) {
+            case 1: launch_backward<T, 1, 32>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+            case 2: launch_backward<T, 2, 32>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+            default: launch_backward<T, 4, 32>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+            }
+            return;
+        }
+    }
+    constexpr int D = race::HD;
     switch (p.nw) {
-    case 1: launch_backward<T, 1>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
-    case 2: launch_backward<T, 2>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
-    case 4: launch_backward<T, 4>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+    case 1: launch_backward<T, 1, D>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+    case 2: launch_backward<T, 2, D>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
+    case 4: launch_backward<T, 4, D>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
     default:
         if constexpr (std::is_same<T, bf16>::value)
-            launch_backward<T, 8>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW);
+            launch_backward<T, 8, D>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW);
         break;
     }
 }
@@ -585,7 +612,7 @@ race_status_t check_trace(race_trace_t *trace)
 // Streaming state (race_stream.h)
 
 struct StreamPlan {
-    int BH, L, F, fpt, nthr;
+    int BH, L, d, F, fpt, nthr;
     int64_t elems;  // floats of one head's state
 };
 
@@ -593,17 +620,18 @@ race_status_t stream_plan(int B, int H, int64_t N, int d, int L, int P, race_dty
                           StreamPlan *sp)
 {
     if (B < 1 || H < 1 || N < 0 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
-    if (d != race::HD || P != race::NP || L > 64) return RACE_ERR_UNSUPPORTED;
+    if (d > race::HD || P != race::NP || L > 64) return RACE_ERR_UNSUPPORTED;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH > 65535) return RACE_ERR_UNSUPPORTED;  // heads go to the second grid dimension
-    if (N > ((int64_t)1 << 62) / (BH * race::HD)) return RACE_ERR_SHAPE;
+    if (N > ((int64_t)1 << 62) / (BH * d)) return RACE_ERR_SHAPE;
     sp->BH = (int)BH;
     sp->L = L;
+    sp->d = d;
     sp->F = L * race::NR;
     sp->fpt = sp->F > 256 ? 64 : 32;
     sp->nthr = 64 * ((sp->F + sp->fpt - 1) / sp->fpt);  // one wave per feature group
-    sp->elems = (int64_t)sp->F * race::S_C;
+    sp->elems = (int64_t)sp->F * (d + 1);
     return RACE_OK;
 }
 
@@ -628,7 +656,7 @@ void launch_stream(const StreamPlan &sp, const void *Q, const void *K, const voi
              : sp.nthr <= 512   ? race::stream_kernel<T, MODE, 64, 512>
                                 : race::stream_kernel<T, MODE, 64, 1024>;
     hipLaunchKernelGGL(k, grid, dim3(sp.nthr), 0, s, static_cast<const T *>(Q),
-                       static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, 1.f / tau,
+                       static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, sp.d, 1.f / tau,
                        N, blk, state, part, static_cast<T *>(O), den);
 }
 

@@ -8,7 +8,9 @@
 // costs the same however long the prefix) and §2.2 (bucket sums A and B, the
 // ratio readout).
 //
-// State of one head: S[f][c] for f < F = 16 L, c <= d (fp32, [F][d + 1]):
+// State of one head: S[f][c] for f < F = 16 L, c <= d (fp32, [F][d + 1]),
+// d <= 64 (rows and W are read with their own length d; lane c < d of a wave
+// holds column c):
 //   S[f][c] = sum_j psi_f(k_j) v_j[c] (c < d),  S[f][d] = sum_j psi_f(k_j),
 //   psi_{16 l + s}(x) = 1/4 prod_{p in s} t_{lp}(x)  (s: a subset of the
 //   table's 4 hyperplanes, bit p set when p is in it),
@@ -38,7 +40,6 @@
 namespace race {
 
 constexpr int SM_ADD = 0, SM_DECODE = 1, SM_READOUT = 2;
-constexpr int S_C = HD + 1;      // state columns
 constexpr int S_XS = HD + 1;     // LDS row stride of staged rows and W (odd: no bank conflicts)
 
 template <typename T> __device__ __forceinline__ float sload(const T *p) { return (float)*p; }
@@ -50,7 +51,7 @@ template <typename T, int MODE, int FPT, int MAXT>
 __global__ __launch_bounds__(MAXT)
 __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) void stream_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
-    const float *__restrict__ W, int L, float inv_tau, int64_t N, int64_t blk,
+    const float *__restrict__ W, int L, int d, float inv_tau, int64_t N, int64_t blk,
     float *__restrict__ state, float *__restrict__ part, T *__restrict__ O, float *__restrict__ den)
 {
     constexpr bool UPD = MODE != SM_READOUT, RD = MODE != SM_ADD;
@@ -68,27 +69,30 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     __shared__ float pn[RD ? S_TT : 1][NWV][HD];       // partial readouts n of the waves
     __shared__ float pm[RD ? S_TT : 1][NWV];           // and of m
 
-    const int LP = L * NP, F = L * NR;
+    const int LP = L * NP, F = L * NR, sc = d + 1;  // sc: state columns
     const int QN = (F + FPT - 1) / FPT;
     const int nthr = blockDim.x, tid = threadIdx.x;
     const int c = tid & 63, grp = tid >> 6, f0 = grp * FPT;
     const int64_t bh = blockIdx.y;
     const int64_t t_begin = (int64_t)blockIdx.x * blk, t_end = min(N, t_begin + blk);
     const int64_t row0 = bh * N;
-    float *sh = state + bh * (int64_t)F * S_C;
+    float *sh = state + bh * (int64_t)F * sc;
 
     // W rows in LDS for the parallel modes; decode (mostly a few tokens) reads
     // them from global memory instead of waiting for the staging
     constexpr bool wlds = MODE != SM_DECODE;
     if (wlds)
-        for (int e = tid; e < LP * HD; e += nthr) wl[(e / HD) * S_XS + e % HD] = W[e];
+        for (int e = tid; e < LP * HD; e += nthr) {
+            const int h = e / HD, k = e % HD;
+            wl[h * S_XS + k] = k < d ? W[h * d + k] : 0.f;
+        }
     float S[FPT], Z[ZP];
 #pragma unroll
-    for (int i = 0; i < FPT; ++i) S[i] = (MODE != SM_ADD && f0 + i < F) ? sh[(int64_t)(f0 + i) * S_C + c] : 0.f;
+    for (int i = 0; i < FPT; ++i) S[i] = (MODE != SM_ADD && f0 + i < F && c < d) ? sh[(int64_t)(f0 + i) * sc + c] : 0.f;
 #pragma unroll
     for (int z = 0; z < ZP; ++z) {
         const int f = f0 + 64 * z + c;
-        Z[z] = (MODE != SM_ADD && 64 * z + c < FPT && f < F) ? sh[(int64_t)f * S_C + HD] : 0.f;
+        Z[z] = (MODE != SM_ADD && 64 * z + c < FPT && f < F) ? sh[(int64_t)f * sc + d] : 0.f;
     }
 
     for (int64_t tile = t_begin; tile < t_end; tile += S_TT) {
@@ -97,8 +101,8 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
         for (int e = tid; e < S_TT * HD; e += nthr) {
             const int t = e / HD, k = e % HD;
             float q = 0.f, kk = 0.f, v = 0.f;
-            if (t < nt) {
-                const int64_t off = (row0 + tile + t) * HD + k;
+            if (t < nt && k < d) {  // zeros past column d
+                const int64_t off = (row0 + tile + t) * d + k;
                 if (RD) q = sload(Q + off);
                 if (UPD) {
                     kk = sload(K + off);
@@ -135,9 +139,9 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
                     for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
                 }
             } else {
-                const float *wg = W + (int64_t)h * HD;
+                const float *wg = W + (int64_t)h * d;
 #pragma unroll 4
-                for (int k = 0; k < HD; ++k) {
+                for (int k = 0; k < d; ++k) {
                     const float wk = wg[k];
 #pragma unroll
                     for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
@@ -188,16 +192,16 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
         }
         __syncthreads();
         if (RD) {
-            for (int e = tid; e < nt * S_C; e += nthr) {
-                const int t = e / S_C, col = e % S_C;
+            for (int e = tid; e < nt * (d + 1); e += nthr) {
+                const int t = e / (d + 1), col = e % (d + 1);
                 float n = 0.f, m = 0.f;
                 for (int g = 0; g < QN; ++g) {
-                    if (col < HD) n += pn[t][g][col];
+                    if (col < d) n += pn[t][g][col];
                     m += pm[t][g];
                 }
                 const int64_t row = row0 + tile + t;
-                if (col < HD)
-                    O[row * HD + col] = (T)(n / m);
+                if (col < d)
+                    O[row * d + col] = (T)(n / m);
                 else
                     den[row] = m;
             }
@@ -205,14 +209,14 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
         }
     }
     if (MODE != SM_READOUT) {
-        float *dst = MODE == SM_DECODE ? sh : part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * S_C;
+        float *dst = MODE == SM_DECODE ? sh : part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * sc;
 #pragma unroll
         for (int i = 0; i < FPT; ++i)
-            if (f0 + i < F) dst[(int64_t)(f0 + i) * S_C + c] = S[i];
+            if (f0 + i < F && c < d) dst[(int64_t)(f0 + i) * sc + c] = S[i];
 #pragma unroll
         for (int z = 0; z < ZP; ++z) {
             const int f = f0 + 64 * z + c;
-            if (64 * z + c < FPT && f < F) dst[(int64_t)f * S_C + HD] = Z[z];
+            if (64 * z + c < FPT && f < F) dst[(int64_t)f * sc + d] = Z[z];
         }
     }
 }

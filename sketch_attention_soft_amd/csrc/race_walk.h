@@ -196,10 +196,11 @@ __device__ __forceinline__ void for_chunks2(int n, F &&body)
         if (ci + 1 < n) body(ci + 1, Par<1>{});
     }
 }
-// rows of a [token][HD] array of 16-bit elements
-template <typename IO> __device__ __forceinline__ Rsrc row_res(const IO *seg_rows, const Chunk &c)
+// rows of a [token][D] array of 16-bit elements (D = d: 64, or 32 staged
+// into the 64 columns of the kernels with zeros past column D)
+template <int D, typename IO> __device__ __forceinline__ Rsrc row_res(const IO *seg_rows, const Chunk &c)
 {
-    return make_rsrc(seg_rows + c.tok0 * HD, c.nv * HD * 2);
+    return make_rsrc(seg_rows + c.tok0 * D, c.nv * D * 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -219,13 +220,16 @@ template <int NTHR, bool UP> __device__ __forceinline__ int xitem(int it)
     return (UP && NTHR == 512 ? (int)threadIdx.x ^ 256 : (int)threadIdx.x) + it * NTHR;
 }
 
-template <int NTHR, bool UP = false>
+template <int NTHR, bool UP, int D>
 __device__ __forceinline__ void xstage_load(Rsrc r, XStage<NTHR> &xs)
 {
 #pragma unroll
     for (int it = 0; it < XStage<NTHR>::ITEMS; ++it) {
         const int e = xitem<NTHR, UP>(it);
-        xs.v[it] = bld128(r, e < WCT * 8 ? e * 16 : OOB);
+        if constexpr (D == HD)
+            xs.v[it] = bld128(r, e < WCT * 8 ? e * 16 : OOB);
+        else  // columns past D read as zeros
+            xs.v[it] = bld128(r, e < WCT * 8 && (e & 7) * 8 < D ? (e >> 3) * (D * 2) + (e & 7) * 16 : OOB);
     }
 }
 
@@ -275,13 +279,13 @@ __device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, f
 struct YRes {
     Rsrc v, o, d;
 };
-template <bool DVAL, typename IO>
+template <bool DVAL, int D, typename IO>
 __device__ __forceinline__ YRes yres(const ValSrc<IO> &s, const Chunk &c)
 {
     YRes r;
-    r.v = row_res(s.V, c);
+    r.v = row_res<D>(s.V, c);
     if constexpr (DVAL) {
-        r.o = row_res(s.O, c);
+        r.o = row_res<D>(s.O, c);
         r.d = make_rsrc(s.den + c.tok0, c.nv * 4);
     } else {
         r.o = r.v;
@@ -297,7 +301,7 @@ template <int NTHR, bool DVAL> struct YStage {
     float m[DVAL ? ITEMS : 1][2];
 };
 
-template <int NTHR, bool DVAL>
+template <int NTHR, bool DVAL, int D>
 __device__ __forceinline__ void ystage_load(const YRes &r, YStage<NTHR, DVAL> &ys)
 {
 #pragma unroll
@@ -307,7 +311,8 @@ __device__ __forceinline__ void ystage_load(const YRes &r, YStage<NTHR, DVAL> &y
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int tok = 2 * (e >> 4) + h;
-            const int off = act ? tok * (HD * 2) + (e & 15) * 8 : OOB;
+            // columns past D read as zeros (m is read with the row)
+            const int off = act && (D == HD || (e & 15) * 4 < D) ? tok * (D * 2) + (e & 15) * 8 : OOB;
             ys.x[it][h] = bld64(r.v, off);
             if constexpr (DVAL) {
                 ys.o[it][h] = bld64(r.o, off);
@@ -422,6 +427,7 @@ struct WRows {
     bf16x8 hi[2], lo[2];
 };
 
+template <int D>
 __device__ __forceinline__ void load_wrows(const float *__restrict__ W, int LP, WRows &wr)
 {
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
@@ -430,7 +436,8 @@ __device__ __forceinline__ void load_wrows(const float *__restrict__ W, int LP, 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float v = hp < LP ? W[hp * HD + kb * 32 + g * 8 + i] : 0.f;
+            const int c = kb * 32 + g * 8 + i;
+            const float v = hp < LP && c < D ? W[hp * D + c] : 0.f;
             wr.hi[kb][i] = (bf16)v;
             wr.lo[kb][i] = (bf16)(v - (float)wr.hi[kb][i]);
         }
@@ -448,12 +455,12 @@ __device__ __forceinline__ bf16x8 selection(int par)
 }
 
 // W rows (hi, lo) of all waves staged once per workgroup, wl[2][NW * 16][XRS]
-template <int NW>
+template <int NW, int D>
 __device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int LP, bf16 *wl)
 {
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NW * 64) {
         const int hp = e / HD, c = e % HD;
-        const float v = hp < LP ? W[hp * HD + c] : 0.f;
+        const float v = hp < LP && c < D ? W[hp * D + c] : 0.f;
         const bf16 hi = (bf16)v;
         wl[hp * XRS + c] = hi;
         wl[(NW * 16 + hp) * XRS + c] = (bf16)(v - (float)hi);
@@ -680,7 +687,7 @@ __device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 //   SRC = 0: the rows X are hashed here; WR bit 0 / bit 1 store their t /
 //            dt/du' into the cache `co`.
 //   SRC = 1: t comes from the cache `ci_` (X is not read).
-template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO>
+template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, Squash sq,
     int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st)
@@ -698,18 +705,18 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const IO *Xs = X + row0 * HD;
+    const IO *Xs = X + row0 * D;
     ValSrc<IO> vh = vsrc;
-    vh.V += row0 * HD;
+    vh.V += row0 * D;
     if (DVAL) {
-        vh.O += row0 * HD;
+        vh.O += row0 * D;
         vh.den += row0;
     }
     const _Float16 *cin_t = HASH ? nullptr : ci_.t + hc_seg<NW>(ci_, bh, t_begin);
     _Float16 *cout_t = co.t ? co.t + hc_seg<NW>(co, bh, t_begin) : nullptr;
     _Float16 *cout_c = co.c ? co.c + hc_seg<NW>(co, bh, t_begin) : nullptr;
     WRows wr;
-    if (HASH) load_wrows(W, L * NP, wr);
+    if (HASH) load_wrows<D>(W, L * NP, wr);
     const bf16x8 sel[2] = {selection(0), selection(1)};
     const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
     floatx4 af[4][NT];
@@ -727,16 +734,16 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     ystage_zero_pad<NTHR>(ycol[0]);
     ystage_zero_pad<NTHR>(ycol[1]);
     const Chunk c0 = chunk(0), c1 = chunk(1);
-    ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c0), ys);
+    ystage_load<NTHR, DVAL, D>(yres<DVAL, D>(vh, c0), ys);
     if (HASH) {
-        xstage_load<NTHR>(row_res(Xs, c0), xs);
+        xstage_load<NTHR, false, D>(row_res<D>(Xs, c0), xs);
         xstage_store<NTHR, false, IO>(xs, xbuf[0], kbuf[0]);
     } else {
         hc_load<NW>(hc_res<NW>(cin_t, c0), tc);
     }
     ystage_store<NTHR, DVAL, IO>(ys, c0.nv, ycol[0]);
-    if (HASH) xstage_load<NTHR>(row_res(Xs, c1), xs);
-    ystage_load<NTHR, DVAL>(yres<DVAL>(vh, c1), ys);
+    if (HASH) xstage_load<NTHR, false, D>(row_res<D>(Xs, c1), xs);
+    ystage_load<NTHR, DVAL, D>(yres<DVAL, D>(vh, c1), ys);
     lds_barrier();
     for_chunks2(nch, [&](int ci, auto par) {
         constexpr int b = decltype(par)::v;
@@ -749,10 +756,10 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
         }
         const halfx4 tcur[2] = {tc[0], tc[1]};
         if (HASH)
-            xstage_load<NTHR>(row_res(Xs, chunk(ci + 2)), xs);
+            xstage_load<NTHR, false, D>(row_res<D>(Xs, chunk(ci + 2)), xs);
         else
             hc_load<NW>(hc_res<NW>(cin_t, chunk(ci + 1)), tc);
-        ystage_load<NTHR, DVAL>(yres<DVAL>(vh, chunk(ci + 2)), ys);
+        ystage_load<NTHR, DVAL, D>(yres<DVAL, D>(vh, chunk(ci + 2)), ys);
         if (!HASH) pin_loads();
         bf16x8 ptm[2][2], pfm[4];
         Rsrc rto, rco;
@@ -804,7 +811,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // One barrier per chunk: staging buffers and the partial outputs are double
 // buffered, and the partial outputs of chunk c are summed after the barrier
 // of chunk c + 1, beside that chunk's products.
-template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO>
+template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
@@ -830,21 +837,21 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const IO *Rs = R + row0 * HD;
+    const IO *Rs = R + row0 * D;
     ValSrc<IO> vh = vsrc;
-    vh.V += row0 * HD;
+    vh.V += row0 * D;
     if (BWD) {
-        vh.O += row0 * HD;
+        vh.O += row0 * D;
         vh.den += row0;
     }
-    IO *Os = Out + row0 * HD;
+    IO *Os = Out + row0 * D;
     float *dens = BWD ? nullptr : den + row0;
     const _Float16 *rt_seg = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
     const _Float16 *rc_seg = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
     WRows wr;  // the forward's W rows (hi, lo), kept in registers
-    if (HASH) stage_wrows<NW>(W, L * NP, reinterpret_cast<bf16 *>(red));
+    if (HASH) stage_wrows<NW, D>(W, L * NP, reinterpret_cast<bf16 *>(red));
     stage_sel(sl);
     __syncthreads();
     // red is next written after two more barriers
@@ -873,13 +880,13 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     if (CAUSAL) {
         ystage_zero_pad<NTHR>(ycol[0]);
         ystage_zero_pad<NTHR>(ycol[1]);
-        ystage_load<NTHR, BWD>(yres<BWD>(vh, c0), ys);
+        ystage_load<NTHR, BWD, D>(yres<BWD, D>(vh, c0), ys);
         hc_load<NW>(hc_res<NW>(wt_seg, c0), wt);
     }
     if (HASH) {
-        xstage_load<NTHR>(row_res(Rs, c0), xs);
+        xstage_load<NTHR, false, D>(row_res<D>(Rs, c0), xs);
         xstage_store<NTHR, false, IO>(xs, xbuf[0], kbuf[0]);
-        xstage_load<NTHR>(row_res(Rs, chunk(1)), xs);
+        xstage_load<NTHR, false, D>(row_res<D>(Rs, chunk(1)), xs);
     } else {
         hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     }
@@ -921,7 +928,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     auto finish = [&](int ci, int pb) {
         const Chunk c = chunk(ci);
         const float *rn = red + pb * (REDN + REDM), *rm = rn + REDN;
-        const Rsrc ro = row_res(Os, c);
+        const Rsrc ro = row_res<D>(Os, c);
 #pragma unroll
         for (int it = 0; it < RIT; ++it) {
             const int sl_ = threadIdx.x + it * NTHR;
@@ -933,7 +940,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 #pragma unroll
                 for (int ww = 1; ww < NW; ++ww)
                     n += *reinterpret_cast<const floatx4 *>(rn + (((ww * 2 + tt) * 4 + ct) * 64 + ln) * 4);
-                const int off = (tt * 16 + (ln & 15)) * (HD * 2) + (16 * ct + 4 * (ln >> 4)) * 2;
+                const int col = 16 * ct + 4 * (ln >> 4);  // columns past D are not stored
+                const int off = (D == HD || col < D) ? (tt * 16 + (ln & 15)) * (D * 2) + col * 2 : OOB;
                 if (BWD) {
                     bst64(u32x2{pk_io<IO>(n[0], n[1]), pk_io<IO>(n[2], n[3])}, ro, off);
                 } else {
@@ -953,7 +961,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
         if (CAUSAL) {
             ystage_store<NTHR, BWD, IO>(ys, cc.nv, ycol[b]);
-            ystage_load<NTHR, BWD>(yres<BWD>(vh, cn), ys);
+            ystage_load<NTHR, BWD, D>(yres<BWD, D>(vh, cn), ys);
         }
         bf16x8 pr[2][2];
         if constexpr (PIPE) {
@@ -969,7 +977,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         bf16x8 kA8;   // two-tile scores (fwd: reader tile 1, bwd: reader tile 0)
         if (HASH) {  // the next chunk's rows into the other buffer (last read before the previous barrier)
             if (ci + 1 < nch) xstage_store<NTHR, false, IO>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            xstage_load<NTHR>(row_res(Rs, chunk(ci + 2)), xs);
+            xstage_load<NTHR, false, D>(row_res<D>(Rs, chunk(ci + 2)), xs);
         }
         lds_barrier();  // value columns and next rows staged; partial outputs of chunk ci - 1 in LDS
         finish(ci - 1, b ^ 1);  // (none before the first chunk: its stores are dropped)
@@ -1081,7 +1089,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 // 64 dims] on MFMA (both operands read transposed from du and the staged
 // rows), summed in LDS, and the workgroup's sum written to dwp[workgroup]
 // ([NW * 16][64] fp32) for a reduction over segments.
-template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO>
+template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
     const float *__restrict__ W, int L, int64_t N, int seg, int64_t nseg,
@@ -1114,18 +1122,18 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
     const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
-    const IO *Rs = Xr + row0 * HD;
+    const IO *Rs = Xr + row0 * D;
     ValSrc<IO> vrh = vr_src, vwh = vw_src;
-    vrh.V += row0 * HD;
-    vwh.V += row0 * HD;
+    vrh.V += row0 * D;
+    vwh.V += row0 * D;
     if (RD) {
-        vrh.O += row0 * HD;
+        vrh.O += row0 * D;
         vrh.den += row0;
     } else {
-        vwh.O += row0 * HD;
+        vwh.O += row0 * D;
         vwh.den += row0;
     }
-    IO *dXs = dX + row0 * HD;
+    IO *dXs = dX + row0 * D;
     const _Float16 *rt_seg = rc.t + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
@@ -1138,7 +1146,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     // itself.
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
         const int hp = e / HD, c = e % HD;
-        wt_l[c * WTS + hp] = (bf16)(hp < L * NP ? W[hp * HD + c] : 0.f);
+        wt_l[c * WTS + hp] = (bf16)(hp < L * NP && c < D ? W[hp * D + c] : 0.f);
     }
     if constexpr (DW)
         for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) dwl[e] = 0.f;
@@ -1167,13 +1175,13 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         }
     }
     if (CAUSAL) {
-        ystage_load<NTHR, !RD>(yres<!RD>(vwh, c0), ysw);
+        ystage_load<NTHR, !RD, D>(yres<!RD, D>(vwh, c0), ysw);
         hc_load<NW>(hc_res<NW>(wt_seg, c0), wt);
     }
-    ystage_load<NTHR, RD>(yres<RD>(vrh, c0), ysr);
+    ystage_load<NTHR, RD, D>(yres<RD, D>(vrh, c0), ysr);
     hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     hc_load<NW>(hc_res<NW>(rc_seg, c0), rcv);
-    xstage_load<NTHR, true>(row_res(Rs, c0), xs);
+    xstage_load<NTHR, true, D>(row_res<D>(Rs, c0), xs);
 
     // dxh = du W of chunk ci (du in buffer pb) for this wave's tiles; the
     // partial dots with x go to dotp[pb], dxh, x and |x|^2 stay in registers
@@ -1230,7 +1238,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     // dots in dotp[pb]: dx = (dxh - x (x . dxh) / |x|^2) / |x| for
     // |x| > 1e-12, else dxh 1e12
     auto finish = [&](int ci, int pb) {
-        const Rsrc rdx = row_res(dXs, chunk(ci));
+        const Rsrc rdx = row_res<D>(dXs, chunk(ci));
 #pragma unroll
         for (int i = 0; i < TPWV; ++i) {
             const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
@@ -1247,7 +1255,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) rv[r] = (dxh[i][r] - coef * (float)xkeep[i][r]) * inv;
             const u32x2 v = {pk_io<IO>(rv[0], rv[1]), pk_io<IO>(rv[2], rv[3])};
-            bst64(v, rdx, tok * (HD * 2) + (nt * 16 + 4 * g) * 2);
+            const int col = nt * 16 + 4 * g;  // columns past D are not stored
+            bst64(v, rdx, (D == HD || col < D) ? tok * (D * 2) + col * 2 : OOB);
         }
     };
 
@@ -1260,8 +1269,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
         ystage_store<NTHR, RD, IO>(ysr, cc.nv, nullptr, yrow_r[b]);
         if (CAUSAL) ystage_store<NTHR, !RD, IO>(ysw, cc.nv, ycol_w[b], yrow_w[b]);
-        ystage_load<NTHR, RD>(yres<RD>(vrh, cn), ysr);
-        if (CAUSAL) ystage_load<NTHR, !RD>(yres<!RD>(vwh, cn), ysw);
+        ystage_load<NTHR, RD, D>(yres<RD, D>(vrh, cn), ysr);
+        if (CAUSAL) ystage_load<NTHR, !RD, D>(yres<!RD, D>(vwh, cn), ysw);
         const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
         hc_load<NW>(hc_res<NW>(rt_seg, cn), rt);
         hc_load<NW>(hc_res<NW>(rc_seg, cn), rcv);
@@ -1279,7 +1288,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
         // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
         xstage_store<NTHR, true, IO>(xs, xbuf[b], kbuf[b]);
-        xstage_load<NTHR, true>(row_res(Rs, cn), xs);
+        xstage_load<NTHR, true, D>(row_res<D>(Rs, cn), xs);
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][3];
 #pragma unroll
@@ -1395,7 +1404,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 // then the 8 group sums are added in group order (a fixed order, whatever the
 // launch).
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int64_t nparts,
-                                                        int rows, int LP, float *__restrict__ dW)
+                                                        int rows, int LP, int d, float *__restrict__ dW)
 {
     __shared__ float gs[8][32];
     const int grp = threadIdx.x >> 5, j = threadIdx.x & 31;
@@ -1411,7 +1420,8 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
         float t = gs[0][j];
 #pragma unroll
         for (int g2 = 1; g2 < 8; ++g2) t += gs[g2][j];
-        dW[e] = t;
+        // dW is [LP][d]: the columns past d of the blocks are zero padding
+        if (e % HD < d) dW[(e / HD) * d + e % HD] = t;
     }
 }
 

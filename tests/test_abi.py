@@ -86,12 +86,22 @@ def test_workspace_sizes(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
-    (dict(d=32), E_UNSUP), (dict(P=3), E_UNSUP), (dict(L=65), E_UNSUP),
+    (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
+    (dict(d=32, L=33), E_UNSUP), (dict(P=3), E_UNSUP), (dict(L=65), E_UNSUP),
     (dict(L=33, dt=F32), E_UNSUP), (dict(L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
     (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
 ])
 def test_workspace_validation(lib, kw, code):
     assert ws_bytes(lib, **kw)[0] == code
+
+
+def test_head_dim_32(lib):
+    # d = 32 runs the fused kernels with rows zero-padded on chip: the same
+    # workspace as d = 64 for 16-bit rows and L <= 32
+    for dt in (BF16, F16):
+        for bwd in (0, 1, 2):
+            st, b = ws_bytes(lib, d=32, L=32, dt=dt, bwd=bwd)
+            assert st == OK and b > 0 and (st, b) == ws_bytes(lib, d=64, L=32, dt=dt, bwd=bwd)
 
 
 def test_saved_bytes(lib):
@@ -272,7 +282,12 @@ def test_state_bytes(lib):
     assert L.race_attn_state_bytes(1, 1, 64, 5, 4, ctypes.byref(out)) == OK
     assert out.value == 80 * 65 * 4
     assert L.race_attn_state_bytes(1, 1, 64, 32, 4, None) == E_NULL
-    for args, code in (((0, 1, 64, 8, 4), E_SHAPE), ((1, 1, 32, 8, 4), E_UNSUP),
+    # any d <= 64: [16 L][d + 1]
+    assert L.race_attn_state_bytes(1, 2, 32, 8, 4, ctypes.byref(out)) == OK
+    assert out.value == 2 * 128 * 33 * 4
+    assert L.race_attn_state_bytes(1, 1, 1, 8, 4, ctypes.byref(out)) == OK and out.value == 128 * 2 * 4
+    for args, code in (((0, 1, 64, 8, 4), E_SHAPE), ((1, 1, 65, 8, 4), E_UNSUP),
+                       ((1, 1, 0, 8, 4), E_SHAPE),
                        ((1, 1, 64, 8, 3), E_UNSUP), ((1, 1, 64, 65, 4), E_UNSUP),
                        ((1, 1, 64, 0, 4), E_SHAPE), ((65536, 1, 64, 8, 4), E_UNSUP)):
         assert L.race_attn_state_bytes(*args, ctypes.byref(out)) == code, args
