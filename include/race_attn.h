@@ -37,9 +37,11 @@
  *     frees or synchronises, keeps no global mutable state and is safe to
  *     call from several threads.
  *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32 and
- *     RACE_F16); also d = 32 for RACE_BF16 and RACE_F16 with L <= 32 (the
+ *     RACE_F16); for RACE_BF16 and RACE_F16 with L <= 32 also d = 32 (the
  *     rows are zero-padded to 64 columns on chip: the same work per token as
- *     d = 64, half the memory traffic),
+ *     d = 64, half the memory traffic) and P = 1, 2, 3 (the kernels keep 4
+ *     hyperplanes per table with t = 0 on the padding ones, an exact
+ *     reduction to the P-plane corner product at the work of P = 4),
  *     any B, H, N >= 1 (int64 offsets), tau finite and > 0.
  *   - chunk: tokens per scan segment, 0 = the library chooses; otherwise a
  *     multiple of 16.  It changes only the order of the floating-point sums.

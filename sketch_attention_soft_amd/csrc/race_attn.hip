@@ -55,6 +55,7 @@ struct Plan {
     int64_t BH, N, rows;
     int L, nw, F, LP;
     int d;             // head dimension (64, or 32 on the fused path)
+    int P;             // hyperplanes per table (4, or 1..3 on the fused path)
     bool fused;        // bf16 and L <= 32: kernels hash their own rows
     int64_t seg, nseg;
     size_t st_bytes;   // one set of segment states (nseg + 1 per head)
@@ -80,13 +81,16 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     if (B < 1 || H < 1 || N < 1 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
-    if (P != race::NP) return RACE_ERR_UNSUPPORTED;
+    if (P > race::NP) return RACE_ERR_UNSUPPORTED;
     if (L > 64 || (dt != RACE_BF16 && L > 32)) return RACE_ERR_UNSUPPORTED;
-    // d = 64, or d = 32 on the fused path (16-bit rows, L <= 32)
-    if (d != race::HD && !(d == 32 && dt != RACE_F32 && L <= 32)) return RACE_ERR_UNSUPPORTED;
+    // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32)
+    const bool fusable = dt != RACE_F32 && L <= 32;
+    if (d != race::HD && !(d == 32 && fusable)) return RACE_ERR_UNSUPPORTED;
+    if (P != race::NP && !fusable) return RACE_ERR_UNSUPPORTED;
     if (chunk < 0 || chunk % race::CH != 0) return RACE_ERR_CHUNK;
     p->BH = (int64_t)B * H;
     p->d = d;
+    p->P = P;
     p->N = N;
     p->rows = p->BH * N;
     p->L = L;
@@ -331,10 +335,10 @@ void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squas
     if constexpr (sizeof(T) == 2) {
         if (SRC == 1 || sq.deg >= 0)
             LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T, D>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
+                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
         else
             LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T, D>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
+                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
     }
 }
 
@@ -347,10 +351,10 @@ void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squa
     if constexpr (sizeof(T) == 2) {
         if (RSRC == 1 || sq.deg >= 0)
             LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D>), grid,
-                   dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
+                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
         else
             LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D>), grid,
-                   dim3(NW * 64), R, vs, W, p.L, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
+                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
     }
 }
 
@@ -363,10 +367,10 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
     if constexpr (sizeof(T) == 2) {
         if (dwp)
             LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D>), grid, dim3(NW * 64), Xr,
-                   vr, vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp);
+                   vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp);
         else
             LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D>), grid, dim3(NW * 64), Xr, vr,
-                   vw, W, p.L, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr);
+                   vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr);
     }
 }
 
@@ -481,7 +485,7 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
                                            dwp ? dwp + dwb : nullptr);
         if (dW)
             LAUNCH(tr, "dw_reduce", race::dw_reduce_kernel, dim3((p.LP * race::HD + 31) / 32),
-                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, D, dW);
+                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, p.P, D, dW);
         launch_walk<WW, CAUSAL != 0, true, 1, 0, D>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV,
                                                  nullptr);
         return;

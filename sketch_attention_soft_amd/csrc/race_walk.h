@@ -422,13 +422,43 @@ template <int NTHR> __device__ __forceinline__ void yrow_zero_pad(bf16 *yr)
 }
 
 // ---------------------------------------------------------------------------
+// Hyperplanes per table P <= 4.  The kernels always work with 4 hyperplanes
+// (16 Walsh features) per table; for P < 4, hyperplanes p >= P are padding:
+// their W rows are zero and their t is +0 exactly, so every feature that
+// contains one vanishes on the writer side, and with writer features scaled by
+// 2^-P each table's kernel is prod_{p < P} (1 + t_p t'_p) / 2^P, the P-plane
+// corner product.  W is [L][P][d]: internal hyperplane 4 l + p <- row P l + p.
+__device__ __forceinline__ float w_elem(const float *__restrict__ W, int L, int P, int D, int hp, int c)
+{
+    const int l = hp >> 2, p = hp & 3;
+    return l < L && p < P && c < D ? W[(l * P + p) * D + c] : 0.f;
+}
+// masks of |t| for the fp16 pairs (p = 0, 1) and (2, 3): zero for padding
+// hyperplanes
+struct TMask {
+    uint32_t m[2];
+};
+__device__ __forceinline__ TMask t_mask(int P)
+{
+    TMask t;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        t.m[q] = (2 * q < P ? 0x7fffu : 0u) | (2 * q + 1 < P ? 0x7fff0000u : 0u);
+    return t;
+}
+// writer feature scale 2^-P (padding tables: 0)
+__device__ __forceinline__ float writer_scale(int P, bool table_in_use)
+{
+    return table_in_use ? __builtin_ldexpf(1.f, -P) : 0.f;
+}
+
 // W rows of this wave's 16 hyperplanes as the A operand of U^T = W x^T.
 struct WRows {
     bf16x8 hi[2], lo[2];
 };
 
 template <int D>
-__device__ __forceinline__ void load_wrows(const float *__restrict__ W, int LP, WRows &wr)
+__device__ __forceinline__ void load_wrows(const float *__restrict__ W, int L, int P, WRows &wr)
 {
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     const int hp = w * 16 + c16;
@@ -436,8 +466,7 @@ __device__ __forceinline__ void load_wrows(const float *__restrict__ W, int LP, 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = kb * 32 + g * 8 + i;
-            const float v = hp < LP && c < D ? W[hp * D + c] : 0.f;
+            const float v = w_elem(W, L, P, D, hp, kb * 32 + g * 8 + i);
             wr.hi[kb][i] = (bf16)v;
             wr.lo[kb][i] = (bf16)(v - (float)wr.hi[kb][i]);
         }
@@ -456,11 +485,11 @@ __device__ __forceinline__ bf16x8 selection(int par)
 
 // W rows (hi, lo) of all waves staged once per workgroup, wl[2][NW * 16][XRS]
 template <int NW, int D>
-__device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int LP, bf16 *wl)
+__device__ __forceinline__ void stage_wrows(const float *__restrict__ W, int L, int P, bf16 *wl)
 {
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NW * 64) {
         const int hp = e / HD, c = e % HD;
-        const float v = hp < LP && c < D ? W[hp * D + c] : 0.f;
+        const float v = w_elem(W, L, P, D, hp, c);
         const bf16 hi = (bf16)v;
         wl[hp * XRS + c] = hi;
         wl[(NW * 16 + hp) * XRS + c] = (bf16)(v - (float)hi);
@@ -498,6 +527,7 @@ __device__ __forceinline__ void sel_lds(const bf16 *sl, bf16x8 (&sel)[2])
 //         in fp16 pairs (two values per instruction); the sign of u is copied
 //         onto the pair's sign bits.
 //   else: the functions themselves in fp32.
+// Padding hyperplanes (tm) get t = +0.
 __device__ __forceinline__ half2v horner16(const uint32_t (&cf)[DEG16 + 1], half2v y)
 {
     half2v h = __builtin_bit_cast(half2v, cf[DEG16]);
@@ -514,7 +544,7 @@ __device__ __forceinline__ uint32_t sign_pair(float a, float b)
 
 template <bool POLY, bool CHAIN>
 __device__ __forceinline__ void hash_staged(const bf16 *xb, const float *kb, int tt, const WRows &wr,
-                                            const Squash &sq, halfx4 &t, halfx4 &c)
+                                            const Squash &sq, const TMask &tm, halfx4 &t, halfx4 &c)
 {
     const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
     const int row = tt * 16 + c16;
@@ -534,7 +564,7 @@ __device__ __forceinline__ void hash_staged(const bf16 *xb, const float *kb, int
             const float e1 = __builtin_amdgcn_exp2f(fabsf(u[2 * q + 1]) * kf);
             const half2v y = {(_Float16)fmaf(2.f, e0, -1.f), (_Float16)fmaf(2.f, e1, -1.f)};
             const uint32_t h = __builtin_bit_cast(uint32_t, horner16(sq.t16, y));
-            tp[q] = (h & 0x7fff7fffu) | sign_pair(u[2 * q], u[2 * q + 1]);
+            tp[q] = (h & tm.m[q]) | sign_pair(u[2 * q], u[2 * q + 1]);  // padding: +0
             if constexpr (CHAIN) cp[q] = __builtin_bit_cast(uint32_t, horner16(sq.c16, y));
         }
         const u32x2 tv = {tp[0], tp[1]};
@@ -551,7 +581,7 @@ __device__ __forceinline__ void hash_staged(const bf16 *xb, const float *kb, int
             const float z = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
             const float e2 = __builtin_amdgcn_exp2f(-2.8853900817779268f * z * sq.inv_tau);
             const float h = (1.f - e2) * __builtin_amdgcn_rcpf(1.f + e2);
-            tf[p] = copysignf(h, u[p]);
+            tf[p] = (tm.m[p >> 1] >> (16 * (p & 1))) & 1u ? copysignf(h, u[p]) : 0.f;
             if constexpr (CHAIN) {
                 const float r = __builtin_amdgcn_rcpf(1.f + e);
                 cf[p] = (1.f - h * h) * (4.f * sq.inv_tau) * e * r * r;
@@ -563,10 +593,10 @@ __device__ __forceinline__ void hash_staged(const bf16 *xb, const float *kb, int
 }
 
 // token-major Walsh features of one table, q prod_{p in S} t_p: lo = S 0..7,
-// hi = S 8..15.  The features are 1/4 prod t_p; the kernels form reader
-// features with q = 1 and writer features with q = 1/16 (0 for padding
-// tables), which gives every score and state product its factor 1/16 exactly
-// (powers of two) and saves the reader side four products.
+// hi = S 8..15.  The features are 2^(-P/2) prod t_p (1/4 for P = 4); the
+// kernels form reader features with q = 1 and writer features with q = 2^-P
+// (0 for padding tables), which gives every score and state product its
+// factor 2^-P exactly (powers of two) and saves the reader side four products.
 __device__ __forceinline__ void walsh_tm(const floatx4 &t, float q, bf16x8 &lo, bf16x8 &hi)
 {
     const float a1 = q * t[0], a2 = q * t[1], a3 = a1 * t[1], b3 = t[2] * t[3];
@@ -689,7 +719,7 @@ __device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 //   SRC = 1: t comes from the cache `ci_` (X is not read).
 template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void sum_kernel(
-    const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, Squash sq,
+    const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st)
 {
     constexpr int NTHR = NW * 64;
@@ -716,9 +746,10 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     _Float16 *cout_t = co.t ? co.t + hc_seg<NW>(co, bh, t_begin) : nullptr;
     _Float16 *cout_c = co.c ? co.c + hc_seg<NW>(co, bh, t_begin) : nullptr;
     WRows wr;
-    if (HASH) load_wrows<D>(W, L * NP, wr);
+    if (HASH) load_wrows<D>(W, L, P, wr);
+    const TMask tm = t_mask(P);
     const bf16x8 sel[2] = {selection(0), selection(1)};
-    const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
+    const float qw = writer_scale(P, 4 * w + g < L);  // writer features: 2^-P, padding 0
     floatx4 af[4][NT];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -770,7 +801,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
             halfx4 t;
             if constexpr (HASH) {
                 halfx4 c;
-                hash_staged<POLY, (WR & 2) != 0>(xbuf[b], kbuf[b], tt, wr, sq, t, c);
+                hash_staged<POLY, (WR & 2) != 0>(xbuf[b], kbuf[b], tt, wr, sq, tm, t, c);
                 if constexpr ((WR & 2) != 0) hc_store<NW>(rco, tt, c);
                 if constexpr ((WR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
@@ -813,7 +844,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // of chunk c + 1, beside that chunk's products.
 template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
-    const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, Squash sq,
+    const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
     IO *__restrict__ Out, float *__restrict__ den)
 {
@@ -851,12 +882,13 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
 
     WRows wr;  // the forward's W rows (hi, lo), kept in registers
-    if (HASH) stage_wrows<NW, D>(W, L * NP, reinterpret_cast<bf16 *>(red));
+    if (HASH) stage_wrows<NW, D>(W, L, P, reinterpret_cast<bf16 *>(red));
+    const TMask tm = t_mask(P);
     stage_sel(sl);
     __syncthreads();
     // red is next written after two more barriers
     if (HASH) wrows_lds<NW>(reinterpret_cast<const bf16 *>(red), wr);
-    const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
+    const float qw = writer_scale(P, 4 * w + g < L);  // writer features: 2^-P, padding 0
     floatx4 acc[4][NT];
     {
         const float *src = st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL);
@@ -905,7 +937,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             halfx4 t;
             if constexpr (HASH) {
                 halfx4 cd;
-                hash_staged<POLY, (RWR & 2) != 0>(xb, kb, tt, wr, sq, t, cd);
+                hash_staged<POLY, (RWR & 2) != 0>(xb, kb, tt, wr, sq, tm, t, cd);
                 if constexpr ((RWR & 2) != 0) hc_store<NW>(rco, tt, cd);
                 if constexpr ((RWR & 1) != 0) hc_store<NW>(rto, tt, t);
             } else {
@@ -1092,7 +1124,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
-    const float *__restrict__ W, int L, int64_t N, int seg, int64_t nseg,
+    const float *__restrict__ W, int L, int P, int64_t N, int seg, int64_t nseg,
     const float *__restrict__ st, HCache rc, HCache wc, IO *__restrict__ dX,
     float *__restrict__ dwp)
 {
@@ -1140,18 +1172,21 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 
     // W^T and the selection operands, once per workgroup.  dxh = du W takes W
     // in bf16, the precision of du itself (the forward projection keeps W to
-    // about 16 bits as bf16 hi + lo).  With writer features scaled by 1/16 and
+    // about 16 bits as bf16 hi + lo).  With writer features scaled by 2^-P and
     // reader features by 1, the products below give the gradient with respect
     // to the unscaled reader features prod t_p, so that walsh_grad yields dt
     // itself.
     for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
         const int hp = e / HD, c = e % HD;
-        wt_l[c * WTS + hp] = (bf16)(hp < L * NP && c < D ? W[hp * D + c] : 0.f);
+        wt_l[c * WTS + hp] = (bf16)w_elem(W, L, P, D, hp, c);
     }
     if constexpr (DW)
         for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) dwl[e] = 0.f;
     stage_sel(sl);
-    const float qw = (4 * w + g < L) ? 0.0625f : 0.f;  // writer features: 1/16, padding 0
+    // the selection operands are read in the first chunk before its barrier
+    // (and a wave whose W rows are all padding reaches that read early)
+    __syncthreads();
+    const float qw = writer_scale(P, 4 * w + g < L);  // writer features: 2^-P, padding 0
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
 
@@ -1404,7 +1439,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 // then the 8 group sums are added in group order (a fixed order, whatever the
 // launch).
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int64_t nparts,
-                                                        int rows, int LP, int d, float *__restrict__ dW)
+                                                        int rows, int LP, int P, int d,
+                                                        float *__restrict__ dW)
 {
     __shared__ float gs[8][32];
     const int grp = threadIdx.x >> 5, j = threadIdx.x & 31;
@@ -1420,8 +1456,10 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
         float t = gs[0][j];
 #pragma unroll
         for (int g2 = 1; g2 < 8; ++g2) t += gs[g2][j];
-        // dW is [LP][d]: the columns past d of the blocks are zero padding
-        if (e % HD < d) dW[(e / HD) * d + e % HD] = t;
+        // dW is [L][P][d]: padding hyperplanes (p >= P) and columns past d of
+        // the blocks are dropped
+        const int hp = e / HD, c = e % HD;
+        if ((hp & 3) < P && c < d) dW[((hp >> 2) * P + (hp & 3)) * d + c] = t;
     }
 }
 

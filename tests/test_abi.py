@@ -87,12 +87,23 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
     (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
-    (dict(d=32, L=33), E_UNSUP), (dict(P=3), E_UNSUP), (dict(L=65), E_UNSUP),
+    (dict(d=32, L=33), E_UNSUP), (dict(P=5), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
+    (dict(P=2, L=33), E_UNSUP), (dict(P=0), E_SHAPE), (dict(L=65), E_UNSUP),
     (dict(L=33, dt=F32), E_UNSUP), (dict(L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
     (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
 ])
 def test_workspace_validation(lib, kw, code):
     assert ws_bytes(lib, **kw)[0] == code
+
+
+def test_fewer_hyperplanes(lib):
+    # P = 1..3 run the fused kernels with padding hyperplanes: the same
+    # workspace as P = 4 for 16-bit rows and L <= 32
+    for P in (1, 2, 3):
+        for dt in (BF16, F16):
+            for bwd in (0, 1, 2):
+                st, b = ws_bytes(lib, P=P, L=32, dt=dt, bwd=bwd)
+                assert st == OK and (st, b) == ws_bytes(lib, P=4, L=32, dt=dt, bwd=bwd)
 
 
 def test_head_dim_32(lib):
@@ -364,6 +375,6 @@ def test_forward_hard_validation(lib):
     fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, sz, vp]
     F = FAKE
     assert fn(None, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_NULL
-    assert fn(F, F, F, F, 8, 3, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
+    assert fn(F, F, F, F, 8, 5, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
     assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 17, F, F, F, 1 << 30, None) == E_CHUNK
     assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F * 16, 16, None) == E_WS
