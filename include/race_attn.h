@@ -122,6 +122,27 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
                                  race_dtype_t dt, int chunk, void *dQ, void *dK, void *dV,
                                  void *workspace, size_t ws_bytes, void *stream);
 
+/* Right-padded batches: batch b holds seqlens[b] rows (0 <= seqlens[b] <= N
+ * after clamping) followed by padding.  Each sequence is attended on its own
+ * rows only (causal or not), as if it had been passed alone with N =
+ * seqlens[b]; padding rows are never read and their outputs (O, den; dQ, dK,
+ * dV) are left as they are, so padding costs no work.  seqlens: device
+ * pointer, int32 [B], read by the kernels.  Otherwise as race_attn_forward /
+ * race_attn_backward; the backward also writes dW when dW is not NULL (as
+ * race_attn_backward_dw: RACE_BF16 / RACE_F16, L <= 32, workspace with
+ * for_backward = 2).  No saved state. */
+race_status_t race_attn_forward_padded(const void *Q, const void *K, const void *V,
+                                       const float *W, int L, int P, float tau, int causal, int B,
+                                       int H, int64_t N, int d, race_dtype_t dt, int chunk,
+                                       const int *seqlens, void *O, float *den, void *workspace,
+                                       size_t ws_bytes, void *stream);
+race_status_t race_attn_backward_padded(const void *Q, const void *K, const void *V,
+                                        const float *W, const void *O, const float *den,
+                                        const void *dO, int L, int P, float tau, int causal, int B,
+                                        int H, int64_t N, int d, race_dtype_t dt, int chunk,
+                                        const int *seqlens, void *dQ, void *dK, void *dV,
+                                        float *dW, void *workspace, size_t ws_bytes, void *stream);
+
 /* Per-kernel timing for the *_ex entry points.  The caller creates the HIP
  * events (hipEventCreate, timing enabled) and owns them; the library records
  * start[i] / stop[i] on the call's stream around the i-th kernel it enqueues

@@ -21,7 +21,8 @@ STATUS = {
 }
 EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forward",
            "race_attn_backward", "race_attn_forward_ex", "race_attn_backward_ex",
-           "race_attn_backward_dw", "race_attn_forward_hard",
+           "race_attn_backward_dw", "race_attn_forward_hard", "race_attn_forward_padded",
+           "race_attn_backward_padded",
            "race_attn_squash_coeffs", "race_attn_squash_deriv_coeffs",
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
            "race_attn_decode", "race_attn_state_readout", "race_attn_status_string")
@@ -96,6 +97,13 @@ def lib():
         L.race_attn_backward_dw.argtypes = (L.race_attn_backward.argtypes[:20] + [vp]
                                             + L.race_attn_backward.argtypes[20:] + [vp, tp])
         L.race_attn_backward_dw.restype = i32
+        L.race_attn_forward_padded.argtypes = (L.race_attn_forward.argtypes[:14] + [vp]
+                                               + L.race_attn_forward.argtypes[14:])
+        L.race_attn_forward_padded.restype = i32
+        L.race_attn_backward_padded.argtypes = (L.race_attn_backward.argtypes[:17] + [vp]
+                                                + L.race_attn_backward.argtypes[17:20] + [vp]
+                                                + L.race_attn_backward.argtypes[20:])
+        L.race_attn_backward_padded.restype = i32
         L.race_attn_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_state_bytes.restype = i32
         L.race_attn_state_add_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32,
@@ -260,6 +268,55 @@ def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, w
                                        workspace.data_ptr(), workspace.numel(), _stream(),
                                        _ptr(saved), _tp(trace)))
     return dq, dk, dv
+
+
+def _check_lens(seqlens, q):
+    B = q.shape[0]
+    if (seqlens.dtype != torch.int32 or seqlens.shape != (B,) or not seqlens.is_contiguous()
+            or seqlens.device != q.device):
+        raise ValueError("seqlens must be a contiguous int32 [B] tensor on the same device")
+
+
+def forward_padded(q, k, v, W, seqlens, tau: float, causal: bool, chunk: int = 0,
+                   workspace=None):
+    """Forward over right-padded batches: batch b has seqlens[b] rows.  Returns
+    (o, den) with zeros on the padding rows."""
+    B, H, N, d = _shape(q)
+    _check_tensors(q, k, v)
+    L, P = _check_w(W, q)
+    _check_lens(seqlens, q)
+    o = torch.zeros_like(q)
+    den = torch.zeros((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().race_attn_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
+                                          L, P, float(tau), int(causal), B, H, N, d,
+                                          dtype_code(q.dtype), chunk, seqlens.data_ptr(),
+                                          o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream()))
+    return o, den
+
+
+def backward_padded(q, k, v, W, o, den, do, seqlens, tau: float, causal: bool, chunk: int = 0,
+                    workspace=None, dw: bool = False):
+    """Backward over right-padded batches; returns (dq, dk, dv) with zeros on
+    the padding rows, and dW last with dw=True."""
+    B, H, N, d = _shape(q)
+    _check_tensors(q, k, v, o, do)
+    L, P = _check_w(W, q)
+    _check_lens(seqlens, q)
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    gW = torch.empty_like(W) if dw else None
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, 2 if dw else 1)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().race_attn_backward_padded(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), o.data_ptr(), den.data_ptr(),
+        do.data_ptr(), L, P, float(tau), int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
+        seqlens.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(gW),
+        workspace.data_ptr(), workspace.numel(), _stream()))
+    return (dq, dk, dv, gW) if dw else (dq, dk, dv)
 
 
 class RaceAttention(torch.autograd.Function):

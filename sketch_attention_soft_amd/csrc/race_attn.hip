@@ -56,6 +56,7 @@ struct Plan {
     int L, nw, F, LP;
     int d;             // head dimension (64, or 32 on the fused path)
     int P;             // hyperplanes per table (4, or 1..3 on the fused path)
+    race::Lens lens;   // per-batch valid rows (right-padded batches), or none
     bool fused;        // bf16 and L <= 32: kernels hash their own rows
     int64_t seg, nseg;
     size_t st_bytes;   // one set of segment states (nseg + 1 per head)
@@ -91,6 +92,7 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->BH = (int64_t)B * H;
     p->d = d;
     p->P = P;
+    p->lens = race::Lens{nullptr, H};
     p->N = N;
     p->rows = p->BH * N;
     p->L = L;
@@ -335,10 +337,10 @@ void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squas
     if constexpr (sizeof(T) == 2) {
         if (SRC == 1 || sq.deg >= 0)
             LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T, D>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
+                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st, p.lens);
         else
             LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T, D>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st);
+                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st, p.lens);
     }
 }
 
@@ -351,10 +353,10 @@ void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squa
     if constexpr (sizeof(T) == 2) {
         if (RSRC == 1 || sq.deg >= 0)
             LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D>), grid,
-                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
+                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den, p.lens);
         else
             LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D>), grid,
-                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den);
+                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den, p.lens);
     }
 }
 
@@ -367,10 +369,10 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
     if constexpr (sizeof(T) == 2) {
         if (dwp)
             LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D>), grid, dim3(NW * 64), Xr,
-                   vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp);
+                   vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp, p.lens);
         else
             LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D>), grid, dim3(NW * 64), Xr, vr,
-                   vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr);
+                   vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr, p.lens);
     }
 }
 
@@ -423,14 +425,14 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     const race::ValSrc<T> vs{V, nullptr, nullptr};
     const dim3 nblk((unsigned)(p.BH * p.nseg));
     LAUNCH(tr, "seg_sum_kv", (race::seg_sum_kernel<T, NW, false, false>), nblk, bw, tk, race::NP,
-           vs, p.N, p.L, (int)p.seg, p.nseg, st);
+           vs, p.N, p.L, (int)p.seg, p.nseg, st, p.lens);
     launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
     if (causal)
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, true, false>), nblk, bw, tq, tk,
-               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
+               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens);
     else
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, false, false>), nblk, bw, tq, tk,
-               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den);
+               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens);
     }
 }
 
@@ -503,24 +505,24 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     const int ts = 2 * race::NP;
     // key-side state S (CxF, for dQ): prefix over segments
     LAUNCH(tr, "seg_sum_kv_t", (race::seg_sum_kernel<T, NW, true, false>), nblk, bw, tk, ts, vv,
-           p.N, p.L, (int)p.seg, p.nseg, sS);
+           p.N, p.L, (int)p.seg, p.nseg, sS, p.lens);
     launch_scan(tr, "scan_kv_t", p, sS, scan_tmp, 0);
     // query-side gradient states G (CxF for dK, FxC for dV): suffix over segments
     LAUNCH(tr, "seg_sum_qd_t", (race::seg_sum_kernel<T, NW, true, true>), nblk, bw, tq, ts, vd,
-           p.N, p.L, (int)p.seg, p.nseg, sGt);
+           p.N, p.L, (int)p.seg, p.nseg, sGt, p.lens);
     launch_scan(tr, "scan_qd_t", p, sGt, scan_tmp, 1);
     LAUNCH(tr, "seg_sum_qd", (race::seg_sum_kernel<T, NW, false, true>), nblk, bw, tq, ts, vd,
-           p.N, p.L, (int)p.seg, p.nseg, sG);
+           p.N, p.L, (int)p.seg, p.nseg, sG, p.lens);
     launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
     // dQ: readers Q (values D), writers K (values [v|1]), token order
     LAUNCH(tr, "dpsi_q", (race::dpsi_kernel<T, NW, CAUSAL, false, true>), nblk, bw, Q, tq, tk, vd,
-           vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ);
+           vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ, p.lens);
     // dK: readers K (values [v|1]), writers Q (values D), reverse order
     LAUNCH(tr, "dpsi_k", (race::dpsi_kernel<T, NW, CAUSAL, true, false>), nblk, bw, K, tk, tq, vv,
-           vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK);
+           vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK, p.lens);
     // dV: keys read the FxC gradient state, reverse order
     LAUNCH(tr, "readout_dv", (race::readout_kernel<T, NW, CAUSAL != 0, true>), nblk, bw, tk, tq,
-           ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr);
+           ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr, p.lens);
     }
 }
 
@@ -694,11 +696,13 @@ race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P
     return RACE_OK;
 }
 
-race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, const float *W,
-                                   int L, int P, float tau, int causal, int B, int H, int64_t N,
-                                   int d, race_dtype_t dt, int chunk, void *O, float *den,
-                                   void *workspace, size_t ws_bytes, void *stream, void *saved,
-                                   race_trace_t *trace)
+// forward / backward of every variant; lens: per-batch valid rows (device
+// int32 [B]) or NULL; dW: the projection gradient (fused path) or NULL
+static race_status_t forward_impl(const void *Q, const void *K, const void *V, const float *W,
+                                  int L, int P, float tau, int causal, int B, int H, int64_t N,
+                                  int d, race_dtype_t dt, int chunk, void *O, float *den,
+                                  void *workspace, size_t ws_bytes, void *stream, void *saved,
+                                  race_trace_t *trace, const int *lens)
 {
     if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
     Plan p;
@@ -708,6 +712,7 @@ race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, 
     if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
     if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
+    p.lens.len = lens;
     float *sv = p.fused ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
@@ -719,6 +724,58 @@ race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, 
     else
         dispatch_forward<float>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+static race_status_t backward_impl(const void *Q, const void *K, const void *V, const float *W,
+                                   const void *O, const float *den, const void *dO, int L, int P,
+                                   float tau, int causal, int B, int H, int64_t N, int d,
+                                   race_dtype_t dt, int chunk, void *dQ, void *dK, void *dV,
+                                   float *dW, void *workspace, size_t ws_bytes, void *stream,
+                                   const void *saved, race_trace_t *trace, const int *lens)
+{
+    if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !workspace)
+        return RACE_ERR_NULL;
+    Plan p;
+    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    if (st != RACE_OK) return st;
+    if (dW && !p.fused) return RACE_ERR_UNSUPPORTED;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if ((st = check_ws(p, dW ? p.dw_total : p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
+    if ((st = check_trace(trace)) != RACE_OK) return st;
+    if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
+    p.lens.len = lens;
+    const float *sv = p.fused ? static_cast<const float *>(saved) : nullptr;
+    const Tracer tr{trace, static_cast<hipStream_t>(stream)};
+    (void)hipGetLastError();
+    char *ws = static_cast<char *>(workspace);
+    if (dt == RACE_BF16)
+        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
+    else if (dt == RACE_F16)
+        dispatch_backward<_Float16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
+    else
+        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_forward_ex(const void *Q, const void *K, const void *V, const float *W,
+                                   int L, int P, float tau, int causal, int B, int H, int64_t N,
+                                   int d, race_dtype_t dt, int chunk, void *O, float *den,
+                                   void *workspace, size_t ws_bytes, void *stream, void *saved,
+                                   race_trace_t *trace)
+{
+    return forward_impl(Q, K, V, W, L, P, tau, causal, B, H, N, d, dt, chunk, O, den, workspace,
+                        ws_bytes, stream, saved, trace, nullptr);
+}
+
+race_status_t race_attn_forward_padded(const void *Q, const void *K, const void *V,
+                                       const float *W, int L, int P, float tau, int causal, int B,
+                                       int H, int64_t N, int d, race_dtype_t dt, int chunk,
+                                       const int *seqlens, void *O, float *den, void *workspace,
+                                       size_t ws_bytes, void *stream)
+{
+    if (!seqlens) return RACE_ERR_NULL;
+    return forward_impl(Q, K, V, W, L, P, tau, causal, B, H, N, d, dt, chunk, O, den, workspace,
+                        ws_bytes, stream, nullptr, nullptr, seqlens);
 }
 
 race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
@@ -759,26 +816,8 @@ race_status_t race_attn_backward_ex(const void *Q, const void *K, const void *V,
                                     void *dK, void *dV, void *workspace, size_t ws_bytes,
                                     void *stream, const void *saved, race_trace_t *trace)
 {
-    if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !workspace)
-        return RACE_ERR_NULL;
-    Plan p;
-    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
-    if (st != RACE_OK) return st;
-    if ((st = check_tau(tau)) != RACE_OK) return st;
-    if ((st = check_ws(p, p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
-    if ((st = check_trace(trace)) != RACE_OK) return st;
-    if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
-    const float *sv = p.fused ? static_cast<const float *>(saved) : nullptr;
-    const Tracer tr{trace, static_cast<hipStream_t>(stream)};
-    (void)hipGetLastError();
-    char *ws = static_cast<char *>(workspace);
-    if (dt == RACE_BF16)
-        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
-    else if (dt == RACE_F16)
-        dispatch_backward<_Float16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
-    else
-        dispatch_backward<float>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, nullptr);
-    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+    return backward_impl(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk, dQ, dK,
+                         dV, nullptr, workspace, ws_bytes, stream, saved, trace, nullptr);
 }
 
 race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
@@ -789,25 +828,21 @@ race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
                                     size_t ws_bytes, void *stream, const void *saved,
                                     race_trace_t *trace)
 {
-    if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !dW || !workspace)
-        return RACE_ERR_NULL;
-    Plan p;
-    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
-    if (st != RACE_OK) return st;
-    if (!p.fused) return RACE_ERR_UNSUPPORTED;
-    if ((st = check_tau(tau)) != RACE_OK) return st;
-    if ((st = check_ws(p, p.dw_total, workspace, ws_bytes)) != RACE_OK) return st;
-    if ((st = check_trace(trace)) != RACE_OK) return st;
-    if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
-    const Tracer tr{trace, static_cast<hipStream_t>(stream)};
-    (void)hipGetLastError();
-    char *ws = static_cast<char *>(workspace);
-    const float *sv = static_cast<const float *>(saved);
-    if (dt == RACE_F16)
-        dispatch_backward<_Float16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
-    else
-        dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
-    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+    if (!dW) return RACE_ERR_NULL;
+    return backward_impl(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk, dQ, dK,
+                         dV, dW, workspace, ws_bytes, stream, saved, trace, nullptr);
+}
+
+race_status_t race_attn_backward_padded(const void *Q, const void *K, const void *V,
+                                        const float *W, const void *O, const float *den,
+                                        const void *dO, int L, int P, float tau, int causal, int B,
+                                        int H, int64_t N, int d, race_dtype_t dt, int chunk,
+                                        const int *seqlens, void *dQ, void *dK, void *dV,
+                                        float *dW, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!seqlens) return RACE_ERR_NULL;
+    return backward_impl(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk, dQ, dK,
+                         dV, dW, workspace, ws_bytes, stream, nullptr, nullptr, seqlens);
 }
 
 race_status_t race_attn_backward(const void *Q, const void *K, const void *V, const float *W,

@@ -50,7 +50,7 @@ template <typename T, int NW, int CAUSAL, bool REVERSE, bool READER_D>
 __global__ __launch_bounds__(NW * 64) void dpsi_kernel(
     const T *__restrict__ X, const float *__restrict__ tr, const float *__restrict__ tw,
     ValSrc<T> vr_src, ValSrc<T> vw_src, const char *__restrict__ wt, int lp32, int64_t N, int L,
-    int seg, int64_t nseg, const float *__restrict__ st, T *__restrict__ dX)
+    int seg, int64_t nseg, const float *__restrict__ st, T *__restrict__ dX, Lens ls)
 {
     constexpr int F = NW * FPW;
     constexpr int TS = 2 * NP;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NW * 64) void dpsi_kernel(
             for (int ct = 0; ct < NT; ++ct)
                 acc[ct][ft] = *reinterpret_cast<const floatx4 *>(src + st_index(w, ft, ct, lane));
     }
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(valid_rows(ls, bh, N), t_begin + seg);
     const int64_t nch = (t_end - t_begin + CH - 1) / CH;
     for (int64_t ci = 0; ci < nch; ++ci) {
         const int64_t tok0 = t_begin + (REVERSE ? nch - 1 - ci : ci) * CH;

@@ -147,6 +147,20 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Rows of head bh that exist: N, or for right-padded batches the length of
+// its batch, len[bh / H] clamped to [0, N] (rows past it are neither read nor
+// written: the sums skip them and their outputs are left as they are).
+struct Lens {
+    const int *len;
+    int H;
+};
+__device__ __forceinline__ int64_t valid_rows(const Lens &ls, int64_t bh, int64_t N)
+{
+    if (!ls.len) return N;
+    const int64_t n = ls.len[bh / ls.H];
+    return n < 0 ? 0 : n < N ? n : N;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

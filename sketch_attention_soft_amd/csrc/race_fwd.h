@@ -285,7 +285,7 @@ template <typename T, int NW, bool CXF, bool DVAL>
 __global__ __launch_bounds__(NW * 64) void seg_sum_kernel(const float *__restrict__ t, int ts,
                                                           ValSrc<T> vs, int64_t N, int L,
                                                           int seg, int64_t nseg,
-                                                          float *__restrict__ st)
+                                                          float *__restrict__ st, Lens ls)
 {
     __shared__ __attribute__((aligned(16))) T pt[NW * FPW * CH];
     __shared__ __attribute__((aligned(16))) T vt[NCOL * CH];
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(NW * 64) void seg_sum_kernel(const float *__restric
     for (int a = 0; a < MT; ++a)
 #pragma unroll
         for (int b = 0; b < NT; ++b) acc[a][b] = {0.f, 0.f, 0.f, 0.f};
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(valid_rows(ls, bh, N), t_begin + seg);
     for (int64_t tok0 = t_begin; tok0 < t_end; tok0 += CH) {
         __syncthreads();
         load_vals<T, DVAL>(vh, tok0, t_end, vt, nullptr);
@@ -411,7 +411,7 @@ template <typename T, int NW, bool CAUSAL, bool BWD>
 __global__ __launch_bounds__(NW * 64) void readout_kernel(
     const float *__restrict__ tr, const float *__restrict__ tw, int ts, ValSrc<T> vs, int64_t N,
     int L, int seg, int64_t nseg, const float *__restrict__ st, T *__restrict__ Out,
-    float *__restrict__ den)
+    float *__restrict__ den, Lens ls)
 {
     constexpr int F = NW * FPW;
     __shared__ __attribute__((aligned(16))) T pr[CH * F];
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(
             for (int nt = 0; nt < NT; ++nt)
                 acc[mt][nt] = *reinterpret_cast<const floatx4 *>(src + st_index(w, mt, nt, lane));
     }
-    const int64_t t_begin = sg * seg, t_end = min<int64_t>(N, t_begin + seg);
+    const int64_t t_begin = sg * seg, t_end = min<int64_t>(valid_rows(ls, bh, N), t_begin + seg);
     const int64_t nch = (t_end - t_begin + CH - 1) / CH;
     for (int64_t ci = 0; ci < nch; ++ci) {
         const int64_t tok0 = t_begin + (BWD ? nch - 1 - ci : ci) * CH;

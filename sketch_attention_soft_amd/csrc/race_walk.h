@@ -720,7 +720,7 @@ __device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
-    int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st)
+    int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st, Lens ls)
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = SRC == 0;
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const int lane = lane_id(), w = wave_id(), g = lane >> 4;
     // segment-relative row pointers; chunk positions go into buffer resources
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
-    const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
+    const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
     const IO *Xs = X + row0 * D;
     ValSrc<IO> vh = vsrc;
@@ -846,7 +846,7 @@ template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename 
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
-    IO *__restrict__ Out, float *__restrict__ den)
+    IO *__restrict__ Out, float *__restrict__ den, Lens ls)
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = RSRC == 0;
@@ -866,7 +866,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     // segment-relative row pointers; chunk positions go into buffer resources
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
-    const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
+    const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
     const IO *Rs = R + row0 * D;
     ValSrc<IO> vh = vsrc;
@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
     const float *__restrict__ W, int L, int P, int64_t N, int seg, int64_t nseg,
     const float *__restrict__ st, HCache rc, HCache wc, IO *__restrict__ dX,
-    float *__restrict__ dwp)
+    float *__restrict__ dwp, Lens ls)
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
     constexpr int NTHR = NW * 64;
@@ -1152,7 +1152,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     // segment-relative row pointers; chunk positions go into buffer resources
     const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
-    const int tend = (int)(min<int64_t>(N, t_begin + seg) - t_begin);
+    const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
     const IO *Rs = Xr + row0 * D;
     ValSrc<IO> vrh = vr_src, vwh = vw_src;

@@ -378,3 +378,41 @@ def test_forward_hard_validation(lib):
     assert fn(F, F, F, F, 8, 5, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
     assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 17, F, F, F, 1 << 30, None) == E_CHUNK
     assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F * 16, 16, None) == E_WS
+
+
+def test_padded_validation(lib):
+    i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    F = FAKE
+    fwd = lib.race_attn_forward_padded
+    fwd.argtypes = [vp] * 4 + [i32, i32, f32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, vp,
+                               sz, vp]
+    args = [F] * 4 + [8, 4, 1.0, 0, 2, 1, 1024, 64, BF16, 0, F, F, F, F * 16, 1 << 40, None]
+    bad = list(args)
+    bad[14] = None  # seqlens
+    assert fwd(*bad) == E_NULL
+    bad = list(args)
+    bad[6] = 0.0  # tau
+    assert fwd(*bad) == E_TAU
+    bad = list(args)
+    bad[18] = 16  # workspace too small
+    assert fwd(*bad) == E_WS
+    bwd = lib.race_attn_backward_padded
+    bwd.argtypes = [vp] * 7 + [i32, i32, f32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, vp,
+                               vp, vp, sz, vp]
+    args = [F] * 7 + [8, 4, 1.0, 0, 2, 1, 1024, 64, BF16, 0, F, F, F, F, F, F * 16, 1 << 40,
+                      None]
+    bad = list(args)
+    bad[17] = None  # seqlens
+    assert bwd(*bad) == E_NULL
+    bad = list(args)
+    bad[15] = F32  # dW (not NULL) needs the fused path
+    assert bwd(*bad) == E_UNSUP
+    bad = list(args)
+    bad[23] = 16  # workspace too small
+    assert bwd(*bad) == E_WS
+    # dW = NULL is allowed: then only the workspace of the plain backward is needed
+    ok = list(args)
+    ok[21] = None
+    ok[15] = 7  # unsupported dtype code: rejected before anything is enqueued
+    assert bwd(*ok) == E_UNSUP
