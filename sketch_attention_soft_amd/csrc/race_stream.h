@@ -60,7 +60,7 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     constexpr int NWV = MAXT / 64, FMAX = FPT * NWV, LPMAX = FMAX / NR * NP;
     constexpr int ZP = (FPT + 63) / 64;                // count-column slots per lane
     constexpr int S_TT = NS == 2 && FMAX > 512 ? 4 : 8;  // tokens per tile (LDS of L > 32 decode)
-    __shared__ float wl[MODE != SM_DECODE ? LPMAX * S_XS : 1];  // W rows
+    __shared__ float wl[LPMAX * S_XS];                 // W rows
     __shared__ float xr[NS][S_TT][S_XS];               // staged rows
     __shared__ float yv[UPD ? S_TT : 1][HD];           // staged v rows
     __shared__ float inrm[NS][S_TT];                   // 1 / max(|x|, 1e-12)
@@ -78,14 +78,23 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     const int64_t row0 = bh * N;
     float *sh = state + bh * (int64_t)F * sc;
 
-    // W rows in LDS for the parallel modes; decode (mostly a few tokens) reads
-    // them from global memory instead of waiting for the staging
-    constexpr bool wlds = MODE != SM_DECODE;
-    if (wlds)
-        for (int e = tid; e < LP * HD; e += nthr) {
-            const int h = e / HD, k = e % HD;
-            wl[h * S_XS + k] = k < d ? W[h * d + k] : 0.f;
+    // W rows in LDS: each thread issues all its loads before its stores, so
+    // the staging costs one memory round trip (LP HD <= WPT nthr, since nthr =
+    // 64 ceil(16 L / FPT))
+    constexpr int WPT = FPT / 4;
+    {
+        float wv[WPT];
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            const int e = tid + j * nthr, h = e / HD, k = e % HD;
+            wv[j] = (e < LP * HD && k < d) ? W[h * d + k] : 0.f;
         }
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            const int e = tid + j * nthr;
+            if (e < LP * HD) wl[(e / HD) * S_XS + e % HD] = wv[j];
+        }
+    }
     float S[FPT], Z[ZP];
 #pragma unroll
     for (int i = 0; i < FPT; ++i) S[i] = (MODE != SM_ADD && f0 + i < F && c < d) ? sh[(int64_t)(f0 + i) * sc + c] : 0.f;
@@ -131,21 +140,11 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
             float u[S_TT];
 #pragma unroll
             for (int t = 0; t < S_TT; ++t) u[t] = 0.f;
-            if constexpr (wlds) {
 #pragma unroll 8
-                for (int k = 0; k < HD; ++k) {
-                    const float wk = wl[h * S_XS + k];
+            for (int k = 0; k < HD; ++k) {
+                const float wk = wl[h * S_XS + k];
 #pragma unroll
-                    for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
-                }
-            } else {
-                const float *wg = W + (int64_t)h * d;
-#pragma unroll 4
-                for (int k = 0; k < d; ++k) {
-                    const float wk = wg[k];
-#pragma unroll
-                    for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
-                }
+                for (int t = 0; t < S_TT; ++t) u[t] = fmaf(wk, xr[side][t][k], u[t]);
             }
 #pragma unroll
             for (int t = 0; t < S_TT; ++t)
