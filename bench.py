@@ -115,6 +115,9 @@ def main() -> int:
                          "(race_attn_backward_dw, learned hyperplanes)")
     ap.add_argument("--hard", action="store_true",
                     help="time the hard-hash forward (race_attn_forward_hard) on the workload")
+    ap.add_argument("--generality", action="store_true",
+                    help="time fwd+bwd of the 4M-token head with fp16 rows, d = 32, P = 2 and a "
+                         "right-padded batch beside the bf16 d = 64 P = 4 step")
     ap.add_argument("--stream", action="store_true",
                     help="time the streaming state entry points instead (decode of one token "
                          "per head over 64 heads, bulk state_add of the 4M-token head)")
@@ -142,6 +145,8 @@ def main() -> int:
 
     if args.stream:
         return stream_bench(args, binding, I, np, torch)
+    if args.generality:
+        return generality_bench(args, binding, I, np, torch)
     if args.hard:
         return hard_bench(args, binding, I, np, torch)
 
@@ -255,6 +260,106 @@ def main() -> int:
                           "frac": round(max(t_mfma, t_hbm) / ms, 5)},
         "kernels_ms": {k2: round(v2, 4) for k2, v2 in kern.items()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def generality_bench(args, binding, I, np, torch) -> int:
+    """One JSON line: the fwd+bwd step (saved state, as the main bench times
+    it) of causal_n4m_bf16's shape in the variants the library supports
+    beyond it -- fp16 rows, head dimension 32, P = 2 hyperplanes per table,
+    and a right-padded batch of four sequences of 4M, 3M, 2M and 1M tokens
+    padded to 4M (tokens/s counts real tokens only; the binding's padded_chunk
+    segments) -- beside the bf16 d = 64
+    P = 4 step itself, in one process.  Inputs are drawn on the device (torch
+    N(0, 1), Q and K rows normalised): these are timing runs, parity is
+    tested elsewhere.  Each variant reports its algorithmic flops and bytes
+    against the MFMA and HBM peaks (step_frac = max(t_mfma, t_hbm) / t)."""
+    import dataclasses
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    base = I.WORKLOADS["causal_n4m_bf16"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4243)
+    variants = [("bf16_d64_P4", torch.bfloat16, 64, 4, None),
+                ("f16_d64_P4", torch.float16, 64, 4, None),
+                ("bf16_d32_P4", torch.bfloat16, 32, 4, None),
+                ("bf16_d64_P2", torch.bfloat16, 64, 2, None),
+                ("bf16_padded_4x4M", torch.bfloat16, 64, 4, (4 << 20, 3 << 20, 2 << 20, 1 << 20))]
+    out = {}
+    for name, tdt, d, P, lens in variants:
+        B = len(lens) if lens else 1
+        N, L = base.N, base.L
+
+        def rows(normalise):
+            x = torch.randn((B, 1, N, d), generator=gen, device=dev, dtype=torch.float32)
+            if normalise:
+                x = x / x.norm(dim=-1, keepdim=True)
+            return x.to(tdt)
+
+        q, k, v, do = rows(True), rows(True), rows(False), rows(False)
+        W = torch.randn((L, P, d), generator=gen, device=dev, dtype=torch.float32)
+        tokens = sum(lens) if lens else N
+        o = torch.zeros_like(q)
+        den = torch.zeros((B, 1, N), dtype=torch.float32, device=dev)
+        grads = tuple(torch.zeros_like(q) for _ in range(3))
+        ch = binding.padded_chunk(B, 1, N) if lens else 0
+        wsf = torch.empty(binding.workspace_bytes(B, 1, N, d, L, P, True, ch, tdt, False),
+                          dtype=torch.uint8, device=dev)
+        wsb = torch.empty(binding.workspace_bytes(B, 1, N, d, L, P, True, ch, tdt, True),
+                          dtype=torch.uint8, device=dev)
+        if lens:
+            sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+
+            def step():
+                binding.forward_padded(q, k, v, W, sl, base.tau, True, ch, workspace=wsf,
+                                       out=(o, den))
+                binding.backward_padded(q, k, v, W, o, den, do, sl, base.tau, True, ch,
+                                        workspace=wsb, out=grads)
+        else:
+            saved = binding.new_saved(q, W, True, 0)
+
+            def step():
+                binding.forward(q, k, v, W, base.tau, True, 0, workspace=wsf, out=(o, den),
+                                saved=saved)
+                binding.backward(q, k, v, W, o, den, do, base.tau, True, 0, workspace=wsb,
+                                 out=grads, saved=saved)
+
+        for _ in range(args.warmup):
+            step()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        wv = dataclasses.replace(base, d=d, P=P, dtype="bf16")
+        flops_tok, bytes_tok, _ = algorithmic_per_token(wv)
+        t_mfma = flops_tok * tokens / (PEAK_TFLOPS["bf16"] * 1e12) * 1e3
+        t_hbm = bytes_tok * tokens / (PEAK_HBM_GBS * 1e9) * 1e3
+        out[name] = {"ms_per_step": round(ms, 4), "tokens": tokens,
+                     "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+                     "flops_per_token": flops_tok, "bytes_per_token": bytes_tok,
+                     "step_frac": round(max(t_mfma, t_hbm) / ms, 5)}
+        print(f"[bench] {name}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+        del q, k, v, do, o, den, grads, wsf, wsb
+        torch.cuda.empty_cache()
+    ref = out["bf16_d64_P4"]["tokens_per_s"]
+    for r in out.values():
+        r["vs_bf16_d64_P4"] = round(r["tokens_per_s"] / ref, 4)
+    line = {
+        "metric": "RACE attn fwd+bwd tokens/s, library variants at the 4M-token causal shape",
+        "value": out["bf16_d64_P4"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": out["bf16_d64_P4"]["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (torch N(0,1) on the device; Q, K rows L2-normalised)",
+        "config": {"workload": "causal_n4m_variants", "N": base.N, "L": base.L, "tau": base.tau,
+                   "causal": True, "passes": "fwd+bwd"},
+        "variants": out,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -130,7 +130,10 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
  * pointer, int32 [B], read by the kernels.  Otherwise as race_attn_forward /
  * race_attn_backward; the backward also writes dW when dW is not NULL (as
  * race_attn_backward_dw: RACE_BF16 / RACE_F16, L <= 32, workspace with
- * for_backward = 2).  No saved state. */
+ * for_backward = 2).  No saved state.  chunk = 0 picks the dense default
+ * (about one segment per compute unit over all B H N rows); with unequal
+ * lengths the segments past a sequence's end have no work, and a smaller
+ * chunk (about B H N / 2048) keeps more workgroups busy. */
 race_status_t race_attn_forward_padded(const void *Q, const void *K, const void *V,
                                        const float *W, int L, int P, float tau, int causal, int B,
                                        int H, int64_t N, int d, race_dtype_t dt, int chunk,

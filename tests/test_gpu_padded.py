@@ -73,9 +73,10 @@ def test_padded_full_lengths_match_the_dense_entry_points():
     sl = torch.full((B,), N, dtype=torch.int32, device="cuda")
     o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], tau, True)
     g = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau, True, dw=True)
-    op, denp = binding.forward_padded(dx["q"], dx["k"], dx["v"], dx["W"], sl, tau, True)
+    # chunk 0: the dense entry points' segments
+    op, denp = binding.forward_padded(dx["q"], dx["k"], dx["v"], dx["W"], sl, tau, True, 0)
     gp = binding.backward_padded(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], sl, tau,
-                                 True, dw=True)
+                                 True, 0, dw=True)
     torch.cuda.synchronize()
     assert torch.equal(o, op) and torch.equal(den, denp)
     for a, b in zip(g, gp):
