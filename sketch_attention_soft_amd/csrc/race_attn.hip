@@ -658,9 +658,11 @@ void launch_stream(const StreamPlan &sp, const void *Q, const void *K, const voi
     const dim3 grid((unsigned)nblk, (unsigned)sp.BH);
     // 32 or 64 features per wave; up to 8 waves (256 registers per lane), or
     // 16 for L > 32 (128 registers)
-    auto k = sp.fpt == 32       ? race::stream_kernel<T, MODE, 32, 512>
-             : sp.nthr <= 512   ? race::stream_kernel<T, MODE, 64, 512>
-                                : race::stream_kernel<T, MODE, 64, 1024>;
+    // one token per head (decode): tiles of one token
+    const bool one = MODE == race::SM_DECODE && N == 1;
+    auto k = sp.fpt == 32     ? (one ? race::stream_kernel<T, MODE, 32, 512, 1> : race::stream_kernel<T, MODE, 32, 512>)
+             : sp.nthr <= 512 ? (one ? race::stream_kernel<T, MODE, 64, 512, 1> : race::stream_kernel<T, MODE, 64, 512>)
+                              : (one ? race::stream_kernel<T, MODE, 64, 1024, 1> : race::stream_kernel<T, MODE, 64, 1024>);
     hipLaunchKernelGGL(k, grid, dim3(sp.nthr), 0, s, static_cast<const T *>(Q),
                        static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, sp.d, 1.f / tau,
                        N, blk, state, part, static_cast<T *>(O), den);

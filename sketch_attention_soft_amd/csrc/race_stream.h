@@ -46,8 +46,10 @@ template <typename T> __device__ __forceinline__ float sload(const T *p) { retur
 
 // MAXT threads = MAXT / 64 waves of FPT features: F <= FMAX = FPT MAXT / 64
 // and L P <= FMAX P / 16 (the launch picks the instance that fits).  Tiles
-// of S_TT tokens.
-template <typename T, int MODE, int FPT, int MAXT>
+// of S_TT tokens: TT, or with TT = 0 eight (four for L > 32 decode, for LDS);
+// a decode of one token per head takes TT = 1, so that the projections of a
+// tile are not formed for tokens it does not have.
+template <typename T, int MODE, int FPT, int MAXT, int TT = 0>
 __global__ __launch_bounds__(MAXT)
 __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) void stream_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
@@ -59,7 +61,7 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     constexpr int KS = RD ? 1 : 0;                     // side of the keys
     constexpr int NWV = MAXT / 64, FMAX = FPT * NWV, LPMAX = FMAX / NR * NP;
     constexpr int ZP = (FPT + 63) / 64;                // count-column slots per lane
-    constexpr int S_TT = NS == 2 && FMAX > 512 ? 4 : 8;  // tokens per tile (LDS of L > 32 decode)
+    constexpr int S_TT = TT > 0 ? TT : NS == 2 && FMAX > 512 ? 4 : 8;  // tokens per tile
     __shared__ float wl[LPMAX * S_XS];                 // W rows
     __shared__ float xr[NS][S_TT][S_XS];               // staged rows
     __shared__ float yv[UPD ? S_TT : 1][HD];           // staged v rows
