@@ -164,14 +164,15 @@ def bucket_sums(k, v, W, tau: float):
 
 def walsh_state(k, v, W, tau: float):
     """The streaming state of one head after the keys k (values v), in the
-    Walsh basis of each table: S[16 l + s, :] = 1/4 sum_r chi_s(r) AB[l, r, :]
-    with chi_s(r) = prod_{p in s} c_rp and AB from bucket_sums.  Since the
-    corner weights are phi_lr = prod_p (1 + c_rp t_lp) / 2 (pin P-2),
-    1/4 sum_r chi_s(r) phi_lr = 1/4 prod_{p in s} t_lp: S is the sum over the
-    keys of those products times [v | 1].  Returns [L * R, d + 1] fp64.
+    Walsh basis of each table: S[R l + s, :] = 2^(-P/2) sum_r chi_s(r) AB[l, r, :]
+    with chi_s(r) = prod_{p in s} c_rp and AB from bucket_sums (R = 2^P; the
+    scale is 1/4 for P = 4).  Since the corner weights are
+    phi_lr = prod_p (1 + c_rp t_lp) / 2 (pin P-2), 2^(-P/2) sum_r chi_s(r) phi_lr
+    = 2^(-P/2) prod_{p in s} t_lp: S is the sum over the keys of those
+    products times [v | 1].  Returns [L * R, d + 1] fp64.
 
     The readout of step 7 ([zh] §2.2) from it, sum_l phi_l(q)^T AB_l, equals
-    psi(q) S with psi_{16 l + s}(q) = 1/4 sum_r chi_s(r) phi_lr(q), because
+    psi(q) S with psi_{R l + s}(q) = 2^(-P/2) sum_r chi_s(r) phi_lr(q), because
     sum_s chi_s(r) chi_s(r') = R [r == r']."""
     AB = bucket_sums(k, v, W, tau)                     # [L, R, d + 1]
     L, R, C = AB.shape
@@ -180,4 +181,4 @@ def walsh_state(k, v, W, tau: float):
     c = np.where(((r[:, None] >> np.arange(P)[None, :]) & 1) == 1, 1.0, -1.0)   # [R, P]
     s_bits = ((np.arange(R)[:, None] >> np.arange(P)[None, :]) & 1) == 1        # [S, P]
     chi = np.prod(np.where(s_bits[:, None, :], c[None, :, :], 1.0), axis=2)     # [S, R]
-    return (0.25 * np.einsum("sr,lrc->lsc", chi, AB)).reshape(L * R, C)
+    return (2.0 ** (-P / 2) * np.einsum("sr,lrc->lsc", chi, AB)).reshape(L * R, C)

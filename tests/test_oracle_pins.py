@@ -338,25 +338,27 @@ def test_invalid_arguments_raise():
 
 # -- P-13: the streaming state in the Walsh basis (zh §2.2 bucket sums, §2.3
 # running sums) -- pins of oracle.bucket_sums and oracle.walsh_state
-def test_p13_walsh_state_closed_forms():
-    rng = np.random.default_rng(61)
-    N, d, L, P, tau = 57, 12, 3, 4, 0.7
+@pytest.mark.parametrize("P", [2, 3, 4])
+def test_p13_walsh_state_closed_forms(P):
+    rng = np.random.default_rng(61 + P)
+    N, d, L, tau = 57, 12, 3, 0.7
+    R, sc = 1 << P, 2.0 ** (-P / 2)
     k, v = rng.standard_normal((N, d)), rng.standard_normal((N, d))
     W = rng.standard_normal((L, P, d))
     S = oracle.walsh_state(k, v, W, tau)
-    assert S.shape == (L * 16, d + 1)
-    # the empty subset has psi = 1/4 for every key: count column N / 4, values sum / 4
+    assert S.shape == (L * R, d + 1)
+    # the empty subset has psi = 2^(-P/2) for every key: count column N 2^(-P/2)
     for l in range(L):
-        np.testing.assert_allclose(S[16 * l, d], N / 4, rtol=1e-13)
-        np.testing.assert_allclose(S[16 * l, :d], v.sum(0) / 4, rtol=1e-12, atol=1e-13)
-    # brute force: psi_s = 1/4 prod_{p in s} tanh(z_p / tau), from the oracle's z
+        np.testing.assert_allclose(S[R * l, d], N * sc, rtol=1e-13)
+        np.testing.assert_allclose(S[R * l, :d], v.sum(0) * sc, rtol=1e-12, atol=1e-13)
+    # brute force: psi_s = 2^(-P/2) prod_{p in s} tanh(z_p / tau), from the oracle's z
     _, z = oracle.soft_hash(k, W, tau)
     t = np.tanh(z / tau)
-    psi = np.empty((N, L, 16))
-    for s in range(16):
-        psi[:, :, s] = 0.25 * np.prod([t[:, :, p] if (s >> p) & 1 else np.ones((N, L))
-                                       for p in range(P)], axis=0)
-    brute = np.einsum("jf,jc->fc", psi.reshape(N, L * 16),
+    psi = np.empty((N, L, R))
+    for s_ in range(R):
+        psi[:, :, s_] = sc * np.prod([t[:, :, p] if (s_ >> p) & 1 else np.ones((N, L))
+                                      for p in range(P)], axis=0)
+    brute = np.einsum("jf,jc->fc", psi.reshape(N, L * R),
                       np.concatenate([v, np.ones((N, 1))], axis=1))
     np.testing.assert_allclose(S, brute, rtol=1e-10, atol=1e-12)
     # additive over a split of the keys
@@ -364,19 +366,21 @@ def test_p13_walsh_state_closed_forms():
     np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
 
 
-def test_p13_walsh_readout_is_the_non_causal_forward():
-    rng = np.random.default_rng(62)
-    N, M, d, L, P, tau = 40, 9, 16, 5, 4, 1.3
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+def test_p13_walsh_readout_is_the_non_causal_forward(P):
+    rng = np.random.default_rng(62 + P)
+    N, M, d, L, tau = 40, 9, 16, 5, 1.3
+    R, sc = 1 << P, 2.0 ** (-P / 2)
     k, v, q = (rng.standard_normal((n, d)) for n in (N, N, M))
     W = rng.standard_normal((L, P, d))
     S = oracle.walsh_state(k, v, W, tau)
     _, zq = oracle.soft_hash(q, W, tau)
     tq = np.tanh(zq / tau)
-    psi = np.empty((M, L, 16))
-    for s in range(16):
-        psi[:, :, s] = 0.25 * np.prod([tq[:, :, p] if (s >> p) & 1 else np.ones((M, L))
-                                       for p in range(P)], axis=0)
-    nm = psi.reshape(M, L * 16) @ S
+    psi = np.empty((M, L, R))
+    for s_ in range(R):
+        psi[:, :, s_] = sc * np.prod([tq[:, :, p] if (s_ >> p) & 1 else np.ones((M, L))
+                                      for p in range(P)], axis=0)
+    nm = psi.reshape(M, L * R) @ S
     # the same queries against all N keys, from the oracle's own readout
     qq = np.concatenate([q, np.zeros((N - M, d))]) if M < N else q
     o, den = oracle.forward(qq, k, v, W, tau, False)
