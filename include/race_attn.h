@@ -234,16 +234,18 @@ race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
  *
  * State of one head: fp32 S[F][d + 1], F = 16 L, row f = 16 l + s:
  *   S[f][c] = sum_j psi_f(k_j) v_j[c] for c < d,  S[f][d] = sum_j psi_f(k_j),
- *   psi_{16 l + s}(x) = 1/4 prod_{p in s} t_lp(x),  t_lp = tanh(z_lp / tau),
- * over the keys j appended so far, where s is a subset of the table's P = 4
- * hyperplanes (bit p of s set when p is in it).  The corner weights of step 2
+ *   psi_{16 l + s}(x) = 2^(-P/2) prod_{p in s} t_lp(x),  t_lp = tanh(z_lp / tau),
+ * over the keys j appended so far, where s is a subset of the table's
+ * hyperplanes (bit p of s set when p is in it; 2^(-P/2) = 1/4 for P = 4).  For
+ * P < 4 the rows are still 16 per table; those whose s contains a p >= P are
+ * zero.  The corner weights of step 2
  * are phi_lr = prod_p (1 + c_rp t_lp) / 2, so psi_l is their Walsh-Hadamard
  * transform, psi(q).psi(k) = phi(q).phi(k), and S holds the bucket sums A_l,
  * B_l of step 3 in that basis.  A readout is [n | m] = sum_f psi_f(q) S[f][:],
  * o = n / m, den = m (step 4).  The states of all heads are one contiguous
  * device array [B][H][F][d + 1], owned by the caller; all zeros is the empty
  * prefix.  These entry points compute in fp32 (t with tanhf) whatever dt is.
- * Supported for 1 <= d <= 64, P = 4, L <= 64 and B * H <= 65535; N or T = 0
+ * Supported for 1 <= d <= 64, 1 <= P <= 4, L <= 64 and B * H <= 65535; N or T = 0
  * is a no-op (the row pointers may then be NULL; W and state may not).  Calls
  * that write one state must not overlap. */
 

@@ -404,11 +404,11 @@ def state_bytes(B, H, d, L, P) -> int:
 def new_state(B, H, d, L, P, device) -> torch.Tensor:
     """Zeroed states [B, H, 16 L, d + 1] (fp32): the empty prefix of every head."""
     state_bytes(B, H, d, L, P)  # validates the shape
-    return torch.zeros((B, H, L << P, d + 1), dtype=torch.float32, device=device)
+    return torch.zeros((B, H, 16 * L, d + 1), dtype=torch.float32, device=device)
 
 
 def _check_state(state, B, H, d, L, P, ref):
-    if (state.dtype != torch.float32 or state.shape != (B, H, L << P, d + 1)
+    if (state.dtype != torch.float32 or state.shape != (B, H, 16 * L, d + 1)
             or not state.is_contiguous() or state.device != ref.device):
         raise ValueError("state must be a contiguous fp32 [B, H, 16 L, d + 1] tensor")
 

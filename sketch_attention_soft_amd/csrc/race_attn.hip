@@ -618,7 +618,7 @@ race_status_t check_trace(race_trace_t *trace)
 // Streaming state (race_stream.h)
 
 struct StreamPlan {
-    int BH, L, d, F, fpt, nthr;
+    int BH, L, P, d, F, fpt, nthr;
     int64_t elems;  // floats of one head's state
 };
 
@@ -626,13 +626,14 @@ race_status_t stream_plan(int B, int H, int64_t N, int d, int L, int P, race_dty
                           StreamPlan *sp)
 {
     if (B < 1 || H < 1 || N < 0 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
-    if (d > race::HD || P != race::NP || L > 64) return RACE_ERR_UNSUPPORTED;
+    if (d > race::HD || P > race::NP || L > 64) return RACE_ERR_UNSUPPORTED;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH > 65535) return RACE_ERR_UNSUPPORTED;  // heads go to the second grid dimension
     if (N > ((int64_t)1 << 62) / (BH * d)) return RACE_ERR_SHAPE;
     sp->BH = (int)BH;
     sp->L = L;
+    sp->P = P;
     sp->d = d;
     sp->F = L * race::NR;
     sp->fpt = sp->F > 256 ? 64 : 32;
@@ -664,7 +665,7 @@ void launch_stream(const StreamPlan &sp, const void *Q, const void *K, const voi
              : sp.nthr <= 512 ? (one ? race::stream_kernel<T, MODE, 64, 512, 1> : race::stream_kernel<T, MODE, 64, 512>)
                               : (one ? race::stream_kernel<T, MODE, 64, 1024, 1> : race::stream_kernel<T, MODE, 64, 1024>);
     hipLaunchKernelGGL(k, grid, dim3(sp.nthr), 0, s, static_cast<const T *>(Q),
-                       static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, sp.d, 1.f / tau,
+                       static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, sp.P, sp.d, 1.f / tau,
                        N, blk, state, part, static_cast<T *>(O), den);
 }
 

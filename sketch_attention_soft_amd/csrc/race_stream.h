@@ -12,9 +12,12 @@
 // d <= 64 (rows and W are read with their own length d; lane c < d of a wave
 // holds column c):
 //   S[f][c] = sum_j psi_f(k_j) v_j[c] (c < d),  S[f][d] = sum_j psi_f(k_j),
-//   psi_{16 l + s}(x) = 1/4 prod_{p in s} t_{lp}(x)  (s: a subset of the
-//   table's 4 hyperplanes, bit p set when p is in it),
+//   psi_{16 l + s}(x) = 2^(-P/2) prod_{p in s} t_{lp}(x)  (s: a subset of the
+//   table's hyperplanes, bit p set when p is in it; 1/4 for P = 4),
 //   t_{lp}(x) = tanh(tanh(<w_lp, x / max(|x|, 1e-12)>) / tau).
+// For P < 4 the kernel keeps 16 rows per table: hyperplanes p >= P have zero
+// W rows, so t = tanh(0) = 0 exactly and every row whose s contains one is
+// zero.
 // The corner weights of the pages are phi_lr = prod_p (1 + c_rp t_lp) / 2, so
 // psi is their Walsh-Hadamard transform and psi(q).psi(k) = phi(q).phi(k): S
 // holds the pages' bucket sums A and B in that basis, and a readout is
@@ -53,7 +56,7 @@ template <typename T, int MODE, int FPT, int MAXT, int TT = 0>
 __global__ __launch_bounds__(MAXT)
 __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) void stream_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
-    const float *__restrict__ W, int L, int d, float inv_tau, int64_t N, int64_t blk,
+    const float *__restrict__ W, int L, int P, int d, float inv_tau, int64_t N, int64_t blk,
     float *__restrict__ state, float *__restrict__ part, T *__restrict__ O, float *__restrict__ den)
 {
     constexpr bool UPD = MODE != SM_READOUT, RD = MODE != SM_ADD;
@@ -72,6 +75,7 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     __shared__ float pm[RD ? S_TT : 1][NWV];           // and of m
 
     const int LP = L * NP, F = L * NR, sc = d + 1;  // sc: state columns
+    const float fscale = __builtin_sqrtf(__builtin_ldexpf(1.f, -P));  // 2^(-P/2): 1/4 for P = 4
     const int QN = (F + FPT - 1) / FPT;
     const int nthr = blockDim.x, tid = threadIdx.x;
     const int c = tid & 63, grp = tid >> 6, f0 = grp * FPT;
@@ -88,8 +92,9 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
         float wv[WPT];
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
-            const int e = tid + j * nthr, h = e / HD, k = e % HD;
-            wv[j] = (e < LP * HD && k < d) ? W[h * d + k] : 0.f;
+            // internal hyperplane h = 4 l + p <- W row P l + p (p < P), else zero
+            const int e = tid + j * nthr, h = e / HD, k = e % HD, p = h & 3;
+            wv[j] = (e < LP * HD && k < d && p < P) ? W[((h >> 2) * P + p) * d + k] : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
@@ -160,7 +165,7 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
             float p = 0.f;
             if (f < F) {
                 const float *tl = &tv[side][t][(f >> 4) * NP];
-                p = 0.25f;
+                p = fscale;
 #pragma unroll
                 for (int b = 0; b < NP; ++b)
                     if ((f >> b) & 1) p *= tl[b];

@@ -293,13 +293,15 @@ def test_state_bytes(lib):
     assert L.race_attn_state_bytes(1, 1, 64, 5, 4, ctypes.byref(out)) == OK
     assert out.value == 80 * 65 * 4
     assert L.race_attn_state_bytes(1, 1, 64, 32, 4, None) == E_NULL
+    # P < 4 keeps 16 rows per table
+    assert L.race_attn_state_bytes(1, 1, 64, 8, 3, ctypes.byref(out)) == OK and out.value == 128 * 65 * 4
     # any d <= 64: [16 L][d + 1]
     assert L.race_attn_state_bytes(1, 2, 32, 8, 4, ctypes.byref(out)) == OK
     assert out.value == 2 * 128 * 33 * 4
     assert L.race_attn_state_bytes(1, 1, 1, 8, 4, ctypes.byref(out)) == OK and out.value == 128 * 2 * 4
     for args, code in (((0, 1, 64, 8, 4), E_SHAPE), ((1, 1, 65, 8, 4), E_UNSUP),
                        ((1, 1, 0, 8, 4), E_SHAPE),
-                       ((1, 1, 64, 8, 3), E_UNSUP), ((1, 1, 64, 65, 4), E_UNSUP),
+                       ((1, 1, 64, 8, 5), E_UNSUP), ((1, 1, 64, 65, 4), E_UNSUP),
                        ((1, 1, 64, 0, 4), E_SHAPE), ((65536, 1, 64, 8, 4), E_UNSUP)):
         assert L.race_attn_state_bytes(*args, ctypes.byref(out)) == code, args
 

@@ -119,3 +119,35 @@ def test_gradients_are_deterministic(P):
     for rep in outs[1:]:
         for a, b in zip(outs[0], rep):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P", [1, 2, 3])
+def test_planes_streaming_state(dtype, P):
+    """Streaming state at P < 4: decode from the empty state is the causal
+    forward, readout the non-causal one, and the state's rows are the oracle's
+    Walsh-basis state (scale 2^(-P/2)), the 16 - 2^P rows per table that
+    contain a padding hyperplane being zero."""
+    B, H, N, N0, L, tau = 1, 2, 300, 120, 8, 0.9
+    R = 1 << P
+    dx, hx = _inputs(dtype, B, H, N, 64, L, P, 1990 + P, grad=False)
+    print(f"[case] P={P} stream {dtype}", flush=True)
+    st = binding.new_state(B, H, 64, L, P, dx["q"].device)
+    assert st.shape == (B, H, 16 * L, 65)
+    binding.state_add(st, dx["k"][:, :, :N0].contiguous(), dx["v"][:, :, :N0].contiguous(),
+                      dx["W"], tau)
+    q, k, v = (dx[n][:, :, N0:].contiguous() for n in ("q", "k", "v"))
+    o, den = binding.decode(st, q, k, v, dx["W"], tau)
+    ro2, rden2 = binding.state_readout(st, dx["q"], dx["W"], tau)
+    torch.cuda.synchronize()
+    ro, rden = oracle.forward(hx["q"], hx["k"], hx["v"], hx["W"], tau, True)
+    assert head_relf(to_host64(o), ro[:, :, N0:]) <= TOL[dtype]
+    assert head_relf(to_host64(den), rden[:, :, N0:]) <= TOL[dtype]
+    nro, nrden = oracle.forward(hx["q"], hx["k"], hx["v"], hx["W"], tau, False)
+    assert head_relf(to_host64(ro2), nro) <= TOL[dtype]
+    assert head_relf(to_host64(rden2), nrden) <= TOL[dtype]
+    s = to_host64(st).reshape(B, H, L, 16, 65)
+    assert not np.any(s[:, :, :, R:])
+    ws = np.stack([np.stack([oracle.walsh_state(hx["k"][b, h], hx["v"][b, h], hx["W"], tau)
+                             for h in range(H)]) for b in range(B)]).reshape(B, H, L, R, 65)
+    assert head_relf(s[:, :, :, :R].reshape(B, H, L * R, 65), ws.reshape(B, H, L * R, 65)) <= 1e-4
