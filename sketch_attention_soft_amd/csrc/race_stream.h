@@ -39,6 +39,7 @@
 // written once per call.
 #pragma once
 #include "race_common.h"
+#include "race_walk.h"
 
 namespace race {
 
@@ -96,20 +97,32 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
             const int e = tid + j * nthr, h = e / HD, k = e % HD, p = h & 3;
             wv[j] = (e < LP * HD && k < d && p < P) ? W[((h >> 2) * P + p) * d + k] : 0.f;
         }
+        // (e / HD < WPT nthr / 64 <= LPMAX: every store is in the array, and
+        // those past L P rows store zeros)
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
             const int e = tid + j * nthr;
-            if (e < LP * HD) wl[(e / HD) * S_XS + e % HD] = wv[j];
+            wl[(e / HD) * S_XS + e % HD] = wv[j];
         }
     }
+    // The head's state through a buffer resource: row f, column c at byte
+    // 4 (f sc + c).  Lanes c >= d take an offset past the resource, and rows
+    // f >= F fall past it (F sc floats), so loads read zero and stores are
+    // dropped without branches; the row step is a scalar offset.
+    const int lane_off = c < d ? (f0 * sc + c) * 4 : OOB, rstep = sc * 4;
+    const Rsrc rs = make_rsrc(sh, F * sc * 4);
+    auto z_off = [&](int z) {
+        const int f = f0 + 64 * z + c;
+        return 64 * z + c < FPT && f < F ? (f * sc + d) * 4 : OOB;
+    };
     float S[FPT], Z[ZP];
 #pragma unroll
-    for (int i = 0; i < FPT; ++i) S[i] = (MODE != SM_ADD && f0 + i < F && c < d) ? sh[(int64_t)(f0 + i) * sc + c] : 0.f;
+    for (int i = 0; i < FPT; ++i)
+        S[i] = MODE != SM_ADD
+                   ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, i * rstep, 0))
+                   : 0.f;
 #pragma unroll
-    for (int z = 0; z < ZP; ++z) {
-        const int f = f0 + 64 * z + c;
-        Z[z] = (MODE != SM_ADD && 64 * z + c < FPT && f < F) ? sh[(int64_t)f * sc + d] : 0.f;
-    }
+    for (int z = 0; z < ZP; ++z) Z[z] = MODE != SM_ADD ? bldf(rs, z_off(z)) : 0.f;
 
     for (int64_t tile = t_begin; tile < t_end; tile += S_TT) {
         const int nt = (int)min<int64_t>(S_TT, t_end - tile);
@@ -216,14 +229,12 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     }
     if (MODE != SM_READOUT) {
         float *dst = MODE == SM_DECODE ? sh : part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * sc;
+        const Rsrc rd = make_rsrc(dst, F * sc * 4);
 #pragma unroll
         for (int i = 0; i < FPT; ++i)
-            if (f0 + i < F && c < d) dst[(int64_t)(f0 + i) * sc + c] = S[i];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, S[i]), rd, lane_off, i * rstep, 0);
 #pragma unroll
-        for (int z = 0; z < ZP; ++z) {
-            const int f = f0 + 64 * z + c;
-            if (64 * z + c < FPT && f < F) dst[(int64_t)f * sc + d] = Z[z];
-        }
+        for (int z = 0; z < ZP; ++z) bstf(Z[z], rd, z_off(z));
     }
 }
 
