@@ -82,7 +82,7 @@ def test_backward_parity(dtype, causal, case, saved):
     res, ref = _run(dtype, causal, *case, backward=True, saved=saved)
     tol = TOL[dtype]
     # N = 1: every query sees only its own key, so o = v and the exact dQ, dK
-    # are zero; the computed values are rounding noise, judged on dV's scale.
+    # are zero; the computed values are rounding noise, measured on dV's scale.
     floor = 1.0 if case[2] == 1 else 1e-3
     errs = {n: head_relf(res[n], ref[n], ref["dv"] if n in ("dq", "dk") else None, floor)
             for n in ("o", "dq", "dk", "dv")}
