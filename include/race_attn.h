@@ -36,8 +36,10 @@
  *     after enqueueing, without synchronising.  The library never allocates,
  *     frees or synchronises, keeps no global mutable state and is safe to
  *     call from several threads.
- *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32 and
- *     RACE_F16); for RACE_BF16 and RACE_F16 with L <= 32 also d = 32 (the
+ *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32; for
+ *     16-bit rows L > 32 runs as two passes over 32 and L - 32 tables, the
+ *     second adding the first's fp32 partial sums); for RACE_BF16 and
+ *     RACE_F16 with L <= 32 also d = 32 (the
  *     rows are zero-padded to 64 columns on chip: the same work per token as
  *     d = 64, half the memory traffic) and P = 1, 2, 3 (the kernels keep 4
  *     hyperplanes per table with t = 0 on the padding ones, an exact
@@ -129,7 +131,7 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
  * dV) are left as they are, so padding costs no work.  seqlens: device
  * pointer, int32 [B], read by the kernels.  Otherwise as race_attn_forward /
  * race_attn_backward; the backward also writes dW when dW is not NULL (as
- * race_attn_backward_dw: RACE_BF16 / RACE_F16, L <= 32, workspace with
+ * race_attn_backward_dw: RACE_BF16 / RACE_F16, workspace with
  * for_backward = 2).  No saved state.  chunk = 0 picks the dense default
  * (about one segment per compute unit over all B H N rows); with unequal
  * lengths the segments past a sequence's end have no work, and a smaller
@@ -166,7 +168,7 @@ typedef struct {
  * statistics with the per-head totals (step 3 / zh §2.3, fp32), and the
  * squashed projections t of Q and K with their derivatives (steps 1-2, fp16,
  * 512 bytes per row of Q and of K at L = 32).  0 when the configuration does
- * not use it (RACE_F32, or L > 32).  Pure host function. */
+ * not use it (RACE_F32).  Pure host function. */
 race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P, int causal,
                                     int chunk, race_dtype_t dt, size_t *bytes);
 
@@ -217,7 +219,7 @@ race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *c
  * dW (device, fp32 [L][P][d], overwritten).  dQ, dK and dV are the same as
  * race_attn_backward_ex's.  The per-workgroup sums are added in a fixed order,
  * so the result does not depend on the launch.  Supported for RACE_BF16 and
- * RACE_F16 with L <= 32 (RACE_ERR_UNSUPPORTED otherwise); workspace: race_attn_workspace_bytes
+ * RACE_F16 (RACE_ERR_UNSUPPORTED for RACE_F32); workspace: race_attn_workspace_bytes
  * with for_backward = 2. */
 race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
                                     const float *W, const void *O, const float *den,

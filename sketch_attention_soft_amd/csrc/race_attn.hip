@@ -57,6 +57,11 @@ struct Plan {
     int d;             // head dimension (64, or 32 on the fused path)
     int P;             // hyperplanes per table (4, or 1..3 on the fused path)
     race::Lens lens;   // per-batch valid rows (right-padded batches), or none
+    // L > 32 with 16-bit rows: two fused passes over 32 and L - 32 tables
+    // (the sizes below are then those of both passes and the partial sums)
+    bool split;
+    int part_mode;     // PART_NONE, or this pass's PART_OUT / PART_IN
+    race::Part part_o, part_dq, part_dk, part_dv;
     bool fused;        // bf16 and L <= 32: kernels hash their own rows
     int64_t seg, nseg;
     size_t st_bytes;   // one set of segment states (nseg + 1 per head)
@@ -83,16 +88,21 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     if (P > race::NP) return RACE_ERR_UNSUPPORTED;
-    if (L > 64 || (dt != RACE_BF16 && L > 32)) return RACE_ERR_UNSUPPORTED;
+    if (L > 64 || (dt == RACE_F32 && L > 32)) return RACE_ERR_UNSUPPORTED;
+    // 16-bit rows with L > 32: two fused passes, d = 64 only
+    if (dt != RACE_F32 && L > 32 && d != race::HD) return RACE_ERR_UNSUPPORTED;
     // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32)
     const bool fusable = dt != RACE_F32 && L <= 32;
     if (d != race::HD && !(d == 32 && fusable)) return RACE_ERR_UNSUPPORTED;
-    if (P != race::NP && !fusable) return RACE_ERR_UNSUPPORTED;
+    if (P != race::NP && dt == RACE_F32) return RACE_ERR_UNSUPPORTED;
     if (chunk < 0 || chunk % race::CH != 0) return RACE_ERR_CHUNK;
     p->BH = (int64_t)B * H;
     p->d = d;
     p->P = P;
     p->lens = race::Lens{nullptr, H};
+    p->split = false;
+    p->part_mode = race::PART_NONE;
+    p->part_o = p->part_dq = p->part_dk = p->part_dv = race::Part{nullptr, nullptr};
     p->N = N;
     p->rows = p->BH * N;
     p->L = L;
@@ -150,6 +160,21 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->dw_total = p->fused ? p->b_dw + align256((size_t)2 * p->BH * p->nseg * (2 * p->nw * 16) *
                                                 race::HD * sizeof(float))
                            : 0;
+    if (dt != RACE_F32 && L > 32) {
+        // two fused passes (the first 32 tables, then the other L - 32): both
+        // passes' buffers, then the fp32 partial sums
+        Plan a, b;
+        race_status_t st = make_plan(B, H, N, d, 32, P, chunk, dt, &a);
+        if (st != RACE_OK) return st;
+        if ((st = make_plan(B, H, N, d, L - 32, P, chunk, dt, &b)) != RACE_OK) return st;
+        const size_t pv = align256((size_t)p->rows * race::HD * sizeof(float));
+        const size_t pm = align256((size_t)p->rows * sizeof(float));
+        p->split = true;
+        p->f_total = a.f_total + b.f_total + pv + pm;
+        p->b_total = a.b_total + b.b_total + 3 * pv;
+        p->dw_total = a.dw_total + b.dw_total + 3 * pv;
+        p->s_total = a.s_total + b.s_total;
+    }
     return RACE_OK;
 }
 
@@ -351,12 +376,27 @@ void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squa
                  const race::HCache &rc, const race::HCache &wc, T *out, float *den)
 {
     if constexpr (sizeof(T) == 2) {
-        if (RSRC == 1 || sq.deg >= 0)
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D>), grid,
-                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den, p.lens);
-        else
-            LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D>), grid,
-                   dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out, den, p.lens);
+        const race::Part pt = BWD ? p.part_dv : p.part_o;
+        auto go = [&](auto part_c) {
+            constexpr int PT = decltype(part_c)::value;
+            if (RSRC == 1 || sq.deg >= 0)
+                LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D, PT>), grid,
+                       dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out,
+                       den, p.lens, pt);
+            else
+                LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D, PT>), grid,
+                       dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out,
+                       den, p.lens, pt);
+        };
+        // the first of two passes always has 32 tables (NW = 8); split runs have d = 64
+        if (p.part_mode == race::PART_NONE) {
+            go(std::integral_constant<int, race::PART_NONE>{});
+        } else if constexpr (D == race::HD) {
+            if (p.part_mode == race::PART_IN)
+                go(std::integral_constant<int, race::PART_IN>{});
+            else if constexpr (NW == 8)
+                go(std::integral_constant<int, race::PART_OUT>{});
+        }
     }
 }
 
@@ -367,12 +407,26 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
                  T *dX, float *dwp)
 {
     if constexpr (sizeof(T) == 2) {
-        if (dwp)
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D>), grid, dim3(NW * 64), Xr,
-                   vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, dwp, p.lens);
-        else
-            LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D>), grid, dim3(NW * 64), Xr, vr,
-                   vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX, nullptr, p.lens);
+        const race::Part pt = REVERSE ? p.part_dk : p.part_dq;
+        auto go = [&](auto part_c) {
+            constexpr int PT = decltype(part_c)::value;
+            if (dwp)
+                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D, PT>), grid,
+                       dim3(NW * 64), Xr, vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX,
+                       dwp, p.lens, pt);
+            else
+                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D, PT>), grid,
+                       dim3(NW * 64), Xr, vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX,
+                       nullptr, p.lens, pt);
+        };
+        if (p.part_mode == race::PART_NONE) {
+            go(std::integral_constant<int, race::PART_NONE>{});
+        } else if constexpr (D == race::HD) {
+            if (p.part_mode == race::PART_IN)
+                go(std::integral_constant<int, race::PART_IN>{});
+            else if constexpr (NW == 8)
+                go(std::integral_constant<int, race::PART_OUT>{});
+        }
     }
 }
 
@@ -604,6 +658,59 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     }
 }
 
+// L > 32 with 16-bit rows: the first 32 tables, then the other L - 32, as two
+// fused passes over the same rows.  The first stores its sums in fp32 (the
+// readout's n and m; dx_hat of Q and of K; dV) in partial arrays after both
+// passes' buffers, the second adds them before its last step.  Each pass has
+// its own buffers and saved state; dW rows are those of its tables.
+template <typename T>
+void split_forward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, const void *Q,
+                   const void *K, const void *V, const float *W, float tau, int causal, void *O,
+                   float *den, char *ws, float *saved, const Tracer &tr)
+{
+    Plan a, b;
+    make_plan(B, H, p.N, p.d, 32, p.P, chunk, dt, &a);
+    make_plan(B, H, p.N, p.d, p.L - 32, p.P, chunk, dt, &b);
+    a.lens = b.lens = p.lens;
+    float *pv = reinterpret_cast<float *>(ws + a.f_total + b.f_total);
+    float *pm = reinterpret_cast<float *>(reinterpret_cast<char *>(pv) +
+                                          align256((size_t)p.rows * race::HD * sizeof(float)));
+    a.part_o = b.part_o = race::Part{pv, pm};
+    a.part_mode = race::PART_OUT;
+    b.part_mode = race::PART_IN;
+    float *sb = saved ? reinterpret_cast<float *>(reinterpret_cast<char *>(saved) + a.s_total) : nullptr;
+    dispatch_forward<T>(a, Q, K, V, W, tau, causal, O, den, ws, saved, tr);
+    dispatch_forward<T>(b, Q, K, V, W + 32 * p.P * p.d, tau, causal, O, den, ws + a.f_total, sb, tr);
+}
+
+template <typename T>
+void split_backward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, const void *Q,
+                    const void *K, const void *V, const float *W, const void *O, const float *den,
+                    const void *dO, float tau, int causal, void *dQ, void *dK, void *dV, char *ws,
+                    const float *saved, const Tracer &tr, float *dW)
+{
+    Plan a, b;
+    make_plan(B, H, p.N, p.d, 32, p.P, chunk, dt, &a);
+    make_plan(B, H, p.N, p.d, p.L - 32, p.P, chunk, dt, &b);
+    a.lens = b.lens = p.lens;
+    const size_t ta = dW ? a.dw_total : a.b_total, tb = dW ? b.dw_total : b.b_total;
+    const size_t pvb = align256((size_t)p.rows * race::HD * sizeof(float));
+    char *pbase = ws + ta + tb;
+    const race::Part pq{reinterpret_cast<float *>(pbase), nullptr};
+    const race::Part pk{reinterpret_cast<float *>(pbase + pvb), nullptr};
+    const race::Part pd{reinterpret_cast<float *>(pbase + 2 * pvb), nullptr};
+    a.part_dq = b.part_dq = pq;
+    a.part_dk = b.part_dk = pk;
+    a.part_dv = b.part_dv = pd;
+    a.part_mode = race::PART_OUT;
+    b.part_mode = race::PART_IN;
+    const float *sb =
+        saved ? reinterpret_cast<const float *>(reinterpret_cast<const char *>(saved) + a.s_total) : nullptr;
+    dispatch_backward<T>(a, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, saved, tr, dW);
+    dispatch_backward<T>(b, Q, K, V, W + 32 * p.P * p.d, O, den, dO, tau, causal, dQ, dK, dV, ws + ta,
+                         sb, tr, dW ? dW + 32 * p.P * p.d : nullptr);
+}
+
 race_status_t check_trace(race_trace_t *trace)
 {
     if (!trace) return RACE_OK;
@@ -682,7 +789,7 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     Plan p;
     const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
-    if (for_backward == 2 && !p.fused) return RACE_ERR_UNSUPPORTED;
+    if (for_backward == 2 && !p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
     *bytes = for_backward == 2 ? p.dw_total : for_backward ? p.b_total : p.f_total;
     return RACE_OK;
 }
@@ -716,11 +823,15 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
     if ((st = check_trace(trace)) != RACE_OK) return st;
     if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
     p.lens.len = lens;
-    float *sv = p.fused ? static_cast<float *>(saved) : nullptr;
+    float *sv = p.fused || p.split ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
-    if (dt == RACE_BF16)
+    if (p.split && dt == RACE_BF16)
+        split_forward<bf16>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
+    else if (p.split)
+        split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
+    else if (dt == RACE_BF16)
         dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else if (dt == RACE_F16)
         dispatch_forward<_Float16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
@@ -741,17 +852,22 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
     Plan p;
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
-    if (dW && !p.fused) return RACE_ERR_UNSUPPORTED;
+    if (dW && !p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, dW ? p.dw_total : p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
     if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
     p.lens.len = lens;
-    const float *sv = p.fused ? static_cast<const float *>(saved) : nullptr;
+    const float *sv = p.fused || p.split ? static_cast<const float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
-    if (dt == RACE_BF16)
+    if (p.split && dt == RACE_BF16)
+        split_backward<bf16>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
+    else if (p.split)
+        split_backward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr,
+                                 dW);
+    else if (dt == RACE_BF16)
         dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
     else if (dt == RACE_F16)
         dispatch_backward<_Float16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
@@ -794,7 +910,11 @@ race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V
     const Tracer tr{nullptr, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
-    if (dt == RACE_BF16)
+    if (p.split && dt == RACE_BF16)
+        split_forward<bf16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+    else if (p.split)
+        split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+    else if (dt == RACE_BF16)
         dispatch_forward<bf16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
     else if (dt == RACE_F16)
         dispatch_forward<_Float16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);

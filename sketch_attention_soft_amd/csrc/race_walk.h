@@ -168,6 +168,7 @@ __device__ __forceinline__ float bldf(Rsrc r, int off)
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 __device__ __forceinline__ void bst64(u32x2 v, Rsrc r, int off) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0); }
+__device__ __forceinline__ void bst128(u32x4 v, Rsrc r, int off) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
 __device__ __forceinline__ void bstf(float v, Rsrc r, int off)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
@@ -196,6 +197,17 @@ __device__ __forceinline__ void for_chunks2(int n, F &&body)
         if (ci + 1 < n) body(ci + 1, Par<1>{});
     }
 }
+// Tables in two passes (L > 32: the first 32 tables, then the rest).  The
+// outputs are sums over tables before the last, nonlinear step, so the first
+// pass stores its sums in fp32 (PART_OUT) and the second adds them (PART_IN):
+// the readout's n and m before o = n / m, dV, and dx_hat before the
+// normalisation backward.  Partial rows are [token][64] fp32 (and m [token]).
+constexpr int PART_NONE = 0, PART_OUT = 1, PART_IN = 2;
+struct Part {
+    float *v;  // [rows][64]
+    float *m;  // [rows] (readout denominators) or null
+};
+
 // rows of a [token][D] array of 16-bit elements (D = d: 64, or 32 staged
 // into the 64 columns of the kernels with zeros past column D)
 template <int D, typename IO> __device__ __forceinline__ Rsrc row_res(const IO *seg_rows, const Chunk &c)
@@ -842,11 +854,12 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // One barrier per chunk: staging buffers and the partial outputs are double
 // buffered, and the partial outputs of chunk c are summed after the barrier
 // of chunk c + 1, beside that chunk's products.
-template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO, int D>
+template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO, int D,
+          int PART = PART_NONE>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
-    IO *__restrict__ Out, float *__restrict__ den, Lens ls)
+    IO *__restrict__ Out, float *__restrict__ den, Lens ls, Part part)
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = RSRC == 0;
@@ -876,6 +889,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         vh.den += row0;
     }
     IO *Os = Out + row0 * D;
+    float *pv = PART != PART_NONE ? part.v + row0 * HD : nullptr;
+    float *pm = PART != PART_NONE && !BWD ? part.m + row0 : nullptr;
     float *dens = BWD ? nullptr : den + row0;
     const _Float16 *rt_seg = rc.t ? rc.t + hc_seg<NW>(rc, bh, t_begin) : nullptr;
     const _Float16 *rc_seg = rc.c ? rc.c + hc_seg<NW>(rc, bh, t_begin) : nullptr;
@@ -974,15 +989,30 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                     n += *reinterpret_cast<const floatx4 *>(rn + (((ww * 2 + tt) * 4 + ct) * 64 + ln) * 4);
                 const int col = 16 * ct + 4 * (ln >> 4);  // columns past D are not stored
                 const int off = (D == HD || col < D) ? (tt * 16 + (ln & 15)) * (D * 2) + col * 2 : OOB;
+                const int tok = tt * 16 + (ln & 15);
+                if constexpr (PART != PART_NONE) {
+                    const Rsrc rp = make_rsrc(pv + c.tok0 * HD, c.nv * HD * 4);
+                    if constexpr (PART == PART_OUT)
+                        bst128(__builtin_bit_cast(u32x4, n), rp, tok * (HD * 4) + col * 4);
+                    else
+                        n += __builtin_bit_cast(floatx4, bld128(rp, tok * (HD * 4) + col * 4));
+                }
                 if (BWD) {
-                    bst64(u32x2{pk_io<IO>(n[0], n[1]), pk_io<IO>(n[2], n[3])}, ro, off);
+                    if constexpr (PART != PART_OUT)
+                        bst64(u32x2{pk_io<IO>(n[0], n[1]), pk_io<IO>(n[2], n[3])}, ro, off);
                 } else {
                     float m = rm[tt * 64 + (ln & 15)];
 #pragma unroll
                     for (int ww = 1; ww < NW; ++ww) m += rm[(ww * 2 + tt) * 64 + (ln & 15)];
-                    const float inv = __builtin_amdgcn_rcpf(m);
-                    bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
-                    bstf(m, make_rsrc(dens + c.tok0, c.nv * 4), (ct == 0 && ln < 16) ? (tt * 16 + ln) * 4 : OOB);
+                    const int moff = (ct == 0 && ln < 16) ? tok * 4 : OOB;
+                    if constexpr (PART == PART_OUT) {
+                        bstf(m, make_rsrc(pm + c.tok0, c.nv * 4), moff);
+                    } else {
+                        if constexpr (PART == PART_IN) m += bldf(make_rsrc(pm + c.tok0, c.nv * 4), tok * 4);
+                        const float inv = __builtin_amdgcn_rcpf(m);
+                        bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
+                        bstf(m, make_rsrc(dens + c.tok0, c.nv * 4), moff);
+                    }
                 }
             }
         }
@@ -1121,12 +1151,12 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 // 64 dims] on MFMA (both operands read transposed from du and the staged
 // rows), summed in LDS, and the workgroup's sum written to dwp[workgroup]
 // ([NW * 16][64] fp32) for a reduction over segments.
-template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D>
+template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D, int PART = PART_NONE>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
     const float *__restrict__ W, int L, int P, int64_t N, int seg, int64_t nseg,
     const float *__restrict__ st, HCache rc, HCache wc, IO *__restrict__ dX,
-    float *__restrict__ dwp, Lens ls)
+    float *__restrict__ dwp, Lens ls, Part part)
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
     constexpr int NTHR = NW * 64;
@@ -1166,6 +1196,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         vwh.den += row0;
     }
     IO *dXs = dX + row0 * D;
+    float *pv = PART != PART_NONE ? part.v + row0 * HD : nullptr;
     const _Float16 *rt_seg = rc.t + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *wt_seg = wc.t ? wc.t + hc_seg<NW>(wc, bh, t_begin) : nullptr;
@@ -1225,7 +1256,13 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     floatx4 dxh[TPWV];
     bf16x4 xkeep[TPWV];
     float sskeep[TPWV];
-    auto dxh_tiles = [&](int pb) {
+    // (ci: the chunk whose du is in buffer pb, for the partial sums of dx_hat)
+    auto dxh_tiles = [&](int pb, int ci) {
+        Rsrc rp;
+        if constexpr (PART != PART_NONE) {
+            const Chunk c = chunk(ci);
+            rp = make_rsrc(pv + c.tok0 * HD, c.nv * HD * 4);
+        }
 #pragma unroll
         for (int i = 0; i < TPWV; ++i) {
             const int tile = w + NW * i, tt = tile >> 2, nt = tile & 3, tok = tt * 16 + c16;
@@ -1236,6 +1273,12 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + 32 * k + 8 * g;
                 mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow), dub);
             }
+            if constexpr (PART == PART_OUT) {
+                bst128(__builtin_bit_cast(u32x4, xa), rp, tok * (HD * 4) + (nt * 16 + 4 * g) * 4);
+                continue;
+            }
+            if constexpr (PART == PART_IN)
+                xa += __builtin_bit_cast(floatx4, bld128(rp, tok * (HD * 4) + (nt * 16 + 4 * g) * 4));
             const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[pb] + tok * XRS + nt * 16 + 4 * g);
             float dot = 0.f;
 #pragma unroll
@@ -1273,6 +1316,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     // dots in dotp[pb]: dx = (dxh - x (x . dxh) / |x|^2) / |x| for
     // |x| > 1e-12, else dxh 1e12
     auto finish = [&](int ci, int pb) {
+        if constexpr (PART == PART_OUT) return;  // dx_hat went to the partial sums
         const Rsrc rdx = row_res<D>(dXs, chunk(ci));
 #pragma unroll
         for (int i = 0; i < TPWV; ++i) {
@@ -1409,7 +1453,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             *reinterpret_cast<bf16x4 *>(du_l[b] + (tt * 16 + c16) * DUS + w * 16 + 4 * g) =
                 pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
         }
-        dxh_tiles(b ^ 1);  // (before the first chunk: unused values)
+        dxh_tiles(b ^ 1, ci - 1);  // (before the first chunk: unused values)
         if constexpr (DW) {
             if (ci >= 1) dw_tiles(b ^ 1);
         }
@@ -1418,7 +1462,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         const int pl = (nch - 1) & 1;  // buffers of the last chunk
         lds_barrier();
         if (nch >= 2) finish(nch - 2, pl ^ 1);
-        dxh_tiles(pl);
+        dxh_tiles(pl, nch - 1);
         if constexpr (DW) dw_tiles(pl);
         lds_barrier();
         finish(nch - 1, pl);

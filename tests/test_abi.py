@@ -88,8 +88,8 @@ def test_workspace_sizes(lib):
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
     (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
     (dict(d=32, L=33), E_UNSUP), (dict(P=5), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
-    (dict(P=2, L=33), E_UNSUP), (dict(P=0), E_SHAPE), (dict(L=65), E_UNSUP),
-    (dict(L=33, dt=F32), E_UNSUP), (dict(L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
+    (dict(P=0), E_SHAPE), (dict(L=65), E_UNSUP),
+    (dict(L=33, dt=F32), E_UNSUP), (dict(d=32, L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
     (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
 ])
 def test_workspace_validation(lib, kw, code):
@@ -131,7 +131,11 @@ def test_saved_bytes(lib):
     assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, F16, ctypes.byref(o16)) == OK
     assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, ctypes.byref(ob)) == OK
     assert o16.value == ob.value > 0
-    assert fn(1, 1, 1 << 16, 64, 64, 4, 1, 0, BF16, ctypes.byref(out)) == OK and out.value == 0
+    # L > 32 (two passes of the fused kernels): both passes' saved states
+    o32, o64 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, ctypes.byref(o32)) == OK
+    assert fn(1, 1, 1 << 16, 64, 64, 4, 1, 0, BF16, ctypes.byref(o64)) == OK
+    assert o64.value == 2 * o32.value
     assert fn(1, 1, 1 << 16, 64, 32, 4, 1, 0, BF16, None) == E_NULL
     assert fn(1, 1, 0, 64, 32, 4, 1, 0, BF16, ctypes.byref(out)) == E_SHAPE
 
@@ -357,7 +361,7 @@ def test_backward_dw_validation(lib):
     st2, b2 = ws_bytes(lib, L=32, bwd=2)
     assert st1 == OK and st2 == OK and b2 > b1
     assert ws_bytes(lib, L=32, dt=F32, bwd=2)[0] == E_UNSUP
-    assert ws_bytes(lib, L=64, bwd=2)[0] == E_UNSUP
+    assert ws_bytes(lib, L=64, bwd=2)[0] == OK and ws_bytes(lib, L=64, dt=F32, bwd=2)[0] == E_UNSUP
     args = [F] * 7 + [32, 4, 1.0, 1, 1, 1, 1024, 64, BF16, 0, F, F, F, F, F * 16, 1 << 40, None,
                       None, None]
     bad = list(args)
