@@ -239,7 +239,7 @@ def forward_hard(q, k, v, W, causal: bool, chunk: int = 0, workspace=None, out=N
 def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, workspace=None,
              out=None, trace: Trace | None = None, saved=None, dw: bool = False):
     """RACE attention backward; returns (dq, dk, dv), and dW last with dw=True
-    (race_attn_backward_dw: bf16, L <= 32).  out = (dq, dk, dv) reuses buffers;
+    (race_attn_backward_dw: bf16 or fp16 rows).  out = (dq, dk, dv) reuses buffers;
     saved: the buffer the forward of the same inputs filled, or None."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v, o, do)
@@ -340,7 +340,7 @@ def backward_padded(q, k, v, W, o, den, do, seqlens, tau: float, causal: bool,
 
 class RaceAttention(torch.autograd.Function):
     """Autograd wrapper: o = race_attention(q, k, v, W).  W gets a gradient when
-    it requires one (learned hyperplanes; bf16 inputs with L <= 32)."""
+    it requires one (learned hyperplanes; bf16 or fp16 inputs)."""
 
     @staticmethod
     def forward(ctx, q, k, v, W, tau, causal, chunk=0):
@@ -369,7 +369,7 @@ def race_attention(q, k, v, W, tau: float = 1.0, causal: bool = True, chunk: int
 class RaceAttentionLayer(torch.nn.Module):
     """Drop-in attention core on [B, H, N, d] tensors: o = race_attention(q, k, v, W)
     with W [L, P, d] drawn from N(0, 1) (the pages' random hyperplanes), kept as a
-    buffer, or as a parameter with learn_projection=True (bf16, L <= 32)."""
+    buffer, or as a parameter with learn_projection=True (bf16 or fp16)."""
 
     def __init__(self, d: int = 64, L: int = 32, P: int = 4, tau: float = 1.0,
                  causal: bool = True, chunk: int = 0, learn_projection: bool = False,
