@@ -483,6 +483,12 @@ def stream_bench(args, binding, I, np, torch) -> int:
                    1)
     flops_tok = 2 * F * (d + 1) + 2 * d * L * P
     tflops = flops_tok * w.N / (ms_add * 1e-3) / 1e12
+    # the same add through the fused segment sum (bf16 operands, fp32 sums)
+    wsf = torch.empty(binding.workspace_bytes(1, 1, w.N, d, L, P, True, 0, torch.bfloat16, False),
+                      dtype=torch.uint8, device=dev)
+    ms_fast = timed(lambda: binding.state_add(sa, ka, va, Wa, tau, workspace=wsf, fast=True),
+                    max(args.steps, 3), 1)
+    tf_fast = flops_tok * w.N / (ms_fast * 1e-3) / 1e12
 
     line = {
         "metric": "RACE streaming decode tokens/s (64 heads x 1 token, L=32, d=64, bf16 rows, "
@@ -503,6 +509,12 @@ def stream_bench(args, binding, I, np, torch) -> int:
                                    "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                                    "frac": round(tflops / PEAK_TFLOPS["f32"], 5),
                                    "flops_per_token": flops_tok}},
+        "state_add_fast": {"workload": w.name, "tokens": w.N, "ms": round(ms_fast, 4),
+                           "tokens_per_s": round(w.N / (ms_fast * 1e-3), 1),
+                           "roofline": {"bound": "mfma", "achieved": round(tf_fast, 3),
+                                        "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                                        "frac": round(tf_fast / PEAK_TFLOPS["bf16"], 5),
+                                        "flops_per_token": flops_tok}},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -269,6 +269,20 @@ race_status_t race_attn_state_add(const void *K, const void *V, const float *W, 
                                   float tau, int B, int H, int64_t N, int d, race_dtype_t dt,
                                   float *state, void *workspace, size_t ws_bytes, void *stream);
 
+/* race_attn_state_add through the fused matrix-core kernels (RACE_BF16 /
+ * RACE_F16 rows, L <= 32, d = 32 or 64): the keys' segment sums of the
+ * forward (bf16 features and values, fp32 sums) and their scan give the
+ * total, which is added into the state.  Much faster for long prompts; the
+ * state then carries the bf16 rounding of the features and values (about
+ * 1e-3 relative, the forward's own precision) instead of race_attn_state_add's
+ * fp32 arithmetic.  workspace: race_attn_workspace_bytes(B, H, N, d, L, P, 1,
+ * 0, dt, 0, ...) bytes, 256-byte aligned.  RACE_ERR_UNSUPPORTED for other
+ * configurations. */
+race_status_t race_attn_state_add_fast(const void *K, const void *V, const float *W, int L, int P,
+                                       float tau, int B, int H, int64_t N, int d,
+                                       race_dtype_t dt, float *state, void *workspace,
+                                       size_t ws_bytes, void *stream);
+
 /* Decode step: appends T tokens per head in order and returns their causal
  * outputs; token i reads the state after its own key is added (step 5: keys
  * j <= i).  Q, K, V: [B][H][T][d] (type dt); O: [B][H][T][d] (type dt); den:

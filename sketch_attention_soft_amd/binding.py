@@ -25,6 +25,7 @@ EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forw
            "race_attn_backward_padded",
            "race_attn_squash_coeffs", "race_attn_squash_deriv_coeffs",
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
+           "race_attn_state_add_fast",
            "race_attn_decode", "race_attn_state_readout", "race_attn_status_string")
 TRACE_MAX = 24
 
@@ -112,6 +113,8 @@ def lib():
         L.race_attn_state_add.argtypes = [vp, vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
                                           vp, sz, vp]
         L.race_attn_state_add.restype = i32
+        L.race_attn_state_add_fast.argtypes = L.race_attn_state_add.argtypes
+        L.race_attn_state_add_fast.restype = i32
         L.race_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
                                        vp, vp, vp]
         L.race_attn_decode.restype = i32
@@ -419,18 +422,25 @@ def state_add_workspace_bytes(B, H, N, d, L, P) -> int:
     return out.value
 
 
-def state_add(state, k, v, W, tau: float, workspace=None):
-    """state += the sums of the rows of k, v ([B, H, N, d]); returns state."""
+def state_add(state, k, v, W, tau: float, workspace=None, fast: bool = False):
+    """state += the sums of the rows of k, v ([B, H, N, d]); returns state.
+    fast: through the fused matrix-core kernels (race_attn_state_add_fast:
+    bf16 / fp16 rows, L <= 32; the forward's bf16 precision)."""
     B, H, N, d = _shape(k)
     _check_tensors(k, v)
     L, P = _check_w(W, k)
     _check_state(state, B, H, d, L, P, k)
-    nbytes = state_add_workspace_bytes(B, H, N, d, L, P)
+    if fast:
+        nbytes = workspace_bytes(B, H, max(N, 1), d, L, P, True, 0, k.dtype, False)
+        fn = lib().race_attn_state_add_fast
+    else:
+        nbytes = state_add_workspace_bytes(B, H, N, d, L, P)
+        fn = lib().race_attn_state_add
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
-    _check(lib().race_attn_state_add(k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P, float(tau),
-                                     B, H, N, d, dtype_code(k.dtype), state.data_ptr(),
-                                     workspace.data_ptr(), workspace.numel(), _stream()))
+    _check(fn(k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P, float(tau), B, H, N, d,
+              dtype_code(k.dtype), state.data_ptr(), workspace.data_ptr(), workspace.numel(),
+              _stream()))
     return state
 
 

@@ -711,6 +711,50 @@ void split_backward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, con
                          sb, tr, dW ? dW + 32 * p.P * p.d : nullptr);
 }
 
+// Bulk add through the fused segment sum (16-bit rows, L <= 32): the keys'
+// segment sums and their scan give the head total, which is added into the
+// streaming state in its own layout and scale.
+template <typename T, int NW, int D>
+void fused_state_add(const Plan &p, const T *K, const T *V, const float *W, float tau, char *ws,
+                     float *state, const Tracer &tr)
+{
+    constexpr int WS = 2 * NW;
+    const race::Squash sq = fit_squash(tau, RACE_BF16);
+    const dim3 nblk((unsigned)(p.BH * p.nseg));
+    const race::ValSrc<T> vv{V, nullptr, nullptr};
+    float *st = reinterpret_cast<float *>(ws + p.f_st);
+    const race::HCache hk = hcache(p, ws + p.f_hc, 0, -1), none = hcache(p, nullptr, -1, -1);
+    launch_sum<WS, false, 0, 1, D>(tr, "sum_kv", nblk, sq, K, vv, W, p, none, hk, st);
+    launch_scan(tr, "scan_kv", p, st, reinterpret_cast<float *>(ws + p.f_scan), 0);
+    const int total = WS * 4 * race::NT * 64 * 4;
+    tr.begin("state_from_sums");
+    hipLaunchKernelGGL(race::stream_from_sums_kernel, dim3((total + 255) / 256, (unsigned)p.BH),
+                       dim3(256), 0, tr.s, st, p.nseg, WS, p.L, p.d, std::sqrt(std::ldexp(1.f, p.P)),
+                       state);
+    tr.end();
+}
+
+template <typename T>
+void dispatch_fused_state_add(const Plan &p, const void *K, const void *V, const float *W,
+                              float tau, char *ws, float *state, const Tracer &tr)
+{
+    auto k = static_cast<const T *>(K);
+    auto v = static_cast<const T *>(V);
+    if (p.d == 32) {
+        switch (p.nw) {
+        case 1: fused_state_add<T, 1, 32>(p, k, v, W, tau, ws, state, tr); break;
+        case 2: fused_state_add<T, 2, 32>(p, k, v, W, tau, ws, state, tr); break;
+        default: fused_state_add<T, 4, 32>(p, k, v, W, tau, ws, state, tr); break;
+        }
+    } else {
+        switch (p.nw) {
+        case 1: fused_state_add<T, 1, race::HD>(p, k, v, W, tau, ws, state, tr); break;
+        case 2: fused_state_add<T, 2, race::HD>(p, k, v, W, tau, ws, state, tr); break;
+        default: fused_state_add<T, 4, race::HD>(p, k, v, W, tau, ws, state, tr); break;
+        }
+    }
+}
+
 race_status_t check_trace(race_trace_t *trace)
 {
     if (!trace) return RACE_OK;
@@ -1052,6 +1096,32 @@ race_status_t race_attn_state_add(const void *K, const void *V, const float *W, 
                                            nullptr, nullptr, s);
     hipLaunchKernelGGL(race::stream_reduce_kernel, dim3((unsigned)((sp.elems + 255) / 256), sp.BH),
                        dim3(256), 0, s, part, (int)nblk, sp.elems, state);
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_state_add_fast(const void *K, const void *V, const float *W, int L, int P,
+                                       float tau, int B, int H, int64_t N, int d,
+                                       race_dtype_t dt, float *state, void *workspace,
+                                       size_t ws_bytes, void *stream)
+{
+    if (!W || !state) return RACE_ERR_NULL;
+    StreamPlan sp;
+    race_status_t st = stream_plan(B, H, N, d, L, P, dt, &sp);
+    if (st != RACE_OK) return st;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if (N == 0) return RACE_OK;  // the row pointers may be NULL then
+    if (!K || !V) return RACE_ERR_NULL;
+    Plan p;
+    if ((st = make_plan(B, H, N, d, L, P, 0, dt, &p)) != RACE_OK) return st;
+    if (!p.fused) return RACE_ERR_UNSUPPORTED;
+    if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
+    const Tracer tr{nullptr, static_cast<hipStream_t>(stream)};
+    (void)hipGetLastError();
+    char *ws = static_cast<char *>(workspace);
+    if (dt == RACE_BF16)
+        dispatch_fused_state_add<bf16>(p, K, V, W, tau, ws, state, tr);
+    else
+        dispatch_fused_state_add<_Float16>(p, K, V, W, tau, ws, state, tr);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 

@@ -253,3 +253,36 @@ __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restr
 }
 
 }  // namespace race
+
+namespace race {
+
+// state[head] += scale x (the key-state total of a fused segment sum).  The
+// total is slot nseg of the head's segment states, FxC blocks
+// [wave][s][ct][lane][4]: element (w, s, ct, lane (g, c16), r) is feature
+// 16 (4 w + g) + 4 s + r (table 4 w + g, Walsh subset 4 s + r) and value
+// column 16 ct + c16, column HD being the count column.  Tables >= L and the
+// padding columns are skipped.  scale = 2^(P/2): the fused writer features
+// are 2^-P prod t, the streaming state's 2^(-P/2) prod t.
+__global__ __launch_bounds__(256) void stream_from_sums_kernel(const float *__restrict__ st,
+                                                               int64_t nseg, int nwaves, int L,
+                                                               int d, float scale,
+                                                               float *__restrict__ state)
+{
+    const int per_wave = 4 * NT * 64 * 4;
+    const int total = nwaves * per_wave;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const int64_t bh = blockIdx.y;
+    const int r = e & 3, lane = (e >> 2) & 63, wsct = e >> 8;
+    const int ct = wsct % NT, s = (wsct / NT) & 3, w = wsct / (NT * 4);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int table = 4 * w + g, col = 16 * ct + c16;
+    const int c = col < d ? col : col == HD ? d : -1;
+    if (table >= L || c < 0) return;
+    const int sc = d + 1, f = 16 * table + 4 * s + r;
+    const float v = st[(bh * (nseg + 1) + nseg) * (int64_t)total + e];
+    float *dst = state + bh * (int64_t)(16 * L) * sc + (int64_t)f * sc + c;
+    *dst += scale * v;
+}
+
+}  // namespace race

@@ -422,3 +422,16 @@ def test_padded_validation(lib):
     ok[21] = None
     ok[15] = 7  # unsupported dtype code: rejected before anything is enqueued
     assert bwd(*ok) == E_UNSUP
+
+
+def test_state_add_fast_validation(lib):
+    L = _stream_lib(lib)
+    F = FAKE
+    fn = lib.race_attn_state_add_fast
+    fn.argtypes = L.race_attn_state_add.argtypes
+    assert fn(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, None, F, 1 << 30, None) == E_NULL
+    assert fn(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, F32, F, F, 1 << 30, None) == E_UNSUP   # fp32 rows
+    assert fn(F, F, F, 33, 4, 1.0, 1, 1, 64, 64, BF16, F, F, 1 << 30, None) == E_UNSUP  # L > 32
+    assert fn(F, F, F, 8, 4, 0.0, 1, 1, 64, 64, BF16, F, F, 1 << 30, None) == E_TAU
+    assert fn(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, F, F, 16, None) == E_WS
+    assert fn(None, None, F, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, None, 0, None) == OK      # N = 0
