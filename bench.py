@@ -49,7 +49,9 @@ def algorithmic_per_token(w, dw: bool = False):
         "sum_kv": proj + 2 * F * d1,            # hash K, sketch of the keys
         "fwd_o": proj + 2 * F * d1,             # hash Q, readout
         "sum_qd": proj + 2 * F * d1,            # recomputed hash Q, gradient sketch
-        "dq": proj + 2 * F * d1 + proj,         # hash Q, query-side gradient, dx_hat = du W
+        # (the backward's recomputed hash of Q is counted once, in sum_qd; dq
+        # reads it, so that the kernels' shares add up to the step's total)
+        "dq": 2 * F * d1 + proj,                # query-side gradient, dx_hat = du W
         "dk": proj + 2 * F * d + proj,          # hash K, dphi(k), dx_hat = du W
         "dv": 2 * F * d,                        # dV readout
         # unfused kernels (fp32, L > 32)
