@@ -23,18 +23,35 @@ sys.path.insert(0, HERE)
 
 METRIC = "RACE attn fwd+bwd tokens/s at N=4M causal d=64; % of MFMA/HBM roofline"
 
+
+def metric_name(w) -> str:
+    """The headline workload keeps the library's headline metric string; the
+    others name their own shape and passes."""
+    if w.name == "causal_n4m_bf16":
+        return METRIC
+    passes = "fwd+bwd" if w.backward else "fwd"
+    mode = "causal" if w.causal else "non-causal"
+    n = f"{w.N / 1e6:g}M" if w.N >= 1_000_000 else (f"{w.N // 1024}K" if w.N % 1024 == 0 else str(w.N))
+    heads = f" B*H={w.B * w.H}" if w.B * w.H > 1 else ""
+    tail = ("; latency-bound, see latency_us" if not w.backward and w.tokens <= 4096
+            else "; % of MFMA/HBM roofline")
+    return (f"RACE attn {passes} tokens/s at N={n}{heads} {mode} d={w.d} L={w.L} {w.dtype}"
+            f"{tail}")
+
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
-def algorithmic_per_token(w, dw: bool = False):
+def algorithmic_per_token(w, dw: bool = False, saved: bool = True):
     """Algorithmic work of the method per token (one (b, h) row).
 
-    flops: projections 2 d L P per hashed row (Q and K in the forward; again
-    for the recomputed hash and the dx_hat = du W product of Q and K in the
-    backward), sketch and readout 2 F (d+1) each, the query-side gradient
-    2 F (d+1), the gradient sketch 2 F (d+1), dV and dphi(k) 2 F d each.
+    flops: projections 2 d L P per hashed row (Q and K in the forward, and
+    the dx_hat = du W product of Q and of K in the backward), sketch and
+    readout 2 F (d+1) each, the query-side gradient 2 F (d+1), the gradient
+    sketch 2 F (d+1), dV and dphi(k) 2 F d each.  saved = False: the
+    backward also recomputes the hash of Q and K (2 d L P each); with the
+    forward's saved state (how the step is timed) it reads them instead.
     bytes: one read of every input and one write of every output per pass.
     dw: the backward also forms the projection gradient, 2 d L P per row of Q
     (in dq) and of K (in dk).
@@ -44,15 +61,14 @@ def algorithmic_per_token(w, dw: bool = False):
     e = 2 if w.dtype == "bf16" else 4
     proj = 2 * d * L * P
     # kernels that hash their own rows carry those projections
+    rehash = 0 if saved else proj
     per_kernel = {
         # fused kernels (bf16, L <= 32)
         "sum_kv": proj + 2 * F * d1,            # hash K, sketch of the keys
         "fwd_o": proj + 2 * F * d1,             # hash Q, readout
-        "sum_qd": proj + 2 * F * d1,            # recomputed hash Q, gradient sketch
-        # (the backward's recomputed hash of Q is counted once, in sum_qd; dq
-        # reads it, so that the kernels' shares add up to the step's total)
+        "sum_qd": rehash + 2 * F * d1,          # (recomputed hash Q), gradient sketch
         "dq": 2 * F * d1 + proj,                # query-side gradient, dx_hat = du W
-        "dk": proj + 2 * F * d + proj,          # hash K, dphi(k), dx_hat = du W
+        "dk": rehash + 2 * F * d + proj,        # (recomputed hash K), dphi(k), dx_hat = du W
         "dv": 2 * F * d,                        # dV readout
         # unfused kernels (fp32, L > 32)
         "hash_q": proj, "hash_k": proj,
@@ -66,7 +82,8 @@ def algorithmic_per_token(w, dw: bool = False):
         per_kernel["dq"] += proj
         per_kernel["dk"] += proj
     fwd_flops = 4 * d * L * P + 4 * F * d1
-    bwd_flops = 8 * d * L * P + 4 * F * d1 + 4 * F * d + (4 * d * L * P if dw else 0)
+    bwd_flops = (4 * d * L * P + 2 * rehash + 4 * F * d1 + 4 * F * d
+                 + (4 * d * L * P if dw else 0))
     if not w.backward:
         return fwd_flops, 4 * d * e + 4, per_kernel
     return fwd_flops + bwd_flops, 12 * d * e + 8, per_kernel
@@ -249,8 +266,9 @@ def main() -> int:
                          f"{'fwd+bwd' if w.backward else 'fwd'} in fp64 ({dt:.1f} s)"}
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric_name(w), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "latency_us": round(ms * 1e3, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded Philox N(0,1); Q, K rows L2-normalised)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "L": w.L,
@@ -486,7 +504,7 @@ def stream_bench(args, binding, I, np, torch) -> int:
     flops_tok = 2 * F * (d + 1) + 2 * d * L * P
     tflops = flops_tok * w.N / (ms_add * 1e-3) / 1e12
     # the same add through the fused segment sum (bf16 operands, fp32 sums)
-    wsf = torch.empty(binding.workspace_bytes(1, 1, w.N, d, L, P, True, 0, torch.bfloat16, False),
+    wsf = torch.empty(binding.workspace_bytes(1, 1, w.N, d, L, P, True, 0, torch.bfloat16, 3),
                       dtype=torch.uint8, device=dev)
     ms_fast = timed(lambda: binding.state_add(sa, ka, va, Wa, tau, workspace=wsf, fast=True),
                     max(args.steps, 3), 1)

@@ -83,8 +83,10 @@ typedef enum {
 typedef enum { RACE_F32 = 0, RACE_BF16 = 1, RACE_F16 = 2 } race_dtype_t;
 
 /* Workspace size, in bytes, that race_attn_forward (for_backward = 0),
- * race_attn_backward (for_backward = 1) or race_attn_backward_dw
- * (for_backward = 2; RACE_ERR_UNSUPPORTED where that entry point is) needs
+ * race_attn_backward (for_backward = 1), race_attn_backward_dw
+ * (for_backward = 2; RACE_ERR_UNSUPPORTED where that entry point is) or
+ * race_attn_state_add_fast (for_backward = 3, with causal = 1, chunk = 0;
+ * RACE_ERR_UNSUPPORTED where that entry point is) needs
  * for this problem.  Pure host function; `bytes` (host pointer) receives the
  * size. */
 race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, int P,
@@ -276,8 +278,8 @@ race_status_t race_attn_state_add(const void *K, const void *V, const float *W, 
  * state then carries the bf16 rounding of the features and values (about
  * 1e-3 relative, the forward's own precision) instead of race_attn_state_add's
  * fp32 arithmetic.  workspace: race_attn_workspace_bytes(B, H, N, d, L, P, 1,
- * 0, dt, 0, ...) bytes, 256-byte aligned.  RACE_ERR_UNSUPPORTED for other
- * configurations. */
+ * 0, dt, 3, ...) bytes (the segment states and the scan's group totals),
+ * 256-byte aligned.  RACE_ERR_UNSUPPORTED for other configurations. */
 race_status_t race_attn_state_add_fast(const void *K, const void *V, const float *W, int L, int P,
                                        float tau, int B, int H, int64_t N, int d,
                                        race_dtype_t dt, float *state, void *workspace,
@@ -303,6 +305,7 @@ race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int 
 
 /* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);
+
 
 #ifdef __cplusplus
 }

@@ -182,8 +182,67 @@ def _check_tensors(ref: torch.Tensor, *ts: torch.Tensor) -> None:
             raise ValueError("Q, K, V (and O, dO) must share shape, dtype and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _require_gpu(ref: torch.Tensor) -> None:
+    """Last check before the library is called: every argument check above
+    it runs on any device, so that mistakes are reported the same way
+    everywhere."""
     if ref.device.type != "cuda":
         raise ValueError("tensors must be on a GPU")
+
+
+def _check_out(t, shape, dtype, device, name):
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+
+
+def _outputs_fwd(q, out, alloc=torch.empty):
+    """(o, den) for a forward or readout over the rows of q: new, or out checked."""
+    B, H, N, _ = q.shape
+    if out is None:
+        return alloc(q.shape, dtype=q.dtype, device=q.device), alloc(
+            (B, H, N), dtype=torch.float32, device=q.device)
+    o, den = out
+    _check_out(o, q.shape, q.dtype, q.device, "o")
+    _check_out(den, (B, H, N), torch.float32, q.device, "den")
+    return o, den
+
+
+def _outputs_bwd(q, out, alloc):
+    if out is None:
+        return alloc(q), alloc(q), alloc(q)
+    for t, n in zip(out, ("dq", "dk", "dv")):
+        _check_out(t, q.shape, q.dtype, q.device, n)
+    return tuple(out)
+
+
+def _check_den(den, q):
+    B, H, N, _ = q.shape
+    _check_out(den, (B, H, N), torch.float32, q.device, "den")
+
+
+def _check_saved(saved, B, H, N, d, L, P, causal, chunk, q):
+    """A saved-state buffer must be a uint8 device tensor of at least
+    saved_bytes(...) bytes (the library cannot check its size)."""
+    if saved is None:
+        return
+    need = saved_bytes(B, H, N, d, L, P, causal, chunk, q.dtype)
+    if (not isinstance(saved, torch.Tensor) or saved.dtype != torch.uint8
+            or saved.device != q.device or not saved.is_contiguous() or saved.numel() < need):
+        raise ValueError(f"saved must be a contiguous uint8 tensor of at least {need} bytes "
+                         f"on {q.device} (new_saved)")
+
+
+def _workspace(ws, nbytes, device):
+    """The caller's workspace as bytes when it is a contiguous tensor on the
+    device with at least nbytes bytes, else a new one."""
+    if (ws is not None and ws.device == device and ws.is_contiguous()
+            and ws.numel() * ws.element_size() >= nbytes):
+        return ws.reshape(-1).view(torch.uint8)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def _stream() -> int:
@@ -200,17 +259,12 @@ def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None
     saved (from new_saved) receives the key state for the backward."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v)
-    if W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous() or W.device != q.device:
-        raise ValueError("W must be a contiguous fp32 [L, P, d] tensor on the same device")
-    L, P, _ = W.shape
-    if out is None:
-        o = torch.empty_like(q)
-        den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    else:
-        o, den = out
+    L, P = _check_w(W, q)
+    o, den = _outputs_fwd(q, out)
+    _check_saved(saved, B, H, N, d, L, P, causal, chunk, q)
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
     _check(lib().race_attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L,
                                       P, float(tau), int(causal), B, H, N, d,
                                       dtype_code(q.dtype), chunk, o.data_ptr(), den.data_ptr(),
@@ -224,14 +278,10 @@ def forward_hard(q, k, v, W, causal: bool, chunk: int = 0, workspace=None, out=N
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v)
     L, P = _check_w(W, q)
-    if out is None:
-        o = torch.empty_like(q)
-        den = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    else:
-        o, den = out
+    o, den = _outputs_fwd(q, out)
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
     _check(lib().race_attn_forward_hard(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L,
                                         P, int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
                                         o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
@@ -246,16 +296,13 @@ def backward(q, k, v, W, o, den, do, tau: float, causal: bool, chunk: int = 0, w
     saved: the buffer the forward of the same inputs filled, or None."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v, o, do)
-    if den.dtype != torch.float32 or den.shape != (B, H, N) or not den.is_contiguous():
-        raise ValueError("den must be a contiguous fp32 [B, H, N] tensor")
-    L, P, _ = W.shape
-    if out is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    else:
-        dq, dk, dv = out
+    _check_den(den, q)
+    L, P = _check_w(W, q)
+    _check_saved(saved, B, H, N, d, L, P, causal, chunk, q)
+    dq, dk, dv = _outputs_bwd(q, out, torch.empty_like)
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, 2 if dw else 1)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
     if dw:
         gW = torch.empty_like(W)
         _check(lib().race_attn_backward_dw(
@@ -298,14 +345,10 @@ def forward_padded(q, k, v, W, seqlens, tau: float, causal: bool, chunk: int | N
     _check_tensors(q, k, v)
     L, P = _check_w(W, q)
     _check_lens(seqlens, q)
-    if out is None:
-        o = torch.zeros_like(q)
-        den = torch.zeros((B, H, N), dtype=torch.float32, device=q.device)
-    else:
-        o, den = out
+    o, den = _outputs_fwd(q, out, torch.zeros)
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
     _check(lib().race_attn_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
                                           L, P, float(tau), int(causal), B, H, N, d,
                                           dtype_code(q.dtype), chunk, seqlens.data_ptr(),
@@ -324,15 +367,13 @@ def backward_padded(q, k, v, W, o, den, do, seqlens, tau: float, causal: bool,
     chunk = padded_chunk(B, H, N) if chunk is None else chunk
     _check_tensors(q, k, v, o, do)
     L, P = _check_w(W, q)
+    _check_den(den, q)
     _check_lens(seqlens, q)
-    if out is None:
-        dq, dk, dv = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
-    else:
-        dq, dk, dv = out
+    dq, dk, dv = _outputs_bwd(q, out, torch.zeros_like)
     gW = torch.empty_like(W) if dw else None
     nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, 2 if dw else 1)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
     _check(lib().race_attn_backward_padded(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), o.data_ptr(), den.data_ptr(),
         do.data_ptr(), L, P, float(tau), int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
@@ -393,8 +434,12 @@ class RaceAttentionLayer(torch.nn.Module):
 # Streaming state (race_attn_state_* / race_attn_decode in include/race_attn.h)
 
 def _check_w(W, ref):
-    if W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous() or W.device != ref.device:
-        raise ValueError("W must be a contiguous fp32 [L, P, d] tensor on the same device")
+    """W must be a contiguous fp32 [L, P, d] tensor on the rows' device, with
+    d the rows' width (the library takes no width for W)."""
+    if (W.dtype != torch.float32 or W.dim() != 3 or not W.is_contiguous()
+            or W.device != ref.device or W.shape[2] != ref.shape[-1]):
+        raise ValueError("W must be a contiguous fp32 [L, P, d] tensor on the rows' device, "
+                         "with d the rows' width")
     return W.shape[0], W.shape[1]
 
 
@@ -431,13 +476,13 @@ def state_add(state, k, v, W, tau: float, workspace=None, fast: bool = False):
     L, P = _check_w(W, k)
     _check_state(state, B, H, d, L, P, k)
     if fast:
-        nbytes = workspace_bytes(B, H, max(N, 1), d, L, P, True, 0, k.dtype, False)
+        nbytes = workspace_bytes(B, H, max(N, 1), d, L, P, True, 0, k.dtype, 3)
         fn = lib().race_attn_state_add_fast
     else:
         nbytes = state_add_workspace_bytes(B, H, N, d, L, P)
         fn = lib().race_attn_state_add
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    _require_gpu(k)
+    workspace = _workspace(workspace, nbytes, k.device)
     _check(fn(k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P, float(tau), B, H, N, d,
               dtype_code(k.dtype), state.data_ptr(), workspace.data_ptr(), workspace.numel(),
               _stream()))
@@ -451,11 +496,8 @@ def decode(state, q, k, v, W, tau: float, out=None):
     _check_tensors(q, k, v)
     L, P = _check_w(W, q)
     _check_state(state, B, H, d, L, P, q)
-    if out is None:
-        o = torch.empty_like(q)
-        den = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    else:
-        o, den = out
+    o, den = _outputs_fwd(q, out)
+    _require_gpu(q)
     _check(lib().race_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P,
                                   float(tau), B, H, T, d, dtype_code(q.dtype), state.data_ptr(),
                                   o.data_ptr(), den.data_ptr(), _stream()))
@@ -468,11 +510,8 @@ def state_readout(state, q, W, tau: float, out=None):
     _check_tensors(q)
     L, P = _check_w(W, q)
     _check_state(state, B, H, d, L, P, q)
-    if out is None:
-        o = torch.empty_like(q)
-        den = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    else:
-        o, den = out
+    o, den = _outputs_fwd(q, out)
+    _require_gpu(q)
     _check(lib().race_attn_state_readout(q.data_ptr(), W.data_ptr(), L, P, float(tau), B, H, T,
                                          d, dtype_code(q.dtype), state.data_ptr(), o.data_ptr(),
                                          den.data_ptr(), _stream()))

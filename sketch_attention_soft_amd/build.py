@@ -1,20 +1,33 @@
-"""Build librace_attn.so (HIP, gfx950) in-tree with hipcc."""
+"""Build librace_attn.so (HIP, gfx950) in-tree with hipcc.
+
+Every csrc/*.hip file is one translation unit: the C ABI (race_attn.hip) and
+the launch sequences instantiated per row type and direction
+(race_inst_*.hip).  They are compiled to objects in parallel under _build/
+and linked into one shared library next to this file.
+"""
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "race_attn.hip")
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("race_common.h", "race_fwd.h", "race_bwd.h",
-                                                   "race_squash.h", "race_walk.h")]
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 INCLUDE = os.path.join(ROOT, "include")
+OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librace_attn.so")
 
 ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 VALU instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
 
 
 def hipcc() -> str:
@@ -24,25 +37,49 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str, extra=()) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # no packed-fp32 VALU instructions in device code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, *extra, SRC, "-o", out,
-    ]
+def compile_command(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), *FLAGS, "-I", INCLUDE, *extra, "-c", src, "-o", obj]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile unconditionally; returns the library path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp, extra)
+def link_command(objs, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _jobs() -> int:
+    n = os.environ.get("MAX_JOBS")
+    if n and n.isdigit():
+        return max(1, min(int(n), 16))
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building librace_attn.so")
+    return res.returncode, res.stdout + res.stderr
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every translation unit and link, unconditionally; returns the
+    library path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + f".{tag}.o") for s in SOURCES]
+    with ThreadPoolExecutor(_jobs()) as ex:
+        results = list(ex.map(lambda so: _run(compile_command(so[0], so[1], extra), verbose),
+                              zip(SOURCES, objs)))
+    failed = [(s, out) for s, (rc, out) in zip(SOURCES, results) if rc != 0]
+    if failed:
+        for s, out in failed:
+            sys.stderr.write(f"--- {os.path.basename(s)}\n{out}")
+        raise RuntimeError("hipcc failed compiling " + ", ".join(os.path.basename(s) for s, _ in failed))
+    tmp = LIB + ".tmp" + tag
+    rc, out = _run(link_command(objs, tmp), verbose)
+    for o in objs:
+        os.remove(o)
+    if rc != 0:
+        sys.stderr.write(out)
+        raise RuntimeError("hipcc failed linking librace_attn.so")
     os.replace(tmp, LIB)
     return LIB
 

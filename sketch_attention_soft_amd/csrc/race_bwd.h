@@ -27,7 +27,7 @@ namespace race {
 
 // W^T in three forms for the dxh product: bf16 hi, bf16 lo (W = hi + lo) and
 // fp32, each [HD][lp32] with hyperplanes beyond L*P zero.
-__global__ __launch_bounds__(256) void prep_wt_kernel(const float *__restrict__ W, int LP,
+static __global__ __launch_bounds__(256) void prep_wt_kernel(const float *__restrict__ W, int LP,
                                                       int lp32, char *__restrict__ wt)
 {
     const int e = blockIdx.x * 256 + threadIdx.x;

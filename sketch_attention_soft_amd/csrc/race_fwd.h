@@ -338,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void seg_sum_kernel(const float *__restric
 // are split into G groups of consecutive segments; scan_reduce_kernel writes
 // the group totals to tmp[head][G][elems], scan_apply_kernel rescans each
 // group starting from the totals of the groups before (after) it.
-__global__ __launch_bounds__(256) void scan_reduce_kernel(const float *__restrict__ st,
+static __global__ __launch_bounds__(256) void scan_reduce_kernel(const float *__restrict__ st,
                                                           float *__restrict__ tmp, int64_t nseg,
                                                           int64_t elems, int G)
 {
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void scan_reduce_kernel(const float *__restric
     tmp[(bh * G + grp) * elems + e] = sum;
 }
 
-__global__ __launch_bounds__(256) void scan_apply_kernel(float *__restrict__ st,
+static __global__ __launch_bounds__(256) void scan_apply_kernel(float *__restrict__ st,
                                                          const float *__restrict__ tmp,
                                                          int64_t nseg, int64_t elems, int G,
                                                          int reverse)

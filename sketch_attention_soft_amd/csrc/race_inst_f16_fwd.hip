@@ -1,0 +1,11 @@
+// race_inst_f16_fwd.hip -- launch sequences of the RACE attention library
+// instantiated for one row type and direction (race_host.h), compiled apart
+// from the other race_inst_*.hip files so that the library builds in parallel.
+#include "race_host.h"
+
+namespace race_host {
+
+RACE_FWD_INST(, _Float16);
+RACE_SPLIT_FWD_INST(, _Float16);
+
+}  // namespace race_host

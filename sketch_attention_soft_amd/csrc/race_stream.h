@@ -240,7 +240,7 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
 
 // state[head] += sum over the blocks b = 0, 1, ... of part[head][b] (in that
 // order, so the result does not depend on the launch)
-__global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part, int nblk,
+static __global__ __launch_bounds__(256) void stream_reduce_kernel(const float *__restrict__ part, int nblk,
                                                             int64_t elems, float *__restrict__ state)
 {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -263,7 +263,7 @@ namespace race {
 // column 16 ct + c16, column HD being the count column.  Tables >= L and the
 // padding columns are skipped.  scale = 2^(P/2): the fused writer features
 // are 2^-P prod t, the streaming state's 2^(-P/2) prod t.
-__global__ __launch_bounds__(256) void stream_from_sums_kernel(const float *__restrict__ st,
+static __global__ __launch_bounds__(256) void stream_from_sums_kernel(const float *__restrict__ st,
                                                                int64_t nseg, int nwaves, int L,
                                                                int d, float scale,
                                                                float *__restrict__ state)

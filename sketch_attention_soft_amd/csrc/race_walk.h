@@ -69,8 +69,8 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // io_lo / io_hi give them as floats (exact), io_bf16w as bf16 bits (as they
 // are for bf16 rows, rounded to nearest even for fp16 rows), and pk_io packs
 // two floats as IO (round to nearest even).
-template <typename IO> constexpr bool is_bf16 = false;
-template <> constexpr bool is_bf16<bf16> = true;
+template <typename IO> inline constexpr bool is_bf16 = false;
+template <> inline constexpr bool is_bf16<bf16> = true;
 template <typename IO> __device__ __forceinline__ float io_lo(uint32_t w)
 {
     if constexpr (is_bf16<IO>) return __builtin_bit_cast(float, w << 16);
@@ -1482,7 +1482,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 // consecutive entries; its 8 thread groups sum every 8th block (in order),
 // then the 8 group sums are added in group order (a fixed order, whatever the
 // launch).
-__global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int64_t nparts,
+static __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int64_t nparts,
                                                         int rows, int LP, int P, int d,
                                                         float *__restrict__ dW)
 {

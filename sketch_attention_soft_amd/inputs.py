@@ -17,6 +17,13 @@ reproduced on its own):
 * W[L, P, d] stays fp32;
 * the counter of block b of stream s is (0, b, 0, 0) under key
   seed * 16 + s, so generation is identical on every machine.
+
+Un-normalised rows (``row_scale=True``, a test recipe, not a workload's):
+after the normalisation each row of Q and K is multiplied by 10**(6u - 3),
+u ~ U(0, 1), a log-uniform factor in [1e-3, 1e3], and with probability 1/64
+by zero instead; u and the zero draw come from the stream ``STREAM_SCALE +
+s`` of the same block, so the rows' directions are those of the normalised
+recipe.
 """
 from __future__ import annotations
 
@@ -28,6 +35,8 @@ import numpy as np
 ROWS_PER_BLOCK = 1 << 16
 
 STREAM_W, STREAM_Q, STREAM_K, STREAM_V, STREAM_DO = range(5)
+STREAM_SCALE = 8  # + the stream of the scaled tensor (Q or K)
+ZERO_ROW_P = 1.0 / 64
 
 
 @dataclasses.dataclass(frozen=True)
@@ -94,7 +103,8 @@ def _gen(seed: int, stream: int, block: int) -> np.random.Generator:
                                                 counter=[0, block, 0, 0]))
 
 
-def _rows(seed: int, stream: int, r0: int, r1: int, d: int, normalise: bool) -> np.ndarray:
+def _rows(seed: int, stream: int, r0: int, r1: int, d: int, normalise: bool,
+          scale: bool = False) -> np.ndarray:
     """fp32 rows [r0, r1) of a stream (blocks are drawn whole, then sliced)."""
     out = np.empty((r1 - r0, d), dtype=np.float32)
     b0, b1 = r0 // ROWS_PER_BLOCK, (r1 - 1) // ROWS_PER_BLOCK
@@ -103,6 +113,11 @@ def _rows(seed: int, stream: int, r0: int, r1: int, d: int, normalise: bool) -> 
         if normalise:
             x = blk.astype(np.float64)
             x /= np.sqrt((x * x).sum(axis=1, keepdims=True))
+            if scale:
+                gs = _gen(seed, STREAM_SCALE + stream, b)
+                f = 10.0 ** (6.0 * gs.random(ROWS_PER_BLOCK) - 3.0)
+                f[gs.random(ROWS_PER_BLOCK) < ZERO_ROW_P] = 0.0
+                x *= f[:, None]
             blk = x.astype(np.float32)
         lo = max(r0, b * ROWS_PER_BLOCK)
         hi = min(r1, (b + 1) * ROWS_PER_BLOCK)
@@ -124,15 +139,17 @@ def make_w(seed: int, L: int, P: int, d: int) -> np.ndarray:
 
 
 def make_tensor(seed: int, stream: int, BH: int, N: int, d: int, dtype: str,
-                n_rows: int | None = None, threads: int = 8) -> np.ndarray:
+                n_rows: int | None = None, threads: int = 8, row_scale: bool = False) -> np.ndarray:
     """Rows of one input tensor [BH, n_rows, d] in storage form.
 
     Head h of a [BH, N, d] tensor occupies stream rows [h*N, (h+1)*N); only the
     first ``n_rows`` (default N) rows of each head are produced, so a prefix of
     a long workload is bit-identical to the same rows of the full tensor.
+    row_scale: Q and K rows scaled as the module docstring describes.
     """
     n = N if n_rows is None else n_rows
     normalise = stream in (STREAM_Q, STREAM_K)
+    scale = row_scale and normalise
     out = np.empty((BH, n, d), dtype=np.uint16 if dtype in ("bf16", "f16") else np.float32)
     jobs = []
     for h in range(BH):
@@ -141,7 +158,8 @@ def make_tensor(seed: int, stream: int, BH: int, N: int, d: int, dtype: str,
 
     def work(job):
         h, r0, r1 = job
-        out[h, r0:r1] = _store(_rows(seed, stream, h * N + r0, h * N + r1, d, normalise), dtype)
+        out[h, r0:r1] = _store(_rows(seed, stream, h * N + r0, h * N + r1, d, normalise, scale),
+                               dtype)
 
     if len(jobs) > 1 and threads > 1:
         with ThreadPoolExecutor(threads) as ex:
@@ -153,13 +171,16 @@ def make_tensor(seed: int, stream: int, BH: int, N: int, d: int, dtype: str,
 
 
 def make_inputs(B: int, H: int, N: int, d: int, L: int, P: int, dtype: str, seed: int,
-                with_grad: bool = True, n_rows: int | None = None) -> dict:
-    """All inputs of a workload in storage form: W (fp32) and q, k, v[, do]."""
+                with_grad: bool = True, n_rows: int | None = None,
+                row_scale: bool = False) -> dict:
+    """All inputs of a workload in storage form: W (fp32) and q, k, v[, do].
+    row_scale: un-normalised Q and K rows (module docstring)."""
     BH = B * H
     n = N if n_rows is None else n_rows
     res = {"W": make_w(seed, L, P, d)}
     for name, s in (("q", STREAM_Q), ("k", STREAM_K), ("v", STREAM_V)):
-        res[name] = make_tensor(seed, s, BH, N, d, dtype, n).reshape(B, H, n, d)
+        res[name] = make_tensor(seed, s, BH, N, d, dtype, n,
+                                row_scale=row_scale).reshape(B, H, n, d)
     if with_grad:
         res["do"] = make_tensor(seed, STREAM_DO, BH, N, d, dtype, n).reshape(B, H, n, d)
     return res

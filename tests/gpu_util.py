@@ -59,3 +59,49 @@ def host_inputs(x: dict, dtype: str) -> dict:
         if n in x:
             out[n] = I.to_f64(x[n], dtype)
     return out
+
+
+# per-row gate: a row is compared with its reference relative to its own norm,
+# floored at ROW_FLOOR times the root mean square row norm of its head; the
+# bar is ten times the Frobenius bar, so rounding passes and a row that is
+# wholly wrong (error ~ 1) does not
+ROW_TOL = {k: 10 * v for k, v in TOL.items()}
+ROW_FLOOR = 0.05
+# dQ and dK rows are differences of nearly equal terms for some rows (a query
+# whose keys carry similar values: early causal rows above all), so their
+# rounding is measured against a quarter of the head's RMS row norm; a row
+# that is wholly wrong still scores about 1 or more
+GRAD_FLOOR = 0.25
+
+
+def row_errors(x: np.ndarray, ref: np.ndarray, floor: float = ROW_FLOOR,
+               vanishing: tuple = ()) -> np.ndarray:
+    """Per-row relative errors ||x_i - ref_i|| / max(||ref_i||, floor rms_h),
+    rows over the last axis, rms_h over the rows of each leading (b, h).
+
+    vanishing: row indices (within every head) whose exact value is zero for
+    any input -- the causal dQ of row 0, whose output o_0 = v_0 does not
+    depend on q_0 -- so that the computed row is rounding noise; they are
+    measured on the head's scale (floor 1)."""
+    xs, rs = _heads(x), _heads(ref)
+    out = []
+    for a, b in zip(xs, rs):
+        a = a.reshape(a.shape[0], -1) if a.ndim > 1 else a[:, None]
+        b = b.reshape(b.shape[0], -1) if b.ndim > 1 else b[:, None]
+        nb = np.linalg.norm(b, axis=1)
+        rms = np.sqrt(np.mean(nb * nb)) if nb.size else 0.0
+        fl = np.full(nb.shape, floor * rms)
+        for i in vanishing:
+            if i < fl.size:
+                fl[i] = rms
+        den = np.maximum(nb, fl)
+        den[den == 0] = 1.0
+        out.append(np.linalg.norm(a - b, axis=1) / den)
+    return np.concatenate(out) if out else np.zeros(0)
+
+
+def row_report(name: str, e: np.ndarray) -> str:
+    if e.size == 0:
+        return f"rows_{name}: none"
+    return (f"rows_{name}: max={e.max():.2e} (row {int(np.argmax(e))}) "
+            f"p99={np.percentile(e, 99):.2e} median={np.median(e):.2e}")

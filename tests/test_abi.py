@@ -435,3 +435,23 @@ def test_state_add_fast_validation(lib):
     assert fn(F, F, F, 8, 4, 0.0, 1, 1, 64, 64, BF16, F, F, 1 << 30, None) == E_TAU
     assert fn(F, F, F, 8, 4, 1.0, 1, 1, 64, 64, BF16, F, F, 16, None) == E_WS
     assert fn(None, None, F, 8, 4, 1.0, 1, 1, 0, 64, BF16, F, None, 0, None) == OK      # N = 0
+
+
+def test_state_add_fast_workspace(lib):
+    """for_backward = 3 sizes race_attn_state_add_fast: the segment states and
+    the scan's group totals only, less than the forward's workspace (which
+    also holds the keys' hash-feature cache)."""
+    L = _stream_lib(lib)
+    sz = ctypes.c_size_t(0)
+    ws = lib.race_attn_workspace_bytes
+    for (N, Lt, dt) in ((4096, 8, BF16), (1 << 20, 32, BF16), (70000, 16, 2)):
+        assert ws(1, 2, N, 64, Lt, 4, 1, 0, dt, 3, ctypes.byref(sz)) == OK
+        fast = sz.value
+        assert ws(1, 2, N, 64, Lt, 4, 1, 0, dt, 0, ctypes.byref(sz)) == OK
+        assert 0 < fast < sz.value
+        fn = lib.race_attn_state_add_fast
+        fn.argtypes = L.race_attn_state_add.argtypes
+        assert fn(FAKE, FAKE, FAKE, Lt, 4, 1.0, 1, 2, N, 64, dt, FAKE, FAKE, fast - 1, None) == E_WS
+    assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 3, ctypes.byref(sz)) == E_UNSUP
+    assert ws(1, 1, 4096, 64, 40, 4, 1, 0, BF16, 3, ctypes.byref(sz)) == E_UNSUP
+    assert ws(1, 1, 4096, 64, 8, 4, 1, 0, BF16, 4, ctypes.byref(sz)) != OK

@@ -20,12 +20,26 @@ def test_more_than_one_gpu_is_refused():
 
 def test_algorithmic_work_of_the_headline():
     w = I.WORKLOADS["causal_n4m_bf16"]
-    flops, nbytes, per_kernel = bench.algorithmic_per_token(w)
     d, L, P = w.d, w.L, w.P
     F = L << P
-    # 12 d L P + 8 F (d + 1) + 4 F d and 12 d e + 8 (e = 2 bytes)
-    assert flops == 12 * d * L * P + 8 * F * (d + 1) + 4 * F * d == 495616
-    assert nbytes == 12 * d * 2 + 8 == 1544
-    # the fused kernels' shares add up to the whole step
     fused = ("sum_kv", "fwd_o", "sum_qd", "dq", "dk", "dv")
+    # the backward recomputing the hash: 12 d L P + 8 F (d + 1) + 4 F d
+    flops, nbytes, per_kernel = bench.algorithmic_per_token(w, saved=False)
+    assert flops == 12 * d * L * P + 8 * F * (d + 1) + 4 * F * d == 495616
     assert sum(per_kernel[k] for k in fused) == flops
+    # with the forward's saved hash features (as the step is timed): 8 d L P
+    flops, nbytes, per_kernel = bench.algorithmic_per_token(w)
+    assert flops == 8 * d * L * P + 8 * F * (d + 1) + 4 * F * d == 462848
+    assert sum(per_kernel[k] for k in fused) == flops
+    # one read of Q, K, V, O, dO, den and one write of O, dQ, dK, dV (e = 2 bytes)
+    assert nbytes == 12 * d * 2 + 8 == 1544
+
+
+def test_metric_names():
+    assert bench.metric_name(I.WORKLOADS["causal_n4m_bf16"]) == bench.METRIC
+    names = {k: bench.metric_name(w) for k, w in I.WORKLOADS.items()}
+    assert len(set(names.values())) == len(names)
+    assert "N=75M" in names["causal_n75m_bf16"] and "L=16" in names["causal_n75m_bf16"]
+    assert "N=16K" in names["causal_b4h16_n16k_bf16"] and "B*H=64" in names["causal_b4h16_n16k_bf16"]
+    assert "latency" in names["noncausal_fwd_n1k_f32"] and "fwd" in names["noncausal_fwd_n1k_f32"]
+    assert "4M" not in names["causal_h8_n64k_f32"]

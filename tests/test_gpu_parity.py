@@ -13,7 +13,8 @@ import torch
 import oracle
 from sketch_attention_soft_amd import binding
 from sketch_attention_soft_amd import inputs as I
-from tests.gpu_util import TOL, device_inputs, head_relf, host_inputs, to_host64
+from tests.gpu_util import (GRAD_FLOOR, ROW_FLOOR, ROW_TOL, TOL, device_inputs, head_relf,
+                            host_inputs, row_errors, row_report, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,10 +68,12 @@ def test_forward_parity(dtype, causal, case):
     tol = TOL[dtype]
     e_o = head_relf(res["o"], ref["o"])
     e_den = np.abs(res["den"] - ref["den"]).max() / np.abs(ref["den"]).max()
-    print(f"  rel_o={e_o:.3e} rel_den={e_den:.3e}")
+    e_row = row_errors(res["o"], ref["o"])
+    print(f"  rel_o={e_o:.3e} rel_den={e_den:.3e} " + row_report("o", e_row))
     assert np.all(np.isfinite(res["o"]))
     assert e_o <= tol, e_o
     assert e_den <= tol, e_den
+    assert e_row.max() <= ROW_TOL[dtype], e_row.max()
 
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)
@@ -90,3 +93,9 @@ def test_backward_parity(dtype, causal, case, saved):
     for n, e in errs.items():
         assert np.all(np.isfinite(res[n])), n
         assert e <= tol, (n, e)
+    # per-row gate (dQ, dK: skipped at N = 1, where they vanish exactly)
+    for n in ("o", "dv") + (("dq", "dk") if case[2] > 1 else ()):
+        e_row = row_errors(res[n], ref[n], GRAD_FLOOR if n in ("dq", "dk") else ROW_FLOOR,
+                           vanishing=(0,) if n == "dq" and causal else ())
+        print("  " + row_report(n, e_row))
+        assert e_row.max() <= ROW_TOL[dtype], (n, e_row.max())

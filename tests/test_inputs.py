@@ -61,3 +61,25 @@ def test_f16_storage_matches_torch():
     for k in ("q", "k", "v", "do"):
         assert f[k].dtype == np.uint16
         assert np.array_equal(I.to_f64(f[k], "f16"), g[k].astype(np.float16).astype(np.float64))
+
+
+def test_row_scale_recipe():
+    """Un-normalised rows: the normalised recipe's directions, norms log-uniform
+    in [1e-3, 1e3] or exactly zero (about 1 row in 64); V and dO unchanged."""
+    a = I.make_inputs(1, 2, 70000, 64, 4, 4, "f32", 5, row_scale=True)
+    b = I.make_inputs(1, 2, 70000, 64, 4, 4, "f32", 5)
+    for n in ("q", "k"):
+        x, y = a[n].astype(np.float64), b[n].astype(np.float64)
+        nx = np.linalg.norm(x, axis=-1)
+        zero = nx == 0
+        assert 0.8 / 64 < zero.mean() < 1.25 / 64
+        assert nx[~zero].min() >= 0.999e-3 and nx.max() <= 1.001e3
+        # roughly log-uniform: about half the rows on each side of 1
+        assert 0.45 < (nx[~zero] > 1).mean() < 0.55
+        cos = (x * y).sum(-1)[~zero] / (nx[~zero] * np.linalg.norm(y, axis=-1)[~zero])
+        assert cos.min() > 1 - 1e-6
+    for n in ("v", "do"):
+        assert np.array_equal(a[n], b[n])
+    # the same rows (head 0: stream rows 0..99) in every storage type
+    c = I.make_inputs(1, 2, 100, 64, 4, 4, "bf16", 5, row_scale=True)
+    assert np.array_equal(c["q"][:, 0], I.f32_to_bf16_bits(a["q"][:, 0, :100]))
