@@ -306,6 +306,31 @@ race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int 
 /* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);
 
+/* Bytes of the device scratch array that race_attn_forward_noalloc uses as
+ * its workspace (one array per GPU, held until the process ends). */
+#define RACE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* race_attn_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace race_attn_forward would
+ * take is a file-scope device array of RACE_NOALLOC_SCRATCH_BYTES bytes in
+ * the library instead (one per GPU; its address is looked up once per
+ * device, on the first call with that device current).  This entry point
+ * calls no hipMalloc, hipFree or allocating routine, and no saved state or
+ * trace is taken.  Problems whose race_attn_workspace_bytes(..., 0) exceeds
+ * RACE_NOALLOC_SCRATCH_BYTES return RACE_ERR_WORKSPACE before anything is
+ * enqueued (with chunk = 0 and 16-bit rows that is about 300,000 tokens at
+ * L = 32, the segment states taking about 42 MB of it).  `stream` must
+ * belong to the current device.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (two streams, or two threads) race
+ * and must be ordered by the caller.  Every scratch element the kernels read
+ * is written earlier in the same call, so nothing needs clearing and the
+ * contents left by a previous call do not matter.  Results equal
+ * race_attn_forward's for the same arguments. */
+race_status_t race_attn_forward_noalloc(const void *Q, const void *K, const void *V,
+                                        const float *W, int L, int P, float tau, int causal,
+                                        int B, int H, int64_t N, int d, race_dtype_t dt, int chunk,
+                                        void *O, float *den, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forw
            "race_attn_squash_coeffs", "race_attn_squash_deriv_coeffs",
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
            "race_attn_state_add_fast",
-           "race_attn_decode", "race_attn_state_readout", "race_attn_status_string")
+           "race_attn_decode", "race_attn_state_readout", "race_attn_status_string",
+           "race_attn_forward_noalloc")
 TRACE_MAX = 24
 
 
@@ -121,6 +122,8 @@ def lib():
         L.race_attn_state_readout.argtypes = [vp, vp, i32, i32, f32, i32, i32, i64, i32, i32, vp,
                                               vp, vp, vp]
         L.race_attn_state_readout.restype = i32
+        L.race_attn_forward_noalloc.argtypes = L.race_attn_forward.argtypes[:16] + [vp]
+        L.race_attn_forward_noalloc.restype = i32
         L.race_attn_status_string.argtypes = [i32]
         L.race_attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -271,6 +274,25 @@ def forward(q, k, v, W, tau: float, causal: bool, chunk: int = 0, workspace=None
                                       workspace.data_ptr(), workspace.numel(), _stream(),
                                       _ptr(saved), _tp(trace)))
     return o, den
+
+
+def forward_noalloc(q, k, v, W, tau: float, causal: bool, chunk: int = 0, out=None):
+    """race_attn_forward_noalloc: the forward with the library's per-GPU scratch
+    array as its workspace (nothing is allocated for it); returns (o, den).
+    Calls on one GPU share that array and must not overlap."""
+    B, H, N, d = _shape(q)
+    _check_tensors(q, k, v)
+    L, P = _check_w(W, q)
+    o, den = _outputs_fwd(q, out)
+    _require_gpu(q)
+    _check(lib().race_attn_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           W.data_ptr(), L, P, float(tau), int(causal), B, H, N,
+                                           d, dtype_code(q.dtype), chunk, o.data_ptr(),
+                                           den.data_ptr(), _stream()))
+    return o, den
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def forward_hard(q, k, v, W, causal: bool, chunk: int = 0, workspace=None, out=None):

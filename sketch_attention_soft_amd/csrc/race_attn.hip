@@ -1,16 +1,24 @@
 // race_attn.hip -- C ABI of the RACE attention library (declared in include/race_attn.h).
 //
 // Host side: argument validation, workspace planning and kernel sequencing
-// on the caller's stream.  No allocation, no synchronisation, no global
-// mutable state.
+// on the caller's stream.  No allocation and no synchronisation; the only
+// global state is the per-device address of the allocation-free forward's
+// scratch array, looked up once per device.
 #include "race_attn.h"
 
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "race_host.h"
+
+// Workspace of race_attn_forward_noalloc: one copy per GPU, allocated when the
+// code object is loaded on that device and held until the process ends.  In
+// host code this name is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress (scratch_address below).
+__device__ __align__(256) char scratch[RACE_NOALLOC_SCRATCH_BYTES];
 
 namespace race_host {
 
@@ -246,6 +254,29 @@ double f16_value(uint32_t bits)
 namespace {
 
 using namespace race_host;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call with that device current and kept per device.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+race_status_t scratch_address(char **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RACE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return RACE_ERR_HIP;
+        }
+        g_scratch[dev] = ptr;
+    }
+    *out = static_cast<char *>(g_scratch[dev]);
+    return RACE_OK;
+}
 
 race_status_t check_tau(float tau)
 {
@@ -647,6 +678,23 @@ race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int 
         launch_stream<float, race::SM_READOUT>(sp, Q, nullptr, nullptr, W, tau, T, nblk, sv,
                                                nullptr, O, den, s);
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_forward_noalloc(const void *Q, const void *K, const void *V,
+                                        const float *W, int L, int P, float tau, int causal,
+                                        int B, int H, int64_t N, int d, race_dtype_t dt, int chunk,
+                                        void *O, float *den, void *stream)
+{
+    if (!Q || !K || !V || !W || !O || !den) return RACE_ERR_NULL;
+    Plan p;
+    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    if (st != RACE_OK) return st;
+    if ((st = check_tau(tau)) != RACE_OK) return st;
+    if (p.f_total > RACE_NOALLOC_SCRATCH_BYTES) return RACE_ERR_WORKSPACE;
+    char *ws = nullptr;
+    if ((st = scratch_address(&ws)) != RACE_OK) return st;
+    return forward_impl(Q, K, V, W, L, P, tau, causal, B, H, N, d, dt, chunk, O, den, ws,
+                        RACE_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, nullptr);
 }
 
 const char *race_attn_status_string(race_status_t status)
