@@ -36,9 +36,10 @@
  *     after enqueueing, without synchronising.  The library never allocates,
  *     frees or synchronises, keeps no global mutable state and is safe to
  *     call from several threads.
- *   - Supported: d = 64, P = 4, 1 <= L <= 64 (L <= 32 for RACE_F32; for
- *     16-bit rows L > 32 runs as two passes over 32 and L - 32 tables, the
- *     second adding the first's fp32 partial sums); for RACE_BF16 and
+ *   - Supported: d = 64, P = 4, 1 <= L <= 128 (L <= 32 for RACE_F32; for
+ *     16-bit rows L > 32 runs as passes over tables 0..31, 32..63, ..., each
+ *     adding its fp32 partial sums to the previous passes' before the last
+ *     pass finishes the outputs); for RACE_BF16 and
  *     RACE_F16 with L <= 32 also d = 32 (the
  *     rows are zero-padded to 64 columns on chip: the same work per token as
  *     d = 64, half the memory traffic) and P = 1, 2, 3 (the kernels keep 4
@@ -149,6 +150,33 @@ race_status_t race_attn_backward_padded(const void *Q, const void *K, const void
                                         int H, int64_t N, int d, race_dtype_t dt, int chunk,
                                         const int *seqlens, void *dQ, void *dK, void *dV,
                                         float *dW, void *workspace, size_t ws_bytes, void *stream);
+
+/* Packed batches (variable-length sequences without padding): every head's
+ * rows are the B sequences back to back, Q, K, V, O, dO, dQ, dK, dV being
+ * [H][T][d] and den [H][T]; sequence b holds rows cu_seqlens[b] ..
+ * cu_seqlens[b + 1] - 1 of each head (cu_seqlens: device pointer, int32
+ * [B + 1], non-decreasing from 0 to T, read by the kernels; values are
+ * clamped to [0, T]).  Each sequence is attended on its own rows only, as if
+ * it had been passed alone (causal or not); every row of T belongs to one
+ * sequence.  max_seqlen bounds every sequence's length (longer ones are cut
+ * to it) and sizes the workspace: race_attn_workspace_bytes(B, H,
+ * max_seqlen, ...), as for race_attn_forward_padded.  T <= B max_seqlen.
+ * RACE_BF16 and RACE_F16 rows only (the fused kernels: d = 32 or 64; any L up
+ * to 128); RACE_ERR_UNSUPPORTED otherwise.  The backward writes dW when dW
+ * is not NULL (workspace with for_backward = 2).  chunk = 0 as for the padded
+ * entry points. */
+race_status_t race_attn_forward_varlen(const void *Q, const void *K, const void *V,
+                                       const float *W, int L, int P, float tau, int causal, int B,
+                                       int H, int64_t T, int64_t max_seqlen, int d,
+                                       race_dtype_t dt, int chunk, const int *cu_seqlens, void *O,
+                                       float *den, void *workspace, size_t ws_bytes, void *stream);
+race_status_t race_attn_backward_varlen(const void *Q, const void *K, const void *V,
+                                        const float *W, const void *O, const float *den,
+                                        const void *dO, int L, int P, float tau, int causal, int B,
+                                        int H, int64_t T, int64_t max_seqlen, int d,
+                                        race_dtype_t dt, int chunk, const int *cu_seqlens,
+                                        void *dQ, void *dK, void *dV, float *dW, void *workspace,
+                                        size_t ws_bytes, void *stream);
 
 /* Per-kernel timing for the *_ex entry points.  The caller creates the HIP
  * events (hipEventCreate, timing enabled) and owns them; the library records

@@ -27,7 +27,7 @@ EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forw
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
            "race_attn_state_add_fast",
            "race_attn_decode", "race_attn_state_readout", "race_attn_status_string",
-           "race_attn_forward_noalloc")
+           "race_attn_forward_noalloc", "race_attn_forward_varlen", "race_attn_backward_varlen")
 TRACE_MAX = 24
 
 
@@ -106,6 +106,13 @@ def lib():
                                                 + L.race_attn_backward.argtypes[17:20] + [vp]
                                                 + L.race_attn_backward.argtypes[20:])
         L.race_attn_backward_padded.restype = i32
+        L.race_attn_forward_varlen.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i32, i64,
+                                               i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.race_attn_forward_varlen.restype = i32
+        L.race_attn_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, i32,
+                                                i32, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp,
+                                                vp, vp, sz, vp]
+        L.race_attn_backward_varlen.restype = i32
         L.race_attn_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_state_bytes.restype = i32
         L.race_attn_state_add_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32,
@@ -401,6 +408,73 @@ def backward_padded(q, k, v, W, o, den, do, seqlens, tau: float, causal: bool,
         do.data_ptr(), L, P, float(tau), int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
         seqlens.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(gW),
         workspace.data_ptr(), workspace.numel(), _stream()))
+    return (dq, dk, dv, gW) if dw else (dq, dk, dv)
+
+
+def _check_cu(cu_seqlens, T, ref):
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or not cu_seqlens.is_contiguous()
+            or cu_seqlens.device != ref.device):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor on the rows' device")
+    return cu_seqlens.numel() - 1
+
+
+def _packed_shape(q):
+    if q.dim() != 3:
+        raise ValueError("packed batches take [H, T, d] tensors")
+    return q.shape
+
+
+def forward_varlen(q, k, v, W, cu_seqlens, max_seqlen: int, tau: float, causal: bool,
+                   chunk: int | None = None, workspace=None, out=None):
+    """Forward over packed batches: q, k, v [H, T, d], sequence b at rows
+    cu_seqlens[b] .. cu_seqlens[b + 1] of every head, none longer than
+    max_seqlen.  Returns (o [H, T, d], den [H, T]).  chunk None: padded_chunk."""
+    H, T, d = _packed_shape(q)
+    _check_tensors(q, k, v)
+    L, P = _check_w(W, q)
+    B = _check_cu(cu_seqlens, T, q)
+    chunk = padded_chunk(B, H, max_seqlen) if chunk is None else chunk
+    if out is None:
+        o = torch.empty_like(q)
+        den = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    else:
+        o, den = out
+        _check_out(o, q.shape, q.dtype, q.device, "o")
+        _check_out(den, (H, T), torch.float32, q.device, "den")
+    nbytes = workspace_bytes(B, H, max_seqlen, d, L, P, causal, chunk, q.dtype, False)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
+    _check(lib().race_attn_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(),
+                                          L, P, float(tau), int(causal), B, H, T, int(max_seqlen),
+                                          d, dtype_code(q.dtype), chunk, cu_seqlens.data_ptr(),
+                                          o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream()))
+    return o, den
+
+
+def backward_varlen(q, k, v, W, o, den, do, cu_seqlens, max_seqlen: int, tau: float,
+                    causal: bool, chunk: int | None = None, workspace=None, dw: bool = False,
+                    out=None):
+    """Backward over packed batches ([H, T, d] tensors, den [H, T]); returns
+    (dq, dk, dv), and dW last with dw=True.  chunk None: padded_chunk (it must
+    be the forward's)."""
+    H, T, d = _packed_shape(q)
+    _check_tensors(q, k, v, o, do)
+    L, P = _check_w(W, q)
+    B = _check_cu(cu_seqlens, T, q)
+    _check_out(den, (H, T), torch.float32, q.device, "den")
+    chunk = padded_chunk(B, H, max_seqlen) if chunk is None else chunk
+    dq, dk, dv = _outputs_bwd(q, out, torch.empty_like)
+    gW = torch.empty_like(W) if dw else None
+    nbytes = workspace_bytes(B, H, max_seqlen, d, L, P, causal, chunk, q.dtype, 2 if dw else 1)
+    _require_gpu(q)
+    workspace = _workspace(workspace, nbytes, q.device)
+    _check(lib().race_attn_backward_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), o.data_ptr(), den.data_ptr(),
+        do.data_ptr(), L, P, float(tau), int(causal), B, H, T, int(max_seqlen),
+        d, dtype_code(q.dtype), chunk, cu_seqlens.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), _ptr(gW), workspace.data_ptr(), workspace.numel(), _stream()))
     return (dq, dk, dv, gW) if dw else (dq, dk, dv)
 
 

@@ -29,8 +29,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     if (P > race::NP) return RACE_ERR_UNSUPPORTED;
-    if (L > 64 || (dt == RACE_F32 && L > 32)) return RACE_ERR_UNSUPPORTED;
-    // 16-bit rows with L > 32: two fused passes, d = 64 only
+    if (L > 128 || (dt == RACE_F32 && L > 32)) return RACE_ERR_UNSUPPORTED;
+    // 16-bit rows with L > 32: fused passes of up to 32 tables, d = 64 only
     if (dt != RACE_F32 && L > 32 && d != race::HD) return RACE_ERR_UNSUPPORTED;
     // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32)
     const bool fusable = dt != RACE_F32 && L <= 32;
@@ -102,19 +102,23 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
                                                 race::HD * sizeof(float))
                            : 0;
     if (dt != RACE_F32 && L > 32) {
-        // two fused passes (the first 32 tables, then the other L - 32): both
-        // passes' buffers, then the fp32 partial sums
-        Plan a, b;
-        race_status_t st = make_plan(B, H, N, d, 32, P, chunk, dt, &a);
-        if (st != RACE_OK) return st;
-        if ((st = make_plan(B, H, N, d, L - 32, P, chunk, dt, &b)) != RACE_OK) return st;
+        // fused passes over tables 0..31, 32..63, ... (split_passes): every
+        // pass's buffers, then the fp32 partial sums
         const size_t pv = align256((size_t)p->rows * race::HD * sizeof(float));
         const size_t pm = align256((size_t)p->rows * sizeof(float));
         p->split = true;
-        p->f_total = a.f_total + b.f_total + pv + pm;
-        p->b_total = a.b_total + b.b_total + 3 * pv;
-        p->dw_total = a.dw_total + b.dw_total + 3 * pv;
-        p->s_total = a.s_total + b.s_total;
+        p->f_total = pv + pm;
+        p->b_total = p->dw_total = 3 * pv;
+        p->s_total = 0;
+        for (int i = 0; i < split_passes(L); ++i) {
+            Plan a;
+            race_status_t st = make_plan(B, H, N, d, split_tables(L, i), P, chunk, dt, &a);
+            if (st != RACE_OK) return st;
+            p->f_total += a.f_total;
+            p->b_total += a.b_total;
+            p->dw_total += a.dw_total;
+            p->s_total += a.s_total;
+        }
     }
     return RACE_OK;
 }
@@ -291,6 +295,15 @@ race_status_t check_ws(const Plan &p, size_t need, const void *ws, size_t ws_byt
     return RACE_OK;
 }
 
+// Packed batches run on the fused kernels only (16-bit rows); the T rows of
+// every head must fit the B N rows the plan sizes its partial sums for.
+race_status_t check_packed(const Plan &p, int B, int64_t N, int64_t T)
+{
+    if (!p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
+    if (T < 1 || T > (int64_t)B * N) return RACE_ERR_SHAPE;
+    return RACE_OK;
+}
+
 race_status_t check_trace(race_trace_t *trace)
 {
     if (!trace) return RACE_OK;
@@ -362,17 +375,21 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
                                   int L, int P, float tau, int causal, int B, int H, int64_t N,
                                   int d, race_dtype_t dt, int chunk, void *O, float *den,
                                   void *workspace, size_t ws_bytes, void *stream, void *saved,
-                                  race_trace_t *trace, const int *lens)
+                                  race_trace_t *trace, const int *lens, const int *cu = nullptr,
+                                  int64_t T = 0)
 {
     if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
     Plan p;
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
+    if (cu && (st = check_packed(p, B, N, T)) != RACE_OK) return st;
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
     if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
     p.lens.len = lens;
+    p.lens.cu = cu;
+    p.lens.T = T;
     float *sv = p.fused || p.split ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
@@ -395,19 +412,23 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
                                    float tau, int causal, int B, int H, int64_t N, int d,
                                    race_dtype_t dt, int chunk, void *dQ, void *dK, void *dV,
                                    float *dW, void *workspace, size_t ws_bytes, void *stream,
-                                   const void *saved, race_trace_t *trace, const int *lens)
+                                   const void *saved, race_trace_t *trace, const int *lens,
+                                   const int *cu = nullptr, int64_t T = 0)
 {
     if (!Q || !K || !V || !W || !O || !den || !dO || !dQ || !dK || !dV || !workspace)
         return RACE_ERR_NULL;
     Plan p;
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
+    if (cu && (st = check_packed(p, B, N, T)) != RACE_OK) return st;
     if (dW && !p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, dW ? p.dw_total : p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
     if (saved && ((uintptr_t)saved & 255) != 0) return RACE_ERR_WORKSPACE;
     p.lens.len = lens;
+    p.lens.cu = cu;
+    p.lens.T = T;
     const float *sv = p.fused || p.split ? static_cast<const float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
@@ -516,6 +537,31 @@ race_status_t race_attn_backward_padded(const void *Q, const void *K, const void
     if (!seqlens) return RACE_ERR_NULL;
     return backward_impl(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, N, d, dt, chunk, dQ, dK,
                          dV, dW, workspace, ws_bytes, stream, nullptr, nullptr, seqlens);
+}
+
+race_status_t race_attn_forward_varlen(const void *Q, const void *K, const void *V,
+                                       const float *W, int L, int P, float tau, int causal, int B,
+                                       int H, int64_t T, int64_t max_seqlen, int d,
+                                       race_dtype_t dt, int chunk, const int *cu_seqlens, void *O,
+                                       float *den, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!cu_seqlens) return RACE_ERR_NULL;
+    return forward_impl(Q, K, V, W, L, P, tau, causal, B, H, max_seqlen, d, dt, chunk, O, den,
+                        workspace, ws_bytes, stream, nullptr, nullptr, nullptr, cu_seqlens, T);
+}
+
+race_status_t race_attn_backward_varlen(const void *Q, const void *K, const void *V,
+                                        const float *W, const void *O, const float *den,
+                                        const void *dO, int L, int P, float tau, int causal, int B,
+                                        int H, int64_t T, int64_t max_seqlen, int d,
+                                        race_dtype_t dt, int chunk, const int *cu_seqlens,
+                                        void *dQ, void *dK, void *dV, float *dW, void *workspace,
+                                        size_t ws_bytes, void *stream)
+{
+    if (!cu_seqlens) return RACE_ERR_NULL;
+    return backward_impl(Q, K, V, W, O, den, dO, L, P, tau, causal, B, H, max_seqlen, d, dt,
+                         chunk, dQ, dK, dV, dW, workspace, ws_bytes, stream, nullptr, nullptr,
+                         nullptr, cu_seqlens, T);
 }
 
 race_status_t race_attn_backward(const void *Q, const void *K, const void *V, const float *W,

@@ -147,18 +147,49 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Rows of head bh that exist: N, or for right-padded batches the length of
-// its batch, len[bh / H] clamped to [0, N] (rows past it are neither read nor
-// written: the sums skip them and their outputs are left as they are).
+// Rows of head bh = b H + h that exist: N, or for right-padded batches the
+// length of its batch, len[b] clamped to [0, N] (rows past it are neither
+// read nor written: the sums skip them and their outputs are left as they
+// are).  Packed batches (cu != null): the sequences of head h lie back to
+// back in rows [h T, (h + 1) T), sequence b at rows cu[b] .. cu[b + 1] of
+// them; its length is clamped to [0, N] and to the T rows.
 struct Lens {
     const int *len;
     int H;
+    const int *cu = nullptr;  // cu_seqlens [B + 1] (packed batches) or null
+    int64_t T = 0;            // rows per head of a packed batch
 };
+__device__ __forceinline__ void packed_range(const Lens &ls, int64_t bh, int64_t N, int64_t &start,
+                                             int64_t &len)
+{
+    const int64_t b = bh / ls.H;
+    int64_t s0 = ls.cu[b], s1 = ls.cu[b + 1];
+    s0 = s0 < 0 ? 0 : s0 < ls.T ? s0 : ls.T;
+    s1 = s1 < s0 ? s0 : s1 < ls.T ? s1 : ls.T;
+    start = s0;
+    len = s1 - s0 < N ? s1 - s0 : N;
+}
 __device__ __forceinline__ int64_t valid_rows(const Lens &ls, int64_t bh, int64_t N)
 {
+    if (ls.cu) {
+        int64_t s, n;
+        packed_range(ls, bh, N, s, n);
+        return n;
+    }
     if (!ls.len) return N;
     const int64_t n = ls.len[bh / ls.H];
     return n < 0 ? 0 : n < N ? n : N;
+}
+// First row of head bh in the [rows][d] tensors: bh N, or h T + cu[b] for
+// packed batches.
+__device__ __forceinline__ int64_t row_base(const Lens &ls, int64_t bh, int64_t N)
+{
+    if (ls.cu) {
+        int64_t s, n;
+        packed_range(ls, bh, N, s, n);
+        return (bh % ls.H) * ls.T + s;
+    }
+    return bh * N;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -153,14 +153,18 @@ void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squa
                        dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out,
                        den, p.lens, pt);
         };
-        // the first of two passes always has 32 tables (NW = 8); split runs have d = 64
+        // every pass but the last has 32 tables (NW = 8); split runs have d = 64
         if (p.part_mode == race::PART_NONE) {
             go(std::integral_constant<int, race::PART_NONE>{});
         } else if constexpr (D == race::HD) {
-            if (p.part_mode == race::PART_IN)
+            if (p.part_mode == race::PART_IN) {
                 go(std::integral_constant<int, race::PART_IN>{});
-            else if constexpr (NW == 8)
-                go(std::integral_constant<int, race::PART_OUT>{});
+            } else if constexpr (NW == 8) {
+                if (p.part_mode == race::PART_OUT)
+                    go(std::integral_constant<int, race::PART_OUT>{});
+                else
+                    go(std::integral_constant<int, race::PART_MID>{});
+            }
         }
     }
 }
@@ -187,10 +191,14 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
         if (p.part_mode == race::PART_NONE) {
             go(std::integral_constant<int, race::PART_NONE>{});
         } else if constexpr (D == race::HD) {
-            if (p.part_mode == race::PART_IN)
+            if (p.part_mode == race::PART_IN) {
                 go(std::integral_constant<int, race::PART_IN>{});
-            else if constexpr (NW == 8)
-                go(std::integral_constant<int, race::PART_OUT>{});
+            } else if constexpr (NW == 8) {
+                if (p.part_mode == race::PART_OUT)
+                    go(std::integral_constant<int, race::PART_OUT>{});
+                else
+                    go(std::integral_constant<int, race::PART_MID>{});
+            }
         }
     }
 }
@@ -415,29 +423,44 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     }
 }
 
-// L > 32 with 16-bit rows: the first 32 tables, then the other L - 32, as two
-// fused passes over the same rows.  The first stores its sums in fp32 (the
-// readout's n and m; dx_hat of Q and of K; dV) in partial arrays after both
-// passes' buffers, the second adds them before its last step.  Each pass has
-// its own buffers and saved state; dW rows are those of its tables.
+// L > 32 with 16-bit rows: passes over tables 0..31, 32..63, ... (the last
+// pass takes the rest) over the same rows.  The first pass stores its sums in
+// fp32 (the readout's n and m; dx_hat of Q and of K; dV) in partial arrays
+// after every pass's buffers, the middle passes add theirs, the last adds the
+// stored sums before its last step.  Each pass has its own buffers and saved
+// state; dW rows are those of its tables.
+inline int split_passes(int L) { return (L + 31) / 32; }
+inline int split_tables(int L, int pass) { return std::min(32, L - 32 * pass); }
+inline int split_mode(int L, int pass)
+{
+    return pass == 0 ? race::PART_OUT : pass + 1 == split_passes(L) ? race::PART_IN : race::PART_MID;
+}
+
 template <typename T>
 void split_forward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, const void *Q,
                    const void *K, const void *V, const float *W, float tau, int causal, void *O,
                    float *den, char *ws, float *saved, const Tracer &tr)
 {
-    Plan a, b;
-    make_plan(B, H, p.N, p.d, 32, p.P, chunk, dt, &a);
-    make_plan(B, H, p.N, p.d, p.L - 32, p.P, chunk, dt, &b);
-    a.lens = b.lens = p.lens;
-    float *pv = reinterpret_cast<float *>(ws + a.f_total + b.f_total);
+    const int np = split_passes(p.L);
+    Plan q[4];
+    size_t fw = 0, sv = 0;
+    for (int i = 0; i < np; ++i) {
+        make_plan(B, H, p.N, p.d, split_tables(p.L, i), p.P, chunk, dt, &q[i]);
+        fw += q[i].f_total;
+    }
+    float *pv = reinterpret_cast<float *>(ws + fw);
     float *pm = reinterpret_cast<float *>(reinterpret_cast<char *>(pv) +
                                           align256((size_t)p.rows * race::HD * sizeof(float)));
-    a.part_o = b.part_o = race::Part{pv, pm};
-    a.part_mode = race::PART_OUT;
-    b.part_mode = race::PART_IN;
-    float *sb = saved ? reinterpret_cast<float *>(reinterpret_cast<char *>(saved) + a.s_total) : nullptr;
-    dispatch_forward<T>(a, Q, K, V, W, tau, causal, O, den, ws, saved, tr);
-    dispatch_forward<T>(b, Q, K, V, W + 32 * p.P * p.d, tau, causal, O, den, ws + a.f_total, sb, tr);
+    size_t off = 0;
+    for (int i = 0; i < np; ++i) {
+        q[i].lens = p.lens;
+        q[i].part_o = race::Part{pv, pm};
+        q[i].part_mode = split_mode(p.L, i);
+        float *sb = saved ? reinterpret_cast<float *>(reinterpret_cast<char *>(saved) + sv) : nullptr;
+        dispatch_forward<T>(q[i], Q, K, V, W + 32 * i * p.P * p.d, tau, causal, O, den, ws + off, sb, tr);
+        off += q[i].f_total;
+        sv += q[i].s_total;
+    }
 }
 
 template <typename T>
@@ -446,26 +469,32 @@ void split_backward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, con
                     const void *dO, float tau, int causal, void *dQ, void *dK, void *dV, char *ws,
                     const float *saved, const Tracer &tr, float *dW)
 {
-    Plan a, b;
-    make_plan(B, H, p.N, p.d, 32, p.P, chunk, dt, &a);
-    make_plan(B, H, p.N, p.d, p.L - 32, p.P, chunk, dt, &b);
-    a.lens = b.lens = p.lens;
-    const size_t ta = dW ? a.dw_total : a.b_total, tb = dW ? b.dw_total : b.b_total;
+    const int np = split_passes(p.L);
+    Plan q[4];
+    size_t bw = 0;
+    for (int i = 0; i < np; ++i) {
+        make_plan(B, H, p.N, p.d, split_tables(p.L, i), p.P, chunk, dt, &q[i]);
+        bw += dW ? q[i].dw_total : q[i].b_total;
+    }
     const size_t pvb = align256((size_t)p.rows * race::HD * sizeof(float));
-    char *pbase = ws + ta + tb;
+    char *pbase = ws + bw;
     const race::Part pq{reinterpret_cast<float *>(pbase), nullptr};
     const race::Part pk{reinterpret_cast<float *>(pbase + pvb), nullptr};
     const race::Part pd{reinterpret_cast<float *>(pbase + 2 * pvb), nullptr};
-    a.part_dq = b.part_dq = pq;
-    a.part_dk = b.part_dk = pk;
-    a.part_dv = b.part_dv = pd;
-    a.part_mode = race::PART_OUT;
-    b.part_mode = race::PART_IN;
-    const float *sb =
-        saved ? reinterpret_cast<const float *>(reinterpret_cast<const char *>(saved) + a.s_total) : nullptr;
-    dispatch_backward<T>(a, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, saved, tr, dW);
-    dispatch_backward<T>(b, Q, K, V, W + 32 * p.P * p.d, O, den, dO, tau, causal, dQ, dK, dV, ws + ta,
-                         sb, tr, dW ? dW + 32 * p.P * p.d : nullptr);
+    size_t off = 0, sv = 0;
+    for (int i = 0; i < np; ++i) {
+        q[i].lens = p.lens;
+        q[i].part_dq = pq;
+        q[i].part_dk = pk;
+        q[i].part_dv = pd;
+        q[i].part_mode = split_mode(p.L, i);
+        const float *sb =
+            saved ? reinterpret_cast<const float *>(reinterpret_cast<const char *>(saved) + sv) : nullptr;
+        dispatch_backward<T>(q[i], Q, K, V, W + 32 * i * p.P * p.d, O, den, dO, tau, causal, dQ, dK,
+                             dV, ws + off, sb, tr, dW ? dW + 32 * i * p.P * p.d : nullptr);
+        off += dW ? q[i].dw_total : q[i].b_total;
+        sv += q[i].s_total;
+    }
 }
 
 // Bulk add through the fused segment sum (16-bit rows, L <= 32): the keys'

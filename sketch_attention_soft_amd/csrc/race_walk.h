@@ -197,12 +197,14 @@ __device__ __forceinline__ void for_chunks2(int n, F &&body)
         if (ci + 1 < n) body(ci + 1, Par<1>{});
     }
 }
-// Tables in two passes (L > 32: the first 32 tables, then the rest).  The
+// Tables in passes of at most 32 (L > 32: tables 0..31, 32..63, ...).  The
 // outputs are sums over tables before the last, nonlinear step, so the first
-// pass stores its sums in fp32 (PART_OUT) and the second adds them (PART_IN):
-// the readout's n and m before o = n / m, dV, and dx_hat before the
-// normalisation backward.  Partial rows are [token][64] fp32 (and m [token]).
-constexpr int PART_NONE = 0, PART_OUT = 1, PART_IN = 2;
+// pass stores its sums in fp32 (PART_OUT), the middle ones add theirs to the
+// stored sums (PART_MID) and the last adds the stored sums to its own
+// (PART_IN): the readout's n and m before o = n / m, dV, and dx_hat before
+// the normalisation backward.  Partial rows are [token][64] fp32 (and m
+// [token]).
+constexpr int PART_NONE = 0, PART_OUT = 1, PART_IN = 2, PART_MID = 3;
 struct Part {
     float *v;  // [rows][64]
     float *m;  // [rows] (readout denominators) or null
@@ -744,7 +746,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4;
     // segment-relative row pointers; chunk positions go into buffer resources
-    const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
+    const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
     const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
     const IO *Xs = X + row0 * D;
@@ -878,7 +880,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     // segment-relative row pointers; chunk positions go into buffer resources
-    const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
+    const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
     const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
     const IO *Rs = R + row0 * D;
@@ -992,20 +994,21 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                 const int tok = tt * 16 + (ln & 15);
                 if constexpr (PART != PART_NONE) {
                     const Rsrc rp = make_rsrc(pv + c.tok0 * HD, c.nv * HD * 4);
-                    if constexpr (PART == PART_OUT)
-                        bst128(__builtin_bit_cast(u32x4, n), rp, tok * (HD * 4) + col * 4);
-                    else
+                    if constexpr (PART != PART_OUT)
                         n += __builtin_bit_cast(floatx4, bld128(rp, tok * (HD * 4) + col * 4));
+                    if constexpr (PART == PART_OUT || PART == PART_MID)
+                        bst128(__builtin_bit_cast(u32x4, n), rp, tok * (HD * 4) + col * 4);
                 }
                 if (BWD) {
-                    if constexpr (PART != PART_OUT)
+                    if constexpr (PART == PART_NONE || PART == PART_IN)
                         bst64(u32x2{pk_io<IO>(n[0], n[1]), pk_io<IO>(n[2], n[3])}, ro, off);
                 } else {
                     float m = rm[tt * 64 + (ln & 15)];
 #pragma unroll
                     for (int ww = 1; ww < NW; ++ww) m += rm[(ww * 2 + tt) * 64 + (ln & 15)];
                     const int moff = (ct == 0 && ln < 16) ? tok * 4 : OOB;
-                    if constexpr (PART == PART_OUT) {
+                    if constexpr (PART == PART_OUT || PART == PART_MID) {
+                        if constexpr (PART == PART_MID) m += bldf(make_rsrc(pm + c.tok0, c.nv * 4), tok * 4);
                         bstf(m, make_rsrc(pm + c.tok0, c.nv * 4), moff);
                     } else {
                         if constexpr (PART == PART_IN) m += bldf(make_rsrc(pm + c.tok0, c.nv * 4), tok * 4);
@@ -1181,7 +1184,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     // segment-relative row pointers; chunk positions go into buffer resources
-    const int64_t t_begin = sg * seg, row0 = bh * N + t_begin;
+    const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
     const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
     const int nch = (tend + WCT - 1) / WCT;
     const IO *Rs = Xr + row0 * D;
@@ -1273,12 +1276,12 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 const bf16 *wrow = wt_l + (nt * 16 + c16) * WTS + 32 * k + 8 * g;
                 mma32(xa, *reinterpret_cast<const bf16x8 *>(wrow), dub);
             }
-            if constexpr (PART == PART_OUT) {
+            if constexpr (PART == PART_IN || PART == PART_MID)
+                xa += __builtin_bit_cast(floatx4, bld128(rp, tok * (HD * 4) + (nt * 16 + 4 * g) * 4));
+            if constexpr (PART == PART_OUT || PART == PART_MID) {
                 bst128(__builtin_bit_cast(u32x4, xa), rp, tok * (HD * 4) + (nt * 16 + 4 * g) * 4);
                 continue;
             }
-            if constexpr (PART == PART_IN)
-                xa += __builtin_bit_cast(floatx4, bld128(rp, tok * (HD * 4) + (nt * 16 + 4 * g) * 4));
             const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xbuf[pb] + tok * XRS + nt * 16 + 4 * g);
             float dot = 0.f;
 #pragma unroll
@@ -1316,7 +1319,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     // dots in dotp[pb]: dx = (dxh - x (x . dxh) / |x|^2) / |x| for
     // |x| > 1e-12, else dxh 1e12
     auto finish = [&](int ci, int pb) {
-        if constexpr (PART == PART_OUT) return;  // dx_hat went to the partial sums
+        if constexpr (PART == PART_OUT || PART == PART_MID) return;  // dx_hat went to the partial sums
         const Rsrc rdx = row_res<D>(dXs, chunk(ci));
 #pragma unroll
         for (int i = 0; i < TPWV; ++i) {

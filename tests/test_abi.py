@@ -88,12 +88,32 @@ def test_workspace_sizes(lib):
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
     (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
     (dict(d=32, L=33), E_UNSUP), (dict(P=5), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
-    (dict(P=0), E_SHAPE), (dict(L=65), E_UNSUP),
+    (dict(P=0), E_SHAPE), (dict(L=129), E_UNSUP), (dict(L=65, dt=F32), E_UNSUP),
     (dict(L=33, dt=F32), E_UNSUP), (dict(d=32, L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
     (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
 ])
 def test_workspace_validation(lib, kw, code):
     assert ws_bytes(lib, **kw)[0] == code
+
+
+def test_tables_in_passes(lib):
+    """16-bit rows with L > 32 run as passes of up to 32 tables: the workspace
+    grows with every pass plus the partial sums, up to L = 128."""
+    prev = 0
+    for L in (32, 33, 64, 65, 96, 97, 128):
+        for bwd in (0, 1, 2):
+            st, b = ws_bytes(lib, L=L, bwd=bwd, N=5000)
+            assert st == OK and b > 0, (L, bwd)
+        st, b = ws_bytes(lib, L=L, N=5000)
+        assert b > prev
+        prev = b
+    # a saved state for every pass
+    sz = ctypes.c_size_t(0)
+    sizes = []
+    for L in (32, 64, 96, 128):
+        assert lib.race_attn_saved_bytes(1, 1, 5000, 64, L, 4, 1, 0, BF16, ctypes.byref(sz)) == OK
+        sizes.append(sz.value)
+    assert sizes[1] == 2 * sizes[0] and sizes[3] == 4 * sizes[0] and sizes[2] == 3 * sizes[0]
 
 
 def test_fewer_hyperplanes(lib):
@@ -455,3 +475,18 @@ def test_state_add_fast_workspace(lib):
     assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 3, ctypes.byref(sz)) == E_UNSUP
     assert ws(1, 1, 4096, 64, 40, 4, 1, 0, BF16, 3, ctypes.byref(sz)) == E_UNSUP
     assert ws(1, 1, 4096, 64, 8, 4, 1, 0, BF16, 4, ctypes.byref(sz)) != OK
+
+
+def test_varlen_validation(lib):
+    """Packed batches: cu_seqlens required, 16-bit rows only, T <= B max_seqlen."""
+    f = lib.race_attn_forward_varlen
+    i32, i64, f32, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    f.argtypes = [vp, vp, vp, vp, i32, i32, f32, i32, i32, i32, i64, i64, i32, i32, i32, vp, vp, vp,
+                  vp, sz, vp]
+    F = FAKE
+    # B = 2, H = 1, T = 100, max_seqlen = 60
+    assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 64, BF16, 0, None, F, F, F, 1 << 40, None) == E_NULL
+    assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 64, F32, 0, F, F, F, F, 1 << 40, None) == E_UNSUP
+    assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 121, 60, 64, BF16, 0, F, F, F, F, 1 << 40, None) == E_SHAPE
+    assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 0, 60, 64, BF16, 0, F, F, F, F, 1 << 40, None) == E_SHAPE
+    assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 64, BF16, 0, F, F, F, F, 16, None) == E_WS

@@ -140,3 +140,19 @@ def test_mismatched_rows_rejected():
         binding.forward(q, k[..., :N - 1, :], v, W, 1.0, True)
     with pytest.raises(ValueError, match="share shape"):
         binding.forward(q, k.float(), v, W, 1.0, True)
+
+
+def test_varlen_checks():
+    H, T = 2, 50
+    q = torch.zeros((H, T, d), dtype=torch.bfloat16)
+    W = torch.zeros((L, P, d), dtype=torch.float32)
+    cu = torch.tensor([0, 20, 50], dtype=torch.int32)
+    _gpu_only(binding.forward_varlen, q, q, q, W, cu, 30, 1.0, True)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        binding.forward_varlen(q, q, q, W, cu.long(), 30, 1.0, True)
+    with pytest.raises(ValueError, match="packed"):
+        binding.forward_varlen(q[None], q[None], q[None], W, cu, 30, 1.0, True)
+    den = torch.ones((H, T))
+    _gpu_only(binding.backward_varlen, q, q, q, W, q, den, q, cu, 30, 1.0, True)
+    with pytest.raises(ValueError, match="den must be"):
+        binding.backward_varlen(q, q, q, W, q, den[:, 1:], q, cu, 30, 1.0, True)

@@ -1,6 +1,7 @@
-"""More than 32 tables on 16-bit rows: two passes of the fused kernels (the
-first 32 tables, then the rest), the second adding the first's fp32 partial
-sums before the ratio, dV and the normalisation backward.
+"""More than 32 tables on 16-bit rows: passes of the fused kernels over
+tables 0..31, 32..63, ... (up to L = 128, four passes), the first storing
+fp32 partial sums, the middle ones adding to them and the last adding them
+before the ratio, dV and the normalisation backward.
 
 The readout and its gradients are sums over tables until those last steps
 (pages: "RACE Attention: A Strictly Linear-Time Attention for Long-Sequence
@@ -27,6 +28,10 @@ CASES = [
     ("bf16", 2, 1, 257, 33, 4, 1.0, 64),
     ("f16", 1, 2, 700, 48, 3, 1.0, 0),
     ("bf16", 1, 1, 1, 40, 4, 1.0, 0),
+    ("bf16", 1, 1, 2100, 128, 4, 0.5, 0),
+    ("f16", 1, 2, 600, 96, 4, 1.0, 64),
+    ("bf16", 2, 1, 333, 65, 4, 1.0, 0),
+    ("bf16", 1, 1, 1500, 100, 2, 1.0, 128),
 ]
 
 
@@ -59,11 +64,12 @@ def test_split_tables(case, causal, saved):
         assert e <= TOL[dtype], (n, e)
 
 
-def test_split_dw_and_hard():
-    B, H, N, L, tau = 1, 2, 900, 64, 1.0
-    x = I.make_inputs(B, H, N, 64, L, 4, "bf16", 2190, with_grad=True)
+@pytest.mark.parametrize("L", [64, 100])
+def test_split_dw_and_hard(L):
+    B, H, N, tau = 1, 2, 900, 1.0
+    x = I.make_inputs(B, H, N, 64, L, 4, "bf16", 2190 + L, with_grad=True)
     dx, hx = device_inputs(x, "bf16"), host_inputs(x, "bf16")
-    print("[case] split dW + hard", flush=True)
+    print(f"[case] split dW + hard L={L}", flush=True)
     o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], tau, True)
     *_, dW = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau, True,
                               dw=True)
