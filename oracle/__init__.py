@@ -61,6 +61,15 @@ def _load():
         lib.race_oracle_forward_backward.restype = c_int
         lib.race_oracle_forward_backward_w.argtypes = lib.race_oracle_forward_backward.argtypes + [dp]
         lib.race_oracle_forward_backward_w.restype = c_int
+        lib.race_oracle_stream_forward.argtypes = [dp, dp, dp, dp, c_int, c_int, c_dbl, i64, c_int,
+                                                   dp, dp, dp]
+        lib.race_oracle_stream_forward.restype = c_int
+        lib.race_oracle_stream_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, c_int, c_int,
+                                                    c_dbl, i64, c_int, dp, dp, dp, dp, dp]
+        lib.race_oracle_stream_backward.restype = c_int
+        lib.race_oracle_block_sums.argtypes = [dp, dp, c_int, i64, c_int, dp, c_int, c_int, c_dbl,
+                                               dp]
+        lib.race_oracle_block_sums.restype = c_int
         _lib = lib
     return _lib
 
@@ -182,3 +191,75 @@ def walsh_state(k, v, W, tau: float):
     s_bits = ((np.arange(R)[:, None] >> np.arange(P)[None, :]) & 1) == 1        # [S, P]
     chi = np.prod(np.where(s_bits[:, None, :], c[None, :, :], 1.0), axis=2)     # [S, R]
     return (2.0 ** (-P / 2) * np.einsum("sr,lrc->lsc", chi, AB)).reshape(L * R, C)
+
+
+# ---------------------------------------------------------------------------
+# Causal streaming over consecutive blocks of one head (the running sums of
+# [zh] §2.3 handed from block to block), for sequences too long to hold at
+# once.  States are fp64 [d + 1, L R]: row c < d holds the bucket sums B of
+# value column c, row d the key mass A (features f = R l + r in table-major
+# order), i.e. the transpose of bucket_sums(...).reshape(L R, d + 1).
+
+def new_stream_state(L: int, P: int, d: int) -> np.ndarray:
+    """The empty state (no keys / no queries yet)."""
+    return np.zeros((d + 1, L << P))
+
+
+def stream_forward(q, k, v, W, tau: float, state: np.ndarray):
+    """Causal forward of one block [n, d] of a head continuing a sequence:
+    state holds the sums of every earlier key and is advanced in place
+    through the block's last key.  Returns (o, den) of the block's rows."""
+    q, k, v, W = _f64(q), _f64(k), _f64(v), _f64(W)
+    n, d = q.shape
+    L, P, dw = W.shape
+    assert k.shape == v.shape == (n, d) and dw == d
+    assert state.dtype == np.float64 and state.shape == (d + 1, L << P) and state.flags.c_contiguous
+    o = np.empty((n, d))
+    den = np.empty(n)
+    _check(_load().race_oracle_stream_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), L, P,
+                                              float(tau), n, d, _ptr(state), _ptr(o), _ptr(den)),
+           "stream_forward")
+    return o, den
+
+
+def stream_backward(q, k, v, g, o, den, W, tau: float, key_state: np.ndarray,
+                    grad_state: np.ndarray):
+    """Causal backward of one block, given the block's own (o, den) from
+    stream_forward and g = dL/do.  key_state: the sums of the keys before the
+    block (advanced in place through the block); grad_state: the gradient
+    sums sum_i phi(q_i) [g_i/m_i | -(g_i . o_i)/m_i]^T of the queries after
+    the block (extended in place by the block's queries).  Returns (dq, dk,
+    dv) of the block's rows."""
+    q, k, v, g, o, den, W = (_f64(a) for a in (q, k, v, g, o, den, W))
+    n, d = q.shape
+    L, P, dw = W.shape
+    assert k.shape == v.shape == g.shape == o.shape == (n, d) and den.shape == (n,) and dw == d
+    for st in (key_state, grad_state):
+        assert st.dtype == np.float64 and st.shape == (d + 1, L << P) and st.flags.c_contiguous
+    dq, dk, dv = np.empty((n, d)), np.empty((n, d)), np.empty((n, d))
+    _check(_load().race_oracle_stream_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(den), _ptr(W), L, P, float(tau), n, d,
+        _ptr(key_state), _ptr(grad_state), _ptr(dq), _ptr(dk), _ptr(dv)), "stream_backward")
+    return dq, dk, dv
+
+
+def block_sums(x, y, W, tau: float, state: np.ndarray) -> np.ndarray:
+    """state [C, L R] += sum_j phi(x_j) y_j^T over the rows of x [n, d] and
+    y [n, C], in row order; returns state.  With y = [v | 1]: a block's
+    bucket sums ([zh] §2.2)."""
+    x, y, W = _f64(x), _f64(y), _f64(W)
+    n, d = x.shape
+    L, P, dw = W.shape
+    C = y.shape[1]
+    assert y.shape == (n, C) and dw == d
+    assert state.dtype == np.float64 and state.shape == (C, L << P) and state.flags.c_contiguous
+    _check(_load().race_oracle_block_sums(_ptr(x), _ptr(y), C, n, d, _ptr(W), L, P, float(tau),
+                                          _ptr(state)), "block_sums")
+    return state
+
+
+def ratio_gradients(g, o, den) -> np.ndarray:
+    """D_i = [g_i / m_i | -(g_i . o_i) / m_i] of the ratio readout o = n / m
+    (the values the gradient sums carry)."""
+    g, o, den = _f64(g), _f64(o), _f64(den)
+    return np.concatenate([g / den[:, None], (-(g * o).sum(axis=1) / den)[:, None]], axis=1)

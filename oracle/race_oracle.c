@@ -457,6 +457,71 @@ static int backward_head(const headp *hp, double *dq, double *dk, double *dv, do
 }
 
 /* ------------------------------------------------------------------------ */
+/* Causal streaming over consecutive blocks of one head ([zh] §2.3: the     */
+/* running sums A_cum, B_cum carried from token to token).  The state that */
+/* one block hands to the next is passed in and out explicitly, so a        */
+/* sequence too long to hold at once is processed block by block in the    */
+/* same token order as forward_head / backward_head.                        */
+
+/* Forward of one block: M [d1][F] holds the sums of every earlier key on
+ * entry (zero for the first block) and of every key up to the block's last
+ * on return; each token adds its key before its query reads (step 8). */
+static int stream_forward_block(const headp *hp, double *M, double *o, double *den)
+{
+    const int d = hp->d, d1 = hp->d1, F = hp->h.F;
+    blockbuf bb;
+    if (alloc_block(&bb, F, d1) != ORC_OK) return ORC_ENOMEM;
+    for (int64_t b0 = 0; b0 < hp->N; b0 += BLK) {
+        const int n = (int)(hp->N - b0 < BLK ? hp->N - b0 : BLK);
+        fill_block(hp, b0, n, 1, 1, 0, &bb);
+        col_sweep(F, d1, n, 0, bb.phk, bb.v1, d1, bb.phq, M, bb.out, d1, 1, 1);
+        for (int i = 0; i < n; ++i) {
+            const double *nm = bb.out + (size_t)i * d1;
+            den[b0 + i] = nm[d];
+            for (int c = 0; c < d; ++c) o[(b0 + i) * d + c] = nm[c] / nm[d];
+        }
+    }
+    free_block(&bb);
+    return ORC_OK;
+}
+
+/* Backward of one block, given the block's own o and m from
+ * stream_forward_block.  S [d1][F]: sums of the keys before the block (in),
+ * through its last key (out).  G [d1][F]: gradient sums sum_i phi(q_i) D_i^T
+ * of the queries after the block (in), from its first query on (out).  The
+ * three sweeps of backward_head (dq forward with S, dphi(k) and dv in
+ * reverse with G) each start from the state handed in. */
+static int stream_backward_block(const headp *hp, double *S, double *G, double *dq, double *dk,
+                                 double *dv)
+{
+    const int d = hp->d, d1 = hp->d1, F = hp->h.F;
+    const int64_t N = hp->N;
+    const size_t sz = sizeof(double) * (size_t)F * d1;
+    blockbuf bb;
+    double *Gv = malloc(sz);
+    if (!Gv || alloc_block(&bb, F, d1) != ORC_OK) { free(Gv); return ORC_ENOMEM; }
+    memcpy(Gv, G, sz);
+    int err = ORC_OK;
+    for (int64_t b0 = 0; b0 < N && !err; b0 += BLK) {
+        const int n = (int)(N - b0 < BLK ? N - b0 : BLK);
+        fill_block(hp, b0, n, 0, 1, 1, &bb);
+        row_sweep(F, d1, n, 0, bb.phk, bb.v1, bb.D, S, bb.out, 1, 1);
+        err = block_hash_backward(hp, hp->q, b0, n, bb.out, dq, NULL);
+    }
+    for (int64_t e = N; e > 0 && !err; e -= BLK) {
+        const int64_t b0 = e - BLK > 0 ? e - BLK : 0;
+        const int n = (int)(e - b0);
+        fill_block(hp, b0, n, 1, 1, 1, &bb);
+        row_sweep(F, d1, n, 1, bb.phq, bb.D, bb.v1, G, bb.out, 1, 1);
+        err = block_hash_backward(hp, hp->k, b0, n, bb.out, dk, NULL);
+        if (!err) col_sweep(F, d, n, 1, bb.phq, bb.D, d1, bb.phk, Gv, dv + b0 * d, d, 1, 1);
+    }
+    free(Gv);
+    free_block(&bb);
+    return err;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Exported entry points.  All tensors are contiguous fp64:                 */
 /*   q, k, v, g, o, dq, dk, dv : [BH][N][d]     den : [BH][N]                */
 /*   W : [L][P][d], shared by all heads                                     */
@@ -564,4 +629,69 @@ int race_oracle_forward_backward(const double *q, const double *k, const double 
 {
     return race_oracle_forward_backward_w(q, k, v, g, W, L, P, tau, causal, BH, N, d, o, den, dq,
                                           dk, dv, NULL);
+}
+
+/* Causal forward of one block of a head's rows q, k, v [n][d], continuing a
+ * sequence: M [d + 1][L R] holds, column-major (column c is M[c L R ..]),
+ * the bucket sums B (columns 0..d-1) and A (column d) of every earlier key on
+ * entry and of every key through the block on return. */
+int race_oracle_stream_forward(const double *q, const double *k, const double *v,
+                               const double *W, int L, int P, double tau, int64_t n, int d,
+                               double *M, double *o, double *den)
+{
+    if (check_args(1, n, d, L, P, tau, 0) || !M) return ORC_EINVAL;
+    headp hp;
+    memset(&hp, 0, sizeof hp);
+    make_hashp(&hp.h, d, L, P, tau, 0, W);
+    hp.d = d; hp.d1 = d + 1; hp.causal = 1; hp.N = n;
+    hp.q = q; hp.k = k; hp.v = v;
+    return stream_forward_block(&hp, M, o, den);
+}
+
+/* Causal backward of one block, given its own o and den from
+ * race_oracle_stream_forward and g = dL/do [n][d].  S [d + 1][L R]: key
+ * sums before the block (in), through it (out).  G [d + 1][L R]: the
+ * queries' gradient sums sum_i phi(q_i) D_i^T, D_i = [g_i/m_i | -(g_i .
+ * o_i)/m_i], over the queries after the block (in), from the block's first
+ * query on (out). */
+int race_oracle_stream_backward(const double *q, const double *k, const double *v,
+                                const double *g, const double *o, const double *den,
+                                const double *W, int L, int P, double tau, int64_t n, int d,
+                                double *S, double *G, double *dq, double *dk, double *dv)
+{
+    if (check_args(1, n, d, L, P, tau, 0) || !S || !G) return ORC_EINVAL;
+    headp hp;
+    memset(&hp, 0, sizeof hp);
+    make_hashp(&hp.h, d, L, P, tau, 0, W);
+    hp.d = d; hp.d1 = d + 1; hp.causal = 1; hp.N = n;
+    hp.q = q; hp.k = k; hp.v = v; hp.g = g; hp.o = o; hp.m = den;
+    return stream_backward_block(&hp, S, G, dq, dk, dv);
+}
+
+/* M [ycols][L R] += sum_j phi(x_j) y_j^T over the n rows of x [n][d] and
+ * y [n][ycols], in row order (column-major as above).  With y = [v | 1] these
+ * are a block's bucket sums B and A ([zh] §2.2); with y = D the gradient sums
+ * of race_oracle_stream_backward. */
+int race_oracle_block_sums(const double *x, const double *y, int ycols, int64_t n, int d,
+                           const double *W, int L, int P, double tau, double *M)
+{
+    if (check_args(1, n, d, L, P, tau, 0) || ycols < 1 || !M) return ORC_EINVAL;
+    hashp h;
+    make_hashp(&h, d, L, P, tau, 0, W);
+    double *ph = malloc(sizeof(double) * (size_t)BLK * h.F);
+    if (!ph) return ORC_ENOMEM;
+    for (int64_t b0 = 0; b0 < n; b0 += BLK) {
+        const int nb = (int)(n - b0 < BLK ? n - b0 : BLK);
+#pragma omp parallel
+        {
+            double *xh = malloc(sizeof(double) * d), *z = malloc(sizeof(double) * L * P);
+#pragma omp for schedule(static)
+            for (int i = 0; i < nb; ++i) hash_row(&h, x + (b0 + i) * d, xh, z, ph + (size_t)i * h.F, NULL);
+            free(xh);
+            free(z);
+        }
+        col_sweep(h.F, ycols, nb, 0, ph, y + b0 * ycols, ycols, NULL, M, NULL, 0, 1, 0);
+    }
+    free(ph);
+    return ORC_OK;
 }

@@ -133,6 +133,12 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return x
 
 
+def stream_rows(seed: int, stream: int, r0: int, r1: int, d: int, dtype: str) -> np.ndarray:
+    """Rows [r0, r1) of one stream in storage form (Q and K normalised): for a
+    single-head workload, rows r0..r1 of that tensor, without drawing the rest."""
+    return _store(_rows(seed, stream, r0, r1, d, stream in (STREAM_Q, STREAM_K)), dtype)
+
+
 def make_w(seed: int, L: int, P: int, d: int) -> np.ndarray:
     """Projection tensor W[L, P, d], fp32 N(0, 1)."""
     return _gen(seed, STREAM_W, 0).standard_normal((L, P, d), dtype=np.float32)
