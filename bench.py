@@ -407,7 +407,7 @@ def hard_bench(args, binding, I, np, torch) -> int:
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     o = torch.empty_like(q)
     den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    ws = torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, False),
+    ws = torch.empty(binding.workspace_bytes(B, H, N, d, w.L, w.P, w.causal, w.chunk, tdt, 4),
                      dtype=torch.uint8, device=dev)
 
     def step():

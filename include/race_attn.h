@@ -85,9 +85,10 @@ typedef enum { RACE_F32 = 0, RACE_BF16 = 1, RACE_F16 = 2 } race_dtype_t;
 
 /* Workspace size, in bytes, that race_attn_forward (for_backward = 0),
  * race_attn_backward (for_backward = 1), race_attn_backward_dw
- * (for_backward = 2; RACE_ERR_UNSUPPORTED where that entry point is) or
+ * (for_backward = 2; RACE_ERR_UNSUPPORTED where that entry point is),
  * race_attn_state_add_fast (for_backward = 3, with causal = 1, chunk = 0;
- * RACE_ERR_UNSUPPORTED where that entry point is) needs
+ * RACE_ERR_UNSUPPORTED where that entry point is) or race_attn_forward_hard
+ * and race_attn_forward_hard_counts (for_backward = 4) needs
  * for this problem.  Pure host function; `bytes` (host pointer) receives the
  * size. */
 race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, int P,
@@ -103,19 +104,35 @@ race_status_t race_attn_forward(const void *Q, const void *K, const void *V, con
                                 void *workspace, size_t ws_bytes, void *stream);
 
 /* Forward pass with hard hashing: each row falls in exactly one corner per
- * table, r_l(x) = sum_p [z_lp >= 0] 2^p, and the bucket sums of steps 3-5 are
- * true counts and value sums (the tau -> 0 limit of step 2: the original RACE
- * sketch and YOSO-style attention the pages contrast soft hashing with, zh
- * §2.2 and §3).  o_i = sum_l B_l[r_l(q_i)] / sum_l A_l[r_l(q_i)] over keys
- * j <= i (causal) or all keys.  No tau; otherwise as race_attn_forward (same
- * workspace size).  Inference only: the hash has no gradient.  A query that
- * collides with no visible key gets den = 0 and a non-finite o (0 / 0).  The
- * corner of a RACE_BF16 / RACE_F16 row is decided on its bf16 value (the
- * matrix-core operand), with W to about 16 bits. */
+ * table, r_l(x) = sum_p [u_lp >= 0] 2^p with u = W x (the signs of W x_hat),
+ * and the bucket sums of steps 3-5 are true counts and value sums (the
+ * tau -> 0 limit of step 2: the original RACE sketch and YOSO-style
+ * attention the pages contrast soft hashing with, zh §2.2 and §3).
+ * o_i = sum_l B_l[r_l(q_i)] / sum_l A_l[r_l(q_i)] over keys j <= i (causal)
+ * or all keys; den_i = that count.  No tau.  Inference only: the hash has no
+ * gradient.  A query that collides with no visible key in any table (the
+ * sums are empty) gets den = 0 and o = 0.
+ * RACE_BF16 / RACE_F16 rows with L <= 32, P <= 4, d = 32 or 64 run on the
+ * bucket ids of race_attn_hash_ids (every sign decided on exact products):
+ * int32 counts, kept and gathered exactly, and fp32 value sums (read as
+ * bf16 matrix-core operands, the precision of the outputs); den is the count
+ * (exact below 2^24).  Other shapes (fp32 rows, L > 32) run the chunked soft
+ * kernels with t = +-1 (counts through the sums' fp32 and bf16 arithmetic).
+ * workspace: race_attn_workspace_bytes(..., for_backward = 4). */
 race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
                                      const float *W, int L, int P, int causal, int B, int H,
                                      int64_t N, int d, race_dtype_t dt, int chunk, void *O,
                                      float *den, void *workspace, size_t ws_bytes, void *stream);
+
+/* race_attn_forward_hard that also writes every row's count
+ * sum_l A_l[r_l(q_i)] as int32 [B][H][N] (device pointer `count`, exact at any
+ * length).  Only where the bucket-id kernels run (see above);
+ * RACE_ERR_UNSUPPORTED otherwise. */
+race_status_t race_attn_forward_hard_counts(const void *Q, const void *K, const void *V,
+                                            const float *W, int L, int P, int causal, int B, int H,
+                                            int64_t N, int d, race_dtype_t dt, int chunk, void *O,
+                                            float *den, int32_t *count, void *workspace,
+                                            size_t ws_bytes, void *stream);
 
 /* Backward pass: the exact gradient of the forward (the pages state the
  * method is differentiable end to end, es §2 item 3, fr §3 item 3).  Given
@@ -333,6 +350,23 @@ race_status_t race_attn_state_readout(const void *Q, const float *W, int L, int 
 
 /* Static, NUL-terminated description of a status code. */
 const char *race_attn_status_string(race_status_t status);
+
+/* Hard-hash bucket ids (the tau -> 0 limit of step 2, zh §2.2 and §3: the
+ * original RACE count arrays): ids[row][l] = sum_p [u_lp >= 0] 2^p with
+ * u = W x over the `rows` rows of X ([rows][d], type dt; d a multiple of 8,
+ * at most 128; 1 <= L <= 128, 1 <= P <= 6), as uint8 [rows][L] (device
+ * pointer).  The sign of x / |x| is that of x, so rows are not normalised; a
+ * zero row falls in the last corner (every u = 0 counts as >= 0).  W and the
+ * row are split into bf16 terms that add up to their values exactly, so
+ * every product is exact and only the fp32 additions round: a decision can
+ * differ from the exact sign only where |sum_t W_t x_t| <= n 2^-24 sum_t
+ * |W_t x_t|, n = 3 t (d rounded up to 32) + 16, t = 1, 2, 3 row terms for
+ * bf16, fp16, fp32.  workspace: race_attn_hash_ids_workspace_bytes (the W
+ * terms), 256-byte aligned.  rows = 0 returns RACE_OK without enqueueing. */
+race_status_t race_attn_hash_ids_workspace_bytes(int L, int P, int d, size_t *bytes);
+race_status_t race_attn_hash_ids(const void *X, int64_t rows, int d, race_dtype_t dt,
+                                 const float *W, int L, int P, uint8_t *ids, void *workspace,
+                                 size_t ws_bytes, void *stream);
 
 /* Bytes of the device scratch array that race_attn_forward_noalloc uses as
  * its workspace (one array per GPU, held until the process ends). */

@@ -27,7 +27,9 @@ EXPORTS = ("race_attn_workspace_bytes", "race_attn_saved_bytes", "race_attn_forw
            "race_attn_state_bytes", "race_attn_state_add_workspace_bytes", "race_attn_state_add",
            "race_attn_state_add_fast",
            "race_attn_decode", "race_attn_state_readout", "race_attn_status_string",
-           "race_attn_forward_noalloc", "race_attn_forward_varlen", "race_attn_backward_varlen")
+           "race_attn_forward_noalloc", "race_attn_forward_varlen", "race_attn_backward_varlen",
+           "race_attn_hash_ids_workspace_bytes", "race_attn_hash_ids",
+           "race_attn_forward_hard_counts")
 TRACE_MAX = 24
 
 
@@ -88,6 +90,8 @@ def lib():
         L.race_attn_forward_hard.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32,
                                              i32, i32, vp, vp, vp, sz, vp]
         L.race_attn_forward_hard.restype = i32
+        L.race_attn_forward_hard_counts.argtypes = L.race_attn_forward_hard.argtypes[:15] + [vp, vp, sz, vp]
+        L.race_attn_forward_hard_counts.restype = i32
         L.race_attn_saved_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32,
                                             ctypes.POINTER(sz)]
         L.race_attn_saved_bytes.restype = i32
@@ -113,6 +117,10 @@ def lib():
                                                 i32, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp,
                                                 vp, vp, sz, vp]
         L.race_attn_backward_varlen.restype = i32
+        L.race_attn_hash_ids_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.race_attn_hash_ids_workspace_bytes.restype = i32
+        L.race_attn_hash_ids.argtypes = [vp, i64, i32, i32, vp, i32, i32, vp, vp, sz, vp]
+        L.race_attn_hash_ids.restype = i32
         L.race_attn_state_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
         L.race_attn_state_bytes.restype = i32
         L.race_attn_state_add_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32,
@@ -302,19 +310,25 @@ def forward_noalloc(q, k, v, W, tau: float, causal: bool, chunk: int = 0, out=No
 NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
-def forward_hard(q, k, v, W, causal: bool, chunk: int = 0, workspace=None, out=None):
-    """Hard-hash forward (one bucket per table and row, true counts): (o, den)."""
+def forward_hard(q, k, v, W, causal: bool, chunk: int = 0, workspace=None, out=None,
+                 counts: bool = False):
+    """Hard-hash forward (one bucket per table and row, true counts): (o, den),
+    and the int32 counts last with counts=True (race_attn_forward_hard_counts)."""
     B, H, N, d = _shape(q)
     _check_tensors(q, k, v)
     L, P = _check_w(W, q)
     o, den = _outputs_fwd(q, out)
-    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, False)
+    cnt = torch.empty((B, H, N), dtype=torch.int32, device=q.device) if counts else None
+    nbytes = workspace_bytes(B, H, N, d, L, P, causal, chunk, q.dtype, 4)
     _require_gpu(q)
     workspace = _workspace(workspace, nbytes, q.device)
-    _check(lib().race_attn_forward_hard(q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L,
-                                        P, int(causal), B, H, N, d, dtype_code(q.dtype), chunk,
-                                        o.data_ptr(), den.data_ptr(), workspace.data_ptr(),
-                                        workspace.numel(), _stream()))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), L, P, int(causal), B, H, N, d,
+            dtype_code(q.dtype), chunk, o.data_ptr(), den.data_ptr())
+    if counts:
+        _check(lib().race_attn_forward_hard_counts(*args, cnt.data_ptr(), workspace.data_ptr(),
+                                                   workspace.numel(), _stream()))
+        return o, den, cnt
+    _check(lib().race_attn_forward_hard(*args, workspace.data_ptr(), workspace.numel(), _stream()))
     return o, den
 
 
@@ -476,6 +490,30 @@ def backward_varlen(q, k, v, W, o, den, do, cu_seqlens, max_seqlen: int, tau: fl
         d, dtype_code(q.dtype), chunk, cu_seqlens.data_ptr(), dq.data_ptr(), dk.data_ptr(),
         dv.data_ptr(), _ptr(gW), workspace.data_ptr(), workspace.numel(), _stream()))
     return (dq, dk, dv, gW) if dw else (dq, dk, dv)
+
+
+def hash_ids(x, W, workspace=None, out=None):
+    """Hard-hash bucket ids of the rows of x (any shape [..., d]): uint8
+    [..., L], ids[..., l] = sum_p [u_lp >= 0] 2^p with u = W x
+    (race_attn_hash_ids)."""
+    if x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [..., d] tensor")
+    L, P = _check_w(W, x)
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if out is None:
+        ids = torch.empty((*x.shape[:-1], L), dtype=torch.uint8, device=x.device)
+    else:
+        ids = out
+        _check_out(ids, (*x.shape[:-1], L), torch.uint8, x.device, "ids")
+    nb = ctypes.c_size_t(0)
+    _check(lib().race_attn_hash_ids_workspace_bytes(L, P, d, ctypes.byref(nb)))
+    _require_gpu(x)
+    workspace = _workspace(workspace, nb.value, x.device)
+    _check(lib().race_attn_hash_ids(x.data_ptr(), rows, d, dtype_code(x.dtype), W.data_ptr(), L, P,
+                                    ids.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    _stream()))
+    return ids
 
 
 class RaceAttention(torch.autograd.Function):

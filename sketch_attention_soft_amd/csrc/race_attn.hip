@@ -349,8 +349,9 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     if (st != RACE_OK) return st;
     if (for_backward == 2 && !p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
     if (for_backward == 3 && !p.fused) return RACE_ERR_UNSUPPORTED;
-    if (for_backward < 0 || for_backward > 3) return RACE_ERR_SHAPE;
-    *bytes = for_backward == 3   ? p.st_bytes + p.scan_bytes
+    if (for_backward < 0 || for_backward > 4) return RACE_ERR_SHAPE;
+    *bytes = for_backward == 4   ? (hard_fused(p, dt) ? hard_plan(p).total : p.f_total)
+             : for_backward == 3 ? p.st_bytes + p.scan_bytes
              : for_backward == 2 ? p.dw_total
              : for_backward      ? p.b_total
                                  : p.f_total;
@@ -468,30 +469,63 @@ race_status_t race_attn_forward_padded(const void *Q, const void *K, const void 
                         ws_bytes, stream, nullptr, nullptr, seqlens);
 }
 
-race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
-                                     const float *W, int L, int P, int causal, int B, int H,
-                                     int64_t N, int d, race_dtype_t dt, int chunk, void *O,
-                                     float *den, void *workspace, size_t ws_bytes, void *stream)
+// Hard hashing: the bucket-id kernels for 16-bit rows with L <= 32, P <= 4,
+// d = 32 or 64; otherwise the chunked soft kernels with t = +-1 (no int32
+// counts there).
+static race_status_t hard_impl(const void *Q, const void *K, const void *V, const float *W, int L,
+                               int P, int causal, int B, int H, int64_t N, int d, race_dtype_t dt,
+                               int chunk, void *O, float *den, int32_t *count, void *workspace,
+                               size_t ws_bytes, void *stream)
 {
     if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
     Plan p;
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
-    if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
-    const Tracer tr{nullptr, static_cast<hipStream_t>(stream)};
+    if (!hard_fused(p, dt)) {
+        // tau = 0 selects hard hashing in the soft kernels
+        if (count) return RACE_ERR_UNSUPPORTED;
+        if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
+        const Tracer tr{nullptr, static_cast<hipStream_t>(stream)};
+        (void)hipGetLastError();
+        char *ws = static_cast<char *>(workspace);
+        if (p.split && dt == RACE_BF16)
+            split_forward<bf16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+        else if (p.split)
+            split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+        else if (dt == RACE_BF16)
+            dispatch_forward<bf16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+        else if (dt == RACE_F16)
+            dispatch_forward<_Float16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+        else
+            dispatch_forward<float>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+        return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+    }
+    const HardPlan h = hard_plan(p);
+    if (ws_bytes < h.total || ((uintptr_t)workspace & 255)) return RACE_ERR_WORKSPACE;
     (void)hipGetLastError();
-    char *ws = static_cast<char *>(workspace);
-    if (p.split && dt == RACE_BF16)
-        split_forward<bf16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
-    else if (p.split)
-        split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
-    else if (dt == RACE_BF16)
-        dispatch_forward<bf16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
-    else if (dt == RACE_F16)
-        dispatch_forward<_Float16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
-    else
-        dispatch_forward<float>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+    hard_forward_launch(p, dt, Q, K, V, W, causal, O, den, count, static_cast<char *>(workspace),
+                        static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
+}
+
+race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
+                                     const float *W, int L, int P, int causal, int B, int H,
+                                     int64_t N, int d, race_dtype_t dt, int chunk, void *O,
+                                     float *den, void *workspace, size_t ws_bytes, void *stream)
+{
+    return hard_impl(Q, K, V, W, L, P, causal, B, H, N, d, dt, chunk, O, den, nullptr, workspace,
+                     ws_bytes, stream);
+}
+
+race_status_t race_attn_forward_hard_counts(const void *Q, const void *K, const void *V,
+                                            const float *W, int L, int P, int causal, int B, int H,
+                                            int64_t N, int d, race_dtype_t dt, int chunk, void *O,
+                                            float *den, int32_t *count, void *workspace,
+                                            size_t ws_bytes, void *stream)
+{
+    if (!count) return RACE_ERR_NULL;
+    return hard_impl(Q, K, V, W, L, P, causal, B, H, N, d, dt, chunk, O, den, count, workspace,
+                     ws_bytes, stream);
 }
 
 race_status_t race_attn_forward(const void *Q, const void *K, const void *V, const float *W,
@@ -741,6 +775,33 @@ race_status_t race_attn_forward_noalloc(const void *Q, const void *K, const void
     if ((st = scratch_address(&ws)) != RACE_OK) return st;
     return forward_impl(Q, K, V, W, L, P, tau, causal, B, H, N, d, dt, chunk, O, den, ws,
                         RACE_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, nullptr);
+}
+
+race_status_t race_attn_hash_ids_workspace_bytes(int L, int P, int d, size_t *bytes)
+{
+    if (!bytes) return RACE_ERR_NULL;
+    if (L < 1 || P < 1 || d < 1) return RACE_ERR_SHAPE;
+    if (L > 128 || P > 6 || d > 128 || d % 8 != 0) return RACE_ERR_UNSUPPORTED;
+    *bytes = hard_ids_ws(L, P, d);
+    return RACE_OK;
+}
+
+race_status_t race_attn_hash_ids(const void *X, int64_t rows, int d, race_dtype_t dt,
+                                 const float *W, int L, int P, uint8_t *ids, void *workspace,
+                                 size_t ws_bytes, void *stream)
+{
+    size_t need = 0;
+    race_status_t st = race_attn_hash_ids_workspace_bytes(L, P, d, &need);
+    if (st != RACE_OK) return st;
+    if (rows < 0 || rows > ((int64_t)1 << 40)) return RACE_ERR_SHAPE;
+    if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
+    if (rows == 0) return RACE_OK;
+    if (!X || !W || !ids || !workspace) return RACE_ERR_NULL;
+    if (ws_bytes < need || ((uintptr_t)workspace & 255)) return RACE_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    hard_ids_launch(X, rows, d, dt, W, L, P, ids, static_cast<char *>(workspace),
+                    static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }
 
 const char *race_attn_status_string(race_status_t status)

@@ -516,7 +516,8 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(
                     float m = 0.f;
 #pragma unroll
                     for (int ww = 0; ww < NW; ++ww) m += red[ww][i * NCOL + HD];
-                    Outh[tok * HD + c] = from_f32<T>(n / m);
+                    // m = 0 only under hard hashing (no colliding key): o = 0
+                    Outh[tok * HD + c] = from_f32<T>(m != 0.f ? n / m : 0.f);
                     if (c == 0) denh[tok] = m;
                 }
             }

@@ -1,0 +1,515 @@
+// race_hard.h -- hard-hash RACE attention for gfx950: integer bucket ids per
+// (row, table), int32 bucket counts and fp32 value sums.
+//
+// Pages: "RACE Attention: A Strictly Linear-Time Attention for Long-Sequence
+// Training", gist.science/zh/paper/2510.04008, technical summary §2.2 (the
+// original RACE count arrays, which the soft hash makes differentiable) and
+// §3; gist.science/es/paper/2510.04008, technical summary §2 item 3 (hard,
+// YOSO-style hashing as the contrast).  With tau -> 0 the corner softmax of
+// table l becomes one corner, r_l(x) = sum_p [u_lp >= 0] 2^p with u = W x
+// (x / |x| has the same signs), and the bucket statistics are true counts
+// A_l[r] and value sums B_l[r].
+//
+// Bucket ids.  A sign decided in floating point is exact unless the sum is
+// within its rounding error of zero.  Here every product is exact: W is
+// split into three bf16 terms that add up to the fp32 value exactly, and
+// a row into one (bf16), two (fp16) or three (fp32) bf16 terms, so every
+// product of terms is exact in the fp32 MFMA accumulators; only the fp32
+// additions round, and the decision differs from the exact sign only when
+// |sum_t W_t x_t| is within n 2^-24 sum_t |W_t x_t|, n the number of terms.
+#pragma once
+#include "race_walk.h"
+
+namespace race {
+
+// W [L][P][d] fp32 -> three bf16 terms [3][LPpad][Dpad] (zero padding), with
+// W = t0 + t1 + t2 exactly: each term is the previous remainder rounded to
+// bf16, and after two roundings at most 8 significant bits remain.
+static __global__ __launch_bounds__(256) void hard_wsplit_kernel(const float *__restrict__ W, int LP,
+                                                                 int d, int LPpad, int Dpad,
+                                                                 bf16 *__restrict__ out)
+{
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= LPpad * Dpad) return;
+    const int hp = e / Dpad, c = e % Dpad;
+    const float w = hp < LP && c < d ? W[hp * d + c] : 0.f;
+    const bf16 a = (bf16)w;
+    const float r1 = w - (float)a;
+    const bf16 b = (bf16)r1;
+    const bf16 c2 = (bf16)(r1 - (float)b);
+    const int n = LPpad * Dpad;
+    out[e] = a;
+    out[n + e] = b;
+    out[2 * n + e] = c2;
+}
+
+// bf16 terms of eight row elements: XT terms, x = sum of the terms exactly
+template <typename IO> struct XTerms;
+template <> struct XTerms<bf16> {
+    static constexpr int N = 1;
+    static __device__ __forceinline__ void split(u32x4 raw, bf16x8 (&t)[1]) { t[0] = __builtin_bit_cast(bf16x8, raw); }
+};
+template <> struct XTerms<_Float16> {
+    static constexpr int N = 2;
+    static __device__ __forceinline__ void split(u32x4 raw, bf16x8 (&t)[2])
+    {
+        const halfx4 *h = reinterpret_cast<const halfx4 *>(&raw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = (float)h[i >> 2][i & 3];
+            const bf16 a = (bf16)x;
+            t[0][i] = a;
+            t[1][i] = (bf16)(x - (float)a);
+        }
+    }
+};
+template <> struct XTerms<float> {
+    static constexpr int N = 3;
+    static __device__ __forceinline__ void split(const float (&x)[8], bf16x8 (&t)[3])
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bf16 a = (bf16)x[i];
+            const float r1 = x[i] - (float)a;
+            const bf16 b = (bf16)r1;
+            t[0][i] = a;
+            t[1][i] = b;
+            t[2][i] = (bf16)(r1 - (float)b);
+        }
+    }
+};
+
+// hard_ids_kernel: ids[row][l] = sum_p [u_lp >= 0] 2^p, u = W x, for `rows`
+// rows of d elements (d a multiple of 8, at most 128).  A wave takes 16 rows:
+// U^T tiles of 16 hyperplanes x 16 rows on MFMA (W terms x row terms, every
+// product exact), the signs gathered into a bit mask per row in LDS, then one
+// thread per (row, table) assembles the id.
+constexpr int HARD_ROWS = 64;  // rows per workgroup (4 waves)
+constexpr int HARD_MAXW = 24;  // 32-bit mask words per row: L P <= 768
+
+template <typename IO>
+__global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X, int64_t rows, int d,
+                                                       const bf16 *__restrict__ wsp, int L, int P,
+                                                       int LPpad, int Dpad, uint8_t *__restrict__ ids)
+{
+    __shared__ uint32_t mask[HARD_ROWS][HARD_MAXW + 1];
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const int64_t r0 = (int64_t)blockIdx.x * HARD_ROWS;
+    const int64_t row = r0 + w * 16 + c16;
+    const int nkb = Dpad / 32, nht = LPpad / 16, nterm = LPpad * Dpad;
+    constexpr int XT = XTerms<IO>::N;
+    // this lane's row pieces: dims 32 kb + 8 g .. + 8 (zeros past d or past the rows)
+    const Rsrc rx = make_rsrc(X + r0 * d, (int)(min<int64_t>(HARD_ROWS, rows - r0) * d * sizeof(IO)));
+    bf16x8 xt[4][XT];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        if (kb >= nkb) break;
+        const int col = kb * 32 + 8 * g;
+        const int off = col < d ? (int)(((w * 16 + c16) * d + col) * sizeof(IO)) : OOB;
+        if constexpr (sizeof(IO) == 2) {
+            XTerms<IO>::split(bld128(rx, off), xt[kb]);
+        } else {
+            // (the whole vector is reinterpreted: a bit cast of one element of
+            // the loaded vector was compiled as a read of its first element)
+            const floatx4 a = __builtin_bit_cast(floatx4, bld128(rx, off));
+            const floatx4 b = __builtin_bit_cast(floatx4, bld128(rx, col < d ? off + 16 : OOB));
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = a[i];
+                x[4 + i] = b[i];
+            }
+            XTerms<IO>::split(x, xt[kb]);
+        }
+    }
+    // pairs of hyperplane tiles make one 32-bit word: lane group g holds the
+    // nibbles at bits 4 g (tile 2 j) and 16 + 4 g (tile 2 j + 1)
+    for (int wd = 0; wd < (nht + 1) / 2; ++wd) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int ht = 2 * wd + h2;
+            if (ht >= nht) break;
+            floatx4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < nkb; ++kb) {
+                const int hp = ht * 16 + c16, col = kb * 32 + 8 * g;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    const bf16x8 wa = *reinterpret_cast<const bf16x8 *>(wsp + t * nterm + hp * Dpad + col);
+#pragma unroll
+                    for (int s = 0; s < XT; ++s) mma32(u, wa, xt[kb][s]);
+                }
+            }
+            // u[r]: hyperplane 16 ht + 4 g + r of row c16; u = 0 counts as >= 0
+            uint32_t nib = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nib |= (u[r] >= 0.f ? 1u : 0u) << r;
+            word |= nib << (16 * h2 + 4 * g);
+        }
+        word |= __shfl_xor(word, 16);
+        word |= __shfl_xor(word, 32);
+        if (g == 0) mask[w * 16 + c16][wd] = word;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < HARD_ROWS * L; e += 256) {
+        const int rr = e / L, l = e % L;
+        if (r0 + rr >= rows) continue;
+        const int b0 = l * P;
+        // bits b0 .. b0 + P - 1 of the row's mask (P <= 8: at most two words)
+        const uint64_t two = (uint64_t)mask[rr][b0 >> 5] |
+                             ((b0 >> 5) + 1 < HARD_MAXW ? (uint64_t)mask[rr][(b0 >> 5) + 1] << 32 : 0);
+        ids[(r0 + rr) * L + l] = (uint8_t)((two >> (b0 & 31)) & ((1u << P) - 1));
+    }
+}
+
+}  // namespace race
+
+namespace race {
+
+// ---------------------------------------------------------------------------
+// Hard-hash sums and readout on the bucket ids (L <= 32, P <= 4, 16-bit rows).
+// The work split is the soft kernels': a workgroup per (head, segment), NW
+// waves of 4 tables each, chunks of 32 tokens.  A wave keeps the value sums
+// of its 4 tables as 4 MFMA tiles of 16 buckets x 64 value columns (fp32);
+// the one-hot operands built from the ids make every product 0 or a value,
+// exact.  Counts are int32 in LDS, [table][16 buckets]: added per key, and
+// gathered per query, exactly.
+constexpr int HNT = 4;  // value column tiles (64 columns)
+
+// bf16 one-hot quadruples: entry n holds 1.0 in slot i when bit i of n is set
+__device__ __forceinline__ void stage_lut(uint32_t *lut)
+{
+    if (threadIdx.x < 16) {
+        const uint32_t n = threadIdx.x;
+        lut[2 * n] = (n & 1 ? 0x3F80u : 0u) | (n & 2 ? 0x3F800000u : 0u);
+        lut[2 * n + 1] = (n & 4 ? 0x3F80u : 0u) | (n & 8 ? 0x3F800000u : 0u);
+    }
+}
+__device__ __forceinline__ bf16x4 lut4(const uint32_t *lut, uint32_t nib)
+{
+    return __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(lut + 2 * nib));
+}
+// token-major one-hot operand (lane group g: buckets 4g .. 4g + 3 of tables
+// t0 then t1, the K-slot order of the state operands); id 16 (none) gives zeros
+__device__ __forceinline__ uint32_t onehot_bit(uint32_t id) { return id < 16u ? 1u << id : 0u; }
+__device__ __forceinline__ bf16x8 onehot_tm(const uint32_t *lut, uint32_t id0, uint32_t id1, int g)
+{
+    return cat8(lut4(lut, (onehot_bit(id0) >> (4 * g)) & 15u), lut4(lut, (onehot_bit(id1) >> (4 * g)) & 15u));
+}
+// feature-major one-hot operand of one table from its bucket's token mask
+// (bit j: token j of the chunk falls in the bucket); K-slots (g, r) <-> token
+// 4g + r, (g, 4 + r) <-> token 16 + 4g + r, as ycol_frag
+__device__ __forceinline__ bf16x8 onehot_fm(const uint32_t *lut, uint32_t m, int g)
+{
+    return cat8(lut4(lut, (m >> (4 * g)) & 15u), lut4(lut, (m >> (16 + 4 * g)) & 15u));
+}
+
+// ids of one chunk's rows: rsrc over its nv rows of L bytes, rounded up to
+// whole dwords (a dword past the range reads as zero; the id arrays carry
+// padding, and bytes past the valid rows are never counted)
+__device__ __forceinline__ Rsrc id_res(const uint8_t *seg_ids, int L, const Chunk &c)
+{
+    return make_rsrc(seg_ids + (int64_t)c.tok0 * L, (c.nv * L + 3) & ~3);
+}
+// the chunk's 32 L id bytes as dwords into LDS (zeros past the valid rows)
+template <int NTHR>
+__device__ __forceinline__ void stage_ids(Rsrc r, int L, uint32_t *dst)
+{
+    for (int e = threadIdx.x; e < 8 * L; e += NTHR) dst[e] = __builtin_amdgcn_raw_buffer_load_b32(r, 4 * e, 0, 0);
+}
+__device__ __forceinline__ uint32_t id_at(const uint32_t *ids, int L, int tok, int l)
+{
+    const int b = tok * L + l;
+    return (ids[b >> 2] >> (8 * (b & 3))) & 0xffu;
+}
+
+// hard_sum_kernel: per (head, segment) the value sums B[l][r][:] (FxC
+// tiles, stored as the soft kernels' state blocks) and int32 counts
+// A[l][r] of the segment's keys.
+template <int NW, typename IO, int D>
+__global__ __launch_bounds__(NW * 64) void hard_sum_kernel(
+    const IO *__restrict__ V, const uint8_t *__restrict__ idk, int L, int64_t N, int seg,
+    int64_t nseg, float *__restrict__ st, int *__restrict__ cst, Lens ls)
+{
+    constexpr int NTHR = NW * 64;
+    __shared__ __attribute__((aligned(16))) bf16 ycol[2][NCOL * YCS];
+    __shared__ uint32_t ids[2][8 * 32];
+    __shared__ uint32_t bmask[2][32 * 16];
+    __shared__ int cnt[32 * 16];
+    __shared__ uint32_t lut[32];
+    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
+    const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
+    const int nch = (tend + WCT - 1) / WCT;
+    ValSrc<IO> vh{V + row0 * D, nullptr, nullptr};
+    const uint8_t *ids_seg = idk + row0 * L;
+    stage_lut(lut);
+    for (int e = threadIdx.x; e < 32 * 16; e += NTHR) {
+        cnt[e] = 0;
+        bmask[0][e] = 0u;
+        bmask[1][e] = 0u;
+    }
+    ystage_zero_pad<NTHR>(ycol[0]);
+    ystage_zero_pad<NTHR>(ycol[1]);
+    floatx4 acc[4][HNT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < HNT; ++ct) acc[s][ct] = {0.f, 0.f, 0.f, 0.f};
+    auto chunk = [&](int ci) -> Chunk {
+        if (ci >= nch) return Chunk{0, 0};
+        return Chunk{ci * WCT, min(WCT, tend - ci * WCT)};
+    };
+    YStage<NTHR, false> ys;
+    __syncthreads();
+    for (int ci = 0; ci < nch; ++ci) {
+        const int b = ci & 1;
+        const Chunk cc = chunk(ci);
+        // stage ids and [v | 1] of chunk ci; clear the masks of chunk ci + 1
+        stage_ids<NTHR>(id_res(ids_seg, L, cc), L, ids[b]);
+        ystage_load<NTHR, false, D>(yres<false, D>(vh, cc), ys);
+        ystage_store<NTHR, false, IO>(ys, cc.nv, ycol[b]);
+        __syncthreads();
+        // the other chunks' mask buffer was last read before this barrier
+        for (int e = threadIdx.x; e < 32 * 16; e += NTHR) bmask[b ^ 1][e] = 0u;
+        // bucket token masks and counts of the chunk's keys
+        for (int e = threadIdx.x; e < 32 * L; e += NTHR) {
+            const int j = e / L, l = e % L;
+            if (j < cc.nv) {
+                const uint32_t id = id_at(ids[b], L, j, l);
+                atomicOr(&bmask[b][l * 16 + id], 1u << j);
+                atomicAdd(&cnt[l * 16 + id], 1);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int T = 4 * w + s;
+            const bf16x8 a = onehot_fm(lut, T < L ? bmask[b][T * 16 + c16] : 0u, g);
+#pragma unroll
+            for (int ct = 0; ct < HNT; ++ct) mma32(acc[s][ct], a, ycol_frag(ycol[b], ct * 16 + c16));
+        }
+    }
+    const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 4 * HNT * 64 * 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ct = 0; ct < HNT; ++ct)
+            *reinterpret_cast<floatx4 *>(st + blk + (((w * 4 + s) * HNT + ct) * 64 + lane) * 4) = acc[s][ct];
+    __syncthreads();
+    int *cdst = cst + (bh * (nseg + 1) + sg) * (int64_t)(32 * 16);
+    for (int e = threadIdx.x; e < 32 * 16; e += NTHR) cdst[e] = e < L * 16 ? cnt[e] : 0;
+}
+
+// Scan of the int32 count blocks over segments (exclusive prefix, head
+// total at index nseg), one thread per count, in segment order.
+static __global__ __launch_bounds__(256) void hard_count_scan_kernel(int *__restrict__ cst, int64_t nseg,
+                                                                     int elems)
+{
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= elems) return;
+    int *p = cst + blockIdx.y * (nseg + 1) * (int64_t)elems + e;
+    int run = 0;
+    for (int64_t g = 0; g < nseg; ++g) {
+        const int v = p[g * elems];
+        p[g * elems] = run;
+        run += v;
+    }
+    p[nseg * elems] = run;
+}
+
+// hard_walk_kernel: o_i = sum_l B_l[r_l(q_i)] / sum_l A_l[r_l(q_i)] over the
+// keys j <= i (causal) or all keys, from the segment's prefix state (values:
+// fp32 tiles read as bf16 MFMA operands; counts: int32, exact), the chunks
+// before i in the segment, and the chunk's own keys j <= i.  den = the count
+// (as fp32) and, when count is not null, the count itself (int32).
+template <int NW, bool CAUSAL, typename IO, int D>
+__global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
+    const IO *__restrict__ V, const uint8_t *__restrict__ idq, const uint8_t *__restrict__ idk,
+    int L, int64_t N, int seg, int64_t nseg, const float *__restrict__ st,
+    const int *__restrict__ cst, IO *__restrict__ Out, float *__restrict__ den,
+    int *__restrict__ count, Lens ls)
+{
+    constexpr int NTHR = NW * 64;
+    constexpr int REDN = NW * 2 * HNT * 64 * 4;  // partial outputs of every wave
+    constexpr int REDM = NW * 2 * 64;            // and their intra-chunk counts
+    __shared__ __attribute__((aligned(16))) bf16 ycol[2][CAUSAL ? NCOL * YCS : 8];
+    __shared__ uint32_t qids[2][8 * 32];
+    __shared__ uint32_t kids[2][CAUSAL ? 8 * 32 : 1];
+    __shared__ uint32_t bmask[2][CAUSAL ? 32 * 16 : 1];
+    __shared__ int cnt[2][32];     // per query: counts gathered from A
+    __shared__ int A[32 * 16];     // counts of the keys before the chunk
+    __shared__ uint32_t lut[32];
+    __shared__ __attribute__((aligned(16))) float red[REDN + REDM];
+    const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
+    const int tend = (int)max<int64_t>(0, min<int64_t>(valid_rows(ls, bh, N), t_begin + seg) - t_begin);
+    const int nch = (tend + WCT - 1) / WCT;
+    ValSrc<IO> vh{V + row0 * D, nullptr, nullptr};
+    const uint8_t *q_seg = idq + row0 * L, *k_seg = idk + row0 * L;
+    IO *Os = Out + row0 * D;
+    float *dens = den + row0;
+    int *cnts = count ? count + row0 : nullptr;
+    stage_lut(lut);
+    const int64_t sidx = bh * (nseg + 1) + (CAUSAL ? sg : nseg);
+    {
+        const int *src = cst + sidx * (int64_t)(32 * 16);
+        for (int e = threadIdx.x; e < 32 * 16; e += NTHR) A[e] = src[e];
+        for (int e = threadIdx.x; e < 2 * 32 * 16; e += NTHR)
+            if (CAUSAL) bmask[e >> 9][e & 511] = 0u;
+        if (threadIdx.x < 64) cnt[threadIdx.x >> 5][threadIdx.x & 31] = 0;
+    }
+    if (CAUSAL) {
+        ystage_zero_pad<NTHR>(ycol[0]);
+        ystage_zero_pad<NTHR>(ycol[1]);
+    }
+    floatx4 acc[4][HNT];
+    {
+        const float *src = st + sidx * (int64_t)(NW * 4 * HNT * 64 * 4);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int ct = 0; ct < HNT; ++ct)
+                acc[s][ct] = *reinterpret_cast<const floatx4 *>(src + (((w * 4 + s) * HNT + ct) * 64 + lane) * 4);
+    }
+    auto chunk = [&](int ci) -> Chunk {
+        if (ci >= nch) return Chunk{0, 0};
+        return Chunk{ci * WCT, min(WCT, tend - ci * WCT)};
+    };
+    YStage<NTHR, false> ys;
+    __syncthreads();
+    for (int ci = 0; ci < nch; ++ci) {
+        const int b = ci & 1;
+        const Chunk cc = chunk(ci);
+        // stage ids (and keys' [v | 1]); clear the next chunk's masks and counts
+        stage_ids<NTHR>(id_res(q_seg, L, cc), L, qids[b]);
+        if (CAUSAL) {
+            stage_ids<NTHR>(id_res(k_seg, L, cc), L, kids[b]);
+            ystage_load<NTHR, false, D>(yres<false, D>(vh, cc), ys);
+            ystage_store<NTHR, false, IO>(ys, cc.nv, ycol[b]);
+            for (int e = threadIdx.x; e < 32 * 16; e += NTHR) bmask[b ^ 1][e] = 0u;
+        }
+        if (threadIdx.x < 32) cnt[b ^ 1][threadIdx.x] = 0;
+        __syncthreads();
+        // keys' bucket token masks; queries' counts of the keys before the chunk
+        for (int e = threadIdx.x; e < 32 * L; e += NTHR) {
+            const int j = e / L, l = e % L;
+            if (j < cc.nv) {
+                if (CAUSAL) atomicOr(&bmask[b][l * 16 + id_at(kids[b], L, j, l)], 1u << j);
+                atomicAdd(&cnt[b][j], A[l * 16 + id_at(qids[b], L, j, l)]);
+            }
+        }
+        __syncthreads();
+        // one-hot operands of this wave's tables 4w .. 4w + 3 (16: none)
+        bf16x8 pr[2][2], pw[2][2], pfm[4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int t0 = 4 * w + 2 * k, tok = 16 * tt + c16;
+                const uint32_t q0 = t0 < L ? id_at(qids[b], L, tok, t0) : 16u;
+                const uint32_t q1 = t0 + 1 < L ? id_at(qids[b], L, tok, t0 + 1) : 16u;
+                pr[tt][k] = onehot_tm(lut, q0, q1, g);
+                if (CAUSAL) {
+                    const uint32_t k0 = t0 < L ? id_at(kids[b], L, tok, t0) : 16u;
+                    const uint32_t k1 = t0 + 1 < L ? id_at(kids[b], L, tok, t0 + 1) : 16u;
+                    pw[tt][k] = onehot_tm(lut, k0, k1, g);
+                }
+            }
+        if (CAUSAL)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                pfm[s] = onehot_fm(lut, 4 * w + s < L ? bmask[b][(4 * w + s) * 16 + c16] : 0u, g);
+        floatx4 oacc[2][HNT + 1];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ct = 0; ct <= HNT; ++ct) oacc[tt][ct] = {0.f, 0.f, 0.f, 0.f};
+        // the state of the keys before the chunk (value columns)
+#pragma unroll
+        for (int ct = 0; ct < HNT; ++ct) {
+            bf16x8 sf[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) sf[k] = cat8(acc2bf4(acc[2 * k][ct]), acc2bf4(acc[2 * k + 1][ct]));
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) mma32(oacc[tt][ct], sf[k], pr[tt][k]);
+        }
+        if (CAUSAL) {
+            // collision counts D[j][i] of writer j and reader i over the wave's
+            // tables (exact small integers), keys j <= i only
+            constexpr int TJ[3] = {0, 0, 1}, TI[3] = {0, 1, 1};
+            floatx4 sc[3];
+#pragma unroll
+            for (int pi = 0; pi < 3; ++pi) {
+                sc[pi] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < 2; ++k) mma32(sc[pi], pw[TJ[pi]][k], pr[TI[pi]][k]);
+            }
+#pragma unroll
+            for (int pi = 0; pi < 3; pi += 2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[pi][r] = 4 * g + r <= c16 ? sc[pi][r] : 0.f;
+            const bf16x4 z4 = pk4(0, 0);
+            const bf16x8 kA1 = cat8(acc2bf4(sc[0]), z4);              // reader tile 0: writer tile 0
+            const bf16x8 kA8 = cat8(acc2bf4(sc[1]), acc2bf4(sc[2]));  // reader tile 1: writer tiles 0, 1
+#pragma unroll
+            for (int ct = 0; ct <= HNT; ++ct) {
+                const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + c16);
+                mma32(oacc[0][ct], yb, kA1);
+                mma32(oacc[1][ct], yb, kA8);
+                if (ct < HNT)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
+            }
+        }
+        // partial outputs of this wave: value tiles and the intra-chunk counts
+        // (count column 64: row 0 of column tile HNT, lanes 0 .. 15)
+        float *rn = red, *rm = red + REDN;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int ct = 0; ct < HNT; ++ct)
+                *reinterpret_cast<floatx4 *>(rn + (((w * 2 + tt) * HNT + ct) * 64 + lane) * 4) = oacc[tt][ct];
+            rm[(w * 2 + tt) * 64 + lane] = oacc[tt][HNT][0];
+        }
+        __syncthreads();
+        // outputs of the chunk: thread slot (token tile tt, column tile ct, lane)
+        const Rsrc ro = row_res<D>(Os, cc);
+        for (int sl = threadIdx.x; sl < 2 * HNT * 64; sl += NTHR) {
+            const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63, tok = tt * 16 + (ln & 15);
+            floatx4 n = *reinterpret_cast<const floatx4 *>(rn + ((tt * HNT + ct) * 64 + ln) * 4);
+            float mi = rm[tt * 64 + (ln & 15)];
+            for (int ww = 1; ww < NW; ++ww) {
+                n += *reinterpret_cast<const floatx4 *>(rn + (((ww * 2 + tt) * HNT + ct) * 64 + ln) * 4);
+                mi += rm[(ww * 2 + tt) * 64 + (ln & 15)];
+            }
+            // the chunk's own collisions are at most 32 L: exact in fp32
+            const int m = cnt[b][tok] + (CAUSAL ? (int)mi : 0);
+            // a query that meets no visible key in any table: an empty sum,
+            // o = 0 (n is 0 too)
+            const float inv = m > 0 ? 1.f / (float)m : 0.f;
+            const int col = 16 * ct + 4 * (ln >> 4);
+            const int off = (D == HD || col < D) ? tok * (D * 2) + col * 2 : OOB;
+            bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
+            if (ct == 0 && ln < 16) {
+                bstf((float)m, make_rsrc(dens + cc.tok0, cc.nv * 4), tok * 4);
+                if (cnts)
+                    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)m, make_rsrc(cnts + cc.tok0, cc.nv * 4),
+                                                          tok * 4, 0, 0);
+            }
+        }
+        // the chunk's keys join the counts (read again after the next barrier)
+        if (CAUSAL)
+            for (int e = threadIdx.x; e < 32 * L; e += NTHR) {
+                const int j = e / L, l = e % L;
+                if (j < cc.nv) atomicAdd(&A[l * 16 + id_at(kids[b], L, j, l)], 1);
+            }
+        __syncthreads();
+    }
+}
+
+}  // namespace race

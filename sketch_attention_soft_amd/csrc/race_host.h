@@ -15,6 +15,7 @@
 #include "race_fwd.h"
 #include "race_stream.h"
 #include "race_walk.h"
+#include "race_hard.h"
 
 namespace race_host {
 
@@ -577,6 +578,53 @@ void launch_stream(const StreamPlan &sp, const void *Q, const void *K, const voi
                        static_cast<const T *>(K), static_cast<const T *>(V), W, sp.L, sp.P, sp.d, 1.f / tau,
                        N, blk, state, part, static_cast<T *>(O), den);
 }
+
+// Hard hashing (race_hard.h, launched from race_inst_hard.hip).  Workspace of
+// the bucket ids: the three bf16 terms of W, [3][LPpad][Dpad].
+inline int hard_lppad(int L, int P) { return (L * P + 31) / 32 * 32; }
+inline int hard_dpad(int d) { return (d + 31) / 32 * 32; }
+inline size_t hard_ids_ws(int L, int P, int d)
+{
+    return align256((size_t)3 * hard_lppad(L, P) * hard_dpad(d) * sizeof(bf16));
+}
+void hard_ids_launch(const void *X, int64_t rows, int d, race_dtype_t dt, const float *W, int L,
+                     int P, uint8_t *ids, char *ws, hipStream_t s);
+
+// Hard forward on the bucket ids (16-bit rows, L <= 32, P <= 4, d = 32 or 64).
+// Workspace: ids of Q and K (padded), the W terms, value states, count
+// states and the value scan's group totals.
+struct HardPlan {
+    size_t ids_bytes, wsplit, vstate, cstate, scan, total;
+    size_t o_idq, o_idk, o_w, o_v, o_c, o_scan;
+    int hw;            // waves per workgroup (4 tables each)
+    int64_t velems;    // floats of one value state block
+};
+inline HardPlan hard_plan(const Plan &p)
+{
+    HardPlan h;
+    h.hw = 2 * p.nw;
+    h.velems = (int64_t)h.hw * 4 * race::HNT * 64 * 4;
+    h.ids_bytes = align256((size_t)p.rows * p.L + 4);
+    h.wsplit = hard_ids_ws(p.L, p.P, p.d);
+    h.vstate = align256((size_t)p.BH * (p.nseg + 1) * h.velems * sizeof(float));
+    h.cstate = align256((size_t)p.BH * (p.nseg + 1) * 32 * 16 * sizeof(int));
+    h.scan = align256((size_t)p.BH * p.scan_groups * h.velems * sizeof(float));
+    h.o_idq = 0;
+    h.o_idk = h.o_idq + h.ids_bytes;
+    h.o_w = h.o_idk + h.ids_bytes;
+    h.o_v = h.o_w + h.wsplit;
+    h.o_c = h.o_v + h.vstate;
+    h.o_scan = h.o_c + h.cstate;
+    h.total = h.o_scan + h.scan;
+    return h;
+}
+inline bool hard_fused(const Plan &p, race_dtype_t dt)
+{
+    return (dt == RACE_BF16 || dt == RACE_F16) && p.L <= 32 && p.P <= 4 && (p.d == 64 || p.d == 32);
+}
+void hard_forward_launch(const Plan &p, race_dtype_t dt, const void *Q, const void *K, const void *V,
+                         const float *W, int causal, void *O, float *den, int *count, char *ws,
+                         hipStream_t s);
 
 // Launch sequences instantiated in race_inst_*.hip (one file per row type
 // and direction), not in the files that call them.

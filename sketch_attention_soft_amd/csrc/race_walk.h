@@ -1012,7 +1012,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
                         bstf(m, make_rsrc(pm + c.tok0, c.nv * 4), moff);
                     } else {
                         if constexpr (PART == PART_IN) m += bldf(make_rsrc(pm + c.tok0, c.nv * 4), tok * 4);
-                        const float inv = __builtin_amdgcn_rcpf(m);
+                        // m = 0 only under hard hashing (no colliding key): o = 0
+                        const float inv = m != 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
                         bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
                         bstf(m, make_rsrc(dens + c.tok0, c.nv * 4), moff);
                     }

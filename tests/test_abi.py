@@ -474,7 +474,23 @@ def test_state_add_fast_workspace(lib):
         assert fn(FAKE, FAKE, FAKE, Lt, 4, 1.0, 1, 2, N, 64, dt, FAKE, FAKE, fast - 1, None) == E_WS
     assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 3, ctypes.byref(sz)) == E_UNSUP
     assert ws(1, 1, 4096, 64, 40, 4, 1, 0, BF16, 3, ctypes.byref(sz)) == E_UNSUP
-    assert ws(1, 1, 4096, 64, 8, 4, 1, 0, BF16, 4, ctypes.byref(sz)) != OK
+    assert ws(1, 1, 4096, 64, 8, 4, 1, 0, BF16, 5, ctypes.byref(sz)) != OK    # no such code
+
+
+def test_hard_forward_workspace(lib):
+    """for_backward = 4 sizes race_attn_forward_hard(_counts): on the
+    bucket-id shapes the ids of Q and K (one byte per row and table) and the
+    value and count states; elsewhere the soft forward's workspace."""
+    sz = ctypes.c_size_t(0)
+    ws = lib.race_attn_workspace_bytes
+    for (N, Lt) in ((4096, 8), (1 << 20, 32), (70000, 16)):
+        assert ws(1, 2, N, 64, Lt, 4, 1, 0, BF16, 4, ctypes.byref(sz)) == OK
+        assert sz.value >= 2 * 2 * N * Lt    # the two id arrays
+    # fp32 rows: the soft kernels with t = +-1, the forward's workspace
+    assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 4, ctypes.byref(sz)) == OK
+    hard = sz.value
+    assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 0, ctypes.byref(sz)) == OK
+    assert hard == sz.value
 
 
 def test_varlen_validation(lib):
