@@ -70,7 +70,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Both enums are int-sized.  Seen from C++ they have int as fixed underlying
+ * type, so any int a C caller passes (an unknown dtype, say) is a value the
+ * library can test and refuse rather than an out-of-range enum. */
+#ifdef __cplusplus
+#define RACE_ENUM_INT : int
+#else
+#define RACE_ENUM_INT
+#endif
+
+typedef enum RACE_ENUM_INT {
     RACE_OK = 0,
     RACE_ERR_NULL = 1,
     RACE_ERR_SHAPE = 2,
@@ -81,7 +90,7 @@ typedef enum {
     RACE_ERR_HIP = 7
 } race_status_t;
 
-typedef enum { RACE_F32 = 0, RACE_BF16 = 1, RACE_F16 = 2 } race_dtype_t;
+typedef enum RACE_ENUM_INT { RACE_F32 = 0, RACE_BF16 = 1, RACE_F16 = 2 } race_dtype_t;
 
 /* Workspace size, in bytes, that race_attn_forward (for_backward = 0),
  * race_attn_backward (for_backward = 1), race_attn_backward_dw

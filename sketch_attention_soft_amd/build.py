@@ -41,8 +41,8 @@ def compile_command(src: str, obj: str, extra=()) -> list:
     return [hipcc(), *FLAGS, "-I", INCLUDE, *extra, "-c", src, "-o", obj]
 
 
-def link_command(objs, out: str) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+def link_command(objs, out: str, extra=()) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", out]
 
 
 def _jobs() -> int:
@@ -59,11 +59,13 @@ def _run(cmd, verbose):
     return res.returncode, res.stdout + res.stderr
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB, link_extra=()) -> str:
     """Compile every translation unit and link, unconditionally; returns the
-    library path."""
+    library path.  extra / link_extra: more compiler / linker flags; out:
+    where the library goes (another build of the same sources, e.g. one
+    instrumented for a test, goes elsewhere)."""
     os.makedirs(OBJDIR, exist_ok=True)
-    tag = "%d" % os.getpid()
+    tag = "%d_%d" % (os.getpid(), abs(hash(out)) % 100000)
     objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + f".{tag}.o") for s in SOURCES]
     with ThreadPoolExecutor(_jobs()) as ex:
         results = list(ex.map(lambda so: _run(compile_command(so[0], so[1], extra), verbose),
@@ -73,15 +75,15 @@ def build(verbose: bool = False, extra=()) -> str:
         for s, out in failed:
             sys.stderr.write(f"--- {os.path.basename(s)}\n{out}")
         raise RuntimeError("hipcc failed compiling " + ", ".join(os.path.basename(s) for s, _ in failed))
-    tmp = LIB + ".tmp" + tag
-    rc, out = _run(link_command(objs, tmp), verbose)
+    tmp = out + ".tmp" + tag
+    rc, log = _run(link_command(objs, tmp, link_extra), verbose)
     for o in objs:
         os.remove(o)
     if rc != 0:
-        sys.stderr.write(out)
-        raise RuntimeError("hipcc failed linking librace_attn.so")
-    os.replace(tmp, LIB)
-    return LIB
+        sys.stderr.write(log)
+        raise RuntimeError("hipcc failed linking " + os.path.basename(out))
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

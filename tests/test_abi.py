@@ -20,11 +20,17 @@ OK, E_NULL, E_SHAPE, E_UNSUP, E_TAU, E_CHUNK, E_WS, E_HIP = range(8)
 F32, BF16, F16 = 0, 1, 2
 
 
+# the library under test: the built one, or another build of the same
+# sources (tests/test_sanitizers.py runs this file against a host build with
+# AddressSanitizer and UndefinedBehaviorSanitizer)
+LIB_UNDER_TEST = os.environ.get("RACE_ABI_TEST_LIB") or hip_build.LIB
+
+
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(hip_build.LIB):
+    if LIB_UNDER_TEST == hip_build.LIB and not os.path.exists(hip_build.LIB):
         hip_build.build()
-    L = ctypes.CDLL(hip_build.LIB)
+    L = ctypes.CDLL(LIB_UNDER_TEST)
     i32, i64, f32, vp, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                              ctypes.c_size_t)
     L.race_attn_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32, i32,
