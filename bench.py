@@ -388,8 +388,10 @@ def generality_bench(args, binding, I, np, torch) -> int:
 def hard_bench(args, binding, I, np, torch) -> int:
     """One JSON line for the hard-hash forward on the workload (forward only:
     the hash has no gradient).  Its algorithmic bytes are one read of Q, K, V
-    and one write of O and den; the step runs the same chunked kernels as the
-    soft forward with t = +-1, so it is reported against HBM and MFMA both."""
+    and one write of O and den (4 d e + 4 per token); on 16-bit rows with
+    L <= 32 it runs on integer bucket ids (hash ids of Q and K, count and
+    value sums per segment, scans, the walk), so it is reported against HBM,
+    with the projections' matrix-core rate beside it."""
     w = I.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -425,8 +427,9 @@ def hard_bench(args, binding, I, np, torch) -> int:
     ms = a.elapsed_time(b) / args.steps
     e = 2 if w.dtype == "bf16" else 4
     bytes_tok = 4 * d * e + 4
-    import dataclasses
-    fwd_flops_tok = algorithmic_per_token(dataclasses.replace(w, backward=False))[0]
+    # the projections u = W x of the query and the key rows; the rest of the
+    # hard path is integer counting and value gathers
+    fwd_flops_tok = 2 * 2 * d * w.L * w.P
     gbs = bytes_tok * w.tokens / (ms * 1e-3) / 1e9
     tfl = fwd_flops_tok * w.tokens / (ms * 1e-3) / 1e12
     line = {
@@ -439,7 +442,8 @@ def hard_bench(args, binding, I, np, torch) -> int:
                    "P": w.P, "causal": w.causal, "passes": "fwd (hard hash)", "chunk": w.chunk},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 5), "traffic": None,
-                     "kernel": "whole forward (sum_kv, scan, fwd_o)", "bytes_per_token": bytes_tok},
+                     "kernel": "whole forward (ids of Q and K, sums, scans, walk)",
+                     "bytes_per_token": bytes_tok},
         "mfma": {"achieved": round(tfl, 3), "peak": PEAK_TFLOPS["bf16" if w.dtype == "bf16" else "f32"],
                  "unit": "TFLOP/s", "flops_per_token": fwd_flops_tok},
     }

@@ -80,37 +80,31 @@ template <> struct XTerms<float> {
 };
 
 // hard_ids_kernel: ids[row][l] = sum_p [u_lp >= 0] 2^p, u = W x, for `rows`
-// rows of d elements (d a multiple of 8, at most 128).  A wave takes 16 rows:
-// U^T tiles of 16 hyperplanes x 16 rows on MFMA (W terms x row terms, every
-// product exact), the signs gathered into a bit mask per row in LDS, then one
-// thread per (row, table) assembles the id.
-constexpr int HARD_ROWS = 64;  // rows per workgroup (4 waves)
+// rows of d elements (d a multiple of 8, at most 32 NKB).  A workgroup takes
+// 256 rows; wave w keeps the W terms of the hyperplane words w, w + 4, ...
+// (32 hyperplanes each) in registers and streams the block's 16 row tiles
+// through them: U^T tiles of 16 hyperplanes x 16 rows on MFMA (W terms x row
+// terms, every product exact), the next row tile loading while the current
+// one is multiplied.  The signs are gathered into a bit mask per row in LDS,
+// then one thread per row cuts the row's L ids out of its mask and stores
+// them.
 constexpr int HARD_MAXW = 24;  // 32-bit mask words per row: L P <= 768
+constexpr int IDS_ROWS = 256;  // rows per workgroup (4 waves)
 
-template <typename IO>
-__global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X, int64_t rows, int d,
-                                                       const bf16 *__restrict__ wsp, int L, int P,
-                                                       int LPpad, int Dpad, uint8_t *__restrict__ ids)
+// bf16 terms of one lane's 8 elements of a row (zeros past d or the rows)
+template <typename IO, int NKB>
+__device__ __forceinline__ void ids_row_terms(Rsrc rx, int d, int rr, int g,
+                                              bf16x8 (&xt)[NKB][XTerms<IO>::N])
 {
-    __shared__ uint32_t mask[HARD_ROWS][HARD_MAXW + 1];
-    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    const int64_t r0 = (int64_t)blockIdx.x * HARD_ROWS;
-    const int64_t row = r0 + w * 16 + c16;
-    const int nkb = Dpad / 32, nht = LPpad / 16, nterm = LPpad * Dpad;
-    constexpr int XT = XTerms<IO>::N;
-    // this lane's row pieces: dims 32 kb + 8 g .. + 8 (zeros past d or past the rows)
-    const Rsrc rx = make_rsrc(X + r0 * d, (int)(min<int64_t>(HARD_ROWS, rows - r0) * d * sizeof(IO)));
-    bf16x8 xt[4][XT];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        if (kb >= nkb) break;
+    for (int kb = 0; kb < NKB; ++kb) {
         const int col = kb * 32 + 8 * g;
-        const int off = col < d ? (int)(((w * 16 + c16) * d + col) * sizeof(IO)) : OOB;
+        const int off = col < d ? (int)((rr * d + col) * sizeof(IO)) : OOB;
         if constexpr (sizeof(IO) == 2) {
             XTerms<IO>::split(bld128(rx, off), xt[kb]);
         } else {
             // (the whole vector is reinterpreted: a bit cast of one element of
-            // the loaded vector was compiled as a read of its first element)
+            // the loaded vector was compiled as a read of its first one)
             const floatx4 a = __builtin_bit_cast(floatx4, bld128(rx, off));
             const floatx4 b = __builtin_bit_cast(floatx4, bld128(rx, col < d ? off + 16 : OOB));
             float x[8];
@@ -122,43 +116,87 @@ __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X,
             XTerms<IO>::split(x, xt[kb]);
         }
     }
+}
+
+template <typename IO, int NKB>
+__global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X, int64_t rows, int d,
+                                                       const bf16 *__restrict__ wsp, int L, int P,
+                                                       int LPpad, int Dpad, uint8_t *__restrict__ ids)
+{
+    constexpr int XT = XTerms<IO>::N, NRT = IDS_ROWS / 16;
+    __shared__ uint32_t mask[IDS_ROWS][HARD_MAXW + 1];
+    const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
+    const int64_t r0 = (int64_t)blockIdx.x * IDS_ROWS;
+    const int nv = (int)min<int64_t>(IDS_ROWS, rows - r0);
+    const int nht = LPpad / 16, nterm = LPpad * Dpad;
+    const Rsrc rx = make_rsrc(X + r0 * d, (int)(nv * d * sizeof(IO)));
     // pairs of hyperplane tiles make one 32-bit word: lane group g holds the
-    // nibbles at bits 4 g (tile 2 j) and 16 + 4 g (tile 2 j + 1)
-    for (int wd = 0; wd < (nht + 1) / 2; ++wd) {
-        uint32_t word = 0;
+    // nibbles at bits 4 g (tile 2 wd) and 16 + 4 g (tile 2 wd + 1)
+    for (int wd = w; wd < (nht + 1) / 2; wd += 4) {
+        bf16x8 wa[2][NKB][3];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const int ht = 2 * wd + h2;
-            if (ht >= nht) break;
-            floatx4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb < nkb; ++kb) {
-                const int hp = ht * 16 + c16, col = kb * 32 + 8 * g;
+            const int ht = min(2 * wd + h2, nht - 1);  // (a missing second tile is not used)
 #pragma unroll
-                for (int t = 0; t < 3; ++t) {
-                    const bf16x8 wa = *reinterpret_cast<const bf16x8 *>(wsp + t * nterm + hp * Dpad + col);
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                    for (int s = 0; s < XT; ++s) mma32(u, wa, xt[kb][s]);
-                }
-            }
-            // u[r]: hyperplane 16 ht + 4 g + r of row c16; u = 0 counts as >= 0
-            uint32_t nib = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) nib |= (u[r] >= 0.f ? 1u : 0u) << r;
-            word |= nib << (16 * h2 + 4 * g);
+                for (int t = 0; t < 3; ++t)
+                    wa[h2][kb][t] = *reinterpret_cast<const bf16x8 *>(wsp + t * nterm + (ht * 16 + c16) * Dpad +
+                                                                      kb * 32 + 8 * g);
         }
-        word |= __shfl_xor(word, 16);
-        word |= __shfl_xor(word, 32);
-        if (g == 0) mask[w * 16 + c16][wd] = word;
+        const bool two = 2 * wd + 1 < nht;
+        bf16x8 xt[NKB][XT], xn[NKB][XT];
+        ids_row_terms<IO, NKB>(rx, d, c16, g, xt);
+#pragma unroll 1
+        for (int rt = 0; rt < NRT; ++rt) {
+            if (rt + 1 < NRT) ids_row_terms<IO, NKB>(rx, d, (rt + 1) * 16 + c16, g, xn);
+            uint32_t word = 0;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                if (h2 == 1 && !two) break;
+                floatx4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int t = 0; t < 3; ++t)
+#pragma unroll
+                        for (int s = 0; s < XT; ++s) mma32(u, wa[h2][kb][t], xt[kb][s]);
+                // u[r]: hyperplane 16 (2 wd + h2) + 4 g + r of row c16; u = 0
+                // counts as >= 0
+                uint32_t nib = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) nib |= (u[r] >= 0.f ? 1u : 0u) << r;
+                word |= nib << (16 * h2 + 4 * g);
+            }
+            word |= __shfl_xor(word, 16);
+            word |= __shfl_xor(word, 32);
+            if (g == 0) mask[rt * 16 + c16][wd] = word;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int s = 0; s < XT; ++s) xt[kb][s] = xn[kb][s];
+        }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < HARD_ROWS * L; e += 256) {
-        const int rr = e / L, l = e % L;
-        if (r0 + rr >= rows) continue;
-        const int b0 = l * P;
-        // bits b0 .. b0 + P - 1 of the row's mask (P <= 8: at most two words)
-        const uint64_t two = (uint64_t)mask[rr][b0 >> 5] |
-                             ((b0 >> 5) + 1 < HARD_MAXW ? (uint64_t)mask[rr][(b0 >> 5) + 1] << 32 : 0);
-        ids[(r0 + rr) * L + l] = (uint8_t)((two >> (b0 & 31)) & ((1u << P) - 1));
+    // one thread per row: bits l P .. l P + P - 1 of its mask (P <= 8, so at
+    // most two words) are id l; ids are stored four to a dword when the rows'
+    // byte offsets allow it (L a multiple of 4), else byte by byte
+    const int rr = threadIdx.x;
+    const Rsrc ro = make_rsrc(ids + r0 * L, nv * L);
+    const uint32_t pm = (1u << P) - 1u;
+    auto id = [&](int l) -> uint32_t {
+        const int b0 = l * P, wi = b0 >> 5;
+        const uint32_t lo = mask[rr][wi], hi = wi + 1 < HARD_MAXW ? mask[rr][wi + 1] : 0u;
+        return __builtin_amdgcn_alignbit(hi, lo, b0 & 31) & pm;
+    };
+    if ((L & 3) == 0) {
+        for (int l = 0; l < L; l += 4) {
+            const uint32_t v = id(l) | id(l + 1) << 8 | id(l + 2) << 16 | id(l + 3) << 24;
+            __builtin_amdgcn_raw_buffer_store_b32(v, ro, rr < nv ? rr * L + l : OOB, 0, 0);
+        }
+    } else {
+        for (int l = 0; l < L; ++l)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)id(l), ro, rr < nv ? rr * L + l : OOB, 0, 0);
     }
 }
 
@@ -172,8 +210,11 @@ namespace race {
 // waves of 4 tables each, chunks of 32 tokens.  A wave keeps the value sums
 // of its 4 tables as 4 MFMA tiles of 16 buckets x 64 value columns (fp32);
 // the one-hot operands built from the ids make every product 0 or a value,
-// exact.  Counts are int32 in LDS, [table][16 buckets]: added per key, and
-// gathered per query, exactly.
+// exact.  Counts are integers: the 4 tables x 16 buckets of a wave are one
+// per lane, so each lane keeps its bucket's count in a register and adds the
+// number of the chunk's keys in that bucket (the population count of the
+// bucket's token mask); a query reads its buckets' counts from the wave's
+// copy in LDS and adds the keys of its own chunk that come before it.
 constexpr int HNT = 4;  // value column tiles (64 columns)
 
 // bf16 one-hot quadruples: entry n holds 1.0 in slot i when bit i of n is set
@@ -211,11 +252,16 @@ __device__ __forceinline__ Rsrc id_res(const uint8_t *seg_ids, int L, const Chun
 {
     return make_rsrc(seg_ids + (int64_t)c.tok0 * L, (c.nv * L + 3) & ~3);
 }
-// the chunk's 32 L id bytes as dwords into LDS (zeros past the valid rows)
-template <int NTHR>
-__device__ __forceinline__ void stage_ids(Rsrc r, int L, uint32_t *dst)
+// the chunk's 32 L id bytes as dwords: thread e < 8 L loads dword e (zeros
+// past the valid rows), and later stores it to LDS.  Every launch has at
+// least 8 L threads (2 waves per 8 tables).
+__device__ __forceinline__ uint32_t load_ids(Rsrc r, int L)
 {
-    for (int e = threadIdx.x; e < 8 * L; e += NTHR) dst[e] = __builtin_amdgcn_raw_buffer_load_b32(r, 4 * e, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)threadIdx.x < 8 * L ? 4 * (int)threadIdx.x : OOB, 0, 0);
+}
+__device__ __forceinline__ void store_ids(uint32_t v, int L, uint32_t *dst)
+{
+    if ((int)threadIdx.x < 8 * L) dst[threadIdx.x] = v;
 }
 __device__ __forceinline__ uint32_t id_at(const uint32_t *ids, int L, int tok, int l)
 {
@@ -223,8 +269,26 @@ __device__ __forceinline__ uint32_t id_at(const uint32_t *ids, int L, int tok, i
     return (ids[b >> 2] >> (8 * (b & 3))) & 0xffu;
 }
 
+// The bucket token masks of this wave's tables for one chunk: bm[16 s + r]
+// bit j is set when key j of the chunk falls in bucket r of table 4 w + s.
+// Only the wave itself reads them, so no workgroup barrier is needed: its
+// LDS operations complete in program order.
+__device__ __forceinline__ void wave_masks(uint32_t *bm, const uint32_t *kid, int L, int nv, int w)
+{
+    const int lane = lane_id();
+    bm[lane] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        // lanes take tokens, the two halves of the wave two tables
+        const int j = lane & 31, s = (lane >> 5) + 2 * it, T = 4 * w + s;
+        if (T < L && j < nv) atomicOr(&bm[s * 16 + id_at(kid, L, j, T)], 1u << j);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 // hard_sum_kernel: per (head, segment) the value sums B[l][r][:] (FxC
-// tiles, stored as the soft kernels' state blocks) and int32 counts
+// tiles, stored as the soft kernels' state blocks) and the int32 counts
 // A[l][r] of the segment's keys.
 template <int NW, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void hard_sum_kernel(
@@ -234,8 +298,7 @@ __global__ __launch_bounds__(NW * 64) void hard_sum_kernel(
     constexpr int NTHR = NW * 64;
     __shared__ __attribute__((aligned(16))) bf16 ycol[2][NCOL * YCS];
     __shared__ uint32_t ids[2][8 * 32];
-    __shared__ uint32_t bmask[2][32 * 16];
-    __shared__ int cnt[32 * 16];
+    __shared__ uint32_t bmw[NW][64];
     __shared__ uint32_t lut[32];
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
@@ -244,62 +307,59 @@ __global__ __launch_bounds__(NW * 64) void hard_sum_kernel(
     const int nch = (tend + WCT - 1) / WCT;
     ValSrc<IO> vh{V + row0 * D, nullptr, nullptr};
     const uint8_t *ids_seg = idk + row0 * L;
+    uint32_t *bm = bmw[w];
     stage_lut(lut);
-    for (int e = threadIdx.x; e < 32 * 16; e += NTHR) {
-        cnt[e] = 0;
-        bmask[0][e] = 0u;
-        bmask[1][e] = 0u;
-    }
-    ystage_zero_pad<NTHR>(ycol[0]);
-    ystage_zero_pad<NTHR>(ycol[1]);
     floatx4 acc[4][HNT];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int ct = 0; ct < HNT; ++ct) acc[s][ct] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t cnt = 0;  // keys in bucket (lane & 15) of table 4 w + lane / 16
     auto chunk = [&](int ci) -> Chunk {
         if (ci >= nch) return Chunk{0, 0};
         return Chunk{ci * WCT, min(WCT, tend - ci * WCT)};
     };
+    // chunk ci + 1 is loaded into registers while chunk ci is summed
     YStage<NTHR, false> ys;
-    __syncthreads();
+    uint32_t kid = 0;
+    if (nch > 0) {
+        kid = load_ids(id_res(ids_seg, L, chunk(0)), L);
+        ystage_load<NTHR, false, D>(yres<false, D>(vh, chunk(0)), ys);
+    }
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
-        const Chunk cc = chunk(ci);
-        // stage ids and [v | 1] of chunk ci; clear the masks of chunk ci + 1
-        stage_ids<NTHR>(id_res(ids_seg, L, cc), L, ids[b]);
-        ystage_load<NTHR, false, D>(yres<false, D>(vh, cc), ys);
+        const Chunk cc = chunk(ci), cn = chunk(ci + 1);
+        // stage ids and [v | 1] of chunk ci (buffers last read before the
+        // previous barrier), then start loading chunk ci + 1
+        store_ids(kid, L, ids[b]);
         ystage_store<NTHR, false, IO>(ys, cc.nv, ycol[b]);
-        __syncthreads();
-        // the other chunks' mask buffer was last read before this barrier
-        for (int e = threadIdx.x; e < 32 * 16; e += NTHR) bmask[b ^ 1][e] = 0u;
-        // bucket token masks and counts of the chunk's keys
-        for (int e = threadIdx.x; e < 32 * L; e += NTHR) {
-            const int j = e / L, l = e % L;
-            if (j < cc.nv) {
-                const uint32_t id = id_at(ids[b], L, j, l);
-                atomicOr(&bmask[b][l * 16 + id], 1u << j);
-                atomicAdd(&cnt[l * 16 + id], 1);
-            }
+        if (ci + 1 < nch) {
+            kid = load_ids(id_res(ids_seg, L, cn), L);
+            ystage_load<NTHR, false, D>(yres<false, D>(vh, cn), ys);
         }
         __syncthreads();
+        wave_masks(bm, ids[b], L, cc.nv, w);
+        cnt += __builtin_popcount(bm[lane]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int T = 4 * w + s;
-            const bf16x8 a = onehot_fm(lut, T < L ? bmask[b][T * 16 + c16] : 0u, g);
+            const bf16x8 a = onehot_fm(lut, T < L ? bm[s * 16 + c16] : 0u, g);
 #pragma unroll
             for (int ct = 0; ct < HNT; ++ct) mma32(acc[s][ct], a, ycol_frag(ycol[b], ct * 16 + c16));
         }
     }
-    const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 4 * HNT * 64 * 4);
+    const int64_t blk = bh * (nseg + 1) + sg;
+    float *vdst = st + blk * (int64_t)(NW * 4 * HNT * 64 * 4);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int ct = 0; ct < HNT; ++ct)
-            *reinterpret_cast<floatx4 *>(st + blk + (((w * 4 + s) * HNT + ct) * 64 + lane) * 4) = acc[s][ct];
-    __syncthreads();
-    int *cdst = cst + (bh * (nseg + 1) + sg) * (int64_t)(32 * 16);
-    for (int e = threadIdx.x; e < 32 * 16; e += NTHR) cdst[e] = e < L * 16 ? cnt[e] : 0;
+            *reinterpret_cast<floatx4 *>(vdst + (((w * 4 + s) * HNT + ct) * 64 + lane) * 4) = acc[s][ct];
+    // count block [32 tables][16 buckets]: this wave's 64, zeros past the
+    // waves' tables
+    int *cdst = cst + blk * (int64_t)(32 * 16);
+    cdst[w * 64 + lane] = (int)cnt;
+    for (int e = NW * 64 + (int)threadIdx.x; e < 32 * 16; e += NTHR) cdst[e] = 0;
 }
 
 // Scan of the int32 count blocks over segments (exclusive prefix, head
@@ -321,9 +381,10 @@ static __global__ __launch_bounds__(256) void hard_count_scan_kernel(int *__rest
 
 // hard_walk_kernel: o_i = sum_l B_l[r_l(q_i)] / sum_l A_l[r_l(q_i)] over the
 // keys j <= i (causal) or all keys, from the segment's prefix state (values:
-// fp32 tiles read as bf16 MFMA operands; counts: int32, exact), the chunks
-// before i in the segment, and the chunk's own keys j <= i.  den = the count
-// (as fp32) and, when count is not null, the count itself (int32).
+// fp32 tiles read as bf16 MFMA operands; counts: integers, exact), the
+// chunks before i in the segment, and the chunk's own keys j <= i.  den =
+// the count (as fp32) and, when count is not null, the count itself (int32).
+// Two barriers per chunk: after staging, and after the partial outputs.
 template <int NW, bool CAUSAL, typename IO, int D>
 __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
     const IO *__restrict__ V, const uint8_t *__restrict__ idq, const uint8_t *__restrict__ idk,
@@ -333,15 +394,14 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
 {
     constexpr int NTHR = NW * 64;
     constexpr int REDN = NW * 2 * HNT * 64 * 4;  // partial outputs of every wave
-    constexpr int REDM = NW * 2 * 64;            // and their intra-chunk counts
     __shared__ __attribute__((aligned(16))) bf16 ycol[2][CAUSAL ? NCOL * YCS : 8];
     __shared__ uint32_t qids[2][8 * 32];
     __shared__ uint32_t kids[2][CAUSAL ? 8 * 32 : 1];
-    __shared__ uint32_t bmask[2][CAUSAL ? 32 * 16 : 1];
-    __shared__ int cnt[2][32];     // per query: counts gathered from A
-    __shared__ int A[32 * 16];     // counts of the keys before the chunk
+    __shared__ uint32_t bmw[CAUSAL ? NW : 1][64];  // this chunk's bucket token masks, per wave
+    __shared__ uint32_t cntw[NW][64];              // counts of the keys before the chunk, per wave
     __shared__ uint32_t lut[32];
-    __shared__ __attribute__((aligned(16))) float red[REDN + REDM];
+    __shared__ __attribute__((aligned(16))) float red[REDN];
+    __shared__ uint32_t redm[NW][32];              // each wave's count of every query
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
@@ -352,15 +412,12 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
     IO *Os = Out + row0 * D;
     float *dens = den + row0;
     int *cnts = count ? count + row0 : nullptr;
+    uint32_t *bm = bmw[CAUSAL ? w : 0], *cw = cntw[w];
     stage_lut(lut);
     const int64_t sidx = bh * (nseg + 1) + (CAUSAL ? sg : nseg);
-    {
-        const int *src = cst + sidx * (int64_t)(32 * 16);
-        for (int e = threadIdx.x; e < 32 * 16; e += NTHR) A[e] = src[e];
-        for (int e = threadIdx.x; e < 2 * 32 * 16; e += NTHR)
-            if (CAUSAL) bmask[e >> 9][e & 511] = 0u;
-        if (threadIdx.x < 64) cnt[threadIdx.x >> 5][threadIdx.x & 31] = 0;
-    }
+    // counts before the segment (all keys: non-causal), one bucket per lane
+    uint32_t cnt = (uint32_t)cst[sidx * (int64_t)(32 * 16) + w * 64 + lane];
+    cw[lane] = cnt;
     if (CAUSAL) {
         ystage_zero_pad<NTHR>(ycol[0]);
         ystage_zero_pad<NTHR>(ycol[1]);
@@ -378,30 +435,60 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
         if (ci >= nch) return Chunk{0, 0};
         return Chunk{ci * WCT, min(WCT, tend - ci * WCT)};
     };
+    // chunk ci + 1 is loaded into registers while chunk ci is read out
     YStage<NTHR, false> ys;
-    __syncthreads();
+    uint32_t qid = 0, kid = 0;
+    if (nch > 0) {
+        qid = load_ids(id_res(q_seg, L, chunk(0)), L);
+        if (CAUSAL) {
+            kid = load_ids(id_res(k_seg, L, chunk(0)), L);
+            ystage_load<NTHR, false, D>(yres<false, D>(vh, chunk(0)), ys);
+        }
+    }
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
-        const Chunk cc = chunk(ci);
-        // stage ids (and keys' [v | 1]); clear the next chunk's masks and counts
-        stage_ids<NTHR>(id_res(q_seg, L, cc), L, qids[b]);
+        const Chunk cc = chunk(ci), cn = chunk(ci + 1);
+        // stage ids (and keys' [v | 1]) of chunk ci into buffers last read
+        // before the previous barrier, then start loading chunk ci + 1
+        store_ids(qid, L, qids[b]);
         if (CAUSAL) {
-            stage_ids<NTHR>(id_res(k_seg, L, cc), L, kids[b]);
-            ystage_load<NTHR, false, D>(yres<false, D>(vh, cc), ys);
+            store_ids(kid, L, kids[b]);
             ystage_store<NTHR, false, IO>(ys, cc.nv, ycol[b]);
-            for (int e = threadIdx.x; e < 32 * 16; e += NTHR) bmask[b ^ 1][e] = 0u;
         }
-        if (threadIdx.x < 32) cnt[b ^ 1][threadIdx.x] = 0;
-        __syncthreads();
-        // keys' bucket token masks; queries' counts of the keys before the chunk
-        for (int e = threadIdx.x; e < 32 * L; e += NTHR) {
-            const int j = e / L, l = e % L;
-            if (j < cc.nv) {
-                if (CAUSAL) atomicOr(&bmask[b][l * 16 + id_at(kids[b], L, j, l)], 1u << j);
-                atomicAdd(&cnt[b][j], A[l * 16 + id_at(qids[b], L, j, l)]);
+        if (ci + 1 < nch) {
+            qid = load_ids(id_res(q_seg, L, cn), L);
+            if (CAUSAL) {
+                kid = load_ids(id_res(k_seg, L, cn), L);
+                ystage_load<NTHR, false, D>(yres<false, D>(vh, cn), ys);
             }
         }
         __syncthreads();
+        if (CAUSAL) wave_masks(bm, kids[b], L, cc.nv, w);
+        {
+            // this wave's count of each query: its buckets' counts before the
+            // chunk, and (causal) the chunk's keys j <= i in them; lanes take
+            // tokens, the two halves of the wave two tables each
+            const int tok = lane & 31;
+            uint32_t m = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int s = 2 * (lane >> 5) + h, T = 4 * w + s;
+                if (T < L) {
+                    const uint32_t id = id_at(qids[b], L, tok, T);
+                    m += cw[s * 16 + id];
+                    if (CAUSAL) m += __builtin_popcount(bm[s * 16 + id] & ((2u << tok) - 1u));
+                }
+            }
+            m += __shfl_xor(m, 32);
+            if (lane < 32) redm[w][tok] = m;
+        }
+        if (CAUSAL) {
+            // the chunk's keys join the counts (after the reads above: this
+            // wave's LDS operations complete in order)
+            cnt += __builtin_popcount(bm[lane]);
+            __builtin_amdgcn_wave_barrier();
+            cw[lane] = cnt;
+        }
         // one-hot operands of this wave's tables 4w .. 4w + 3 (16: none)
         bf16x8 pr[2][2], pw[2][2], pfm[4];
 #pragma unroll
@@ -420,13 +507,12 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             }
         if (CAUSAL)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                pfm[s] = onehot_fm(lut, 4 * w + s < L ? bmask[b][(4 * w + s) * 16 + c16] : 0u, g);
-        floatx4 oacc[2][HNT + 1];
+            for (int s = 0; s < 4; ++s) pfm[s] = onehot_fm(lut, 4 * w + s < L ? bm[s * 16 + c16] : 0u, g);
+        floatx4 oacc[2][HNT];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int ct = 0; ct <= HNT; ++ct) oacc[tt][ct] = {0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < HNT; ++ct) oacc[tt][ct] = {0.f, 0.f, 0.f, 0.f};
         // the state of the keys before the chunk (value columns)
 #pragma unroll
         for (int ct = 0; ct < HNT; ++ct) {
@@ -457,38 +543,31 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             const bf16x8 kA1 = cat8(acc2bf4(sc[0]), z4);              // reader tile 0: writer tile 0
             const bf16x8 kA8 = cat8(acc2bf4(sc[1]), acc2bf4(sc[2]));  // reader tile 1: writer tiles 0, 1
 #pragma unroll
-            for (int ct = 0; ct <= HNT; ++ct) {
+            for (int ct = 0; ct < HNT; ++ct) {
                 const bf16x8 yb = ycol_frag(ycol[b], ct * 16 + c16);
                 mma32(oacc[0][ct], yb, kA1);
                 mma32(oacc[1][ct], yb, kA8);
-                if (ct < HNT)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
+                for (int s = 0; s < 4; ++s) mma32(acc[s][ct], pfm[s], yb);
             }
         }
-        // partial outputs of this wave: value tiles and the intra-chunk counts
-        // (count column 64: row 0 of column tile HNT, lanes 0 .. 15)
-        float *rn = red, *rm = red + REDN;
+        // partial outputs of this wave
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int ct = 0; ct < HNT; ++ct)
-                *reinterpret_cast<floatx4 *>(rn + (((w * 2 + tt) * HNT + ct) * 64 + lane) * 4) = oacc[tt][ct];
-            rm[(w * 2 + tt) * 64 + lane] = oacc[tt][HNT][0];
-        }
+                *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * HNT + ct) * 64 + lane) * 4) = oacc[tt][ct];
         __syncthreads();
         // outputs of the chunk: thread slot (token tile tt, column tile ct, lane)
         const Rsrc ro = row_res<D>(Os, cc);
         for (int sl = threadIdx.x; sl < 2 * HNT * 64; sl += NTHR) {
             const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63, tok = tt * 16 + (ln & 15);
-            floatx4 n = *reinterpret_cast<const floatx4 *>(rn + ((tt * HNT + ct) * 64 + ln) * 4);
-            float mi = rm[tt * 64 + (ln & 15)];
+            floatx4 n = *reinterpret_cast<const floatx4 *>(red + ((tt * HNT + ct) * 64 + ln) * 4);
+            uint32_t m = redm[0][tok];
             for (int ww = 1; ww < NW; ++ww) {
-                n += *reinterpret_cast<const floatx4 *>(rn + (((ww * 2 + tt) * HNT + ct) * 64 + ln) * 4);
-                mi += rm[(ww * 2 + tt) * 64 + (ln & 15)];
+                n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * HNT + ct) * 64 + ln) * 4);
+                m += redm[ww][tok];
             }
-            // the chunk's own collisions are at most 32 L: exact in fp32
-            const int m = cnt[b][tok] + (CAUSAL ? (int)mi : 0);
             // a query that meets no visible key in any table: an empty sum,
             // o = 0 (n is 0 too)
             const float inv = m > 0 ? 1.f / (float)m : 0.f;
@@ -498,17 +577,10 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             if (ct == 0 && ln < 16) {
                 bstf((float)m, make_rsrc(dens + cc.tok0, cc.nv * 4), tok * 4);
                 if (cnts)
-                    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)m, make_rsrc(cnts + cc.tok0, cc.nv * 4),
-                                                          tok * 4, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(m, make_rsrc(cnts + cc.tok0, cc.nv * 4), tok * 4,
+                                                          0, 0);
             }
         }
-        // the chunk's keys join the counts (read again after the next barrier)
-        if (CAUSAL)
-            for (int e = threadIdx.x; e < 32 * L; e += NTHR) {
-                const int j = e / L, l = e % L;
-                if (j < cc.nv) atomicAdd(&A[l * 16 + id_at(kids[b], L, j, l)], 1);
-            }
-        __syncthreads();
     }
 }
 

@@ -620,7 +620,9 @@ inline HardPlan hard_plan(const Plan &p)
 }
 inline bool hard_fused(const Plan &p, race_dtype_t dt)
 {
-    return (dt == RACE_BF16 || dt == RACE_F16) && p.L <= 32 && p.P <= 4 && (p.d == 64 || p.d == 32);
+    // (int32 counts: every count is at most N L)
+    return (dt == RACE_BF16 || dt == RACE_F16) && p.L <= 32 && p.P <= 4 && (p.d == 64 || p.d == 32) &&
+           (int64_t)p.N * p.L < ((int64_t)1 << 31);
 }
 void hard_forward_launch(const Plan &p, race_dtype_t dt, const void *Q, const void *K, const void *V,
                          const float *W, int causal, void *O, float *den, int *count, char *ws,

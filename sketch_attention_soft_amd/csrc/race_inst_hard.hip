@@ -5,6 +5,20 @@
 
 namespace race_host {
 
+template <typename IO>
+static void hard_ids_t(const IO *X, int64_t rows, int d, const bf16 *wsp, int L, int P, int LPpad,
+                       int Dpad, uint8_t *ids, hipStream_t s)
+{
+    constexpr int R = race::IDS_ROWS;
+    const dim3 grid((unsigned)((rows + R - 1) / R));
+    switch (Dpad / 32) {
+    case 1: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 1>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
+    case 2: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 2>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
+    case 3: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 3>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
+    default: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 4>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
+    }
+}
+
 void hard_ids_launch(const void *X, int64_t rows, int d, race_dtype_t dt, const float *W, int L,
                      int P, uint8_t *ids, char *ws, hipStream_t s)
 {
@@ -12,16 +26,13 @@ void hard_ids_launch(const void *X, int64_t rows, int d, race_dtype_t dt, const 
     bf16 *wsp = reinterpret_cast<bf16 *>(ws);
     hipLaunchKernelGGL(race::hard_wsplit_kernel, dim3((LPpad * Dpad + 255) / 256), dim3(256), 0, s, W,
                        L * P, d, LPpad, Dpad, wsp);
-    const dim3 grid((unsigned)((rows + race::HARD_ROWS - 1) / race::HARD_ROWS));
+    if (rows == 0) return;
     if (dt == RACE_BF16)
-        hipLaunchKernelGGL(race::hard_ids_kernel<bf16>, grid, dim3(256), 0, s,
-                           static_cast<const bf16 *>(X), rows, d, wsp, L, P, LPpad, Dpad, ids);
+        hard_ids_t(static_cast<const bf16 *>(X), rows, d, wsp, L, P, LPpad, Dpad, ids, s);
     else if (dt == RACE_F16)
-        hipLaunchKernelGGL(race::hard_ids_kernel<_Float16>, grid, dim3(256), 0, s,
-                           static_cast<const _Float16 *>(X), rows, d, wsp, L, P, LPpad, Dpad, ids);
+        hard_ids_t(static_cast<const _Float16 *>(X), rows, d, wsp, L, P, LPpad, Dpad, ids, s);
     else
-        hipLaunchKernelGGL(race::hard_ids_kernel<float>, grid, dim3(256), 0, s,
-                           static_cast<const float *>(X), rows, d, wsp, L, P, LPpad, Dpad, ids);
+        hard_ids_t(static_cast<const float *>(X), rows, d, wsp, L, P, LPpad, Dpad, ids, s);
 }
 
 template <typename T, int NW, int D>
