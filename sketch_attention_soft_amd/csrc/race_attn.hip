@@ -29,7 +29,7 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
     if (P > race::NP) return RACE_ERR_UNSUPPORTED;
-    if (L > 128 || (dt == RACE_F32 && L > 32)) return RACE_ERR_UNSUPPORTED;
+    if (L > 128) return RACE_ERR_UNSUPPORTED;
     // 16-bit rows with L > 32: fused passes of up to 32 tables, d = 64 only
     if (dt != RACE_F32 && L > 32 && d != race::HD) return RACE_ERR_UNSUPPORTED;
     // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32)
@@ -101,9 +101,10 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->dw_total = p->fused ? p->b_dw + align256((size_t)2 * p->BH * p->nseg * (2 * p->nw * 16) *
                                                 race::HD * sizeof(float))
                            : 0;
-    if (dt != RACE_F32 && L > 32) {
-        // fused passes over tables 0..31, 32..63, ... (split_passes): every
-        // pass's buffers, then the fp32 partial sums
+    if (L > 32) {
+        // passes over tables 0..31, 32..63, ... (split_passes; the fused
+        // kernels for 16-bit rows, the unfused ones for fp32): every pass's
+        // buffers, then the fp32 partial sums
         const size_t pv = align256((size_t)p->rows * race::HD * sizeof(float));
         const size_t pm = align256((size_t)p->rows * sizeof(float));
         p->split = true;
@@ -347,7 +348,7 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     Plan p;
     const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
-    if (for_backward == 2 && !p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
+    if (for_backward == 2 && (dt == RACE_F32 || (!p.fused && !p.split))) return RACE_ERR_UNSUPPORTED;
     if (for_backward == 3 && !p.fused) return RACE_ERR_UNSUPPORTED;
     if (for_backward < 0 || for_backward > 4) return RACE_ERR_SHAPE;
     *bytes = for_backward == 4   ? (hard_fused(p, dt) ? hard_plan(p).total : p.f_total)
@@ -391,14 +392,17 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
     p.lens.len = lens;
     p.lens.cu = cu;
     p.lens.T = T;
-    float *sv = p.fused || p.split ? static_cast<float *>(saved) : nullptr;
+    // (the saved state is the fused kernels'; fp32 rows recompute)
+    float *sv = (p.fused || p.split) && dt != RACE_F32 ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
     if (p.split && dt == RACE_BF16)
         split_forward<bf16>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
-    else if (p.split)
+    else if (p.split && dt == RACE_F16)
         split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
+    else if (p.split)
+        split_forward<float>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, nullptr, tr);
     else if (dt == RACE_BF16)
         dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else if (dt == RACE_F16)
@@ -422,7 +426,7 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
     if (cu && (st = check_packed(p, B, N, T)) != RACE_OK) return st;
-    if (dW && !p.fused && !p.split) return RACE_ERR_UNSUPPORTED;
+    if (dW && (dt == RACE_F32 || (!p.fused && !p.split))) return RACE_ERR_UNSUPPORTED;
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, dW ? p.dw_total : p.b_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
@@ -430,15 +434,18 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
     p.lens.len = lens;
     p.lens.cu = cu;
     p.lens.T = T;
-    const float *sv = p.fused || p.split ? static_cast<const float *>(saved) : nullptr;
+    const float *sv = (p.fused || p.split) && dt != RACE_F32 ? static_cast<const float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
     if (p.split && dt == RACE_BF16)
         split_backward<bf16>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
-    else if (p.split)
+    else if (p.split && dt == RACE_F16)
         split_backward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr,
                                  dW);
+    else if (p.split)
+        split_backward<float>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, nullptr,
+                              tr, nullptr);
     else if (dt == RACE_BF16)
         dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
     else if (dt == RACE_F16)
@@ -490,8 +497,10 @@ static race_status_t hard_impl(const void *Q, const void *K, const void *V, cons
         char *ws = static_cast<char *>(workspace);
         if (p.split && dt == RACE_BF16)
             split_forward<bf16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
-        else if (p.split)
+        else if (p.split && dt == RACE_F16)
             split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
+        else if (p.split)
+            split_forward<float>(p, B, H, chunk, dt, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
         else if (dt == RACE_BF16)
             dispatch_forward<bf16>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
         else if (dt == RACE_F16)

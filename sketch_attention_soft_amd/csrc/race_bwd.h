@@ -50,7 +50,8 @@ template <typename T, int NW, int CAUSAL, bool REVERSE, bool READER_D>
 __global__ __launch_bounds__(NW * 64) void dpsi_kernel(
     const T *__restrict__ X, const float *__restrict__ tr, const float *__restrict__ tw,
     ValSrc<T> vr_src, ValSrc<T> vw_src, const char *__restrict__ wt, int lp32, int64_t N, int L,
-    int seg, int64_t nseg, const float *__restrict__ st, T *__restrict__ dX, Lens ls)
+    int seg, int64_t nseg, const float *__restrict__ st, T *__restrict__ dX, Lens ls,
+    Part prt = Part{nullptr, nullptr}, int pmode = PART_NONE)
 {
     constexpr int F = NW * FPW;
     constexpr int TS = 2 * NP;
@@ -200,6 +201,21 @@ __global__ __launch_bounds__(NW * 64) void dpsi_kernel(
                 for (int c = 0; c < 4; ++c) {
                     x[c] = to_f32(Xh[tok * HD + part * 4 + c]);
                     dh[c] = dxh[i * HD + part * 4 + c];
+                }
+            }
+            // table passes (L > 32): dx_hat of the tables so far in fp32
+            // partial rows; every pass but the last stores the sum and stops
+            // before the normalisation backward (uniform per launch)
+            if (pmode != PART_NONE) {
+                float *pr = prt.v + (bh * N + tok) * HD + part * 4;
+                if (ok && pmode != PART_OUT)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dh[c] += pr[c];
+                if (pmode != PART_IN) {
+                    if (ok)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) pr[c] = dh[c];
+                    continue;
                 }
             }
             float ss = 0.f, dot = 0.f;

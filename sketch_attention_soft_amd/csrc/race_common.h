@@ -192,6 +192,19 @@ __device__ __forceinline__ int64_t row_base(const Lens &ls, int64_t bh, int64_t 
     return bh * N;
 }
 
+// Tables in passes of at most 32 (L > 32: tables 0..31, 32..63, ...).  The
+// outputs are sums over tables before the last, nonlinear step, so the first
+// pass stores its sums in fp32 (PART_OUT), the middle ones add theirs to the
+// stored sums (PART_MID) and the last adds the stored sums to its own
+// (PART_IN): the readout's n and m before o = n / m, dV, and dx_hat before
+// the normalisation backward.  Partial rows are [token][64] fp32 (and m
+// [token]).
+constexpr int PART_NONE = 0, PART_OUT = 1, PART_IN = 2, PART_MID = 3;
+struct Part {
+    float *v;  // [rows][64]
+    float *m;  // [rows] (readout denominators) or null
+};
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

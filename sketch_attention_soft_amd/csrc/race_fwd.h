@@ -411,7 +411,7 @@ template <typename T, int NW, bool CAUSAL, bool BWD>
 __global__ __launch_bounds__(NW * 64) void readout_kernel(
     const float *__restrict__ tr, const float *__restrict__ tw, int ts, ValSrc<T> vs, int64_t N,
     int L, int seg, int64_t nseg, const float *__restrict__ st, T *__restrict__ Out,
-    float *__restrict__ den, Lens ls)
+    float *__restrict__ den, Lens ls, Part part = Part{nullptr, nullptr}, int pmode = PART_NONE)
 {
     constexpr int F = NW * FPW;
     __shared__ __attribute__((aligned(16))) T pr[CH * F];
@@ -420,6 +420,7 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(
     __shared__ __attribute__((aligned(16))) float scp[CAUSAL ? NW : 1][CH * CH];
     __shared__ __attribute__((aligned(16))) T abuf[CAUSAL ? CH * CH : 8];
     __shared__ __attribute__((aligned(16))) float red[NW][CH * NCOL];
+    __shared__ float mrow[CH];  // table passes: each row's denominator, partial sums included
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
@@ -503,6 +504,25 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) red[w][(g * 4 + r) * NCOL + nt * 16 + c16] = oacc[nt][r];
         __syncthreads();
+        // table passes (L > 32): n (and m) of the tables so far are added
+        // from fp32 partial rows [rows][64] (and [rows]); the first pass
+        // stores its sums there, middle passes add theirs, the last one adds
+        // the stored sums and writes the outputs
+        float *pv = pmode != PART_NONE ? part.v + bh * N * HD : nullptr;
+        if (!BWD && pmode != PART_NONE) {
+            // each row's m once, before any thread updates the stored one
+            if (threadIdx.x < CH && tok0 + (int64_t)threadIdx.x < t_end) {
+                const int64_t tok = tok0 + threadIdx.x;
+                float m = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) m += red[ww][threadIdx.x * NCOL + HD];
+                float *pm = part.m + bh * N;
+                if (pmode != PART_OUT) m += pm[tok];
+                if (pmode != PART_IN) pm[tok] = m;
+                mrow[threadIdx.x] = m;
+            }
+            __syncthreads();
+        }
         for (int e = threadIdx.x; e < CH * HD; e += NW * 64) {
             const int i = e / HD, c = e % HD;
             const int64_t tok = tok0 + i;
@@ -510,12 +530,23 @@ __global__ __launch_bounds__(NW * 64) void readout_kernel(
                 float n = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) n += red[ww][i * NCOL + c];
+                if (pmode != PART_NONE) {
+                    if (pmode != PART_OUT) n += pv[tok * HD + c];
+                    if (pmode != PART_IN) {
+                        pv[tok * HD + c] = n;
+                        continue;
+                    }
+                }
                 if (BWD) {
                     Outh[tok * HD + c] = from_f32<T>(n);
                 } else {
                     float m = 0.f;
+                    if (pmode == PART_NONE) {
 #pragma unroll
-                    for (int ww = 0; ww < NW; ++ww) m += red[ww][i * NCOL + HD];
+                        for (int ww = 0; ww < NW; ++ww) m += red[ww][i * NCOL + HD];
+                    } else {
+                        m = mrow[i];
+                    }
                     // m = 0 only under hard hashing (no colliding key): o = 0
                     Outh[tok * HD + c] = from_f32<T>(m != 0.f ? n / m : 0.f);
                     if (c == 0) denh[tok] = m;

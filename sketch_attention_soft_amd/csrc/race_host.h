@@ -257,10 +257,10 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
     launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
     if (causal)
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, true, false>), nblk, bw, tq, tk,
-               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens);
+               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens, p.part_o, p.part_mode);
     else
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, false, false>), nblk, bw, tq, tk,
-               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens);
+               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens, p.part_o, p.part_mode);
     }
 }
 
@@ -344,13 +344,13 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
     // dQ: readers Q (values D), writers K (values [v|1]), token order
     LAUNCH(tr, "dpsi_q", (race::dpsi_kernel<T, NW, CAUSAL, false, true>), nblk, bw, Q, tq, tk, vd,
-           vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ, p.lens);
+           vv, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sS, dQ, p.lens, p.part_dq, p.part_mode);
     // dK: readers K (values [v|1]), writers Q (values D), reverse order
     LAUNCH(tr, "dpsi_k", (race::dpsi_kernel<T, NW, CAUSAL, true, false>), nblk, bw, K, tk, tq, vv,
-           vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK, p.lens);
+           vd, wt, lp32, p.N, p.L, (int)p.seg, p.nseg, sGt, dK, p.lens, p.part_dk, p.part_mode);
     // dV: keys read the FxC gradient state, reverse order
     LAUNCH(tr, "readout_dv", (race::readout_kernel<T, NW, CAUSAL != 0, true>), nblk, bw, tk, tq,
-           ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr, p.lens);
+           ts, vd, p.N, p.L, (int)p.seg, p.nseg, sG, dV, nullptr, p.lens, p.part_dv, p.part_mode);
     }
 }
 
@@ -663,11 +663,13 @@ RACE_FWD_INST(extern, _Float16);
 RACE_FWD_INST(extern, float);
 RACE_SPLIT_FWD_INST(extern, bf16);
 RACE_SPLIT_FWD_INST(extern, _Float16);
+RACE_SPLIT_FWD_INST(extern, float);
 RACE_BWD_INST(extern, bf16);
 RACE_BWD_INST(extern, _Float16);
 RACE_BWD_INST(extern, float);
 RACE_SPLIT_BWD_INST(extern, bf16);
 RACE_SPLIT_BWD_INST(extern, _Float16);
+RACE_SPLIT_BWD_INST(extern, float);
 RACE_STATE_ADD_INST(extern, bf16);
 RACE_STATE_ADD_INST(extern, _Float16);
 RACE_STREAM_INST(extern, bf16, race::SM_ADD);

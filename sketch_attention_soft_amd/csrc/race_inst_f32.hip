@@ -7,5 +7,7 @@ namespace race_host {
 
 RACE_FWD_INST(, float);
 RACE_BWD_INST(, float);
+RACE_SPLIT_FWD_INST(, float);
+RACE_SPLIT_BWD_INST(, float);
 
 }  // namespace race_host

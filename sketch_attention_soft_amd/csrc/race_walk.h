@@ -197,18 +197,6 @@ __device__ __forceinline__ void for_chunks2(int n, F &&body)
         if (ci + 1 < n) body(ci + 1, Par<1>{});
     }
 }
-// Tables in passes of at most 32 (L > 32: tables 0..31, 32..63, ...).  The
-// outputs are sums over tables before the last, nonlinear step, so the first
-// pass stores its sums in fp32 (PART_OUT), the middle ones add theirs to the
-// stored sums (PART_MID) and the last adds the stored sums to its own
-// (PART_IN): the readout's n and m before o = n / m, dV, and dx_hat before
-// the normalisation backward.  Partial rows are [token][64] fp32 (and m
-// [token]).
-constexpr int PART_NONE = 0, PART_OUT = 1, PART_IN = 2, PART_MID = 3;
-struct Part {
-    float *v;  // [rows][64]
-    float *m;  // [rows] (readout denominators) or null
-};
 
 // rows of a [token][D] array of 16-bit elements (D = d: 64, or 32 staged
 // into the 64 columns of the kernels with zeros past column D)

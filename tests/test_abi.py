@@ -94,8 +94,9 @@ def test_workspace_sizes(lib):
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
     (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
     (dict(d=32, L=33), E_UNSUP), (dict(P=5), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
-    (dict(P=0), E_SHAPE), (dict(L=129), E_UNSUP), (dict(L=65, dt=F32), E_UNSUP),
-    (dict(L=33, dt=F32), E_UNSUP), (dict(d=32, L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
+    (dict(P=0), E_SHAPE), (dict(L=129), E_UNSUP), (dict(L=129, dt=F32), E_UNSUP),
+    (dict(L=33, dt=F32, bwd=2), E_UNSUP), (dict(L=8, dt=F32, bwd=2), E_UNSUP),
+    (dict(d=32, L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
     (dict(chunk=17), E_CHUNK), (dict(chunk=-16), E_CHUNK),
 ])
 def test_workspace_validation(lib, kw, code):
@@ -113,6 +114,18 @@ def test_tables_in_passes(lib):
         st, b = ws_bytes(lib, L=L, N=5000)
         assert b > prev
         prev = b
+    # fp32 rows: passes of the unfused kernels, no saved state
+    prev = 0
+    for L in (32, 33, 64, 65, 128):
+        for bwd in (0, 1):
+            st, b = ws_bytes(lib, L=L, bwd=bwd, N=5000, dt=F32)
+            assert st == OK and b > 0, (L, bwd)
+        st, b = ws_bytes(lib, L=L, N=5000, dt=F32)
+        assert b > prev
+        prev = b
+        sz0 = ctypes.c_size_t(1)
+        assert lib.race_attn_saved_bytes(1, 1, 5000, 64, L, 4, 1, 0, F32, ctypes.byref(sz0)) == OK
+        assert sz0.value == 0
     # a saved state for every pass
     sz = ctypes.c_size_t(0)
     sizes = []

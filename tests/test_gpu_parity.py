@@ -36,8 +36,6 @@ def _ids(c):
 
 
 def _run(dtype, causal, B, H, N, L, tau, chunk, backward, saved=False):
-    if dtype == "f32" and L > 32:
-        pytest.skip("fp32 supports L <= 32")
     seed = 7 + N + 31 * L + (1 if causal else 0)
     x = I.make_inputs(B, H, N, 64, L, 4, dtype, seed, with_grad=backward)
     dx, hx = device_inputs(x, dtype), host_inputs(x, dtype)

@@ -1,14 +1,16 @@
-"""More than 32 tables on 16-bit rows: passes of the fused kernels over
-tables 0..31, 32..63, ... (up to L = 128, four passes), the first storing
-fp32 partial sums, the middle ones adding to them and the last adding them
-before the ratio, dV and the normalisation backward.
+"""More than 32 tables: passes over tables 0..31, 32..63, ... (up to
+L = 128, four passes) of the fused kernels (16-bit rows) or of the unfused
+fp32 kernels, the first storing fp32 partial sums, the middle ones adding to
+them and the last adding them before the ratio, dV and the normalisation
+backward.
 
 The readout and its gradients are sums over tables until those last steps
 (pages: "RACE Attention: A Strictly Linear-Time Attention for Long-Sequence
 Training", gist.science/zh/paper/2510.04008, technical summary §2.2: n and m
 sum the tables' bucket statistics), so splitting the tables changes only the
 order of the sums.  Bar: the parity bar of the storage type, against the
-fp64 oracle on the same inputs.
+fp64 oracle on the same inputs, per head (relative Frobenius) and per row
+(tests/gpu_util.row_errors).
 """
 import numpy as np
 import pytest
@@ -17,7 +19,8 @@ import torch
 import oracle
 from sketch_attention_soft_amd import binding
 from sketch_attention_soft_amd import inputs as I
-from tests.gpu_util import TOL, device_inputs, head_relf, host_inputs, to_host64
+from tests.gpu_util import (GRAD_FLOOR, ROW_FLOOR, ROW_TOL, TOL, device_inputs, head_relf,
+                            host_inputs, row_errors, row_report, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +65,85 @@ def test_split_tables(case, causal, saved):
         e = head_relf(g, ref[n], floor_ref=fr, floor=1.0 if N == 1 else 1e-3)
         print(f"  rel_{n}={e:.2e}")
         assert e <= TOL[dtype], (n, e)
+    _row_gate(got, ref, dtype, N, causal)
+
+
+def _row_gate(got, ref, dtype, N, causal):
+    """Per-row errors (dQ, dK: skipped at N = 1, where they vanish exactly;
+    causal dQ row 0 is exactly zero and measured on the head's scale)."""
+    for n in ("o", "dv") + (("dq", "dk") if N > 1 else ()):
+        e_row = row_errors(to_host64(got[n]), ref[n], GRAD_FLOOR if n in ("dq", "dk") else ROW_FLOOR,
+                           vanishing=(0,) if n == "dq" and causal else ())
+        print("  " + row_report(n, e_row))
+        assert e_row.max() <= ROW_TOL[dtype], (n, e_row.max())
+
+
+F32_CASES = [
+    # B, H, N, L, tau, chunk: two passes (the second full or of 8 tables),
+    # four passes (first, two middle, last), one token
+    (1, 2, 1000, 64, 1.0, 0),
+    (2, 1, 700, 40, 0.5, 64),
+    (1, 1, 1300, 128, 1.0, 256),
+    (1, 1, 1, 65, 1.0, 0),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "f32_B%dH%dN%dL%d_tau%g_ch%d" % c)
+def test_split_tables_f32(case, causal):
+    """fp32 rows with L > 32: passes of the unfused fp32 kernels, the fp32
+    bar (1e-4)."""
+    B, H, N, L, tau, chunk = case
+    x = I.make_inputs(B, H, N, 64, L, 4, "f32", 2300 + N + L + causal, with_grad=True)
+    dx, hx = device_inputs(x, "f32"), host_inputs(x, "f32")
+    print(f"[case] split f32 B={B} H={H} N={N} L={L} causal={causal}", flush=True)
+    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], tau, causal, chunk)
+    dq, dk, dv = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau,
+                                  causal, chunk)
+    torch.cuda.synchronize()
+    ref = dict(zip(("o", "den", "dq", "dk", "dv"),
+                   oracle.forward_backward(hx["q"], hx["k"], hx["v"], hx["do"], hx["W"], tau,
+                                           causal)))
+    got = {"o": o, "den": den, "dq": dq, "dk": dk, "dv": dv}
+    for n in got:
+        g = to_host64(got[n])
+        assert np.all(np.isfinite(g)), n
+        fr = ref["dv"] if n in ("dq", "dk") else None
+        e = head_relf(g, ref[n], floor_ref=fr, floor=1.0 if N == 1 else 1e-3)
+        print(f"  rel_{n}={e:.2e}")
+        assert e <= TOL["f32"], (n, e)
+    _row_gate(got, ref, "f32", N, causal)
+    with pytest.raises(binding.RaceError):  # no dW on fp32 rows
+        binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau, causal, chunk,
+                         dw=True)
+
+
+def test_split_f32_padded_and_hard():
+    """fp32, L = 64: a right-padded batch against the oracle on each sequence,
+    and the hard forward (t = +-1 on the unfused kernels) against the
+    oracle's hard mode."""
+    H, N, L, tau, lens = 1, 600, 64, 1.0, (600, 250)
+    B = len(lens)
+    x = I.make_inputs(B, H, N, 64, L, 4, "f32", 2395, with_grad=True)
+    dx, hx = device_inputs(x, "f32"), host_inputs(x, "f32")
+    print("[case] split f32 padded + hard", flush=True)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, den = binding.forward_padded(dx["q"], dx["k"], dx["v"], dx["W"], sl, tau, True)
+    dq, dk, dv = binding.backward_padded(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], sl,
+                                         tau, True)
+    oh, denh = binding.forward_hard(dx["q"], dx["k"], dx["v"], dx["W"], True)
+    torch.cuda.synchronize()
+    for b, n_b in enumerate(lens):
+        sub = {k_: hx[k_][b:b + 1, :, :n_b] for k_ in ("q", "k", "v", "do")}
+        ref = oracle.forward_backward(sub["q"], sub["k"], sub["v"], sub["do"], hx["W"], tau, True)
+        for t, r in zip((o, den, dq, dk, dv), ref):
+            assert head_relf(to_host64(t)[b:b + 1, :, :n_b], r) <= TOL["f32"]
+        assert not torch.any(o[b, :, n_b:])
+    ro, rden = oracle.forward(hx["q"], hx["k"], hx["v"], hx["W"], 1.0, True, hard=True)
+    d = to_host64(denh)
+    assert np.array_equal(d, np.round(d)) and np.mean(d == rden) >= 0.999
+    ok = d == rden
+    assert head_relf(np.where(ok[..., None], to_host64(oh), 0.0), np.where(ok[..., None], ro, 0.0)) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("L", [64, 100])
