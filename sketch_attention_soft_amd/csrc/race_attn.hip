@@ -54,10 +54,11 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     int64_t seg = chunk;
     if (seg == 0) {
         // one workgroup per compute unit (MI355X: 256 CUs; every segment
-        // kernel keeps one workgroup per CU resident), segments >= 64 tokens
+        // kernel keeps one workgroup per CU resident), segments >= 32 tokens
+        // (short sequences: more, shorter segments, for latency)
         const int64_t want = (p->rows + 255) / 256;
         seg = (want + 31) / 32 * 32;
-        if (seg < 64) seg = 64;
+        if (seg < 32) seg = 32;
     }
     if (seg > n16) seg = n16;
     seg = (seg + 31) / 32 * 32;  // whole 32-token sub-chunks per segment
