@@ -80,33 +80,35 @@ template <> struct XTerms<float> {
 };
 
 // hard_ids_kernel: ids[row][l] = sum_p [u_lp >= 0] 2^p, u = W x, for `rows`
-// rows of d elements (d a multiple of 8, at most 32 NKB).  A workgroup takes
-// 256 rows; wave w keeps the W terms of the hyperplane words w, w + 4, ...
-// (32 hyperplanes each) in registers and streams the block's 16 row tiles
-// through them: U^T tiles of 16 hyperplanes x 16 rows on MFMA (W terms x row
-// terms, every product exact), the next row tile loading while the current
-// one is multiplied.  The signs are gathered into a bit mask per row in LDS,
-// then one thread per row cuts the row's L ids out of its mask and stores
-// them.
+// rows of d elements (d a multiple of 8, at most 32 NKB).  Persistent: each
+// workgroup loops over blocks of ids_rows() rows (256, fewer for wide rows),
+// loading the next block into registers while the current one, staged in
+// LDS, is multiplied; wave w keeps the W terms of the hyperplane words w,
+// w + 4, ... (32 hyperplanes each) in registers and runs the block's row
+// tiles of 16 through them: U^T tiles of 16 hyperplanes x 16 rows on MFMA (W terms x row
+// terms, every product exact).  The signs are gathered into a bit mask per
+// row in LDS, then one thread per row cuts the row's L ids out of its mask
+// and stores them.
 constexpr int HARD_MAXW = 24;  // 32-bit mask words per row: L P <= 768
-constexpr int IDS_ROWS = 256;  // rows per workgroup (4 waves)
+template <typename IO, int NKB> constexpr int ids_rows()
+{
+    // at most 32 KB of staged rows per workgroup, whole row tiles of 16
+    return 32768 / (NKB * 32 * (int)sizeof(IO)) >= 256 ? 256 : 32768 / (NKB * 32 * (int)sizeof(IO)) / 16 * 16;
+}
 
-// bf16 terms of one lane's 8 elements of a row (zeros past d or the rows)
+// bf16 terms of one lane's 8 elements of a staged row
 template <typename IO, int NKB>
-__device__ __forceinline__ void ids_row_terms(Rsrc rx, int d, int rr, int g,
+__device__ __forceinline__ void ids_row_terms(const uint8_t *xs, int stride, int rr, int g,
                                               bf16x8 (&xt)[NKB][XTerms<IO>::N])
 {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-        const int col = kb * 32 + 8 * g;
-        const int off = col < d ? (int)((rr * d + col) * sizeof(IO)) : OOB;
+        const uint8_t *src = xs + rr * stride + (kb * 32 + 8 * g) * (int)sizeof(IO);
         if constexpr (sizeof(IO) == 2) {
-            XTerms<IO>::split(bld128(rx, off), xt[kb]);
+            XTerms<IO>::split(*reinterpret_cast<const u32x4 *>(src), xt[kb]);
         } else {
-            // (the whole vector is reinterpreted: a bit cast of one element of
-            // the loaded vector was compiled as a read of its first one)
-            const floatx4 a = __builtin_bit_cast(floatx4, bld128(rx, off));
-            const floatx4 b = __builtin_bit_cast(floatx4, bld128(rx, col < d ? off + 16 : OOB));
+            const floatx4 a = *reinterpret_cast<const floatx4 *>(src);
+            const floatx4 b = *reinterpret_cast<const floatx4 *>(src + 16);
             float x[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -123,17 +125,32 @@ __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X,
                                                        const bf16 *__restrict__ wsp, int L, int P,
                                                        int LPpad, int Dpad, uint8_t *__restrict__ ids)
 {
-    constexpr int XT = XTerms<IO>::N, NRT = IDS_ROWS / 16;
-    __shared__ uint32_t mask[IDS_ROWS][HARD_MAXW + 1];
+    constexpr int XT = XTerms<IO>::N, ROWS = ids_rows<IO, NKB>(), NRT = ROWS / 16;
+    constexpr int RB = NKB * 32 * (int)sizeof(IO);  // bytes of a staged row
+    constexpr int STRIDE = RB + 16;                 // (padding: conflict-free 16-byte reads)
+    constexpr int PIECES = ROWS * RB / 16, PER = (PIECES + 255) / 256;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[ROWS * STRIDE];
+    __shared__ uint32_t mask[ROWS][HARD_MAXW + 1];
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
-    const int64_t r0 = (int64_t)blockIdx.x * IDS_ROWS;
-    const int nv = (int)min<int64_t>(IDS_ROWS, rows - r0);
-    const int nht = LPpad / 16, nterm = LPpad * Dpad;
-    const Rsrc rx = make_rsrc(X + r0 * d, (int)(nv * d * sizeof(IO)));
-    // pairs of hyperplane tiles make one 32-bit word: lane group g holds the
-    // nibbles at bits 4 g (tile 2 wd) and 16 + 4 g (tile 2 wd + 1)
-    for (int wd = w; wd < (nht + 1) / 2; wd += 4) {
-        bf16x8 wa[2][NKB][3];
+    const int nht = LPpad / 16, nwd = (nht + 1) / 2, nterm = LPpad * Dpad;
+    const int64_t nblk = (rows + ROWS - 1) / ROWS;
+    // a block's rows into registers, every load in flight at once (zeros
+    // past d and past the rows); then into LDS
+    u32x4 v[PER];
+    auto load_block = [&](int64_t blk) {
+        const int64_t r0 = blk * ROWS;
+        const int nv = (int)min<int64_t>(ROWS, rows - r0);
+        const Rsrc rx = make_rsrc(X + r0 * d, (int)(nv * d * sizeof(IO)));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = (int)threadIdx.x + i * 256, rr = e / (RB / 16), pc = e % (RB / 16);
+            const int col = pc * 16 / (int)sizeof(IO);
+            v[i] = bld128(rx, e < PIECES && col < d ? (int)((rr * d + col) * sizeof(IO)) : OOB);
+        }
+    };
+    // the W terms of a hyperplane word: two tiles of 16 hyperplanes
+    bf16x8 wa[2][NKB][3];
+    auto load_w = [&](int wd) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int ht = min(2 * wd + h2, nht - 1);  // (a missing second tile is not used)
@@ -144,59 +161,79 @@ __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X,
                     wa[h2][kb][t] = *reinterpret_cast<const bf16x8 *>(wsp + t * nterm + (ht * 16 + c16) * Dpad +
                                                                       kb * 32 + 8 * g);
         }
-        const bool two = 2 * wd + 1 < nht;
-        bf16x8 xt[NKB][XT], xn[NKB][XT];
-        ids_row_terms<IO, NKB>(rx, d, c16, g, xt);
-#pragma unroll 1
-        for (int rt = 0; rt < NRT; ++rt) {
-            if (rt + 1 < NRT) ids_row_terms<IO, NKB>(rx, d, (rt + 1) * 16 + c16, g, xn);
-            uint32_t word = 0;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                if (h2 == 1 && !two) break;
-                floatx4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int t = 0; t < 3; ++t)
-#pragma unroll
-                        for (int s = 0; s < XT; ++s) mma32(u, wa[h2][kb][t], xt[kb][s]);
-                // u[r]: hyperplane 16 (2 wd + h2) + 4 g + r of row c16; u = 0
-                // counts as >= 0
-                uint32_t nib = 0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) nib |= (u[r] >= 0.f ? 1u : 0u) << r;
-                word |= nib << (16 * h2 + 4 * g);
-            }
-            word |= __shfl_xor(word, 16);
-            word |= __shfl_xor(word, 32);
-            if (g == 0) mask[rt * 16 + c16][wd] = word;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int s = 0; s < XT; ++s) xt[kb][s] = xn[kb][s];
-        }
-    }
-    __syncthreads();
-    // one thread per row: bits l P .. l P + P - 1 of its mask (P <= 8, so at
-    // most two words) are id l; ids are stored four to a dword when the rows'
-    // byte offsets allow it (L a multiple of 4), else byte by byte
-    const int rr = threadIdx.x;
-    const Rsrc ro = make_rsrc(ids + r0 * L, nv * L);
-    const uint32_t pm = (1u << P) - 1u;
-    auto id = [&](int l) -> uint32_t {
-        const int b0 = l * P, wi = b0 >> 5;
-        const uint32_t lo = mask[rr][wi], hi = wi + 1 < HARD_MAXW ? mask[rr][wi + 1] : 0u;
-        return __builtin_amdgcn_alignbit(hi, lo, b0 & 31) & pm;
     };
-    if ((L & 3) == 0) {
-        for (int l = 0; l < L; l += 4) {
-            const uint32_t v = id(l) | id(l + 1) << 8 | id(l + 2) << 16 | id(l + 3) << 24;
-            __builtin_amdgcn_raw_buffer_store_b32(v, ro, rr < nv ? rr * L + l : OOB, 0, 0);
+    // with at most 4 words (L P <= 128) each wave keeps its word's W terms
+    // for every block; otherwise it loads them per word and block
+    const bool resident = nwd <= 4;
+    if (resident && w < nwd) load_w(w);
+    if ((int64_t)blockIdx.x < nblk) load_block(blockIdx.x);
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int64_t r0 = blk * ROWS;
+        const int nv = (int)min<int64_t>(ROWS, rows - r0);
+        // the previous block's products and ids are done with xs and mask
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = (int)threadIdx.x + i * 256, rr = e / (RB / 16), pc = e % (RB / 16);
+            if (e < PIECES) *reinterpret_cast<u32x4 *>(xs + rr * STRIDE + pc * 16) = v[i];
         }
-    } else {
-        for (int l = 0; l < L; ++l)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)id(l), ro, rr < nv ? rr * L + l : OOB, 0, 0);
+        if (blk + gridDim.x < nblk) load_block(blk + gridDim.x);
+        __syncthreads();
+        // pairs of hyperplane tiles make one 32-bit word: lane group g holds
+        // the nibbles at bits 4 g (tile 2 wd) and 16 + 4 g (tile 2 wd + 1)
+        for (int wd = w; wd < nwd; wd += 4) {
+            if (!resident) load_w(wd);
+            const bool two = 2 * wd + 1 < nht;
+#pragma unroll 4
+            for (int rt = 0; rt < NRT; ++rt) {
+                bf16x8 xt[NKB][XT];
+                ids_row_terms<IO, NKB>(xs, STRIDE, rt * 16 + c16, g, xt);
+                uint32_t word = 0;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    if (h2 == 1 && !two) break;
+                    floatx4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int t = 0; t < 3; ++t)
+#pragma unroll
+                            for (int s = 0; s < XT; ++s) mma32(u, wa[h2][kb][t], xt[kb][s]);
+                    // u[r]: hyperplane 16 (2 wd + h2) + 4 g + r of row c16;
+                    // u = 0 counts as >= 0
+                    uint32_t nib = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) nib |= (u[r] >= 0.f ? 1u : 0u) << r;
+                    word |= nib << (16 * h2 + 4 * g);
+                }
+                word |= __shfl_xor(word, 16);
+                word |= __shfl_xor(word, 32);
+                if (g == 0) mask[rt * 16 + c16][wd] = word;
+            }
+        }
+        __syncthreads();
+        // one thread per row: bits l P .. l P + P - 1 of its mask (P <= 8, so
+        // at most two words) are id l; ids are stored four to a dword when the
+        // rows' byte offsets allow it (L a multiple of 4), else byte by byte
+        const int rr = threadIdx.x;
+        if (rr < ROWS) {
+            const Rsrc ro = make_rsrc(ids + r0 * L, nv * L);
+            const uint32_t pm = (1u << P) - 1u;
+            auto id = [&](int l) -> uint32_t {
+                const int b0 = l * P, wi = b0 >> 5;
+                const uint32_t lo = mask[rr][wi], hi = wi + 1 < HARD_MAXW ? mask[rr][wi + 1] : 0u;
+                return __builtin_amdgcn_alignbit(hi, lo, b0 & 31) & pm;
+            };
+            if ((L & 3) == 0) {
+                for (int l = 0; l < L; l += 4) {
+                    const uint32_t val = id(l) | id(l + 1) << 8 | id(l + 2) << 16 | id(l + 3) << 24;
+                    __builtin_amdgcn_raw_buffer_store_b32(val, ro, rr < nv ? rr * L + l : OOB, 0, 0);
+                }
+            } else {
+                for (int l = 0; l < L; ++l)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)id(l), ro, rr < nv ? rr * L + l : OOB, 0, 0);
+            }
+        }
     }
 }
 
@@ -263,11 +300,15 @@ __device__ __forceinline__ void store_ids(uint32_t v, int L, uint32_t *dst)
 {
     if ((int)threadIdx.x < 8 * L) dst[threadIdx.x] = v;
 }
-__device__ __forceinline__ uint32_t id_at(const uint32_t *ids, int L, int tok, int l)
+// ids of tables 4 w .. 4 w + 3 of one token (bytes 0..3; the bytes of tables
+// past L are not ids and must not be used): one funnel shift over the two
+// dwords that hold them (the id arrays in LDS carry one dword of padding)
+__device__ __forceinline__ uint32_t ids4_at(const uint32_t *ids, int L, int tok, int w)
 {
-    const int b = tok * L + l;
-    return (ids[b >> 2] >> (8 * (b & 3))) & 0xffu;
+    const int b = tok * L + 4 * w;
+    return __builtin_amdgcn_alignbit(ids[(b >> 2) + 1], ids[b >> 2], 8 * (b & 3));
 }
+__device__ __forceinline__ uint32_t byte_of(uint32_t v, int i) { return (v >> (8 * i)) & 0xffu; }
 
 // The bucket token masks of this wave's tables for one chunk: bm[16 s + r]
 // bit j is set when key j of the chunk falls in bucket r of table 4 w + s.
@@ -278,11 +319,13 @@ __device__ __forceinline__ void wave_masks(uint32_t *bm, const uint32_t *kid, in
     const int lane = lane_id();
     bm[lane] = 0u;
     __builtin_amdgcn_wave_barrier();
+    // lanes take tokens, the two halves of the wave two tables each
+    const int j = lane & 31;
+    const uint32_t k4 = ids4_at(kid, L, j, w);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        // lanes take tokens, the two halves of the wave two tables
-        const int j = lane & 31, s = (lane >> 5) + 2 * it, T = 4 * w + s;
-        if (T < L && j < nv) atomicOr(&bm[s * 16 + id_at(kid, L, j, T)], 1u << j);
+        const int s = (lane >> 5) + 2 * it, T = 4 * w + s;
+        if (T < L && j < nv) atomicOr(&bm[s * 16 + byte_of(k4, s)], 1u << j);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -297,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) void hard_sum_kernel(
 {
     constexpr int NTHR = NW * 64;
     __shared__ __attribute__((aligned(16))) bf16 ycol[2][NCOL * YCS];
-    __shared__ uint32_t ids[2][8 * 32];
+    __shared__ uint32_t ids[2][8 * 32 + 1];
     __shared__ uint32_t bmw[NW][64];
     __shared__ uint32_t lut[32];
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
@@ -371,7 +414,19 @@ static __global__ __launch_bounds__(256) void hard_count_scan_kernel(int *__rest
     if (e >= elems) return;
     int *p = cst + blockIdx.y * (nseg + 1) * (int64_t)elems + e;
     int run = 0;
-    for (int64_t g = 0; g < nseg; ++g) {
+    constexpr int U = 8;  // loads in flight per thread
+    int64_t g = 0;
+    for (; g + U <= nseg; g += U) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = p[(g + u) * elems];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            p[(g + u) * elems] = run;
+            run += v[u];
+        }
+    }
+    for (; g < nseg; ++g) {
         const int v = p[g * elems];
         p[g * elems] = run;
         run += v;
@@ -395,8 +450,8 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
     constexpr int NTHR = NW * 64;
     constexpr int REDN = NW * 2 * HNT * 64 * 4;  // partial outputs of every wave
     __shared__ __attribute__((aligned(16))) bf16 ycol[2][CAUSAL ? NCOL * YCS : 8];
-    __shared__ uint32_t qids[2][8 * 32];
-    __shared__ uint32_t kids[2][CAUSAL ? 8 * 32 : 1];
+    __shared__ uint32_t qids[2][8 * 32 + 1];
+    __shared__ uint32_t kids[2][CAUSAL ? 8 * 32 + 1 : 1];
     __shared__ uint32_t bmw[CAUSAL ? NW : 1][64];  // this chunk's bucket token masks, per wave
     __shared__ uint32_t cntw[NW][64];              // counts of the keys before the chunk, per wave
     __shared__ uint32_t lut[32];
@@ -469,12 +524,13 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             // chunk, and (causal) the chunk's keys j <= i in them; lanes take
             // tokens, the two halves of the wave two tables each
             const int tok = lane & 31;
+            const uint32_t q4 = ids4_at(qids[b], L, tok, w);
             uint32_t m = 0;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int s = 2 * (lane >> 5) + h, T = 4 * w + s;
                 if (T < L) {
-                    const uint32_t id = id_at(qids[b], L, tok, T);
+                    const uint32_t id = byte_of(q4, s);
                     m += cw[s * 16 + id];
                     if (CAUSAL) m += __builtin_popcount(bm[s * 16 + id] & ((2u << tok) - 1u));
                 }
@@ -492,19 +548,23 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
         // one-hot operands of this wave's tables 4w .. 4w + 3 (16: none)
         bf16x8 pr[2][2], pw[2][2], pfm[4];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
+            const int tok = 16 * tt + c16;
+            const uint32_t q4 = ids4_at(qids[b], L, tok, w);
+            const uint32_t k4 = CAUSAL ? ids4_at(kids[b], L, tok, w) : 0u;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int t0 = 4 * w + 2 * k, tok = 16 * tt + c16;
-                const uint32_t q0 = t0 < L ? id_at(qids[b], L, tok, t0) : 16u;
-                const uint32_t q1 = t0 + 1 < L ? id_at(qids[b], L, tok, t0 + 1) : 16u;
+                const int t0 = 4 * w + 2 * k;
+                const uint32_t q0 = t0 < L ? byte_of(q4, 2 * k) : 16u;
+                const uint32_t q1 = t0 + 1 < L ? byte_of(q4, 2 * k + 1) : 16u;
                 pr[tt][k] = onehot_tm(lut, q0, q1, g);
                 if (CAUSAL) {
-                    const uint32_t k0 = t0 < L ? id_at(kids[b], L, tok, t0) : 16u;
-                    const uint32_t k1 = t0 + 1 < L ? id_at(kids[b], L, tok, t0 + 1) : 16u;
+                    const uint32_t k0 = t0 < L ? byte_of(k4, 2 * k) : 16u;
+                    const uint32_t k1 = t0 + 1 < L ? byte_of(k4, 2 * k + 1) : 16u;
                     pw[tt][k] = onehot_tm(lut, k0, k1, g);
                 }
             }
+        }
         if (CAUSAL)
 #pragma unroll
             for (int s = 0; s < 4; ++s) pfm[s] = onehot_fm(lut, 4 * w + s < L ? bm[s * 16 + c16] : 0u, g);

@@ -1,21 +1,32 @@
 // race_inst_hard.hip -- launch sequences of the hard-hash kernels
 // (race_hard.h), compiled apart from the other race_inst_*.hip files so that
 // the library builds in parallel.
+#include <algorithm>
+
 #include "race_host.h"
 
 namespace race_host {
 
+template <typename IO, int NKB>
+static void hard_ids_nkb(const IO *X, int64_t rows, int d, const bf16 *wsp, int L, int P, int LPpad,
+                         int Dpad, uint8_t *ids, hipStream_t s)
+{
+    // persistent workgroups: two per compute unit (256 CUs), or one per block
+    constexpr int R = race::ids_rows<IO, NKB>();
+    const int64_t blocks = (rows + R - 1) / R;
+    const dim3 grid((unsigned)std::min<int64_t>(blocks, 512));
+    hipLaunchKernelGGL((race::hard_ids_kernel<IO, NKB>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad,
+                       Dpad, ids);
+}
 template <typename IO>
 static void hard_ids_t(const IO *X, int64_t rows, int d, const bf16 *wsp, int L, int P, int LPpad,
                        int Dpad, uint8_t *ids, hipStream_t s)
 {
-    constexpr int R = race::IDS_ROWS;
-    const dim3 grid((unsigned)((rows + R - 1) / R));
     switch (Dpad / 32) {
-    case 1: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 1>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
-    case 2: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 2>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
-    case 3: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 3>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
-    default: hipLaunchKernelGGL((race::hard_ids_kernel<IO, 4>), grid, dim3(256), 0, s, X, rows, d, wsp, L, P, LPpad, Dpad, ids); break;
+    case 1: hard_ids_nkb<IO, 1>(X, rows, d, wsp, L, P, LPpad, Dpad, ids, s); break;
+    case 2: hard_ids_nkb<IO, 2>(X, rows, d, wsp, L, P, LPpad, Dpad, ids, s); break;
+    case 3: hard_ids_nkb<IO, 3>(X, rows, d, wsp, L, P, LPpad, Dpad, ids, s); break;
+    default: hard_ids_nkb<IO, 4>(X, rows, d, wsp, L, P, LPpad, Dpad, ids, s); break;
     }
 }
 
