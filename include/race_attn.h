@@ -121,12 +121,15 @@ race_status_t race_attn_forward(const void *Q, const void *K, const void *V, con
  * or all keys; den_i = that count.  No tau.  Inference only: the hash has no
  * gradient.  A query that collides with no visible key in any table (the
  * sums are empty) gets den = 0 and o = 0.
- * RACE_BF16 / RACE_F16 rows with L <= 32, P <= 4, d = 32 or 64 run on the
- * bucket ids of race_attn_hash_ids (every sign decided on exact products):
+ * RACE_BF16 / RACE_F16 rows with d = 32 or 64 and L <= 32, P <= 4 (or, for
+ * P = 5 and 6, L 2^(P-4) <= 32: each table of 2^P buckets as 2^(P-4) tables
+ * of 16), with N L < 2^31, run on the bucket ids of race_attn_hash_ids (every
+ * sign decided on exact products):
  * int32 counts, kept and gathered exactly, and fp32 value sums (read as
  * bf16 matrix-core operands, the precision of the outputs); den is the count
- * (exact below 2^24).  Other shapes (fp32 rows, L > 32) run the chunked soft
- * kernels with t = +-1 (counts through the sums' fp32 and bf16 arithmetic).
+ * (exact below 2^24).  Other shapes with P <= 4 (fp32 rows, L > 32) run the
+ * chunked soft kernels with t = +-1 (counts through the sums' fp32 and bf16
+ * arithmetic); P = 5, 6 elsewhere, and P > 6, return RACE_ERR_UNSUPPORTED.
  * workspace: race_attn_workspace_bytes(..., for_backward = 4). */
 race_status_t race_attn_forward_hard(const void *Q, const void *K, const void *V,
                                      const float *W, int L, int P, int causal, int B, int H,

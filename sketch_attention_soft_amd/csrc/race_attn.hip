@@ -336,6 +336,29 @@ race_status_t stream_plan(int B, int H, int64_t N, int d, int L, int P, race_dty
     return RACE_OK;
 }
 
+// The hard forward's plan: P = 5, 6 run on the id path only, as L 2^(P-4)
+// virtual tables of 4 planes (16 buckets each) for the sum and walk kernels;
+// ids_path tells whether the id kernels run (else the soft kernels with
+// t = +-1 on the real tables).
+race_status_t hard_forward_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
+                                race_dtype_t dt, Plan *p, bool *ids_path)
+{
+    const int vs = P > race::NP && P <= 6 ? P - race::NP : 0;
+    if (vs) {
+        if (L < 1) return RACE_ERR_SHAPE;
+        if (L > 128) return RACE_ERR_UNSUPPORTED;
+        const race_status_t st = make_plan(B, H, N, d, L << vs, race::NP, chunk, dt, p);
+        if (st != RACE_OK) return st;
+        if (!hard_fused(*p, dt)) return RACE_ERR_UNSUPPORTED;
+        *ids_path = true;
+        return RACE_OK;
+    }
+    const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, p);
+    if (st != RACE_OK) return st;
+    *ids_path = hard_fused(*p, dt);
+    return RACE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -347,13 +370,19 @@ race_status_t race_attn_workspace_bytes(int B, int H, int64_t N, int d, int L, i
     (void)causal;
     if (!bytes) return RACE_ERR_NULL;
     Plan p;
+    if (for_backward == 4) {
+        bool ids_path = false;
+        const race_status_t st = hard_forward_plan(B, H, N, d, L, P, chunk, dt, &p, &ids_path);
+        if (st != RACE_OK) return st;
+        *bytes = ids_path ? hard_plan(p, L, P).total : p.f_total;
+        return RACE_OK;
+    }
     const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
     if (for_backward == 2 && (dt == RACE_F32 || (!p.fused && !p.split))) return RACE_ERR_UNSUPPORTED;
     if (for_backward == 3 && !p.fused) return RACE_ERR_UNSUPPORTED;
     if (for_backward < 0 || for_backward > 4) return RACE_ERR_SHAPE;
-    *bytes = for_backward == 4   ? (hard_fused(p, dt) ? hard_plan(p).total : p.f_total)
-             : for_backward == 3 ? p.st_bytes + p.scan_bytes
+    *bytes = for_backward == 3   ? p.st_bytes + p.scan_bytes
              : for_backward == 2 ? p.dw_total
              : for_backward      ? p.b_total
                                  : p.f_total;
@@ -487,9 +516,10 @@ static race_status_t hard_impl(const void *Q, const void *K, const void *V, cons
 {
     if (!Q || !K || !V || !W || !O || !den || !workspace) return RACE_ERR_NULL;
     Plan p;
-    race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
+    bool ids_path = false;
+    race_status_t st = hard_forward_plan(B, H, N, d, L, P, chunk, dt, &p, &ids_path);
     if (st != RACE_OK) return st;
-    if (!hard_fused(p, dt)) {
+    if (!ids_path) {
         // tau = 0 selects hard hashing in the soft kernels
         if (count) return RACE_ERR_UNSUPPORTED;
         if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
@@ -510,10 +540,10 @@ static race_status_t hard_impl(const void *Q, const void *K, const void *V, cons
             dispatch_forward<float>(p, Q, K, V, W, 0.f, causal, O, den, ws, nullptr, tr);
         return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
     }
-    const HardPlan h = hard_plan(p);
+    const HardPlan h = hard_plan(p, L, P);
     if (ws_bytes < h.total || ((uintptr_t)workspace & 255)) return RACE_ERR_WORKSPACE;
     (void)hipGetLastError();
-    hard_forward_launch(p, dt, Q, K, V, W, causal, O, den, count, static_cast<char *>(workspace),
+    hard_forward_launch(p, L, P, dt, Q, K, V, W, causal, O, den, count, static_cast<char *>(workspace),
                         static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? RACE_OK : RACE_ERR_HIP;
 }

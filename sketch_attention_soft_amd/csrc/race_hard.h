@@ -120,10 +120,15 @@ __device__ __forceinline__ void ids_row_terms(const uint8_t *xs, int stride, int
     }
 }
 
+// vshift > 0 (P = 5, 6 in the hard forward): each table of 2^P buckets is
+// written as 2^vshift virtual tables of 16 buckets: bucket r becomes bucket
+// r & 15 of virtual table r >> 4 and id 16 (none) of the others, L 2^vshift
+// ids per row.
 template <typename IO, int NKB>
 __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X, int64_t rows, int d,
                                                        const bf16 *__restrict__ wsp, int L, int P,
-                                                       int LPpad, int Dpad, uint8_t *__restrict__ ids)
+                                                       int LPpad, int Dpad, uint8_t *__restrict__ ids,
+                                                       int vshift)
 {
     constexpr int XT = XTerms<IO>::N, ROWS = ids_rows<IO, NKB>(), NRT = ROWS / 16;
     constexpr int RB = NKB * 32 * (int)sizeof(IO);  // bytes of a staged row
@@ -217,21 +222,24 @@ __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X,
         // rows' byte offsets allow it (L a multiple of 4), else byte by byte
         const int rr = threadIdx.x;
         if (rr < ROWS) {
-            const Rsrc ro = make_rsrc(ids + r0 * L, nv * L);
+            const int Lv = L << vshift;  // ids per row written
+            const Rsrc ro = make_rsrc(ids + r0 * Lv, nv * Lv);
             const uint32_t pm = (1u << P) - 1u;
-            auto id = [&](int l) -> uint32_t {
-                const int b0 = l * P, wi = b0 >> 5;
+            auto id = [&](int e) -> uint32_t {
+                const int l = e >> vshift, b0 = l * P, wi = b0 >> 5;
                 const uint32_t lo = mask[rr][wi], hi = wi + 1 < HARD_MAXW ? mask[rr][wi + 1] : 0u;
-                return __builtin_amdgcn_alignbit(hi, lo, b0 & 31) & pm;
+                const uint32_t r = __builtin_amdgcn_alignbit(hi, lo, b0 & 31) & pm;
+                if (vshift == 0) return r;
+                return (r >> 4) == (uint32_t)(e & ((1 << vshift) - 1)) ? (r & 15u) : 16u;
             };
-            if ((L & 3) == 0) {
-                for (int l = 0; l < L; l += 4) {
-                    const uint32_t val = id(l) | id(l + 1) << 8 | id(l + 2) << 16 | id(l + 3) << 24;
-                    __builtin_amdgcn_raw_buffer_store_b32(val, ro, rr < nv ? rr * L + l : OOB, 0, 0);
+            if ((Lv & 3) == 0) {
+                for (int e = 0; e < Lv; e += 4) {
+                    const uint32_t val = id(e) | id(e + 1) << 8 | id(e + 2) << 16 | id(e + 3) << 24;
+                    __builtin_amdgcn_raw_buffer_store_b32(val, ro, rr < nv ? rr * Lv + e : OOB, 0, 0);
                 }
             } else {
-                for (int l = 0; l < L; ++l)
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)id(l), ro, rr < nv ? rr * L + l : OOB, 0, 0);
+                for (int e = 0; e < Lv; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)id(e), ro, rr < nv ? rr * Lv + e : OOB, 0, 0);
             }
         }
     }
@@ -325,7 +333,8 @@ __device__ __forceinline__ void wave_masks(uint32_t *bm, const uint32_t *kid, in
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int s = (lane >> 5) + 2 * it, T = 4 * w + s;
-        if (T < L && j < nv) atomicOr(&bm[s * 16 + byte_of(k4, s)], 1u << j);
+        const uint32_t id = byte_of(k4, s);  // (16: no bucket in this virtual table)
+        if (T < L && j < nv && id < 16u) atomicOr(&bm[s * 16 + id], 1u << j);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -529,8 +538,8 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int s = 2 * (lane >> 5) + h, T = 4 * w + s;
-                if (T < L) {
-                    const uint32_t id = byte_of(q4, s);
+                const uint32_t id = byte_of(q4, s);
+                if (T < L && id < 16u) {
                     m += cw[s * 16 + id];
                     if (CAUSAL) m += __builtin_popcount(bm[s * 16 + id] & ((2u << tok) - 1u));
                 }

@@ -588,7 +588,7 @@ inline size_t hard_ids_ws(int L, int P, int d)
     return align256((size_t)3 * hard_lppad(L, P) * hard_dpad(d) * sizeof(bf16));
 }
 void hard_ids_launch(const void *X, int64_t rows, int d, race_dtype_t dt, const float *W, int L,
-                     int P, uint8_t *ids, char *ws, hipStream_t s);
+                     int P, uint8_t *ids, char *ws, hipStream_t s, int vshift = 0);
 
 // Hard forward on the bucket ids (16-bit rows, L <= 32, P <= 4, d = 32 or 64).
 // Workspace: ids of Q and K (padded), the W terms, value states, count
@@ -599,13 +599,16 @@ struct HardPlan {
     int hw;            // waves per workgroup (4 tables each)
     int64_t velems;    // floats of one value state block
 };
-inline HardPlan hard_plan(const Plan &p)
+// p: the plan of the tables the sum and walk kernels see (for P = 5, 6 the
+// L 2^(P-4) virtual tables of 4 planes); Lr, Pr: the real tables, whose W
+// the id kernel splits
+inline HardPlan hard_plan(const Plan &p, int Lr, int Pr)
 {
     HardPlan h;
     h.hw = 2 * p.nw;
     h.velems = (int64_t)h.hw * 4 * race::HNT * 64 * 4;
     h.ids_bytes = align256((size_t)p.rows * p.L + 4);
-    h.wsplit = hard_ids_ws(p.L, p.P, p.d);
+    h.wsplit = hard_ids_ws(Lr, Pr, p.d);
     h.vstate = align256((size_t)p.BH * (p.nseg + 1) * h.velems * sizeof(float));
     h.cstate = align256((size_t)p.BH * (p.nseg + 1) * 32 * 16 * sizeof(int));
     h.scan = align256((size_t)p.BH * p.scan_groups * h.velems * sizeof(float));
@@ -624,9 +627,9 @@ inline bool hard_fused(const Plan &p, race_dtype_t dt)
     return (dt == RACE_BF16 || dt == RACE_F16) && p.L <= 32 && p.P <= 4 && (p.d == 64 || p.d == 32) &&
            (int64_t)p.N * p.L < ((int64_t)1 << 31);
 }
-void hard_forward_launch(const Plan &p, race_dtype_t dt, const void *Q, const void *K, const void *V,
-                         const float *W, int causal, void *O, float *den, int *count, char *ws,
-                         hipStream_t s);
+void hard_forward_launch(const Plan &p, int Lr, int Pr, race_dtype_t dt, const void *Q, const void *K,
+                         const void *V, const float *W, int causal, void *O, float *den, int *count,
+                         char *ws, hipStream_t s);
 
 // Launch sequences instantiated in race_inst_*.hip (one file per row type
 // and direction), not in the files that call them.

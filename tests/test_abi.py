@@ -420,7 +420,11 @@ def test_forward_hard_validation(lib):
     fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, sz, vp]
     F = FAKE
     assert fn(None, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_NULL
-    assert fn(F, F, F, F, 8, 5, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
+    assert fn(F, F, F, F, 8, 7, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
+    assert fn(F, F, F, F, 17, 5, 1, 1, 1, 64, 64, BF16, 0, F, F, F, 1 << 30, None) == E_UNSUP
+    assert fn(F, F, F, F, 8, 5, 1, 1, 1, 64, 64, F32, 0, F, F, F, 1 << 30, None) == E_UNSUP
+    # P = 5 is accepted on 16-bit rows: refused here only for the workspace
+    assert fn(F, F, F, F, 8, 5, 1, 1, 1, 64, 64, BF16, 0, F, F, F * 16, 16, None) == E_WS
     assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 17, F, F, F, 1 << 30, None) == E_CHUNK
     assert fn(F, F, F, F, 8, 4, 1, 1, 1, 64, 64, BF16, 0, F, F, F * 16, 16, None) == E_WS
 
@@ -505,6 +509,13 @@ def test_hard_forward_workspace(lib):
     for (N, Lt) in ((4096, 8), (1 << 20, 32), (70000, 16)):
         assert ws(1, 2, N, 64, Lt, 4, 1, 0, BF16, 4, ctypes.byref(sz)) == OK
         assert sz.value >= 2 * 2 * N * Lt    # the two id arrays
+    # P = 5, 6 (16-bit rows, L 2^(P-4) <= 32): virtual tables of 16 buckets,
+    # one id byte per row and virtual table
+    for (Lt, P) in ((8, 5), (16, 5), (8, 6), (3, 6)):
+        assert ws(1, 2, 4096, 64, Lt, P, 1, 0, BF16, 4, ctypes.byref(sz)) == OK
+        assert sz.value >= 2 * 2 * 4096 * Lt * 2 ** (P - 4)
+    for (Lt, P, dt) in ((17, 5, BF16), (9, 6, BF16), (8, 5, F32), (8, 7, BF16)):
+        assert ws(1, 1, 4096, 64, Lt, P, 1, 0, dt, 4, ctypes.byref(sz)) == E_UNSUP
     # fp32 rows: the soft kernels with t = +-1, the forward's workspace
     assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 4, ctypes.byref(sz)) == OK
     hard = sz.value

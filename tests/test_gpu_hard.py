@@ -9,7 +9,8 @@ assignment, and the bucket sums are true counts.  The oracle's hard mode is
 pinned by the SimHash collision rate (P-4) and the convergence to angular
 attention (P-7).
 
-16-bit rows with L <= 32, P <= 4 run on integer bucket ids: every row's int32
+16-bit rows with L <= 32, P <= 4 (or L 2^(P-4) <= 32 for P = 5, 6: each table
+as 2^(P-4) virtual tables of 16 buckets) run on integer bucket ids: every row's int32
 count sum_l A_l[r_l(q_i)] must equal the oracle's exactly, except on rows that
 a bucket decided within fp32 rounding of zero can reach (a query id that
 differs from the oracle's, or, causal, any row after a key id that does);
@@ -36,6 +37,11 @@ ID_CASES = [
     ("bf16", 32, 1, 2, 1200, 32, 3, True, 64),
     ("f16", 32, 2, 1, 900, 12, 2, False, 0),
     ("bf16", 64, 1, 1, 70000, 32, 4, True, 0),
+    # P = 5, 6: each table as 2, 4 virtual tables of 16 buckets
+    ("bf16", 64, 1, 2, 1000, 8, 5, True, 0),
+    ("bf16", 64, 1, 1, 3000, 8, 6, True, 64),
+    ("f16", 32, 2, 1, 700, 3, 6, False, 0),
+    ("bf16", 64, 1, 1, 1500, 16, 5, True, 0),
 ]
 DENSE_CASES = [
     ("bf16", 1, 1, 1500, 64, True, 128),
