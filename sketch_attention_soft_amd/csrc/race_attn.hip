@@ -28,13 +28,20 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     if (B < 1 || H < 1 || N < 1 || d < 1 || L < 1 || P < 1) return RACE_ERR_SHAPE;
     if (N > kMaxN || (int64_t)B * H > 65535) return RACE_ERR_SHAPE;
     if (dt != RACE_F32 && dt != RACE_BF16 && dt != RACE_F16) return RACE_ERR_UNSUPPORTED;
-    if (P > race::NP) return RACE_ERR_UNSUPPORTED;
+    if (P > 6) return RACE_ERR_UNSUPPORTED;
     if (L > 128) return RACE_ERR_UNSUPPORTED;
-    // 16-bit rows with L > 32: fused passes of up to 32 tables, d = 64 only
-    if (dt != RACE_F32 && L > 32 && d != race::HD) return RACE_ERR_UNSUPPORTED;
-    // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32)
-    const bool fusable = dt != RACE_F32 && L <= 32;
-    if (d != race::HD && !(d == 32 && fusable)) return RACE_ERR_UNSUPPORTED;
+    // P = 5, 6: 2^(P-4) virtual tables of 4 planes per table, on the fused
+    // kernels (16-bit rows, d = 64)
+    const int vs = vt_shift(P), Lv = L << vs;
+    if (vs && (dt == RACE_F32 || d != race::HD)) return RACE_ERR_UNSUPPORTED;
+    // 16-bit rows with more than 32 (virtual) tables: fused passes of up to
+    // 32, d = 64 only
+    if (dt != RACE_F32 && Lv > 32 && d != race::HD) return RACE_ERR_UNSUPPORTED;
+    // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32);
+    // d = 128 in two passes of 64 value columns (16-bit rows, L <= 32, P <= 4)
+    const bool fusable = dt != RACE_F32 && Lv <= 32;
+    const bool wide = false && d == 2 * race::HD && fusable && P <= race::NP;
+    if (d != race::HD && !(d == 32 && fusable) && !wide) return RACE_ERR_UNSUPPORTED;
     if (P != race::NP && dt == RACE_F32) return RACE_ERR_UNSUPPORTED;
     if (chunk < 0 || chunk % race::CH != 0) return RACE_ERR_CHUNK;
     p->BH = (int64_t)B * H;
@@ -47,9 +54,9 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->N = N;
     p->rows = p->BH * N;
     p->L = L;
-    p->nw = L <= 8 ? 1 : L <= 16 ? 2 : L <= 32 ? 4 : 8;
+    p->nw = Lv <= 8 ? 1 : Lv <= 16 ? 2 : Lv <= 32 ? 4 : 8;
     p->F = p->nw * race::FPW;
-    p->LP = L * race::NP;
+    p->LP = Lv * race::NP;  // internal hyperplane rows
     const int64_t n16 = (N + 15) / 16 * 16;
     int64_t seg = chunk;
     if (seg == 0) {
@@ -65,7 +72,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->seg = seg;
     p->nseg = (N + seg - 1) / seg;
     if (p->BH * p->nseg > 0x7fffffffLL) return RACE_ERR_SHAPE;
-    p->fused = (dt == RACE_BF16 || dt == RACE_F16) && L <= 32;
+    p->wide = wide;
+    p->fused = (dt == RACE_BF16 || dt == RACE_F16) && Lv <= 32 && !wide;
     p->st_bytes = align256((size_t)p->BH * (p->nseg + 1) * p->F * race::NCOL * sizeof(float));
     // the fused kernels keep hash features on chip: no per-row buffers
     p->t_bytes = p->fused ? 0 : align256((size_t)p->rows * L * race::NP * sizeof(float));
@@ -78,7 +86,7 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->scan_bytes = align256((size_t)p->BH * p->scan_groups * p->F * race::NCOL * sizeof(float));
     p->hc_tiles = (N + 31) / 32 * 2;
     // per 16-token tile: 2 nw waves x 64 lanes x 4 fp16 values
-    p->hc_bytes = p->fused ? align256((size_t)p->BH * p->hc_tiles * (2 * p->nw) * 64 * 4 * 2) : 0;
+    p->hc_bytes = p->fused || wide ? align256((size_t)p->BH * p->hc_tiles * (2 * p->nw) * 64 * 4 * 2) : 0;
     p->f_tq = 0;
     p->f_tk = p->f_tq + p->t_bytes;
     p->f_st = p->f_tk + p->t_bytes;
@@ -102,19 +110,42 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->dw_total = p->fused ? p->b_dw + align256((size_t)2 * p->BH * p->nseg * (2 * p->nw * 16) *
                                                 race::HD * sizeof(float))
                            : 0;
-    if (L > 32) {
+    p->w_du = p->w_du_bytes = p->w_dm = 0;
+    if (wide) {
+        // forward: the segment states, the scan's totals, t of K and of Q;
+        // backward: key and gradient states, the scan's totals, t and dt/du
+        // of K and of Q, du of Q and K for both passes, the values' last
+        // column.  No saved state (the backward rehashes: one pass over the
+        // rows) and no dW.
+        p->w_du_bytes = align256((size_t)p->rows * (2 * p->nw) * 16 * sizeof(bf16));
+        p->f_st = 0;
+        p->f_scan = p->f_st + p->st_bytes;
+        p->f_hc = p->f_scan + p->scan_bytes;
+        p->f_total = p->f_hc + 2 * p->hc_bytes;
+        p->b_s = 0;
+        p->b_g = p->b_s + p->st_bytes;
+        p->b_scan = p->b_g + p->st_bytes;
+        p->b_hc = p->b_scan + p->scan_bytes;
+        p->w_du = p->b_hc + 4 * p->hc_bytes;
+        p->w_dm = p->w_du + 4 * p->w_du_bytes;
+        p->b_total = p->w_dm + align256((size_t)p->rows * sizeof(float));
+        p->dw_total = 0;
+        p->s_total = 0;
+    }
+    if (Lv > 32) {
         // passes over tables 0..31, 32..63, ... (split_passes; the fused
-        // kernels for 16-bit rows, the unfused ones for fp32): every pass's
-        // buffers, then the fp32 partial sums
+        // kernels for 16-bit rows, the unfused ones for fp32; 32 virtual
+        // tables for P = 5, 6): every pass's buffers, then the fp32 partial
+        // sums
         const size_t pv = align256((size_t)p->rows * race::HD * sizeof(float));
         const size_t pm = align256((size_t)p->rows * sizeof(float));
         p->split = true;
         p->f_total = pv + pm;
         p->b_total = p->dw_total = 3 * pv;
         p->s_total = 0;
-        for (int i = 0; i < split_passes(L); ++i) {
+        for (int i = 0; i < split_passes(L, P); ++i) {
             Plan a;
-            race_status_t st = make_plan(B, H, N, d, split_tables(L, i), P, chunk, dt, &a);
+            race_status_t st = make_plan(B, H, N, d, split_tables(L, P, i), P, chunk, dt, &a);
             if (st != RACE_OK) return st;
             p->f_total += a.f_total;
             p->b_total += a.b_total;
@@ -355,6 +386,7 @@ race_status_t hard_forward_plan(int B, int H, int64_t N, int d, int L, int P, in
     }
     const race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, p);
     if (st != RACE_OK) return st;
+    if (p->wide) return RACE_ERR_UNSUPPORTED;  // d = 128: the soft path only
     *ids_path = hard_fused(*p, dt);
     return RACE_OK;
 }
@@ -415,6 +447,7 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
     if (cu && (st = check_packed(p, B, N, T)) != RACE_OK) return st;
+    if (p.wide && (lens || cu)) return RACE_ERR_UNSUPPORTED;  // d = 128: dense heads only
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, p.f_total, workspace, ws_bytes)) != RACE_OK) return st;
     if ((st = check_trace(trace)) != RACE_OK) return st;
@@ -456,6 +489,7 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
     race_status_t st = make_plan(B, H, N, d, L, P, chunk, dt, &p);
     if (st != RACE_OK) return st;
     if (cu && (st = check_packed(p, B, N, T)) != RACE_OK) return st;
+    if (p.wide && (lens || cu)) return RACE_ERR_UNSUPPORTED;  // d = 128: dense heads only
     if (dW && (dt == RACE_F32 || (!p.fused && !p.split))) return RACE_ERR_UNSUPPORTED;
     if ((st = check_tau(tau)) != RACE_OK) return st;
     if ((st = check_ws(p, dW ? p.dw_total : p.b_total, workspace, ws_bytes)) != RACE_OK) return st;

@@ -46,6 +46,10 @@ template <typename T> struct ValSrc {
     const T *V;
     const T *O;
     const float *den;
+    // rows of 128 elements (two passes of 64 value columns): the gradient
+    // values' last column -(dO . o)/m over the whole row, precomputed, or null
+    // (the pass without the column: zero)
+    const float *dm = nullptr;
 };
 
 // ---------------------------------------------------------------------------

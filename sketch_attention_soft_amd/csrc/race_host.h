@@ -16,6 +16,7 @@
 #include "race_stream.h"
 #include "race_walk.h"
 #include "race_hard.h"
+#include "race_wide.h"
 
 namespace race_host {
 
@@ -64,6 +65,7 @@ struct Plan {
     int part_mode;     // PART_NONE, or this pass's PART_OUT / PART_IN
     race::Part part_o, part_dq, part_dk, part_dv;
     bool fused;        // bf16 and L <= 32: kernels hash their own rows
+    bool wide;         // d = 128 (16-bit rows, L <= 32, P <= 4): two passes of 64 value columns
     int64_t seg, nseg;
     size_t st_bytes;   // one set of segment states (nseg + 1 per head)
     size_t t_bytes;    // forward hash features of Q or K
@@ -80,6 +82,9 @@ struct Plan {
     size_t b_dw, dw_total;  // backward with dW (bf16, L <= 32): partials after b_total
     // saved buffer (bf16 path): key state, then t, dt/du' of K and of Q
     size_t s_hc, s_total;
+    // d = 128, backward: du of Q and K per pass (bf16 [rows][16 * waves]),
+    // the gradient values' last column (fp32 [rows])
+    size_t w_du, w_du_bytes, w_dm;
 };
 
 race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
@@ -126,12 +131,20 @@ void launch_sum(const Tracer &tr, const char *name, dim3 grid, const race::Squas
                 const race::HCache &cout, float *st)
 {
     if constexpr (sizeof(T) == 2) {
-        if (SRC == 1 || sq.deg >= 0)
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T, D>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st, p.lens);
-        else
-            LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T, D>), grid, dim3(NW * 64), X, vs,
-                   W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st, p.lens);
+        auto go = [&](auto pv_c) {
+            constexpr bool PV = decltype(pv_c)::value;
+            if (SRC == 1 || sq.deg >= 0)
+                LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, true, T, D, PV>), grid, dim3(NW * 64),
+                       X, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st, p.lens);
+            else
+                LAUNCH(tr, name, (race::sum_kernel<NW, DVAL, SRC, WR, false, T, D, PV>), grid, dim3(NW * 64),
+                       X, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, cin, cout, st, p.lens);
+        };
+        // P = 5, 6 (virtual tables): d = 64 only
+        if constexpr (D == race::HD) {
+            if (p.P > race::NP) return go(std::true_type{});
+        }
+        go(std::false_type{});
     }
 }
 
@@ -143,16 +156,24 @@ void launch_walk(const Tracer &tr, const char *name, dim3 grid, const race::Squa
 {
     if constexpr (sizeof(T) == 2) {
         const race::Part pt = BWD ? p.part_dv : p.part_o;
-        auto go = [&](auto part_c) {
+        auto go2 = [&](auto part_c, auto pv_c) {
             constexpr int PT = decltype(part_c)::value;
+            constexpr bool PV = decltype(pv_c)::value;
             if (RSRC == 1 || sq.deg >= 0)
-                LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D, PT>), grid,
+                LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, true, T, D, PT, PV>), grid,
                        dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out,
                        den, p.lens, pt);
             else
-                LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D, PT>), grid,
+                LAUNCH(tr, name, (race::walk_kernel<NW, CAUSAL, BWD, RSRC, RWR, false, T, D, PT, PV>), grid,
                        dim3(NW * 64), R, vs, W, p.L, p.P, sq, p.N, (int)p.seg, p.nseg, st, rc, wc, out,
                        den, p.lens, pt);
+        };
+        // P = 5, 6 (virtual tables): d = 64 only
+        auto go = [&](auto part_c) {
+            if constexpr (D == race::HD) {
+                if (p.P > race::NP) return go2(part_c, std::true_type{});
+            }
+            go2(part_c, std::false_type{});
         };
         // every pass but the last has 32 tables (NW = 8); split runs have d = 64
         if (p.part_mode == race::PART_NONE) {
@@ -178,16 +199,28 @@ void launch_grad(const Tracer &tr, const char *name, dim3 grid, const T *Xr,
 {
     if constexpr (sizeof(T) == 2) {
         const race::Part pt = REVERSE ? p.part_dk : p.part_dq;
-        auto go = [&](auto part_c) {
+        auto go2 = [&](auto part_c, auto pv_c) {
             constexpr int PT = decltype(part_c)::value;
-            if (dwp)
-                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D, PT>), grid,
+            constexpr bool PV = decltype(pv_c)::value;
+            if constexpr (D > race::HD)  // rows of 128: dwp takes du
+                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D, PT, PV>), grid,
+                       dim3(NW * 64), Xr, vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX,
+                       dwp, p.lens, pt);
+            else if (dwp)
+                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, true, T, D, PT, PV>), grid,
                        dim3(NW * 64), Xr, vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX,
                        dwp, p.lens, pt);
             else
-                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D, PT>), grid,
+                LAUNCH(tr, name, (race::grad_kernel<NW, CAUSAL, REVERSE, false, T, D, PT, PV>), grid,
                        dim3(NW * 64), Xr, vr, vw, W, p.L, p.P, p.N, (int)p.seg, p.nseg, st, rc, wc, dX,
                        nullptr, p.lens, pt);
+        };
+        // P = 5, 6 (virtual tables): d = 64 only
+        auto go = [&](auto part_c) {
+            if constexpr (D == race::HD) {
+                if (p.P > race::NP) return go2(part_c, std::true_type{});
+            }
+            go2(part_c, std::false_type{});
         };
         if (p.part_mode == race::PART_NONE) {
             go(std::integral_constant<int, race::PART_NONE>{});
@@ -315,7 +348,7 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
                                            dwp ? dwp + dwb : nullptr);
         if (dW)
             LAUNCH(tr, "dw_reduce", race::dw_reduce_kernel, dim3((p.LP * race::HD + 31) / 32),
-                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, p.P, D, dW);
+                   dim3(256), dwp, 2 * p.BH * p.nseg, WD * 16, p.LP, p.L, p.P, D, dW);
         launch_walk<WW, CAUSAL != 0, true, 1, 0, D>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV,
                                                  nullptr);
         return;
@@ -365,6 +398,94 @@ void launch_backward(const Plan &p, const T *Q, const T *K, const T *V, const fl
         launch_backward_body<T, NW, 0, D>(p, Q, K, V, W, O, den, dO, tau, dQ, dK, dV, ws, saved, tr, dW);
 }
 
+// Heads of d = 128 (16-bit rows, up to 32 tables, P <= 4).  The rows are
+// hashed once into the feature cache (hash_rows_kernel); the fused kernels
+// then run twice from the cache, on value columns 0..63 and 64..127 (both
+// passes carry the count column, so each finds m).  In the backward both
+// passes end at du (the first with the gradient values' last column, the
+// second with a zero column: the gradient is linear in the values'
+// columns), and du_rows_kernel adds them and forms dx_hat = du W and the
+// normalisation backward over the whole row.
+template <typename T>
+void launch_hash_rows(const Tracer &tr, const char *name, const Plan &p, const T *X, const float *W,
+                      float tau, const race::HCache &h)
+{
+    const dim3 grid((unsigned)((p.N + race::WROWS - 1) / race::WROWS), (unsigned)p.BH);
+    LAUNCH(tr, name, race::hash_rows_kernel<T>, grid, dim3(256), X, p.N, p.d, W, p.L, p.P, 1.0f / tau,
+           2 * p.nw, p.hc_tiles, h.t, h.c);
+}
+
+template <typename T, int NW>
+void launch_forward_wide(const Plan &p, const T *Q, const T *K, const T *V, const float *W, float tau,
+                         int causal, T *O, float *den, char *ws, const Tracer &tr)
+{
+    if constexpr (sizeof(T) == 2) {
+        constexpr int WS = 2 * NW, D = 2 * race::HD;
+        const race::Squash sq = fit_squash(tau, RACE_BF16);  // (not evaluated: t comes from the cache)
+        const dim3 nblk((unsigned)(p.BH * p.nseg));
+        float *st = reinterpret_cast<float *>(ws + p.f_st);
+        float *scan_tmp = reinterpret_cast<float *>(ws + p.f_scan);
+        const race::HCache hk = hcache(p, ws + p.f_hc, 0, -1), hq = hcache(p, ws + p.f_hc, 1, -1);
+        const race::HCache none = hcache(p, nullptr, -1, -1);
+        launch_hash_rows(tr, "hash_k", p, K, W, tau, hk);
+        launch_hash_rows(tr, "hash_q", p, Q, W, tau, hq);
+        for (int c0 = 0; c0 < D; c0 += race::HD) {
+            const race::ValSrc<T> vv{V + c0, nullptr, nullptr};
+            launch_sum<WS, false, 1, 0, D>(tr, "sum_kv", nblk, sq, K, vv, W, p, hk, none, st);
+            launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
+            if (causal)
+                launch_walk<WS, true, false, 1, 0, D>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O + c0, den);
+            else
+                launch_walk<WS, false, false, 1, 0, D>(tr, "fwd_o", nblk, sq, Q, vv, W, p, st, hq, hk, O + c0, den);
+        }
+    }
+}
+
+template <typename T, int NW, int CAUSAL>
+void launch_backward_wide(const Plan &p, const T *Q, const T *K, const T *V, const float *W, const T *O,
+                          const float *den, const T *dO, float tau, T *dQ, T *dK, T *dV, char *ws,
+                          const Tracer &tr)
+{
+    if constexpr (sizeof(T) == 2) {
+        constexpr int WS = 2 * NW, D = 2 * race::HD;
+        const race::Squash sq = fit_squash(tau, RACE_BF16);
+        const dim3 nblk((unsigned)(p.BH * p.nseg));
+        float *sS = reinterpret_cast<float *>(ws + p.b_s);
+        float *sG = reinterpret_cast<float *>(ws + p.b_g);
+        float *scan_tmp = reinterpret_cast<float *>(ws + p.b_scan);
+        const race::HCache hk = hcache(p, ws + p.b_hc, 0, 1), hq = hcache(p, ws + p.b_hc, 2, 3);
+        const race::HCache none = hcache(p, nullptr, -1, -1);
+        // du of Q for passes 0, 1, then of K
+        bf16 *du[4];
+        for (int i = 0; i < 4; ++i) du[i] = reinterpret_cast<bf16 *>(ws + p.w_du + i * p.w_du_bytes);
+        float *dm = reinterpret_cast<float *>(ws + p.w_dm);
+        launch_hash_rows(tr, "hash_k_chain", p, K, W, tau, hk);
+        launch_hash_rows(tr, "hash_q_chain", p, Q, W, tau, hq);
+        LAUNCH(tr, "dm_rows", race::dm_rows_kernel<T>, dim3((unsigned)((p.rows + race::WROWS - 1) / race::WROWS)),
+               dim3(256), dO, O, den, p.rows, p.d, dm);
+        for (int pass = 0; pass < 2; ++pass) {
+            const int c0 = pass * race::HD;
+            const race::ValSrc<T> vv{V + c0, nullptr, nullptr};                      // [v | 1]
+            const race::ValSrc<T> vd{dO + c0, O + c0, den, pass == 0 ? dm : nullptr};  // [dO/m | dm or 0]
+            launch_sum<WS, false, 1, 0, D>(tr, "sum_kv_t", nblk, sq, K, vv, W, p, hk, none, sS);
+            launch_scan(tr, "scan_kv_t", p, sS, scan_tmp, 0);
+            launch_sum<WS, true, 1, 0, D>(tr, "sum_qd", nblk, sq, Q, vd, W, p, hq, none, sG);
+            launch_scan(tr, "scan_qd", p, sG, scan_tmp, 1);
+            launch_grad<WS, CAUSAL != 0, false, D>(tr, "dq", nblk, Q, vd, vv, W, p, sS, hq, hk, dQ,
+                                                   reinterpret_cast<float *>(du[pass]));
+            launch_grad<WS, CAUSAL != 0, true, D>(tr, "dk", nblk, K, vv, vd, W, p, sG, hk, hq, dK,
+                                                  reinterpret_cast<float *>(du[2 + pass]));
+            launch_walk<WS, CAUSAL != 0, true, 1, 0, D>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV + c0,
+                                                        nullptr);
+        }
+        const dim3 rg((unsigned)((p.rows + race::WROWS - 1) / race::WROWS));
+        LAUNCH(tr, "du_rows_q", race::du_rows_kernel<T>, rg, dim3(256), Q, p.rows, p.d, W, p.L, p.P, WS * 16,
+               du[0], du[1], dQ);
+        LAUNCH(tr, "du_rows_k", race::du_rows_kernel<T>, rg, dim3(256), K, p.rows, p.d, W, p.L, p.P, WS * 16,
+               du[2], du[3], dK);
+    }
+}
+
 template <typename T>
 void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V, const float *W,
                       float tau, int causal, void *O, float *den, char *ws, float *saved,
@@ -375,6 +496,14 @@ void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V
     auto v = static_cast<const T *>(V);
     auto o = static_cast<T *>(O);
     if constexpr (sizeof(T) == 2) {
+        if (p.wide) {
+            switch (p.nw) {
+            case 1: launch_forward_wide<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+            case 2: launch_forward_wide<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+            default: launch_forward_wide<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+            }
+            return;
+        }
         if (p.d == 32) {  // the fused path only (L <= 32)
             switch (p.nw) {
             case 1: launch_forward<T, 1, 32>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
@@ -407,6 +536,21 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
     auto dk = static_cast<T *>(dK);
     auto dv = static_cast<T *>(dV);
     if constexpr (sizeof(T) == 2) {
+        if (p.wide) {
+            auto run = [&](auto nw_c) {
+                constexpr int NW = decltype(nw_c)::value;
+                if (causal)
+                    launch_backward_wide<T, NW, 1>(p, q, k, v, W, o, den, go, tau, dq, dk, dv, ws, tr);
+                else
+                    launch_backward_wide<T, NW, 0>(p, q, k, v, W, o, den, go, tau, dq, dk, dv, ws, tr);
+            };
+            switch (p.nw) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
+            }
+            return;
+        }
         if (p.d == 32) {  // the fused path only (L <= 32)
             switch (p.nw) {
             case 1: launch_backward<T, 1, 32>(p, q, k, v, W, o, den, go, tau, causal, dq, dk, dv, ws, saved, tr, dW); break;
@@ -430,23 +574,28 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
 // after every pass's buffers, the middle passes add theirs, the last adds the
 // stored sums before its last step.  Each pass has its own buffers and saved
 // state; dW rows are those of its tables.
-inline int split_passes(int L) { return (L + 31) / 32; }
-inline int split_tables(int L, int pass) { return std::min(32, L - 32 * pass); }
-inline int split_mode(int L, int pass)
+// 2^vt_shift(P) virtual tables per table (P = 5, 6)
+inline int vt_shift(int P) { return P > race::NP ? P - race::NP : 0; }
+// real tables per pass: 32 virtual tables
+inline int split_step(int P) { return 32 >> vt_shift(P); }
+inline int split_passes(int L, int P) { return (L + split_step(P) - 1) / split_step(P); }
+inline int split_tables(int L, int P, int pass) { return std::min(split_step(P), L - split_step(P) * pass); }
+inline int split_mode(int L, int P, int pass)
 {
-    return pass == 0 ? race::PART_OUT : pass + 1 == split_passes(L) ? race::PART_IN : race::PART_MID;
+    return pass == 0 ? race::PART_OUT : pass + 1 == split_passes(L, P) ? race::PART_IN : race::PART_MID;
 }
+constexpr int kMaxPasses = 16;  // L <= 128 tables, up to 4 virtual tables each
 
 template <typename T>
 void split_forward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, const void *Q,
                    const void *K, const void *V, const float *W, float tau, int causal, void *O,
                    float *den, char *ws, float *saved, const Tracer &tr)
 {
-    const int np = split_passes(p.L);
-    Plan q[4];
+    const int np = split_passes(p.L, p.P), step = split_step(p.P);
+    Plan q[kMaxPasses];
     size_t fw = 0, sv = 0;
     for (int i = 0; i < np; ++i) {
-        make_plan(B, H, p.N, p.d, split_tables(p.L, i), p.P, chunk, dt, &q[i]);
+        make_plan(B, H, p.N, p.d, split_tables(p.L, p.P, i), p.P, chunk, dt, &q[i]);
         fw += q[i].f_total;
     }
     float *pv = reinterpret_cast<float *>(ws + fw);
@@ -456,9 +605,9 @@ void split_forward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, cons
     for (int i = 0; i < np; ++i) {
         q[i].lens = p.lens;
         q[i].part_o = race::Part{pv, pm};
-        q[i].part_mode = split_mode(p.L, i);
+        q[i].part_mode = split_mode(p.L, p.P, i);
         float *sb = saved ? reinterpret_cast<float *>(reinterpret_cast<char *>(saved) + sv) : nullptr;
-        dispatch_forward<T>(q[i], Q, K, V, W + 32 * i * p.P * p.d, tau, causal, O, den, ws + off, sb, tr);
+        dispatch_forward<T>(q[i], Q, K, V, W + step * i * p.P * p.d, tau, causal, O, den, ws + off, sb, tr);
         off += q[i].f_total;
         sv += q[i].s_total;
     }
@@ -470,11 +619,11 @@ void split_backward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, con
                     const void *dO, float tau, int causal, void *dQ, void *dK, void *dV, char *ws,
                     const float *saved, const Tracer &tr, float *dW)
 {
-    const int np = split_passes(p.L);
-    Plan q[4];
+    const int np = split_passes(p.L, p.P), step = split_step(p.P);
+    Plan q[kMaxPasses];
     size_t bw = 0;
     for (int i = 0; i < np; ++i) {
-        make_plan(B, H, p.N, p.d, split_tables(p.L, i), p.P, chunk, dt, &q[i]);
+        make_plan(B, H, p.N, p.d, split_tables(p.L, p.P, i), p.P, chunk, dt, &q[i]);
         bw += dW ? q[i].dw_total : q[i].b_total;
     }
     const size_t pvb = align256((size_t)p.rows * race::HD * sizeof(float));
@@ -488,11 +637,11 @@ void split_backward(const Plan &p, int B, int H, int chunk, race_dtype_t dt, con
         q[i].part_dq = pq;
         q[i].part_dk = pk;
         q[i].part_dv = pd;
-        q[i].part_mode = split_mode(p.L, i);
+        q[i].part_mode = split_mode(p.L, p.P, i);
         const float *sb =
             saved ? reinterpret_cast<const float *>(reinterpret_cast<const char *>(saved) + sv) : nullptr;
-        dispatch_backward<T>(q[i], Q, K, V, W + 32 * i * p.P * p.d, O, den, dO, tau, causal, dQ, dK,
-                             dV, ws + off, sb, tr, dW ? dW + 32 * i * p.P * p.d : nullptr);
+        dispatch_backward<T>(q[i], Q, K, V, W + step * i * p.P * p.d, O, den, dO, tau, causal, dQ, dK,
+                             dV, ws + off, sb, tr, dW ? dW + step * i * p.P * p.d : nullptr);
         off += dW ? q[i].dw_total : q[i].b_total;
         sv += q[i].s_total;
     }

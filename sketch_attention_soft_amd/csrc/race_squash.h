@@ -34,7 +34,9 @@ __device__ __forceinline__ int64_t st_idx(int w, int a, int ct, int lane, int at
 // P(t) = sum_S dpsi_S prod_{p in S} t_p (the features without their common
 // factor 1/4), dt[p] = dP/dt_p.  P is multilinear: contracting t_3, then t_2
 // and t_1, yields the four partial derivatives in 24 fused multiply-adds.
-__device__ __forceinline__ void walsh_grad(const float dp[16], const floatx4 &t, float dt[4])
+// Returns P(t) itself (the gradient of a factor that multiplies every
+// feature of the table).
+__device__ __forceinline__ float walsh_grad(const float dp[16], const floatx4 &t, float dt[4])
 {
     float a[8], c[4], b[4];
 #pragma unroll
@@ -47,6 +49,7 @@ __device__ __forceinline__ void walsh_grad(const float dp[16], const floatx4 &t,
     for (int i = 0; i < 4; ++i) b[i] = fmaf(t[2], a[i + 4], a[i]);  // then t_2
     dt[1] = fmaf(t[0], b[3], b[2]);
     dt[0] = fmaf(t[1], b[3], b[1]);
+    return fmaf(t[0], dt[0], fmaf(t[1], b[2], b[0]));  // b0 + t0 b1 + t1 b2 + t0 t1 b3
 }
 
 }  // namespace race

@@ -174,6 +174,15 @@ __device__ __forceinline__ void bstf(float v, Rsrc r, int off)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
 
+#ifndef RACE_SETPRIO
+#define RACE_SETPRIO 0
+#endif
+// wave priority around a block of matrix products (mode m of RACE_SETPRIO)
+template <int M, int P> __device__ __forceinline__ void prio()
+{
+    if constexpr (RACE_SETPRIO == M) __builtin_amdgcn_s_setprio(P);
+}
+
 // Keeps the loads issued above it in place: the scheduler would otherwise
 // sink prefetches towards the end of the loop body, next to their first use.
 __device__ __forceinline__ void pin_loads() { __builtin_amdgcn_sched_barrier(0); }
@@ -278,8 +287,13 @@ __device__ __forceinline__ void xstage_store(const XStage<NTHR> &xs, bf16 *xb, f
 // Staging of value rows y_j: [v | 1] (DVAL = false) or [dO/m | -(dO . o)/m]
 // (DVAL = true).  Item e < 256 -> tokens 2 (e >> 4) and 2 (e >> 4) + 1,
 // columns (e & 15) * 4 .. + 4.
+//
+// Rows of D = 128 elements run in two passes of 64 value columns (the value
+// pointers point at the pass's first column, rows keep their stride): the
+// gradient values' last column comes precomputed over the whole row (dm), or
+// is zero in the pass without it.
 struct YRes {
-    Rsrc v, o, d;
+    Rsrc v, o, d, dm;
 };
 template <bool DVAL, int D, typename IO>
 __device__ __forceinline__ YRes yres(const ValSrc<IO> &s, const Chunk &c)
@@ -287,11 +301,14 @@ __device__ __forceinline__ YRes yres(const ValSrc<IO> &s, const Chunk &c)
     YRes r;
     r.v = row_res<D>(s.V, c);
     if constexpr (DVAL) {
-        r.o = row_res<D>(s.O, c);
+        r.o = D > HD ? r.v : row_res<D>(s.O, c);
         r.d = make_rsrc(s.den + c.tok0, c.nv * 4);
+        // (a pass without the column: an empty resource, loads read zero)
+        r.dm = D > HD ? make_rsrc(s.dm ? s.dm + c.tok0 : s.den, s.dm ? c.nv * 4 : 0) : r.d;
     } else {
         r.o = r.v;
         r.d = r.v;
+        r.dm = r.v;
     }
     return r;
 }
@@ -317,7 +334,10 @@ __device__ __forceinline__ void ystage_load(const YRes &r, YStage<NTHR, DVAL> &y
             const int off = act && (D == HD || (e & 15) * 4 < D) ? tok * (D * 2) + (e & 15) * 8 : OOB;
             ys.x[it][h] = bld64(r.v, off);
             if constexpr (DVAL) {
-                ys.o[it][h] = bld64(r.o, off);
+                if constexpr (D > HD)  // the last column, precomputed
+                    ys.o[it][h] = u32x2{__builtin_bit_cast(uint32_t, bldf(r.dm, act ? tok * 4 : OOB)), 0u};
+                else
+                    ys.o[it][h] = bld64(r.o, off);
                 ys.m[it][h] = bldf(r.d, act ? tok * 4 : OOB);
             }
         }
@@ -331,7 +351,7 @@ constexpr int YRS = YRC + 8;
 
 // yc: column-major [NCOL][YCS] and / or yr: token-major [WCT][YRS] (either may
 // be null); nv = valid rows of the chunk (the others are staged as zeros)
-template <int NTHR, bool DVAL, typename IO>
+template <int NTHR, bool DVAL, typename IO, int D = HD>
 __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int nv, bf16 *yc,
                                              bf16 *yr = nullptr)
 {
@@ -388,6 +408,7 @@ __device__ __forceinline__ void ystage_store(const YStage<NTHR, DVAL> &ys, int n
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[h][i] = xv[i] * inv_m;
                 extra[h] = -dot * inv_m;
+                if constexpr (D > HD) extra[h] = __builtin_bit_cast(float, ys.o[it][h][0]);
             }
             if (yc) {
 #pragma unroll
@@ -430,28 +451,112 @@ template <int NTHR> __device__ __forceinline__ void yrow_zero_pad(bf16 *yr)
 // contains one vanishes on the writer side, and with writer features scaled by
 // 2^-P each table's kernel is prod_{p < P} (1 + t_p t'_p) / 2^P, the P-plane
 // corner product.  W is [L][P][d]: internal hyperplane 4 l + p <- row P l + p.
+//
+// P = 5, 6: a table of 2^P features is V = 2^(P-4) virtual tables of 16.
+// Its features prod_{p in S} t_p, S a subset of {0..P-1}, split as S = A + B
+// with A in {0..3} and B in {4, 5}: virtual table B (b = bit mask of B) holds
+// the 16 Walsh features of t_0..t_3 times tau_b = prod_{p in B} t_p, so the
+// sum over the virtual tables of their kernels is the real table's,
+// prod_{p < P} (1 + t_p t'_p) / 2^P.  Internal rows: virtual table 0 projects
+// hyperplanes 0..3, virtual table 1 hyperplanes 4 (and 5), the others none
+// (zero rows, t = +0); vt_expand moves t_0..t_3 and t_4, t_5 between the
+// lanes of a real table, vt_reduce adds the virtual tables' gradients back.
+// Virtual table 4 w + g of a wave is real table (4 w + g) >> (P - 4), b = g & (V - 1).
+__device__ __forceinline__ int vt_shift(int P) { return P > NP ? P - NP : 0; }
+// internal tables of L real ones
+__device__ __forceinline__ int vtables(int L, int P) { return L << vt_shift(P); }
+// row of W [L][P][d] of internal hyperplane hp, or -1 (padding)
+__device__ __forceinline__ int w_row(int L, int P, int hp)
+{
+    int l = hp >> 2, p = hp & 3;
+    if (P > NP) {
+        const int sh = P - NP, b = l & ((1 << sh) - 1);
+        l >>= sh;
+        p = b == 0 ? p : b == 1 ? NP + p : P;
+    }
+    return l < L && p < P ? l * P + p : -1;
+}
 __device__ __forceinline__ float w_elem(const float *__restrict__ W, int L, int P, int D, int hp, int c)
 {
-    const int l = hp >> 2, p = hp & 3;
-    return l < L && p < P && c < D ? W[(l * P + p) * D + c] : 0.f;
+    const int r = w_row(L, P, hp);
+    return r >= 0 && c < D ? W[r * D + c] : 0.f;
 }
 // masks of |t| for the fp16 pairs (p = 0, 1) and (2, 3): zero for padding
-// hyperplanes
+// hyperplanes (P > 4: of this lane's virtual table)
 struct TMask {
     uint32_t m[2];
 };
-__device__ __forceinline__ TMask t_mask(int P)
+template <bool PV = false> __device__ __forceinline__ TMask t_mask(int P)
 {
+    int n = P;  // hyperplanes of this lane's table that are not padding
+    if (PV) {
+        const int b = (lane_id() >> 4) & ((1 << (P - NP)) - 1);
+        n = b == 0 ? NP : b == 1 ? P - NP : 0;
+    }
     TMask t;
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-        t.m[q] = (2 * q < P ? 0x7fffu : 0u) | (2 * q + 1 < P ? 0x7fff0000u : 0u);
+        t.m[q] = (2 * q < n ? 0x7fffu : 0u) | (2 * q + 1 < n ? 0x7fff0000u : 0u);
     return t;
 }
 // writer feature scale 2^-P (padding tables: 0)
 __device__ __forceinline__ float writer_scale(int P, bool table_in_use)
 {
     return table_in_use ? __builtin_ldexpf(1.f, -P) : 0.f;
+}
+
+// t_0..t_3 of this lane's table, with (P > 4) the factor tau_b of its
+// virtual table b and t_4, t_5 of the real table
+struct VT {
+    floatx4 t;
+    float tau, t4, t5;
+    int b;
+};
+// P > 4: from the per-row t of the lanes of virtual tables 0 (t_0..t_3) and
+// 1 (t_4, t_5) of the same token; P <= 4: t itself, tau = 1.
+template <bool PV> __device__ __forceinline__ VT vt_expand(const halfx4 &raw, int P)
+{
+    VT v;
+    if constexpr (!PV) {
+        v.t = to_f4(raw);
+        v.tau = 1.f;
+        v.t4 = v.t5 = 0.f;
+        v.b = 0;
+    } else {
+        const int lane = lane_id();
+        v.b = (lane >> 4) & ((1 << (P - NP)) - 1);
+        const u32x2 r = __builtin_bit_cast(u32x2, raw);
+        const int src = (lane - 16 * v.b) * 4;  // byte address of the lane of virtual table 0
+        const u32x2 t03 = {(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)r[0]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)r[1])};
+        const half2v t45 = __builtin_bit_cast(half2v, __builtin_amdgcn_ds_bpermute(src + 64, (int)r[0]));
+        v.t = to_f4(__builtin_bit_cast(halfx4, t03));
+        v.t4 = (float)t45[0];
+        v.t5 = (float)t45[1];
+        v.tau = v.b == 0 ? 1.f : v.b == 1 ? v.t4 : v.b == 2 ? v.t5 : v.t4 * v.t5;
+    }
+    return v;
+}
+// P > 4: dt holds the gradient of this lane's 16 features with respect to
+// t_0..t_3 of its table without the factor tau_b, dtau the gradient with
+// respect to tau_b.  Sums the shares of the V virtual tables of the real
+// table and leaves in dt the gradient of this lane's own rows: t_0..t_3
+// (virtual table 0), t_4, t_5 (virtual table 1), zero (the others).
+template <bool PV> __device__ __forceinline__ void vt_reduce(const VT &v, int P, float dtau, float (&dt)[4])
+{
+    if constexpr (PV) {
+        float x[6];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) x[p] = v.tau * dt[p];
+        x[4] = v.b == 1 ? dtau : v.b == 3 ? dtau * v.t5 : 0.f;  // d tau_b / d t_4
+        x[5] = v.b == 2 ? dtau : v.b == 3 ? dtau * v.t4 : 0.f;  // d tau_b / d t_5
+        for (int m = 16; m < (16 << (P - NP)); m <<= 1)
+#pragma unroll
+            for (int i = 0; i < 6; ++i) x[i] += __shfl_xor(x[i], m);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            dt[p] = v.b == 0 ? x[p] : v.b == 1 && p < 2 ? x[4 + p] : 0.f;
+    }
 }
 
 // W rows of this wave's 16 hyperplanes as the A operand of U^T = W x^T.
@@ -719,13 +824,14 @@ __device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 //   SRC = 0: the rows X are hashed here; WR bit 0 / bit 1 store their t /
 //            dt/du' into the cache `co`.
 //   SRC = 1: t comes from the cache `ci_` (X is not read).
-template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO, int D>
+template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO, int D, bool PV = false>
 __global__ __launch_bounds__(NW * 64) void sum_kernel(
     const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st, Lens ls)
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = SRC == 0;
+    static_assert(!(HASH && D > HD), "rows of 128 elements are hashed by hash_rows_kernel");
     // double-buffered: chunk c is hashed and summed while chunk c + 1 is staged
     __shared__ __attribute__((aligned(16))) bf16 xbuf[2][HASH ? WCT * XRS : 8];
     __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
@@ -743,15 +849,16 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     if (DVAL) {
         vh.O += row0 * D;
         vh.den += row0;
+        if (vh.dm) vh.dm += row0;
     }
     const _Float16 *cin_t = HASH ? nullptr : ci_.t + hc_seg<NW>(ci_, bh, t_begin);
     _Float16 *cout_t = co.t ? co.t + hc_seg<NW>(co, bh, t_begin) : nullptr;
     _Float16 *cout_c = co.c ? co.c + hc_seg<NW>(co, bh, t_begin) : nullptr;
     WRows wr;
     if (HASH) load_wrows<D>(W, L, P, wr);
-    const TMask tm = t_mask(P);
+    const TMask tm = t_mask<PV>(P);
     const bf16x8 sel[2] = {selection(0), selection(1)};
-    const float qw = writer_scale(P, 4 * w + g < L);  // writer features: 2^-P, padding 0
+    const float qw = writer_scale(P, 4 * w + g < vtables(L, P));  // writer features: 2^-P, padding 0
     floatx4 af[4][NT];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -774,7 +881,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
     } else {
         hc_load<NW>(hc_res<NW>(cin_t, c0), tc);
     }
-    ystage_store<NTHR, DVAL, IO>(ys, c0.nv, ycol[0]);
+    ystage_store<NTHR, DVAL, IO, D>(ys, c0.nv, ycol[0]);
     if (HASH) xstage_load<NTHR, false, D>(row_res<D>(Xs, c1), xs);
     ystage_load<NTHR, DVAL, D>(yres<DVAL, D>(vh, c1), ys);
     lds_barrier();
@@ -785,7 +892,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
         // which were last read before the previous barrier, then prefetch ci + 2
         if (ci + 1 < nch) {
             if (HASH) xstage_store<NTHR, false, IO>(xs, xbuf[b ^ 1], kbuf[b ^ 1]);
-            ystage_store<NTHR, DVAL, IO>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
+            ystage_store<NTHR, DVAL, IO, D>(ys, chunk(ci + 1).nv, ycol[b ^ 1]);
         }
         const halfx4 tcur[2] = {tc[0], tc[1]};
         if (HASH)
@@ -809,8 +916,10 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
             } else {
                 t = tcur[tt];
             }
-            walsh_tm(to_f4(t), qw, ptm[tt][0], ptm[tt][1]);
+            const VT vt = vt_expand<PV>(t, P);
+            walsh_tm(vt.t, qw * vt.tau, ptm[tt][0], ptm[tt][1]);
         }
+        prio<1, 1>();
         feat_major(ptm, sel, pfm);
         // tokens past the end have psi_0 = 1/4 but zero value rows
 #pragma unroll
@@ -819,6 +928,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) mma32(af[s][ct], pfm[s], yb);
         }
+        prio<1, 0>();
         lds_barrier();
     });
     const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 64 * NCOL);
@@ -845,7 +955,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // buffered, and the partial outputs of chunk c are summed after the barrier
 // of chunk c + 1, beside that chunk's products.
 template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO, int D,
-          int PART = PART_NONE>
+          int PART = PART_NONE, bool PV = false>
 __global__ __launch_bounds__(NW * 64) void walk_kernel(
     const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
@@ -853,6 +963,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 {
     constexpr int NTHR = NW * 64;
     constexpr bool HASH = RSRC == 0;
+    static_assert(!(HASH && D > HD), "rows of 128 elements are hashed by hash_rows_kernel");
     constexpr int RSLOTS = 2 * 4 * 64;  // (token tile, value column tile < 4, lane) output slots
     constexpr int RIT = (RSLOTS + NTHR - 1) / NTHR;
     constexpr int REDN = NW * 2 * 4 * 64 * 4;  // partial outputs: value columns (4 tiles) of every wave
@@ -877,6 +988,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     if (BWD) {
         vh.O += row0 * D;
         vh.den += row0;
+        if (vh.dm) vh.dm += row0;
     }
     IO *Os = Out + row0 * D;
     float *pv = PART != PART_NONE ? part.v + row0 * HD : nullptr;
@@ -888,12 +1000,12 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 
     WRows wr;  // the forward's W rows (hi, lo), kept in registers
     if (HASH) stage_wrows<NW, D>(W, L, P, reinterpret_cast<bf16 *>(red));
-    const TMask tm = t_mask(P);
+    const TMask tm = t_mask<PV>(P);
     stage_sel(sl);
     __syncthreads();
     // red is next written after two more barriers
     if (HASH) wrows_lds<NW>(reinterpret_cast<const bf16 *>(red), wr);
-    const float qw = writer_scale(P, 4 * w + g < L);  // writer features: 2^-P, padding 0
+    const float qw = writer_scale(P, 4 * w + g < vtables(L, P));  // writer features: 2^-P, padding 0
     floatx4 acc[4][NT];
     {
         const float *src = st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL);
@@ -948,7 +1060,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             } else {
                 t = rt[tt];
             }
-            walsh_tm(to_f4(t), 1.f, pr[tt][0], pr[tt][1]);
+            const VT vt = vt_expand<PV>(t, P);
+            walsh_tm(vt.t, vt.tau, pr[tt][0], pr[tt][1]);
         }
         if (!HASH) hc_load<NW>(hc_res<NW>(rt_seg, chunk(ci + 1)), rt);
     };
@@ -1014,7 +1127,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         constexpr int b = decltype(par)::v;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
         if (CAUSAL) {
-            ystage_store<NTHR, BWD, IO>(ys, cc.nv, ycol[b]);
+            ystage_store<NTHR, BWD, IO, D>(ys, cc.nv, ycol[b]);
             ystage_load<NTHR, BWD, D>(yres<BWD, D>(vh, cn), ys);
         }
         bf16x8 pr[2][2];
@@ -1036,6 +1149,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         lds_barrier();  // value columns and next rows staged; partial outputs of chunk ci - 1 in LDS
         finish(ci - 1, b ^ 1);  // (none before the first chunk: its stores are dropped)
         __builtin_amdgcn_sched_barrier(0);
+        prio<2, 1>();
         // the next chunk's reader features, computed beside this chunk's
         // products (past the last chunk: nothing is read or stored)
         if constexpr (PIPE) reader_feats(ci + 1, xbuf[b ^ 1], kbuf[b ^ 1], prc);
@@ -1044,7 +1158,10 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), qw, pw[tt][0], pw[tt][1]);
+            for (int tt = 0; tt < 2; ++tt) {
+                const VT vt = vt_expand<PV>(wt[tt], P);
+                walsh_tm(vt.t, qw * vt.tau, pw[tt][0], pw[tt][1]);
+            }
             hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             // scores^T tiles D[j][i] = psi_w(j) . psi_r(i) over this wave's tables
             constexpr int TJ[3] = {0, BWD ? 1 : 0, 1}, TI[3] = {0, BWD ? 0 : 1, 1};
@@ -1076,6 +1193,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
+        prio<1, 1>();
         // O^T tiles (tt, ct): lane (columns 16 ct + 4g + r, token 16 tt + c16)
         floatx4 oacc[2][NT];
 #pragma unroll
@@ -1108,6 +1226,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
+        prio<1, 0>();
         float *rn = red + b * (REDN + REDM), *rm = rn + REDN;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1118,6 +1237,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             // 0..15 (the other lanes' values are not read)
             if (!BWD) rm[(w * 2 + tt) * 64 + lane] = oacc[tt][4][0];
         }
+        prio<2, 0>();
     });
     if (nch > 0) {
         lds_barrier();
@@ -1143,7 +1263,12 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 // 64 dims] on MFMA (both operands read transposed from du and the staged
 // rows), summed in LDS, and the workgroup's sum written to dwp[workgroup]
 // ([NW * 16][64] fp32) for a reduction over segments.
-template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D, int PART = PART_NONE>
+// D = 128 (rows of 128 elements, in two passes of 64 value columns): the
+// kernel stops at du, which it stores (bf16, [row][NW * 16], at dwp) for
+// du_rows_kernel, which adds the passes and forms dx_hat = du W and the
+// normalisation backward over the whole row.
+template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D, int PART = PART_NONE,
+          bool PV = false>
 __global__ __launch_bounds__(NW * 64) void grad_kernel(
     const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
     const float *__restrict__ W, int L, int P, int64_t N, int seg, int64_t nseg,
@@ -1151,6 +1276,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     float *__restrict__ dwp, Lens ls, Part part)
 {
     constexpr bool RD = !REVERSE;  // the readers carry the gradient values D
+    constexpr bool DUO = D > HD;   // store du, no dx_hat here
+    static_assert(!DUO || (!DW && PART == PART_NONE), "rows of 128: du only");
     constexpr int NTHR = NW * 64;
     constexpr int DUS = NW * 16 + 8;  // du row stride (bf16)
     constexpr int TPWV = 8 / NW;      // dxh tiles per wave
@@ -1183,11 +1310,14 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     if (RD) {
         vrh.O += row0 * D;
         vrh.den += row0;
+        if (vrh.dm) vrh.dm += row0;
     } else {
         vwh.O += row0 * D;
         vwh.den += row0;
+        if (vwh.dm) vwh.dm += row0;
     }
     IO *dXs = dX + row0 * D;
+    bf16 *dug = DUO ? reinterpret_cast<bf16 *>(dwp) + row0 * (NW * 16) : nullptr;
     float *pv = PART != PART_NONE ? part.v + row0 * HD : nullptr;
     const _Float16 *rt_seg = rc.t + hc_seg<NW>(rc, bh, t_begin);
     const _Float16 *rc_seg = rc.c + hc_seg<NW>(rc, bh, t_begin);
@@ -1199,17 +1329,18 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     // reader features by 1, the products below give the gradient with respect
     // to the unscaled reader features prod t_p, so that walsh_grad yields dt
     // itself.
-    for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
-        const int hp = e / HD, c = e % HD;
-        wt_l[c * WTS + hp] = (bf16)w_elem(W, L, P, D, hp, c);
-    }
+    if constexpr (!DUO)
+        for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) {
+            const int hp = e / HD, c = e % HD;
+            wt_l[c * WTS + hp] = (bf16)w_elem(W, L, P, D, hp, c);
+        }
     if constexpr (DW)
         for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) dwl[e] = 0.f;
     stage_sel(sl);
     // the selection operands are read in the first chunk before its barrier
     // (and a wave whose W rows are all padding reaches that read early)
     __syncthreads();
-    const float qw = writer_scale(P, 4 * w + g < L);  // writer features: 2^-P, padding 0
+    const float qw = writer_scale(P, 4 * w + g < vtables(L, P));  // writer features: 2^-P, padding 0
     floatx4 acc[4][NT];  // CxF state
     load_state_cxf(st + (bh * (nseg + 1) + (CAUSAL ? sg : nseg)) * (int64_t)(NW * 64 * NCOL), acc);
 
@@ -1239,7 +1370,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     ystage_load<NTHR, RD, D>(yres<RD, D>(vrh, c0), ysr);
     hc_load<NW>(hc_res<NW>(rt_seg, c0), rt);
     hc_load<NW>(hc_res<NW>(rc_seg, c0), rcv);
-    xstage_load<NTHR, true, D>(row_res<D>(Rs, c0), xs);
+    if constexpr (!DUO) xstage_load<NTHR, true, D>(row_res<D>(Rs, c0), xs);
 
     // dxh = du W of chunk ci (du in buffer pb) for this wave's tiles; the
     // partial dots with x go to dotp[pb], dxh, x and |x|^2 stay in registers
@@ -1338,8 +1469,8 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
-        ystage_store<NTHR, RD, IO>(ysr, cc.nv, nullptr, yrow_r[b]);
-        if (CAUSAL) ystage_store<NTHR, !RD, IO>(ysw, cc.nv, ycol_w[b], yrow_w[b]);
+        ystage_store<NTHR, RD, IO, D>(ysr, cc.nv, nullptr, yrow_r[b]);
+        if (CAUSAL) ystage_store<NTHR, !RD, IO, D>(ysw, cc.nv, ycol_w[b], yrow_w[b]);
         ystage_load<NTHR, RD, D>(yres<RD, D>(vrh, cn), ysr);
         if (CAUSAL) ystage_load<NTHR, !RD, D>(yres<!RD, D>(vwh, cn), ysw);
         const halfx4 trh[2] = {rt[0], rt[1]}, crh[2] = {rcv[0], rcv[1]};
@@ -1349,17 +1480,23 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         if (CAUSAL) {
             bf16x8 pw[2][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) walsh_tm(to_f4(wt[tt]), qw, pw[tt][0], pw[tt][1]);
+            for (int tt = 0; tt < 2; ++tt) {
+                const VT vt = vt_expand<PV>(wt[tt], P);
+                walsh_tm(vt.t, qw * vt.tau, pw[tt][0], pw[tt][1]);
+            }
             hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             bf16x8 sel[2];
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
         lds_barrier();  // value rows of this chunk; du and rows of ci - 1; dots of ci - 2
-        finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
-        // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
-        xstage_store<NTHR, true, IO>(xs, xbuf[b], kbuf[b]);
-        xstage_load<NTHR, true, D>(row_res<D>(Rs, cn), xs);
+        prio<2, 1>();
+        if constexpr (!DUO) {
+            finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
+            // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
+            xstage_store<NTHR, true, IO>(xs, xbuf[b], kbuf[b]);
+            xstage_load<NTHR, true, D>(row_res<D>(Rs, cn), xs);
+        }
         // reader value rows as B operands (token-major)
         bf16x8 yb8[2][3];
 #pragma unroll
@@ -1406,6 +1543,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         }
         // inter-chunk part with the state before this chunk (consecutive
         // products go to the two token tiles' independent accumulators)
+        prio<1, 1>();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             bf16x8 sa[3];
@@ -1432,6 +1570,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], ya, pfm[s]);
             }
         }
+        prio<1, 0>();
         // Walsh gradient -> du of this wave's 16 hyperplanes (token-major, LDS)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1440,17 +1579,26 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dp[4 * s + r] = dps[s][tt][r];
-            walsh_grad(dp, to_f4(trh[tt]), dt);
+            const VT vt = vt_expand<PV>(trh[tt], P);
+            const float dtau = walsh_grad(dp, vt.t, dt);
+            vt_reduce<PV>(vt, P, dtau, dt);
             const floatx4 cr = to_f4(crh[tt]);
-            *reinterpret_cast<bf16x4 *>(du_l[b] + (tt * 16 + c16) * DUS + w * 16 + 4 * g) =
-                pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
+            const bf16x4 du = pk4(pk_bf16(dt[0] * cr[0], dt[1] * cr[1]), pk_bf16(dt[2] * cr[2], dt[3] * cr[3]));
+            if constexpr (DUO)  // rows past the chunk's end are dropped
+                bst64(__builtin_bit_cast(u32x2, du), make_rsrc(dug + cc.tok0 * (NW * 16), cc.nv * (NW * 16) * 2),
+                      ((tt * 16 + c16) * (NW * 16) + w * 16 + 4 * g) * 2);
+            else
+                *reinterpret_cast<bf16x4 *>(du_l[b] + (tt * 16 + c16) * DUS + w * 16 + 4 * g) = du;
         }
-        dxh_tiles(b ^ 1, ci - 1);  // (before the first chunk: unused values)
-        if constexpr (DW) {
-            if (ci >= 1) dw_tiles(b ^ 1);
+        if constexpr (!DUO) {
+            dxh_tiles(b ^ 1, ci - 1);  // (before the first chunk: unused values)
+            if constexpr (DW) {
+                if (ci >= 1) dw_tiles(b ^ 1);
+            }
         }
+        prio<2, 0>();
     }
-    if (nch > 0) {
+    if (!DUO && nch > 0) {
         const int pl = (nch - 1) & 1;  // buffers of the last chunk
         lds_barrier();
         if (nch >= 2) finish(nch - 2, pl ^ 1);
@@ -1475,7 +1623,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
 // then the 8 group sums are added in group order (a fixed order, whatever the
 // launch).
 static __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part, int64_t nparts,
-                                                        int rows, int LP, int P, int d,
+                                                        int rows, int LP, int L, int P, int d,
                                                         float *__restrict__ dW)
 {
     __shared__ float gs[8][32];
@@ -1492,10 +1640,10 @@ static __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__re
         float t = gs[0][j];
 #pragma unroll
         for (int g2 = 1; g2 < 8; ++g2) t += gs[g2][j];
-        // dW is [L][P][d]: padding hyperplanes (p >= P) and columns past d of
-        // the blocks are dropped
-        const int hp = e / HD, c = e % HD;
-        if ((hp & 3) < P && c < d) dW[((hp >> 2) * P + (hp & 3)) * d + c] = t;
+        // dW is [L][P][d]: padding hyperplanes and columns past d of the
+        // blocks are dropped
+        const int hp = e / HD, c = e % HD, r = w_row(L, P, hp);
+        if (r >= 0 && c < d) dW[r * d + c] = t;
     }
 }
 

@@ -93,7 +93,8 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
     (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
-    (dict(d=32, L=33), E_UNSUP), (dict(P=5), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
+    (dict(d=32, L=33), E_UNSUP), (dict(P=7), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
+    (dict(P=5, dt=F32), E_UNSUP), (dict(P=6, d=32), E_UNSUP), (dict(P=6, L=129), E_UNSUP),
     (dict(P=0), E_SHAPE), (dict(L=129), E_UNSUP), (dict(L=129, dt=F32), E_UNSUP),
     (dict(L=33, dt=F32, bwd=2), E_UNSUP), (dict(L=8, dt=F32, bwd=2), E_UNSUP),
     (dict(d=32, L=33, dt=F16), E_UNSUP), (dict(dt=5), E_UNSUP),
@@ -101,6 +102,22 @@ def test_workspace_sizes(lib):
 ])
 def test_workspace_validation(lib, kw, code):
     assert ws_bytes(lib, **kw)[0] == code
+
+
+def test_virtual_tables(lib):
+    """P = 5, 6 on 16-bit rows: 2^(P-4) virtual tables of 16 features per
+    table, in passes of 32 virtual tables when there are more."""
+    for P in (5, 6):
+        prev = 0
+        for L in (1, 4, 8, 9, 16, 17, 33, 128):
+            for bwd in (0, 1, 2):
+                st, b = ws_bytes(lib, L=L, P=P, bwd=bwd, N=3000)
+                assert st == OK and b > 0, (P, L, bwd)
+            st, b = ws_bytes(lib, L=L, P=P, N=3000)
+            assert b >= prev
+            prev = b
+        # a P = 6 table takes the room of four P = 4 tables
+        assert ws_bytes(lib, L=8, P=6, N=3000)[1] == ws_bytes(lib, L=32, P=4, N=3000)[1]
 
 
 def test_tables_in_passes(lib):

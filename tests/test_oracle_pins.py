@@ -71,7 +71,9 @@ def test_p12_single_hyperplane_is_logistic():
 
 # -- P-3: exact quadratic closed form, causal and non-causal
 @pytest.mark.parametrize("N,d,L,P,tau", [(200, 16, 6, 3, 0.7), (128, 64, 8, 4, 1.0),
-                                         (97, 32, 5, 4, 0.5), (64, 8, 3, 1, 1.3)])
+                                         (97, 32, 5, 4, 0.5), (64, 8, 3, 1, 1.3),
+                                         (90, 128, 4, 4, 1.0), (77, 24, 3, 5, 0.8),
+                                         (66, 16, 2, 6, 1.0)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_p3_quadratic_closed_form(N, d, L, P, tau, causal):
     rng = np.random.default_rng(N + d + L)
@@ -262,12 +264,29 @@ def _loss_grads_fd(fwd, q, k, v, g, h=1e-6):
 
 # -- P-9: backward against finite differences of the oracle's forward
 @pytest.mark.parametrize("P,tau,causal", [(2, 1.0, True), (3, 0.5, False), (4, 1.0, True),
-                                          (4, 0.5, False), (3, 0.7, True)])
+                                          (4, 0.5, False), (3, 0.7, True), (5, 0.8, True),
+                                          (6, 1.0, False), (6, 0.5, True)])
 def test_p9_finite_differences(P, tau, causal):
     rng = np.random.default_rng(50 + P)
     N, d, L = 12, 6, 3
     q = rng.standard_normal((N, d)) * 1.7  # un-normalised rows
     k = rng.standard_normal((N, d)) * 0.6
+    v = rng.standard_normal((N, d))
+    g = rng.standard_normal((N, d))
+    W = rng.standard_normal((L, P, d))
+    o, den, dq, dk, dv = oracle.forward_backward(q, k, v, g, W, tau, causal)
+    fd = _loss_grads_fd(lambda a, b, c: oracle.forward(a, b, c, W, tau, causal)[0], q, k, v, g)
+    for an, num in zip((dq, dk, dv), fd):
+        assert _relf(an, num) < 1e-6, _relf(an, num)
+
+
+# -- P-9 at head dimension 128 (un-normalised rows, causal and not)
+@pytest.mark.parametrize("causal", [True, False])
+def test_p9_finite_differences_d128(causal):
+    rng = np.random.default_rng(57)
+    N, d, L, P, tau = 6, 128, 2, 4, 0.8
+    q = rng.standard_normal((N, d)) * 1.3
+    k = rng.standard_normal((N, d)) * 0.4
     v = rng.standard_normal((N, d))
     g = rng.standard_normal((N, d))
     W = rng.standard_normal((L, P, d))
