@@ -331,8 +331,8 @@ def main() -> int:
 def generality_bench(args, binding, I, np, torch) -> int:
     """One JSON line: the fwd+bwd step (saved state, as the main bench times
     it) of causal_n4m_bf16's shape in the variants the library supports
-    beyond it -- fp16 rows, head dimension 32, P = 2 hyperplanes per table,
-    and a right-padded batch of four sequences of 4M, 3M, 2M and 1M tokens
+    beyond it -- fp16 rows, head dimension 32 and 128, P = 2, 5 and 6
+    hyperplanes per table, and a right-padded batch of four sequences of 4M, 3M, 2M and 1M tokens
     padded to 4M (tokens/s counts real tokens only; the binding's padded_chunk
     segments) -- beside the bf16 d = 64
     P = 4 step itself, in one process.  Inputs are drawn on the device (torch
@@ -349,6 +349,9 @@ def generality_bench(args, binding, I, np, torch) -> int:
                 ("f16_d64_P4", torch.float16, 64, 4, None),
                 ("bf16_d32_P4", torch.bfloat16, 32, 4, None),
                 ("bf16_d64_P2", torch.bfloat16, 64, 2, None),
+                ("bf16_d64_P5", torch.bfloat16, 64, 5, None),
+                ("bf16_d64_P6", torch.bfloat16, 64, 6, None),
+                ("bf16_d128_P4", torch.bfloat16, 128, 4, None),
                 ("bf16_padded_4x4M", torch.bfloat16, 64, 4, (4 << 20, 3 << 20, 2 << 20, 1 << 20))]
     out = {}
     for name, tdt, d, P, lens in variants:

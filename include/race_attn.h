@@ -44,7 +44,15 @@
  *     rows are zero-padded to 64 columns on chip: the same work per token as
  *     d = 64, half the memory traffic) and P = 1, 2, 3 (the kernels keep 4
  *     hyperplanes per table with t = 0 on the padding ones, an exact
- *     reduction to the P-plane corner product at the work of P = 4),
+ *     reduction to the P-plane corner product at the work of P = 4);
+ *     for RACE_BF16 and RACE_F16 also P = 5 and 6 at any L <= 128 (a table of
+ *     2^P buckets runs as 2^(P-4) virtual tables of 16: the Walsh features
+ *     of hyperplanes 0..3 times those of hyperplanes 4, 5, whose kernels add
+ *     up to the table's; the work of L 2^(P-4) tables of P = 4, in passes of
+ *     32) and d = 128 with L <= 32, P <= 4 (the rows are hashed once over all
+ *     128 elements, then the chunk kernels run on value columns 0..63 and
+ *     64..127; no saved state: race_attn_saved_bytes gives 0, and the
+ *     backward rehashes),
  *     any B, H, N >= 1 (int64 offsets), tau finite and > 0.
  *   - chunk: tokens per scan segment, 0 = the library chooses; otherwise a
  *     multiple of 16.  It changes only the order of the floating-point sums.
@@ -167,7 +175,8 @@ race_status_t race_attn_backward(const void *Q, const void *K, const void *V, co
  * for_backward = 2).  No saved state.  chunk = 0 picks the dense default
  * (about one segment per compute unit over all B H N rows); with unequal
  * lengths the segments past a sequence's end have no work, and a smaller
- * chunk (about B H N / 2048) keeps more workgroups busy. */
+ * chunk (about B H N / 2048) keeps more workgroups busy.  d = 128 rows:
+ * RACE_ERR_UNSUPPORTED. */
 race_status_t race_attn_forward_padded(const void *Q, const void *K, const void *V,
                                        const float *W, int L, int P, float tau, int causal, int B,
                                        int H, int64_t N, int d, race_dtype_t dt, int chunk,
@@ -191,7 +200,7 @@ race_status_t race_attn_backward_padded(const void *Q, const void *K, const void
  * to it) and sizes the workspace: race_attn_workspace_bytes(B, H,
  * max_seqlen, ...), as for race_attn_forward_padded.  T <= B max_seqlen.
  * RACE_BF16 and RACE_F16 rows only (the fused kernels: d = 32 or 64; any L up
- * to 128); RACE_ERR_UNSUPPORTED otherwise.  The backward writes dW when dW
+ * to 128, P up to 6); RACE_ERR_UNSUPPORTED otherwise.  The backward writes dW when dW
  * is not NULL (workspace with for_backward = 2).  chunk = 0 as for the padded
  * entry points. */
 race_status_t race_attn_forward_varlen(const void *Q, const void *K, const void *V,
@@ -278,8 +287,8 @@ race_status_t race_attn_squash_deriv_coeffs(float tau, race_dtype_t dt, float *c
  * dW (device, fp32 [L][P][d], overwritten).  dQ, dK and dV are the same as
  * race_attn_backward_ex's.  The per-workgroup sums are added in a fixed order,
  * so the result does not depend on the launch.  Supported for RACE_BF16 and
- * RACE_F16 (RACE_ERR_UNSUPPORTED for RACE_F32); workspace: race_attn_workspace_bytes
- * with for_backward = 2. */
+ * RACE_F16 with d = 32 or 64 (RACE_ERR_UNSUPPORTED for RACE_F32 and d = 128);
+ * workspace: race_attn_workspace_bytes with for_backward = 2. */
 race_status_t race_attn_backward_dw(const void *Q, const void *K, const void *V,
                                     const float *W, const void *O, const float *den,
                                     const void *dO, int L, int P, float tau, int causal, int B,

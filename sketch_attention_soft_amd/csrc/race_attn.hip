@@ -40,7 +40,7 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     // d = 64 and P = 4, or d = 32 and P < 4 on the fused path (16-bit rows, L <= 32);
     // d = 128 in two passes of 64 value columns (16-bit rows, L <= 32, P <= 4)
     const bool fusable = dt != RACE_F32 && Lv <= 32;
-    const bool wide = false && d == 2 * race::HD && fusable && P <= race::NP;
+    const bool wide = d == 2 * race::HD && fusable && P <= race::NP;
     if (d != race::HD && !(d == 32 && fusable) && !wide) return RACE_ERR_UNSUPPORTED;
     if (P != race::NP && dt == RACE_F32) return RACE_ERR_UNSUPPORTED;
     if (chunk < 0 || chunk % race::CH != 0) return RACE_ERR_CHUNK;

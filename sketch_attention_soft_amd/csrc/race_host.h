@@ -410,9 +410,12 @@ template <typename T>
 void launch_hash_rows(const Tracer &tr, const char *name, const Plan &p, const T *X, const float *W,
                       float tau, const race::HCache &h)
 {
-    const dim3 grid((unsigned)((p.N + race::WROWS - 1) / race::WROWS), (unsigned)p.BH);
+    // every tile the chunk kernels read, a tile per wave at a time; two
+    // workgroups per compute unit (the staged W takes 70 KB of LDS)
+    const int64_t items = p.hc_tiles * p.BH;
+    const dim3 grid((unsigned)std::min<int64_t>((items + 3) / 4, 512));
     LAUNCH(tr, name, race::hash_rows_kernel<T>, grid, dim3(256), X, p.N, p.d, W, p.L, p.P, 1.0f / tau,
-           2 * p.nw, p.hc_tiles, h.t, h.c);
+           2 * p.nw, p.hc_tiles, p.BH, h.t, h.c);
 }
 
 template <typename T, int NW>
@@ -478,7 +481,8 @@ void launch_backward_wide(const Plan &p, const T *Q, const T *K, const T *V, con
             launch_walk<WS, CAUSAL != 0, true, 1, 0, D>(tr, "dv", nblk, sq, K, vd, W, p, sG, hk, hq, dV + c0,
                                                         nullptr);
         }
-        const dim3 rg((unsigned)((p.rows + race::WROWS - 1) / race::WROWS));
+        // blocks of 16 rows, one per wave at a time; four workgroups per compute unit
+        const dim3 rg((unsigned)std::min<int64_t>(((p.rows + race::WROWS - 1) / race::WROWS + 3) / 4, 1024));
         LAUNCH(tr, "du_rows_q", race::du_rows_kernel<T>, rg, dim3(256), Q, p.rows, p.d, W, p.L, p.P, WS * 16,
                du[0], du[1], dQ);
         LAUNCH(tr, "du_rows_k", race::du_rows_kernel<T>, rg, dim3(256), K, p.rows, p.d, W, p.L, p.P, WS * 16,

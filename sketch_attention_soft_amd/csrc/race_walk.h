@@ -174,14 +174,12 @@ __device__ __forceinline__ void bstf(float v, Rsrc r, int off)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
 
-#ifndef RACE_SETPRIO
-#define RACE_SETPRIO 0
-#endif
-// wave priority around a block of matrix products (mode m of RACE_SETPRIO)
-template <int M, int P> __device__ __forceinline__ void prio()
-{
-    if constexpr (RACE_SETPRIO == M) __builtin_amdgcn_s_setprio(P);
-}
+// Wave priority: the two waves of a SIMD leave a chunk's barrier together
+// and would reach their matrix-product blocks together; raising a wave's
+// priority for its products lets the other one issue its vector work in
+// between (measured: 2-3% off the walk kernels and the hashing sum, nothing
+// or worse on the gradient kernels, which do without).
+template <int P> __device__ __forceinline__ void prio() { __builtin_amdgcn_s_setprio(P); }
 
 // Keeps the loads issued above it in place: the scheduler would otherwise
 // sink prefetches towards the end of the loop body, next to their first use.
@@ -919,7 +917,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
             const VT vt = vt_expand<PV>(t, P);
             walsh_tm(vt.t, qw * vt.tau, ptm[tt][0], ptm[tt][1]);
         }
-        prio<1, 1>();
+        if constexpr (HASH) prio<1>();
         feat_major(ptm, sel, pfm);
         // tokens past the end have psi_0 = 1/4 but zero value rows
 #pragma unroll
@@ -928,7 +926,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) mma32(af[s][ct], pfm[s], yb);
         }
-        prio<1, 0>();
+        if constexpr (HASH) prio<0>();
         lds_barrier();
     });
     const int64_t blk = (bh * (nseg + 1) + sg) * (int64_t)(NW * 64 * NCOL);
@@ -1149,7 +1147,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
         lds_barrier();  // value columns and next rows staged; partial outputs of chunk ci - 1 in LDS
         finish(ci - 1, b ^ 1);  // (none before the first chunk: its stores are dropped)
         __builtin_amdgcn_sched_barrier(0);
-        prio<2, 1>();
+        prio<1>();
         // the next chunk's reader features, computed beside this chunk's
         // products (past the last chunk: nothing is read or stored)
         if constexpr (PIPE) reader_feats(ci + 1, xbuf[b ^ 1], kbuf[b ^ 1], prc);
@@ -1193,7 +1191,6 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             sel_lds(sl, sel);
             feat_major(pw, sel, pfm);
         }
-        prio<1, 1>();
         // O^T tiles (tt, ct): lane (columns 16 ct + 4g + r, token 16 tt + c16)
         floatx4 oacc[2][NT];
 #pragma unroll
@@ -1226,7 +1223,6 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
-        prio<1, 0>();
         float *rn = red + b * (REDN + REDM), *rm = rn + REDN;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1237,7 +1233,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             // 0..15 (the other lanes' values are not read)
             if (!BWD) rm[(w * 2 + tt) * 64 + lane] = oacc[tt][4][0];
         }
-        prio<2, 0>();
+        prio<0>();
     });
     if (nch > 0) {
         lds_barrier();
@@ -1490,7 +1486,6 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             feat_major(pw, sel, pfm);
         }
         lds_barrier();  // value rows of this chunk; du and rows of ci - 1; dots of ci - 2
-        prio<2, 1>();
         if constexpr (!DUO) {
             finish(ci - 2, b);  // (branch-free: before the first chunks the stores are dropped)
             // this chunk's raw rows (the buffer was last read by dxh of ci - 2)
@@ -1543,7 +1538,6 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
         }
         // inter-chunk part with the state before this chunk (consecutive
         // products go to the two token tiles' independent accumulators)
-        prio<1, 1>();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             bf16x8 sa[3];
@@ -1570,7 +1564,6 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 for (int s = 0; s < 4; ++s) mma32(acc[s][ct], ya, pfm[s]);
             }
         }
-        prio<1, 0>();
         // Walsh gradient -> du of this wave's 16 hyperplanes (token-major, LDS)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1596,7 +1589,6 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
                 if (ci >= 1) dw_tiles(b ^ 1);
             }
         }
-        prio<2, 0>();
     }
     if (!DUO && nch > 0) {
         const int pl = (nch - 1) & 1;  // buffers of the last chunk

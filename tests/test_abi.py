@@ -92,7 +92,9 @@ def test_workspace_sizes(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), E_SHAPE), (dict(H=-1), E_SHAPE), (dict(N=0), E_SHAPE), (dict(L=0), E_SHAPE),
-    (dict(d=48), E_UNSUP), (dict(d=128), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
+    (dict(d=48), E_UNSUP), (dict(d=96), E_UNSUP), (dict(d=128, dt=F32), E_UNSUP),
+    (dict(d=128, L=33), E_UNSUP), (dict(d=128, P=5), E_UNSUP), (dict(d=128, bwd=2), E_UNSUP),
+    (dict(d=256), E_UNSUP), (dict(d=32, dt=F32), E_UNSUP),
     (dict(d=32, L=33), E_UNSUP), (dict(P=7), E_UNSUP), (dict(P=3, dt=F32), E_UNSUP),
     (dict(P=5, dt=F32), E_UNSUP), (dict(P=6, d=32), E_UNSUP), (dict(P=6, L=129), E_UNSUP),
     (dict(P=0), E_SHAPE), (dict(L=129), E_UNSUP), (dict(L=129, dt=F32), E_UNSUP),
@@ -102,6 +104,21 @@ def test_workspace_sizes(lib):
 ])
 def test_workspace_validation(lib, kw, code):
     assert ws_bytes(lib, **kw)[0] == code
+
+
+def test_head_dim_128(lib):
+    """d = 128 on 16-bit rows (up to 32 tables, P <= 4): two passes of 64 value
+    columns; the backward keeps du of both passes, so it needs more room than
+    d = 64, and nothing is saved between the passes."""
+    for dt in (BF16, F16):
+        for L in (1, 8, 32):
+            for bwd in (0, 1):
+                st, b = ws_bytes(lib, d=128, L=L, dt=dt, bwd=bwd, N=3000)
+                assert st == OK and b > 0, (dt, L, bwd)
+        assert ws_bytes(lib, d=128, dt=dt, bwd=1, N=3000)[1] > ws_bytes(lib, d=64, dt=dt, bwd=1, N=3000)[1]
+    out = ctypes.c_size_t(7)
+    assert lib.race_attn_saved_bytes(1, 1, 3000, 128, 8, 4, 1, 0, BF16, ctypes.byref(out)) == OK
+    assert out.value == 0
 
 
 def test_virtual_tables(lib):
@@ -229,7 +246,9 @@ def test_forward_validation(lib):
     assert fwd(lib, ptrs=(None,) + (FAKE,) * 6) == E_NULL
     assert fwd(lib, ws=None) == E_NULL
     assert fwd(lib, N=0) == E_SHAPE
-    assert fwd(lib, d=128) == E_UNSUP
+    assert fwd(lib, d=96) == E_UNSUP
+    assert fwd(lib, d=128, dt=F32) == E_UNSUP
+    assert fwd(lib, d=128, L=33) == E_UNSUP
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         assert fwd(lib, tau=bad) == E_TAU
     assert fwd(lib, chunk=24) == E_CHUNK
@@ -427,6 +446,9 @@ def test_backward_dw_validation(lib):
     bad[15] = F32
     assert fn(*bad) == E_UNSUP
     bad = list(args)
+    bad[14] = 128  # d = 128: no dW
+    assert fn(*bad) == E_UNSUP
+    bad = list(args)
     bad[22] = 16  # workspace too small
     assert fn(*bad) == E_WS
 
@@ -463,6 +485,9 @@ def test_padded_validation(lib):
     bad = list(args)
     bad[18] = 16  # workspace too small
     assert fwd(*bad) == E_WS
+    bad = list(args)
+    bad[11] = 128  # d = 128: dense heads only
+    assert fwd(*bad) == E_UNSUP
     bwd = lib.race_attn_backward_padded
     bwd.argtypes = [vp] * 7 + [i32, i32, f32, i32, i32, i32, i64, i32, i32, i32, vp, vp, vp, vp,
                                vp, vp, sz, vp]
@@ -533,6 +558,8 @@ def test_hard_forward_workspace(lib):
         assert sz.value >= 2 * 2 * 4096 * Lt * 2 ** (P - 4)
     for (Lt, P, dt) in ((17, 5, BF16), (9, 6, BF16), (8, 5, F32), (8, 7, BF16)):
         assert ws(1, 1, 4096, 64, Lt, P, 1, 0, dt, 4, ctypes.byref(sz)) == E_UNSUP
+    # d = 128: the soft path only
+    assert ws(1, 1, 4096, 128, 8, 4, 1, 0, BF16, 4, ctypes.byref(sz)) == E_UNSUP
     # fp32 rows: the soft kernels with t = +-1, the forward's workspace
     assert ws(1, 1, 4096, 64, 8, 4, 1, 0, F32, 4, ctypes.byref(sz)) == OK
     hard = sz.value
@@ -550,6 +577,7 @@ def test_varlen_validation(lib):
     # B = 2, H = 1, T = 100, max_seqlen = 60
     assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 64, BF16, 0, None, F, F, F, 1 << 40, None) == E_NULL
     assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 64, F32, 0, F, F, F, F, 1 << 40, None) == E_UNSUP
+    assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 128, BF16, 0, F, F, F, F, 1 << 40, None) == E_UNSUP
     assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 121, 60, 64, BF16, 0, F, F, F, F, 1 << 40, None) == E_SHAPE
     assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 0, 60, 64, BF16, 0, F, F, F, F, 1 << 40, None) == E_SHAPE
     assert f(F, F, F, F, 8, 4, 1.0, 1, 2, 1, 100, 60, 64, BF16, 0, F, F, F, F, 16, None) == E_WS
