@@ -51,8 +51,8 @@
  *     up to the table's; the work of L 2^(P-4) tables of P = 4, in passes of
  *     32) and d = 128 with L <= 32, P <= 4 (the rows are hashed once over all
  *     128 elements, then the chunk kernels run on value columns 0..63 and
- *     64..127; no saved state: race_attn_saved_bytes gives 0, and the
- *     backward rehashes),
+ *     64..127; the saved buffer keeps the hash features of Q and K, without
+ *     it the backward rehashes),
  *     any B, H, N >= 1 (int64 offsets), tau finite and > 0.
  *   - chunk: tokens per scan segment, 0 = the library chooses; otherwise a
  *     multiple of 16.  It changes only the order of the floating-point sums.

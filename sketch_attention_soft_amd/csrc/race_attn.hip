@@ -115,8 +115,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
         // forward: the segment states, the scan's totals, t of K and of Q;
         // backward: key and gradient states, the scan's totals, t and dt/du
         // of K and of Q, du of Q and K for both passes, the values' last
-        // column.  No saved state (the backward rehashes: one pass over the
-        // rows) and no dW.
+        // column.  The saved buffer keeps t and dt/du of K and Q (the
+        // backward rehashes without it); no dW.
         p->w_du_bytes = align256((size_t)p->rows * (2 * p->nw) * 16 * sizeof(bf16));
         p->f_st = 0;
         p->f_scan = p->f_st + p->st_bytes;
@@ -130,7 +130,8 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
         p->w_dm = p->w_du + 4 * p->w_du_bytes;
         p->b_total = p->w_dm + align256((size_t)p->rows * sizeof(float));
         p->dw_total = 0;
-        p->s_total = 0;
+        p->s_hc = 0;
+        p->s_total = 4 * p->hc_bytes;
     }
     if (Lv > 32) {
         // passes over tables 0..31, 32..63, ... (split_passes; the fused
@@ -456,7 +457,7 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
     p.lens.cu = cu;
     p.lens.T = T;
     // (the saved state is the fused kernels'; fp32 rows recompute)
-    float *sv = (p.fused || p.split) && dt != RACE_F32 ? static_cast<float *>(saved) : nullptr;
+    float *sv = (p.fused || p.split || p.wide) && dt != RACE_F32 ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
@@ -498,7 +499,7 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
     p.lens.len = lens;
     p.lens.cu = cu;
     p.lens.T = T;
-    const float *sv = (p.fused || p.split) && dt != RACE_F32 ? static_cast<const float *>(saved) : nullptr;
+    const float *sv = (p.fused || p.split || p.wide) && dt != RACE_F32 ? static_cast<const float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);

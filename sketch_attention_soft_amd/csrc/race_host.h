@@ -418,9 +418,10 @@ void launch_hash_rows(const Tracer &tr, const char *name, const Plan &p, const T
            2 * p.nw, p.hc_tiles, p.BH, h.t, h.c);
 }
 
+// saved (optional): t and dt/du of K and Q, kept for the backward
 template <typename T, int NW>
 void launch_forward_wide(const Plan &p, const T *Q, const T *K, const T *V, const float *W, float tau,
-                         int causal, T *O, float *den, char *ws, const Tracer &tr)
+                         int causal, T *O, float *den, char *ws, float *saved, const Tracer &tr)
 {
     if constexpr (sizeof(T) == 2) {
         constexpr int WS = 2 * NW, D = 2 * race::HD;
@@ -428,7 +429,9 @@ void launch_forward_wide(const Plan &p, const T *Q, const T *K, const T *V, cons
         const dim3 nblk((unsigned)(p.BH * p.nseg));
         float *st = reinterpret_cast<float *>(ws + p.f_st);
         float *scan_tmp = reinterpret_cast<float *>(ws + p.f_scan);
-        const race::HCache hk = hcache(p, ws + p.f_hc, 0, -1), hq = hcache(p, ws + p.f_hc, 1, -1);
+        char *sb = reinterpret_cast<char *>(saved);
+        const race::HCache hk = saved ? hcache(p, sb + p.s_hc, 0, 1) : hcache(p, ws + p.f_hc, 0, -1);
+        const race::HCache hq = saved ? hcache(p, sb + p.s_hc, 2, 3) : hcache(p, ws + p.f_hc, 1, -1);
         const race::HCache none = hcache(p, nullptr, -1, -1);
         launch_hash_rows(tr, "hash_k", p, K, W, tau, hk);
         launch_hash_rows(tr, "hash_q", p, Q, W, tau, hq);
@@ -444,10 +447,11 @@ void launch_forward_wide(const Plan &p, const T *Q, const T *K, const T *V, cons
     }
 }
 
+// saved (optional): the forward's t and dt/du of K and Q (else rehashed)
 template <typename T, int NW, int CAUSAL>
 void launch_backward_wide(const Plan &p, const T *Q, const T *K, const T *V, const float *W, const T *O,
                           const float *den, const T *dO, float tau, T *dQ, T *dK, T *dV, char *ws,
-                          const Tracer &tr)
+                          const float *saved, const Tracer &tr)
 {
     if constexpr (sizeof(T) == 2) {
         constexpr int WS = 2 * NW, D = 2 * race::HD;
@@ -456,14 +460,17 @@ void launch_backward_wide(const Plan &p, const T *Q, const T *K, const T *V, con
         float *sS = reinterpret_cast<float *>(ws + p.b_s);
         float *sG = reinterpret_cast<float *>(ws + p.b_g);
         float *scan_tmp = reinterpret_cast<float *>(ws + p.b_scan);
-        const race::HCache hk = hcache(p, ws + p.b_hc, 0, 1), hq = hcache(p, ws + p.b_hc, 2, 3);
+        char *hb = saved ? const_cast<char *>(reinterpret_cast<const char *>(saved)) + p.s_hc : ws + p.b_hc;
+        const race::HCache hk = hcache(p, hb, 0, 1), hq = hcache(p, hb, 2, 3);
         const race::HCache none = hcache(p, nullptr, -1, -1);
         // du of Q for passes 0, 1, then of K
         bf16 *du[4];
         for (int i = 0; i < 4; ++i) du[i] = reinterpret_cast<bf16 *>(ws + p.w_du + i * p.w_du_bytes);
         float *dm = reinterpret_cast<float *>(ws + p.w_dm);
-        launch_hash_rows(tr, "hash_k_chain", p, K, W, tau, hk);
-        launch_hash_rows(tr, "hash_q_chain", p, Q, W, tau, hq);
+        if (!saved) {
+            launch_hash_rows(tr, "hash_k_chain", p, K, W, tau, hk);
+            launch_hash_rows(tr, "hash_q_chain", p, Q, W, tau, hq);
+        }
         LAUNCH(tr, "dm_rows", race::dm_rows_kernel<T>, dim3((unsigned)((p.rows + race::WROWS - 1) / race::WROWS)),
                dim3(256), dO, O, den, p.rows, p.d, dm);
         for (int pass = 0; pass < 2; ++pass) {
@@ -502,9 +509,9 @@ void dispatch_forward(const Plan &p, const void *Q, const void *K, const void *V
     if constexpr (sizeof(T) == 2) {
         if (p.wide) {
             switch (p.nw) {
-            case 1: launch_forward_wide<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
-            case 2: launch_forward_wide<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
-            default: launch_forward_wide<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, tr); break;
+            case 1: launch_forward_wide<T, 1>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+            case 2: launch_forward_wide<T, 2>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
+            default: launch_forward_wide<T, 4>(p, q, k, v, W, tau, causal, o, den, ws, saved, tr); break;
             }
             return;
         }
@@ -544,9 +551,9 @@ void dispatch_backward(const Plan &p, const void *Q, const void *K, const void *
             auto run = [&](auto nw_c) {
                 constexpr int NW = decltype(nw_c)::value;
                 if (causal)
-                    launch_backward_wide<T, NW, 1>(p, q, k, v, W, o, den, go, tau, dq, dk, dv, ws, tr);
+                    launch_backward_wide<T, NW, 1>(p, q, k, v, W, o, den, go, tau, dq, dk, dv, ws, saved, tr);
                 else
-                    launch_backward_wide<T, NW, 0>(p, q, k, v, W, o, den, go, tau, dq, dk, dv, ws, tr);
+                    launch_backward_wide<T, NW, 0>(p, q, k, v, W, o, den, go, tau, dq, dk, dv, ws, saved, tr);
             };
             switch (p.nw) {
             case 1: run(std::integral_constant<int, 1>{}); break;

@@ -109,7 +109,7 @@ def test_workspace_validation(lib, kw, code):
 def test_head_dim_128(lib):
     """d = 128 on 16-bit rows (up to 32 tables, P <= 4): two passes of 64 value
     columns; the backward keeps du of both passes, so it needs more room than
-    d = 64, and nothing is saved between the passes."""
+    d = 64; the saved buffer holds the hash features of Q and K only."""
     for dt in (BF16, F16):
         for L in (1, 8, 32):
             for bwd in (0, 1):
@@ -118,7 +118,9 @@ def test_head_dim_128(lib):
         assert ws_bytes(lib, d=128, dt=dt, bwd=1, N=3000)[1] > ws_bytes(lib, d=64, dt=dt, bwd=1, N=3000)[1]
     out = ctypes.c_size_t(7)
     assert lib.race_attn_saved_bytes(1, 1, 3000, 128, 8, 4, 1, 0, BF16, ctypes.byref(out)) == OK
-    assert out.value == 0
+    s128 = out.value
+    assert lib.race_attn_saved_bytes(1, 1, 3000, 64, 8, 4, 1, 0, BF16, ctypes.byref(out)) == OK
+    assert 0 < s128 < out.value  # no key state
 
 
 def test_virtual_tables(lib):

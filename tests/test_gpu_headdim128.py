@@ -66,9 +66,27 @@ def test_headdim128_forward_backward(case):
     _compare("dv", to_host64(dv), ref[4], dtype)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_headdim128_saved_features(causal):
+    """With the forward's saved buffer the backward reads the hash features
+    instead of rehashing: the same gradients, bit for bit."""
+    B, H, N, L, tau = 1, 2, 1300, 16, 1.0
+    x = I.make_inputs(B, H, N, 128, L, 4, "bf16", 12870 + causal, with_grad=True)
+    dx = device_inputs(x, "bf16")
+    print(f"[case] d=128 saved causal={causal}", flush=True)
+    sv = binding.new_saved(dx["q"], dx["W"], causal, 0)
+    assert sv is not None
+    o, den = binding.forward(dx["q"], dx["k"], dx["v"], dx["W"], tau, causal, saved=sv)
+    a = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau, causal, saved=sv)
+    b = binding.backward(dx["q"], dx["k"], dx["v"], dx["W"], o, den, dx["do"], tau, causal)
+    torch.cuda.synchronize()
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
+
+
 def test_headdim128_autograd():
-    """The autograd wrapper (which keeps a saved state for d = 64) runs d = 128
-    heads too: the library recomputes what it would have kept."""
+    """The autograd wrapper (forward with a saved buffer, then the backward)
+    on d = 128 heads."""
     B, H, N, L, tau = 1, 1, 900, 8, 1.0
     x = I.make_inputs(B, H, N, 128, L, 4, "bf16", 12899, with_grad=True)
     dx, hx = device_inputs(x, "bf16"), host_inputs(x, "bf16")
