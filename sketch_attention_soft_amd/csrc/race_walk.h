@@ -1286,7 +1286,10 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
     __shared__ __attribute__((aligned(16))) bf16 yrow_w[2][CAUSAL ? WCT * YRS : 8];
     __shared__ __attribute__((aligned(16))) bf16 ycol_w[2][CAUSAL ? NCOL * YCS : 8];
     __shared__ __attribute__((aligned(16))) bf16 du_l[2][WCT * DUS];
-    __shared__ __attribute__((aligned(16))) float dotp[2][WCT * 16];  // partial x . dxh [token][nt][g]
+    // partial x . dxh [token][nt][g]; rows of 20 words, so that the 16 tokens
+    // of a tile fall in different banks (rows of 16 put them in 2)
+    constexpr int DPS = 20;
+    __shared__ __attribute__((aligned(16))) float dotp[2][WCT * DPS];
     __shared__ __attribute__((aligned(16))) bf16 wt_l[HD * WTS];     // W^T (bf16): [dim][hyperplane]
     // this block's dW as [hyperplane / 4][column][hyperplane % 4]: a lane's
     // four accumulator values are one 16-byte word (each wave owns its rows)
@@ -1402,7 +1405,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             float dot = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dot = fmaf(xa[r], (float)xv[r], dot);
-            dotp[pb][tok * 16 + nt * 4 + g] = dot;
+            dotp[pb][tok * DPS + nt * 4 + g] = dot;
             dxh[i] = xa;
             xkeep[i] = xv;
             sskeep[i] = kbuf[pb][tok];
@@ -1443,7 +1446,7 @@ __global__ __launch_bounds__(NW * 64) void grad_kernel(
             float dot = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const floatx4 v = *reinterpret_cast<const floatx4 *>(dotp[pb] + tok * 16 + 4 * q);
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(dotp[pb] + tok * DPS + 4 * q);
                 dot += (v[0] + v[1]) + (v[2] + v[3]);
             }
             const float ss = sskeep[i];
