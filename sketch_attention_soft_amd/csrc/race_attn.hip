@@ -60,10 +60,12 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     const int64_t n16 = (N + 15) / 16 * 16;
     int64_t seg = chunk;
     if (seg == 0) {
-        // one workgroup per compute unit (MI355X: 256 CUs; every segment
-        // kernel keeps one workgroup per CU resident), segments >= 32 tokens
-        // (short sequences: more, shorter segments, for latency)
-        const int64_t want = (p->rows + 255) / 256;
+        // one round of workgroups over the compute units (MI355X: 256 CUs):
+        // one 8-wave workgroup per CU (32 tables), two 4-wave ones (16
+        // tables), four 2-wave ones; segments >= 32 tokens (short sequences:
+        // more, shorter segments, for latency)
+        const int64_t wgs = 256 * (4 / std::min(p->nw, 4));
+        const int64_t want = (p->rows + wgs - 1) / wgs;
         seg = (want + 31) / 32 * 32;
         if (seg < 32) seg = 32;
     }

@@ -823,7 +823,7 @@ __device__ __forceinline__ void hc_store(Rsrc r, int tt, const halfx4 &v)
 //            dt/du' into the cache `co`.
 //   SRC = 1: t comes from the cache `ci_` (X is not read).
 template <int NW, bool DVAL, int SRC, int WR, bool POLY, typename IO, int D, bool PV = false>
-__global__ __launch_bounds__(NW * 64) void sum_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void sum_kernel(
     const IO *__restrict__ X, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, HCache ci_, HCache co, float *__restrict__ st, Lens ls)
 {
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(NW * 64) void sum_kernel(
 // of chunk c + 1, beside that chunk's products.
 template <int NW, bool CAUSAL, bool BWD, int RSRC, int RWR, bool POLY, typename IO, int D,
           int PART = PART_NONE, bool PV = false>
-__global__ __launch_bounds__(NW * 64) void walk_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void walk_kernel(
     const IO *__restrict__ R, ValSrc<IO> vsrc, const float *__restrict__ W, int L, int P, Squash sq,
     int64_t N, int seg, int64_t nseg, const float *__restrict__ st, HCache rc, HCache wc,
     IO *__restrict__ Out, float *__restrict__ den, Lens ls, Part part)
@@ -966,13 +966,20 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     constexpr int RIT = (RSLOTS + NTHR - 1) / NTHR;
     constexpr int REDN = NW * 2 * 4 * 64 * 4;  // partial outputs: value columns (4 tiles) of every wave
     constexpr int REDM = NW * 2 * 64;          // and their count column
+    // Workgroups of 8 waves fill a compute unit (two waves per SIMD at up to
+    // 256 registers) and double-buffer the partial outputs, so that a chunk
+    // needs one barrier.  Narrower workgroups (fewer tables) run two or more
+    // per compute unit, which LDS allows only with one buffer: the chunk then
+    // takes a second barrier before it overwrites the sums the previous
+    // chunk's finish reads.
+    constexpr int NRED = NW >= 8 ? 2 : 1;
     __shared__ __attribute__((aligned(16))) bf16 xbuf[2][HASH ? WCT * XRS : 8];
     __shared__ __attribute__((aligned(16))) float kbuf[2][WCT];
     __shared__ __attribute__((aligned(16))) bf16 ycol[2][CAUSAL ? NCOL * YCS : 8];
-    // [2][REDN + REDM]; before the loop the forward's W rows are staged here
-    __shared__ __attribute__((aligned(16))) float red[2 * (REDN + REDM)];
+    // [NRED][REDN + REDM]; before the loop the forward's W rows are staged here
+    __shared__ __attribute__((aligned(16))) float red[NRED * (REDN + REDM)];
     __shared__ __attribute__((aligned(16))) bf16 sl[2 * 64 * 8];
-    static_assert(!HASH || 2 * NW * 16 * XRS * 2 <= 2 * (REDN + REDM) * 4, "W rows fit the partial-output buffer");
+    static_assert(!HASH || 2 * NW * 16 * XRS * 2 <= NRED * (REDN + REDM) * 4, "W rows fit the partial-output buffer");
 
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
@@ -1075,7 +1082,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
     // or dV = n.  Thread slot: token tile tt, column tile ct, lane (g, c16).
     auto finish = [&](int ci, int pb) {
         const Chunk c = chunk(ci);
-        const float *rn = red + pb * (REDN + REDM), *rm = rn + REDN;
+        const float *rn = red + (NRED == 2 ? pb : 0) * (REDN + REDM), *rm = rn + REDN;
         const Rsrc ro = row_res<D>(Os, c);
 #pragma unroll
         for (int it = 0; it < RIT; ++it) {
@@ -1223,7 +1230,8 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
-        float *rn = red + b * (REDN + REDM), *rm = rn + REDN;
+        if constexpr (NRED == 1) lds_barrier();  // every finish(ci - 1) has read the sums
+        float *rn = red + (NRED == 2 ? b : 0) * (REDN + REDM), *rm = rn + REDN;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -1265,7 +1273,7 @@ __global__ __launch_bounds__(NW * 64) void walk_kernel(
 // normalisation backward over the whole row.
 template <int NW, bool CAUSAL, bool REVERSE, bool DW, typename IO, int D, int PART = PART_NONE,
           bool PV = false>
-__global__ __launch_bounds__(NW * 64) void grad_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void grad_kernel(
     const IO *__restrict__ Xr, ValSrc<IO> vr_src, ValSrc<IO> vw_src,
     const float *__restrict__ W, int L, int P, int64_t N, int seg, int64_t nseg,
     const float *__restrict__ st, HCache rc, HCache wc, IO *__restrict__ dX,

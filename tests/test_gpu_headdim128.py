@@ -58,7 +58,7 @@ def test_headdim128_forward_backward(case):
     assert e_den.max() <= ROW_TOL[dtype]
     if N == 1:
         for g in (dq, dk):
-            assert np.linalg.norm(to_host64(g)) <= TOL[dtype] * np.linalg.norm(ref[4])
+            assert np.linalg.norm(to_host64(g)) <= 2 * TOL[dtype] * np.linalg.norm(ref[4])
     else:
         _compare("dq", to_host64(dq), ref[2], dtype, _row_norms(hx["q"]),
                  vanishing=(0,) if causal else ())

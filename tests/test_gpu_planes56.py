@@ -65,7 +65,7 @@ def test_planes56_forward_backward(case):
     if N == 1:
         # one token: o = v and the exact dQ, dK vanish (rounding noise on dV's scale)
         for g in grads[:2]:
-            assert np.linalg.norm(to_host64(g)) <= TOL[dtype] * np.linalg.norm(ref[4])
+            assert np.linalg.norm(to_host64(g)) <= 2 * TOL[dtype] * np.linalg.norm(ref[4])
     else:
         _compare("dq", to_host64(grads[0]), ref[2], dtype, _row_norms(hx["q"]),
                  vanishing=(0,) if causal else ())

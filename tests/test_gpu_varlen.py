@@ -25,6 +25,10 @@ CASES = [
     ("f16", 64, 1, 32, 4, 0.5, (4133, 64, 300)),
     ("bf16", 32, 2, 16, 3, 1.0, (257, 1500)),
     ("bf16", 64, 1, 64, 4, 1.0, (900, 0, 1201)),
+    # P = 5, 6: virtual tables (one pass, and two passes of 32)
+    ("bf16", 64, 1, 8, 6, 1.0, (700, 1, 1300)),
+    ("f16", 64, 2, 12, 5, 0.5, (333, 2000)),
+    ("bf16", 64, 1, 12, 6, 1.0, (600, 1111)),
 ]
 
 
@@ -65,7 +69,11 @@ def test_varlen_against_oracle_and_padded(case, causal):
             fr = ref["dv"] if n in ("dq", "dk") else None
             e = head_relf(g, ref[n], floor_ref=fr, floor=1.0 if s1 - s0 == 1 else 1e-3)
             assert np.all(np.isfinite(g)), (b, n)
-            assert e <= TOL[dtype], (b, n, e)
+            # one token: the exact dq, dk vanish and what is measured is
+            # rounding noise on dv's scale, which grows with the features
+            # (2.0e-2 at P = 6): twice the bar
+            bar = 2 * TOL[dtype] if s1 - s0 == 1 and fr is not None else TOL[dtype]
+            assert e <= bar, (b, n, e)
             if s1 - s0 > 1:
                 er = row_errors(g, ref[n], GRAD_FLOOR if n in ("dq", "dk") else ROW_FLOOR,
                                 vanishing=(0,) if n == "dq" and causal else ())
