@@ -147,6 +147,18 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Wait until every global load and store this wave has issued is complete.
+// Placed before a chunk loop: memory operations complete in order, and where
+// the prologue issues its loads in another order than the loop body, the
+// compiler's wait at the loop head has to cover both paths and becomes a wait
+// for everything outstanding -- in every iteration, the prefetch of the next
+// chunk's rows included.  With nothing outstanding on entry, the waits inside
+// the loop follow the loop's own issue order.
+__device__ __forceinline__ void vm_drain()
+{
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt, lgkmcnt unchanged
+}
+
 // Rows of head bh = b H + h that exist: N, or for right-padded batches the
 // length of its batch, len[b] clamped to [0, N] (rows past it are neither
 // read nor written: the sums skip them and their outputs are left as they

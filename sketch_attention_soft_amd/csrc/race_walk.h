@@ -883,6 +883,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sum_kernel(
     if (HASH) xstage_load<NTHR, false, D>(row_res<D>(Xs, c1), xs);
     ystage_load<NTHR, DVAL, D>(yres<DVAL, D>(vh, c1), ys);
     lds_barrier();
+    vm_drain();
     for_chunks2(nch, [&](int ci, auto par) {
         constexpr int b = decltype(par)::v;
         const Chunk cc = chunk(ci);
@@ -1128,6 +1129,7 @@ __global__ __launch_bounds__(NW * 64, 2) void walk_kernel(
         }
     };
 
+    vm_drain();
     for_chunks2(nch, [&](int ci, auto par) {
         constexpr int b = decltype(par)::v;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
@@ -1473,6 +1475,7 @@ __global__ __launch_bounds__(NW * 64, 2) void grad_kernel(
     // normalisation backward of chunk ci - 2 (whose dots are complete), chunk
     // ci's rows and products, and last dxh of chunk ci - 1 (whose du is
     // complete).
+    vm_drain();
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
