@@ -232,11 +232,13 @@ typedef struct {
 } race_trace_t;
 
 /* Size, in bytes, of the state that race_attn_forward_ex can save for
- * race_attn_backward_ex: the per-segment prefix sums of the keys' bucket
- * statistics with the per-head totals (step 3 / zh §2.3, fp32), and the
- * squashed projections t of Q and K with their derivatives (steps 1-2, fp16,
- * 512 bytes per row of Q and of K at L = 32).  0 when the configuration does
- * not use it (RACE_F32).  Pure host function. */
+ * race_attn_backward_ex.  16-bit rows: the per-segment prefix sums of the
+ * keys' bucket statistics with the per-head totals (step 3 / zh §2.3, fp32),
+ * and the squashed projections t of Q and K with their derivatives (steps
+ * 1-2, fp16, 512 bytes per row of Q and of K at L = 32).  RACE_F32 rows: t
+ * and its derivative of Q and of K in fp32 (1024 bytes per row of each at
+ * L = 32); the fp32 backward keeps the key statistics in another layout and
+ * sums them again.  Pure host function. */
 race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P, int causal,
                                     int chunk, race_dtype_t dt, size_t *bytes);
 
@@ -247,8 +249,8 @@ race_status_t race_attn_saved_bytes(int B, int H, int64_t N, int d, int L, int P
  *     owned by the caller) or NULL.  The forward writes the state there
  *     (its outputs are the same either way); a backward given the same
  *     buffer, for the same Q, K, V, W, tau, causal and chunk, reads it
- *     instead of recomputing it (the gradients agree to rounding).  Ignored
- *     when race_attn_saved_bytes is 0.  A misaligned saved buffer is
+ *     instead of recomputing it (the gradients agree to rounding; bitwise
+ *     for RACE_F32 rows).  Ignored when race_attn_saved_bytes is 0.  A misaligned saved buffer is
  *     RACE_ERR_WORKSPACE.
  * With trace = NULL and saved = NULL these are exactly the plain entry
  * points. */

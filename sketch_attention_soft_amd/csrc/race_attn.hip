@@ -96,7 +96,10 @@ race_status_t make_plan(int B, int H, int64_t N, int d, int L, int P, int chunk,
     p->f_scan = p->f_hc + p->hc_bytes;
     p->f_total = p->f_scan + p->scan_bytes;
     p->s_hc = p->st_bytes;
-    p->s_total = p->fused ? p->s_hc + 4 * p->hc_bytes : 0;
+    // saved state: the key state and the fp16 hash features of Q and K (fused
+    // path); t and dt/du' of Q and of K in fp32 (fp32 rows, whose backward
+    // reads them instead of hashing again)
+    p->s_total = p->fused ? p->s_hc + 4 * p->hc_bytes : dt == RACE_F32 ? 2 * p->tb_bytes : 0;
     p->b_tq = 0;
     p->b_tk = p->b_tq + p->tb_bytes;
     p->b_s = p->b_tk + p->tb_bytes;
@@ -458,8 +461,7 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
     p.lens.len = lens;
     p.lens.cu = cu;
     p.lens.T = T;
-    // (the saved state is the fused kernels'; fp32 rows recompute)
-    float *sv = (p.fused || p.split || p.wide) && dt != RACE_F32 ? static_cast<float *>(saved) : nullptr;
+    float *sv = p.s_total > 0 ? static_cast<float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
@@ -468,7 +470,7 @@ static race_status_t forward_impl(const void *Q, const void *K, const void *V, c
     else if (p.split && dt == RACE_F16)
         split_forward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else if (p.split)
-        split_forward<float>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, nullptr, tr);
+        split_forward<float>(p, B, H, chunk, dt, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else if (dt == RACE_BF16)
         dispatch_forward<bf16>(p, Q, K, V, W, tau, causal, O, den, ws, sv, tr);
     else if (dt == RACE_F16)
@@ -501,7 +503,7 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
     p.lens.len = lens;
     p.lens.cu = cu;
     p.lens.T = T;
-    const float *sv = (p.fused || p.split || p.wide) && dt != RACE_F32 ? static_cast<const float *>(saved) : nullptr;
+    const float *sv = p.s_total > 0 ? static_cast<const float *>(saved) : nullptr;
     const Tracer tr{trace, static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();
     char *ws = static_cast<char *>(workspace);
@@ -511,8 +513,8 @@ static race_status_t backward_impl(const void *Q, const void *K, const void *V, 
         split_backward<_Float16>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr,
                                  dW);
     else if (p.split)
-        split_backward<float>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, nullptr,
-                              tr, nullptr);
+        split_backward<float>(p, B, H, chunk, dt, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr,
+                              nullptr);
     else if (dt == RACE_BF16)
         dispatch_backward<bf16>(p, Q, K, V, W, O, den, dO, tau, causal, dQ, dK, dV, ws, sv, tr, dW);
     else if (dt == RACE_F16)

@@ -281,19 +281,31 @@ void launch_forward(const Plan &p, const T *Q, const T *K, const T *V, const flo
         return;
     }
     if constexpr (!std::is_same<T, _Float16>::value && D == race::HD) {  // fp16 rows, d = 32: fused path only
-    LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
-    LAUNCH(tr, "hash_k", (race::hash_kernel<T, false>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
+    // fp32 rows: t of Q and K in the workspace, or t and dt/du' (the
+    // backward's chain rows, 8 floats per table) in the saved buffer
+    int ts = race::NP;
+    if (saved) {
+        tq = saved;
+        tk = reinterpret_cast<float *>(reinterpret_cast<char *>(saved) + p.tb_bytes);
+        ts = 2 * race::NP;
+        st = reinterpret_cast<float *>(ws + p.f_st);
+        LAUNCH(tr, "hash_q", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
+        LAUNCH(tr, "hash_k", (race::hash_kernel<T, true>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
+    } else {
+        LAUNCH(tr, "hash_q", (race::hash_kernel<T, false>), hg, b256, Q, p.rows, W, p.L, inv_tau, tq);
+        LAUNCH(tr, "hash_k", (race::hash_kernel<T, false>), hg, b256, K, p.rows, W, p.L, inv_tau, tk);
+    }
     const race::ValSrc<T> vs{V, nullptr, nullptr};
     const dim3 nblk((unsigned)(p.BH * p.nseg));
-    LAUNCH(tr, "seg_sum_kv", (race::seg_sum_kernel<T, NW, false, false>), nblk, bw, tk, race::NP,
+    LAUNCH(tr, "seg_sum_kv", (race::seg_sum_kernel<T, NW, false, false>), nblk, bw, tk, ts,
            vs, p.N, p.L, (int)p.seg, p.nseg, st, p.lens);
     launch_scan(tr, "scan_kv", p, st, scan_tmp, 0);
     if (causal)
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, true, false>), nblk, bw, tq, tk,
-               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens, p.part_o, p.part_mode);
+               ts, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens, p.part_o, p.part_mode);
     else
         LAUNCH(tr, "readout_o", (race::readout_kernel<T, NW, false, false>), nblk, bw, tq, tk,
-               race::NP, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens, p.part_o, p.part_mode);
+               ts, vs, p.N, p.L, (int)p.seg, p.nseg, st, O, den, p.lens, p.part_o, p.part_mode);
     }
 }
 
@@ -356,10 +368,16 @@ void launch_backward_body(const Plan &p, const T *Q, const T *K, const T *V, con
     if constexpr (!std::is_same<T, _Float16>::value && D == race::HD) {  // fp16 rows, d = 32: fused path only
     LAUNCH(tr, "prep_wt", race::prep_wt_kernel, dim3((race::HD * lp32 + 255) / 256), b256, W,
            p.LP, lp32, wt);
-    LAUNCH(tr, "hash_q_chain", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L,
-           inv_tau, tq);
-    LAUNCH(tr, "hash_k_chain", (race::hash_kernel<T, true>), hg, b256, K, p.rows, W, p.L,
-           inv_tau, tk);
+    // t and dt/du' of Q and K: the forward's saved rows, or hashed here
+    if (saved) {
+        tq = const_cast<float *>(saved);
+        tk = reinterpret_cast<float *>(reinterpret_cast<char *>(const_cast<float *>(saved)) + p.tb_bytes);
+    } else {
+        LAUNCH(tr, "hash_q_chain", (race::hash_kernel<T, true>), hg, b256, Q, p.rows, W, p.L,
+               inv_tau, tq);
+        LAUNCH(tr, "hash_k_chain", (race::hash_kernel<T, true>), hg, b256, K, p.rows, W, p.L,
+               inv_tau, tk);
+    }
     const race::ValSrc<T> vv{V, nullptr, nullptr};  // [v | 1]
     const race::ValSrc<T> vd{dO, O, den};           // [dO/m | -(dO.o)/m]
     const dim3 nblk((unsigned)(p.BH * p.nseg));
