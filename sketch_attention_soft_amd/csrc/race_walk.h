@@ -729,6 +729,82 @@ __device__ __forceinline__ void feat_major(const bf16x8 (&ptm)[2][2], const bf16
     }
 }
 
+// The same features of a writer row in fp16, formed from the fp16 t with
+// packed multiplies (two features per instruction, no conversion): feature
+// pairs (S, S + 1) differ in t_0 only, so pair m is g_m (1, t_0) with g_m the
+// product over the bits of S = 2m in t_1..t_3.  The selection product below
+// moves them to the feature-major operand, rounded there to bf16.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void walsh_tm16(const halfx4 &t, _Float16 q, halfx8 &lo, halfx8 &hi)
+{
+    const half2v u = half2v{q, q} * half2v{(_Float16)1.f, t[0]};  // S = 0, 1
+    const half2v p2 = u * t[1];                                    // S = 2, 3
+    const half2v p4 = u * t[2];                                    // S = 4, 5
+    const half2v p6 = p2 * t[2];                                   // S = 6, 7
+    const half2v p8 = u * t[3], p10 = p2 * t[3], p12 = p4 * t[3], p14 = p6 * t[3];
+    const halfx4 a = __builtin_shufflevector(u, p2, 0, 1, 2, 3), b = __builtin_shufflevector(p4, p6, 0, 1, 2, 3);
+    const halfx4 c = __builtin_shufflevector(p8, p10, 0, 1, 2, 3), e = __builtin_shufflevector(p12, p14, 0, 1, 2, 3);
+    lo = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    hi = __builtin_shufflevector(c, e, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ halfx8 selection16(int par)
+{
+    const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+    halfx8 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (g == (c16 >> 2) && i == 4 * par + (c16 & 3)) ? (_Float16)1.f : (_Float16)0.f;
+    return f;
+}
+__device__ __forceinline__ void feat_major16(const halfx8 (&ptm)[2][2], const halfx8 (&sel)[2], bf16x8 (&pfm)[4])
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        bf16x4 half[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            floatx4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ptm[tt][s >> 1], sel[s & 1], d, 0, 0, 0);
+            half[tt] = acc2bf4(d);
+        }
+        pfm[s] = cat8(half[0], half[1]);
+    }
+}
+// the fp16 selection operands, sl[2][64 lanes][8]
+__device__ __forceinline__ void stage_sel16(_Float16 *sl)
+{
+    if (threadIdx.x < 64) {
+        *reinterpret_cast<halfx8 *>(sl + threadIdx.x * 8) = selection16(0);
+        *reinterpret_cast<halfx8 *>(sl + (64 + threadIdx.x) * 8) = selection16(1);
+    }
+}
+__device__ __forceinline__ void sel_lds16(const _Float16 *sl, halfx8 (&sel)[2])
+{
+    sel[0] = *reinterpret_cast<const halfx8 *>(sl + lane_id() * 8);
+    sel[1] = *reinterpret_cast<const halfx8 *>(sl + (64 + lane_id()) * 8);
+}
+// Writer features of one chunk (two token tiles, cached or freshly hashed t)
+// in the feature-major layout of the state update.  P <= 4 take the fp16
+// route above; P > 4 (virtual tables, t moved between lanes) the fp32 one.
+template <bool PV>
+__device__ __forceinline__ void writer_fm(const halfx4 (&t)[2], int P, float qw, const bf16x8 (&sel)[2],
+                                          const halfx8 (&sel16)[2], bf16x8 (&pfm)[4])
+{
+    if constexpr (PV) {
+        bf16x8 ptm[2][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const VT vt = vt_expand<PV>(t[tt], P);
+            walsh_tm(vt.t, qw * vt.tau, ptm[tt][0], ptm[tt][1]);
+        }
+        feat_major(ptm, sel, pfm);
+    } else {
+        halfx8 ptm[2][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) walsh_tm16(t[tt], (_Float16)qw, ptm[tt][0], ptm[tt][1]);
+        feat_major16(ptm, sel16, pfm);
+    }
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane i receives element i % 4 of the 8-byte reads of lanes 4j + i / 4,
 // j = 0..3 (four consecutive 16-bit values read by four lanes become one
@@ -856,6 +932,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sum_kernel(
     if (HASH) load_wrows<D>(W, L, P, wr);
     const TMask tm = t_mask<PV>(P);
     const bf16x8 sel[2] = {selection(0), selection(1)};
+    const halfx8 sel16[2] = {selection16(0), selection16(1)};
     const float qw = writer_scale(P, 4 * w + g < vtables(L, P));  // writer features: 2^-P, padding 0
     floatx4 af[4][NT];
 #pragma unroll
@@ -900,26 +977,24 @@ __global__ __launch_bounds__(NW * 64, 2) void sum_kernel(
             hc_load<NW>(hc_res<NW>(cin_t, chunk(ci + 1)), tc);
         ystage_load<NTHR, DVAL, D>(yres<DVAL, D>(vh, chunk(ci + 2)), ys);
         if (!HASH) pin_loads();
-        bf16x8 ptm[2][2], pfm[4];
+        bf16x8 pfm[4];
         Rsrc rto, rco;
         if constexpr (HASH && (WR & 1) != 0) rto = hc_res<NW>(cout_t, cc);
         if constexpr (HASH && (WR & 2) != 0) rco = hc_res<NW>(cout_c, cc);
+        halfx4 tw[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            halfx4 t;
             if constexpr (HASH) {
                 halfx4 c;
-                hash_staged<POLY, (WR & 2) != 0>(xbuf[b], kbuf[b], tt, wr, sq, tm, t, c);
+                hash_staged<POLY, (WR & 2) != 0>(xbuf[b], kbuf[b], tt, wr, sq, tm, tw[tt], c);
                 if constexpr ((WR & 2) != 0) hc_store<NW>(rco, tt, c);
-                if constexpr ((WR & 1) != 0) hc_store<NW>(rto, tt, t);
+                if constexpr ((WR & 1) != 0) hc_store<NW>(rto, tt, tw[tt]);
             } else {
-                t = tcur[tt];
+                tw[tt] = tcur[tt];
             }
-            const VT vt = vt_expand<PV>(t, P);
-            walsh_tm(vt.t, qw * vt.tau, ptm[tt][0], ptm[tt][1]);
         }
         if constexpr (HASH) prio<1>();
-        feat_major(ptm, sel, pfm);
+        writer_fm<PV>(tw, P, qw, sel, sel16, pfm);
         // tokens past the end have psi_0 = 1/4 but zero value rows
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
@@ -1345,7 +1420,10 @@ __global__ __launch_bounds__(NW * 64, 2) void grad_kernel(
         }
     if constexpr (DW)
         for (int e = threadIdx.x; e < NW * 16 * HD; e += NTHR) dwl[e] = 0.f;
-    stage_sel(sl);
+    if constexpr (PV)
+        stage_sel(sl);
+    else
+        stage_sel16(reinterpret_cast<_Float16 *>(sl));
     // the selection operands are read in the first chunk before its barrier
     // (and a wave whose W rows are all padding reaches that read early)
     __syncthreads();
@@ -1488,16 +1566,15 @@ __global__ __launch_bounds__(NW * 64, 2) void grad_kernel(
         hc_load<NW>(hc_res<NW>(rc_seg, cn), rcv);
         bf16x8 pfm[4];
         if (CAUSAL) {
-            bf16x8 pw[2][2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const VT vt = vt_expand<PV>(wt[tt], P);
-                walsh_tm(vt.t, qw * vt.tau, pw[tt][0], pw[tt][1]);
-            }
+            const halfx4 wcur[2] = {wt[0], wt[1]};
             hc_load<NW>(hc_res<NW>(wt_seg, cn), wt);
             bf16x8 sel[2];
-            sel_lds(sl, sel);
-            feat_major(pw, sel, pfm);
+            halfx8 sel16[2];
+            if constexpr (PV)
+                sel_lds(sl, sel);
+            else
+                sel_lds16(reinterpret_cast<const _Float16 *>(sl), sel16);
+            writer_fm<PV>(wcur, P, qw, sel, sel16, pfm);
         }
         lds_barrier();  // value rows of this chunk; du and rows of ci - 1; dots of ci - 2
         if constexpr (!DUO) {
