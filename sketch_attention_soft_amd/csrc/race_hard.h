@@ -458,14 +458,20 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
 {
     constexpr int NTHR = NW * 64;
     constexpr int REDN = NW * 2 * HNT * 64 * 4;  // partial outputs of every wave
+    // 8-wave workgroups (one per compute unit) double-buffer the partial
+    // outputs and counts, so that a chunk needs one barrier: chunk c's are
+    // summed after the barrier of chunk c + 1.  Narrower ones run two per
+    // compute unit, which LDS allows only with one buffer and a second
+    // barrier per chunk.
+    constexpr int NRED = NW >= 8 ? 2 : 1;
     __shared__ __attribute__((aligned(16))) bf16 ycol[2][CAUSAL ? NCOL * YCS : 8];
     __shared__ uint32_t qids[2][8 * 32 + 1];
     __shared__ uint32_t kids[2][CAUSAL ? 8 * 32 + 1 : 1];
     __shared__ uint32_t bmw[CAUSAL ? NW : 1][64];  // this chunk's bucket token masks, per wave
     __shared__ uint32_t cntw[NW][64];              // counts of the keys before the chunk, per wave
     __shared__ uint32_t lut[32];
-    __shared__ __attribute__((aligned(16))) float red[REDN];
-    __shared__ uint32_t redm[NW][32];              // each wave's count of every query
+    __shared__ __attribute__((aligned(16))) float red[NRED][REDN];
+    __shared__ uint32_t redm[NRED][NW][32];        // each wave's count of every query
     const int64_t bh = blockIdx.x / nseg, sg = blockIdx.x % nseg;
     const int lane = lane_id(), w = wave_id(), g = lane >> 4, c16 = lane & 15;
     const int64_t t_begin = sg * seg, row0 = row_base(ls, bh, N) + t_begin;
@@ -509,8 +515,37 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             ystage_load<NTHR, false, D>(yres<false, D>(vh, chunk(0)), ys);
         }
     }
-    for (int ci = 0; ci < nch; ++ci) {
-        const int b = ci & 1;
+    // outputs of chunk ci from the partial sums in buffer pb: thread slot
+    // (token tile tt, column tile ct, lane)
+    auto finish = [&](int ci, int pb) {
+        const Chunk cc = chunk(ci);
+        const Rsrc ro = row_res<D>(Os, cc);
+        const float *rd = red[NRED == 2 ? pb : 0];
+        const uint32_t(*rm)[32] = redm[NRED == 2 ? pb : 0];
+        for (int sl = threadIdx.x; sl < 2 * HNT * 64; sl += NTHR) {
+            const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63, tok = tt * 16 + (ln & 15);
+            floatx4 n = *reinterpret_cast<const floatx4 *>(rd + ((tt * HNT + ct) * 64 + ln) * 4);
+            uint32_t m = rm[0][tok];
+            for (int ww = 1; ww < NW; ++ww) {
+                n += *reinterpret_cast<const floatx4 *>(rd + (((ww * 2 + tt) * HNT + ct) * 64 + ln) * 4);
+                m += rm[ww][tok];
+            }
+            // a query that meets no visible key in any table: an empty sum,
+            // o = 0 (n is 0 too)
+            const float inv = m > 0 ? 1.f / (float)m : 0.f;
+            const int col = 16 * ct + 4 * (ln >> 4);
+            const int off = (D == HD || col < D) ? tok * (D * 2) + col * 2 : OOB;
+            bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
+            if (ct == 0 && ln < 16) {
+                bstf((float)m, make_rsrc(dens + cc.tok0, cc.nv * 4), tok * 4);
+                if (cnts)
+                    __builtin_amdgcn_raw_buffer_store_b32(m, make_rsrc(cnts + cc.tok0, cc.nv * 4), tok * 4,
+                                                          0, 0);
+            }
+        }
+    };
+    for_chunks2(nch, [&](int ci, auto par) {
+        constexpr int b = decltype(par)::v;
         const Chunk cc = chunk(ci), cn = chunk(ci + 1);
         // stage ids (and keys' [v | 1]) of chunk ci into buffers last read
         // before the previous barrier, then start loading chunk ci + 1
@@ -527,6 +562,8 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             }
         }
         __syncthreads();
+        // (the previous chunk's partial sums, in the other buffer)
+        if (NRED == 2 && ci > 0) finish(ci - 1, b ^ 1);
         if (CAUSAL) wave_masks(bm, kids[b], L, cc.nv, w);
         {
             // this wave's count of each query: its buckets' counts before the
@@ -545,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
                 }
             }
             m += __shfl_xor(m, 32);
-            if (lane < 32) redm[w][tok] = m;
+            if (lane < 32) redm[NRED == 2 ? b : 0][w][tok] = m;
         }
         if (CAUSAL) {
             // the chunk's keys join the counts (after the reads above: this
@@ -621,35 +658,20 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             }
         }
         // partial outputs of this wave
+        float *rd = red[NRED == 2 ? b : 0];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int ct = 0; ct < HNT; ++ct)
-                *reinterpret_cast<floatx4 *>(red + (((w * 2 + tt) * HNT + ct) * 64 + lane) * 4) = oacc[tt][ct];
-        __syncthreads();
-        // outputs of the chunk: thread slot (token tile tt, column tile ct, lane)
-        const Rsrc ro = row_res<D>(Os, cc);
-        for (int sl = threadIdx.x; sl < 2 * HNT * 64; sl += NTHR) {
-            const int tt = sl >> 8, ct = (sl >> 6) & 3, ln = sl & 63, tok = tt * 16 + (ln & 15);
-            floatx4 n = *reinterpret_cast<const floatx4 *>(red + ((tt * HNT + ct) * 64 + ln) * 4);
-            uint32_t m = redm[0][tok];
-            for (int ww = 1; ww < NW; ++ww) {
-                n += *reinterpret_cast<const floatx4 *>(red + (((ww * 2 + tt) * HNT + ct) * 64 + ln) * 4);
-                m += redm[ww][tok];
-            }
-            // a query that meets no visible key in any table: an empty sum,
-            // o = 0 (n is 0 too)
-            const float inv = m > 0 ? 1.f / (float)m : 0.f;
-            const int col = 16 * ct + 4 * (ln >> 4);
-            const int off = (D == HD || col < D) ? tok * (D * 2) + col * 2 : OOB;
-            bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
-            if (ct == 0 && ln < 16) {
-                bstf((float)m, make_rsrc(dens + cc.tok0, cc.nv * 4), tok * 4);
-                if (cnts)
-                    __builtin_amdgcn_raw_buffer_store_b32(m, make_rsrc(cnts + cc.tok0, cc.nv * 4), tok * 4,
-                                                          0, 0);
-            }
+                *reinterpret_cast<floatx4 *>(rd + (((w * 2 + tt) * HNT + ct) * 64 + lane) * 4) = oacc[tt][ct];
+        if constexpr (NRED == 1) {
+            __syncthreads();
+            finish(ci, 0);
         }
+    });
+    if (NRED == 2 && nch > 0) {
+        __syncthreads();
+        finish(nch - 1, (nch - 1) & 1);
     }
 }
 
