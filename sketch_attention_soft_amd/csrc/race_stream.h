@@ -48,6 +48,17 @@ constexpr int S_XS = HD + 1;     // LDS row stride of staged rows and W (odd: no
 
 template <typename T> __device__ __forceinline__ float sload(const T *p) { return (float)*p; }
 
+// sum over the 64 lanes of a wave (every lane active): rows of 16 through
+// DPP, then the four row sums read out of lanes 0, 16, 32, 48 (uniform)
+__device__ __forceinline__ float wave_sum(float x)
+{
+    const int r = __builtin_bit_cast(int, sum16(x));
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 48)));
+}
+
 // MAXT threads = MAXT / 64 waves of FPT features: F <= FMAX = FPT MAXT / 64
 // and L P <= FMAX P / 16 (the launch picks the instance that fits).  Tiles
 // of S_TT tokens: TT, or with TT = 0 eight (four for L > 32 decode, for LDS);
@@ -84,6 +95,21 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
     const int64_t t_begin = (int64_t)blockIdx.x * blk, t_end = min(N, t_begin + blk);
     const int64_t row0 = bh * N;
     float *sh = state + bh * (int64_t)F * sc;
+    // One decode token per head (TT = 1 instances, launched for N = 1 only):
+    // the single tile's row elements are loaded first, beside W, and the
+    // state after the rows are staged, so that one memory round trip comes
+    // before the first barrier and the state arrives while the token is
+    // hashed; the state is stored as soon as it is updated, under the readout.
+    constexpr bool ONE = MODE == SM_DECODE && TT == 1;
+    float r1q = 0.f, r1k = 0.f, r1v = 0.f;
+    if constexpr (ONE) {
+        if (tid < d && t_begin < t_end) {
+            const int64_t off = (row0 + t_begin) * d + tid;
+            r1q = sload(Q + off);
+            r1k = sload(K + off);
+            r1v = sload(V + off);
+        }
+    }
 
     // W rows in LDS: each thread issues all its loads before its stores, so
     // the staging costs one memory round trip (LP HD <= WPT nthr, since nthr =
@@ -116,17 +142,38 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
         return 64 * z + c < FPT && f < F ? (f * sc + d) * 4 : OOB;
     };
     float S[FPT], Z[ZP];
+    auto load_state = [&]() {
 #pragma unroll
-    for (int i = 0; i < FPT; ++i)
-        S[i] = MODE != SM_ADD
-                   ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, i * rstep, 0))
-                   : 0.f;
+        for (int i = 0; i < FPT; ++i)
+            S[i] = MODE != SM_ADD
+                       ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off, i * rstep, 0))
+                       : 0.f;
 #pragma unroll
-    for (int z = 0; z < ZP; ++z) Z[z] = MODE != SM_ADD ? bldf(rs, z_off(z)) : 0.f;
+        for (int z = 0; z < ZP; ++z) Z[z] = MODE != SM_ADD ? bldf(rs, z_off(z)) : 0.f;
+    };
+    float *dst = MODE == SM_DECODE ? sh
+                 : MODE == SM_ADD    ? part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * sc
+                                     : nullptr;
+    auto store_state = [&]() {
+        const Rsrc rd = make_rsrc(dst, F * sc * 4);
+#pragma unroll
+        for (int i = 0; i < FPT; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, S[i]), rd, lane_off, i * rstep, 0);
+#pragma unroll
+        for (int z = 0; z < ZP; ++z) bstf(Z[z], rd, z_off(z));
+    };
+    if constexpr (!ONE) load_state();
 
     for (int64_t tile = t_begin; tile < t_end; tile += S_TT) {
         const int nt = (int)min<int64_t>(S_TT, t_end - tile);
         // rows of the tile (zeros past the end)
+        if constexpr (ONE) {
+            if (tid < HD) {
+                xr[0][0][tid] = r1q;
+                xr[KS][0][tid] = r1k;
+                yv[0][tid] = r1v;
+            }
+        } else
         for (int e = tid; e < S_TT * HD; e += nthr) {
             const int t = e / HD, k = e % HD;
             float q = 0.f, kk = 0.f, v = 0.f;
@@ -145,12 +192,11 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
             }
         }
         __syncthreads();
+        if constexpr (ONE) load_state();
         // squared norms: wave w takes rows w, w + NWV, ...; lane k one element
         for (int r = grp; r < NS * nt; r += nthr >> 6) {
             const int side = r / nt, t = r % nt;
-            float ss = xr[side][t][c] * xr[side][t][c];
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+            const float ss = wave_sum(xr[side][t][c] * xr[side][t][c]);
             if (c == 0) inrm[side][t] = 1.f / fmaxf(sqrtf(ss), 1e-12f);
         }
         __syncthreads();
@@ -204,11 +250,11 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
                 for (int z = 0; z < ZP; ++z)
                     if (64 * z + c < FPT) m = fmaf(ps[0][t][f0 + 64 * z + c], Z[z], m);
                 pn[t][grp][c] = n;
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) m += __shfl_xor(m, o, 64);
+                m = wave_sum(m);
                 if (c == 0) pm[t][grp] = m;
             }
         }
+        if constexpr (ONE) store_state();
         __syncthreads();
         if (RD) {
             for (int e = tid; e < nt * (d + 1); e += nthr) {
@@ -227,15 +273,7 @@ __attribute__((amdgpu_waves_per_eu(MODE != SM_DECODE && MAXT <= 512 ? 4 : 1))) v
             __syncthreads();  // the tile's LDS is rewritten next
         }
     }
-    if (MODE != SM_READOUT) {
-        float *dst = MODE == SM_DECODE ? sh : part + ((int64_t)bh * gridDim.x + blockIdx.x) * (int64_t)F * sc;
-        const Rsrc rd = make_rsrc(dst, F * sc * 4);
-#pragma unroll
-        for (int i = 0; i < FPT; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, S[i]), rd, lane_off, i * rstep, 0);
-#pragma unroll
-        for (int z = 0; z < ZP; ++z) bstf(Z[z], rd, z_off(z));
-    }
+    if (MODE != SM_READOUT && !ONE) store_state();
 }
 
 // state[head] += sum over the blocks b = 0, 1, ... of part[head][b] (in that
