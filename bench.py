@@ -89,12 +89,22 @@ def algorithmic_per_token(w, dw: bool = False, saved: bool = True):
     return fwd_flops + bwd_flops, 12 * d * e + 8, per_kernel
 
 
+# The sources the fused 16-bit kernels (sum_kv ... dv) are built, launched and
+# planned from; the other files of csrc/ hold other kernels (the fp32 path,
+# d = 128 rows, hard hashing, the streaming state) that leave these unchanged.
+FUSED_SOURCES = ("csrc/race_walk.h", "csrc/race_common.h", "csrc/race_fwd.h", "csrc/race_squash.h",
+                 "csrc/race_host.h", "csrc/race_attn.hip", "csrc/race_inst_bf16_fwd.hip",
+                 "csrc/race_inst_bf16_bwd.hip")
+
+
 def kernel_sources_digest() -> str:
-    """sha256 over the kernel sources (file names and bytes, sorted by name)."""
-    import glob
+    """sha256 over the fused kernels' sources and the C header (each file's
+    name, then its bytes, sorted by name)."""
     import hashlib
+    files = [os.path.join(HERE, "sketch_attention_soft_amd", f) for f in FUSED_SOURCES]
+    files.append(os.path.join(HERE, "include", "race_attn.h"))
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(HERE, "sketch_attention_soft_amd", "csrc", "*"))):
+    for f in sorted(files, key=os.path.basename):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
