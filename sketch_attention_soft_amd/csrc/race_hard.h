@@ -183,6 +183,9 @@ __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X,
             if (e < PIECES) *reinterpret_cast<u32x4 *>(xs + rr * STRIDE + pc * 16) = v[i];
         }
         if (blk + gridDim.x < nblk) load_block(blk + gridDim.x);
+        // the words are OR-ed together below: clear them (their last reads,
+        // the previous block's ids, came before the barrier above)
+        for (int e = threadIdx.x; e < ROWS * nwd; e += 256) mask[e / nwd][e % nwd] = 0u;
         __syncthreads();
         // pairs of hyperplane tiles make one 32-bit word: lane group g holds
         // the nibbles at bits 4 g (tile 2 wd) and 16 + 4 g (tile 2 wd + 1)
@@ -211,9 +214,9 @@ __global__ __launch_bounds__(256) void hard_ids_kernel(const IO *__restrict__ X,
                     for (int r = 0; r < 4; ++r) nib |= (u[r] >= 0.f ? 1u : 0u) << r;
                     word |= nib << (16 * h2 + 4 * g);
                 }
-                word |= __shfl_xor(word, 16);
-                word |= __shfl_xor(word, 32);
-                if (g == 0) mask[rt * 16 + c16][wd] = word;
+                // the four lane groups' nibbles meet in LDS (an OR that
+                // returns nothing, so the next tile does not wait on it)
+                atomicOr(&mask[rt * 16 + c16][wd], word);
             }
         }
         __syncthreads();
