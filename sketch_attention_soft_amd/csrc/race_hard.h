@@ -280,10 +280,17 @@ __device__ __forceinline__ bf16x4 lut4(const uint32_t *lut, uint32_t nib)
 }
 // token-major one-hot operand (lane group g: buckets 4g .. 4g + 3 of tables
 // t0 then t1, the K-slot order of the state operands); id 16 (none) gives zeros
-__device__ __forceinline__ uint32_t onehot_bit(uint32_t id) { return id < 16u ? 1u << id : 0u; }
+// (ids of valid rows are 0 .. 16: the bit of id 16 lies past every group's
+// nibble, bits 4 g .. 4 g + 3 with g <= 3, so it needs no test; bytes past a
+// chunk's valid rows only reach tokens whose scores are masked out or whose
+// value rows and outputs are zero or dropped)
+__device__ __forceinline__ uint32_t onehot_nib(uint32_t id, int g)
+{
+    return __builtin_amdgcn_ubfe(1u << (id & 31u), 4 * g, 4);
+}
 __device__ __forceinline__ bf16x8 onehot_tm(const uint32_t *lut, uint32_t id0, uint32_t id1, int g)
 {
-    return cat8(lut4(lut, (onehot_bit(id0) >> (4 * g)) & 15u), lut4(lut, (onehot_bit(id1) >> (4 * g)) & 15u));
+    return cat8(lut4(lut, onehot_nib(id0, g)), lut4(lut, onehot_nib(id1, g)));
 }
 // feature-major one-hot operand of one table from its bucket's token mask
 // (bit j: token j of the chunk falls in the bucket); K-slots (g, r) <-> token
