@@ -297,7 +297,7 @@ __device__ __forceinline__ bf16x8 onehot_tm(const uint32_t *lut, uint32_t id0, u
 // 4g + r, (g, 4 + r) <-> token 16 + 4g + r, as ycol_frag
 __device__ __forceinline__ bf16x8 onehot_fm(const uint32_t *lut, uint32_t m, int g)
 {
-    return cat8(lut4(lut, (m >> (4 * g)) & 15u), lut4(lut, (m >> (16 + 4 * g)) & 15u));
+    return cat8(lut4(lut, __builtin_amdgcn_ubfe(m, 4 * g, 4)), lut4(lut, __builtin_amdgcn_ubfe(m, 16 + 4 * g, 4)));
 }
 
 // ids of one chunk's rows: rsrc over its nv rows of L bytes, rounded up to
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(NW * 64) void hard_walk_kernel(
             }
             // a query that meets no visible key in any table: an empty sum,
             // o = 0 (n is 0 too)
-            const float inv = m > 0 ? 1.f / (float)m : 0.f;
+            const float inv = m > 0 ? __builtin_amdgcn_rcpf((float)m) : 0.f;
             const int col = 16 * ct + 4 * (ln >> 4);
             const int off = (D == HD || col < D) ? tok * (D * 2) + col * 2 : OOB;
             bst64(u32x2{pk_io<IO>(n[0] * inv, n[1] * inv), pk_io<IO>(n[2] * inv, n[3] * inv)}, ro, off);
